@@ -1,0 +1,250 @@
+"""Pins for the fp64 oracle, independent of the oracle's own code.
+
+Each test checks the recurrent C oracle against something the mathematics
+fixes: the definition's double sum on tiny inputs, closed forms (lambda = 1,
+lambda = 0, d = 1 geometric series, zero keys), the block decomposition, and
+invariants (split with carried state, prefill == decode steps, linearity,
+head/batch equivariance).  The decayed linear-attention recurrence itself is
+the one the Ling and Ring 2.6 Technical Report (§4.1.1) describes as an
+RNN-style recurrence over a [B,H,D,D] state.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rand_inputs(rng, B, H, N, d, with_state=True):
+    q = rng.standard_normal((B, H, N, d)) / math.sqrt(d)
+    k = rng.standard_normal((B, H, N, d)) / math.sqrt(d)
+    v = rng.standard_normal((B, H, N, d))
+    S0 = 0.1 * rng.standard_normal((B, H, d, d)) if with_state else None
+    return q, k, v, S0
+
+
+def slopes_for(lams):
+    return np.array([math.inf if l == 0 else -math.log(l) for l in lams])
+
+
+LAMS = [0.0, 0.4, 0.94, 0.996, 1.0]
+
+
+@pytest.mark.parametrize("N,d", [(1, 1), (7, 3), (37, 8), (64, 5)])
+def test_recurrent_matches_quadratic_definition(N, d):
+    rng = np.random.default_rng(N * 100 + d)
+    B, H = 2, len(LAMS)
+    q, k, v, S0 = rand_inputs(rng, B, H, N, d)
+    s = slopes_for(LAMS)
+    o_r, f_r = oracle.prefill(q, k, v, s, S0)
+    o_q, f_q = oracle.quadratic(q, k, v, s, S0)
+    assert oracle.rel_l2(o_r, o_q) <= 1e-12
+    assert oracle.rel_l2(f_r, f_q) <= 1e-12
+
+
+def test_non_square_roles_are_not_transposed():
+    # asymmetric state and distinct q/k/v: a transposed S (S[j][i]) or swapped
+    # q/k roles changes the result; the double sum fixes which is right.
+    rng = np.random.default_rng(7)
+    q, k, v, S0 = rand_inputs(rng, 1, 1, 9, 4)
+    s = slopes_for([0.7])
+    o_r, f_r = oracle.prefill(q, k, v, s, S0)
+    o_q, f_q = oracle.quadratic(q, k, v, s, S0)
+    assert oracle.rel_l2(o_r, o_q) <= 1e-12
+    o_t, _ = oracle.quadratic(q, k, v, s, np.swapaxes(S0, -1, -2))
+    assert oracle.rel_l2(o_t, o_q) > 1e-3        # the transpose is detectable
+    o_s, _ = oracle.quadratic(k, q, v, s, S0)
+    assert oracle.rel_l2(o_s, o_q) > 1e-3        # swapping q and k is detectable
+
+
+def test_lambda_one_is_plain_causal_linear_attention():
+    # lambda = 1: o_t = q_t (S_init + sum_{s<=t} k_s^T v_s), final S_init + K^T V
+    rng = np.random.default_rng(11)
+    B, H, N, d = 2, 2, 33, 6
+    q, k, v, S0 = rand_inputs(rng, B, H, N, d)
+    s = np.zeros(H)
+    o, f = oracle.prefill(q, k, v, s, S0)
+    kv = np.einsum("bhti,bhtj->bhtij", k, v)
+    pref = S0[:, :, None] + np.cumsum(kv, axis=2)
+    o_ref = np.einsum("bhti,bhtij->bhtj", q, pref)
+    assert oracle.rel_l2(o, o_ref) <= 1e-12
+    assert oracle.rel_l2(f, S0 + np.einsum("bhti,bhtj->bhij", k, v)) <= 1e-12
+
+
+def test_lambda_zero_keeps_only_the_diagonal():
+    # lambda = 0 (slope +inf): o_t = (q_t . k_t) v_t, final k_{N-1}^T v_{N-1}
+    rng = np.random.default_rng(12)
+    B, H, N, d = 1, 3, 10, 5
+    q, k, v, S0 = rand_inputs(rng, B, H, N, d)
+    s = np.full(H, math.inf)
+    o, f = oracle.prefill(q, k, v, s, S0)
+    o_ref = np.sum(q * k, axis=-1, keepdims=True) * v
+    assert oracle.rel_l2(o, o_ref) <= 1e-15
+    f_ref = np.einsum("bhi,bhj->bhij", k[:, :, -1], v[:, :, -1])
+    assert oracle.rel_l2(f, f_ref) <= 1e-15
+
+
+def test_geometric_series_worked_values():
+    with open(os.path.join(GOLDEN, "geometric_d1.json")) as fh:
+        cases = json.load(fh)["cases"]
+    for c in cases:
+        N = c["N"]
+        one = np.ones((1, 1, N, 1))
+        s = slopes_for([c["lambda"]])
+        S0 = np.full((1, 1, 1, 1), c["S_init"])
+        o, f = oracle.prefill(one, one, one, s, S0)
+        np.testing.assert_allclose(o[0, 0, :, 0], c["out"], rtol=1e-14, atol=1e-15)
+        np.testing.assert_allclose(f[0, 0, 0, 0], c["final"], rtol=1e-14, atol=1e-15)
+
+
+def test_geometric_closed_form_long():
+    # d = 1, q = k = v = 1: o_t = (1 - lam^(t+1)) / (1 - lam) + lam^(t+1) S0
+    N = 300
+    lams = [0.3, 0.9, 0.999]
+    one = np.ones((1, 3, N, 1))
+    S0 = np.array([0.5, -1.0, 3.0]).reshape(1, 3, 1, 1)
+    o, f = oracle.prefill(one, one, one, slopes_for(lams), S0)
+    t = np.arange(N)
+    for h, lam in enumerate(lams):
+        lam = math.exp(-slopes_for([lam])[0])
+        ref = (1 - lam ** (t + 1)) / (1 - lam) + lam ** (t + 1) * S0[0, h, 0, 0]
+        np.testing.assert_allclose(o[0, h, :, 0], ref, rtol=1e-12)
+
+
+def test_initial_state_decays_at_the_first_token():
+    # zero keys: o_t = lam^(t+1) q_t S_init and final = lam^N S_init
+    rng = np.random.default_rng(3)
+    B, H, N, d = 1, 2, 12, 4
+    q, _, v, S0 = rand_inputs(rng, B, H, N, d)
+    k = np.zeros_like(q)
+    lams = [0.8, 0.5]
+    o, f = oracle.prefill(q, k, v, slopes_for(lams), S0)
+    for h, lam in enumerate(lams):
+        lam = math.exp(-slopes_for([lam])[0])
+        for t in range(N):
+            ref = lam ** (t + 1) * (q[0, h, t] @ S0[0, h])
+            np.testing.assert_allclose(o[0, h, t], ref, rtol=1e-13)
+        np.testing.assert_allclose(f[0, h], lam ** N * S0[0, h], rtol=1e-13)
+
+
+@pytest.mark.parametrize("C", [1, 3, 32, 64, 70])
+def test_blockwise_decomposition_reaches_the_definition(C):
+    rng = np.random.default_rng(C)
+    B, H, N, d = 1, 3, 70, 8
+    q, k, v, S0 = rand_inputs(rng, B, H, N, d)
+    s = slopes_for([0.4, 0.94, 0.996])
+    o_r, f_r = oracle.prefill(q, k, v, s, S0)
+    o_b, f_b = oracle.blockwise(q, k, v, s, S0, C=C)
+    assert oracle.rel_l2(o_b, o_r) <= 1e-12
+    assert oracle.rel_l2(f_b, f_r) <= 1e-12
+
+
+@pytest.mark.parametrize("m", [1, 32, 33, 63])
+def test_split_with_carried_state_is_bitwise_identical(m):
+    rng = np.random.default_rng(m)
+    B, H, N, d = 2, 2, 64, 8
+    q, k, v, S0 = rand_inputs(rng, B, H, N, d)
+    s = slopes_for([0.5, 0.99])
+    o, f = oracle.prefill(q, k, v, s, S0)
+    o1, f1 = oracle.prefill(q[:, :, :m], k[:, :, :m], v[:, :, :m], s, S0)
+    o2, f2 = oracle.prefill(q[:, :, m:], k[:, :, m:], v[:, :, m:], s, f1)
+    assert np.array_equal(np.concatenate([o1, o2], axis=2), o)
+    assert np.array_equal(f2, f)
+
+
+def test_prefill_equals_decode_steps():
+    rng = np.random.default_rng(5)
+    B, H, N, d = 2, 3, 9, 6
+    q, k, v, S0 = rand_inputs(rng, B, H, N, d)
+    s = slopes_for([0.3, 0.9, 1.0])
+    o, f = oracle.prefill(q, k, v, s, S0)
+    st = S0
+    for t in range(N):
+        ot, st = oracle.decode_step(q[:, :, t], k[:, :, t], v[:, :, t], s, st)
+        assert np.array_equal(ot, o[:, :, t])
+    assert np.array_equal(st, f)
+
+
+def test_linear_in_v_and_q_bilinear_in_k_v():
+    rng = np.random.default_rng(9)
+    B, H, N, d = 1, 2, 20, 5
+    q, k, v1, _ = rand_inputs(rng, B, H, N, d, with_state=False)
+    v2 = rng.standard_normal(v1.shape)
+    q2 = rng.standard_normal(q.shape)
+    s = slopes_for([0.6, 0.97])
+    a, b = 1.75, -0.5
+    o1, f1 = oracle.prefill(q, k, v1, s)
+    o2, f2 = oracle.prefill(q, k, v2, s)
+    o12, f12 = oracle.prefill(q, k, a * v1 + b * v2, s)
+    assert oracle.rel_l2(o12, a * o1 + b * o2) <= 1e-13
+    assert oracle.rel_l2(f12, a * f1 + b * f2) <= 1e-13
+    oq, _ = oracle.prefill(q2, k, v1, s)
+    oqq, _ = oracle.prefill(a * q + b * q2, k, v1, s)
+    assert oracle.rel_l2(oqq, a * o1 + b * oq) <= 1e-13
+    ok, fk = oracle.prefill(q, 2.0 * k, v1, s)
+    assert oracle.rel_l2(ok, 2.0 * o1) <= 1e-14 and oracle.rel_l2(fk, 2.0 * f1) <= 1e-14
+
+
+def test_heads_and_batch_are_independent():
+    rng = np.random.default_rng(21)
+    B, H, N, d = 3, 4, 15, 4
+    q, k, v, S0 = rand_inputs(rng, B, H, N, d)
+    s = slopes_for([0.2, 0.5, 0.9, 0.99])
+    o, f = oracle.prefill(q, k, v, s, S0)
+    pb = [2, 0, 1]
+    ph = [3, 1, 0, 2]
+    qp, kp, vp, Sp = (x[pb][:, ph] for x in (q, k, v, S0))
+    op, fp = oracle.prefill(qp, kp, vp, s[ph], Sp)
+    assert np.array_equal(op, o[pb][:, ph]) and np.array_equal(fp, f[pb][:, ph])
+
+
+def test_empty_sequence_leaves_state():
+    rng = np.random.default_rng(1)
+    q, k, v, S0 = rand_inputs(rng, 1, 2, 0, 4)
+    o, f = oracle.prefill(q, k, v, slopes_for([0.5, 0.9]), S0)
+    assert o.shape == (1, 2, 0, 4) and np.array_equal(f, S0)
+
+
+# --- the pins catch plausible mistakes: planted in a Python copy of the
+# recurrence (CPU only), each mistake must fail the double-sum comparison.
+
+def _mutant_recurrence(q, k, v, lam, S0, mutation):
+    N, d = q.shape
+    S = S0.copy()
+    o = np.zeros((N, d))
+    for t in range(N):
+        if mutation == "read_before_update":
+            o[t] = q[t] @ S
+            S = lam * S + np.outer(k[t], v[t])
+            continue
+        if mutation == "no_decay_on_state":
+            S = S + np.outer(k[t], v[t])
+        elif mutation == "decay_on_new_term":
+            S = lam * (S + np.outer(k[t], v[t]))
+        elif mutation == "transposed_update":
+            S = lam * S + np.outer(v[t], k[t])
+        else:
+            S = lam * S + np.outer(k[t], v[t])
+        o[t] = (S @ q[t]) if mutation == "transposed_read" else (q[t] @ S)
+    return o
+
+
+@pytest.mark.parametrize("mutation", ["read_before_update", "no_decay_on_state",
+                                      "decay_on_new_term", "transposed_update",
+                                      "transposed_read"])
+def test_pins_detect_planted_mistakes(mutation):
+    rng = np.random.default_rng(99)
+    N, d = 11, 4
+    q, k, v, S0 = rand_inputs(rng, 1, 1, N, d)
+    v = rng.standard_normal(v.shape)
+    lam = 0.8
+    o_q, _ = oracle.quadratic(q, k, v, slopes_for([lam]), S0)
+    good = _mutant_recurrence(q[0, 0], k[0, 0], v[0, 0], lam, S0[0, 0], None)
+    assert oracle.rel_l2(good, o_q[0, 0]) <= 1e-12
+    bad = _mutant_recurrence(q[0, 0], k[0, 0], v[0, 0], lam, S0[0, 0], mutation)
+    assert oracle.rel_l2(bad, o_q[0, 0]) > 1e-3

@@ -1,0 +1,247 @@
+"""Benchmark: decayed causal linear attention (Lightning Attention) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = one pass of the whole hot path over resident synthetic inputs:
+  * prefill of B=1, H=64, N=262,144, d=128 bf16 tokens from a zero state
+    (la_prefill: blockwise intra scores, inter term from the carried state,
+    decayed state scan), and
+  * one batched decode step of B=256 sequences, H=64, d=128 with fp32 states
+    (la_decode_step), cycling through 64 pre-staged bf16 tokens.
+The JSON line's ``value`` is the prefill throughput in algorithmic TFLOP/s
+(B*H*N*(4 d^2 + 2 (C+1) d) with C = 64, i.e. 82,176 flop per token-head,
+whatever block length the kernel uses), from HIP events around each prefill
+launch on its stream.  The decode step is reported in GB/s of state traffic.
+``roofline`` is the prefill kernel's HBM roofline (algorithmic bytes per
+launch / launch time against 8 TB/s); ``cpu_baseline`` times the fp64 CPU
+oracle on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Lightning-attn prefill TFLOP/s (H=64,d=128,N=32K-256K); decode state GB/s"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+C_COUNT = 64                     # block length the flop count is fixed at
+
+PREFILL = dict(B=1, H=64, N=262144, d=128, seed=1003)
+DECODE = dict(B=256, H=64, d=128, steps=64, seed=1004)
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_256k_traffic.txt")
+KERNEL_SRC = os.path.join(ROOT, "long_context_layers_amd", "csrc", "prefill_bf16.hip")
+
+
+def prefill_flops(B, H, N, d):
+    return B * H * N * (4 * d * d + 2 * (C_COUNT + 1) * d)
+
+
+def prefill_bytes(B, H, N, d):
+    # q, k, v read and out written in bf16, plus the fp32 state read and written
+    return B * H * N * d * 2 * 4 + B * H * d * d * 4 * 2
+
+
+def decode_bytes(B, H, d):
+    # state read + written (fp32), q, k, v read and out written (bf16)
+    return B * H * (2 * 4 * d * d + 4 * 2 * d)
+
+
+def kernel_hash():
+    with open(KERNEL_SRC, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per prefill launch from the committed rocprofv3 counter
+    summary, or None when it is absent or was taken on another kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]{16})", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != kernel_hash():
+        return None
+    return float(m_bytes.group(1))
+
+
+def cpu_baseline(pre, target_s=15.0):
+    """The fp64 oracle on a bounded sample of the prefill workload: 16 heads
+    (every 4th) and the first n tokens, n chosen from a short calibration so
+    the timed run takes about ``target_s`` seconds."""
+    import torch
+    import oracle
+    heads = list(range(0, pre["H"], 4))
+    idx = torch.tensor(heads, device=pre["q"].device)
+
+    def sample(n):
+        sl = [t.index_select(1, idx)[:, :, :n].float().cpu().double().numpy()
+              for t in (pre["q"], pre["k"], pre["v"])]
+        return sl, pre["slopes"].index_select(0, idx).cpu().double().numpy()
+
+    n_cal = 512
+    (q, k, v), s = sample(n_cal)
+    t0 = time.perf_counter()
+    oracle.prefill(q, k, v, s)
+    dt = max(time.perf_counter() - t0, 1e-3)
+    n = int(min(pre["N"], max(1024, n_cal * target_s / dt)))
+    n -= n % 64
+    (q, k, v), s = sample(n)
+    t0 = time.perf_counter()
+    oracle.prefill(q, k, v, s)
+    dt = time.perf_counter() - t0
+    fl = prefill_flops(1, len(heads), n, pre["d"])
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(oracle.last_threads),
+            "kind": "oracle",
+            "sample": f"fp64 recurrent oracle, heads {heads[0]}..{heads[-1]} step 4 "
+                      f"({len(heads)} heads) x first {n} tokens of the N={pre['N']} "
+                      f"prefill, {dt:.1f} s wall, algorithmic flops counted as on the GPU",
+            "seconds": dt,
+            "host_threads_available": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU oracle timing (for profiler runs)")
+    ap.add_argument("--copy-only", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(heads and batch shard across GPUs with no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from long_context_layers_amd import binding, inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    binding.load_library()
+
+    if args.copy_only:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(max(args.steps, 1)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 4, "copy_bytes_written": dst.numel() * 4,
+                          "launches": max(args.steps, 1)}))
+        return
+
+    stream = torch.cuda.Stream(dev)
+    with torch.cuda.stream(stream):
+        p = inputs.make_prefill(PREFILL["B"], PREFILL["H"], PREFILL["N"], PREFILL["d"],
+                                torch.bfloat16, PREFILL["seed"], False, dev)
+        dcd = inputs.make_decode(DECODE["B"], DECODE["H"], DECODE["d"], DECODE["steps"],
+                                 torch.bfloat16, DECODE["seed"], dev)
+        out = torch.empty_like(p.q)
+        pstate = torch.zeros_like(p.state)
+        dstate = dcd.state.clone()
+        dout = torch.empty_like(dcd.q[0])
+    stream.synchronize()
+    print(f"[bench] inputs resident: prefill {tuple(p.q.shape)} bf16, decode states "
+          f"{tuple(dstate.shape)} fp32", file=sys.stderr, flush=True)
+
+    def step(i, ev=None):
+        pstate.zero_()
+        if ev is not None:
+            ev[0].record(stream)
+        binding.prefill(p.q, p.k, p.v, p.slopes, pstate, out=out)
+        if ev is not None:
+            ev[1].record(stream)
+        t = i % DECODE["steps"]
+        binding.decode_step(dcd.q[t], dcd.k[t], dcd.v[t], dcd.slopes, dstate, out=dout)
+        if ev is not None:
+            ev[2].record(stream)
+
+    with torch.cuda.stream(stream):
+        for i in range(args.warmup):
+            step(i)
+        stream.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            step(args.warmup + i, evs[i])
+        stream.synchronize()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+    pre_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    dec_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    print(f"[bench] {args.steps} steps: prefill {pre_ms:.3f} ms, decode {dec_ms:.3f} ms, "
+          f"wall {wall * 1e3 / args.steps:.3f} ms/step", file=sys.stderr, flush=True)
+
+    B, H, N, d = PREFILL["B"], PREFILL["H"], PREFILL["N"], PREFILL["d"]
+    fl = prefill_flops(B, H, N, d)
+    by = prefill_bytes(B, H, N, d)
+    tflops = fl / (pre_ms * 1e-3) / 1e12
+    gbs = by / (pre_ms * 1e-3) / 1e9
+    dby = decode_bytes(DECODE["B"], DECODE["H"], DECODE["d"])
+    dgbs = dby / (dec_ms * 1e-3) / 1e9
+
+    res = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "prefill B1 H64 N262144 d128 bf16 from a zero state + one decode "
+                        "step B256 H64 d128 (fp32 states)",
+            "prefill": {"B": B, "H": H, "N": N, "d": d, "flop_count_block": C_COUNT},
+            "decode": {"B": DECODE["B"], "H": DECODE["H"], "d": DECODE["d"]},
+        },
+        "prefill_ms": round(pre_ms, 4),
+        "prefill_tflops_frac_of_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(),
+            "algorithmic_bytes_per_launch": by,
+            "kernel": "prefill_bf16_kernel<128>",
+        },
+        "decode": {
+            "value": round(dgbs, 1),
+            "unit": "GB/s",
+            "ms_per_step": round(dec_ms, 4),
+            "frac_of_hbm_peak": round(dgbs / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes_per_step": dby,
+            "kernel": "decode_kernel<bf16,128>",
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(dict(q=p.q, k=p.k, v=p.v, slopes=p.slopes, N=N, d=d, H=H))
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

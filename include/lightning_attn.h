@@ -1,0 +1,119 @@
+/*
+ * lightning_attn.h — C ABI of the MI355X (gfx950) decayed causal linear
+ * attention library (liblightning_attn.so).
+ *
+ * The operation.  The Ling and Ring 2.6 Technical Report (Fig. 2, the
+ * linear-attention layer) puts a "linear attention kernel" between
+ * QK-Norm/RoPE and the grouped RMSNorm; §4.1.1 describes it as linear
+ * attention evaluated through an RNN-style recurrence that carries one
+ * D x D state per (batch, head), i.e. a [B,H,D,D] tensor.  This library
+ * computes that kernel with a per-head exponential decay:
+ *
+ *     lambda_h = exp(-slopes[h])
+ *     o_t = sum_{s<=t} lambda_h^(t-s) (q_t . k_s) v_s + lambda_h^(t+1) q_t S_init
+ *     S_t = lambda_h S_{t-1} + k_t^T v_t ,  o_t = q_t S_t ,  S_{-1} = S_init
+ *
+ * There is no scale factor and no normaliser inside the kernel (the layer
+ * normalises afterwards).  Prefill evaluates the sum blockwise (intra-block
+ * masked scores times V, plus the inter-block term from the state carried by
+ * a decayed scan); decode applies the recurrence to one token.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller, contiguous
+ *    and row-major.  q, k, v, out: [B][H][N][d] for prefill, [B][H][d] for a
+ *    decode step.  State: [B][H][d][d] fp32 with i (the k index) slow and j
+ *    (the v index) fast, so o = q . S is a row vector times a matrix.
+ *    slopes: [H] fp32, shared by every sequence of the batch.
+ *  - bf16 means IEEE bfloat16 (1-8-7), stored as 16-bit words.  Results are
+ *    rounded to bf16 with round-to-nearest-even; accumulation is fp32 and the
+ *    carried state is never rounded below fp32.
+ *  - d must be 64 or 128 (LA_ERR_UNSUPPORTED otherwise).  B, H >= 1; N >= 0
+ *    (N == 0 is a no-op that leaves the state unchanged; q, k, v and out may
+ *    then be NULL, as empty tensors often are).
+ *  - Pointers to activations and states must be 16-byte aligned (decode
+ *    activations: aligned to their element size); slopes 4-byte aligned.
+ *  - out must not overlap q, k, v or the state.
+ *  - stream is a hipStream_t (NULL = the null stream).  Work is enqueued on
+ *    it and the call returns without synchronising; results are ready when
+ *    the stream reaches them.  The library allocates no memory and keeps no
+ *    per-call global state; concurrent calls on different streams with
+ *    disjoint outputs are safe.  Results are deterministic: the same inputs
+ *    on the same GPU give bitwise-equal outputs.
+ *  - Argument checks run on the host before any HIP call.  Data values are
+ *    not validated: slopes >= 0 (lambda <= 1) is the method's domain; +inf
+ *    is accepted and means lambda = 0.
+ *  - Return value: LA_OK, or an la_status error code (see la_status_string).
+ *    On an error nothing has been enqueued, except LA_ERR_HIP, which reports
+ *    a failed launch (the status hipLaunchKernel returned).
+ */
+#ifndef LIGHTNING_ATTN_H
+#define LIGHTNING_ATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LA_OK = 0,
+    LA_ERR_INVALID_ARG = 1,  /* null pointer, negative or overflowing size */
+    LA_ERR_UNSUPPORTED = 2,  /* d not in {64, 128}, or a grid too large */
+    LA_ERR_HIP = 3           /* the kernel launch failed */
+} la_status;
+
+/*
+ * Prefill, bf16 activations (the hot path).
+ *   q, k, v     [B,H,N,d] bf16, read only.
+ *   slopes      [H] fp32, read only.
+ *   out         [B,H,N,d] bf16, written.
+ *   state       [B,H,d,d] fp32, IN/OUT: on entry the initial state S_init
+ *               (zero-fill it for a fresh sequence), on exit S_{N-1}.  Passing
+ *               the state of one call into the next continues the sequence
+ *               (chunked prefill): results equal one call over the
+ *               concatenated tokens up to rounding.
+ * Source: the report's §4.1.1 (local state and local output per sequence
+ * shard, folded through the carried [B,H,D,D] state) and Fig. 2.
+ */
+int la_prefill(const void *q, const void *k, const void *v, const float *slopes,
+               void *out, float *state,
+               int64_t B, int64_t H, int64_t N, int64_t d, void *stream);
+
+/* Prefill with fp32 activations: same semantics, q, k, v, out are float. */
+int la_prefill_f32(const float *q, const float *k, const float *v, const float *slopes,
+                   float *out, float *state,
+                   int64_t B, int64_t H, int64_t N, int64_t d, void *stream);
+
+/*
+ * One decode step for B*H sequences (one new token each).
+ *   q, k, v     [B,H,d] bf16, read only.
+ *   state       [B,H,d,d] fp32, updated in place: S' = lambda S + k^T v.
+ *   out         [B,H,d] bf16, written: o = q . S'.
+ * The state update happens before the read-out, so the new token attends to
+ * itself, exactly as in prefill; N decode steps equal one prefill of N tokens
+ * up to rounding.  Source: the report's §4.1.1 recurrence; the serving-side
+ * attention step over a carried state (§4.3, Fig. 12).
+ */
+int la_decode_step(const void *q, const void *k, const void *v, const float *slopes,
+                   float *state, void *out,
+                   int64_t B, int64_t H, int64_t d, void *stream);
+
+/* Decode step with fp32 q, k, v, out: same semantics. */
+int la_decode_step_f32(const float *q, const float *k, const float *v, const float *slopes,
+                       float *state, float *out,
+                       int64_t B, int64_t H, int64_t d, void *stream);
+
+/* Static, NUL-terminated description of a status code ("unknown status" for
+ * values outside la_status).  Never NULL; the caller must not free it. */
+const char *la_status_string(int status);
+
+/* ABI version of this header (incremented on incompatible changes). */
+int la_abi_version(void);
+
+#define LA_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIGHTNING_ATTN_H */

@@ -1,0 +1,151 @@
+"""ctypes binding of liblightning_attn.so (argument marshalling only).
+
+Every function here checks dtypes, devices, shapes and contiguity, then passes
+raw device pointers and the current HIP stream to the C ABI declared in
+``include/lightning_attn.h``.  PyTorch only provides device memory and
+streams; all of the layer's arithmetic runs in the library's HIP kernels.
+There is no fallback: if the library is missing or a call fails, an error is
+raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "liblightning_attn.so")
+
+# names and signatures of the C ABI (include/lightning_attn.h)
+_P, _I64, _INT = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+SIGNATURES = {
+    "la_prefill": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], _INT),
+    "la_prefill_f32": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], _INT),
+    "la_decode_step": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], _INT),
+    "la_decode_step_f32": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], _INT),
+    "la_status_string": ([_INT], ctypes.c_char_p),
+    "la_abi_version": ([], _INT),
+}
+ABI_VERSION = 1
+
+_lock = threading.Lock()
+_lib = None
+
+
+class LightningAttnError(RuntimeError):
+    pass
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(path):
+                raise LightningAttnError(
+                    f"{path} is missing: build it with `python -m long_context_layers_amd.build` "
+                    "(there is no CPU fallback)")
+            lib = ctypes.CDLL(path)
+            for name, (args, res) in SIGNATURES.items():
+                fn = getattr(lib, name)
+                fn.argtypes = args
+                fn.restype = res
+            if lib.la_abi_version() != ABI_VERSION:
+                raise LightningAttnError("liblightning_attn.so ABI version mismatch")
+            _lib = lib
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return load_library().la_status_string(code).decode()
+
+
+def _check(code: int, what: str):
+    if code != 0:
+        raise LightningAttnError(f"{what}: {status_string(code)} (status {code})")
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, dev, shape):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: torch.Tensor,
+            state: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Blockwise decayed causal linear attention over N tokens.
+
+    q, k, v: [B,H,N,d] bf16 or fp32 on one GPU; slopes: [H] fp32;
+    state: [B,H,d,d] fp32, IN = initial state, OUT = final state (in place).
+    Returns out [B,H,N,d] (same dtype as q).  Enqueued on the current stream.
+    """
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a [B,H,N,d] tensor")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("prefill runs on a GPU tensor only (no CPU path)")
+    B, H, N, d = q.shape
+    dt = q.dtype
+    if dt not in (torch.bfloat16, torch.float32):
+        raise TypeError("q/k/v must be bfloat16 or float32")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, dt, dev, (B, H, N, d))
+    _need(slopes, "slopes", torch.float32, dev, (H,))
+    _need(state, "state", torch.float32, dev, (B, H, d, d))
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", dt, dev, (B, H, N, d))
+    lib = load_library()
+    fn = lib.la_prefill if dt == torch.bfloat16 else lib.la_prefill_f32
+    with torch.cuda.device(dev):
+        rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), slopes.data_ptr(), out.data_ptr(),
+                state.data_ptr(), B, H, N, d, _stream(dev))
+    _check(rc, "la_prefill" if dt == torch.bfloat16 else "la_prefill_f32")
+    return out
+
+
+def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: torch.Tensor,
+                state: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One recurrent step: state = lambda*state + k^T v (in place); returns q . state.
+
+    q, k, v: [B,H,d] bf16 or fp32; slopes [H] fp32; state [B,H,d,d] fp32.
+    """
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise ValueError("q must be a [B,H,d] tensor")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("decode_step runs on a GPU tensor only (no CPU path)")
+    B, H, d = q.shape
+    dt = q.dtype
+    if dt not in (torch.bfloat16, torch.float32):
+        raise TypeError("q/k/v must be bfloat16 or float32")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, dt, dev, (B, H, d))
+    _need(slopes, "slopes", torch.float32, dev, (H,))
+    _need(state, "state", torch.float32, dev, (B, H, d, d))
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", dt, dev, (B, H, d))
+    lib = load_library()
+    fn = lib.la_decode_step if dt == torch.bfloat16 else lib.la_decode_step_f32
+    with torch.cuda.device(dev):
+        rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), slopes.data_ptr(), state.data_ptr(),
+                out.data_ptr(), B, H, d, _stream(dev))
+    _check(rc, "la_decode_step" if dt == torch.bfloat16 else "la_decode_step_f32")
+    return out

@@ -1,0 +1,120 @@
+// decode.hip — one recurrent decode step per sequence:
+//   S' = lambda S + k^T v   (in place, fp32),   o = q S'
+// (Ling and Ring 2.6 Technical Report, §4.1.1: linear attention as an
+// RNN-style recurrence over a per-(batch, head) D x D state; serving runs it
+// one token per step, §4.3 / Fig. 12.)
+//
+// The step is bound by HBM: every state is read once and written once
+// (2 x 64 KiB per (b, h) at d = 128) while the arithmetic is 4 d^2 flops.
+// One workgroup streams one (b, h) state: thread t owns the 4-column group
+// t % (D/4) on rows t / (D/4) + (256 / (D/4)) m.  All of a thread's rows are
+// loaded up front (dwordx4, non-temporal: a state is touched once per step),
+// updated in registers, written back, and the partial o = q S' sums over
+// rows are reduced across the row groups in LDS (fixed order, no atomics).
+#include "la_internal.h"
+
+namespace la {
+namespace {
+
+constexpr int DT = 256;   // threads per workgroup
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <typename T> __device__ __forceinline__ float load_act(const T *p);
+template <> __device__ __forceinline__ float load_act<uint16_t>(const uint16_t *p) { return bf16_to_f32(*p); }
+template <> __device__ __forceinline__ float load_act<float>(const float *p) { return *p; }
+
+template <typename T> __device__ __forceinline__ void store_act(T *p, float x);
+template <> __device__ __forceinline__ void store_act<uint16_t>(uint16_t *p, float x) {
+    *p = __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+template <> __device__ __forceinline__ void store_act<float>(float *p, float x) { *p = x; }
+
+template <typename T, int D>
+__global__ __launch_bounds__(DT) void decode_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    const float *__restrict__ slopes, float *__restrict__ state, T *__restrict__ out, int64_t H)
+{
+    constexpr int CG = D / 4;         // float4 column groups per row
+    constexpr int RG = DT / CG;       // row groups
+    constexpr int RPT = D / RG;       // rows per thread
+    __shared__ float red[RG][D];
+    __shared__ float qk[2][D];
+
+    const int tid = threadIdx.x;
+    const int64_t bh = blockIdx.x;
+    const float lam = decay_pow(slopes[bh % H], 1);
+    const int cg = tid % CG, rg = tid / CG;
+
+    f32x4 *S = reinterpret_cast<f32x4 *>(state + bh * D * D);
+    f32x4 s[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) s[m] = __builtin_nontemporal_load(&S[(rg + RG * m) * CG + cg]);
+
+    if (tid < D) {
+        qk[0][tid] = load_act<T>(q + bh * D + tid);
+        qk[1][tid] = load_act<T>(k + bh * D + tid);
+    }
+    const T *vb = v + bh * D + 4 * cg;
+    const float v0 = load_act<T>(vb), v1 = load_act<T>(vb + 1), v2 = load_act<T>(vb + 2),
+                v3 = load_act<T>(vb + 3);
+    __syncthreads();
+
+    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int i = rg + RG * m;
+        const float ki = qk[1][i], qi = qk[0][i];
+        f32x4 x = s[m];
+        x.x = fmaf(lam, x.x, ki * v0);
+        x.y = fmaf(lam, x.y, ki * v1);
+        x.z = fmaf(lam, x.z, ki * v2);
+        x.w = fmaf(lam, x.w, ki * v3);
+        __builtin_nontemporal_store(x, &S[i * CG + cg]);
+        o0 = fmaf(qi, x.x, o0);
+        o1 = fmaf(qi, x.y, o1);
+        o2 = fmaf(qi, x.z, o2);
+        o3 = fmaf(qi, x.w, o3);
+    }
+    red[rg][4 * cg + 0] = o0;
+    red[rg][4 * cg + 1] = o1;
+    red[rg][4 * cg + 2] = o2;
+    red[rg][4 * cg + 3] = o3;
+    __syncthreads();
+    if (tid < D) {
+        float acc = 0.f;
+#pragma unroll
+        for (int g = 0; g < RG; ++g) acc += red[g][tid];
+        store_act<T>(out + bh * D + tid, acc);
+    }
+}
+
+template <typename T>
+hipError_t launch_decode(const T *q, const T *k, const T *v, const float *slopes, float *state,
+                         T *out, int64_t B, int64_t H, int d, hipStream_t stream)
+{
+    const dim3 grid((unsigned)(B * H)), block(DT);
+    void *args[] = {(void *)&q, (void *)&k, (void *)&v, (void *)&slopes,
+                    (void *)&state, (void *)&out, (void *)&H};
+    const void *fn = d == 64 ? (const void *)decode_kernel<T, 64>
+                             : (const void *)decode_kernel<T, 128>;
+    return hipLaunchKernel(fn, grid, block, args, 0, stream);
+}
+
+}  // namespace
+
+hipError_t launch_decode_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                              const float *slopes, float *state, uint16_t *out,
+                              int64_t B, int64_t H, int d, hipStream_t stream)
+{
+    return launch_decode<uint16_t>(q, k, v, slopes, state, out, B, H, d, stream);
+}
+
+hipError_t launch_decode_f32(const float *q, const float *k, const float *v,
+                             const float *slopes, float *state, float *out,
+                             int64_t B, int64_t H, int d, hipStream_t stream)
+{
+    return launch_decode<float>(q, k, v, slopes, state, out, B, H, d, stream);
+}
+
+}  // namespace la

@@ -1,0 +1,138 @@
+// la_api.hip — the C ABI (include/lightning_attn.h): host-side argument
+// checks, then one kernel launch on the caller's stream.  No allocation, no
+// synchronisation, no global state.
+#include "lightning_attn.h"
+#include "la_internal.h"
+
+#include <stdint.h>
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// [a, a + na) and [b, b + nb) overlap (byte ranges)
+bool overlap(const void *a, uint64_t na, const void *b, uint64_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return na && nb && x < y + nb && y < x + na;
+}
+
+// x * y without int64 overflow (both >= 0); false on overflow
+bool mul_ok(int64_t x, int64_t y, int64_t *r) {
+    if (x < 0 || y < 0) return false;
+    if (x != 0 && y > INT64_MAX / x) return false;
+    *r = x * y;
+    return true;
+}
+
+// shared checks for prefill; elem = bytes per activation element
+int check_prefill(const void *q, const void *k, const void *v, const float *slopes,
+                  const void *out, const float *state, int64_t B, int64_t H, int64_t N,
+                  int64_t d, int64_t elem)
+{
+    // with N == 0 the activations are empty and may be null (nothing is read)
+    if (N > 0 && (!q || !k || !v || !out)) return LA_ERR_INVALID_ARG;
+    if (!slopes || !state) return LA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || N < 0) return LA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
+    int64_t bh, act, act_bytes, st, st_bytes;
+    if (!mul_ok(B, H, &bh) || !mul_ok(bh, N, &act) || !mul_ok(act, d, &act) ||
+        !mul_ok(act, elem, &act_bytes) || !mul_ok(bh, d * d, &st) || !mul_ok(st, 4, &st_bytes))
+        return LA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        !aligned(state, 16) || !aligned(slopes, 4))
+        return LA_ERR_INVALID_ARG;
+    if (overlap(out, act_bytes, q, act_bytes) || overlap(out, act_bytes, k, act_bytes) ||
+        overlap(out, act_bytes, v, act_bytes) || overlap(out, act_bytes, state, st_bytes))
+        return LA_ERR_INVALID_ARG;
+    return LA_OK;
+}
+
+int check_decode(const void *q, const void *k, const void *v, const float *slopes,
+                 const float *state, const void *out, int64_t B, int64_t H, int64_t d,
+                 int64_t elem)
+{
+    if (!q || !k || !v || !slopes || !out || !state) return LA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1) return LA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
+    int64_t bh, act, act_bytes, st, st_bytes;
+    if (!mul_ok(B, H, &bh) || !mul_ok(bh, d, &act) || !mul_ok(act, elem, &act_bytes) ||
+        !mul_ok(bh, d * d, &st) || !mul_ok(st, 4, &st_bytes))
+        return LA_ERR_INVALID_ARG;
+    if (!aligned(q, elem) || !aligned(k, elem) || !aligned(v, elem) || !aligned(out, elem) ||
+        !aligned(state, 16) || !aligned(slopes, 4))
+        return LA_ERR_INVALID_ARG;
+    if (overlap(out, act_bytes, q, act_bytes) || overlap(out, act_bytes, k, act_bytes) ||
+        overlap(out, act_bytes, v, act_bytes) || overlap(out, act_bytes, state, st_bytes))
+        return LA_ERR_INVALID_ARG;
+    if (bh > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+    return LA_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? LA_OK : LA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int la_prefill(const void *q, const void *k, const void *v, const float *slopes, void *out,
+               float *state, int64_t B, int64_t H, int64_t N, int64_t d, void *stream)
+{
+    const int rc = check_prefill(q, k, v, slopes, out, state, B, H, N, d, 2);
+    if (rc != LA_OK) return rc;
+    if (la::prefill_bf16_grid(B, H, (int)d) > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+    if (N == 0) return LA_OK;
+    return hip_status(la::launch_prefill_bf16(
+        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+        static_cast<const uint16_t *>(v), slopes, static_cast<uint16_t *>(out), state, B, H, N,
+        (int)d, static_cast<hipStream_t>(stream)));
+}
+
+int la_prefill_f32(const float *q, const float *k, const float *v, const float *slopes,
+                   float *out, float *state, int64_t B, int64_t H, int64_t N, int64_t d,
+                   void *stream)
+{
+    const int rc = check_prefill(q, k, v, slopes, out, state, B, H, N, d, 4);
+    if (rc != LA_OK) return rc;
+    if (la::prefill_f32_grid(B, H, (int)d) > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+    if (N == 0) return LA_OK;
+    return hip_status(la::launch_prefill_f32(q, k, v, slopes, out, state, B, H, N, (int)d,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int la_decode_step(const void *q, const void *k, const void *v, const float *slopes,
+                   float *state, void *out, int64_t B, int64_t H, int64_t d, void *stream)
+{
+    const int rc = check_decode(q, k, v, slopes, state, out, B, H, d, 2);
+    if (rc != LA_OK) return rc;
+    return hip_status(la::launch_decode_bf16(
+        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+        static_cast<const uint16_t *>(v), slopes, state, static_cast<uint16_t *>(out), B, H,
+        (int)d, static_cast<hipStream_t>(stream)));
+}
+
+int la_decode_step_f32(const float *q, const float *k, const float *v, const float *slopes,
+                       float *state, float *out, int64_t B, int64_t H, int64_t d, void *stream)
+{
+    const int rc = check_decode(q, k, v, slopes, state, out, B, H, d, 4);
+    if (rc != LA_OK) return rc;
+    return hip_status(la::launch_decode_f32(q, k, v, slopes, state, out, B, H, (int)d,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+const char *la_status_string(int status)
+{
+    switch (status) {
+        case LA_OK: return "LA_OK: success";
+        case LA_ERR_INVALID_ARG:
+            return "LA_ERR_INVALID_ARG: null or misaligned pointer, negative or overflowing "
+                   "size, or an output overlapping an input";
+        case LA_ERR_UNSUPPORTED:
+            return "LA_ERR_UNSUPPORTED: head dimension not in {64, 128} or grid too large";
+        case LA_ERR_HIP: return "LA_ERR_HIP: the kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+int la_abi_version(void) { return LA_ABI_VERSION; }
+
+}  // extern "C"

@@ -102,13 +102,18 @@ def prefill(q, k, v, slopes, state_init=None, want_out: bool = True):
     return out, st
 
 
-def decode_step(q, k, v, slopes, state):
-    """One decode step: q, k, v [B,H,d]; state [B,H,d,d] (not modified).
+def decode_step(q, k, v, slopes, state, inplace: bool = False):
+    """One decode step: q, k, v [B,H,d]; state [B,H,d,d].
 
-    Returns (out [B,H,d], new_state)."""
+    Returns (out [B,H,d], new_state).  The state is copied unless ``inplace``
+    is set and it is already a contiguous fp64 array (then it is updated)."""
     q, k, v, s = _f64(q), _f64(k), _f64(v), _f64(slopes)
     B, H, d = q.shape
-    st = _f64(state).copy()
+    if inplace and isinstance(state, np.ndarray) and state.dtype == np.float64 \
+            and state.flags.c_contiguous:
+        st = state
+    else:
+        st = _f64(state).copy()
     out = np.zeros((B, H, d))
     r = _load().la_oracle_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(s), _ptr(st),
                                       _ptr(out), B, H, d)

@@ -7,7 +7,7 @@
 // in order inside one workgroup).  For one (b, h), the block of c tokens at
 // t0, local indices a, b < c and lambda = exp(-slope_h):
 //   P^T[b][a] = lambda^(a-b) (k_b . q_a)  (b <= a), else 0      [intra scores]
-//   O^T       = diag-scaled S^T Q^T  (column a times lambda^(a+1))  [inter]
+//   O^T       = S^T Q^T with column a scaled by lambda^(a+1)      [inter]
 //             + V^T P^T                                         [intra]
 //   S         = lambda^c S + K^T diag(lambda^(c-1-b)) V          [state scan]
 // Every product is a bf16 x bf16 -> fp32 MFMA (v_mfma_f32_16x16x32_bf16).
@@ -22,163 +22,157 @@
 // four workgroups of a head are placed on one XCD so Q and K come from HBM
 // once and from that XCD's L2 for the other three.
 //
-// Wave roles inside a workgroup (4 waves, 16x16 output tiles):
+// Data movement (wave-specialised).  Waves 4..7 are producers: they only
+// load Q, K and the workgroup's 64 x 32 slice of V with 16-byte buffer loads,
+// four blocks ahead of use (four register sets), and write them into one of
+// two LDS buffers one block ahead (plus a decay-weighted copy of V).  Waves
+// 0..3 are consumers: they only read LDS, run the MFMAs and store outputs.
+// Keeping global loads and stores in different waves matters on gfx9: one
+// counter (vmcnt) tracks both, and a wave with both kinds in flight must
+// drain all of them before it can use any loaded register.  Contractions
+// over tokens (the state update K^T V and the intra output V^T P^T) need the
+// token index contiguous per lane; they read K and V from their token-major
+// LDS tiles with ds_read_b64_tr_b16 (gfx950 transposing LDS read) instead of
+// keeping transposed copies.  K's 16-byte chunks are XOR-swizzled by row so
+// that both its plain reads (8 rows, one chunk) and its transposed reads
+// (4 rows, one chunk pair) hit distinct LDS banks.
+//
+// Consumer wave roles (4 waves, 16x16 output tiles):
 //   scores:  the 10 causal 16x16 tiles of P^T, 2-3 per wave;
 //   output:  wave w owns tokens 16w..16w+15 of the block (both 16-col tiles);
-//   state:   wave w owns rows (D/4) w .. of the 128 x 32 state slice.
-// Operand layouts for v_mfma_f32_16x16x32_bf16 (lane l, l16 = l % 16,
+//   state:   wave w owns rows (D/4) w .. of the D x 32 state slice.
+// Operand layouts of v_mfma_f32_16x16x32_bf16 (lane l, l16 = l % 16,
 // lg = l / 16): A row l16, k = 8 lg .. 8 lg + 7; B column l16, same k;
-// result rows 4 lg + r (r = 0..3), column l16.  A and B are read with the
-// same k pattern, so any consistent permutation of k inside an instruction
-// leaves the products unchanged.
+// result rows 4 lg + r (r = 0..3), column l16.
+// ds_read_b64_tr_b16: within each 16-lane group, lane l16 supplies the
+// address of a 4-element chunk; lane l16 receives element l16 % 4 of chunks
+// 4e + l16 / 4, e = 0..3.  So if lane l16 points at row r0 + l16/4, column
+// c0 + 4 (l16 % 4) of a row-major tile, it receives column c0 + l16 of rows
+// r0 .. r0 + 3: a k-contiguous MFMA operand for a contraction over rows.
 #include "la_internal.h"
 
 namespace la {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int PC = 64;        // tokens per block
 constexpr int PJ = 32;        // state / output columns per workgroup
-constexpr int PT = 256;       // threads per workgroup (4 waves)
-constexpr int PAD = 8;        // bf16 elements of row padding in LDS
+constexpr int PT = 256;       // threads per role (4 consumer + 4 producer waves)
+constexpr int NSET = 4;       // producer register sets (blocks in flight)
+constexpr int QPAD = 8;       // bf16 padding of Q and state-copy rows
+constexpr int VP = 48;        // V row pitch (96 B: transposed reads conflict-free)
+constexpr int PP = PC + 8;    // score row pitch
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int W>
-__device__ __forceinline__ const bf16x8 &frag(const uint16_t (*X)[W], int row, int col) {
-    return *reinterpret_cast<const bf16x8 *>(&X[row][col]);
+__device__ __forceinline__ bf16x8 ld8(const uint16_t *p) {
+    return *reinterpret_cast<const bf16x8 *>(p);
 }
 
-// 32-bit word from the low (sel 0) or high (sel 1) halves of two words:
-// result = {x.half, y.half} with x in bits 0..15.
-__device__ __forceinline__ uint32_t pick_lo(uint32_t x, uint32_t y) {
-    return __builtin_amdgcn_perm(y, x, 0x05040100u);
+// two transposing reads -> one 8-element operand (k = 0..3 from p0, 4..7 from p1)
+__device__ __forceinline__ bf16x8 ldtr8(const uint16_t *p0, const uint16_t *p1) {
+    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p0);
+    const s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p1);
+    const s16x8 c = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, c);
 }
-__device__ __forceinline__ uint32_t pick_hi(uint32_t x, uint32_t y) {
-    return __builtin_amdgcn_perm(y, x, 0x07060302u);
-}
+
+// 16-byte-chunk swizzle of K rows (see the header comment)
+__device__ __forceinline__ int kswz(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
 
 template <int D>
 struct alignas(16) Smem {
-    uint16_t Q[PC][D + PAD];     // Q block, token-major
-    uint16_t K[PC][D + PAD];     // K block, token-major
-    uint16_t KT[D][PC + PAD];    // K block, feature-major (for the state update)
-    uint16_t VT[PJ][PC + PAD];   // V slice, column-major (intra output)
-    uint16_t VW[PJ][PC + PAD];   // V slice times lambda^(c-1-b), column-major
-    uint16_t P[PC][PC + PAD];    // decayed causal scores P[a][b]
-    uint16_t ST[PJ][D + PAD];    // bf16 copy of the state slice, transposed
+    uint16_t Q[2][PC][D + QPAD];     // Q blocks, token-major
+    uint16_t K[2][PC][D];            // K blocks, token-major, chunk-swizzled
+    uint16_t V[2][PC][VP];           // V slices, token-major
+    uint16_t VW[2][PC][VP];          // V slices times lambda^(c-1-b)
+    uint16_t P[PC][PP];              // decayed causal scores P[a][b]
+    uint16_t ST[PJ][D + QPAD];       // bf16 copy of the state slice, transposed
 };
 
-// global -> register staging of one block (prefetched one block ahead)
+// one block's share of this thread, in registers
 template <int D>
-struct Stage {
-    static constexpr int NQ = PC * D / 8 / PT;            // 16-byte chunks of Q per thread
-    static constexpr int NKTASK = (PC / 8) * (D / 4);     // 8x4 tiles of K
-    static constexpr int NVTASK = (PC / 4) * (PJ / 4);    // 4x4 tiles of the V slice
-    uint4 q[NQ];
-    uint2 k[8];
-    uint2 v[4];
+struct Regs {
+    static constexpr int NQ = PC * D / 8 / PT;   // 16-byte chunks of Q (and of K)
+    uint4 q[NQ], k[NQ], v;
 };
 
 template <int D>
-__device__ __forceinline__ void stage_load(Stage<D> &st, const uint16_t *qb, const uint16_t *kb,
-                                           const uint16_t *vb, int64_t t0, int64_t N, int j0,
-                                           int tid)
-{
-#pragma unroll
-    for (int u = 0; u < Stage<D>::NQ; ++u) {
-        const int ch = tid + PT * u;
-        const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-        st.q[u] = (t0 + row < N) ? *reinterpret_cast<const uint4 *>(qb + (t0 + row) * D + col)
-                                 : make_uint4(0, 0, 0, 0);
-    }
-    if (tid < Stage<D>::NKTASK) {
-        const int rg = tid / (D / 4), cg = tid % (D / 4);
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int64_t t = t0 + 8 * rg + r;
-            st.k[r] = (t < N) ? *reinterpret_cast<const uint2 *>(kb + t * D + 4 * cg)
-                              : make_uint2(0, 0);
-        }
-    }
-    const int vt = PT - 1 - tid;
-    if (vt < Stage<D>::NVTASK) {
-        const int rg = vt / (PJ / 4), cg = vt % (PJ / 4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t t = t0 + 4 * rg + r;
-            st.v[r] = (t < N) ? *reinterpret_cast<const uint2 *>(vb + t * D + j0 + 4 * cg)
-                              : make_uint2(0, 0);
-        }
-    }
+struct Addr {                        // per-thread byte offsets inside a block
+    uint32_t qk[Regs<D>::NQ];
+    uint32_t v;
+};
+
+// Buffer resource over rows [t0, t0 + 64) of a (b, h) slice: 16-byte loads
+// at per-thread offsets, rows past N read as zero (hardware range check on
+// the descriptor's byte count), stores past N are dropped.
+constexpr uint32_t RSRC_WORD3 = 0x00020000u;   // raw buffer, 32-bit data format
+
+// tokens of the block starting at t0 (0 past the end)
+__device__ __forceinline__ int block_len(int64_t t0, int64_t N) {
+    return (int)max((int64_t)0, min((int64_t)PC, N - t0));
 }
 
-// registers -> LDS, with the K transpose and the decay-weighted V copy.
-// wv[r] = lambda^(c-1-b) for this thread's 4 tokens b (0 beyond the block).
 template <int D>
-__device__ __forceinline__ void stage_store(const Stage<D> &st, Smem<D> &sm, int tid,
-                                            const float (&wv)[4])
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint16_t *base, int64_t t0,
+                                                              int64_t N)
+{
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(base + t0 * D), (short)0,
+                                             block_len(t0, N) * D * 2, RSRC_WORD3);
+}
+
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+    return make_uint4(x[0], x[1], x[2], x[3]);
+}
+
+template <int D>
+__device__ __forceinline__ void load_block(Regs<D> &r, const uint16_t *qh, const uint16_t *kh,
+                                           const uint16_t *vh, int64_t t0, int64_t N,
+                                           const Addr<D> &ad)
+{
+    const __amdgpu_buffer_rsrc_t rq = block_rsrc<D>(qh, t0, N);
+    const __amdgpu_buffer_rsrc_t rk = block_rsrc<D>(kh, t0, N);
+    const __amdgpu_buffer_rsrc_t rv = block_rsrc<D>(vh, t0, N);
+#pragma unroll
+    for (int u = 0; u < Regs<D>::NQ; ++u) {
+        r.q[u] = bload16(rq, ad.qk[u]);
+        r.k[u] = bload16(rk, ad.qk[u]);
+    }
+    r.v = bload16(rv, ad.v);
+}
+
+__device__ __forceinline__ uint32_t scale_pair(uint32_t x, float w) {
+    return pack_bf16x2(bf16_to_f32(x & 0xffffu) * w, bf16_to_f32(x >> 16) * w);
+}
+
+// registers -> LDS buffer BUF; wv = lambda^(c-1-b) for this thread's token b
+template <int D, int BUF>
+__device__ __forceinline__ void store_block(const Regs<D> &r, Smem<D> &sm, int tid, float wv)
 {
 #pragma unroll
-    for (int u = 0; u < Stage<D>::NQ; ++u) {
+    for (int u = 0; u < Regs<D>::NQ; ++u) {
         const int ch = tid + PT * u;
-        const int row = ch / (D / 8), col = (ch % (D / 8)) * 8;
-        *reinterpret_cast<uint4 *>(&sm.Q[row][col]) = st.q[u];
+        const int row = ch / (D / 8), c8 = ch % (D / 8);
+        *reinterpret_cast<uint4 *>(&sm.Q[BUF][row][c8 * 8]) = r.q[u];
+        *reinterpret_cast<uint4 *>(&sm.K[BUF][row][(c8 ^ kswz(row)) * 8]) = r.k[u];
     }
-    if (tid < Stage<D>::NKTASK) {
-        const int rg = tid / (D / 4), cg = tid % (D / 4);
-#pragma unroll
-        for (int r = 0; r < 8; ++r)
-            *reinterpret_cast<uint2 *>(&sm.K[8 * rg + r][4 * cg]) = st.k[r];
-        // column 4cg+e of rows 8rg..8rg+7 -> KT[4cg+e][8rg..8rg+7]
-        uint4 c0, c1, c2, c3;
-        c0.x = pick_lo(st.k[0].x, st.k[1].x); c0.y = pick_lo(st.k[2].x, st.k[3].x);
-        c0.z = pick_lo(st.k[4].x, st.k[5].x); c0.w = pick_lo(st.k[6].x, st.k[7].x);
-        c1.x = pick_hi(st.k[0].x, st.k[1].x); c1.y = pick_hi(st.k[2].x, st.k[3].x);
-        c1.z = pick_hi(st.k[4].x, st.k[5].x); c1.w = pick_hi(st.k[6].x, st.k[7].x);
-        c2.x = pick_lo(st.k[0].y, st.k[1].y); c2.y = pick_lo(st.k[2].y, st.k[3].y);
-        c2.z = pick_lo(st.k[4].y, st.k[5].y); c2.w = pick_lo(st.k[6].y, st.k[7].y);
-        c3.x = pick_hi(st.k[0].y, st.k[1].y); c3.y = pick_hi(st.k[2].y, st.k[3].y);
-        c3.z = pick_hi(st.k[4].y, st.k[5].y); c3.w = pick_hi(st.k[6].y, st.k[7].y);
-        *reinterpret_cast<uint4 *>(&sm.KT[4 * cg + 0][8 * rg]) = c0;
-        *reinterpret_cast<uint4 *>(&sm.KT[4 * cg + 1][8 * rg]) = c1;
-        *reinterpret_cast<uint4 *>(&sm.KT[4 * cg + 2][8 * rg]) = c2;
-        *reinterpret_cast<uint4 *>(&sm.KT[4 * cg + 3][8 * rg]) = c3;
-    }
-    const int vt = PT - 1 - tid;
-    if (vt < Stage<D>::NVTASK) {
-        const int rg = vt / (PJ / 4), cg = vt % (PJ / 4);
-        // V^T: column 4cg+e of rows 4rg..4rg+3
-        uint2 t0, t1, t2, t3;
-        t0.x = pick_lo(st.v[0].x, st.v[1].x); t0.y = pick_lo(st.v[2].x, st.v[3].x);
-        t1.x = pick_hi(st.v[0].x, st.v[1].x); t1.y = pick_hi(st.v[2].x, st.v[3].x);
-        t2.x = pick_lo(st.v[0].y, st.v[1].y); t2.y = pick_lo(st.v[2].y, st.v[3].y);
-        t3.x = pick_hi(st.v[0].y, st.v[1].y); t3.y = pick_hi(st.v[2].y, st.v[3].y);
-        *reinterpret_cast<uint2 *>(&sm.VT[4 * cg + 0][4 * rg]) = t0;
-        *reinterpret_cast<uint2 *>(&sm.VT[4 * cg + 1][4 * rg]) = t1;
-        *reinterpret_cast<uint2 *>(&sm.VT[4 * cg + 2][4 * rg]) = t2;
-        *reinterpret_cast<uint2 *>(&sm.VT[4 * cg + 3][4 * rg]) = t3;
-        // decay-weighted copy: element (token r, column e) times wv[r]
-        float f[4][4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            f[r][0] = bf16_to_f32(st.v[r].x & 0xffffu) * wv[r];
-            f[r][1] = bf16_to_f32(st.v[r].x >> 16) * wv[r];
-            f[r][2] = bf16_to_f32(st.v[r].y & 0xffffu) * wv[r];
-            f[r][3] = bf16_to_f32(st.v[r].y >> 16) * wv[r];
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            uint2 w;
-            w.x = pack_bf16x2(f[0][e], f[1][e]);
-            w.y = pack_bf16x2(f[2][e], f[3][e]);
-            *reinterpret_cast<uint2 *>(&sm.VW[4 * cg + e][4 * rg]) = w;
-        }
-    }
+    const int vrow = tid / 4, vc = (tid % 4) * 8;
+    *reinterpret_cast<uint4 *>(&sm.V[BUF][vrow][vc]) = r.v;
+    uint4 w;
+    w.x = scale_pair(r.v.x, wv);
+    w.y = scale_pair(r.v.y, wv);
+    w.z = scale_pair(r.v.z, wv);
+    w.w = scale_pair(r.v.w, wv);
+    *reinterpret_cast<uint4 *>(&sm.VW[BUF][vrow][vc]) = w;
 }
 
 // Score tiles (bt, at) of P^T owned by wave W: the 10 causal 16x16 tiles of
@@ -191,18 +185,19 @@ template <> struct ScoreTiles<3> { static constexpr int n = 2; static constexpr 
 
 // dec[dl][r]: decay of score element r of a tile whose token-tile offset is
 // dl = at - bt, for this lane: lambda^(16 dl + l16 - 4 lg - r), 0 if negative.
-template <int D, int W>
+template <int D, int W, int BUF>
 __device__ __forceinline__ void score_tiles(Smem<D> &sm, const float (&dec)[4][4], int l16, int lg)
 {
     using T = ScoreTiles<W>;
+    const int ks0 = kswz(l16);
 #pragma unroll
     for (int u = 0; u < T::n; ++u) {
         const int bt = T::bt[u], at = T::at[u];
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < D / 32; ++ks)
-            acc = mfma(frag(sm.K, 16 * bt + l16, 32 * ks + 8 * lg),
-                       frag(sm.Q, 16 * at + l16, 32 * ks + 8 * lg), acc);
+            acc = mfma(ld8(&sm.K[BUF][16 * bt + l16][((4 * ks + lg) ^ ks0) * 8]),
+                       ld8(&sm.Q[BUF][16 * at + l16][32 * ks + 8 * lg]), acc);
         const int dl = at - bt;
         uint2 p;
         p.x = pack_bf16x2(acc[0] * dec[dl][0], acc[1] * dec[dl][1]);
@@ -212,48 +207,182 @@ __device__ __forceinline__ void score_tiles(Smem<D> &sm, const float (&dec)[4][4
 }
 
 template <int D>
-__global__ __launch_bounds__(PT) void prefill_bf16_kernel(
-    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-    const uint16_t *__restrict__ v, const float *__restrict__ slopes,
-    uint16_t *__restrict__ out, float *__restrict__ state, int64_t H, int64_t N)
-{
-    constexpr int NJ = D / PJ;            // workgroups per head
-    constexpr int ITW = D / 64;           // 16-row state tiles per wave
-    __shared__ Smem<D> sm;
-
-    const int tid = threadIdx.x;
-    const int w = __builtin_amdgcn_readfirstlane(tid / 64);
-    const int l = tid % 64, l16 = l % 16, lg = l / 16;
-
-    // XCD-aware placement: workgroup i runs on XCD i % 8; give the NJ
-    // workgroups of one head consecutive logical ids on the same XCD.
-    const int64_t nwg = gridDim.x;
-    int64_t lid = blockIdx.x;
-    if (nwg % 8 == 0) lid = (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8;
-    const int64_t bh = lid / NJ;
-    const int j0 = (int)(lid % NJ) * PJ;
-    const float s = slopes[bh % H];
-
-    const uint16_t *qb = q + bh * N * D, *kb = k + bh * N * D, *vb = v + bh * N * D;
-    uint16_t *ob = out + bh * N * D;
-    float *St = state + bh * D * D;
-
-    // per-lane decay constants
+struct Ctx {                          // per-thread constants of one workgroup
+    const uint16_t *qh, *kh, *vh;     // this (b, h) slice
+    const uint16_t *oh;
+    int64_t N, nblk;                  // nblk: blocks processed (a multiple of NSET)
+    float s, full_decay, out_scale, wfull;
     float dec[4][4];
+    int w, l16, lg, j0;
+};
+
+// ---- producer waves (4..7): global -> registers -> LDS --------------------
+
+// stage block blk (register set r) into LDS buffer BUF
+template <int D, int BUF>
+__device__ __forceinline__ void produce_store(const Ctx<D> &cx, Smem<D> &sm, const Regs<D> &r,
+                                              int64_t blk, int p)
+{
+    const int c = block_len(blk * PC, cx.N);
+    const int b = p / 4;
+    const float wv = c == PC ? cx.wfull : (b < c ? decay_pow(cx.s, c - 1 - b) : 0.0f);
+    store_block<D, BUF>(r, sm, p, wv);
+}
+
+// One producer step per block blk: after the block's first barrier, stage
+// block blk+1 (register set SET) into the other LDS buffer, then reload SET
+// with block blk+1+NSET.  Loads past the end return zeros without touching
+// memory, so nothing here is conditional (exact vmcnt waits).
+template <int D, int SET>
+__device__ __forceinline__ void produce_step(const Ctx<D> &cx, Smem<D> &sm, Regs<D> (&rs)[NSET],
+                                             const Addr<D> &ad, int64_t blk, int p)
+{
+    __syncthreads();                                   // B1 of block blk
+    if (SET % 2 == 1) produce_store<D, 1>(cx, sm, rs[SET], blk + 1, p);   // blk even -> buffer 1
+    else              produce_store<D, 0>(cx, sm, rs[SET], blk + 1, p);
+    load_block<D>(rs[SET], cx.qh, cx.kh, cx.vh, (blk + 1 + NSET) * PC, cx.N, ad);
+    __syncthreads();                                   // B2 of block blk
+}
+
+template <int D>
+__device__ void producer(const Ctx<D> &cx, Smem<D> &sm, int p)
+{
+    Addr<D> ad;
+#pragma unroll
+    for (int u = 0; u < Regs<D>::NQ; ++u) {
+        const int ch = p + PT * u;
+        ad.qk[u] = (uint32_t)(((ch / (D / 8)) * D + (ch % (D / 8)) * 8) * 2);
+    }
+    ad.v = (uint32_t)(((p / 4) * D + cx.j0 + (p % 4) * 8) * 2);
+
+    Regs<D> rs[NSET];                                   // set i holds block i (mod NSET)
+#pragma unroll
+    for (int i = 0; i < NSET; ++i) load_block<D>(rs[i], cx.qh, cx.kh, cx.vh, i * PC, cx.N, ad);
+    produce_store<D, 0>(cx, sm, rs[0], 0, p);
+    load_block<D>(rs[0], cx.qh, cx.kh, cx.vh, NSET * PC, cx.N, ad);
+
+    // block blk stages block blk+1 from set (blk+1) % NSET into buffer (blk+1) % 2
+    for (int64_t blk = 0; blk < cx.nblk; blk += NSET) {
+        produce_step<D, 1>(cx, sm, rs, ad, blk + 0, p);
+        produce_step<D, 2>(cx, sm, rs, ad, blk + 1, p);
+        produce_step<D, 3>(cx, sm, rs, ad, blk + 2, p);
+        produce_step<D, 0>(cx, sm, rs, ad, blk + 3, p);
+    }
+}
+
+// ---- consumer waves (0..3): scores, outputs, state scan ---------------------
+
+// one 64-token block held in LDS buffer BUF
+template <int D, int BUF>
+__device__ __forceinline__ void consume_step(const Ctx<D> &cx, Smem<D> &sm, int64_t blk,
+                                             f32x4 (&sacc)[D / 64][2])
+{
+    constexpr int ITW = D / 64;
+    const int w = cx.w, l16 = cx.l16, lg = cx.lg;
+    const int64_t t0 = blk * PC;
+    const int c = block_len(t0, cx.N);
+
+    __syncthreads();          // B1: buffer BUF staged; previous block fully consumed
+
+    // intra-block scores
+    switch (w) {
+        case 0: score_tiles<D, 0, BUF>(sm, cx.dec, l16, lg); break;
+        case 1: score_tiles<D, 1, BUF>(sm, cx.dec, l16, lg); break;
+        case 2: score_tiles<D, 2, BUF>(sm, cx.dec, l16, lg); break;
+        default: score_tiles<D, 3, BUF>(sm, cx.dec, l16, lg); break;
+    }
+    // inter-block output from the carried state: O^T = S^T Q^T, column a
+    // scaled by lambda^(a+1); tokens 16w..16w+15
+    f32x4 oacc[2];
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt) {
+        oacc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < D / 32; ++ks)
+            oacc[jt] = mfma(ld8(&sm.ST[16 * jt + l16][32 * ks + 8 * lg]),
+                            ld8(&sm.Q[BUF][16 * w + l16][32 * ks + 8 * lg]), oacc[jt]);
+        oacc[jt] *= cx.out_scale;
+    }
+    // decayed state scan: S = lambda^c S + K^T (lambda^(c-1-b) V)
+    const float sdec = (c == PC) ? cx.full_decay : decay_pow(cx.s, c);   // 1 for an empty block
+    const int trow = l16 >> 2;                 // row within a 4-row transposed read
+    const int tcol = 4 * (l16 & 3);            // column offset within a 16-column tile
+#pragma unroll
+    for (int u = 0; u < ITW; ++u) {
+        const int it = w * ITW + u;
+        bf16x8 ka[PC / 32];
+#pragma unroll
+        for (int ks = 0; ks < PC / 32; ++ks) {
+            const int r0 = 32 * ks + 8 * lg + trow;
+            const int ch = 2 * it + ((l16 & 3) >> 1), sub = 4 * (l16 & 1);
+            ka[ks] = ldtr8(&sm.K[BUF][r0][((ch ^ kswz(r0)) * 8) + sub],
+                           &sm.K[BUF][r0 + 4][((ch ^ kswz(r0 + 4)) * 8) + sub]);
+        }
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+            sacc[u][jt] *= sdec;
+#pragma unroll
+            for (int ks = 0; ks < PC / 32; ++ks) {
+                const int r0 = 32 * ks + 8 * lg + trow;
+                sacc[u][jt] = mfma(ka[ks],
+                                   ldtr8(&sm.VW[BUF][r0][16 * jt + tcol],
+                                         &sm.VW[BUF][r0 + 4][16 * jt + tcol]),
+                                   sacc[u][jt]);
+            }
+        }
+    }
+    __syncthreads();          // B2: scores visible; reads of the old state copy done
+
+    // intra-block output: O^T += V^T P^T over tokens b < 16(w+1)
+#pragma unroll
+    for (int ks = 0; ks < PC / 32; ++ks) {
+        if (ks > w / 2) break;
+        const int r0 = 32 * ks + 8 * lg + trow;
+        const bf16x8 pb = ld8(&sm.P[16 * w + l16][32 * ks + 8 * lg]);
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+            oacc[jt] = mfma(ldtr8(&sm.V[BUF][r0][16 * jt + tcol], &sm.V[BUF][r0 + 4][16 * jt + tcol]),
+                            pb, oacc[jt]);
+    }
+    {   // rows past N are dropped by the descriptor's range check
+        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+        const __amdgpu_buffer_rsrc_t ro = block_rsrc<D>(cx.oh, t0, cx.N);
+        const int a = 16 * w + l16;
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+            u32x2 o;
+            o[0] = pack_bf16x2(oacc[jt][0], oacc[jt][1]);
+            o[1] = pack_bf16x2(oacc[jt][2], oacc[jt][3]);
+            __builtin_amdgcn_raw_buffer_store_b64(o, ro, (a * D + cx.j0 + 16 * jt + 4 * lg) * 2, 0, 0);
+        }
+    }
+    // bf16 copy of the new state for the next block's inter term
+#pragma unroll
+    for (int u = 0; u < ITW; ++u)
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+            const int it = w * ITW + u;
+            uint2 p;
+            p.x = pack_bf16x2(sacc[u][jt][0], sacc[u][jt][1]);
+            p.y = pack_bf16x2(sacc[u][jt][2], sacc[u][jt][3]);
+            *reinterpret_cast<uint2 *>(&sm.ST[16 * jt + l16][16 * it + 4 * lg]) = p;
+        }
+}
+
+template <int D>
+__device__ void consumer(Ctx<D> &cx, Smem<D> &sm, float *St, int tid)
+{
+    constexpr int ITW = D / 64;
+    const int w = cx.w, l16 = cx.l16, lg = cx.lg;
+    // per-lane decay constants
 #pragma unroll
     for (int dl = 0; dl < 4; ++dl)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int e = 16 * dl + l16 - 4 * lg - r;
-            dec[dl][r] = e < 0 ? 0.0f : decay_pow(s, e);
+            cx.dec[dl][r] = e < 0 ? 0.0f : decay_pow(cx.s, e);
         }
-    const float out_scale = decay_pow(s, 16 * w + l16 + 1);     // lambda^(a+1)
-    const float full_decay = decay_pow(s, PC);                   // lambda^C
-    const int vt = PT - 1 - tid;
-    const int vrow = 4 * (vt / (PJ / 4));                          // first token of this thread's V rows
-    float wfull[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) wfull[r] = decay_pow(s, PC - 1 - (vrow + r) < 0 ? 0 : PC - 1 - (vrow + r));
+    cx.out_scale = decay_pow(cx.s, 16 * w + l16 + 1);          // lambda^(a+1)
 
     // state slice in registers (fp32) and its bf16 transposed copy in LDS
     f32x4 sacc[ITW][2];
@@ -264,98 +393,18 @@ __global__ __launch_bounds__(PT) void prefill_bf16_kernel(
             const int it = w * ITW + u;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                sacc[u][jt][r] = St[(16 * it + 4 * lg + r) * D + j0 + 16 * jt + l16];
+                sacc[u][jt][r] = St[(16 * it + 4 * lg + r) * D + cx.j0 + 16 * jt + l16];
             uint2 p;
             p.x = pack_bf16x2(sacc[u][jt][0], sacc[u][jt][1]);
             p.y = pack_bf16x2(sacc[u][jt][2], sacc[u][jt][3]);
             *reinterpret_cast<uint2 *>(&sm.ST[16 * jt + l16][16 * it + 4 * lg]) = p;
         }
     // scores above the causal diagonal tiles are never written: zero them once
-    for (int e = tid; e < PC * (PC + PAD) / 2; e += PT)
-        reinterpret_cast<uint32_t *>(&sm.P[0][0])[e] = 0u;
+    for (int e = tid; e < PC * PP / 2; e += PT) reinterpret_cast<uint32_t *>(&sm.P[0][0])[e] = 0u;
 
-    Stage<D> st;
-    stage_load<D>(st, qb, kb, vb, 0, N, j0, tid);
-
-    const int64_t nblk = (N + PC - 1) / PC;
-    for (int64_t blk = 0; blk < nblk; ++blk) {
-        const int64_t t0 = blk * PC;
-        const int c = (int)min((int64_t)PC, N - t0);
-        float wv[4];
-        if (c == PC) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) wv[r] = wfull[r];
-        } else {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) wv[r] = (vrow + r < c) ? decay_pow(s, c - 1 - (vrow + r)) : 0.0f;
-        }
-        stage_store<D>(st, sm, tid, wv);
-        __syncthreads();                                   // block tiles visible
-        if (blk + 1 < nblk) stage_load<D>(st, qb, kb, vb, t0 + PC, N, j0, tid);
-
-        // intra-block scores
-        switch (w) {
-            case 0: score_tiles<D, 0>(sm, dec, l16, lg); break;
-            case 1: score_tiles<D, 1>(sm, dec, l16, lg); break;
-            case 2: score_tiles<D, 2>(sm, dec, l16, lg); break;
-            default: score_tiles<D, 3>(sm, dec, l16, lg); break;
-        }
-        // inter-block output from the carried state: O^T = S^T Q^T, column a
-        // scaled by lambda^(a+1); tokens 16w..16w+15
-        f32x4 oacc[2];
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-            oacc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < D / 32; ++ks)
-                oacc[jt] = mfma(frag(sm.ST, 16 * jt + l16, 32 * ks + 8 * lg),
-                                frag(sm.Q, 16 * w + l16, 32 * ks + 8 * lg), oacc[jt]);
-            oacc[jt] *= out_scale;
-        }
-        // decayed state scan: S = lambda^c S + K^T (lambda^(c-1-b) V)
-        const float sdec = (c == PC) ? full_decay : decay_pow(s, c);
-#pragma unroll
-        for (int u = 0; u < ITW; ++u)
-#pragma unroll
-            for (int jt = 0; jt < 2; ++jt) {
-                const int it = w * ITW + u;
-                sacc[u][jt] *= sdec;
-#pragma unroll
-                for (int ks = 0; ks < PC / 32; ++ks)
-                    sacc[u][jt] = mfma(frag(sm.KT, 16 * it + l16, 32 * ks + 8 * lg),
-                                       frag(sm.VW, 16 * jt + l16, 32 * ks + 8 * lg), sacc[u][jt]);
-            }
-        __syncthreads();                                   // scores visible; old ST reads done
-
-        // intra-block output: O^T += V^T P^T over tokens b < 16(w+1)
-        const int nks = w / 2 + 1;
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt)
-            for (int ks = 0; ks < nks; ++ks)
-                oacc[jt] = mfma(frag(sm.VT, 16 * jt + l16, 32 * ks + 8 * lg),
-                                frag(sm.P, 16 * w + l16, 32 * ks + 8 * lg), oacc[jt]);
-        const int a = 16 * w + l16;
-        if (a < c) {
-#pragma unroll
-            for (int jt = 0; jt < 2; ++jt) {
-                uint2 o;
-                o.x = pack_bf16x2(oacc[jt][0], oacc[jt][1]);
-                o.y = pack_bf16x2(oacc[jt][2], oacc[jt][3]);
-                *reinterpret_cast<uint2 *>(ob + (t0 + a) * D + j0 + 16 * jt + 4 * lg) = o;
-            }
-        }
-        // bf16 copy of the new state for the next block's inter term
-#pragma unroll
-        for (int u = 0; u < ITW; ++u)
-#pragma unroll
-            for (int jt = 0; jt < 2; ++jt) {
-                const int it = w * ITW + u;
-                uint2 p;
-                p.x = pack_bf16x2(sacc[u][jt][0], sacc[u][jt][1]);
-                p.y = pack_bf16x2(sacc[u][jt][2], sacc[u][jt][3]);
-                *reinterpret_cast<uint2 *>(&sm.ST[16 * jt + l16][16 * it + 4 * lg]) = p;
-            }
-        __syncthreads();                                   // new ST visible; tiles free
+    for (int64_t blk = 0; blk < cx.nblk; blk += 2) {
+        consume_step<D, 0>(cx, sm, blk, sacc);
+        consume_step<D, 1>(cx, sm, blk + 1, sacc);
     }
 
 #pragma unroll
@@ -365,10 +414,52 @@ __global__ __launch_bounds__(PT) void prefill_bf16_kernel(
             const int it = w * ITW + u;
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                St[(16 * it + 4 * lg + r) * D + j0 + 16 * jt + l16] = sacc[u][jt][r];
+                St[(16 * it + 4 * lg + r) * D + cx.j0 + 16 * jt + l16] = sacc[u][jt][r];
         }
 }
 
+template <int D>
+__global__ __launch_bounds__(2 * PT) void prefill_bf16_kernel(
+    const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+    const uint16_t *__restrict__ v, const float *__restrict__ slopes,
+    uint16_t *__restrict__ out, float *__restrict__ state, int64_t H, int64_t N)
+{
+    constexpr int NJ = D / PJ;            // workgroups per head
+    __shared__ Smem<D> sm;
+
+    Ctx<D> cx;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+    cx.w = wave & 3;
+    const int l = tid % 64;
+    cx.l16 = l % 16;
+    cx.lg = l / 16;
+
+    // XCD-aware placement: workgroup i runs on XCD i % 8; give the NJ
+    // workgroups of one head consecutive logical ids on the same XCD.
+    const int64_t nwg = gridDim.x;
+    int64_t lid = blockIdx.x;
+    if (nwg % 8 == 0) lid = (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8;
+    const int64_t bh = lid / NJ;
+    cx.j0 = (int)(lid % NJ) * PJ;
+    cx.s = slopes[bh % H];
+    cx.N = N;
+    // blocks processed: a multiple of NSET (trailing empty blocks are no-ops)
+    cx.nblk = ((N + PC - 1) / PC + NSET - 1) / NSET * NSET;
+    cx.qh = q + bh * N * D;
+    cx.kh = k + bh * N * D;
+    cx.vh = v + bh * N * D;
+    cx.oh = out + bh * N * D;
+    cx.full_decay = decay_pow(cx.s, PC);                        // lambda^C
+
+    if (wave >= 4) {
+        const int p = tid - PT;
+        cx.wfull = decay_pow(cx.s, PC - 1 - p / 4);             // lambda^(C-1-b)
+        producer<D>(cx, sm, p);
+    } else {
+        consumer<D>(cx, sm, state + bh * D * D, tid);
+    }
+}
 }  // namespace
 
 int64_t prefill_bf16_grid(int64_t B, int64_t H, int d) { return B * H * (d / PJ); }
@@ -377,7 +468,7 @@ hipError_t launch_prefill_bf16(const uint16_t *q, const uint16_t *k, const uint1
                                const float *slopes, uint16_t *out, float *state,
                                int64_t B, int64_t H, int64_t N, int d, hipStream_t stream)
 {
-    const dim3 grid((unsigned)prefill_bf16_grid(B, H, d)), block(PT);
+    const dim3 grid((unsigned)prefill_bf16_grid(B, H, d)), block(2 * PT);
     void *args[] = {(void *)&q, (void *)&k, (void *)&v, (void *)&slopes,
                     (void *)&out, (void *)&state, (void *)&H, (void *)&N};
     const void *fn = d == 64 ? (const void *)prefill_bf16_kernel<64>

@@ -10,7 +10,7 @@
 //   O^T       = S^T Q^T with column a scaled by lambda^(a+1)      [inter]
 //             + V^T P^T                                         [intra]
 //   S         = lambda^c S + K^T diag(lambda^(c-1-b)) V          [state scan]
-// Every product is a bf16 x bf16 -> fp32 MFMA (v_mfma_f32_16x16x32_bf16).
+// Every product is a bf16 x bf16 -> fp32 MFMA (v_mfma_f32_32x32x16_bf16).
 // Scores, the bf16 copy of the state and the decay-weighted V are rounded to
 // bf16 as MFMA operands; the state itself is accumulated and carried in fp32
 // registers for the whole sequence and never rounded.
@@ -22,28 +22,32 @@
 // four workgroups of a head are placed on one XCD so Q and K come from HBM
 // once and from that XCD's L2 for the other three.
 //
-// Data movement (wave-specialised).  Waves 4..7 are producers: they only
+// Roles inside a workgroup (8 waves).  Waves 4..7 are producers: they only
 // load Q, K and the workgroup's 64 x 32 slice of V with 16-byte buffer loads,
 // four blocks ahead of use (four register sets), and write them into one of
 // two LDS buffers one block ahead (plus a decay-weighted copy of V).  Waves
-// 0..3 are consumers: they only read LDS, run the MFMAs and store outputs.
-// Keeping global loads and stores in different waves matters on gfx9: one
-// counter (vmcnt) tracks both, and a wave with both kinds in flight must
-// drain all of them before it can use any loaded register.  Contractions
-// over tokens (the state update K^T V and the intra output V^T P^T) need the
-// token index contiguous per lane; they read K and V from their token-major
-// LDS tiles with ds_read_b64_tr_b16 (gfx950 transposing LDS read) instead of
-// keeping transposed copies.  K's 16-byte chunks are XOR-swizzled by row so
-// that both its plain reads (8 rows, one chunk) and its transposed reads
-// (4 rows, one chunk pair) hit distinct LDS banks.
+// 0..3 are consumers: they only read LDS, run the MFMAs and store outputs
+// (roles below).  Keeping global loads and stores in different waves matters
+// on gfx9: one counter (vmcnt) tracks both, and a wave with both kinds in
+// flight must drain all of them before it can use any loaded register.
 //
-// Consumer wave roles (4 waves, 16x16 output tiles):
-//   scores:  the 10 causal 16x16 tiles of P^T, 2-3 per wave;
-//   output:  wave w owns tokens 16w..16w+15 of the block (both 16-col tiles);
-//   state:   wave w owns rows (D/4) w .. of the D x 32 state slice.
-// Operand layouts of v_mfma_f32_16x16x32_bf16 (lane l, l16 = l % 16,
-// lg = l / 16): A row l16, k = 8 lg .. 8 lg + 7; B column l16, same k;
-// result rows 4 lg + r (r = 0..3), column l16.
+// What bounds it: every workgroup of a head pulls the full Q and K blocks
+// through its XCD's L2 (the four copies share one HBM read), and LDS carries
+// the producers' writes plus every MFMA operand.  The layout therefore keeps
+// each operand's LDS reads few: 32x32x16 MFMAs (half the operand bytes per
+// flop of 16x16x32), scores kept in registers and fed straight into V^T P^T,
+// Q fragments shared by the score and inter-term products, and one barrier
+// per block (double-buffered tiles and state copy).
+// Contractions over tokens (the state update K^T V and the intra output
+// V^T P^T) need the token index contiguous per lane; they read K and V from
+// their token-major LDS tiles with ds_read_b64_tr_b16 (gfx950 transposing LDS
+// read).  K's 16-byte chunks are XOR-swizzled by row so that both its plain
+// reads (8 rows, one chunk) and its transposed reads (4 rows, one chunk pair)
+// hit distinct LDS banks.
+//
+// Operand layouts of v_mfma_f32_32x32x16_bf16 (lane l, l32 = l % 32,
+// h = l / 32): A row l32, k = 8 h .. 8 h + 7; B column l32, same k; result
+// register r (0..15): row 8 (r / 4) + 4 h + r % 4, column l32.
 // ds_read_b64_tr_b16: within each 16-lane group, lane l16 supplies the
 // address of a 4-element chunk; lane l16 receives element l16 % 4 of chunks
 // 4e + l16 / 4, e = 0..3.  So if lane l16 points at row r0 + l16/4, column
@@ -51,25 +55,30 @@
 // r0 .. r0 + 3: a k-contiguous MFMA operand for a contraction over rows.
 #include "la_internal.h"
 
+#include <type_traits>
+
 namespace la {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int PC = 64;        // tokens per block
 constexpr int PJ = 32;        // state / output columns per workgroup
-constexpr int PT = 256;       // threads per role (4 consumer + 4 producer waves)
+constexpr int NCONS = 4;      // consumer waves
+constexpr int PT = 256;       // producer threads (4 waves)
+constexpr int NTHREADS = 64 * NCONS + PT;
 constexpr int NSET = 4;       // producer register sets (blocks in flight)
 constexpr int QPAD = 8;       // bf16 padding of Q and state-copy rows
-constexpr int VP = 48;        // V row pitch (96 B: transposed reads conflict-free)
-constexpr int PP = PC + 8;    // score row pitch
+constexpr int VP = 32;        // V row pitch (64 B, unpadded)
 
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ bf16x8 ld8(const uint16_t *p) {
@@ -84,6 +93,16 @@ __device__ __forceinline__ bf16x8 ldtr8(const uint16_t *p0, const uint16_t *p1) 
     return __builtin_bit_cast(bf16x8, c);
 }
 
+// eight fp32 -> one bf16 operand (round to nearest even)
+__device__ __forceinline__ bf16x8 to_bf16x8(const f32x16 &x, int base) {
+    u32x4 w;
+    w[0] = pack_bf16x2(x[base + 0], x[base + 1]);
+    w[1] = pack_bf16x2(x[base + 2], x[base + 3]);
+    w[2] = pack_bf16x2(x[base + 4], x[base + 5]);
+    w[3] = pack_bf16x2(x[base + 6], x[base + 7]);
+    return __builtin_bit_cast(bf16x8, w);
+}
+
 // 16-byte-chunk swizzle of K rows (see the header comment)
 __device__ __forceinline__ int kswz(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
 
@@ -93,13 +112,14 @@ struct alignas(16) Smem {
     uint16_t K[2][PC][D];            // K blocks, token-major, chunk-swizzled
     uint16_t V[2][PC][VP];           // V slices, token-major
     uint16_t VW[2][PC][VP];          // V slices times lambda^(c-1-b)
-    uint16_t P[PC][PP];              // decayed causal scores P[a][b]
-    uint16_t ST[PJ][D + QPAD];       // bf16 copy of the state slice, transposed
+    uint16_t ST[2][PJ][D + QPAD];    // bf16 copies of the state slice, transposed
+    float OP[2][64][20];             // W3 -> W2 partial outputs (one lane's 16 values)
 };
 
-// one block's share of this thread, in registers
+// ---- producer waves: global -> registers -> LDS ----------------------------
+
 template <int D>
-struct Regs {
+struct Regs {                        // one block's share of a producer thread
     static constexpr int NQ = PC * D / 8 / PT;   // 16-byte chunks of Q (and of K)
     uint4 q[NQ], k[NQ], v;
 };
@@ -129,7 +149,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint16_t *bas
 }
 
 __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
     const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
     return make_uint4(x[0], x[1], x[2], x[3]);
 }
@@ -156,16 +175,16 @@ __device__ __forceinline__ uint32_t scale_pair(uint32_t x, float w) {
 
 // registers -> LDS buffer BUF; wv = lambda^(c-1-b) for this thread's token b
 template <int D, int BUF>
-__device__ __forceinline__ void store_block(const Regs<D> &r, Smem<D> &sm, int tid, float wv)
+__device__ __forceinline__ void store_block(const Regs<D> &r, Smem<D> &sm, int p, float wv)
 {
 #pragma unroll
     for (int u = 0; u < Regs<D>::NQ; ++u) {
-        const int ch = tid + PT * u;
+        const int ch = p + PT * u;
         const int row = ch / (D / 8), c8 = ch % (D / 8);
         *reinterpret_cast<uint4 *>(&sm.Q[BUF][row][c8 * 8]) = r.q[u];
         *reinterpret_cast<uint4 *>(&sm.K[BUF][row][(c8 ^ kswz(row)) * 8]) = r.k[u];
     }
-    const int vrow = tid / 4, vc = (tid % 4) * 8;
+    const int vrow = p / 4, vc = (p % 4) * 8;
     *reinterpret_cast<uint4 *>(&sm.V[BUF][vrow][vc]) = r.v;
     uint4 w;
     w.x = scale_pair(r.v.x, wv);
@@ -175,73 +194,37 @@ __device__ __forceinline__ void store_block(const Regs<D> &r, Smem<D> &sm, int t
     *reinterpret_cast<uint4 *>(&sm.VW[BUF][vrow][vc]) = w;
 }
 
-// Score tiles (bt, at) of P^T owned by wave W: the 10 causal 16x16 tiles of
-// the 64x64 block, spread so that score + output MFMA counts balance.
-template <int W> struct ScoreTiles;
-template <> struct ScoreTiles<0> { static constexpr int n = 3; static constexpr int bt[3] = {0, 0, 3}, at[3] = {0, 3, 3}; };
-template <> struct ScoreTiles<1> { static constexpr int n = 3; static constexpr int bt[3] = {0, 1, 1}, at[3] = {1, 1, 3}; };
-template <> struct ScoreTiles<2> { static constexpr int n = 2; static constexpr int bt[3] = {0, 1, 0}, at[3] = {2, 2, 0}; };
-template <> struct ScoreTiles<3> { static constexpr int n = 2; static constexpr int bt[3] = {2, 2, 0}, at[3] = {2, 3, 0}; };
-
-// dec[dl][r]: decay of score element r of a tile whose token-tile offset is
-// dl = at - bt, for this lane: lambda^(16 dl + l16 - 4 lg - r), 0 if negative.
-template <int D, int W, int BUF>
-__device__ __forceinline__ void score_tiles(Smem<D> &sm, const float (&dec)[4][4], int l16, int lg)
-{
-    using T = ScoreTiles<W>;
-    const int ks0 = kswz(l16);
-#pragma unroll
-    for (int u = 0; u < T::n; ++u) {
-        const int bt = T::bt[u], at = T::at[u];
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks)
-            acc = mfma(ld8(&sm.K[BUF][16 * bt + l16][((4 * ks + lg) ^ ks0) * 8]),
-                       ld8(&sm.Q[BUF][16 * at + l16][32 * ks + 8 * lg]), acc);
-        const int dl = at - bt;
-        uint2 p;
-        p.x = pack_bf16x2(acc[0] * dec[dl][0], acc[1] * dec[dl][1]);
-        p.y = pack_bf16x2(acc[2] * dec[dl][2], acc[3] * dec[dl][3]);
-        *reinterpret_cast<uint2 *>(&sm.P[16 * at + l16][16 * bt + 4 * lg]) = p;
-    }
-}
-
 template <int D>
 struct Ctx {                          // per-thread constants of one workgroup
     const uint16_t *qh, *kh, *vh;     // this (b, h) slice
     const uint16_t *oh;
     int64_t N, nblk;                  // nblk: blocks processed (a multiple of NSET)
-    float s, full_decay, out_scale, wfull;
-    float dec[4][4];
-    int w, l16, lg, j0;
+    float s;
+    int j0;
 };
 
-// ---- producer waves (4..7): global -> registers -> LDS --------------------
-
-// stage block blk (register set r) into LDS buffer BUF
 template <int D, int BUF>
 __device__ __forceinline__ void produce_store(const Ctx<D> &cx, Smem<D> &sm, const Regs<D> &r,
-                                              int64_t blk, int p)
+                                              int64_t blk, int p, float wfull)
 {
     const int c = block_len(blk * PC, cx.N);
     const int b = p / 4;
-    const float wv = c == PC ? cx.wfull : (b < c ? decay_pow(cx.s, c - 1 - b) : 0.0f);
+    const float wv = c == PC ? wfull : (b < c ? decay_pow(cx.s, c - 1 - b) : 0.0f);
     store_block<D, BUF>(r, sm, p, wv);
 }
 
-// One producer step per block blk: after the block's first barrier, stage
-// block blk+1 (register set SET) into the other LDS buffer, then reload SET
-// with block blk+1+NSET.  Loads past the end return zeros without touching
+// One producer step per block blk: after the block's barrier, stage block
+// blk+1 (register set SET) into the other LDS buffer, then reload SET with
+// block blk+1+NSET.  Loads past the end return zeros without touching
 // memory, so nothing here is conditional (exact vmcnt waits).
 template <int D, int SET>
 __device__ __forceinline__ void produce_step(const Ctx<D> &cx, Smem<D> &sm, Regs<D> (&rs)[NSET],
-                                             const Addr<D> &ad, int64_t blk, int p)
+                                             const Addr<D> &ad, int64_t blk, int p, float wfull)
 {
-    __syncthreads();                                   // B1 of block blk
-    if (SET % 2 == 1) produce_store<D, 1>(cx, sm, rs[SET], blk + 1, p);   // blk even -> buffer 1
-    else              produce_store<D, 0>(cx, sm, rs[SET], blk + 1, p);
+    __syncthreads();                                   // barrier of block blk
+    if (SET % 2 == 1) produce_store<D, 1>(cx, sm, rs[SET], blk + 1, p, wfull);
+    else              produce_store<D, 0>(cx, sm, rs[SET], blk + 1, p, wfull);
     load_block<D>(rs[SET], cx.qh, cx.kh, cx.vh, (blk + 1 + NSET) * PC, cx.N, ad);
-    __syncthreads();                                   // B2 of block blk
 }
 
 template <int D>
@@ -254,172 +237,281 @@ __device__ void producer(const Ctx<D> &cx, Smem<D> &sm, int p)
         ad.qk[u] = (uint32_t)(((ch / (D / 8)) * D + (ch % (D / 8)) * 8) * 2);
     }
     ad.v = (uint32_t)(((p / 4) * D + cx.j0 + (p % 4) * 8) * 2);
+    const float wfull = decay_pow(cx.s, PC - 1 - p / 4);       // lambda^(C-1-b)
 
-    Regs<D> rs[NSET];                                   // set i holds block i (mod NSET)
+    Regs<D> rs[NSET];                                           // set i holds block i (mod NSET)
 #pragma unroll
     for (int i = 0; i < NSET; ++i) load_block<D>(rs[i], cx.qh, cx.kh, cx.vh, i * PC, cx.N, ad);
-    produce_store<D, 0>(cx, sm, rs[0], 0, p);
+    produce_store<D, 0>(cx, sm, rs[0], 0, p, wfull);
     load_block<D>(rs[0], cx.qh, cx.kh, cx.vh, NSET * PC, cx.N, ad);
 
     // block blk stages block blk+1 from set (blk+1) % NSET into buffer (blk+1) % 2
     for (int64_t blk = 0; blk < cx.nblk; blk += NSET) {
-        produce_step<D, 1>(cx, sm, rs, ad, blk + 0, p);
-        produce_step<D, 2>(cx, sm, rs, ad, blk + 1, p);
-        produce_step<D, 3>(cx, sm, rs, ad, blk + 2, p);
-        produce_step<D, 0>(cx, sm, rs, ad, blk + 3, p);
+        produce_step<D, 1>(cx, sm, rs, ad, blk + 0, p, wfull);
+        produce_step<D, 2>(cx, sm, rs, ad, blk + 1, p, wfull);
+        produce_step<D, 3>(cx, sm, rs, ad, blk + 2, p, wfull);
+        produce_step<D, 0>(cx, sm, rs, ad, blk + 3, p, wfull);
+    }
+    __syncthreads();                                   // final barrier (matches the consumers)
+}
+
+// ---- consumer waves: scores, outputs, state scan ---------------------------
+//
+// Four consumer waves, one per SIMD (each shares its SIMD with one producer):
+//   W0  the state scan: S = lambda^c S + K^T (lambda^(c-1-b) V) on all D
+//       state rows, and the bf16 copy ST of the new state (double-buffered);
+//   W1  tokens 0..31: inter term S^T Q^T + scores P^T(0,0) + V^T P^T, stored;
+//   W2  tokens 32..63: inter term + scores P^T(1,1) + their V^T P^T part;
+//   W3  tokens 32..63: scores P^T(0,1) + their V^T P^T part, handed to W2
+//       through LDS (fp32, double-buffered); W2 adds it one block later and
+//       stores that block's tokens 32..63 then.
+// The per-wave MFMA counts per block (d = 128) are 16 / 18 / 18 / 10, and the
+// sequential part of the method (the state scan) runs on its own wave.
+
+template <int D>
+struct Lane {                               // lane coordinates for 32x32 MFMAs
+    int l32, h, l16, q2, trow, tcol;
+    __device__ explicit Lane(int lane)
+        : l32(lane % 32), h(lane / 32), l16(lane % 16), q2((lane / 16) % 2),
+          trow((lane % 16) >> 2), tcol(4 * ((lane % 16) & 3)) {}
+};
+
+// decay of score accumulator register r for a tile whose a-half is ah and
+// b-half bh: lambda^(a-b), 0 above the diagonal
+__device__ __forceinline__ void score_decay(float (&dec)[16], float s, int ah, int bh, int l32, int h)
+{
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        const int e = (32 * ah + l32) - (32 * bh + 8 * (r / 4) + 4 * h + r % 4);
+        dec[r] = e < 0 ? 0.0f : decay_pow(s, e);
     }
 }
 
-// ---- consumer waves (0..3): scores, outputs, state scan ---------------------
-
-// one 64-token block held in LDS buffer BUF
-template <int D, int BUF>
-__device__ __forceinline__ void consume_step(const Ctx<D> &cx, Smem<D> &sm, int64_t blk,
-                                             f32x4 (&sacc)[D / 64][2])
+// O^T(a-half ah) = scale * S^T Q^T from state copy SB and Q buffer QB
+template <int D>
+__device__ __forceinline__ f32x16 inter_term(const Smem<D> &sm, int qb, int sb, int ah,
+                                              const Lane<D> &ln, float scale, bf16x8 (&qf)[D / 16])
 {
-    constexpr int ITW = D / 64;
-    const int w = cx.w, l16 = cx.l16, lg = cx.lg;
-    const int64_t t0 = blk * PC;
-    const int c = block_len(t0, cx.N);
+    f32x16 acc = {};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) qf[ks] = ld8(&sm.Q[qb][32 * ah + ln.l32][16 * ks + 8 * ln.h]);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+        acc = mfma(ld8(&sm.ST[sb][ln.l32][16 * ks + 8 * ln.h]), qf[ks], acc);
+    return acc * scale;
+}
 
-    __syncthreads();          // B1: buffer BUF staged; previous block fully consumed
+// score tile P^T(bh, ah) (decayed) from Q fragments qf, then acc += V^T P^T
+// over the tile's 32 tokens; the accumulator registers of P^T are the B
+// operand directly (registers 8s..8s+7 hold tokens 32bh + 16s + 8e' + 4h + 0..3)
+template <int D>
+__device__ __forceinline__ void score_pv(const Smem<D> &sm, int buf, int bh,
+                                         const bf16x8 (&qf)[D / 16], const float (&dec)[16],
+                                         const Lane<D> &ln, f32x16 &acc)
+{
+    f32x16 pacc = {};
+    const int krow = 32 * bh + ln.l32;
+    const int ksw = kswz(krow);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+        pacc = mfma(ld8(&sm.K[buf][krow][((2 * ks + ln.h) ^ ksw) * 8]), qf[ks], pacc);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) pacc[r] *= dec[r];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+        const int r0 = 32 * bh + 16 * s2 + 4 * ln.h + ln.trow;
+        const bf16x8 va = ldtr8(&sm.V[buf][r0][16 * ln.q2 + ln.tcol],
+                                &sm.V[buf][r0 + 8][16 * ln.q2 + ln.tcol]);
+        acc = mfma(va, to_bf16x8(pacc, 8 * s2), acc);
+    }
+}
 
-    // intra-block scores
-    switch (w) {
-        case 0: score_tiles<D, 0, BUF>(sm, cx.dec, l16, lg); break;
-        case 1: score_tiles<D, 1, BUF>(sm, cx.dec, l16, lg); break;
-        case 2: score_tiles<D, 2, BUF>(sm, cx.dec, l16, lg); break;
-        default: score_tiles<D, 3, BUF>(sm, cx.dec, l16, lg); break;
+// store a 32x32 O^T tile (tokens 32ah.., columns j0..j0+31) of block t0.
+// Accumulator register group q4 holds columns 8q4 + 4h + 0..3 of token a; a
+// lane-half swap (lanes l <-> l+32) of groups (0,1) and (2,3) gives lane h
+// columns 8h..8h+7 and 16+8h..16+8h+7, so each row is written as 32-byte runs
+// by two 16-byte stores per lane.
+template <int D>
+__device__ __forceinline__ void store_out(const Ctx<D> &cx, int64_t t0, int ah, const Lane<D> &ln,
+                                          const f32x16 &acc)
+{
+    const __amdgpu_buffer_rsrc_t ro = block_rsrc<D>(cx.oh, t0, cx.N);   // rows past N dropped
+    const int a = 32 * ah + ln.l32;
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+        const int g0 = 2 * pr, g1 = 2 * pr + 1;
+        unsigned x0 = pack_bf16x2(acc[4 * g0 + 0], acc[4 * g0 + 1]);
+        unsigned x1 = pack_bf16x2(acc[4 * g0 + 2], acc[4 * g0 + 3]);
+        unsigned y0 = pack_bf16x2(acc[4 * g1 + 0], acc[4 * g1 + 1]);
+        unsigned y1 = pack_bf16x2(acc[4 * g1 + 2], acc[4 * g1 + 3]);
+        const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+        const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+        u32x4 o;
+        o[0] = s0[0]; o[1] = s1[0]; o[2] = s0[1]; o[3] = s1[1];
+        __builtin_amdgcn_raw_buffer_store_b128(o, ro, (a * D + cx.j0 + 16 * pr + 8 * ln.h) * 2, 0, 0);
     }
-    // inter-block output from the carried state: O^T = S^T Q^T, column a
-    // scaled by lambda^(a+1); tokens 16w..16w+15
-    f32x4 oacc[2];
+}
+
+// bf16 copy of state tile it (rows 32it..) into ST[buf][j][i]
+template <int D>
+__device__ __forceinline__ void write_st(Smem<D> &sm, int buf, int it, const Lane<D> &ln,
+                                         const f32x16 &s)
+{
 #pragma unroll
-    for (int jt = 0; jt < 2; ++jt) {
-        oacc[jt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < D / 32; ++ks)
-            oacc[jt] = mfma(ld8(&sm.ST[16 * jt + l16][32 * ks + 8 * lg]),
-                            ld8(&sm.Q[BUF][16 * w + l16][32 * ks + 8 * lg]), oacc[jt]);
-        oacc[jt] *= cx.out_scale;
+    for (int q4 = 0; q4 < 4; ++q4) {
+        uint2 p;
+        p.x = pack_bf16x2(s[4 * q4 + 0], s[4 * q4 + 1]);
+        p.y = pack_bf16x2(s[4 * q4 + 2], s[4 * q4 + 3]);
+        *reinterpret_cast<uint2 *>(&sm.ST[buf][ln.l32][32 * it + 8 * q4 + 4 * ln.h]) = p;
     }
-    // decayed state scan: S = lambda^c S + K^T (lambda^(c-1-b) V)
-    const float sdec = (c == PC) ? cx.full_decay : decay_pow(cx.s, c);   // 1 for an empty block
-    const int trow = l16 >> 2;                 // row within a 4-row transposed read
-    const int tcol = 4 * (l16 & 3);            // column offset within a 16-column tile
+}
+
+// W0: the state scan
+template <int D>
+__device__ void scan_wave(const Ctx<D> &cx, Smem<D> &sm, float *St, int lane)
+{
+    constexpr int NT = D / 32;                  // 32-row state tiles
+    const Lane<D> ln(lane);
+    const float full_decay = decay_pow(cx.s, PC);
+    const int clast = (int)(cx.N - (cx.N - 1) / PC * PC);          // tokens of the last real block
+    const float last_decay = decay_pow(cx.s, clast);
+
+    f32x16 sacc[NT];
 #pragma unroll
-    for (int u = 0; u < ITW; ++u) {
-        const int it = w * ITW + u;
-        bf16x8 ka[PC / 32];
+    for (int it = 0; it < NT; ++it) {
 #pragma unroll
-        for (int ks = 0; ks < PC / 32; ++ks) {
-            const int r0 = 32 * ks + 8 * lg + trow;
-            const int ch = 2 * it + ((l16 & 3) >> 1), sub = 4 * (l16 & 1);
-            ka[ks] = ldtr8(&sm.K[BUF][r0][((ch ^ kswz(r0)) * 8) + sub],
-                           &sm.K[BUF][r0 + 4][((ch ^ kswz(r0 + 4)) * 8) + sub]);
+        for (int r = 0; r < 16; ++r)
+            sacc[it][r] = St[(32 * it + 8 * (r / 4) + 4 * ln.h + r % 4) * D + cx.j0 + ln.l32];
+        write_st<D>(sm, 1, it, ln, sacc[it]);   // read by block 0
+    }
+
+    auto step = [&](int64_t blk, auto BUFC) {
+        constexpr int BUF = decltype(BUFC)::value;
+        const int c = block_len(blk * PC, cx.N);
+        __syncthreads();
+        const float sdec = c == PC ? full_decay : (c == 0 ? 1.0f : last_decay);
+        bf16x8 vwf[PC / 16];
+#pragma unroll
+        for (int ks = 0; ks < PC / 16; ++ks) {
+            const int r0 = 16 * ks + 8 * ln.h + ln.trow;
+            vwf[ks] = ldtr8(&sm.VW[BUF][r0][16 * ln.q2 + ln.tcol], &sm.VW[BUF][r0 + 4][16 * ln.q2 + ln.tcol]);
         }
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-            sacc[u][jt] *= sdec;
+        for (int it = 0; it < NT; ++it) {
+            const int col = 32 * it + 16 * ln.q2 + ln.tcol;        // feature of this lane's chunk
+            const int ch = col >> 3, sub = col & 7;
+            sacc[it] *= sdec;
 #pragma unroll
-            for (int ks = 0; ks < PC / 32; ++ks) {
-                const int r0 = 32 * ks + 8 * lg + trow;
-                sacc[u][jt] = mfma(ka[ks],
-                                   ldtr8(&sm.VW[BUF][r0][16 * jt + tcol],
-                                         &sm.VW[BUF][r0 + 4][16 * jt + tcol]),
-                                   sacc[u][jt]);
+            for (int ks = 0; ks < PC / 16; ++ks) {
+                const int r0 = 16 * ks + 8 * ln.h + ln.trow;
+                const bf16x8 ka = ldtr8(&sm.K[BUF][r0][((ch ^ kswz(r0)) * 8) + sub],
+                                        &sm.K[BUF][r0 + 4][((ch ^ kswz(r0 + 4)) * 8) + sub]);
+                sacc[it] = mfma(ka, vwf[ks], sacc[it]);
             }
+            write_st<D>(sm, BUF, it, ln, sacc[it]);
         }
-    }
-    __syncthreads();          // B2: scores visible; reads of the old state copy done
-
-    // intra-block output: O^T += V^T P^T over tokens b < 16(w+1)
-#pragma unroll
-    for (int ks = 0; ks < PC / 32; ++ks) {
-        if (ks > w / 2) break;
-        const int r0 = 32 * ks + 8 * lg + trow;
-        const bf16x8 pb = ld8(&sm.P[16 * w + l16][32 * ks + 8 * lg]);
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt)
-            oacc[jt] = mfma(ldtr8(&sm.V[BUF][r0][16 * jt + tcol], &sm.V[BUF][r0 + 4][16 * jt + tcol]),
-                            pb, oacc[jt]);
-    }
-    {   // rows past N are dropped by the descriptor's range check
-        typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-        const __amdgpu_buffer_rsrc_t ro = block_rsrc<D>(cx.oh, t0, cx.N);
-        const int a = 16 * w + l16;
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-            u32x2 o;
-            o[0] = pack_bf16x2(oacc[jt][0], oacc[jt][1]);
-            o[1] = pack_bf16x2(oacc[jt][2], oacc[jt][3]);
-            __builtin_amdgcn_raw_buffer_store_b64(o, ro, (a * D + cx.j0 + 16 * jt + 4 * lg) * 2, 0, 0);
-        }
-    }
-    // bf16 copy of the new state for the next block's inter term
-#pragma unroll
-    for (int u = 0; u < ITW; ++u)
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-            const int it = w * ITW + u;
-            uint2 p;
-            p.x = pack_bf16x2(sacc[u][jt][0], sacc[u][jt][1]);
-            p.y = pack_bf16x2(sacc[u][jt][2], sacc[u][jt][3]);
-            *reinterpret_cast<uint2 *>(&sm.ST[16 * jt + l16][16 * it + 4 * lg]) = p;
-        }
-}
-
-template <int D>
-__device__ void consumer(Ctx<D> &cx, Smem<D> &sm, float *St, int tid)
-{
-    constexpr int ITW = D / 64;
-    const int w = cx.w, l16 = cx.l16, lg = cx.lg;
-    // per-lane decay constants
-#pragma unroll
-    for (int dl = 0; dl < 4; ++dl)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int e = 16 * dl + l16 - 4 * lg - r;
-            cx.dec[dl][r] = e < 0 ? 0.0f : decay_pow(cx.s, e);
-        }
-    cx.out_scale = decay_pow(cx.s, 16 * w + l16 + 1);          // lambda^(a+1)
-
-    // state slice in registers (fp32) and its bf16 transposed copy in LDS
-    f32x4 sacc[ITW][2];
-#pragma unroll
-    for (int u = 0; u < ITW; ++u)
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-            const int it = w * ITW + u;
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                sacc[u][jt][r] = St[(16 * it + 4 * lg + r) * D + cx.j0 + 16 * jt + l16];
-            uint2 p;
-            p.x = pack_bf16x2(sacc[u][jt][0], sacc[u][jt][1]);
-            p.y = pack_bf16x2(sacc[u][jt][2], sacc[u][jt][3]);
-            *reinterpret_cast<uint2 *>(&sm.ST[16 * jt + l16][16 * it + 4 * lg]) = p;
-        }
-    // scores above the causal diagonal tiles are never written: zero them once
-    for (int e = tid; e < PC * PP / 2; e += PT) reinterpret_cast<uint32_t *>(&sm.P[0][0])[e] = 0u;
-
+    };
     for (int64_t blk = 0; blk < cx.nblk; blk += 2) {
-        consume_step<D, 0>(cx, sm, blk, sacc);
-        consume_step<D, 1>(cx, sm, blk + 1, sacc);
+        step(blk, std::integral_constant<int, 0>());
+        step(blk + 1, std::integral_constant<int, 1>());
     }
+    __syncthreads();                            // final barrier (W2's last store)
 
 #pragma unroll
-    for (int u = 0; u < ITW; ++u)
+    for (int it = 0; it < NT; ++it)
 #pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-            const int it = w * ITW + u;
+        for (int r = 0; r < 16; ++r)
+            St[(32 * it + 8 * (r / 4) + 4 * ln.h + r % 4) * D + cx.j0 + ln.l32] = sacc[it][r];
+}
+
+// W1: tokens 0..31, complete
+template <int D>
+__device__ void out0_wave(const Ctx<D> &cx, Smem<D> &sm, int lane)
+{
+    const Lane<D> ln(lane);
+    float dec[16];
+    score_decay(dec, cx.s, 0, 0, ln.l32, ln.h);
+    const float scale = decay_pow(cx.s, ln.l32 + 1);               // lambda^(a+1)
+    auto step = [&](int64_t blk, auto BUFC) {
+        constexpr int BUF = decltype(BUFC)::value;
+        __syncthreads();
+        bf16x8 qf[D / 16];
+        f32x16 acc = inter_term<D>(sm, BUF, BUF ^ 1, 0, ln, scale, qf);
+        score_pv<D>(sm, BUF, 0, qf, dec, ln, acc);
+        store_out<D>(cx, blk * PC, 0, ln, acc);
+    };
+    for (int64_t blk = 0; blk < cx.nblk; blk += 2) {
+        step(blk, std::integral_constant<int, 0>());
+        step(blk + 1, std::integral_constant<int, 1>());
+    }
+    __syncthreads();
+}
+
+// W2: tokens 32..63, inter term + diagonal scores; adds W3's part one block later
+template <int D>
+__device__ void out1_wave(const Ctx<D> &cx, Smem<D> &sm, int lane)
+{
+    const Lane<D> ln(lane);
+    float dec[16];
+    score_decay(dec, cx.s, 1, 1, ln.l32, ln.h);
+    const float scale = decay_pow(cx.s, 32 + ln.l32 + 1);
+    f32x16 prev = {};
+    auto finish_prev = [&](int64_t pblk, int pbuf) {               // block pblk's tokens 32..63
+        const float4 *op = reinterpret_cast<const float4 *>(&sm.OP[pbuf][lane][0]);
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                St[(16 * it + 4 * lg + r) * D + cx.j0 + 16 * jt + l16] = sacc[u][jt][r];
+        for (int u = 0; u < 4; ++u) {
+            const float4 x = op[u];
+            prev[4 * u + 0] += x.x; prev[4 * u + 1] += x.y;
+            prev[4 * u + 2] += x.z; prev[4 * u + 3] += x.w;
         }
+        store_out<D>(cx, pblk * PC, 1, ln, prev);
+    };
+    auto step = [&](int64_t blk, auto BUFC) {
+        constexpr int BUF = decltype(BUFC)::value;
+        __syncthreads();
+        bf16x8 qf[D / 16];
+        f32x16 acc = inter_term<D>(sm, BUF, BUF ^ 1, 1, ln, scale, qf);
+        score_pv<D>(sm, BUF, 1, qf, dec, ln, acc);
+        if (blk > 0) finish_prev(blk - 1, BUF ^ 1);
+        prev = acc;
+    };
+    for (int64_t blk = 0; blk < cx.nblk; blk += 2) {
+        step(blk, std::integral_constant<int, 0>());
+        step(blk + 1, std::integral_constant<int, 1>());
+    }
+    __syncthreads();                            // W3's part of the last block is visible
+    finish_prev(cx.nblk - 1, (int)((cx.nblk - 1) & 1));
+}
+
+// W3: tokens 32..63, off-diagonal scores P^T(0,1) and their V^T P^T part
+template <int D>
+__device__ void out1x_wave(const Ctx<D> &cx, Smem<D> &sm, int lane)
+{
+    const Lane<D> ln(lane);
+    float dec[16];
+    score_decay(dec, cx.s, 1, 0, ln.l32, ln.h);
+    auto step = [&](int64_t blk, auto BUFC) {
+        constexpr int BUF = decltype(BUFC)::value;
+        __syncthreads();
+        bf16x8 qf[D / 16];
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) qf[ks] = ld8(&sm.Q[BUF][32 + ln.l32][16 * ks + 8 * ln.h]);
+        f32x16 acc = {};
+        score_pv<D>(sm, BUF, 0, qf, dec, ln, acc);
+        float4 *op = reinterpret_cast<float4 *>(&sm.OP[BUF][lane][0]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            op[u] = make_float4(acc[4 * u + 0], acc[4 * u + 1], acc[4 * u + 2], acc[4 * u + 3]);
+    };
+    for (int64_t blk = 0; blk < cx.nblk; blk += 2) {
+        step(blk, std::integral_constant<int, 0>());
+        step(blk + 1, std::integral_constant<int, 1>());
+    }
+    __syncthreads();
 }
 
 template <int D>
-__global__ __launch_bounds__(2 * PT) void prefill_bf16_kernel(
+__global__ __launch_bounds__(NTHREADS) void prefill_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const float *__restrict__ slopes,
     uint16_t *__restrict__ out, float *__restrict__ state, int64_t H, int64_t N)
@@ -427,13 +519,8 @@ __global__ __launch_bounds__(2 * PT) void prefill_bf16_kernel(
     constexpr int NJ = D / PJ;            // workgroups per head
     __shared__ Smem<D> sm;
 
-    Ctx<D> cx;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
-    cx.w = wave & 3;
-    const int l = tid % 64;
-    cx.l16 = l % 16;
-    cx.lg = l / 16;
 
     // XCD-aware placement: workgroup i runs on XCD i % 8; give the NJ
     // workgroups of one head consecutive logical ids on the same XCD.
@@ -441,6 +528,8 @@ __global__ __launch_bounds__(2 * PT) void prefill_bf16_kernel(
     int64_t lid = blockIdx.x;
     if (nwg % 8 == 0) lid = (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8;
     const int64_t bh = lid / NJ;
+
+    Ctx<D> cx;
     cx.j0 = (int)(lid % NJ) * PJ;
     cx.s = slopes[bh % H];
     cx.N = N;
@@ -450,16 +539,17 @@ __global__ __launch_bounds__(2 * PT) void prefill_bf16_kernel(
     cx.kh = k + bh * N * D;
     cx.vh = v + bh * N * D;
     cx.oh = out + bh * N * D;
-    cx.full_decay = decay_pow(cx.s, PC);                        // lambda^C
 
-    if (wave >= 4) {
-        const int p = tid - PT;
-        cx.wfull = decay_pow(cx.s, PC - 1 - p / 4);             // lambda^(C-1-b)
-        producer<D>(cx, sm, p);
-    } else {
-        consumer<D>(cx, sm, state + bh * D * D, tid);
+    const int lane = tid % 64;
+    switch (wave) {
+        case 0: scan_wave<D>(cx, sm, state + bh * D * D, lane); break;
+        case 1: out0_wave<D>(cx, sm, lane); break;
+        case 2: out1_wave<D>(cx, sm, lane); break;
+        case 3: out1x_wave<D>(cx, sm, lane); break;
+        default: producer<D>(cx, sm, tid - 64 * NCONS); break;
     }
 }
+
 }  // namespace
 
 int64_t prefill_bf16_grid(int64_t B, int64_t H, int d) { return B * H * (d / PJ); }
@@ -468,7 +558,7 @@ hipError_t launch_prefill_bf16(const uint16_t *q, const uint16_t *k, const uint1
                                const float *slopes, uint16_t *out, float *state,
                                int64_t B, int64_t H, int64_t N, int d, hipStream_t stream)
 {
-    const dim3 grid((unsigned)prefill_bf16_grid(B, H, d)), block(2 * PT);
+    const dim3 grid((unsigned)prefill_bf16_grid(B, H, d)), block(NTHREADS);
     void *args[] = {(void *)&q, (void *)&k, (void *)&v, (void *)&slopes,
                     (void *)&out, (void *)&state, (void *)&H, (void *)&N};
     const void *fn = d == 64 ? (const void *)prefill_bf16_kernel<64>

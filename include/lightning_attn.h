@@ -85,6 +85,38 @@ int la_prefill_f32(const float *q, const float *k, const float *v, const float *
                    int64_t B, int64_t H, int64_t N, int64_t d, void *stream);
 
 /*
+ * Packed variable-length prefill: nseq independent sequences of different
+ * lengths in one launch, each with its own state (the state is reset between
+ * sequences, unlike a dense run over the concatenated tokens).
+ *   q, k, v     [H,T,d] bf16, read only: the dense layout with B = 1 and
+ *               N = T; sequence i occupies rows cu_seqlens[i] ..
+ *               cu_seqlens[i+1]-1 of every head.
+ *   cu_seqlens  [nseq+1] int64, DEVICE pointer, 8-byte aligned: 0 =
+ *               cu[0] <= cu[1] <= ... <= cu[nseq] = T.  Empty sequences are
+ *               allowed (their state is left unchanged).  The contents are
+ *               not checked on the host; out-of-order or out-of-range offsets
+ *               are clamped into [0, T] on the device, so they never address
+ *               memory outside the tensors, but the results are then
+ *               unspecified.
+ *   slopes      [H] fp32, shared by all sequences.
+ *   out         [H,T,d] bf16, written (rows outside every sequence untouched).
+ *   states      [nseq,H,d,d] fp32, IN/OUT: initial state of each sequence on
+ *               entry (zero-fill for fresh sequences), its final state on exit.
+ * Results for sequence i equal la_prefill on that sequence alone (B = 1,
+ * N = cu[i+1]-cu[i]), bitwise.  T == 0 is a no-op.  Source: the report's
+ * §4.1.2 (packed training samples made of many short sub-sequences, each
+ * attending only within itself) on top of the §4.1.1 blockwise recurrence.
+ */
+int la_prefill_varlen(const void *q, const void *k, const void *v, const float *slopes,
+                      const int64_t *cu_seqlens, int64_t nseq, void *out, float *states,
+                      int64_t H, int64_t T, int64_t d, void *stream);
+
+/* Packed variable-length prefill with fp32 q, k, v, out: same semantics. */
+int la_prefill_varlen_f32(const float *q, const float *k, const float *v, const float *slopes,
+                          const int64_t *cu_seqlens, int64_t nseq, float *out, float *states,
+                          int64_t H, int64_t T, int64_t d, void *stream);
+
+/*
  * One decode step for B*H sequences (one new token each).
  *   q, k, v     [B,H,d] bf16, read only.
  *   state       [B,H,d,d] fp32, updated in place: S' = lambda S + k^T v.

@@ -24,6 +24,8 @@ _P, _I64, _INT = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
 SIGNATURES = {
     "la_prefill": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], _INT),
     "la_prefill_f32": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], _INT),
+    "la_prefill_varlen": ([_P, _P, _P, _P, _P, _I64, _P, _P, _I64, _I64, _I64, _P], _INT),
+    "la_prefill_varlen_f32": ([_P, _P, _P, _P, _P, _I64, _P, _P, _I64, _I64, _I64, _P], _INT),
     "la_decode_step": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], _INT),
     "la_decode_step_f32": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], _INT),
     "la_status_string": ([_INT], ctypes.c_char_p),
@@ -116,6 +118,47 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: torch.Ten
         rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), slopes.data_ptr(), out.data_ptr(),
                 state.data_ptr(), B, H, N, d, _stream(dev))
     _check(rc, "la_prefill" if dt == torch.bfloat16 else "la_prefill_f32")
+    return out
+
+
+def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: torch.Tensor,
+                   cu_seqlens: torch.Tensor, states: torch.Tensor,
+                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Packed variable-length prefill: independent sequences in one launch.
+
+    q, k, v: [H,T,d] bf16 or fp32 (sequence i is rows cu_seqlens[i]:cu_seqlens[i+1]
+    of every head); cu_seqlens: [nseq+1] int64 on the same GPU (0 = cu[0] <= ... <=
+    cu[nseq] = T); slopes: [H] fp32; states: [nseq,H,d,d] fp32, IN = initial states,
+    OUT = final states (in place).  Returns out [H,T,d].  Enqueued on the current
+    stream; the offsets are not read on the host.
+    """
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise ValueError("q must be a [H,T,d] tensor")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("prefill_varlen runs on GPU tensors only (no CPU path)")
+    H, T, d = q.shape
+    dt = q.dtype
+    if dt not in (torch.bfloat16, torch.float32):
+        raise TypeError("q/k/v must be bfloat16 or float32")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, dt, dev, (H, T, d))
+    if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be a [nseq+1] tensor with nseq >= 1")
+    nseq = cu_seqlens.numel() - 1
+    _need(cu_seqlens, "cu_seqlens", torch.int64, dev, (nseq + 1,))
+    _need(slopes, "slopes", torch.float32, dev, (H,))
+    _need(states, "states", torch.float32, dev, (nseq, H, d, d))
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", dt, dev, (H, T, d))
+    lib = load_library()
+    fn = lib.la_prefill_varlen if dt == torch.bfloat16 else lib.la_prefill_varlen_f32
+    with torch.cuda.device(dev):
+        rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), slopes.data_ptr(), cu_seqlens.data_ptr(),
+                nseq, out.data_ptr(), states.data_ptr(), H, T, d, _stream(dev))
+    _check(rc, "la_prefill_varlen" if dt == torch.bfloat16 else "la_prefill_varlen_f32")
     return out
 
 

@@ -24,19 +24,19 @@ bool mul_ok(int64_t x, int64_t y, int64_t *r) {
     return true;
 }
 
-// shared checks for prefill; elem = bytes per activation element
-int check_prefill(const void *q, const void *k, const void *v, const float *slopes,
-                  const void *out, const float *state, int64_t B, int64_t H, int64_t N,
-                  int64_t d, int64_t elem)
+// shared checks for prefill: activations hold `rows` rows of d elements of
+// `elem` bytes (B*H*N dense, H*T packed), the state `nstate` d x d fp32 slices
+int check_prefill_common(const void *q, const void *k, const void *v, const float *slopes,
+                         const void *out, const float *state, int64_t rows, int64_t nstate,
+                         int64_t d, int64_t elem)
 {
-    // with N == 0 the activations are empty and may be null (nothing is read)
-    if (N > 0 && (!q || !k || !v || !out)) return LA_ERR_INVALID_ARG;
+    // with no rows the activations are empty and may be null (nothing is read)
+    if (rows > 0 && (!q || !k || !v || !out)) return LA_ERR_INVALID_ARG;
     if (!slopes || !state) return LA_ERR_INVALID_ARG;
-    if (B < 1 || H < 1 || N < 0) return LA_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
-    int64_t bh, act, act_bytes, st, st_bytes;
-    if (!mul_ok(B, H, &bh) || !mul_ok(bh, N, &act) || !mul_ok(act, d, &act) ||
-        !mul_ok(act, elem, &act_bytes) || !mul_ok(bh, d * d, &st) || !mul_ok(st, 4, &st_bytes))
+    int64_t act, act_bytes, st, st_bytes;
+    if (!mul_ok(rows, d, &act) || !mul_ok(act, elem, &act_bytes) ||
+        !mul_ok(nstate, d * d, &st) || !mul_ok(st, 4, &st_bytes))
         return LA_ERR_INVALID_ARG;
     if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
         !aligned(state, 16) || !aligned(slopes, 4))
@@ -45,6 +45,28 @@ int check_prefill(const void *q, const void *k, const void *v, const float *slop
         overlap(out, act_bytes, v, act_bytes) || overlap(out, act_bytes, state, st_bytes))
         return LA_ERR_INVALID_ARG;
     return LA_OK;
+}
+
+int check_prefill(const void *q, const void *k, const void *v, const float *slopes,
+                  const void *out, const float *state, int64_t B, int64_t H, int64_t N,
+                  int64_t d, int64_t elem)
+{
+    if (B < 1 || H < 1 || N < 0) return LA_ERR_INVALID_ARG;
+    int64_t bh, rows;
+    if (!mul_ok(B, H, &bh) || !mul_ok(bh, N, &rows)) return LA_ERR_INVALID_ARG;
+    return check_prefill_common(q, k, v, slopes, out, state, rows, bh, d, elem);
+}
+
+// packed launches: also cu_seqlens (device, int64, 8-byte aligned, nseq + 1 entries)
+int check_varlen(const void *q, const void *k, const void *v, const float *slopes,
+                 const int64_t *cu_seqlens, int64_t nseq, const void *out, const float *state,
+                 int64_t H, int64_t T, int64_t d, int64_t elem)
+{
+    if (!cu_seqlens || !aligned(cu_seqlens, 8)) return LA_ERR_INVALID_ARG;
+    if (nseq < 1 || H < 1 || T < 0) return LA_ERR_INVALID_ARG;
+    int64_t rows, nstate;
+    if (!mul_ok(H, T, &rows) || !mul_ok(nseq, H, &nstate)) return LA_ERR_INVALID_ARG;
+    return check_prefill_common(q, k, v, slopes, out, state, rows, nstate, d, elem);
 }
 
 int check_decode(const void *q, const void *k, const void *v, const float *slopes,
@@ -81,10 +103,26 @@ int la_prefill(const void *q, const void *k, const void *v, const float *slopes,
     if (rc != LA_OK) return rc;
     if (la::prefill_bf16_grid(B, H, (int)d) > 0x7fffffff) return LA_ERR_UNSUPPORTED;
     if (N == 0) return LA_OK;
+    const la::SeqMap map = {nullptr, H, N, 0};
     return hip_status(la::launch_prefill_bf16(
         static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
-        static_cast<const uint16_t *>(v), slopes, static_cast<uint16_t *>(out), state, B, H, N,
+        static_cast<const uint16_t *>(v), slopes, static_cast<uint16_t *>(out), state, B, map,
         (int)d, static_cast<hipStream_t>(stream)));
+}
+
+int la_prefill_varlen(const void *q, const void *k, const void *v, const float *slopes,
+                      const int64_t *cu_seqlens, int64_t nseq, void *out, float *states,
+                      int64_t H, int64_t T, int64_t d, void *stream)
+{
+    const int rc = check_varlen(q, k, v, slopes, cu_seqlens, nseq, out, states, H, T, d, 2);
+    if (rc != LA_OK) return rc;
+    if (la::prefill_bf16_grid(nseq, H, (int)d) > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+    if (T == 0) return LA_OK;
+    const la::SeqMap map = {cu_seqlens, H, 0, T};
+    return hip_status(la::launch_prefill_bf16(
+        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+        static_cast<const uint16_t *>(v), slopes, static_cast<uint16_t *>(out), states, nseq,
+        map, (int)d, static_cast<hipStream_t>(stream)));
 }
 
 int la_prefill_f32(const float *q, const float *k, const float *v, const float *slopes,
@@ -95,7 +133,21 @@ int la_prefill_f32(const float *q, const float *k, const float *v, const float *
     if (rc != LA_OK) return rc;
     if (la::prefill_f32_grid(B, H, (int)d) > 0x7fffffff) return LA_ERR_UNSUPPORTED;
     if (N == 0) return LA_OK;
-    return hip_status(la::launch_prefill_f32(q, k, v, slopes, out, state, B, H, N, (int)d,
+    const la::SeqMap map = {nullptr, H, N, 0};
+    return hip_status(la::launch_prefill_f32(q, k, v, slopes, out, state, B, map, (int)d,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int la_prefill_varlen_f32(const float *q, const float *k, const float *v, const float *slopes,
+                          const int64_t *cu_seqlens, int64_t nseq, float *out, float *states,
+                          int64_t H, int64_t T, int64_t d, void *stream)
+{
+    const int rc = check_varlen(q, k, v, slopes, cu_seqlens, nseq, out, states, H, T, d, 4);
+    if (rc != LA_OK) return rc;
+    if (la::prefill_f32_grid(nseq, H, (int)d) > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+    if (T == 0) return LA_OK;
+    const la::SeqMap map = {cu_seqlens, H, 0, T};
+    return hip_status(la::launch_prefill_f32(q, k, v, slopes, out, states, nseq, map, (int)d,
                                              static_cast<hipStream_t>(stream)));
 }
 

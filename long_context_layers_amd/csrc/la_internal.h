@@ -8,13 +8,39 @@
 
 namespace la {
 
+// Where the tokens of one (sequence, head) slice of a prefill launch live.
+// Dense launches: q, k, v, out are [B][H][N][d] and slice (b, h) is rows
+// (b*H + h)*N .. +N.  Packed launches: they are [H][T][d] with sequence i in
+// rows cu[i] .. cu[i+1] of every head (offsets clamped into [0, T], so
+// malformed offsets still address only rows of the tensors).  In both cases
+// the state of slice (seq, h) is state[(seq*H + h)*d*d ..].
+struct SeqMap {
+    const int64_t *cu;    // null: dense launch
+    int64_t H, N, T;      // heads; dense sequence length; packed total length
+};
+
+__device__ __forceinline__ void seq_slice(const SeqMap &m, int64_t seq, int64_t h,
+                                          int64_t *row0, int64_t *len)
+{
+    if (!m.cu) {
+        *row0 = (seq * m.H + h) * m.N;
+        *len = m.N;
+        return;
+    }
+    const int64_t a = min(max(m.cu[seq], (int64_t)0), m.T);
+    const int64_t b = min(max(m.cu[seq + 1], a), m.T);
+    *row0 = h * m.T + a;
+    *len = b - a;
+}
+
 // ---- launchers (return the launch status; arguments already validated) ----
+// Prefill over `seqs` sequences (B for dense launches, nseq for packed ones).
 hipError_t launch_prefill_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                const float *slopes, uint16_t *out, float *state,
-                               int64_t B, int64_t H, int64_t N, int d, hipStream_t stream);
+                               int64_t seqs, const SeqMap &map, int d, hipStream_t stream);
 hipError_t launch_prefill_f32(const float *q, const float *k, const float *v,
                               const float *slopes, float *out, float *state,
-                              int64_t B, int64_t H, int64_t N, int d, hipStream_t stream);
+                              int64_t seqs, const SeqMap &map, int d, hipStream_t stream);
 hipError_t launch_decode_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                               const float *slopes, float *state, uint16_t *out,
                               int64_t B, int64_t H, int d, hipStream_t stream);
@@ -22,9 +48,9 @@ hipError_t launch_decode_f32(const float *q, const float *k, const float *v,
                              const float *slopes, float *state, float *out,
                              int64_t B, int64_t H, int d, hipStream_t stream);
 
-// number of workgroups one prefill launch uses (for the host-side grid check)
-int64_t prefill_bf16_grid(int64_t B, int64_t H, int d);
-int64_t prefill_f32_grid(int64_t B, int64_t H, int d);
+// number of workgroups one prefill launch over `seqs` sequences uses
+int64_t prefill_bf16_grid(int64_t seqs, int64_t H, int d);
+int64_t prefill_f32_grid(int64_t seqs, int64_t H, int d);
 
 // ---- device helpers ----
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {

@@ -135,9 +135,10 @@ struct Addr {                        // per-thread byte offsets inside a block
 // the descriptor's byte count), stores past N are dropped.
 constexpr uint32_t RSRC_WORD3 = 0x00020000u;   // raw buffer, 32-bit data format
 
-// tokens of the block starting at t0 (0 past the end)
+// tokens of the block starting at t0 (0 past the end, and 0 for t0 < 0, so a
+// buffer range built from it never reaches before the slice)
 __device__ __forceinline__ int block_len(int64_t t0, int64_t N) {
-    return (int)max((int64_t)0, min((int64_t)PC, N - t0));
+    return t0 < 0 ? 0 : (int)max((int64_t)0, min((int64_t)PC, N - t0));
 }
 
 template <int D>
@@ -480,7 +481,7 @@ __device__ void out1_wave(const Ctx<D> &cx, Smem<D> &sm, int lane)
         step(blk + 1, std::integral_constant<int, 1>());
     }
     __syncthreads();                            // W3's part of the last block is visible
-    finish_prev(cx.nblk - 1, (int)((cx.nblk - 1) & 1));
+    if (cx.nblk > 0) finish_prev(cx.nblk - 1, (int)((cx.nblk - 1) & 1));   // (empty sequence: none)
 }
 
 // W3: tokens 32..63, off-diagonal scores P^T(0,1) and their V^T P^T part
@@ -514,7 +515,7 @@ template <int D>
 __global__ __launch_bounds__(NTHREADS) void prefill_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const float *__restrict__ slopes,
-    uint16_t *__restrict__ out, float *__restrict__ state, int64_t H, int64_t N)
+    uint16_t *__restrict__ out, float *__restrict__ state, SeqMap map)
 {
     constexpr int NJ = D / PJ;            // workgroups per head
     __shared__ Smem<D> sm;
@@ -527,18 +528,21 @@ __global__ __launch_bounds__(NTHREADS) void prefill_bf16_kernel(
     const int64_t nwg = gridDim.x;
     int64_t lid = blockIdx.x;
     if (nwg % 8 == 0) lid = (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8;
-    const int64_t bh = lid / NJ;
+    const int64_t bh = lid / NJ;          // sequence * H + head
+    int64_t row0, N;
+    seq_slice(map, bh / map.H, bh % map.H, &row0, &N);
 
     Ctx<D> cx;
     cx.j0 = (int)(lid % NJ) * PJ;
-    cx.s = slopes[bh % H];
+    cx.s = slopes[bh % map.H];
     cx.N = N;
-    // blocks processed: a multiple of NSET (trailing empty blocks are no-ops)
+    // blocks processed: a multiple of NSET (trailing empty blocks are no-ops;
+    // an empty sequence leaves its state unchanged)
     cx.nblk = ((N + PC - 1) / PC + NSET - 1) / NSET * NSET;
-    cx.qh = q + bh * N * D;
-    cx.kh = k + bh * N * D;
-    cx.vh = v + bh * N * D;
-    cx.oh = out + bh * N * D;
+    cx.qh = q + row0 * D;
+    cx.kh = k + row0 * D;
+    cx.vh = v + row0 * D;
+    cx.oh = out + row0 * D;
 
     const int lane = tid % 64;
     switch (wave) {
@@ -552,15 +556,16 @@ __global__ __launch_bounds__(NTHREADS) void prefill_bf16_kernel(
 
 }  // namespace
 
-int64_t prefill_bf16_grid(int64_t B, int64_t H, int d) { return B * H * (d / PJ); }
+int64_t prefill_bf16_grid(int64_t seqs, int64_t H, int d) { return seqs * H * (d / PJ); }
 
 hipError_t launch_prefill_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                const float *slopes, uint16_t *out, float *state,
-                               int64_t B, int64_t H, int64_t N, int d, hipStream_t stream)
+                               int64_t seqs, const SeqMap &map, int d, hipStream_t stream)
 {
-    const dim3 grid((unsigned)prefill_bf16_grid(B, H, d)), block(NTHREADS);
+    const dim3 grid((unsigned)prefill_bf16_grid(seqs, map.H, d)), block(NTHREADS);
+    SeqMap m = map;
     void *args[] = {(void *)&q, (void *)&k, (void *)&v, (void *)&slopes,
-                    (void *)&out, (void *)&state, (void *)&H, (void *)&N};
+                    (void *)&out, (void *)&state, (void *)&m};
     const void *fn = d == 64 ? (const void *)prefill_bf16_kernel<64>
                              : (const void *)prefill_bf16_kernel<128>;
     return hipLaunchKernel(fn, grid, block, args, 0, stream);

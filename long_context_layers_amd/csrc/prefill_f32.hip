@@ -11,8 +11,8 @@
 // sequence piece, joined through the carried [B,H,D,D] state (Ling and Ring
 // 2.6 Technical Report, §4.1.1 and Fig. 10), applied block after block.
 //
-// One workgroup per (b, h, 32-column slice of v/S/O); the slice's state stays
-// in LDS for the whole sequence.  Not a throughput kernel: the fp32 path
+// One workgroup per (sequence, head, 32-column slice of v/S/O) of a dense or
+// packed launch; the slice's state stays in LDS for the whole sequence.  Not a throughput kernel: the fp32 path
 // serves small fp32 problems and correctness checks.
 #include "la_internal.h"
 
@@ -27,7 +27,7 @@ template <int D>
 __global__ __launch_bounds__(FT) void prefill_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ slopes, float *__restrict__ out, float *__restrict__ state,
-    int64_t H, int64_t N)
+    SeqMap map)
 {
     constexpr int NJ = D / FJ;
     __shared__ float Qs[FC][D + 1];
@@ -38,16 +38,18 @@ __global__ __launch_bounds__(FT) void prefill_f32_kernel(
     __shared__ float pw[FC + 1];          // lambda^n, n = 0..FC
 
     const int tid = threadIdx.x;
-    const int64_t bh = blockIdx.x / NJ;
+    const int64_t bh = blockIdx.x / NJ;          // sequence * H + head
     const int j0 = (blockIdx.x % NJ) * FJ;
-    const float s = slopes[bh % H];
+    const float s = slopes[bh % map.H];
+    int64_t row0, N;
+    seq_slice(map, bh / map.H, bh % map.H, &row0, &N);
     if (tid <= FC) pw[tid] = decay_pow(s, tid);
 
     float *St = state + bh * D * D;
     for (int e = tid; e < D * FJ; e += FT) Ss[e / FJ][e % FJ] = St[(e / FJ) * D + j0 + e % FJ];
 
-    const float *qb = q + bh * N * D, *kb = k + bh * N * D, *vb = v + bh * N * D;
-    float *ob = out + bh * N * D;
+    const float *qb = q + row0 * D, *kb = k + row0 * D, *vb = v + row0 * D;
+    float *ob = out + row0 * D;
 
     for (int64_t t0 = 0; t0 < N; t0 += FC) {
         const int c = (int)min((int64_t)FC, N - t0);
@@ -100,15 +102,16 @@ __global__ __launch_bounds__(FT) void prefill_f32_kernel(
 
 }  // namespace
 
-int64_t prefill_f32_grid(int64_t B, int64_t H, int d) { return B * H * (d / FJ); }
+int64_t prefill_f32_grid(int64_t seqs, int64_t H, int d) { return seqs * H * (d / FJ); }
 
 hipError_t launch_prefill_f32(const float *q, const float *k, const float *v,
                               const float *slopes, float *out, float *state,
-                              int64_t B, int64_t H, int64_t N, int d, hipStream_t stream)
+                              int64_t seqs, const SeqMap &map, int d, hipStream_t stream)
 {
-    const dim3 grid((unsigned)prefill_f32_grid(B, H, d)), block(FT);
+    const dim3 grid((unsigned)prefill_f32_grid(seqs, map.H, d)), block(FT);
+    SeqMap m = map;
     void *args[] = {(void *)&q, (void *)&k, (void *)&v, (void *)&slopes,
-                    (void *)&out, (void *)&state, (void *)&H, (void *)&N};
+                    (void *)&out, (void *)&state, (void *)&m};
     const void *fn = d == 64 ? (const void *)prefill_f32_kernel<64>
                              : (const void *)prefill_f32_kernel<128>;
     return hipLaunchKernel(fn, grid, block, args, 0, stream);

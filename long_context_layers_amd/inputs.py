@@ -21,6 +21,14 @@ Recipe (every workload):
   * slopes ``s_h = 2**(-8 (h+1) / H)`` for h = 0..H-1, computed in fp64 and
     stored fp32 (so lambda_h = exp(-s_h); h = 0 decays fastest).
 
+Packed variable-length batches (``make_varlen``): sub-sequence lengths come
+from ``varlen_lengths`` (log-uniform between ``lo`` and ``hi`` from a CPU
+generator, the last piece cut to fit the total), then q, k, v are drawn as
+the dense recipe with B = 1 over all T packed rows (shape ``[H, T, d]``),
+then the per-sequence initial states ``[nseq, H, d, d]``.  This stands in for
+packed training samples made of many short sub-sequences (the report's
+§4.1.2); no dataset is involved.
+
 Drawing on the GPU uses torch's device generator (fast for the 256K
 workload); drawing on the CPU uses torch's CPU generator.  The two give
 different numbers for the same seed; each parity check draws once and hands
@@ -64,7 +72,13 @@ WORKLOADS = {
     "decode_b256": Workload("decode_b256", 256, 64, 0, 128, torch.bfloat16, 1004,
                             init_state=True, decode_steps=64,
                             note="batched decode, 64 steps of fresh tokens"),
+    "varlen_256k": Workload("varlen_256k", 1, 64, 262144, 128, torch.bfloat16, 1005,
+                            init_state=True,
+                            note="256K packed tokens in sub-sequences of 256..16384 tokens "
+                                 "(log-uniform), each with its own random fp32 state"),
 }
+
+VARLEN_RANGE = (256, 16384)        # sub-sequence lengths of the varlen_256k workload
 
 
 def slopes(H: int, device="cpu") -> torch.Tensor:
@@ -140,9 +154,59 @@ def make_decode(B: int, H: int, d: int, steps: int, dtype=torch.bfloat16, seed: 
     return DecodeInputs(q, k, v, slopes(H, device), st)
 
 
+def varlen_lengths(total: int, seed: int, lo: int = VARLEN_RANGE[0],
+                   hi: int = VARLEN_RANGE[1]) -> list:
+    """Seeded sub-sequence lengths summing to ``total``: log-uniform in
+    [lo, hi], the last one cut to fit."""
+    g = torch.Generator().manual_seed(seed)
+    lens, rem = [], total
+    while rem > 0:
+        u = float(torch.rand((), generator=g, dtype=torch.float64))
+        n = int(round(math.exp(math.log(lo) + u * (math.log(hi) - math.log(lo)))))
+        n = max(1, min(n, rem))
+        lens.append(n)
+        rem -= n
+    return lens
+
+
+@dataclass
+class VarlenInputs:
+    q: torch.Tensor                # [H,T,d]: sequence i is rows cu[i]:cu[i+1] of every head
+    k: torch.Tensor
+    v: torch.Tensor
+    cu_seqlens: torch.Tensor       # [nseq+1] int64
+    slopes: torch.Tensor
+    states: torch.Tensor           # [nseq,H,d,d] fp32 initial states (zeros if none)
+    lens: list = field(default_factory=list)
+
+
+def make_varlen(H: int, lens, d: int, dtype=torch.bfloat16, seed: int = 0,
+                init_state: bool = False, device="cpu") -> VarlenInputs:
+    lens = [int(n) for n in lens]
+    T = sum(lens)
+    g = _gen(device, seed)
+    sc = 1.0 / math.sqrt(d)
+    q = _draw_heads(g, 1, H, T, d, sc, dtype, device)[0]
+    k = _draw_heads(g, 1, H, T, d, sc, dtype, device)[0]
+    v = _draw_heads(g, 1, H, T, d, sc, dtype, device)[0]
+    if init_state:
+        st = _draw_heads(g, len(lens), H, d, d, 0.1, torch.float32, device)
+    else:
+        st = torch.zeros((len(lens), H, d, d), dtype=torch.float32, device=device)
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    return VarlenInputs(q, k, v, torch.tensor(cu, dtype=torch.int64, device=device),
+                        slopes(H, device), st, lens)
+
+
 def make_workload(name: str, device="cpu", N: Optional[int] = None):
-    """Inputs of a named workload; ``N`` overrides the sequence length."""
+    """Inputs of a named workload; ``N`` overrides the sequence length (the
+    total packed length for a varlen workload)."""
     w = WORKLOADS[name]
+    if name.startswith("varlen"):
+        lens = varlen_lengths(N if N is not None else w.N, w.seed)
+        return make_varlen(w.H, lens, w.d, w.dtype, w.seed, w.init_state, device)
     if w.decode_steps:
         return make_decode(w.B, w.H, w.d, w.decode_steps, w.dtype, w.seed, device)
     return make_prefill(w.B, w.H, N if N is not None else w.N, w.d, w.dtype, w.seed,

@@ -15,6 +15,9 @@ Three independent statements of it live here:
 
 * ``prefill`` / ``decode_step``: the recurrence, in plain C (``la_oracle.c``),
   fp64, OpenMP over the B*H slices.  This is the oracle the GPU is compared to.
+* ``prefill_varlen``: a packed batch of independent sequences (the report's
+  §4.1.2: packed sub-sequences, each attending only within itself), i.e. the
+  same recurrence restarted from each sequence's own state.
 * ``quadratic``: the definition's double sum written out as a masked
   decay-weighted score matrix (NumPy, fp64, tiny sizes only).
 * ``blockwise``: the block decomposition the GPU kernels follow (intra-block
@@ -99,6 +102,36 @@ def prefill(q, k, v, slopes, state_init=None, want_out: bool = True):
     if r < 0:
         raise ValueError("la_oracle_prefill rejected its arguments")
     last_threads = min(r, B * H)
+    return out, st
+
+
+def prefill_varlen(q, k, v, slopes, cu_seqlens, states_init=None, want_out: bool = True):
+    """Packed prefill over independent sequences, fp64.
+
+    q, k, v: [H,T,d]; cu_seqlens: nseq+1 non-decreasing offsets, cu[0] = 0,
+    cu[nseq] = T; states_init: [nseq,H,d,d] or None (zeros).  Sequence i is
+    rows cu[i]:cu[i+1] of every head; it runs the recurrence of ``prefill``
+    from its own initial state and never sees another sequence's tokens.
+    Returns (out [H,T,d] or None, final states [nseq,H,d,d]).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    H, T, d = q.shape
+    cu = [int(x) for x in np.asarray(cu_seqlens).reshape(-1)]
+    nseq = len(cu) - 1
+    if nseq < 1 or cu[0] != 0 or cu[-1] != T or any(a > b for a, b in zip(cu, cu[1:])):
+        raise ValueError("cu_seqlens must rise from 0 to T")
+    st = np.zeros((nseq, H, d, d)) if states_init is None else _f64(states_init).copy()
+    assert st.shape == (nseq, H, d, d)
+    out = np.zeros((H, T, d)) if want_out else None
+    for i in range(nseq):
+        a, b = cu[i], cu[i + 1]
+        if a == b:
+            continue                                   # an empty sequence keeps its state
+        o, fin = prefill(q[None, :, a:b], k[None, :, a:b], v[None, :, a:b], slopes,
+                         st[i:i + 1], want_out)
+        st[i] = fin[0]
+        if want_out:
+            out[:, a:b] = o[0]
     return out, st
 
 

@@ -155,3 +155,51 @@ def test_missing_library_fails_loudly(tmp_path):
             binding.load_library(str(tmp_path / "nope.so"))
         finally:
             binding._lib = saved
+
+
+VARLEN = ["la_prefill_varlen", "la_prefill_varlen_f32"]
+
+
+def _varlen_args(**kw):
+    a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, slopes=FAKE + 0x300000,
+             cu=FAKE + 0x380000, nseq=3, out=FAKE + 0x400000, states=FAKE + 0x500000,
+             H=2, T=0, d=64, stream=None)
+    a.update(kw)
+    return [a[n] for n in ("q", "k", "v", "slopes", "cu", "nseq", "out", "states", "H", "T", "d",
+                           "stream")]
+
+
+@pytest.mark.parametrize("fn", VARLEN)
+def test_varlen_empty_batch_is_a_noop(lib, fn):
+    # T == 0: every sequence is empty; returns before any HIP call (the
+    # offsets are never read on the host)
+    assert getattr(lib, fn)(*_varlen_args(T=0)) == LA_OK
+    assert getattr(lib, fn)(*_varlen_args(T=0, q=None, k=None, v=None, out=None)) == LA_OK
+
+
+@pytest.mark.parametrize("fn", VARLEN)
+@pytest.mark.parametrize("bad,code", [
+    (dict(cu=None), LA_ERR_INVALID_ARG), (dict(cu=FAKE + 4), LA_ERR_INVALID_ARG),
+    (dict(nseq=0), LA_ERR_INVALID_ARG), (dict(nseq=-2), LA_ERR_INVALID_ARG),
+    (dict(H=0), LA_ERR_INVALID_ARG), (dict(T=-1), LA_ERR_INVALID_ARG),
+    (dict(slopes=None), LA_ERR_INVALID_ARG), (dict(states=None), LA_ERR_INVALID_ARG),
+    (dict(d=32), LA_ERR_UNSUPPORTED), (dict(d=256), LA_ERR_UNSUPPORTED),
+    (dict(q=FAKE + 2), LA_ERR_INVALID_ARG), (dict(states=FAKE + 8), LA_ERR_INVALID_ARG),
+    (dict(nseq=2 ** 33, H=2 ** 31), LA_ERR_INVALID_ARG),     # state size overflows
+    (dict(nseq=2 ** 26, H=64), LA_ERR_UNSUPPORTED),          # grid above 2^31 - 1
+])
+def test_varlen_rejects_bad_arguments(lib, fn, bad, code):
+    # T = 0 in every case: even a missing check could not reach a launch
+    assert getattr(lib, fn)(*_varlen_args(**bad)) == code
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("fn", VARLEN)
+@pytest.mark.parametrize("bad", [
+    dict(out=FAKE),                # out aliases q
+    dict(out=FAKE + 0x500000),     # out aliases the states
+    dict(H=2 ** 62),               # size overflow (H * T * d)
+    dict(q=None), dict(v=None), dict(out=None),   # null activations, T > 0
+])
+def test_varlen_rejects_aliasing_and_overflow(lib, fn, bad):
+    assert getattr(lib, fn)(*_varlen_args(T=1, **bad)) == LA_ERR_INVALID_ARG

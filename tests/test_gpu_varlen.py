@@ -1,0 +1,147 @@
+"""GPU parity for packed variable-length prefill (la_prefill_varlen[_f32])
+through the C ABI: against the fp64 packed oracle on the same seeded bytes
+(bar as for dense prefill: 2e-2 bf16, 1e-3 fp32, max over (sequence, head)
+of the relative L2 error of outputs and final states), and bitwise against
+dense launches over each sequence alone."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_layers_amd import binding, inputs
+from tests.gpu_util import BF16_TOL, F32_TOL, log, np64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    binding.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def run_varlen(inp):
+    st = inp.states.clone()
+    out = binding.prefill_varlen(inp.q, inp.k, inp.v, inp.slopes, inp.cu_seqlens, st)
+    torch.cuda.synchronize()
+    return out, st
+
+
+def max_err(out, st, o_ref, s_ref, cu, seqs=None):
+    """max over (sequence, head) of rel-L2 for outputs and states."""
+    eo = es = 0.0
+    out, st = np64(out), np64(st)
+    for i in (range(len(cu) - 1) if seqs is None else seqs):
+        a, b = int(cu[i]), int(cu[i + 1])
+        if b > a:
+            eo = max(eo, oracle.rel_l2(out[:, a:b], o_ref[:, a:b]))
+        es = max(es, oracle.rel_l2(st[i], s_ref[i]))
+    return eo, es
+
+
+MIXED = [0, 1, 63, 64, 65, 130, 0, 1000, 7, 257]
+
+
+@pytest.mark.parametrize("dtype,tol", [(torch.bfloat16, BF16_TOL), (torch.float32, F32_TOL)])
+@pytest.mark.parametrize("d", [64, 128])
+def test_varlen_mixed_lengths(dtype, tol, d):
+    log(f"varlen mixed lengths {MIXED} H4 d{d} {dtype}")
+    inp = inputs.make_varlen(4, MIXED, d, dtype, seed=71 + d, init_state=True, device=DEV)
+    out, st = run_varlen(inp)
+    o_ref, s_ref = oracle.prefill_varlen(np64(inp.q), np64(inp.k), np64(inp.v), np64(inp.slopes),
+                                         inp.cu_seqlens.cpu().numpy(), np64(inp.states))
+    eo, es = max_err(out, st, o_ref, s_ref, inp.cu_seqlens.cpu().numpy())
+    log(f"  out rel-L2 {eo:.3e}  state rel-L2 {es:.3e}  (tol {tol:g})")
+    assert eo <= tol and es <= tol
+    # empty sequences keep their state bitwise
+    for i, n in enumerate(MIXED):
+        if n == 0:
+            assert torch.equal(st[i], inp.states[i])
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_varlen_equals_dense_per_sequence_bitwise(dtype):
+    lens = [5, 64, 200, 1, 129]
+    log(f"varlen vs dense launches per sequence, lengths {lens}, H3 d128 {dtype}")
+    inp = inputs.make_varlen(3, lens, 128, dtype, seed=81, init_state=True, device=DEV)
+    out, st = run_varlen(inp)
+    cu = inp.cu_seqlens.cpu().tolist()
+    for i in range(len(lens)):
+        a, b = cu[i], cu[i + 1]
+        q, k, v = (t[:, a:b].unsqueeze(0).contiguous() for t in (inp.q, inp.k, inp.v))
+        s1 = inp.states[i:i + 1].clone()
+        o1 = binding.prefill(q, k, v, inp.slopes, s1)
+        torch.cuda.synchronize()
+        assert torch.equal(o1[0], out[:, a:b]), f"sequence {i}: outputs differ"
+        assert torch.equal(s1[0], st[i]), f"sequence {i}: states differ"
+
+
+def test_varlen_single_sequence_equals_dense():
+    log("varlen with one sequence == dense prefill (B1 H8 N777 d128 bf16)")
+    inp = inputs.make_varlen(8, [777], 128, torch.bfloat16, seed=82, init_state=True, device=DEV)
+    out, st = run_varlen(inp)
+    s1 = inp.states.clone()
+    o1 = binding.prefill(inp.q.unsqueeze(0), inp.k.unsqueeze(0), inp.v.unsqueeze(0), inp.slopes, s1)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[0], out) and torch.equal(s1, st)
+
+
+def test_varlen_all_sequences_empty_is_a_noop():
+    inp = inputs.make_varlen(2, [0, 0, 0], 64, torch.bfloat16, seed=83, init_state=True, device=DEV)
+    st = inp.states.clone()
+    out = binding.prefill_varlen(inp.q, inp.k, inp.v, inp.slopes, inp.cu_seqlens, st)
+    torch.cuda.synchronize()
+    assert out.shape == (2, 0, 64) and torch.equal(st, inp.states)
+
+
+def test_varlen_256k_workload_sampled():
+    # the packed 256K launch the benchmark times; the oracle recomputes the
+    # shortest, the longest and the last sequence on heads 0 and 63
+    inp = inputs.make_workload("varlen_256k", device=DEV)
+    lens = inp.lens
+    log(f"varlen_256k: H64 T262144 d128 bf16, {len(lens)} sequences ({min(lens)}..{max(lens)})")
+    out, st = run_varlen(inp)
+    cu = inp.cu_seqlens.cpu().tolist()
+    seqs = sorted({int(np.argmin(lens)), int(np.argmax(lens)), len(lens) - 1})
+    heads = torch.tensor([0, 63], device=DEV)
+    worst = 0.0
+    for i in seqs:
+        a, b = cu[i], cu[i + 1]
+        q, k, v = (t.index_select(0, heads)[:, a:b] for t in (inp.q, inp.k, inp.v))
+        o_ref, s_ref = oracle.prefill(np64(q)[None], np64(k)[None], np64(v)[None],
+                                      np64(inp.slopes.index_select(0, heads)),
+                                      np64(inp.states[i].index_select(0, heads))[None])
+        eo = oracle.rel_l2(np64(out.index_select(0, heads)[:, a:b]), o_ref[0])
+        es = oracle.rel_l2(np64(st[i].index_select(0, heads)), s_ref[0])
+        log(f"  sequence {i} ({b - a} tokens): out {eo:.3e} state {es:.3e}")
+        worst = max(worst, eo, es)
+    assert worst <= BF16_TOL
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_varlen_empty_sequences_write_nothing_outside(dtype):
+    # regression: an empty sequence (here first, in the middle and last) must
+    # not write any output row; out sits inside a larger buffer whose guard
+    # regions before and after must keep their sentinel values
+    lens = [0, 70, 0, 33, 0]
+    H, d = 2, 128
+    log(f"varlen guard regions around out, lengths {lens}, {dtype}")
+    inp = inputs.make_varlen(H, lens, d, dtype, seed=84, init_state=True, device=DEV)
+    T = sum(lens)
+    guard = 64 * 64 * d
+    big = torch.full((guard + H * T * d + guard,), 7.0, dtype=dtype, device=DEV)
+    out = big[guard:guard + H * T * d].view(H, T, d)
+    st = inp.states.clone()
+    binding.prefill_varlen(inp.q, inp.k, inp.v, inp.slopes, inp.cu_seqlens, st, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(big[:guard] == 7.0) and torch.all(big[guard + H * T * d:] == 7.0)
+    o_ref, s_ref = oracle.prefill_varlen(np64(inp.q), np64(inp.k), np64(inp.v), np64(inp.slopes),
+                                         inp.cu_seqlens.cpu().numpy(), np64(inp.states))
+    tol = BF16_TOL if dtype == torch.bfloat16 else F32_TOL
+    eo, es = max_err(out, st, o_ref, s_ref, inp.cu_seqlens.cpu().numpy())
+    assert eo <= tol and es <= tol

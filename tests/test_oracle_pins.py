@@ -248,3 +248,79 @@ def test_pins_detect_planted_mistakes(mutation):
     assert oracle.rel_l2(good, o_q[0, 0]) <= 1e-12
     bad = _mutant_recurrence(q[0, 0], k[0, 0], v[0, 0], lam, S0[0, 0], mutation)
     assert oracle.rel_l2(bad, o_q[0, 0]) > 1e-3
+
+
+# --- packed variable-length batches (the report's §4.1.2: packed
+# sub-sequences each attend only within themselves) -------------------------
+
+def _packed(rng, H, lens, d):
+    T = sum(lens)
+    q = rng.standard_normal((H, T, d)) / math.sqrt(d)
+    k = rng.standard_normal((H, T, d)) / math.sqrt(d)
+    v = rng.standard_normal((H, T, d))
+    S0 = 0.1 * rng.standard_normal((len(lens), H, d, d))
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    return q, k, v, S0, cu
+
+
+def test_varlen_matches_quadratic_per_sequence():
+    # each sequence against the double sum on its own rows from its own state
+    rng = np.random.default_rng(31)
+    lens = [0, 1, 5, 17, 0, 9]
+    q, k, v, S0, cu = _packed(rng, len(LAMS), lens, 4)
+    s = slopes_for(LAMS)
+    o, f = oracle.prefill_varlen(q, k, v, s, cu, S0)
+    for i in range(len(lens)):
+        a, b = cu[i], cu[i + 1]
+        oq, fq = oracle.quadratic(q[None, :, a:b], k[None, :, a:b], v[None, :, a:b], s, S0[i:i + 1])
+        if b > a:
+            assert oracle.rel_l2(o[:, a:b], oq[0]) <= 1e-12
+        assert oracle.rel_l2(f[i], fq[0]) <= 1e-12
+
+
+def test_varlen_with_chained_states_is_one_dense_run():
+    # start sequence i from the dense state after cu[i] tokens (double sum on
+    # the prefix): the packed run must then reproduce the dense definition
+    rng = np.random.default_rng(32)
+    lens = [3, 0, 11, 6, 1]
+    q, k, v, S0, cu = _packed(rng, 3, lens, 5)
+    s = slopes_for([0.3, 0.9, 1.0])
+    chained = np.zeros_like(S0)
+    for i in range(len(lens)):
+        _, fp = oracle.quadratic(q[None, :, :cu[i]], k[None, :, :cu[i]], v[None, :, :cu[i]], s, S0[:1])
+        chained[i] = fp[0]
+    o, f = oracle.prefill_varlen(q, k, v, s, cu, chained)
+    od, fd = oracle.quadratic(q[None], k[None], v[None], s, S0[:1])
+    assert oracle.rel_l2(o, od[0]) <= 1e-12
+    assert oracle.rel_l2(f[-1], fd[0]) <= 1e-12
+
+
+def test_varlen_empty_sequences_keep_their_state():
+    rng = np.random.default_rng(33)
+    q, k, v, S0, cu = _packed(rng, 2, [0, 4, 0], 3)
+    _, f = oracle.prefill_varlen(q, k, v, slopes_for([0.5, 0.9]), cu, S0)
+    assert np.array_equal(f[0], S0[0]) and np.array_equal(f[2], S0[2])
+    assert not np.array_equal(f[1], S0[1])
+
+
+def test_varlen_pin_detects_a_missing_reset():
+    # planted mistake: one dense run over the packed tokens (state carried
+    # across sequence boundaries) must fail the per-sequence double sum
+    rng = np.random.default_rng(34)
+    lens = [6, 7]
+    q, k, v, S0, cu = _packed(rng, 1, lens, 4)
+    s = slopes_for([0.9])
+    leaky, _ = oracle.prefill(q[None], k[None], v[None], s, S0[:1])
+    a, b = cu[1], cu[2]
+    oq, _ = oracle.quadratic(q[None, :, a:b], k[None, :, a:b], v[None, :, a:b], s, S0[1:2])
+    assert oracle.rel_l2(leaky[0][:, a:b], oq[0]) > 1e-3
+    good, _ = oracle.prefill_varlen(q, k, v, s, cu, S0)
+    assert oracle.rel_l2(good[:, a:b], oq[0]) <= 1e-12
+
+
+def test_varlen_rejects_bad_offsets():
+    rng = np.random.default_rng(35)
+    q, k, v, S0, _ = _packed(rng, 1, [4, 4], 2)
+    for cu in ([0, 9, 8], [1, 4, 8], [0, 4, 7], [0, 8, 4]):
+        with pytest.raises(ValueError):
+            oracle.prefill_varlen(q, k, v, slopes_for([0.5]), np.array(cu), None)

@@ -135,6 +135,35 @@ int la_decode_step_f32(const float *q, const float *k, const float *v, const flo
                        float *state, float *out,
                        int64_t B, int64_t H, int64_t d, void *stream);
 
+/*
+ * Multi-token decode (draft verification): T tokens per sequence, 1 <= T <= 8,
+ * applied in order from the carried state.
+ *   q, k, v     [B,H,T,d] bf16, read only (token t of sequence b, head h).
+ *   n_commit    [B] int32, DEVICE pointer, or NULL (= T for every sequence):
+ *               how many leading tokens of sequence b are folded into the
+ *               stored state.  Values outside [0, T] are clamped.
+ *   state       [B,H,d,d] fp32, IN/OUT: on exit the state after n_commit[b]
+ *               tokens (unchanged for 0).
+ *   out         [B,H,T,d] bf16, written for every token:
+ *               o_t = q_t S_t,  S_t = lambda S_{t-1} + k_t^T v_t,
+ *               S_{-1} = the state on entry (whatever n_commit says).
+ * With n_commit = T this equals T calls of la_decode_step (and a prefill of
+ * the T tokens) up to rounding.  T > 8 gives LA_ERR_UNSUPPORTED, T < 1
+ * LA_ERR_INVALID_ARG.  Source: serving with multi-token prediction (the
+ * report's §4.3, Table 7 and Fig. 12) and its Appendix B (four speculative
+ * steps, acceptance lengths of about 2.7 to 3.3 in Table 8): several draft
+ * tokens are scored against one carried state and only the accepted prefix
+ * may advance it.
+ */
+int la_decode_multi(const void *q, const void *k, const void *v, const float *slopes,
+                    const int32_t *n_commit, float *state, void *out,
+                    int64_t B, int64_t H, int64_t T, int64_t d, void *stream);
+
+/* Multi-token decode with fp32 q, k, v, out: same semantics. */
+int la_decode_multi_f32(const float *q, const float *k, const float *v, const float *slopes,
+                        const int32_t *n_commit, float *state, float *out,
+                        int64_t B, int64_t H, int64_t T, int64_t d, void *stream);
+
 /* Static, NUL-terminated description of a status code ("unknown status" for
  * values outside la_status).  Never NULL; the caller must not free it. */
 const char *la_status_string(int status);

@@ -3,10 +3,10 @@
 The layer's kernels live in the HIP library ``lib/liblightning_attn.so``
 (C ABI: ``include/lightning_attn.h``); this package is its thin binding.
 
-    from long_context_layers_amd import prefill, prefill_varlen, decode_step
+    from long_context_layers_amd import prefill, prefill_varlen, decode_step, decode_multi
 """
-from .binding import (prefill, prefill_varlen, decode_step, load_library,  # noqa: F401
-                      status_string, LightningAttnError)
+from .binding import (prefill, prefill_varlen, decode_step, decode_multi,  # noqa: F401
+                      load_library, status_string, LightningAttnError)
 
-__all__ = ["prefill", "prefill_varlen", "decode_step", "load_library", "status_string",
-           "LightningAttnError"]
+__all__ = ["prefill", "prefill_varlen", "decode_step", "decode_multi", "load_library",
+           "status_string", "LightningAttnError"]

@@ -27,6 +27,8 @@ SIGNATURES = {
     "la_prefill_varlen": ([_P, _P, _P, _P, _P, _I64, _P, _P, _I64, _I64, _I64, _P], _INT),
     "la_prefill_varlen_f32": ([_P, _P, _P, _P, _P, _I64, _P, _P, _I64, _I64, _I64, _P], _INT),
     "la_decode_step": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], _INT),
+    "la_decode_multi": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], _INT),
+    "la_decode_multi_f32": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], _INT),
     "la_decode_step_f32": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], _INT),
     "la_status_string": ([_INT], ctypes.c_char_p),
     "la_abi_version": ([], _INT),
@@ -191,4 +193,43 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: torch
         rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), slopes.data_ptr(), state.data_ptr(),
                 out.data_ptr(), B, H, d, _stream(dev))
     _check(rc, "la_decode_step" if dt == torch.bfloat16 else "la_decode_step_f32")
+    return out
+
+
+def decode_multi(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: torch.Tensor,
+                 state: torch.Tensor, n_commit: Optional[torch.Tensor] = None,
+                 out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """T draft tokens per sequence (1 <= T <= 8) from the carried state.
+
+    q, k, v: [B,H,T,d] bf16 or fp32; slopes [H] fp32; state [B,H,d,d] fp32,
+    updated in place to the state after n_commit[b] tokens (all T if n_commit
+    is None); n_commit: [B] int32 on the same GPU.  Returns out [B,H,T,d] with
+    o_t = q_t S_t for every token.
+    """
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a [B,H,T,d] tensor")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("decode_multi runs on GPU tensors only (no CPU path)")
+    B, H, T, d = q.shape
+    dt = q.dtype
+    if dt not in (torch.bfloat16, torch.float32):
+        raise TypeError("q/k/v must be bfloat16 or float32")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n, dt, dev, (B, H, T, d))
+    _need(slopes, "slopes", torch.float32, dev, (H,))
+    _need(state, "state", torch.float32, dev, (B, H, d, d))
+    if n_commit is not None:
+        _need(n_commit, "n_commit", torch.int32, dev, (B,))
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _need(out, "out", dt, dev, (B, H, T, d))
+    lib = load_library()
+    fn = lib.la_decode_multi if dt == torch.bfloat16 else lib.la_decode_multi_f32
+    with torch.cuda.device(dev):
+        rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), slopes.data_ptr(),
+                None if n_commit is None else n_commit.data_ptr(), state.data_ptr(),
+                out.data_ptr(), B, H, T, d, _stream(dev))
+    _check(rc, "la_decode_multi" if dt == torch.bfloat16 else "la_decode_multi_f32")
     return out

@@ -1,5 +1,6 @@
-// decode.hip — one recurrent decode step per sequence:
+// decode.hip — recurrent decode steps per sequence:
 //   S' = lambda S + k^T v   (in place, fp32),   o = q S'
+// one token per call (decode_kernel) or up to 8 (decode_multi_kernel).
 // (Ling and Ring 2.6 Technical Report, §4.1.1: linear attention as an
 // RNN-style recurrence over a per-(batch, head) D x D state; serving runs it
 // one token per step, §4.3 / Fig. 12.)
@@ -89,6 +90,105 @@ __global__ __launch_bounds__(DT) void decode_kernel(
     }
 }
 
+// Several tokens per sequence (multi-token decode / draft verification): for
+// t = 0..NT-1, S = lambda S + k_t^T v_t and o_t = q_t S, all in registers; the
+// state goes back to HBM right after token ncommit-1 (ncommit = n_commit[b]
+// clamped to [0, NT], NT if n_commit is null), so tokens past the committed
+// prefix produce outputs but never reach the stored state.  One state read
+// and at most one write serve all NT tokens; the NT partial-sum reductions
+// share one LDS pass.
+constexpr int MAXT = 8;   // tokens per sequence and call
+
+template <typename T, int D>
+__global__ __launch_bounds__(DT) void decode_multi_kernel(
+    const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
+    const float *__restrict__ slopes, const int32_t *__restrict__ n_commit,
+    float *__restrict__ state, T *__restrict__ out, int64_t H, int NT)
+{
+    constexpr int CG = D / 4;         // float4 column groups per row
+    constexpr int RG = DT / CG;       // row groups
+    constexpr int RPT = D / RG;       // rows per thread
+    __shared__ float red[RG][MAXT][D];
+    __shared__ float qk[MAXT][2][D];
+
+    const int tid = threadIdx.x;
+    const int64_t bh = blockIdx.x;
+    const float lam = decay_pow(slopes[bh % H], 1);
+    const int ncommit = n_commit ? min(max(n_commit[bh / H], 0), NT) : NT;
+    const int cg = tid % CG, rg = tid / CG;
+
+    f32x4 *S = reinterpret_cast<f32x4 *>(state + bh * D * D);
+    f32x4 s[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) s[m] = __builtin_nontemporal_load(&S[(rg + RG * m) * CG + cg]);
+
+    const int64_t a0 = bh * NT * D;   // first activation element of this (b, h)
+    for (int e = tid; e < NT * D; e += DT) {
+        qk[e / D][0][e % D] = load_act<T>(q + a0 + e);
+        qk[e / D][1][e % D] = load_act<T>(k + a0 + e);
+    }
+    float vv[MAXT][4];
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vv[t][j] = 0.f;
+        if (t < NT) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) vv[t][j] = load_act<T>(v + a0 + t * D + 4 * cg + j);
+        }
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int t = 0; t < MAXT; ++t) {
+        if (t >= NT) break;
+        float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            const int i = rg + RG * m;
+            const float ki = qk[t][1][i], qi = qk[t][0][i];
+            f32x4 x = s[m];
+            x.x = fmaf(lam, x.x, ki * vv[t][0]);
+            x.y = fmaf(lam, x.y, ki * vv[t][1]);
+            x.z = fmaf(lam, x.z, ki * vv[t][2]);
+            x.w = fmaf(lam, x.w, ki * vv[t][3]);
+            s[m] = x;
+            o0 = fmaf(qi, x.x, o0);
+            o1 = fmaf(qi, x.y, o1);
+            o2 = fmaf(qi, x.z, o2);
+            o3 = fmaf(qi, x.w, o3);
+        }
+        if (t == ncommit - 1) {
+#pragma unroll
+            for (int m = 0; m < RPT; ++m) __builtin_nontemporal_store(s[m], &S[(rg + RG * m) * CG + cg]);
+        }
+        red[rg][t][4 * cg + 0] = o0;
+        red[rg][t][4 * cg + 1] = o1;
+        red[rg][t][4 * cg + 2] = o2;
+        red[rg][t][4 * cg + 3] = o3;
+    }
+    __syncthreads();
+    for (int e = tid; e < NT * D; e += DT) {
+        float acc = 0.f;
+#pragma unroll
+        for (int g = 0; g < RG; ++g) acc += red[g][e / D][e % D];
+        store_act<T>(out + a0 + e, acc);
+    }
+}
+
+template <typename T>
+hipError_t launch_decode_multi(const T *q, const T *k, const T *v, const float *slopes,
+                               const int32_t *n_commit, float *state, T *out, int64_t B,
+                               int64_t H, int nt, int d, hipStream_t stream)
+{
+    const dim3 grid((unsigned)(B * H)), block(DT);
+    void *args[] = {(void *)&q, (void *)&k, (void *)&v, (void *)&slopes, (void *)&n_commit,
+                    (void *)&state, (void *)&out, (void *)&H, (void *)&nt};
+    const void *fn = d == 64 ? (const void *)decode_multi_kernel<T, 64>
+                             : (const void *)decode_multi_kernel<T, 128>;
+    return hipLaunchKernel(fn, grid, block, args, 0, stream);
+}
+
 template <typename T>
 hipError_t launch_decode(const T *q, const T *k, const T *v, const float *slopes, float *state,
                          T *out, int64_t B, int64_t H, int d, hipStream_t stream)
@@ -116,5 +216,25 @@ hipError_t launch_decode_f32(const float *q, const float *k, const float *v,
 {
     return launch_decode<float>(q, k, v, slopes, state, out, B, H, d, stream);
 }
+
+hipError_t launch_decode_multi_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                    const float *slopes, const int32_t *n_commit, float *state,
+                                    uint16_t *out, int64_t B, int64_t H, int nt, int d,
+                                    hipStream_t stream)
+{
+    return launch_decode_multi<uint16_t>(q, k, v, slopes, n_commit, state, out, B, H, nt, d,
+                                         stream);
+}
+
+hipError_t launch_decode_multi_f32(const float *q, const float *k, const float *v,
+                                   const float *slopes, const int32_t *n_commit, float *state,
+                                   float *out, int64_t B, int64_t H, int nt, int d,
+                                   hipStream_t stream)
+{
+    return launch_decode_multi<float>(q, k, v, slopes, n_commit, state, out, B, H, nt, d,
+                                      stream);
+}
+
+int decode_multi_max_tokens() { return MAXT; }
 
 }  // namespace la

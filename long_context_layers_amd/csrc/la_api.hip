@@ -90,6 +90,30 @@ int check_decode(const void *q, const void *k, const void *v, const float *slope
     return LA_OK;
 }
 
+// multi-token decode: activations [B,H,T,d], optional n_commit [B] int32
+int check_decode_multi(const void *q, const void *k, const void *v, const float *slopes,
+                       const int32_t *n_commit, const float *state, const void *out,
+                       int64_t B, int64_t H, int64_t T, int64_t d, int64_t elem)
+{
+    if (!q || !k || !v || !slopes || !out || !state) return LA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || T < 1) return LA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
+    if (T > la::decode_multi_max_tokens()) return LA_ERR_UNSUPPORTED;
+    if (n_commit && !aligned(n_commit, 4)) return LA_ERR_INVALID_ARG;
+    int64_t bh, act, act_bytes, st, st_bytes;
+    if (!mul_ok(B, H, &bh) || !mul_ok(bh, T * d, &act) || !mul_ok(act, elem, &act_bytes) ||
+        !mul_ok(bh, d * d, &st) || !mul_ok(st, 4, &st_bytes))
+        return LA_ERR_INVALID_ARG;
+    if (!aligned(q, elem) || !aligned(k, elem) || !aligned(v, elem) || !aligned(out, elem) ||
+        !aligned(state, 16) || !aligned(slopes, 4))
+        return LA_ERR_INVALID_ARG;
+    if (overlap(out, act_bytes, q, act_bytes) || overlap(out, act_bytes, k, act_bytes) ||
+        overlap(out, act_bytes, v, act_bytes) || overlap(out, act_bytes, state, st_bytes))
+        return LA_ERR_INVALID_ARG;
+    if (bh > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+    return LA_OK;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? LA_OK : LA_ERR_HIP; }
 
 }  // namespace
@@ -171,6 +195,29 @@ int la_decode_step_f32(const float *q, const float *k, const float *v, const flo
                                             static_cast<hipStream_t>(stream)));
 }
 
+int la_decode_multi(const void *q, const void *k, const void *v, const float *slopes,
+                    const int32_t *n_commit, float *state, void *out, int64_t B, int64_t H,
+                    int64_t T, int64_t d, void *stream)
+{
+    const int rc = check_decode_multi(q, k, v, slopes, n_commit, state, out, B, H, T, d, 2);
+    if (rc != LA_OK) return rc;
+    return hip_status(la::launch_decode_multi_bf16(
+        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+        static_cast<const uint16_t *>(v), slopes, n_commit, state, static_cast<uint16_t *>(out),
+        B, H, (int)T, (int)d, static_cast<hipStream_t>(stream)));
+}
+
+int la_decode_multi_f32(const float *q, const float *k, const float *v, const float *slopes,
+                        const int32_t *n_commit, float *state, float *out, int64_t B, int64_t H,
+                        int64_t T, int64_t d, void *stream)
+{
+    const int rc = check_decode_multi(q, k, v, slopes, n_commit, state, out, B, H, T, d, 4);
+    if (rc != LA_OK) return rc;
+    return hip_status(la::launch_decode_multi_f32(q, k, v, slopes, n_commit, state, out, B, H,
+                                                  (int)T, (int)d,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
 const char *la_status_string(int status)
 {
     switch (status) {
@@ -179,7 +226,8 @@ const char *la_status_string(int status)
             return "LA_ERR_INVALID_ARG: null or misaligned pointer, negative or overflowing "
                    "size, or an output overlapping an input";
         case LA_ERR_UNSUPPORTED:
-            return "LA_ERR_UNSUPPORTED: head dimension not in {64, 128} or grid too large";
+            return "LA_ERR_UNSUPPORTED: head dimension not in {64, 128}, more tokens per "
+                   "decode call than supported, or grid too large";
         case LA_ERR_HIP: return "LA_ERR_HIP: the kernel launch failed";
         default: return "unknown status";
     }

@@ -48,6 +48,17 @@ hipError_t launch_decode_f32(const float *q, const float *k, const float *v,
                              const float *slopes, float *state, float *out,
                              int64_t B, int64_t H, int d, hipStream_t stream);
 
+// T tokens per sequence in one step (1 <= T <= decode_multi_max_tokens())
+hipError_t launch_decode_multi_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                    const float *slopes, const int32_t *n_commit, float *state,
+                                    uint16_t *out, int64_t B, int64_t H, int T, int d,
+                                    hipStream_t stream);
+hipError_t launch_decode_multi_f32(const float *q, const float *k, const float *v,
+                                   const float *slopes, const int32_t *n_commit, float *state,
+                                   float *out, int64_t B, int64_t H, int T, int d,
+                                   hipStream_t stream);
+int decode_multi_max_tokens();
+
 // number of workgroups one prefill launch over `seqs` sequences uses
 int64_t prefill_bf16_grid(int64_t seqs, int64_t H, int d);
 int64_t prefill_f32_grid(int64_t seqs, int64_t H, int d);

@@ -18,6 +18,10 @@ Three independent statements of it live here:
 * ``prefill_varlen``: a packed batch of independent sequences (the report's
   §4.1.2: packed sub-sequences, each attending only within itself), i.e. the
   same recurrence restarted from each sequence's own state.
+* ``decode_multi``: several tokens per sequence from the carried state with
+  only a leading prefix committed to the stored state (draft verification in
+  serving with multi-token prediction, the report's §4.3 and Appendix B),
+  i.e. ``decode_step`` applied token after token.
 * ``quadratic``: the definition's double sum written out as a masked
   decay-weighted score matrix (NumPy, fp64, tiny sizes only).
 * ``blockwise``: the block decomposition the GPU kernels follow (intra-block
@@ -153,6 +157,29 @@ def decode_step(q, k, v, slopes, state, inplace: bool = False):
     if r < 0:
         raise ValueError("la_oracle_decode_step rejected its arguments")
     return out, st
+
+
+def decode_multi(q, k, v, slopes, state, n_commit=None):
+    """T tokens per sequence from the carried state, fp64.
+
+    q, k, v: [B,H,T,d]; state: [B,H,d,d]; n_commit: B integers or None (= T).
+    Token t: S_t = lambda S_{t-1} + k_t^T v_t, o_t = q_t S_t, S_{-1} = state.
+    Returns (out [B,H,T,d] for every token, committed state [B,H,d,d] =
+    S_{n-1} with n = n_commit[b] clamped to [0, T]; the entry state for n = 0).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, T, d = q.shape
+    S = _f64(state).copy()
+    n = [T] * B if n_commit is None else [min(max(int(x), 0), T) for x in np.asarray(n_commit)]
+    committed = S.copy()
+    out = np.zeros((B, H, T, d))
+    for t in range(T):
+        o, S = decode_step(q[:, :, t], k[:, :, t], v[:, :, t], slopes, S)
+        out[:, :, t] = o
+        for b in range(B):
+            if n[b] == t + 1:
+                committed[b] = S[b]
+    return out, committed
 
 
 def quadratic(q, k, v, slopes, state_init=None):

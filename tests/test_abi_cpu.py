@@ -203,3 +203,36 @@ def test_varlen_rejects_bad_arguments(lib, fn, bad, code):
 ])
 def test_varlen_rejects_aliasing_and_overflow(lib, fn, bad):
     assert getattr(lib, fn)(*_varlen_args(T=1, **bad)) == LA_ERR_INVALID_ARG
+
+
+MULTI = ["la_decode_multi", "la_decode_multi_f32"]
+
+
+def _multi_args(**kw):
+    a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, slopes=FAKE + 0x300000,
+             n_commit=None, state=FAKE + 0x400000, out=FAKE + 0x900000, B=1, H=2, T=4, d=64,
+             stream=None)
+    a.update(kw)
+    return [a[n] for n in ("q", "k", "v", "slopes", "n_commit", "state", "out", "B", "H", "T",
+                           "d", "stream")]
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("fn", MULTI)
+@pytest.mark.parametrize("bad,code", [
+    (dict(T=0), LA_ERR_INVALID_ARG), (dict(T=-1), LA_ERR_INVALID_ARG),
+    (dict(T=9), LA_ERR_UNSUPPORTED), (dict(T=64), LA_ERR_UNSUPPORTED),
+    (dict(n_commit=FAKE + 0xa00002), LA_ERR_INVALID_ARG),     # misaligned int32 pointer
+    (dict(q=None), LA_ERR_INVALID_ARG), (dict(state=None), LA_ERR_INVALID_ARG),
+    (dict(slopes=None), LA_ERR_INVALID_ARG), (dict(out=None), LA_ERR_INVALID_ARG),
+    (dict(B=0), LA_ERR_INVALID_ARG), (dict(H=0), LA_ERR_INVALID_ARG),
+    (dict(d=96), LA_ERR_UNSUPPORTED),
+    (dict(out=FAKE), LA_ERR_INVALID_ARG),                     # out aliases q
+    (dict(out=FAKE + 0x400000), LA_ERR_INVALID_ARG),          # out aliases the state
+    (dict(state=FAKE + 0x400008), LA_ERR_INVALID_ARG),        # misaligned state
+    (dict(B=2 ** 40, H=2 ** 40), LA_ERR_INVALID_ARG),         # size overflow
+])
+def test_decode_multi_rejects_bad_arguments(lib, fn, bad, code):
+    # every case fails a host check (a missing one would launch on fake
+    # pointers, hence no-GPU machines only)
+    assert getattr(lib, fn)(*_multi_args(**bad)) == code

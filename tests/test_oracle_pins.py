@@ -324,3 +324,48 @@ def test_varlen_rejects_bad_offsets():
     for cu in ([0, 9, 8], [1, 4, 8], [0, 4, 7], [0, 8, 4]):
         with pytest.raises(ValueError):
             oracle.prefill_varlen(q, k, v, slopes_for([0.5]), np.array(cu), None)
+
+
+# --- several tokens per sequence with a committed prefix (draft
+# verification in serving with multi-token prediction) ----------------------
+
+def test_decode_multi_matches_quadratic():
+    rng = np.random.default_rng(41)
+    B, H, T, d = 5, len(LAMS), 4, 6
+    q, k, v, S0 = rand_inputs(rng, B, H, T, d)
+    s = slopes_for(LAMS)
+    n = np.array([0, 1, 2, 3, 4])
+    o, st = oracle.decode_multi(q, k, v, s, S0, n)
+    oq, _ = oracle.quadratic(q, k, v, s, S0)
+    assert oracle.rel_l2(o, oq) <= 1e-12                       # every token's output
+    for b in range(B):
+        _, fq = oracle.quadratic(q[b:b + 1, :, :n[b]], k[b:b + 1, :, :n[b]], v[b:b + 1, :, :n[b]],
+                                 s, S0[b:b + 1])
+        assert oracle.rel_l2(st[b], fq[0]) <= 1e-12             # state after n[b] tokens
+    assert np.array_equal(st[0], S0[0])                         # nothing committed
+
+
+def test_decode_multi_outputs_ignore_the_commit_count():
+    rng = np.random.default_rng(42)
+    q, k, v, S0 = rand_inputs(rng, 3, 2, 3, 4)
+    s = slopes_for([0.5, 0.97])
+    o1, s1 = oracle.decode_multi(q, k, v, s, S0, [3, 3, 3])
+    o2, _ = oracle.decode_multi(q, k, v, s, S0, [0, 1, 2])
+    o3, s3 = oracle.decode_multi(q, k, v, s, S0, None)
+    assert np.array_equal(o1, o2) and np.array_equal(o1, o3) and np.array_equal(s1, s3)
+    # clamping: counts beyond [0, T]
+    _, s4 = oracle.decode_multi(q, k, v, s, S0, [-2, 7, 3])
+    assert np.array_equal(s4[0], S0[0]) and np.array_equal(s4[1], s1[1])
+
+
+def test_decode_multi_pin_detects_committing_every_token():
+    # planted mistake: storing the state after all T tokens whatever the
+    # commit count must fail the double sum over the committed prefix
+    rng = np.random.default_rng(43)
+    q, k, v, S0 = rand_inputs(rng, 1, 1, 4, 5)
+    s = slopes_for([0.9])
+    _, full = oracle.decode_multi(q, k, v, s, S0, [4])
+    _, fq = oracle.quadratic(q[:, :, :2], k[:, :, :2], v[:, :, :2], s, S0)
+    assert oracle.rel_l2(full, fq) > 1e-3
+    _, good = oracle.decode_multi(q, k, v, s, S0, [2])
+    assert oracle.rel_l2(good, fq) <= 1e-12

@@ -15,6 +15,15 @@ launch on its stream.  The decode step is reported in GB/s of state traffic.
 ``roofline`` is the prefill kernel's HBM roofline (algorithmic bytes per
 launch / launch time against 8 TB/s); ``cpu_baseline`` times the fp64 CPU
 oracle on a bounded sample of the same workload.
+
+Outside the timed step, two more launches are measured the same way (HIP
+events on the launch stream, mean over ``--extra-reps``):
+  * ``varlen``: packed prefill of 262,144 tokens split into 74 sub-sequences
+    of 256..16,384 tokens (seeded log-uniform lengths), H=64, d=128 bf16, each
+    sequence with its own fp32 state (la_prefill_varlen, one launch);
+  * ``decode_multi``: draft verification, B=256 sequences x H=64, 4 draft
+    tokens each, seeded commit counts 1..4 (la_decode_multi), next to the
+    same tokens as 4 single decode steps.
 """
 from __future__ import annotations
 
@@ -36,6 +45,7 @@ C_COUNT = 64                     # block length the flop count is fixed at
 
 PREFILL = dict(B=1, H=64, N=262144, d=128, seed=1003)
 DECODE = dict(B=256, H=64, d=128, steps=64, seed=1004)
+MTP = dict(B=256, H=64, T=4, d=128, seed=1006)
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_256k_traffic.txt")
 KERNEL_SRC = os.path.join(ROOT, "long_context_layers_amd", "csrc", "prefill_bf16.hip")
@@ -50,9 +60,92 @@ def prefill_bytes(B, H, N, d):
     return B * H * N * d * 2 * 4 + B * H * d * d * 4 * 2
 
 
-def decode_bytes(B, H, d):
-    # state read + written (fp32), q, k, v read and out written (bf16)
-    return B * H * (2 * 4 * d * d + 4 * 2 * d)
+def decode_bytes(B, H, d, T=1):
+    # state read + written (fp32), q, k, v read and out written (bf16), T tokens
+    return B * H * (2 * 4 * d * d + 4 * 2 * d * T)
+
+
+def time_launches(stream, fn, reps):
+    """mean ms of `reps` launches of fn() on `stream` (HIP events on that stream)."""
+    import torch
+    fn()
+    stream.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for a, b in evs:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    stream.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / reps
+
+
+def measure_varlen(dev, stream, reps, dense_tflops):
+    import torch
+    from long_context_layers_amd import binding, inputs
+    with torch.cuda.stream(stream):
+        inp = inputs.make_workload("varlen_256k", device=dev)
+        st = inp.states.clone()
+        out = torch.empty_like(inp.q)
+    stream.synchronize()
+    H, T, d = inp.q.shape
+    nseq = len(inp.lens)
+
+    def run():
+        binding.prefill_varlen(inp.q, inp.k, inp.v, inp.slopes, inp.cu_seqlens, st, out=out)
+
+    with torch.cuda.stream(stream):
+        ms = time_launches(stream, run, reps)
+    fl = H * T * (4 * d * d + 2 * (C_COUNT + 1) * d)
+    by = H * T * d * 2 * 4 + nseq * H * d * d * 4 * 2
+    tflops = fl / (ms * 1e-3) / 1e12
+    gbs = by / (ms * 1e-3) / 1e9
+    lo, hi = min(inp.lens), max(inp.lens)
+    del inp, st, out
+    return {"workload": f"packed prefill H{H} T{T} d{d} bf16: {nseq} sequences of "
+                        f"{lo}..{hi} tokens (seeded log-uniform), per-sequence fp32 states",
+            "nseq": nseq, "ms": round(ms, 4), "tflops": round(tflops, 3),
+            "gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "algorithmic_bytes_per_launch": by, "vs_dense_256k_tflops": round(tflops / dense_tflops, 4),
+            "kernel": "prefill_bf16_kernel<128> (packed sequence map)"}
+
+
+def measure_decode_multi(dev, stream, reps):
+    import torch
+    from long_context_layers_amd import binding, inputs
+    B, H, T, d = MTP["B"], MTP["H"], MTP["T"], MTP["d"]
+    with torch.cuda.stream(stream):
+        dec = inputs.make_decode(B, H, d, T, torch.bfloat16, MTP["seed"], dev)
+        q, k, v = (x.permute(1, 2, 0, 3).contiguous() for x in (dec.q, dec.k, dec.v))
+        g = torch.Generator().manual_seed(MTP["seed"])
+        n = torch.randint(1, T + 1, (B,), generator=g, dtype=torch.int32).to(dev)
+        st = dec.state.clone()
+        out = torch.empty_like(q)
+        o1 = torch.empty_like(dec.q[0])
+    stream.synchronize()
+
+    def multi():
+        binding.decode_multi(q, k, v, dec.slopes, st, n_commit=n, out=out)
+
+    def singles():
+        for t in range(T):
+            binding.decode_step(dec.q[t], dec.k[t], dec.v[t], dec.slopes, st, out=o1)
+
+    with torch.cuda.stream(stream):
+        ms = time_launches(stream, multi, reps)
+        ms_single = time_launches(stream, singles, reps)
+    by = decode_bytes(B, H, d, T)
+    gbs = by / (ms * 1e-3) / 1e9
+    del dec, q, k, v, st, out
+    return {"workload": f"draft verification B{B} H{H} d{d} bf16, {T} draft tokens per "
+                        "sequence, seeded commit counts 1..4 (fp32 states)",
+            "ms_per_call": round(ms, 4), "gbs": round(gbs, 1),
+            "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "tokens_per_s": round(B * T / (ms * 1e-3), 1),
+            "algorithmic_bytes_per_call": by,
+            "four_single_steps_ms": round(ms_single, 4),
+            "speedup_vs_single_steps": round(ms_single / ms, 3),
+            "kernel": "decode_multi_kernel<bf16,128>"}
 
 
 def kernel_hash():
@@ -114,6 +207,9 @@ def main():
                     help="skip the CPU oracle timing (for profiler runs)")
     ap.add_argument("--copy-only", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--extra-reps", type=int, default=5,
+                    help="launches timed for the packed-prefill and draft-verification lines "
+                         "(0 skips them)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -234,6 +330,12 @@ def main():
             "kernel": "decode_kernel<bf16,128>",
         },
     }
+    if args.extra_reps > 0:
+        print("[bench] packed variable-length prefill", file=sys.stderr, flush=True)
+        res["varlen"] = measure_varlen(dev, stream, args.extra_reps, tflops)
+        torch.cuda.empty_cache()
+        print("[bench] multi-token decode", file=sys.stderr, flush=True)
+        res["decode_multi"] = measure_decode_multi(dev, stream, args.extra_reps)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(dict(q=p.q, k=p.k, v=p.v, slopes=p.slopes, N=N, d=d, H=H))

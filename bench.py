@@ -23,7 +23,12 @@ events on the launch stream, mean over ``--extra-reps``):
     sequence with its own fp32 state (la_prefill_varlen, one launch);
   * ``decode_multi``: draft verification, B=256 sequences x H=64, 4 draft
     tokens each, seeded commit counts 1..4 (la_decode_multi), next to the
-    same tokens as 4 single decode steps.
+    same tokens as 4 single decode steps;
+  * ``layer_ops``: the layer's neighbouring fused ops at the 256K shape
+    (B=1, N=262,144, H=64, d=128 bf16): QK RMSNorm + partial RoPE moving q,
+    k, v from one packed projection buffer to the kernel layout
+    (la_qk_norm_rope), and grouped RMSNorm x sigmoid gate back to the
+    token-major layout (la_group_norm_gate).
 """
 from __future__ import annotations
 
@@ -108,6 +113,44 @@ def measure_varlen(dev, stream, reps, dense_tflops):
             "gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "algorithmic_bytes_per_launch": by, "vs_dense_256k_tflops": round(tflops / dense_tflops, 4),
             "kernel": "prefill_bf16_kernel<128> (packed sequence map)"}
+
+
+def measure_layer_ops(dev, stream, reps):
+    import torch
+    from long_context_layers_amd import binding
+    B, N, H, d = 1, PREFILL["N"], PREFILL["H"], PREFILL["d"]
+    g = torch.Generator(device=dev).manual_seed(1007)
+    with torch.cuda.stream(stream):
+        proj = torch.empty((B, N, 4 * H * d), dtype=torch.bfloat16, device=dev)
+        proj.normal_(generator=g)                     # packed q | k | v | gate rows
+        q, k, v, gate = (proj[..., i * H * d:(i + 1) * H * d] for i in range(4))
+        outs = tuple(torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev) for _ in range(3))
+        y = torch.empty((B, N, H * d), dtype=torch.bfloat16, device=dev)
+        wq = torch.ones(d, device=dev)
+        wo = torch.ones(H * d, device=dev)
+    stream.synchronize()
+
+    def pro():
+        binding.qk_norm_rope(q, k, v, wq, wq, H, theta=6e6, rot_dim=64, outs=outs)
+
+    def epi():
+        binding.group_norm_gate(outs[0], gate, wo, out=y)
+
+    with torch.cuda.stream(stream):
+        ms_pro = time_launches(stream, pro, reps)
+        ms_epi = time_launches(stream, epi, reps)
+    elems = B * N * H * d
+    by_pro, by_epi = elems * 2 * 6, elems * 2 * 3
+    del proj, q, k, v, gate, outs, y
+    gp, ge = by_pro / (ms_pro * 1e-3) / 1e9, by_epi / (ms_epi * 1e-3) / 1e9
+    return {"workload": f"B{B} N{N} H{H} d{d} bf16; q,k,v,gate in one packed [B,N,4*H*d] "
+                        "projection buffer; RoPE base 6e6, rotary dim 64; norm group d",
+            "qk_norm_rope": {"ms": round(ms_pro, 4), "gbs": round(gp, 1),
+                             "frac_of_hbm_peak": round(gp / HBM_PEAK_GBS, 4),
+                             "algorithmic_bytes": by_pro, "kernel": "qk_norm_rope_kernel<128>"},
+            "group_norm_gate": {"ms": round(ms_epi, 4), "gbs": round(ge, 1),
+                                "frac_of_hbm_peak": round(ge / HBM_PEAK_GBS, 4),
+                                "algorithmic_bytes": by_epi, "kernel": "group_norm_gate_kernel<128>"}}
 
 
 def measure_decode_multi(dev, stream, reps):
@@ -336,6 +379,11 @@ def main():
         torch.cuda.empty_cache()
         print("[bench] multi-token decode", file=sys.stderr, flush=True)
         res["decode_multi"] = measure_decode_multi(dev, stream, args.extra_reps)
+        torch.cuda.empty_cache()
+        print("[bench] layer ops (QK norm + RoPE, grouped norm x gate)", file=sys.stderr, flush=True)
+        res["layer_ops"] = measure_layer_ops(dev, stream, args.extra_reps)
+        lo = res["layer_ops"]
+        lo["layer_ms"] = round(lo["qk_norm_rope"]["ms"] + pre_ms + lo["group_norm_gate"]["ms"], 4)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(dict(q=p.q, k=p.k, v=p.v, slopes=p.slopes, N=N, d=d, H=H))

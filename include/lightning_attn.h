@@ -164,6 +164,54 @@ int la_decode_multi_f32(const float *q, const float *k, const float *v, const fl
                         const int32_t *n_commit, float *state, float *out,
                         int64_t B, int64_t H, int64_t T, int64_t d, void *stream);
 
+/*
+ * The layer's neighbouring ops, each one fused kernel (bf16 activations, fp32
+ * weights and arithmetic).  Source: the report's Fig. 2 (the linear-attention
+ * layer: QKV projection -> QK Norm -> RoPE -> this library's kernel -> grouped
+ * RMSNorm, times sigmoid of a gate projection -> output projection), §4.3
+ * (QK Norm + RoPE and Group RMSNorm + Sigmoid Gate each fused into one
+ * kernel) and §2.1.1 (RMSNorm epsilon 1e-6; RoPE base 6,000,000 with rotary
+ * dimension 64, i.e. partial RoPE on part of each head).
+ *
+ * la_qk_norm_rope: from the projection layout to the kernel layout.
+ *   q_in, k_in, v_in  bf16 rows [B,N,H,d]: element (b,t,h,i) at
+ *                     (b*N + t)*in_stride + h*d + i; in_stride >= H*d and a
+ *                     multiple of 8 (a packed [q|k|v|...] projection output
+ *                     passes three offsets into one buffer).
+ *   q_norm_weight, k_norm_weight  [d] fp32, 16-byte aligned.
+ *   For q and k: x <- x / sqrt(mean_i x_i^2 + eps) * weight (RMSNorm over the
+ *   head dimension), then rotate-half RoPE on the first rot_dim dims at
+ *   position p = pos0 + t: for j < rot_dim/2, with a = p * theta^(-2j/rot_dim),
+ *     x'_j = x_j cos a - x_{j+rot/2} sin a,   x'_{j+rot/2} = x_{j+rot/2} cos a + x_j sin a;
+ *   dims >= rot_dim pass through.  v is only moved.
+ *   q_out, k_out, v_out  bf16 [B,H,N,d] (the layout la_prefill reads).
+ *   rot_dim in {0, 16, 32, 64, 128} (<= d), theta > 1 when rot_dim > 0,
+ *   pos0 >= 0, eps >= 0.  Other rot_dim values give LA_ERR_UNSUPPORTED.
+ *   Outputs must not overlap the inputs or each other.  B*N == 0 is a no-op.
+ */
+int la_qk_norm_rope(const void *q_in, const void *k_in, const void *v_in, int64_t in_stride,
+                    const float *q_norm_weight, const float *k_norm_weight, double theta,
+                    int64_t rot_dim, int64_t pos0, float eps, void *q_out, void *k_out,
+                    void *v_out, int64_t B, int64_t N, int64_t H, int64_t d, void *stream);
+
+/*
+ * la_group_norm_gate: from the kernel layout back to the projection layout.
+ *   o            bf16 [B,H,N,d] (la_prefill's output).
+ *   gate         bf16 rows [B,N,H*d] at token stride gate_stride (>= H*d, a
+ *                multiple of 8).
+ *   norm_weight  [H*d] fp32, 16-byte aligned.
+ *   y[b,t,c] = o_c / sqrt(mean over c's group of o^2 + eps) * norm_weight[c]
+ *              * sigmoid(gate[b,t,c]),  c = h*d + i, groups of `group`
+ *              consecutive channels inside one head.
+ *   y            bf16 [B,N,H*d], contiguous; must not overlap o or gate.
+ *   group is a power of two in [8, d] (else LA_ERR_UNSUPPORTED); the pages do
+ *   not give the group size (a head, group = d, is the plain reading).
+ *   eps >= 0.  B*N == 0 is a no-op.
+ */
+int la_group_norm_gate(const void *o, const void *gate, int64_t gate_stride,
+                       const float *norm_weight, int64_t group, float eps, void *y,
+                       int64_t B, int64_t N, int64_t H, int64_t d, void *stream);
+
 /* Static, NUL-terminated description of a status code ("unknown status" for
  * values outside la_status).  Never NULL; the caller must not free it. */
 const char *la_status_string(int status);

@@ -30,6 +30,10 @@ SIGNATURES = {
     "la_decode_multi": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], _INT),
     "la_decode_multi_f32": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], _INT),
     "la_decode_step_f32": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], _INT),
+    "la_qk_norm_rope": ([_P, _P, _P, _I64, _P, _P, ctypes.c_double, _I64, _I64, ctypes.c_float,
+                         _P, _P, _P, _I64, _I64, _I64, _I64, _P], _INT),
+    "la_group_norm_gate": ([_P, _P, _I64, _P, _I64, ctypes.c_float, _P, _I64, _I64, _I64, _I64,
+                            _P], _INT),
     "la_status_string": ([_INT], ctypes.c_char_p),
     "la_abi_version": ([], _INT),
 }
@@ -232,4 +236,82 @@ def decode_multi(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: torc
                 None if n_commit is None else n_commit.data_ptr(), state.data_ptr(),
                 out.data_ptr(), B, H, T, d, _stream(dev))
     _check(rc, "la_decode_multi" if dt == torch.bfloat16 else "la_decode_multi_f32")
+    return out
+
+
+def _rows(t: torch.Tensor, name: str, dev, shape):
+    """[B,N,X] bf16 rows with a contiguous last dim (any token stride)."""
+    if not isinstance(t, torch.Tensor) or t.device != dev or t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be a bfloat16 tensor on {dev}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.stride(2) != 1 or t.stride(0) != t.shape[1] * t.stride(1):
+        raise ValueError(f"{name} must be [B,N,X] rows with unit channel stride and equal token strides")
+    return t.stride(1)
+
+
+def qk_norm_rope(q_in: torch.Tensor, k_in: torch.Tensor, v_in: torch.Tensor,
+                 q_norm_weight: torch.Tensor, k_norm_weight: torch.Tensor, H: int,
+                 theta: float = 6.0e6, rot_dim: int = 64, pos0: int = 0, eps: float = 1e-6,
+                 outs=None):
+    """QK RMSNorm + partial RoPE, and the move of q, k, v to the kernel layout.
+
+    q_in, k_in, v_in: [B,N,H*d] bf16 views (a shared token stride is allowed,
+    e.g. slices of one packed projection output); weights [d] fp32.
+    Returns (q, k, v) as [B,H,N,d] bf16 (written into ``outs`` if given).
+    """
+    dev = q_in.device
+    if dev.type != "cuda":
+        raise ValueError("qk_norm_rope runs on GPU tensors only (no CPU path)")
+    B, N, HD = q_in.shape
+    d = HD // H
+    if d * H != HD:
+        raise ValueError("last dimension must be H*d")
+    st = _rows(q_in, "q_in", dev, (B, N, HD))
+    for t, n in ((k_in, "k_in"), (v_in, "v_in")):
+        if _rows(t, n, dev, (B, N, HD)) != st:
+            raise ValueError("q_in, k_in, v_in must share one token stride")
+    _need(q_norm_weight, "q_norm_weight", torch.float32, dev, (d,))
+    _need(k_norm_weight, "k_norm_weight", torch.float32, dev, (d,))
+    if outs is None:
+        outs = tuple(torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev) for _ in range(3))
+    for t, n in zip(outs, ("q_out", "k_out", "v_out")):
+        _need(t, n, torch.bfloat16, dev, (B, H, N, d))
+    lib = load_library()
+    with torch.cuda.device(dev):
+        rc = lib.la_qk_norm_rope(q_in.data_ptr(), k_in.data_ptr(), v_in.data_ptr(), st,
+                                 q_norm_weight.data_ptr(), k_norm_weight.data_ptr(), float(theta),
+                                 rot_dim, pos0, float(eps), outs[0].data_ptr(), outs[1].data_ptr(),
+                                 outs[2].data_ptr(), B, N, H, d, _stream(dev))
+    _check(rc, "la_qk_norm_rope")
+    return outs
+
+
+def group_norm_gate(o: torch.Tensor, gate: torch.Tensor, norm_weight: torch.Tensor,
+                    group: Optional[int] = None, eps: float = 1e-6,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Grouped RMSNorm of the kernel output times sigmoid(gate), back to [B,N,H*d].
+
+    o: [B,H,N,d] bf16; gate: [B,N,H*d] bf16 view (any token stride);
+    norm_weight: [H*d] fp32; group: channels per group (default d, one head).
+    """
+    if not isinstance(o, torch.Tensor) or o.dim() != 4:
+        raise ValueError("o must be a [B,H,N,d] tensor")
+    dev = o.device
+    if dev.type != "cuda":
+        raise ValueError("group_norm_gate runs on GPU tensors only (no CPU path)")
+    B, H, N, d = o.shape
+    _need(o, "o", torch.bfloat16, dev, (B, H, N, d))
+    gst = _rows(gate, "gate", dev, (B, N, H * d))
+    _need(norm_weight, "norm_weight", torch.float32, dev, (H * d,))
+    if out is None:
+        out = torch.empty((B, N, H * d), dtype=torch.bfloat16, device=dev)
+    else:
+        _need(out, "out", torch.bfloat16, dev, (B, N, H * d))
+    lib = load_library()
+    with torch.cuda.device(dev):
+        rc = lib.la_group_norm_gate(o.data_ptr(), gate.data_ptr(), gst, norm_weight.data_ptr(),
+                                    d if group is None else group, float(eps), out.data_ptr(),
+                                    B, N, H, d, _stream(dev))
+    _check(rc, "la_group_norm_gate")
     return out

@@ -114,6 +114,28 @@ int check_decode_multi(const void *q, const void *k, const void *v, const float 
     return LA_OK;
 }
 
+bool pow2_in(int64_t x, int64_t lo, int64_t hi) { return x >= lo && x <= hi && (x & (x - 1)) == 0; }
+
+// [rows][width] bf16 rows at `stride` elements apart, width <= stride: the
+// byte span they cover (false on overflow)
+bool span_ok(int64_t rows, int64_t stride, int64_t width, int64_t *bytes) {
+    if (rows == 0) { *bytes = 0; return true; }
+    int64_t last;
+    if (!mul_ok(rows - 1, stride, &last) || last > INT64_MAX / 2 - width) return false;
+    *bytes = (last + width) * 2;
+    return true;
+}
+
+int check_layer_common(int64_t B, int64_t N, int64_t H, int64_t d)
+{
+    if (B < 1 || N < 0 || H < 1) return LA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
+    int64_t bn;
+    if (!mul_ok(B, N, &bn)) return LA_ERR_INVALID_ARG;
+    if (bn > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+    return LA_OK;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? LA_OK : LA_ERR_HIP; }
 
 }  // namespace
@@ -218,6 +240,72 @@ int la_decode_multi_f32(const float *q, const float *k, const float *v, const fl
                                                   static_cast<hipStream_t>(stream)));
 }
 
+int la_qk_norm_rope(const void *q_in, const void *k_in, const void *v_in, int64_t in_stride,
+                    const float *q_norm_weight, const float *k_norm_weight, double theta,
+                    int64_t rot_dim, int64_t pos0, float eps, void *q_out, void *k_out,
+                    void *v_out, int64_t B, int64_t N, int64_t H, int64_t d, void *stream)
+{
+    int rc = check_layer_common(B, N, H, d);
+    if (rc != LA_OK) return rc;
+    const int64_t rows = B * N;
+    if (rows > 0 && (!q_in || !k_in || !v_in || !q_out || !k_out || !v_out))
+        return LA_ERR_INVALID_ARG;
+    if (!q_norm_weight || !k_norm_weight || !aligned(q_norm_weight, 16) ||
+        !aligned(k_norm_weight, 16))
+        return LA_ERR_INVALID_ARG;
+    int64_t hd;
+    if (!mul_ok(H, d, &hd) || in_stride < hd || in_stride % 8 != 0) return LA_ERR_INVALID_ARG;
+    if (rot_dim != 0 && !pow2_in(rot_dim, 16, d)) return LA_ERR_UNSUPPORTED;
+    if (rot_dim != 0 && !(theta > 1.0)) return LA_ERR_INVALID_ARG;      // also rejects NaN
+    if (pos0 < 0 || pos0 > INT64_MAX - N || !(eps >= 0.0f)) return LA_ERR_INVALID_ARG;
+    int64_t rh, in_bytes, out_bytes;
+    if (!mul_ok(rows, H, &rh) || !span_ok(rows, in_stride, hd, &in_bytes) ||
+        !span_ok(rh, d, d, &out_bytes))
+        return LA_ERR_INVALID_ARG;
+    const void *ins[3] = {q_in, k_in, v_in};
+    const void *outs[3] = {q_out, k_out, v_out};
+    for (int i = 0; i < 3; ++i) {
+        if (!aligned(ins[i], 16) || !aligned(outs[i], 16)) return LA_ERR_INVALID_ARG;
+        for (int j = 0; j < 3; ++j)
+            if (overlap(outs[i], out_bytes, ins[j], in_bytes)) return LA_ERR_INVALID_ARG;
+        for (int j = 0; j < i; ++j)
+            if (overlap(outs[i], out_bytes, outs[j], out_bytes)) return LA_ERR_INVALID_ARG;
+    }
+    if (rows == 0) return LA_OK;
+    return hip_status(la::launch_qk_norm_rope(
+        static_cast<const uint16_t *>(q_in), static_cast<const uint16_t *>(k_in),
+        static_cast<const uint16_t *>(v_in), in_stride, q_norm_weight, k_norm_weight, theta,
+        (int)rot_dim, pos0, eps, static_cast<uint16_t *>(q_out), static_cast<uint16_t *>(k_out),
+        static_cast<uint16_t *>(v_out), B, N, H, (int)d, static_cast<hipStream_t>(stream)));
+}
+
+int la_group_norm_gate(const void *o, const void *gate, int64_t gate_stride,
+                       const float *norm_weight, int64_t group, float eps, void *y,
+                       int64_t B, int64_t N, int64_t H, int64_t d, void *stream)
+{
+    int rc = check_layer_common(B, N, H, d);
+    if (rc != LA_OK) return rc;
+    const int64_t rows = B * N;
+    if (rows > 0 && (!o || !gate || !y)) return LA_ERR_INVALID_ARG;
+    if (!norm_weight || !aligned(norm_weight, 16)) return LA_ERR_INVALID_ARG;
+    if (!pow2_in(group, 8, d)) return LA_ERR_UNSUPPORTED;
+    int64_t hd;
+    if (!mul_ok(H, d, &hd) || gate_stride < hd || gate_stride % 8 != 0) return LA_ERR_INVALID_ARG;
+    if (!(eps >= 0.0f)) return LA_ERR_INVALID_ARG;
+    int64_t rh, o_bytes, g_bytes, y_bytes;
+    if (!mul_ok(rows, H, &rh) || !span_ok(rh, d, d, &o_bytes) ||
+        !span_ok(rows, gate_stride, hd, &g_bytes) || !span_ok(rows, hd, hd, &y_bytes))
+        return LA_ERR_INVALID_ARG;
+    if (!aligned(o, 16) || !aligned(gate, 16) || !aligned(y, 16)) return LA_ERR_INVALID_ARG;
+    if (overlap(y, y_bytes, o, o_bytes) || overlap(y, y_bytes, gate, g_bytes))
+        return LA_ERR_INVALID_ARG;
+    if (rows == 0) return LA_OK;
+    return hip_status(la::launch_group_norm_gate(
+        static_cast<const uint16_t *>(o), static_cast<const uint16_t *>(gate), gate_stride,
+        norm_weight, (int)group, eps, static_cast<uint16_t *>(y), B, N, H, (int)d,
+        static_cast<hipStream_t>(stream)));
+}
+
 const char *la_status_string(int status)
 {
     switch (status) {
@@ -227,7 +315,8 @@ const char *la_status_string(int status)
                    "size, or an output overlapping an input";
         case LA_ERR_UNSUPPORTED:
             return "LA_ERR_UNSUPPORTED: head dimension not in {64, 128}, more tokens per "
-                   "decode call than supported, or grid too large";
+                   "decode call than supported, a rotary dimension or norm group size the "
+                   "kernels do not take, or grid too large";
         case LA_ERR_HIP: return "LA_ERR_HIP: the kernel launch failed";
         default: return "unknown status";
     }

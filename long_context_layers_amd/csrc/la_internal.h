@@ -59,6 +59,16 @@ hipError_t launch_decode_multi_f32(const float *q, const float *k, const float *
                                    hipStream_t stream);
 int decode_multi_max_tokens();
 
+// the layer's neighbouring ops (one workgroup per token)
+hipError_t launch_qk_norm_rope(const uint16_t *qi, const uint16_t *ki, const uint16_t *vi,
+                               int64_t in_stride, const float *qw, const float *kw, double theta,
+                               int rot, int64_t pos0, float eps, uint16_t *qo, uint16_t *ko,
+                               uint16_t *vo, int64_t B, int64_t N, int64_t H, int d,
+                               hipStream_t stream);
+hipError_t launch_group_norm_gate(const uint16_t *o, const uint16_t *g, int64_t gate_stride,
+                                  const float *w, int group, float eps, uint16_t *y, int64_t B,
+                                  int64_t N, int64_t H, int d, hipStream_t stream);
+
 // number of workgroups one prefill launch over `seqs` sequences uses
 int64_t prefill_bf16_grid(int64_t seqs, int64_t H, int d);
 int64_t prefill_f32_grid(int64_t seqs, int64_t H, int d);

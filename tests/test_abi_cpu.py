@@ -236,3 +236,68 @@ def test_decode_multi_rejects_bad_arguments(lib, fn, bad, code):
     # every case fails a host check (a missing one would launch on fake
     # pointers, hence no-GPU machines only)
     assert getattr(lib, fn)(*_multi_args(**bad)) == code
+
+
+def _rope_args(**kw):
+    a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, stride=3 * 2 * 64, qw=FAKE + 0x300000,
+             kw=FAKE + 0x310000, theta=6e6, rot=64, pos0=0, eps=1e-6, qo=FAKE + 0x400000,
+             ko=FAKE + 0x500000, vo=FAKE + 0x600000, B=1, N=0, H=2, d=64, stream=None)
+    a.update(kw)
+    return [a[n] for n in ("q", "k", "v", "stride", "qw", "kw", "theta", "rot", "pos0", "eps",
+                           "qo", "ko", "vo", "B", "N", "H", "d", "stream")]
+
+
+def _gate_args(**kw):
+    a = dict(o=FAKE, g=FAKE + 0x100000, gstride=2 * 64, w=FAKE + 0x300000, group=64, eps=1e-6,
+             y=FAKE + 0x400000, B=1, N=0, H=2, d=64, stream=None)
+    a.update(kw)
+    return [a[n] for n in ("o", "g", "gstride", "w", "group", "eps", "y", "B", "N", "H", "d",
+                           "stream")]
+
+
+def test_layer_ops_empty_is_a_noop(lib):
+    assert lib.la_qk_norm_rope(*_rope_args(N=0)) == LA_OK
+    assert lib.la_qk_norm_rope(*_rope_args(N=0, q=None, k=None, v=None, qo=None, ko=None,
+                                           vo=None)) == LA_OK
+    assert lib.la_group_norm_gate(*_gate_args(N=0)) == LA_OK
+    assert lib.la_group_norm_gate(*_gate_args(N=0, o=None, g=None, y=None)) == LA_OK
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(rot=48), LA_ERR_UNSUPPORTED), (dict(rot=8), LA_ERR_UNSUPPORTED),
+    (dict(rot=128), LA_ERR_UNSUPPORTED),                    # > d
+    (dict(theta=1.0), LA_ERR_INVALID_ARG), (dict(theta=float("nan")), LA_ERR_INVALID_ARG),
+    (dict(pos0=-1), LA_ERR_INVALID_ARG), (dict(eps=-1.0), LA_ERR_INVALID_ARG),
+    (dict(stride=100), LA_ERR_INVALID_ARG),                 # < H*d
+    (dict(stride=3 * 2 * 64 + 4), LA_ERR_INVALID_ARG),      # not a multiple of 8
+    (dict(qw=None), LA_ERR_INVALID_ARG), (dict(kw=FAKE + 0x310004), LA_ERR_INVALID_ARG),
+    (dict(d=96), LA_ERR_UNSUPPORTED), (dict(B=0), LA_ERR_INVALID_ARG),
+    (dict(H=0), LA_ERR_INVALID_ARG), (dict(N=-1), LA_ERR_INVALID_ARG),
+])
+def test_qk_norm_rope_rejects_bad_arguments(lib, bad, code):
+    # N = 0 unless the case sets it: a missing check could not reach a launch
+    assert lib.la_qk_norm_rope(*_rope_args(**bad)) == code
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(group=4), LA_ERR_UNSUPPORTED), (dict(group=48), LA_ERR_UNSUPPORTED),
+    (dict(group=128), LA_ERR_UNSUPPORTED),                  # > d
+    (dict(gstride=64), LA_ERR_INVALID_ARG), (dict(eps=float("nan")), LA_ERR_INVALID_ARG),
+    (dict(w=None), LA_ERR_INVALID_ARG), (dict(w=FAKE + 0x300008), LA_ERR_INVALID_ARG),
+    (dict(d=32), LA_ERR_UNSUPPORTED), (dict(B=-1), LA_ERR_INVALID_ARG),
+])
+def test_group_norm_gate_rejects_bad_arguments(lib, bad, code):
+    assert lib.la_group_norm_gate(*_gate_args(**bad)) == code
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("bad", [dict(qo=FAKE), dict(vo=FAKE + 0x100000), dict(ko=FAKE + 0x400000),
+                                 dict(q=None), dict(vo=None), dict(q=FAKE + 8)])
+def test_qk_norm_rope_rejects_overlap_and_nulls(lib, bad):
+    assert lib.la_qk_norm_rope(*_rope_args(N=3, **bad)) == LA_ERR_INVALID_ARG
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("bad", [dict(y=FAKE), dict(y=FAKE + 0x100000), dict(o=None), dict(g=FAKE + 2)])
+def test_group_norm_gate_rejects_overlap_and_nulls(lib, bad):
+    assert lib.la_group_norm_gate(*_gate_args(N=3, **bad)) == LA_ERR_INVALID_ARG

@@ -523,17 +523,27 @@ __global__ __launch_bounds__(NTHREADS) void prefill_bf16_kernel(
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
 
-    // XCD-aware placement: workgroup i runs on XCD i % 8; give the NJ
-    // workgroups of one head consecutive logical ids on the same XCD.
-    const int64_t nwg = gridDim.x;
-    int64_t lid = blockIdx.x;
-    if (nwg % 8 == 0) lid = (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8;
-    const int64_t bh = lid / NJ;          // sequence * H + head
+    // XCD-aware placement: workgroup i runs on XCD i % 8 and workgroups start
+    // in index order.  Workgroups 8q + x (x = 0..7) take slice q % NJ of
+    // (sequence, head) slot 8 (q / NJ) + x: the NJ slices of one head run on
+    // one XCD at the same time (Q and K come from HBM once, then from that
+    // XCD's L2), and consecutive heads of a sequence go to different XCDs, so
+    // every XCD gets an equal share of every sequence however long it is.
+    const int64_t nbh = gridDim.x / NJ;
+    int64_t bh, slice;
+    if (nbh % 8 == 0) {
+        const int64_t q8 = blockIdx.x / 8;
+        bh = (q8 / NJ) * 8 + blockIdx.x % 8;
+        slice = q8 % NJ;
+    } else {
+        bh = blockIdx.x / NJ;
+        slice = blockIdx.x % NJ;
+    }
     int64_t row0, N;
     seq_slice(map, bh / map.H, bh % map.H, &row0, &N);
 
     Ctx<D> cx;
-    cx.j0 = (int)(lid % NJ) * PJ;
+    cx.j0 = (int)slice * PJ;
     cx.s = slopes[bh % map.H];
     cx.N = N;
     // blocks processed: a multiple of NSET (trailing empty blocks are no-ops;

@@ -231,6 +231,25 @@ def cpu_baseline(pre, target_s=12.0):
         if spent >= target_s:
             break
     fl = prefill_flops(1, heads_done, N, d)
+    # one thread on the 4K workload (B1 H64 N4096 d128), for a per-core figure
+    one = inputs_4k = None
+    try:
+        from long_context_layers_amd import inputs
+        inputs_4k = inputs.make_workload("prefill_4k", device="cpu")
+        q4, k4, v4 = (t.float().double().numpy() for t in (inputs_4k.q, inputs_4k.k, inputs_4k.v))
+        s4 = inputs_4k.slopes.double().numpy()
+        oracle.set_threads(1)
+        t0 = time.perf_counter()
+        oracle.prefill(q4, k4, v4, s4)
+        one = time.perf_counter() - t0
+    finally:
+        oracle.set_threads(max(1, threads))
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in fh if l.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": fl / spent / 1e12, "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"fp64 recurrent oracle (OpenMP over heads) on heads 0..{heads_done - 1} "
@@ -238,7 +257,11 @@ def cpu_baseline(pre, target_s=12.0):
                       f"{spent:.1f} s of oracle time); flops counted as on the GPU "
                       f"(B*H*N*(4d^2+2(C+1)d), C=64)",
             "seconds": round(spent, 2),
-            "host_threads_available": len(os.sched_getaffinity(0))}
+            "host_threads_available": len(os.sched_getaffinity(0)),
+            "cpu_model": cpu_model,
+            "one_thread_prefill_4k_s": None if one is None else round(one, 2),
+            "one_thread_prefill_4k_tflops": None if one is None else
+            round(prefill_flops(1, 64, 4096, 128) / one / 1e12, 5)}
 
 
 def main():

@@ -73,6 +73,8 @@ def _load():
             lib.la_oracle_prefill.restype = ctypes.c_int
             lib.la_oracle_decode_step.argtypes = [dp, dp, dp, dp, dp, dp, i64, i64, i64]
             lib.la_oracle_decode_step.restype = ctypes.c_int
+            lib.la_oracle_set_threads.argtypes = [ctypes.c_int]
+            lib.la_oracle_set_threads.restype = None
             _lib = lib
     return _lib
 
@@ -86,6 +88,12 @@ def _ptr(a: np.ndarray):
 
 
 last_threads = 0
+
+
+def set_threads(n: int) -> None:
+    """Thread count of the C oracle's OpenMP loops from now on (timing aid;
+    results are independent of it)."""
+    _load().la_oracle_set_threads(int(n))
 
 
 def prefill(q, k, v, slopes, state_init=None, want_out: bool = True):

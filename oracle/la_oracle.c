@@ -65,6 +65,13 @@ static void recurrent_slice(const double *q, const double *k, const double *v,
  * out: [B,H,N,d] or NULL (state only).  Returns the number of OpenMP threads
  * used (>= 1), or -1 on bad arguments.
  */
+/* Threads the oracle's parallel loops use from now on (n >= 1); timing aid
+ * only, the results do not depend on it. */
+void la_oracle_set_threads(int n)
+{
+    if (n >= 1) omp_set_num_threads(n);
+}
+
 int la_oracle_prefill(const double *q, const double *k, const double *v,
                       const double *slopes, double *state, double *out,
                       int64_t B, int64_t H, int64_t N, int64_t d)

@@ -192,8 +192,13 @@ def measure_decode_multi(dev, stream, reps):
 
 
 def kernel_hash():
-    with open(KERNEL_SRC, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()[:16]
+    """sha256 (first 16 hex digits) of the prefill kernel's code with comments
+    and blank space removed, so comment edits keep the recorded counters."""
+    text = open(KERNEL_SRC).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 def measured_traffic():

@@ -33,8 +33,11 @@
 //
 // What bounds it: every workgroup of a head pulls the full Q and K blocks
 // through its XCD's L2 (the four copies share one HBM read), and LDS carries
-// the producers' writes plus every MFMA operand.  The layout therefore keeps
-// each operand's LDS reads few: 32x32x16 MFMAs (half the operand bytes per
+// the producers' writes plus every MFMA operand.  Measured at 256K tokens, a
+// block takes about 2,000 cycles with LDS about 70% busy, set by the consumer
+// waves' reads and their dependent MFMA chains (the HBM stream alone would
+// take two thirds of that).  The layout therefore keeps each operand's LDS
+// reads few: 32x32x16 MFMAs (half the operand bytes per
 // flop of 16x16x32), scores kept in registers and fed straight into V^T P^T,
 // Q fragments shared by the score and inter-term products, and one barrier
 // per block (double-buffered tiles and state copy).

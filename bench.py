@@ -25,10 +25,13 @@ events on the launch stream, mean over ``--extra-reps``):
     tokens each, seeded commit counts 1..4 (la_decode_multi), next to the
     same tokens as 4 single decode steps;
   * ``layer_ops``: the layer's neighbouring fused ops at the 256K shape
-    (B=1, N=262,144, H=64, d=128 bf16): QK RMSNorm + partial RoPE moving q,
-    k, v from one packed projection buffer to the kernel layout
-    (la_qk_norm_rope), and grouped RMSNorm x sigmoid gate back to the
-    token-major layout (la_group_norm_gate).
+    (B=1, N=262,144, H=64, d=128 bf16), in two arrangements: through the
+    kernel layout (la_qk_norm_rope moves q, k, v from one packed projection
+    buffer to [B,H,N,d]; la_prefill; la_group_norm_gate back to the
+    token-major layout), and with no layout copies (QK norm + RoPE in place
+    in the projection buffer, la_prefill_strided reading q, k, v from it and
+    writing [B,H,N,d], la_group_norm_gate on that output); the strided
+    prefill writing its output token-major is timed beside it.
 """
 from __future__ import annotations
 
@@ -115,9 +118,9 @@ def measure_varlen(dev, stream, reps, dense_tflops):
             "kernel": "prefill_bf16_kernel<128> (packed sequence map)"}
 
 
-def measure_layer_ops(dev, stream, reps):
+def measure_layer_ops(dev, stream, reps, pre_ms):
     import torch
-    from long_context_layers_amd import binding
+    from long_context_layers_amd import binding, inputs
     B, N, H, d = 1, PREFILL["N"], PREFILL["H"], PREFILL["d"]
     g = torch.Generator(device=dev).manual_seed(1007)
     with torch.cuda.stream(stream):
@@ -126,8 +129,15 @@ def measure_layer_ops(dev, stream, reps):
         q, k, v, gate = (proj[..., i * H * d:(i + 1) * H * d] for i in range(4))
         outs = tuple(torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev) for _ in range(3))
         y = torch.empty((B, N, H * d), dtype=torch.bfloat16, device=dev)
+        o_tm = torch.empty((B, N, H * d), dtype=torch.bfloat16, device=dev)
         wq = torch.ones(d, device=dev)
         wo = torch.ones(H * d, device=dev)
+        slopes = inputs.slopes(H, dev)
+        st = torch.zeros((B, H, d, d), dtype=torch.float32, device=dev)
+
+    def heads(t):                                     # [B,N,H*d] -> [B,H,N,d] view
+        return t.unflatten(-1, (H, d)).transpose(1, 2)
+
     stream.synchronize()
 
     def pro():
@@ -136,21 +146,52 @@ def measure_layer_ops(dev, stream, reps):
     def epi():
         binding.group_norm_gate(outs[0], gate, wo, out=y)
 
+    def pro_inplace():
+        binding.qk_norm_rope(q, k, None, wq, wq, H, theta=6e6, rot_dim=64, inplace=True)
+
+    def attn_strided():
+        binding.prefill(heads(q), heads(k), heads(v), slopes, st, out=outs[1])
+
+    def attn_strided_tm():
+        binding.prefill(heads(q), heads(k), heads(v), slopes, st, out=heads(o_tm))
+
+    def epi_tm():
+        binding.group_norm_gate(heads(o_tm), gate, wo, out=y)
+
     with torch.cuda.stream(stream):
         ms_pro = time_launches(stream, pro, reps)
         ms_epi = time_launches(stream, epi, reps)
+        ms_pro_ip = time_launches(stream, pro_inplace, reps)
+        ms_attn = time_launches(stream, attn_strided, reps)
+        ms_attn_tm = time_launches(stream, attn_strided_tm, reps)
+        ms_epi_tm = time_launches(stream, epi_tm, reps)
     elems = B * N * H * d
-    by_pro, by_epi = elems * 2 * 6, elems * 2 * 3
-    del proj, q, k, v, gate, outs, y
-    gp, ge = by_pro / (ms_pro * 1e-3) / 1e9, by_epi / (ms_epi * 1e-3) / 1e9
+    by_pro, by_epi, by_pro_ip = elems * 2 * 6, elems * 2 * 3, elems * 2 * 4
+    del proj, q, k, v, gate, outs, y, o_tm, st
+
+    def line(ms, by, kernel):
+        gb = by / (ms * 1e-3) / 1e9
+        return {"ms": round(ms, 4), "gbs": round(gb, 1), "frac_of_hbm_peak": round(gb / HBM_PEAK_GBS, 4),
+                "algorithmic_bytes": by, "kernel": kernel}
+
+    fl = prefill_flops(B, H, N, d)
     return {"workload": f"B{B} N{N} H{H} d{d} bf16; q,k,v,gate in one packed [B,N,4*H*d] "
                         "projection buffer; RoPE base 6e6, rotary dim 64; norm group d",
-            "qk_norm_rope": {"ms": round(ms_pro, 4), "gbs": round(gp, 1),
-                             "frac_of_hbm_peak": round(gp / HBM_PEAK_GBS, 4),
-                             "algorithmic_bytes": by_pro, "kernel": "qk_norm_rope_kernel<128>"},
-            "group_norm_gate": {"ms": round(ms_epi, 4), "gbs": round(ge, 1),
-                                "frac_of_hbm_peak": round(ge / HBM_PEAK_GBS, 4),
-                                "algorithmic_bytes": by_epi, "kernel": "group_norm_gate_kernel<128>"}}
+            "qk_norm_rope": line(ms_pro, by_pro, "qk_norm_rope_kernel<128>"),
+            "group_norm_gate": line(ms_epi, by_epi, "group_norm_gate_kernel<128>"),
+            "layer_ms": round(ms_pro + pre_ms + ms_epi, 4),
+            "no_layout_copies": {
+                "qk_norm_rope_in_place": line(ms_pro_ip, by_pro_ip, "qk_norm_rope_kernel<128>"),
+                "prefill_strided": {"ms": round(ms_attn, 4),
+                                    "tflops": round(fl / (ms_attn * 1e-3) / 1e12, 3),
+                                    "vs_contiguous": round(pre_ms / ms_attn, 4),
+                                    "kernel": "prefill_bf16_kernel<128, true> (token stride "
+                                              "4*H*d in, [B,H,N,d] out)"},
+                "layer_ms": round(ms_pro_ip + ms_attn + ms_epi, 4),
+                "token_major_out": {
+                    "prefill_strided_ms": round(ms_attn_tm, 4),
+                    "group_norm_gate": line(ms_epi_tm, by_epi, "group_norm_gate_kernel<128>"),
+                    "layer_ms": round(ms_pro_ip + ms_attn_tm + ms_epi_tm, 4)}}}
 
 
 def measure_decode_multi(dev, stream, reps):
@@ -409,9 +450,7 @@ def main():
         res["decode_multi"] = measure_decode_multi(dev, stream, args.extra_reps)
         torch.cuda.empty_cache()
         print("[bench] layer ops (QK norm + RoPE, grouped norm x gate)", file=sys.stderr, flush=True)
-        res["layer_ops"] = measure_layer_ops(dev, stream, args.extra_reps)
-        lo = res["layer_ops"]
-        lo["layer_ms"] = round(lo["qk_norm_rope"]["ms"] + pre_ms + lo["group_norm_gate"]["ms"], 4)
+        res["layer_ops"] = measure_layer_ops(dev, stream, args.extra_reps, pre_ms)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(dict(q=p.q, k=p.k, v=p.v, slopes=p.slopes, N=N, d=d, H=H))

@@ -20,7 +20,7 @@
  *
  * Conventions shared by every entry point:
  *  - All tensor pointers are DEVICE pointers owned by the caller, contiguous
- *    and row-major.  q, k, v, out: [B][H][N][d] for prefill, [B][H][d] for a
+ *    and row-major (the strided calls below say otherwise).  q, k, v, out: [B][H][N][d] for prefill, [B][H][d] for a
  *    decode step.  State: [B][H][d][d] fp32 with i (the k index) slow and j
  *    (the v index) fast, so o = q . S is a row vector times a matrix.
  *    slopes: [H] fp32, shared by every sequence of the batch.
@@ -117,6 +117,41 @@ int la_prefill_varlen_f32(const float *q, const float *k, const float *v, const 
                           int64_t H, int64_t T, int64_t d, void *stream);
 
 /*
+ * Strided prefill: la_prefill / la_prefill_varlen reading q, k, v and writing
+ * out through element strides, so the kernel can read straight out of a packed
+ * projection buffer ([B,N,(q|k|v|...)*H*d], token-major) and write its output
+ * token-major for the next op, with no layout copies in between.  Same
+ * arithmetic and results, bitwise, as the contiguous calls.
+ *   Row (b, h, t) of q, k, v starts at element
+ *     b*in_bstride + h*in_hstride + t*in_tstride        (la_prefill_strided)
+ *     h*in_hstride + t*in_tstride, t in [0, T)          (la_prefill_varlen_strided)
+ *   from their own base pointers (the three share the strides), and holds d
+ *   contiguous bf16 channels; out uses the out_* strides the same way.  The
+ *   contiguous calls are the strides (H*N*d, N*d, d) and (T*d, d).
+ *   Strides are in elements, >= 0 and multiples of 8 (16-byte rows); token
+ *   strides are at least d (a slice's rows never overlap), and above 2^24
+ *   give LA_ERR_UNSUPPORTED.  Rows of different heads or sequences of the
+ *   inputs may overlap (they are only read); no two output rows may share an
+ *   element, and out's span
+ *   (base to last element) must not overlap the spans of q, k, v or the state.
+ *   State, slopes, cu_seqlens and every other rule: as la_prefill /
+ *   la_prefill_varlen.  Source: as la_prefill and la_prefill_varlen (Fig. 2 puts
+ *   the kernel between the QKV projection with its QK Norm and RoPE, and the
+ *   grouped RMSNorm, which both work in the projection's token-major layout).
+ */
+int la_prefill_strided(const void *q, const void *k, const void *v, const float *slopes,
+                       void *out, float *state, int64_t B, int64_t H, int64_t N, int64_t d,
+                       int64_t in_bstride, int64_t in_hstride, int64_t in_tstride,
+                       int64_t out_bstride, int64_t out_hstride, int64_t out_tstride,
+                       void *stream);
+
+int la_prefill_varlen_strided(const void *q, const void *k, const void *v, const float *slopes,
+                              const int64_t *cu_seqlens, int64_t nseq, void *out, float *states,
+                              int64_t H, int64_t T, int64_t d, int64_t in_hstride,
+                              int64_t in_tstride, int64_t out_hstride, int64_t out_tstride,
+                              void *stream);
+
+/*
  * One decode step for B*H sequences (one new token each).
  *   q, k, v     [B,H,d] bf16, read only.
  *   state       [B,H,d,d] fp32, updated in place: S' = lambda S + k^T v.
@@ -173,21 +208,28 @@ int la_decode_multi_f32(const float *q, const float *k, const float *v, const fl
  * kernel) and §2.1.1 (RMSNorm epsilon 1e-6; RoPE base 6,000,000 with rotary
  * dimension 64, i.e. partial RoPE on part of each head).
  *
- * la_qk_norm_rope: from the projection layout to the kernel layout.
+ * la_qk_norm_rope: from the projection layout to the kernel layout, or in place.
  *   q_in, k_in, v_in  bf16 rows [B,N,H,d]: element (b,t,h,i) at
  *                     (b*N + t)*in_stride + h*d + i; in_stride >= H*d and a
  *                     multiple of 8 (a packed [q|k|v|...] projection output
- *                     passes three offsets into one buffer).
+ *                     passes three offsets into one buffer).  v_in and
+ *                     v_out may both be NULL: v is then not touched.
  *   q_norm_weight, k_norm_weight  [d] fp32, 16-byte aligned.
  *   For q and k: x <- x / sqrt(mean_i x_i^2 + eps) * weight (RMSNorm over the
  *   head dimension), then rotate-half RoPE on the first rot_dim dims at
  *   position p = pos0 + t: for j < rot_dim/2, with a = p * theta^(-2j/rot_dim),
  *     x'_j = x_j cos a - x_{j+rot/2} sin a,   x'_{j+rot/2} = x_{j+rot/2} cos a + x_j sin a;
  *   dims >= rot_dim pass through.  v is only moved.
- *   q_out, k_out, v_out  bf16 [B,H,N,d] (the layout la_prefill reads).
+ *   q_out, k_out, v_out  bf16 [B,H,N,d] (the layout la_prefill reads).  Or
+ *                     in place: q_out == q_in and k_out == k_in write q and
+ *                     k back over their inputs in the projection layout (for
+ *                     la_prefill_strided); q, k and v rows must then share no
+ *                     element (one packed buffer with disjoint column ranges
+ *                     is fine), and v_out, if given, lies outside all of them.
  *   rot_dim in {0, 16, 32, 64, 128} (<= d), theta > 1 when rot_dim > 0,
  *   pos0 >= 0, eps >= 0.  Other rot_dim values give LA_ERR_UNSUPPORTED.
- *   Outputs must not overlap the inputs or each other.  B*N == 0 is a no-op.
+ *   Out of place, outputs must not overlap the inputs or each other; only
+ *   one of q and k in place is LA_ERR_INVALID_ARG.  B*N == 0 is a no-op.
  */
 int la_qk_norm_rope(const void *q_in, const void *k_in, const void *v_in, int64_t in_stride,
                     const float *q_norm_weight, const float *k_norm_weight, double theta,
@@ -195,8 +237,11 @@ int la_qk_norm_rope(const void *q_in, const void *k_in, const void *v_in, int64_
                     void *v_out, int64_t B, int64_t N, int64_t H, int64_t d, void *stream);
 
 /*
- * la_group_norm_gate: from the kernel layout back to the projection layout.
- *   o            bf16 [B,H,N,d] (la_prefill's output).
+ * la_group_norm_gate: from the kernel's output back to the projection layout.
+ *   o            bf16 rows of d channels, row (b, h, t) at element
+ *                b*o_bstride + h*o_hstride + t*o_tstride (strides >= 0 and
+ *                multiples of 8): (H*N*d, N*d, d) for la_prefill's output,
+ *                (N*H*d, d, H*d) for a token-major one (la_prefill_strided).
  *   gate         bf16 rows [B,N,H*d] at token stride gate_stride (>= H*d, a
  *                multiple of 8).
  *   norm_weight  [H*d] fp32, 16-byte aligned.
@@ -208,9 +253,10 @@ int la_qk_norm_rope(const void *q_in, const void *k_in, const void *v_in, int64_
  *   not give the group size (a head, group = d, is the plain reading).
  *   eps >= 0.  B*N == 0 is a no-op.
  */
-int la_group_norm_gate(const void *o, const void *gate, int64_t gate_stride,
-                       const float *norm_weight, int64_t group, float eps, void *y,
-                       int64_t B, int64_t N, int64_t H, int64_t d, void *stream);
+int la_group_norm_gate(const void *o, int64_t o_bstride, int64_t o_hstride, int64_t o_tstride,
+                       const void *gate, int64_t gate_stride, const float *norm_weight,
+                       int64_t group, float eps, void *y, int64_t B, int64_t N, int64_t H,
+                       int64_t d, void *stream);
 
 /* Static, NUL-terminated description of a status code ("unknown status" for
  * values outside la_status).  Never NULL; the caller must not free it. */
@@ -219,7 +265,7 @@ const char *la_status_string(int status);
 /* ABI version of this header (incremented on incompatible changes). */
 int la_abi_version(void);
 
-#define LA_ABI_VERSION 1
+#define LA_ABI_VERSION 2
 
 #ifdef __cplusplus
 }

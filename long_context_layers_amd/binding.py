@@ -1,9 +1,10 @@
 """ctypes binding of liblightning_attn.so (argument marshalling only).
 
-Every function here checks dtypes, devices, shapes and contiguity, then passes
-raw device pointers and the current HIP stream to the C ABI declared in
-``include/lightning_attn.h``.  PyTorch only provides device memory and
-streams; all of the layer's arithmetic runs in the library's HIP kernels.
+Every function here checks dtypes, devices, shapes and strides, then passes
+raw device pointers, sizes and element strides and the current HIP stream to
+the C ABI declared in ``include/lightning_attn.h``.  PyTorch only provides
+device memory and streams; all of the layer's arithmetic runs in the
+library's HIP kernels.
 There is no fallback: if the library is missing or a call fails, an error is
 raised.
 """
@@ -26,18 +27,22 @@ SIGNATURES = {
     "la_prefill_f32": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], _INT),
     "la_prefill_varlen": ([_P, _P, _P, _P, _P, _I64, _P, _P, _I64, _I64, _I64, _P], _INT),
     "la_prefill_varlen_f32": ([_P, _P, _P, _P, _P, _I64, _P, _P, _I64, _I64, _I64, _P], _INT),
+    "la_prefill_strided": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64,
+                            _I64, _I64, _I64, _I64, _I64, _I64, _P], _INT),
+    "la_prefill_varlen_strided": ([_P, _P, _P, _P, _P, _I64, _P, _P, _I64, _I64, _I64,
+                                   _I64, _I64, _I64, _I64, _P], _INT),
     "la_decode_step": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], _INT),
     "la_decode_multi": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], _INT),
     "la_decode_multi_f32": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], _INT),
     "la_decode_step_f32": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], _INT),
     "la_qk_norm_rope": ([_P, _P, _P, _I64, _P, _P, ctypes.c_double, _I64, _I64, ctypes.c_float,
                          _P, _P, _P, _I64, _I64, _I64, _I64, _P], _INT),
-    "la_group_norm_gate": ([_P, _P, _I64, _P, _I64, ctypes.c_float, _P, _I64, _I64, _I64, _I64,
-                            _P], _INT),
+    "la_group_norm_gate": ([_P, _I64, _I64, _I64, _P, _I64, _P, _I64, ctypes.c_float, _P,
+                            _I64, _I64, _I64, _I64, _P], _INT),
     "la_status_string": ([_INT], ctypes.c_char_p),
     "la_abi_version": ([], _INT),
 }
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 _lock = threading.Lock()
 _lib = None
@@ -93,6 +98,34 @@ def _need(t: torch.Tensor, name: str, dtype, dev, shape):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _view(t: torch.Tensor, name: str, dtype, dev, shape):
+    """A bf16 view of `shape` with unit channel stride: its other strides."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != dev or t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} on {dev}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.stride(-1) != 1 and t.shape[-1] > 1:
+        raise ValueError(f"{name} must have a unit channel stride")
+    return tuple(t.stride()[:-1])
+
+
+def _strided(q, k, v, out, dt, dev, shape) -> bool:
+    """True if q, k, v or out is a non-contiguous view that the strided
+    bf16 prefill takes (q, k, v sharing one set of strides)."""
+    ts = (q, k, v) if out is None else (q, k, v, out)
+    if all(isinstance(t, torch.Tensor) and t.is_contiguous() for t in ts):
+        return False
+    if dt != torch.bfloat16:
+        raise ValueError("strided q/k/v/out are taken for bfloat16 only; pass contiguous fp32 tensors")
+    st = _view(q, "q", dt, dev, shape)
+    for t, n in ((k, "k"), (v, "v")):
+        if _view(t, n, dt, dev, shape) != st:
+            raise ValueError("q, k and v must share one set of strides")
+    return True
+
+
 def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: torch.Tensor,
             state: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Blockwise decayed causal linear attention over N tokens.
@@ -100,6 +133,9 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: torch.Ten
     q, k, v: [B,H,N,d] bf16 or fp32 on one GPU; slopes: [H] fp32;
     state: [B,H,d,d] fp32, IN = initial state, OUT = final state (in place).
     Returns out [B,H,N,d] (same dtype as q).  Enqueued on the current stream.
+    bf16 q, k, v (sharing one set of strides) and out may be strided views
+    with a unit channel stride, e.g. head-split slices of a token-major
+    projection buffer; such calls go to ``la_prefill_strided``.
     """
     if not isinstance(q, torch.Tensor) or q.dim() != 4:
         raise ValueError("q must be a [B,H,N,d] tensor")
@@ -111,9 +147,20 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: torch.Ten
     if dt not in (torch.bfloat16, torch.float32):
         raise TypeError("q/k/v must be bfloat16 or float32")
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n, dt, dev, (B, H, N, d))
+        _view(t, n, dt, dev, (B, H, N, d))
     _need(slopes, "slopes", torch.float32, dev, (H,))
     _need(state, "state", torch.float32, dev, (B, H, d, d))
+    if _strided(q, k, v, out, dt, dev, (B, H, N, d)):
+        if out is None:
+            out = torch.empty((B, H, N, d), dtype=dt, device=dev)
+        so = _view(out, "out", dt, dev, (B, H, N, d))
+        si = q.stride()[:-1]
+        with torch.cuda.device(dev):
+            rc = load_library().la_prefill_strided(
+                q.data_ptr(), k.data_ptr(), v.data_ptr(), slopes.data_ptr(), out.data_ptr(),
+                state.data_ptr(), B, H, N, d, *si, *so, _stream(dev))
+        _check(rc, "la_prefill_strided")
+        return out
     if out is None:
         out = torch.empty_like(q)
     else:
@@ -136,7 +183,9 @@ def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: to
     of every head); cu_seqlens: [nseq+1] int64 on the same GPU (0 = cu[0] <= ... <=
     cu[nseq] = T); slopes: [H] fp32; states: [nseq,H,d,d] fp32, IN = initial states,
     OUT = final states (in place).  Returns out [H,T,d].  Enqueued on the current
-    stream; the offsets are not read on the host.
+    stream; the offsets are not read on the host.  bf16 q, k, v (sharing one
+    set of strides) and out may be strided [H,T,d] views with a unit channel
+    stride (``la_prefill_varlen_strided``).
     """
     if not isinstance(q, torch.Tensor) or q.dim() != 3:
         raise ValueError("q must be a [H,T,d] tensor")
@@ -148,13 +197,25 @@ def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: to
     if dt not in (torch.bfloat16, torch.float32):
         raise TypeError("q/k/v must be bfloat16 or float32")
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n, dt, dev, (H, T, d))
+        _view(t, n, dt, dev, (H, T, d))
     if not isinstance(cu_seqlens, torch.Tensor) or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
         raise ValueError("cu_seqlens must be a [nseq+1] tensor with nseq >= 1")
     nseq = cu_seqlens.numel() - 1
     _need(cu_seqlens, "cu_seqlens", torch.int64, dev, (nseq + 1,))
     _need(slopes, "slopes", torch.float32, dev, (H,))
     _need(states, "states", torch.float32, dev, (nseq, H, d, d))
+    if _strided(q, k, v, out, dt, dev, (H, T, d)):
+        if out is None:
+            out = torch.empty((H, T, d), dtype=dt, device=dev)
+        so = _view(out, "out", dt, dev, (H, T, d))
+        si = q.stride()[:-1]
+        with torch.cuda.device(dev):
+            rc = load_library().la_prefill_varlen_strided(
+                q.data_ptr(), k.data_ptr(), v.data_ptr(), slopes.data_ptr(),
+                cu_seqlens.data_ptr(), nseq, out.data_ptr(), states.data_ptr(), H, T, d,
+                *si, *so, _stream(dev))
+        _check(rc, "la_prefill_varlen_strided")
+        return out
     if out is None:
         out = torch.empty_like(q)
     else:
@@ -250,15 +311,19 @@ def _rows(t: torch.Tensor, name: str, dev, shape):
     return t.stride(1)
 
 
-def qk_norm_rope(q_in: torch.Tensor, k_in: torch.Tensor, v_in: torch.Tensor,
+def qk_norm_rope(q_in: torch.Tensor, k_in: torch.Tensor, v_in: Optional[torch.Tensor],
                  q_norm_weight: torch.Tensor, k_norm_weight: torch.Tensor, H: int,
                  theta: float = 6.0e6, rot_dim: int = 64, pos0: int = 0, eps: float = 1e-6,
-                 outs=None):
+                 outs=None, inplace: bool = False):
     """QK RMSNorm + partial RoPE, and the move of q, k, v to the kernel layout.
 
     q_in, k_in, v_in: [B,N,H*d] bf16 views (a shared token stride is allowed,
     e.g. slices of one packed projection output); weights [d] fp32.
     Returns (q, k, v) as [B,H,N,d] bf16 (written into ``outs`` if given).
+    v_in None: v is not touched and the third result is None.
+    inplace: q and k are written back over q_in and k_in, and the results are
+    [B,H,N,d] views of them (v, if given, is still copied out), ready for the
+    strided prefill.
     """
     dev = q_in.device
     if dev.type != "cuda":
@@ -268,23 +333,41 @@ def qk_norm_rope(q_in: torch.Tensor, k_in: torch.Tensor, v_in: torch.Tensor,
     if d * H != HD:
         raise ValueError("last dimension must be H*d")
     st = _rows(q_in, "q_in", dev, (B, N, HD))
-    for t, n in ((k_in, "k_in"), (v_in, "v_in")):
+    ins = (k_in, "k_in"), (v_in, "v_in")
+    for t, n in ins if v_in is not None else ins[:1]:
         if _rows(t, n, dev, (B, N, HD)) != st:
             raise ValueError("q_in, k_in, v_in must share one token stride")
     _need(q_norm_weight, "q_norm_weight", torch.float32, dev, (d,))
     _need(k_norm_weight, "k_norm_weight", torch.float32, dev, (d,))
     if outs is None:
-        outs = tuple(torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev) for _ in range(3))
-    for t, n in zip(outs, ("q_out", "k_out", "v_out")):
-        _need(t, n, torch.bfloat16, dev, (B, H, N, d))
+        def new():
+            return torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev)
+        outs = (None if inplace else new(), None if inplace else new(),
+                None if v_in is None else new())
+    if inplace:
+        if outs[0] is not None or outs[1] is not None:
+            raise ValueError("inplace: q and k are written over q_in and k_in (outs[0:2] must be None)")
+        outs = (q_in.unflatten(2, (H, d)).transpose(1, 2), k_in.unflatten(2, (H, d)).transpose(1, 2),
+                outs[2])
+    else:
+        for t, n in zip(outs[:2], ("q_out", "k_out")):
+            _need(t, n, torch.bfloat16, dev, (B, H, N, d))
+    if (v_in is None) != (outs[2] is None):
+        raise ValueError("v_in and v_out must both be given or both be None")
+    if outs[2] is not None:
+        _need(outs[2], "v_out", torch.bfloat16, dev, (B, H, N, d))
     lib = load_library()
+    qo = q_in.data_ptr() if inplace else outs[0].data_ptr()
+    ko = k_in.data_ptr() if inplace else outs[1].data_ptr()
     with torch.cuda.device(dev):
-        rc = lib.la_qk_norm_rope(q_in.data_ptr(), k_in.data_ptr(), v_in.data_ptr(), st,
+        rc = lib.la_qk_norm_rope(q_in.data_ptr(), k_in.data_ptr(),
+                                 None if v_in is None else v_in.data_ptr(), st,
                                  q_norm_weight.data_ptr(), k_norm_weight.data_ptr(), float(theta),
-                                 rot_dim, pos0, float(eps), outs[0].data_ptr(), outs[1].data_ptr(),
-                                 outs[2].data_ptr(), B, N, H, d, _stream(dev))
+                                 rot_dim, pos0, float(eps), qo, ko,
+                                 None if outs[2] is None else outs[2].data_ptr(), B, N, H, d,
+                                 _stream(dev))
     _check(rc, "la_qk_norm_rope")
-    return outs
+    return tuple(outs)
 
 
 def group_norm_gate(o: torch.Tensor, gate: torch.Tensor, norm_weight: torch.Tensor,
@@ -292,8 +375,10 @@ def group_norm_gate(o: torch.Tensor, gate: torch.Tensor, norm_weight: torch.Tens
                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Grouped RMSNorm of the kernel output times sigmoid(gate), back to [B,N,H*d].
 
-    o: [B,H,N,d] bf16; gate: [B,N,H*d] bf16 view (any token stride);
-    norm_weight: [H*d] fp32; group: channels per group (default d, one head).
+    o: [B,H,N,d] bf16, any strides with a unit channel stride (la_prefill's
+    contiguous output, or a token-major one from the strided prefill);
+    gate: [B,N,H*d] bf16 view (any token stride); norm_weight: [H*d] fp32;
+    group: channels per group (default d, one head).
     """
     if not isinstance(o, torch.Tensor) or o.dim() != 4:
         raise ValueError("o must be a [B,H,N,d] tensor")
@@ -301,7 +386,7 @@ def group_norm_gate(o: torch.Tensor, gate: torch.Tensor, norm_weight: torch.Tens
     if dev.type != "cuda":
         raise ValueError("group_norm_gate runs on GPU tensors only (no CPU path)")
     B, H, N, d = o.shape
-    _need(o, "o", torch.bfloat16, dev, (B, H, N, d))
+    os_ = _view(o, "o", torch.bfloat16, dev, (B, H, N, d))
     gst = _rows(gate, "gate", dev, (B, N, H * d))
     _need(norm_weight, "norm_weight", torch.float32, dev, (H * d,))
     if out is None:
@@ -310,8 +395,8 @@ def group_norm_gate(o: torch.Tensor, gate: torch.Tensor, norm_weight: torch.Tens
         _need(out, "out", torch.bfloat16, dev, (B, N, H * d))
     lib = load_library()
     with torch.cuda.device(dev):
-        rc = lib.la_group_norm_gate(o.data_ptr(), gate.data_ptr(), gst, norm_weight.data_ptr(),
-                                    d if group is None else group, float(eps), out.data_ptr(),
-                                    B, N, H, d, _stream(dev))
+        rc = lib.la_group_norm_gate(o.data_ptr(), *os_, gate.data_ptr(), gst,
+                                    norm_weight.data_ptr(), d if group is None else group,
+                                    float(eps), out.data_ptr(), B, N, H, d, _stream(dev))
     _check(rc, "la_group_norm_gate")
     return out

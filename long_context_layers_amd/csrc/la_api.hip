@@ -126,6 +126,106 @@ bool span_ok(int64_t rows, int64_t stride, int64_t width, int64_t *bytes) {
     return true;
 }
 
+// A strided view of n[0] x n[1] x n[2] rows of d contiguous elements of
+// `elem` bytes, row (i, j, t) at element i*s[0] + j*s[1] + t*s[2]: the byte
+// span from the base to one past its last element (false on overflow or a
+// negative stride; an empty view spans nothing)
+bool view_span(const int64_t n[3], const int64_t s[3], int64_t d, int64_t elem, int64_t *bytes)
+{
+    for (int i = 0; i < 3; ++i)
+        if (n[i] == 0) { *bytes = 0; return true; }
+    int64_t last = 0;
+    for (int i = 0; i < 3; ++i) {
+        int64_t t;
+        if (n[i] < 0 || s[i] < 0 || !mul_ok(n[i] - 1, s[i], &t) || last > INT64_MAX - t)
+            return false;
+        last += t;
+    }
+    if (last > INT64_MAX / elem - d) return false;
+    *bytes = (last + d) * elem;
+    return true;
+}
+
+// no two elements of the view (spans already checked) share an address: with
+// the dimensions of more than one entry sorted by stride, each stride is at
+// least the extent of everything below it
+bool view_disjoint(const int64_t n[3], const int64_t s[3], int64_t d)
+{
+    int64_t ss[3], nn[3];
+    int m = 0;
+    for (int i = 0; i < 3; ++i)
+        if (n[i] > 1) { ss[m] = s[i]; nn[m] = n[i]; ++m; }
+    for (int i = 1; i < m; ++i)                      // insertion sort by stride
+        for (int j = i; j > 0 && ss[j] < ss[j - 1]; --j) {
+            const int64_t a = ss[j], b = nn[j];
+            ss[j] = ss[j - 1]; nn[j] = nn[j - 1];
+            ss[j - 1] = a; nn[j - 1] = b;
+        }
+    int64_t ext = d;
+    for (int i = 0; i < m; ++i) {
+        if (ss[i] < ext) return false;
+        ext += ss[i] * (nn[i] - 1);
+    }
+    return true;
+}
+
+// strides of the strided prefill: multiples of 8 (16-byte rows), token
+// strides small enough for the kernel's 32-bit buffer offsets over a block
+constexpr int64_t MAX_TOKEN_STRIDE = int64_t(1) << 24;
+
+bool strides_ok(const int64_t s[3]) {
+    for (int i = 0; i < 3; ++i)
+        if (s[i] < 0 || s[i] % 8 != 0) return false;
+    return true;
+}
+
+// strided bf16 prefill: q, k, v share the view (n, si), out has (n, so)
+int check_strided(const void *q, const void *k, const void *v, const float *slopes,
+                  const void *out, const float *state, const int64_t n[3], const int64_t si[3],
+                  const int64_t so[3], int64_t nstate, int64_t d)
+{
+    int64_t rows;
+    if (!mul_ok(n[0], n[1], &rows) || !mul_ok(rows, n[2], &rows)) return LA_ERR_INVALID_ARG;
+    if (rows > 0 && (!q || !k || !v || !out)) return LA_ERR_INVALID_ARG;
+    if (!slopes || !state) return LA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
+    if (!strides_ok(si) || !strides_ok(so)) return LA_ERR_INVALID_ARG;
+    // token rows of one slice never overlap: the kernel's buffer ranges end at
+    // a block's last real row, which zero-fills the rows past it only then
+    if (si[2] < d || so[2] < d) return LA_ERR_INVALID_ARG;
+    int64_t in_bytes, out_bytes, st, st_bytes;
+    if (!view_span(n, si, d, 2, &in_bytes) || !view_span(n, so, d, 2, &out_bytes) ||
+        !mul_ok(nstate, d * d, &st) || !mul_ok(st, 4, &st_bytes))
+        return LA_ERR_INVALID_ARG;
+    if (!view_disjoint(n, so, d)) return LA_ERR_INVALID_ARG;
+    if (si[2] > MAX_TOKEN_STRIDE || so[2] > MAX_TOKEN_STRIDE) return LA_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) ||
+        !aligned(state, 16) || !aligned(slopes, 4))
+        return LA_ERR_INVALID_ARG;
+    if (overlap(out, out_bytes, q, in_bytes) || overlap(out, out_bytes, k, in_bytes) ||
+        overlap(out, out_bytes, v, in_bytes) || overlap(out, out_bytes, state, st_bytes))
+        return LA_ERR_INVALID_ARG;
+    return LA_OK;
+}
+
+// dense [seqs, H, N, d] strides, and the packed [H, T, d] ones
+la::Strides dense_strides(int64_t H, int64_t N, int64_t d) { return {H * N * d, N * d, d}; }
+la::Strides packed_strides(int64_t T, int64_t d) { return {0, T * d, d}; }
+
+// two [rows][width] bf16 arrays whose rows are `stride` elements apart share
+// no element: their spans are apart, or b's offset from a, taken modulo the
+// stride, leaves a whole row width on both sides
+bool rows_disjoint(const void *a, const void *b, int64_t rows, int64_t stride, int64_t width)
+{
+    int64_t span;
+    if (!span_ok(rows, stride, width, &span)) return false;
+    if (!overlap(a, span, b, span)) return true;
+    const intptr_t delta = reinterpret_cast<intptr_t>(b) - reinterpret_cast<intptr_t>(a);
+    if (delta % 2 != 0) return false;
+    const int64_t rem = ((int64_t)(delta / 2) % stride + stride) % stride;
+    return rem >= width && rem <= stride - width;
+}
+
 int check_layer_common(int64_t B, int64_t N, int64_t H, int64_t d)
 {
     if (B < 1 || N < 0 || H < 1) return LA_ERR_INVALID_ARG;
@@ -149,7 +249,8 @@ int la_prefill(const void *q, const void *k, const void *v, const float *slopes,
     if (rc != LA_OK) return rc;
     if (la::prefill_bf16_grid(B, H, (int)d) > 0x7fffffff) return LA_ERR_UNSUPPORTED;
     if (N == 0) return LA_OK;
-    const la::SeqMap map = {nullptr, H, N, 0};
+    const la::Strides s = dense_strides(H, N, d);
+    const la::SeqMap map = {nullptr, H, N, 0, s, s};
     return hip_status(la::launch_prefill_bf16(
         static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
         static_cast<const uint16_t *>(v), slopes, static_cast<uint16_t *>(out), state, B, map,
@@ -164,7 +265,8 @@ int la_prefill_varlen(const void *q, const void *k, const void *v, const float *
     if (rc != LA_OK) return rc;
     if (la::prefill_bf16_grid(nseq, H, (int)d) > 0x7fffffff) return LA_ERR_UNSUPPORTED;
     if (T == 0) return LA_OK;
-    const la::SeqMap map = {cu_seqlens, H, 0, T};
+    const la::Strides s = packed_strides(T, d);
+    const la::SeqMap map = {cu_seqlens, H, 0, T, s, s};
     return hip_status(la::launch_prefill_bf16(
         static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
         static_cast<const uint16_t *>(v), slopes, static_cast<uint16_t *>(out), states, nseq,
@@ -179,7 +281,8 @@ int la_prefill_f32(const float *q, const float *k, const float *v, const float *
     if (rc != LA_OK) return rc;
     if (la::prefill_f32_grid(B, H, (int)d) > 0x7fffffff) return LA_ERR_UNSUPPORTED;
     if (N == 0) return LA_OK;
-    const la::SeqMap map = {nullptr, H, N, 0};
+    const la::Strides s = dense_strides(H, N, d);
+    const la::SeqMap map = {nullptr, H, N, 0, s, s};
     return hip_status(la::launch_prefill_f32(q, k, v, slopes, out, state, B, map, (int)d,
                                              static_cast<hipStream_t>(stream)));
 }
@@ -192,9 +295,59 @@ int la_prefill_varlen_f32(const float *q, const float *k, const float *v, const 
     if (rc != LA_OK) return rc;
     if (la::prefill_f32_grid(nseq, H, (int)d) > 0x7fffffff) return LA_ERR_UNSUPPORTED;
     if (T == 0) return LA_OK;
-    const la::SeqMap map = {cu_seqlens, H, 0, T};
+    const la::Strides s = packed_strides(T, d);
+    const la::SeqMap map = {cu_seqlens, H, 0, T, s, s};
     return hip_status(la::launch_prefill_f32(q, k, v, slopes, out, states, nseq, map, (int)d,
                                              static_cast<hipStream_t>(stream)));
+}
+
+int la_prefill_strided(const void *q, const void *k, const void *v, const float *slopes,
+                       void *out, float *state, int64_t B, int64_t H, int64_t N, int64_t d,
+                       int64_t in_bstride, int64_t in_hstride, int64_t in_tstride,
+                       int64_t out_bstride, int64_t out_hstride, int64_t out_tstride,
+                       void *stream)
+{
+    if (B < 1 || H < 1 || N < 0) return LA_ERR_INVALID_ARG;
+    int64_t bh;
+    if (!mul_ok(B, H, &bh)) return LA_ERR_INVALID_ARG;
+    const int64_t n[3] = {B, H, N};
+    const int64_t si[3] = {in_bstride, in_hstride, in_tstride};
+    const int64_t so[3] = {out_bstride, out_hstride, out_tstride};
+    const int rc = check_strided(q, k, v, slopes, out, state, n, si, so, bh, d);
+    if (rc != LA_OK) return rc;
+    if (la::prefill_bf16_grid(B, H, (int)d) > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+    if (N == 0) return LA_OK;
+    const la::SeqMap map = {nullptr, H, N, 0, {in_bstride, in_hstride, in_tstride},
+                            {out_bstride, out_hstride, out_tstride}};
+    return hip_status(la::launch_prefill_bf16(
+        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+        static_cast<const uint16_t *>(v), slopes, static_cast<uint16_t *>(out), state, B, map,
+        (int)d, static_cast<hipStream_t>(stream)));
+}
+
+int la_prefill_varlen_strided(const void *q, const void *k, const void *v, const float *slopes,
+                              const int64_t *cu_seqlens, int64_t nseq, void *out, float *states,
+                              int64_t H, int64_t T, int64_t d, int64_t in_hstride,
+                              int64_t in_tstride, int64_t out_hstride, int64_t out_tstride,
+                              void *stream)
+{
+    if (!cu_seqlens || !aligned(cu_seqlens, 8)) return LA_ERR_INVALID_ARG;
+    if (nseq < 1 || H < 1 || T < 0) return LA_ERR_INVALID_ARG;
+    int64_t nstate;
+    if (!mul_ok(nseq, H, &nstate)) return LA_ERR_INVALID_ARG;
+    const int64_t n[3] = {1, H, T};
+    const int64_t si[3] = {0, in_hstride, in_tstride};
+    const int64_t so[3] = {0, out_hstride, out_tstride};
+    const int rc = check_strided(q, k, v, slopes, out, states, n, si, so, nstate, d);
+    if (rc != LA_OK) return rc;
+    if (la::prefill_bf16_grid(nseq, H, (int)d) > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+    if (T == 0) return LA_OK;
+    const la::SeqMap map = {cu_seqlens, H, 0, T, {0, in_hstride, in_tstride},
+                            {0, out_hstride, out_tstride}};
+    return hip_status(la::launch_prefill_bf16(
+        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+        static_cast<const uint16_t *>(v), slopes, static_cast<uint16_t *>(out), states, nseq,
+        map, (int)d, static_cast<hipStream_t>(stream)));
 }
 
 int la_decode_step(const void *q, const void *k, const void *v, const float *slopes,
@@ -248,7 +401,8 @@ int la_qk_norm_rope(const void *q_in, const void *k_in, const void *v_in, int64_
     int rc = check_layer_common(B, N, H, d);
     if (rc != LA_OK) return rc;
     const int64_t rows = B * N;
-    if (rows > 0 && (!q_in || !k_in || !v_in || !q_out || !k_out || !v_out))
+    const bool with_v = v_in || v_out;
+    if (rows > 0 && (!q_in || !k_in || !q_out || !k_out || (with_v && (!v_in || !v_out))))
         return LA_ERR_INVALID_ARG;
     if (!q_norm_weight || !k_norm_weight || !aligned(q_norm_weight, 16) ||
         !aligned(k_norm_weight, 16))
@@ -262,26 +416,43 @@ int la_qk_norm_rope(const void *q_in, const void *k_in, const void *v_in, int64_
     if (!mul_ok(rows, H, &rh) || !span_ok(rows, in_stride, hd, &in_bytes) ||
         !span_ok(rh, d, d, &out_bytes))
         return LA_ERR_INVALID_ARG;
+    // in place: q and k are written back over themselves (projection layout)
+    const bool inplace = q_out == q_in && k_out == k_in;
+    if (rows > 0 && !inplace && (q_out == q_in || k_out == k_in)) return LA_ERR_INVALID_ARG;
+    const int nin = with_v ? 3 : 2;
     const void *ins[3] = {q_in, k_in, v_in};
     const void *outs[3] = {q_out, k_out, v_out};
-    for (int i = 0; i < 3; ++i) {
+    for (int i = 0; i < nin; ++i)
         if (!aligned(ins[i], 16) || !aligned(outs[i], 16)) return LA_ERR_INVALID_ARG;
-        for (int j = 0; j < 3; ++j)
-            if (overlap(outs[i], out_bytes, ins[j], in_bytes)) return LA_ERR_INVALID_ARG;
-        for (int j = 0; j < i; ++j)
-            if (overlap(outs[i], out_bytes, outs[j], out_bytes)) return LA_ERR_INVALID_ARG;
+    if (inplace) {
+        // q, k and v rows read element-disjoint; the v copy lands outside all of them
+        for (int i = 0; i < nin; ++i)
+            for (int j = 0; j < i; ++j)
+                if (!rows_disjoint(ins[i], ins[j], rows, in_stride, hd)) return LA_ERR_INVALID_ARG;
+        if (with_v)
+            for (int j = 0; j < 3; ++j)
+                if (overlap(v_out, out_bytes, ins[j], in_bytes)) return LA_ERR_INVALID_ARG;
+    } else {
+        for (int i = 0; i < nin; ++i) {
+            for (int j = 0; j < nin; ++j)
+                if (overlap(outs[i], out_bytes, ins[j], in_bytes)) return LA_ERR_INVALID_ARG;
+            for (int j = 0; j < i; ++j)
+                if (overlap(outs[i], out_bytes, outs[j], out_bytes)) return LA_ERR_INVALID_ARG;
+        }
     }
     if (rows == 0) return LA_OK;
     return hip_status(la::launch_qk_norm_rope(
         static_cast<const uint16_t *>(q_in), static_cast<const uint16_t *>(k_in),
-        static_cast<const uint16_t *>(v_in), in_stride, q_norm_weight, k_norm_weight, theta,
-        (int)rot_dim, pos0, eps, static_cast<uint16_t *>(q_out), static_cast<uint16_t *>(k_out),
-        static_cast<uint16_t *>(v_out), B, N, H, (int)d, static_cast<hipStream_t>(stream)));
+        static_cast<const uint16_t *>(with_v ? v_in : nullptr), in_stride, q_norm_weight,
+        k_norm_weight, theta, (int)rot_dim, pos0, eps, static_cast<uint16_t *>(q_out),
+        static_cast<uint16_t *>(k_out), static_cast<uint16_t *>(with_v ? v_out : nullptr),
+        inplace ? 1 : 0, B, N, H, (int)d, static_cast<hipStream_t>(stream)));
 }
 
-int la_group_norm_gate(const void *o, const void *gate, int64_t gate_stride,
-                       const float *norm_weight, int64_t group, float eps, void *y,
-                       int64_t B, int64_t N, int64_t H, int64_t d, void *stream)
+int la_group_norm_gate(const void *o, int64_t o_bstride, int64_t o_hstride, int64_t o_tstride,
+                       const void *gate, int64_t gate_stride, const float *norm_weight,
+                       int64_t group, float eps, void *y, int64_t B, int64_t N, int64_t H,
+                       int64_t d, void *stream)
 {
     int rc = check_layer_common(B, N, H, d);
     if (rc != LA_OK) return rc;
@@ -292,8 +463,10 @@ int la_group_norm_gate(const void *o, const void *gate, int64_t gate_stride,
     int64_t hd;
     if (!mul_ok(H, d, &hd) || gate_stride < hd || gate_stride % 8 != 0) return LA_ERR_INVALID_ARG;
     if (!(eps >= 0.0f)) return LA_ERR_INVALID_ARG;
-    int64_t rh, o_bytes, g_bytes, y_bytes;
-    if (!mul_ok(rows, H, &rh) || !span_ok(rh, d, d, &o_bytes) ||
+    const int64_t n[3] = {B, H, N};
+    const int64_t os[3] = {o_bstride, o_hstride, o_tstride};
+    int64_t o_bytes, g_bytes, y_bytes;
+    if (!strides_ok(os) || !view_span(n, os, d, 2, &o_bytes) ||
         !span_ok(rows, gate_stride, hd, &g_bytes) || !span_ok(rows, hd, hd, &y_bytes))
         return LA_ERR_INVALID_ARG;
     if (!aligned(o, 16) || !aligned(gate, 16) || !aligned(y, 16)) return LA_ERR_INVALID_ARG;
@@ -301,7 +474,7 @@ int la_group_norm_gate(const void *o, const void *gate, int64_t gate_stride,
         return LA_ERR_INVALID_ARG;
     if (rows == 0) return LA_OK;
     return hip_status(la::launch_group_norm_gate(
-        static_cast<const uint16_t *>(o), static_cast<const uint16_t *>(gate), gate_stride,
+        static_cast<const uint16_t *>(o), os, static_cast<const uint16_t *>(gate), gate_stride,
         norm_weight, (int)group, eps, static_cast<uint16_t *>(y), B, N, H, (int)d,
         static_cast<hipStream_t>(stream)));
 }

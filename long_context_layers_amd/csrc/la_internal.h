@@ -8,28 +8,38 @@
 
 namespace la {
 
+// Element strides of a tensor's rows: element (b or sequence, head h, token
+// t, channel i) sits at b*sb + h*sh + t*st + i (channels contiguous).
+struct Strides {
+    int64_t sb, sh, st;
+};
+
 // Where the tokens of one (sequence, head) slice of a prefill launch live.
-// Dense launches: q, k, v, out are [B][H][N][d] and slice (b, h) is rows
-// (b*H + h)*N .. +N.  Packed launches: they are [H][T][d] with sequence i in
-// rows cu[i] .. cu[i+1] of every head (offsets clamped into [0, T], so
-// malformed offsets still address only rows of the tensors).  In both cases
-// the state of slice (seq, h) is state[(seq*H + h)*d*d ..].
+// Dense launches: slice (b, h) holds N tokens starting at b*sb + h*sh.  Packed
+// launches: sequence i is tokens cu[i] .. cu[i+1] of every head, starting at
+// h*sh + cu[i]*st (offsets clamped into [0, T], so malformed offsets still
+// address only rows of the tensors; sb is unused).  q, k and v share `in`,
+// the output has `out`.  The state of slice (seq, h) is state[(seq*H + h)*d*d ..].
 struct SeqMap {
     const int64_t *cu;    // null: dense launch
     int64_t H, N, T;      // heads; dense sequence length; packed total length
+    Strides in, out;
 };
 
+// start offsets (elements) of slice (seq, h) in the inputs and the output, and its length
 __device__ __forceinline__ void seq_slice(const SeqMap &m, int64_t seq, int64_t h,
-                                          int64_t *row0, int64_t *len)
+                                          int64_t *in0, int64_t *out0, int64_t *len)
 {
     if (!m.cu) {
-        *row0 = (seq * m.H + h) * m.N;
+        *in0 = seq * m.in.sb + h * m.in.sh;
+        *out0 = seq * m.out.sb + h * m.out.sh;
         *len = m.N;
         return;
     }
     const int64_t a = min(max(m.cu[seq], (int64_t)0), m.T);
     const int64_t b = min(max(m.cu[seq + 1], a), m.T);
-    *row0 = h * m.T + a;
+    *in0 = h * m.in.sh + a * m.in.st;
+    *out0 = h * m.out.sh + a * m.out.st;
     *len = b - a;
 }
 
@@ -63,11 +73,12 @@ int decode_multi_max_tokens();
 hipError_t launch_qk_norm_rope(const uint16_t *qi, const uint16_t *ki, const uint16_t *vi,
                                int64_t in_stride, const float *qw, const float *kw, double theta,
                                int rot, int64_t pos0, float eps, uint16_t *qo, uint16_t *ko,
-                               uint16_t *vo, int64_t B, int64_t N, int64_t H, int d,
+                               uint16_t *vo, int inplace, int64_t B, int64_t N, int64_t H, int d,
                                hipStream_t stream);
-hipError_t launch_group_norm_gate(const uint16_t *o, const uint16_t *g, int64_t gate_stride,
-                                  const float *w, int group, float eps, uint16_t *y, int64_t B,
-                                  int64_t N, int64_t H, int d, hipStream_t stream);
+hipError_t launch_group_norm_gate(const uint16_t *o, const int64_t os[3], const uint16_t *g,
+                                  int64_t gate_stride, const float *w, int group, float eps,
+                                  uint16_t *y, int64_t B, int64_t N, int64_t H, int d,
+                                  hipStream_t stream);
 
 // number of workgroups one prefill launch over `seqs` sequences uses
 int64_t prefill_bf16_grid(int64_t seqs, int64_t H, int d);

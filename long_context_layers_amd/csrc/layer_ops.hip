@@ -8,9 +8,11 @@
 // qk_norm_rope: q, k rows [B,N,H,d] (projection layout, any token stride) ->
 //   RMSNorm over d with a per-tensor weight -> rotate-half RoPE on the first
 //   rot dims (pairs j, j + rot/2) at position pos0 + t -> rows [B,H,N,d] (the
-//   attention kernel's layout); v rows are moved to [B,H,N,d] unchanged.
-// group_norm_gate: o rows [B,H,N,d] -> RMSNorm over groups of G channels with
-//   a [H*d] weight -> times sigmoid(gate) -> rows [B,N,H*d].
+//   attention kernel's layout), or back over the inputs in place; v rows are
+//   moved to [B,H,N,d] unchanged, or left alone.
+// group_norm_gate: o rows (any strides: [B,H,N,d] from the attention kernel,
+//   or token-major) -> RMSNorm over groups of G channels with a [H*d] weight
+//   -> times sigmoid(gate) -> rows [B,N,H*d].
 //
 // Both are bound by HBM: every (token, head) row of d bf16 values (256 B at
 // d = 128) is read and written once, and a row is contiguous on both sides,
@@ -56,13 +58,15 @@ __device__ __forceinline__ void ldw8(const float *p, float (&w)[8]) {
 }
 __device__ __forceinline__ void st16(uint16_t *p, uint4 x) { *reinterpret_cast<uint4 *>(p) = x; }
 
+// In place (inplace != 0) each q/k row is written back over itself by the 16
+// lanes that read it, after they read it, so q, k and their outputs are not
+// restrict-qualified.  vi/vo null: v is not touched.
 template <int D>
 __global__ __launch_bounds__(LT) void qk_norm_rope_kernel(
-    const uint16_t *__restrict__ qi, const uint16_t *__restrict__ ki,
-    const uint16_t *__restrict__ vi, int64_t in_stride,
+    const uint16_t *qi, const uint16_t *ki, const uint16_t *__restrict__ vi, int64_t in_stride,
     const float *__restrict__ qw, const float *__restrict__ kw,
     double theta, int rot, int64_t pos0, float eps,
-    uint16_t *__restrict__ qo, uint16_t *__restrict__ ko, uint16_t *__restrict__ vo,
+    uint16_t *qo, uint16_t *ko, uint16_t *__restrict__ vo, int inplace,
     int64_t N, int64_t H)
 {
     constexpr int CH = D / 8;                         // 16-byte chunks per row
@@ -97,7 +101,7 @@ __global__ __launch_bounds__(LT) void qk_norm_rope_kernel(
 
     for (int64_t h = r0; h < H; h += RPP) {
         const int64_t src = bt * in_stride + h * D + 8 * c;
-        const int64_t dst = ((b * H + h) * N + t) * D + 8 * c;
+        const int64_t dst = inplace ? src : ((b * H + h) * N + t) * D + 8 * c;
 #pragma unroll
         for (int which = 0; which < 2; ++which) {
             float x[8];
@@ -118,13 +122,14 @@ __global__ __launch_bounds__(LT) void qk_norm_rope_kernel(
             }
             st16((which ? ko : qo) + dst, pack8(y));
         }
-        st16(vo + dst, ld16(vi + src));
+        if (vo) st16(vo + ((b * H + h) * N + t) * D + 8 * c, ld16(vi + src));
     }
 }
 
 template <int D>
 __global__ __launch_bounds__(LT) void group_norm_gate_kernel(
-    const uint16_t *__restrict__ o, const uint16_t *__restrict__ g, int64_t gate_stride,
+    const uint16_t *__restrict__ o, int64_t osb, int64_t osh, int64_t ost,
+    const uint16_t *__restrict__ g, int64_t gate_stride,
     const float *__restrict__ w, int group, float eps, uint16_t *__restrict__ y,
     int64_t N, int64_t H)
 {
@@ -137,7 +142,7 @@ __global__ __launch_bounds__(LT) void group_norm_gate_kernel(
 
     for (int64_t h = r0; h < H; h += RPP) {
         float x[8], gt[8];
-        unpack8(ld16(o + ((b * H + h) * N + t) * D + 8 * c), x);
+        unpack8(ld16(o + b * osb + h * osh + t * ost + 8 * c), x);
         unpack8(ld16(g + bt * gate_stride + h * D + 8 * c), gt);
         float ss = 0.f;
 #pragma unroll
@@ -160,25 +165,29 @@ __global__ __launch_bounds__(LT) void group_norm_gate_kernel(
 hipError_t launch_qk_norm_rope(const uint16_t *qi, const uint16_t *ki, const uint16_t *vi,
                                int64_t in_stride, const float *qw, const float *kw, double theta,
                                int rot, int64_t pos0, float eps, uint16_t *qo, uint16_t *ko,
-                               uint16_t *vo, int64_t B, int64_t N, int64_t H, int d,
+                               uint16_t *vo, int inplace, int64_t B, int64_t N, int64_t H, int d,
                                hipStream_t stream)
 {
     const dim3 grid((unsigned)(B * N)), block(LT);
     void *args[] = {(void *)&qi, (void *)&ki, (void *)&vi, (void *)&in_stride, (void *)&qw,
                     (void *)&kw, (void *)&theta, (void *)&rot, (void *)&pos0, (void *)&eps,
-                    (void *)&qo, (void *)&ko, (void *)&vo, (void *)&N, (void *)&H};
+                    (void *)&qo, (void *)&ko, (void *)&vo, (void *)&inplace, (void *)&N,
+                    (void *)&H};
     const void *fn = d == 64 ? (const void *)qk_norm_rope_kernel<64>
                              : (const void *)qk_norm_rope_kernel<128>;
     return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 
-hipError_t launch_group_norm_gate(const uint16_t *o, const uint16_t *g, int64_t gate_stride,
-                                  const float *w, int group, float eps, uint16_t *y, int64_t B,
-                                  int64_t N, int64_t H, int d, hipStream_t stream)
+hipError_t launch_group_norm_gate(const uint16_t *o, const int64_t os[3], const uint16_t *g,
+                                  int64_t gate_stride, const float *w, int group, float eps,
+                                  uint16_t *y, int64_t B, int64_t N, int64_t H, int d,
+                                  hipStream_t stream)
 {
     const dim3 grid((unsigned)(B * N)), block(LT);
-    void *args[] = {(void *)&o, (void *)&g, (void *)&gate_stride, (void *)&w, (void *)&group,
-                    (void *)&eps, (void *)&y, (void *)&N, (void *)&H};
+    int64_t osb = os[0], osh = os[1], ost = os[2];
+    void *args[] = {(void *)&o, (void *)&osb, (void *)&osh, (void *)&ost, (void *)&g,
+                    (void *)&gate_stride, (void *)&w, (void *)&group, (void *)&eps, (void *)&y,
+                    (void *)&N, (void *)&H};
     const void *fn = d == 64 ? (const void *)group_norm_gate_kernel<64>
                              : (const void *)group_norm_gate_kernel<128>;
     return hipLaunchKernel(fn, grid, block, args, 0, stream);

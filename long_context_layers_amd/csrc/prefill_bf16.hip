@@ -144,12 +144,16 @@ __device__ __forceinline__ int block_len(int64_t t0, int64_t N) {
     return t0 < 0 ? 0 : (int)max((int64_t)0, min((int64_t)PC, N - t0));
 }
 
+// rows t0 .. t0+63 of a slice whose rows are ts elements apart: the range
+// ends right after the last real row, so later rows read as zero and stores
+// to them are dropped (ts >= D, and 63*ts + D < 2^31 checked on the host)
 template <int D>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint16_t *base, int64_t t0,
-                                                              int64_t N)
+                                                              int64_t N, int ts)
 {
-    return __builtin_amdgcn_make_buffer_rsrc((void *)(base + t0 * D), (short)0,
-                                             block_len(t0, N) * D * 2, RSRC_WORD3);
+    const int c = block_len(t0, N);
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(base + t0 * ts), (short)0,
+                                             c == 0 ? 0 : ((c - 1) * ts + D) * 2, RSRC_WORD3);
 }
 
 __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -160,11 +164,11 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 template <int D>
 __device__ __forceinline__ void load_block(Regs<D> &r, const uint16_t *qh, const uint16_t *kh,
                                            const uint16_t *vh, int64_t t0, int64_t N,
-                                           const Addr<D> &ad)
+                                           int64_t ts, const Addr<D> &ad)
 {
-    const __amdgpu_buffer_rsrc_t rq = block_rsrc<D>(qh, t0, N);
-    const __amdgpu_buffer_rsrc_t rk = block_rsrc<D>(kh, t0, N);
-    const __amdgpu_buffer_rsrc_t rv = block_rsrc<D>(vh, t0, N);
+    const __amdgpu_buffer_rsrc_t rq = block_rsrc<D>(qh, t0, N, ts);
+    const __amdgpu_buffer_rsrc_t rk = block_rsrc<D>(kh, t0, N, ts);
+    const __amdgpu_buffer_rsrc_t rv = block_rsrc<D>(vh, t0, N, ts);
 #pragma unroll
     for (int u = 0; u < Regs<D>::NQ; ++u) {
         r.q[u] = bload16(rq, ad.qk[u]);
@@ -203,6 +207,7 @@ struct Ctx {                          // per-thread constants of one workgroup
     const uint16_t *qh, *kh, *vh;     // this (b, h) slice
     const uint16_t *oh;
     int64_t N, nblk;                  // nblk: blocks processed (a multiple of NSET)
+    int ts, ots;                      // token strides (elements) of q/k/v and of out (<= 2^24)
     float s;
     int j0;
 };
@@ -228,7 +233,7 @@ __device__ __forceinline__ void produce_step(const Ctx<D> &cx, Smem<D> &sm, Regs
     __syncthreads();                                   // barrier of block blk
     if (SET % 2 == 1) produce_store<D, 1>(cx, sm, rs[SET], blk + 1, p, wfull);
     else              produce_store<D, 0>(cx, sm, rs[SET], blk + 1, p, wfull);
-    load_block<D>(rs[SET], cx.qh, cx.kh, cx.vh, (blk + 1 + NSET) * PC, cx.N, ad);
+    load_block<D>(rs[SET], cx.qh, cx.kh, cx.vh, (blk + 1 + NSET) * PC, cx.N, cx.ts, ad);
 }
 
 template <int D>
@@ -238,16 +243,16 @@ __device__ void producer(const Ctx<D> &cx, Smem<D> &sm, int p)
 #pragma unroll
     for (int u = 0; u < Regs<D>::NQ; ++u) {
         const int ch = p + PT * u;
-        ad.qk[u] = (uint32_t)(((ch / (D / 8)) * D + (ch % (D / 8)) * 8) * 2);
+        ad.qk[u] = (uint32_t)(((ch / (D / 8)) * cx.ts + (ch % (D / 8)) * 8) * 2);
     }
-    ad.v = (uint32_t)(((p / 4) * D + cx.j0 + (p % 4) * 8) * 2);
+    ad.v = (uint32_t)(((p / 4) * cx.ts + cx.j0 + (p % 4) * 8) * 2);
     const float wfull = decay_pow(cx.s, PC - 1 - p / 4);       // lambda^(C-1-b)
 
     Regs<D> rs[NSET];                                           // set i holds block i (mod NSET)
 #pragma unroll
-    for (int i = 0; i < NSET; ++i) load_block<D>(rs[i], cx.qh, cx.kh, cx.vh, i * PC, cx.N, ad);
+    for (int i = 0; i < NSET; ++i) load_block<D>(rs[i], cx.qh, cx.kh, cx.vh, i * PC, cx.N, cx.ts, ad);
     produce_store<D, 0>(cx, sm, rs[0], 0, p, wfull);
-    load_block<D>(rs[0], cx.qh, cx.kh, cx.vh, NSET * PC, cx.N, ad);
+    load_block<D>(rs[0], cx.qh, cx.kh, cx.vh, NSET * PC, cx.N, cx.ts, ad);
 
     // block blk stages block blk+1 from set (blk+1) % NSET into buffer (blk+1) % 2
     for (int64_t blk = 0; blk < cx.nblk; blk += NSET) {
@@ -336,11 +341,15 @@ __device__ __forceinline__ void score_pv(const Smem<D> &sm, int buf, int bh,
 // columns 8h..8h+7 and 16+8h..16+8h+7, so each row is written as 32-byte runs
 // by two 16-byte stores per lane.
 template <int D>
-__device__ __forceinline__ void store_out(const Ctx<D> &cx, int64_t t0, int ah, const Lane<D> &ln,
+__device__ __forceinline__ int out_offset(const Ctx<D> &cx, int ah, const Lane<D> &ln) {
+    return ((32 * ah + ln.l32) * cx.ots + cx.j0 + 8 * ln.h) * 2;   // bytes, row 32ah + l32
+}
+
+template <int D>
+__device__ __forceinline__ void store_out(const Ctx<D> &cx, int64_t t0, int ooff,
                                           const f32x16 &acc)
 {
-    const __amdgpu_buffer_rsrc_t ro = block_rsrc<D>(cx.oh, t0, cx.N);   // rows past N dropped
-    const int a = 32 * ah + ln.l32;
+    const __amdgpu_buffer_rsrc_t ro = block_rsrc<D>(cx.oh, t0, cx.N, cx.ots);   // rows past N dropped
 #pragma unroll
     for (int pr = 0; pr < 2; ++pr) {
         const int g0 = 2 * pr, g1 = 2 * pr + 1;
@@ -352,7 +361,7 @@ __device__ __forceinline__ void store_out(const Ctx<D> &cx, int64_t t0, int ah, 
         const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
         u32x4 o;
         o[0] = s0[0]; o[1] = s1[0]; o[2] = s0[1]; o[3] = s1[1];
-        __builtin_amdgcn_raw_buffer_store_b128(o, ro, (a * D + cx.j0 + 16 * pr + 8 * ln.h) * 2, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(o, ro, ooff + 32 * pr, 0, 0);
     }
 }
 
@@ -436,13 +445,14 @@ __device__ void out0_wave(const Ctx<D> &cx, Smem<D> &sm, int lane)
     float dec[16];
     score_decay(dec, cx.s, 0, 0, ln.l32, ln.h);
     const float scale = decay_pow(cx.s, ln.l32 + 1);               // lambda^(a+1)
+    const int ooff = out_offset(cx, 0, ln);
     auto step = [&](int64_t blk, auto BUFC) {
         constexpr int BUF = decltype(BUFC)::value;
         __syncthreads();
         bf16x8 qf[D / 16];
         f32x16 acc = inter_term<D>(sm, BUF, BUF ^ 1, 0, ln, scale, qf);
         score_pv<D>(sm, BUF, 0, qf, dec, ln, acc);
-        store_out<D>(cx, blk * PC, 0, ln, acc);
+        store_out<D>(cx, blk * PC, ooff, acc);
     };
     for (int64_t blk = 0; blk < cx.nblk; blk += 2) {
         step(blk, std::integral_constant<int, 0>());
@@ -459,6 +469,7 @@ __device__ void out1_wave(const Ctx<D> &cx, Smem<D> &sm, int lane)
     float dec[16];
     score_decay(dec, cx.s, 1, 1, ln.l32, ln.h);
     const float scale = decay_pow(cx.s, 32 + ln.l32 + 1);
+    const int ooff = out_offset(cx, 1, ln);
     f32x16 prev = {};
     auto finish_prev = [&](int64_t pblk, int pbuf) {               // block pblk's tokens 32..63
         const float4 *op = reinterpret_cast<const float4 *>(&sm.OP[pbuf][lane][0]);
@@ -468,7 +479,7 @@ __device__ void out1_wave(const Ctx<D> &cx, Smem<D> &sm, int lane)
             prev[4 * u + 0] += x.x; prev[4 * u + 1] += x.y;
             prev[4 * u + 2] += x.z; prev[4 * u + 3] += x.w;
         }
-        store_out<D>(cx, pblk * PC, 1, ln, prev);
+        store_out<D>(cx, pblk * PC, ooff, prev);
     };
     auto step = [&](int64_t blk, auto BUFC) {
         constexpr int BUF = decltype(BUFC)::value;
@@ -514,7 +525,10 @@ __device__ void out1x_wave(const Ctx<D> &cx, Smem<D> &sm, int lane)
     __syncthreads();
 }
 
-template <int D>
+// STRIDED = false: rows of q, k, v and out are D elements apart (a
+// compile-time token stride; head and sequence offsets still come from the
+// map), so the contiguous layouts pay nothing for stride support.
+template <int D, bool STRIDED>
 __global__ __launch_bounds__(NTHREADS) void prefill_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const float *__restrict__ slopes,
@@ -542,8 +556,8 @@ __global__ __launch_bounds__(NTHREADS) void prefill_bf16_kernel(
         bh = blockIdx.x / NJ;
         slice = blockIdx.x % NJ;
     }
-    int64_t row0, N;
-    seq_slice(map, bh / map.H, bh % map.H, &row0, &N);
+    int64_t in0, out0, N;
+    seq_slice(map, bh / map.H, bh % map.H, &in0, &out0, &N);
 
     Ctx<D> cx;
     cx.j0 = (int)slice * PJ;
@@ -552,10 +566,12 @@ __global__ __launch_bounds__(NTHREADS) void prefill_bf16_kernel(
     // blocks processed: a multiple of NSET (trailing empty blocks are no-ops;
     // an empty sequence leaves its state unchanged)
     cx.nblk = ((N + PC - 1) / PC + NSET - 1) / NSET * NSET;
-    cx.qh = q + row0 * D;
-    cx.kh = k + row0 * D;
-    cx.vh = v + row0 * D;
-    cx.oh = out + row0 * D;
+    cx.qh = q + in0;
+    cx.kh = k + in0;
+    cx.vh = v + in0;
+    cx.oh = out + out0;
+    cx.ts = STRIDED ? (int)map.in.st : D;
+    cx.ots = STRIDED ? (int)map.out.st : D;
 
     const int lane = tid % 64;
     switch (wave) {
@@ -579,8 +595,11 @@ hipError_t launch_prefill_bf16(const uint16_t *q, const uint16_t *k, const uint1
     SeqMap m = map;
     void *args[] = {(void *)&q, (void *)&k, (void *)&v, (void *)&slopes,
                     (void *)&out, (void *)&state, (void *)&m};
-    const void *fn = d == 64 ? (const void *)prefill_bf16_kernel<64>
-                             : (const void *)prefill_bf16_kernel<128>;
+    const bool strided = map.in.st != d || map.out.st != d;
+    const void *fn = d == 64 ? (strided ? (const void *)prefill_bf16_kernel<64, true>
+                                        : (const void *)prefill_bf16_kernel<64, false>)
+                             : (strided ? (const void *)prefill_bf16_kernel<128, true>
+                                        : (const void *)prefill_bf16_kernel<128, false>);
     return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 

@@ -41,15 +41,16 @@ __global__ __launch_bounds__(FT) void prefill_f32_kernel(
     const int64_t bh = blockIdx.x / NJ;          // sequence * H + head
     const int j0 = (blockIdx.x % NJ) * FJ;
     const float s = slopes[bh % map.H];
-    int64_t row0, N;
-    seq_slice(map, bh / map.H, bh % map.H, &row0, &N);
+    int64_t in0, out0, N;
+    seq_slice(map, bh / map.H, bh % map.H, &in0, &out0, &N);
+    const int64_t ts = map.in.st, ots = map.out.st;   // token strides (elements)
     if (tid <= FC) pw[tid] = decay_pow(s, tid);
 
     float *St = state + bh * D * D;
     for (int e = tid; e < D * FJ; e += FT) Ss[e / FJ][e % FJ] = St[(e / FJ) * D + j0 + e % FJ];
 
-    const float *qb = q + row0 * D, *kb = k + row0 * D, *vb = v + row0 * D;
-    float *ob = out + row0 * D;
+    const float *qb = q + in0, *kb = k + in0, *vb = v + in0;
+    float *ob = out + out0;
 
     for (int64_t t0 = 0; t0 < N; t0 += FC) {
         const int c = (int)min((int64_t)FC, N - t0);
@@ -57,12 +58,12 @@ __global__ __launch_bounds__(FT) void prefill_f32_kernel(
         for (int e = tid; e < FC * D; e += FT) {
             const int a = e / D, f = e % D;
             const bool ok = a < c;
-            Qs[a][f] = ok ? qb[(t0 + a) * D + f] : 0.0f;
-            Ks[a][f] = ok ? kb[(t0 + a) * D + f] : 0.0f;
+            Qs[a][f] = ok ? qb[(t0 + a) * ts + f] : 0.0f;
+            Ks[a][f] = ok ? kb[(t0 + a) * ts + f] : 0.0f;
         }
         for (int e = tid; e < FC * FJ; e += FT) {
             const int a = e / FJ, j = e % FJ;
-            Vs[a][j] = a < c ? vb[(t0 + a) * D + j0 + j] : 0.0f;
+            Vs[a][j] = a < c ? vb[(t0 + a) * ts + j0 + j] : 0.0f;
         }
         __syncthreads();
         // decayed causal scores of the block
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(FT) void prefill_f32_kernel(
                 float inter = 0.0f, intra = 0.0f;
                 for (int i = 0; i < D; ++i) inter = fmaf(Qs[a][i], Ss[i][j], inter);
                 for (int b = 0; b <= a; ++b) intra = fmaf(Ps[a][b], Vs[b][j], intra);
-                ob[(t0 + a) * D + j0 + j] = fmaf(pw[a + 1], inter, intra);
+                ob[(t0 + a) * ots + j0 + j] = fmaf(pw[a + 1], inter, intra);
             }
         }
         __syncthreads();

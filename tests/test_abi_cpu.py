@@ -248,11 +248,12 @@ def _rope_args(**kw):
 
 
 def _gate_args(**kw):
-    a = dict(o=FAKE, g=FAKE + 0x100000, gstride=2 * 64, w=FAKE + 0x300000, group=64, eps=1e-6,
-             y=FAKE + 0x400000, B=1, N=0, H=2, d=64, stream=None)
+    a = dict(o=FAKE, ob=2 * 3 * 64, oh=3 * 64, ot=64, g=FAKE + 0x100000, gstride=2 * 64,
+             w=FAKE + 0x300000, group=64, eps=1e-6, y=FAKE + 0x400000, B=1, N=0, H=2, d=64,
+             stream=None)
     a.update(kw)
-    return [a[n] for n in ("o", "g", "gstride", "w", "group", "eps", "y", "B", "N", "H", "d",
-                           "stream")]
+    return [a[n] for n in ("o", "ob", "oh", "ot", "g", "gstride", "w", "group", "eps", "y", "B",
+                           "N", "H", "d", "stream")]
 
 
 def test_layer_ops_empty_is_a_noop(lib):
@@ -285,6 +286,7 @@ def test_qk_norm_rope_rejects_bad_arguments(lib, bad, code):
     (dict(gstride=64), LA_ERR_INVALID_ARG), (dict(eps=float("nan")), LA_ERR_INVALID_ARG),
     (dict(w=None), LA_ERR_INVALID_ARG), (dict(w=FAKE + 0x300008), LA_ERR_INVALID_ARG),
     (dict(d=32), LA_ERR_UNSUPPORTED), (dict(B=-1), LA_ERR_INVALID_ARG),
+    (dict(ot=68), LA_ERR_INVALID_ARG), (dict(oh=-64), LA_ERR_INVALID_ARG),   # o strides
 ])
 def test_group_norm_gate_rejects_bad_arguments(lib, bad, code):
     assert lib.la_group_norm_gate(*_gate_args(**bad)) == code
@@ -292,12 +294,75 @@ def test_group_norm_gate_rejects_bad_arguments(lib, bad, code):
 
 @needs_no_gpu
 @pytest.mark.parametrize("bad", [dict(qo=FAKE), dict(vo=FAKE + 0x100000), dict(ko=FAKE + 0x400000),
-                                 dict(q=None), dict(vo=None), dict(q=FAKE + 8)])
+                                 dict(q=None), dict(vo=None), dict(v=None), dict(q=FAKE + 8),
+                                 # in place: q and k rows interleaved in one buffer must not share elements
+                                 dict(k=FAKE + 64, qo=FAKE, ko=FAKE + 64, v=None, vo=None),
+                                 dict(k=FAKE + 3 * 2 * 64 * 2 - 128, qo=FAKE,
+                                      ko=FAKE + 3 * 2 * 64 * 2 - 128, v=None, vo=None),
+                                 # in place with v rows overlapping q's
+                                 dict(v=FAKE + 128, qo=FAKE, ko=FAKE + 0x100000),
+                                 # only q in place
+                                 dict(qo=FAKE, v=None, vo=None)])
 def test_qk_norm_rope_rejects_overlap_and_nulls(lib, bad):
     assert lib.la_qk_norm_rope(*_rope_args(N=3, **bad)) == LA_ERR_INVALID_ARG
 
 
 @needs_no_gpu
-@pytest.mark.parametrize("bad", [dict(y=FAKE), dict(y=FAKE + 0x100000), dict(o=None), dict(g=FAKE + 2)])
+@pytest.mark.parametrize("bad", [dict(y=FAKE), dict(y=FAKE + 0x100000), dict(o=None), dict(g=FAKE + 2),
+                                 dict(y=FAKE + 2 * 3 * 64 * 2 - 16)])   # y inside a strided o's span
 def test_group_norm_gate_rejects_overlap_and_nulls(lib, bad):
     assert lib.la_group_norm_gate(*_gate_args(N=3, **bad)) == LA_ERR_INVALID_ARG
+
+
+STRIDED = ["la_prefill_strided", "la_prefill_varlen_strided"]
+
+
+def _strided_args(fn, **kw):
+    # defaults: B=1, H=2, N (or T) tokens, d=64, token-major [B,N,H,d] layouts
+    a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, slopes=FAKE + 0x300000,
+             cu=FAKE + 0x380000, nseq=3, out=FAKE + 0x400000, state=FAKE + 0x500000,
+             B=1, H=2, N=0, d=64, ib=None, ih=64, it=128, ob=None, oh=64, ot=128, stream=None)
+    a.update(kw)
+    if fn == "la_prefill_strided":
+        ib = a["ib"] if a["ib"] is not None else a["N"] * a["it"]
+        ob = a["ob"] if a["ob"] is not None else a["N"] * a["ot"]
+        return [a[n] for n in ("q", "k", "v", "slopes", "out", "state", "B", "H", "N", "d")] + \
+            [ib, a["ih"], a["it"], ob, a["oh"], a["ot"], a["stream"]]
+    return [a[n] for n in ("q", "k", "v", "slopes", "cu", "nseq", "out", "state", "H", "N", "d",
+                           "ih", "it", "oh", "ot", "stream")]
+
+
+@pytest.mark.parametrize("fn", STRIDED)
+def test_strided_empty_is_a_noop(lib, fn):
+    assert getattr(lib, fn)(*_strided_args(fn, N=0)) == LA_OK
+    assert getattr(lib, fn)(*_strided_args(fn, N=0, q=None, k=None, v=None, out=None)) == LA_OK
+
+
+@pytest.mark.parametrize("fn", STRIDED)
+@pytest.mark.parametrize("bad,code", [
+    (dict(ih=60), LA_ERR_INVALID_ARG), (dict(it=-128), LA_ERR_INVALID_ARG),   # not a multiple of 8 / < 0
+    (dict(oh=4), LA_ERR_INVALID_ARG),
+    (dict(oh=32), LA_ERR_INVALID_ARG),              # output heads share elements
+    (dict(it=32), LA_ERR_INVALID_ARG), (dict(ot=0), LA_ERR_INVALID_ARG),   # token stride < d
+    (dict(slopes=None), LA_ERR_INVALID_ARG), (dict(state=None), LA_ERR_INVALID_ARG),
+    (dict(d=32), LA_ERR_UNSUPPORTED), (dict(q=FAKE + 8), LA_ERR_INVALID_ARG),
+    (dict(out=FAKE + 0x400008), LA_ERR_INVALID_ARG),
+])
+def test_strided_rejects_bad_arguments(lib, fn, bad, code):
+    # no tokens: even a missing check could not reach a launch
+    assert getattr(lib, fn)(*_strided_args(fn, N=0, **bad)) == code
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("fn", STRIDED)
+@pytest.mark.parametrize("bad,code", [
+    (dict(ot=64), LA_ERR_INVALID_ARG),              # output tokens overlap heads (ot < H*d)
+    (dict(ot=0), LA_ERR_INVALID_ARG),               # every output token on one row
+    (dict(out=FAKE + 0x200000 + 256), LA_ERR_INVALID_ARG),   # out inside v's span
+    (dict(out=FAKE + 0x500000), LA_ERR_INVALID_ARG),         # out aliases the state
+    (dict(it=2 ** 24 + 8), LA_ERR_UNSUPPORTED), (dict(ot=2 ** 24 + 8), LA_ERR_UNSUPPORTED),
+    (dict(q=None), LA_ERR_INVALID_ARG), (dict(out=None), LA_ERR_INVALID_ARG),
+    (dict(it=2 ** 62, ib=0), LA_ERR_INVALID_ARG),    # span overflows
+])
+def test_strided_rejects_overlap_and_limits(lib, fn, bad, code):
+    assert getattr(lib, fn)(*_strided_args(fn, N=3, **bad)) == code

@@ -11,7 +11,7 @@ attention as an RNN-style recurrence over a per-(batch, head) D x D state):
     S_t = lambda_h S_{t-1} + k_t^T v_t,   o_t = q_t S_t,   S_{-1} = S_init
     lambda_h = exp(-s_h)
 
-Three independent statements of it live here:
+Several statements of it live here:
 
 * ``prefill`` / ``decode_step``: the recurrence, in plain C (``la_oracle.c``),
   fp64, OpenMP over the B*H slices.  This is the oracle the GPU is compared to.
@@ -28,6 +28,11 @@ Three independent statements of it live here:
   masked scores times V, plus the inter-block term from the carried state,
   plus the decayed state scan), NumPy fp64.  It exists to show that the
   decomposition reaches the definition at any block length.
+* ``cp_fold`` / ``cp_correct``: the two steps of the sequence-sharded
+  (context-parallel) prefill of the report's §4.1.1 and Fig. 10 that follow
+  each rank's local pass from a zero state: the incoming state of rank r from
+  the all-gathered local states, and the correction of the rank's local
+  output with it.  NumPy fp64.
 
 Inputs are NumPy arrays (or anything ``np.asarray`` takes) that are widened
 exactly to fp64; bf16/fp32 tensors are widened by the caller (exact).
@@ -244,6 +249,53 @@ def blockwise(q, k, v, slopes, state_init=None, C: int = 64):
                 S = (lam ** float(c)) * S + (K * (lam ** (c - 1.0 - ai))[:, None]).T @ V
             fin[b, h] = S
     return out, fin
+
+
+def cp_fold(local_states, shard_lens, slopes, rank, state_init=None):
+    """Incoming state of shard ``rank`` of a sequence split into consecutive
+    shards (the report's §4.1.1, Fig. 10: each rank's local state is the
+    decayed sum of k^T v over its own tokens from a zero state; the local
+    states are all-gathered and every rank folds in those of the shards before
+    it).
+
+    local_states: [R,B,H,d,d], shard j's state after its L_j tokens from zero;
+    shard_lens: R lengths L_j; rank in 0..R (R gives the state after the
+    whole sequence).  With start_r = L_0 + ... + L_{r-1}:
+
+        S_in(r) = lambda^start_r S_init + sum_{j<r} lambda^(start_r - start_{j+1}) S_loc(j)
+
+    (shard j's state is decayed by the tokens that follow it up to start_r).
+    Returns [B,H,d,d] fp64.
+    """
+    loc = _f64(local_states)
+    s = _f64(slopes)
+    lens = [int(x) for x in np.asarray(shard_lens).reshape(-1)]
+    R, B, H, d, _ = loc.shape
+    if len(lens) != R or not 0 <= rank <= R or any(n < 0 for n in lens):
+        raise ValueError("bad shard lengths or rank")
+    starts = np.concatenate([[0], np.cumsum(lens)]).astype(np.float64)
+    lam = np.exp(-s)[None, :, None, None]                       # [1,H,1,1]
+    out = np.zeros((B, H, d, d))
+    if state_init is not None:
+        out += lam ** starts[rank] * _f64(state_init)
+    for j in range(rank):
+        out += lam ** (starts[rank] - starts[j + 1]) * loc[j]
+    return out
+
+
+def cp_correct(q, slopes, state_in, out_local):
+    """Shard output from its local output (computed from a zero state) and its
+    incoming state: o_a = o_local_a + lambda^(a+1) q_a S_in for local token
+    index a (the report's §4.1.1, Fig. 10: the rank corrects its local O once
+    the preceding states are known).
+
+    q, out_local: [B,H,L,d]; state_in: [B,H,d,d].  Returns [B,H,L,d] fp64.
+    """
+    q, s, S = _f64(q), _f64(slopes), _f64(state_in)
+    B, H, L, d = q.shape
+    a = np.arange(L, dtype=np.float64)
+    lam = np.exp(-s)[:, None] ** (a[None, :] + 1.0)              # [H, L]
+    return _f64(out_local) + lam[None, :, :, None] * (q @ S)
 
 
 def rel_l2(x, ref, axes=(-2, -1)):

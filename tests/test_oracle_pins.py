@@ -369,3 +369,122 @@ def test_decode_multi_pin_detects_committing_every_token():
     assert oracle.rel_l2(full, fq) > 1e-3
     _, good = oracle.decode_multi(q, k, v, s, S0, [2])
     assert oracle.rel_l2(good, fq) <= 1e-12
+
+
+# ---- sequence-sharded (context-parallel) prefill: fold and correct ----------
+# Ling and Ring 2.6 Technical Report, §4.1.1 and Fig. 10: each rank runs its
+# shard from a zero state (local output, local state), the local states are
+# all-gathered, and each rank folds the states before it into its incoming
+# state and corrects its local output.  Pinned against the recurrence over the
+# unsplit sequence (the state after a prefix; the output rows of a shard).
+
+CP_LENS = [5, 0, 17, 1, 9]           # uneven, with an empty and a one-token shard
+
+
+def cp_setup(seed, lens=CP_LENS, d=4):
+    rng = np.random.default_rng(seed)
+    H = len(LAMS)
+    q, k, v, S0 = rand_inputs(rng, 2, H, sum(lens), d)
+    s = slopes_for(LAMS)
+    starts = np.concatenate([[0], np.cumsum(lens)]).astype(int)
+    loc_out, loc_st = [], []
+    for j in range(len(lens)):
+        a, b = starts[j], starts[j + 1]
+        o, st = oracle.prefill(q[:, :, a:b], k[:, :, a:b], v[:, :, a:b], s)   # zero state
+        loc_out.append(o)
+        loc_st.append(st)
+    return q, k, v, S0, s, starts, loc_out, np.stack(loc_st)
+
+
+def test_cp_fold_is_the_state_after_the_prefix():
+    q, k, v, S0, s, starts, _, loc = cp_setup(11)
+    for r in range(len(CP_LENS) + 1):
+        m = starts[r]
+        _, ref = oracle.prefill(q[:, :, :m], k[:, :, :m], v[:, :, :m], s, S0)
+        got = oracle.cp_fold(loc, CP_LENS, s, r, S0)
+        assert oracle.rel_l2(got, ref) <= 1e-12, r
+        # no initial state: the prefix from zero
+        _, ref0 = oracle.prefill(q[:, :, :m], k[:, :, :m], v[:, :, :m], s)
+        assert oracle.rel_l2(oracle.cp_fold(loc, CP_LENS, s, r), ref0) <= 1e-12, r
+
+
+def test_cp_correct_gives_the_unsplit_output():
+    q, k, v, S0, s, starts, loc_out, loc = cp_setup(12)
+    full, _ = oracle.prefill(q, k, v, s, S0)
+    for r in range(len(CP_LENS)):
+        a, b = starts[r], starts[r + 1]
+        S_in = oracle.cp_fold(loc, CP_LENS, s, r, S0)
+        got = oracle.cp_correct(q[:, :, a:b], s, S_in, loc_out[r])
+        assert oracle.rel_l2(got, full[:, :, a:b]) <= 1e-12, r
+
+
+def test_cp_single_shard_is_the_carried_state_run():
+    # one shard: the fold at rank 1 is the final state, the correction of the
+    # zero-state output is the output from S_init (a closed check by hand)
+    rng = np.random.default_rng(13)
+    q, k, v, S0 = rand_inputs(rng, 1, 2, 9, 3)
+    s = slopes_for([0.5, 0.9])
+    o0, st0 = oracle.prefill(q, k, v, s)
+    full, fin = oracle.prefill(q, k, v, s, S0)
+    lam = np.exp(-s)[None, :, None, None]
+    assert oracle.rel_l2(oracle.cp_fold(st0[None], [9], s, 1, S0), lam ** 9 * S0 + st0) <= 1e-14
+    assert oracle.rel_l2(oracle.cp_fold(st0[None], [9], s, 1, S0), fin) <= 1e-12
+    assert oracle.rel_l2(oracle.cp_correct(q, s, S0, o0), full) <= 1e-12
+
+
+def _fold_mutant(kind):
+    def fold(loc, lens, slopes, rank, S0):
+        lam = np.exp(-np.asarray(slopes, np.float64))[None, :, None, None]
+        starts = np.concatenate([[0], np.cumsum(lens)]).astype(np.float64)
+        out = np.zeros(loc.shape[1:])
+        if kind != "no_init_decay":
+            out += lam ** starts[rank] * S0
+        else:
+            out += S0
+        for j in range(rank):
+            if kind == "decay_own_shard":
+                e = starts[rank] - starts[j]
+            elif kind == "reversed_order":
+                e = starts[j + 1]
+            else:
+                e = starts[rank] - starts[j + 1]
+            out += lam ** e * loc[j]
+        return out
+    return fold
+
+
+@pytest.mark.parametrize("kind", ["no_init_decay", "decay_own_shard", "reversed_order"])
+def test_cp_fold_pin_detects_planted_mistakes(kind):
+    q, k, v, S0, s, starts, _, loc = cp_setup(14)
+    bad = _fold_mutant(kind)
+    worst = 0.0
+    for r in range(len(CP_LENS) + 1):
+        m = starts[r]
+        _, ref = oracle.prefill(q[:, :, :m], k[:, :, :m], v[:, :, :m], s, S0)
+        worst = max(worst, oracle.rel_l2(bad(loc, CP_LENS, s, r, S0), ref))
+    assert worst > 1e-3
+
+
+@pytest.mark.parametrize("kind", ["power_a", "transposed_state"])
+def test_cp_correct_pin_detects_planted_mistakes(kind):
+    q, k, v, S0, s, starts, loc_out, loc = cp_setup(15)
+    full, _ = oracle.prefill(q, k, v, s, S0)
+    worst = 0.0
+    for r in range(len(CP_LENS)):
+        a, b = starts[r], starts[r + 1]
+        S_in = oracle.cp_fold(loc, CP_LENS, s, r, S0)
+        L = b - a
+        idx = np.arange(L, dtype=np.float64)
+        lam = np.exp(-s)[:, None] ** (idx[None, :] + (0.0 if kind == "power_a" else 1.0))
+        S_use = np.swapaxes(S_in, -1, -2) if kind == "transposed_state" else S_in
+        bad = loc_out[r] + lam[None, :, :, None] * (q[:, :, a:b] @ S_use)
+        worst = max(worst, oracle.rel_l2(bad, full[:, :, a:b]))
+    assert worst > 1e-3
+
+
+def test_cp_fold_rejects_bad_arguments():
+    _, _, _, S0, s, _, _, loc = cp_setup(16)
+    with pytest.raises(ValueError):
+        oracle.cp_fold(loc, CP_LENS[:-1], s, 1, S0)
+    with pytest.raises(ValueError):
+        oracle.cp_fold(loc, CP_LENS, s, len(CP_LENS) + 1, S0)

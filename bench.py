@@ -31,7 +31,11 @@ events on the launch stream, mean over ``--extra-reps``):
     token-major layout), and with no layout copies (QK norm + RoPE in place
     in the projection buffer, la_prefill_strided reading q, k, v from it and
     writing [B,H,N,d], la_group_norm_gate on that output); the strided
-    prefill writing its output token-major is timed beside it.
+    prefill writing its output token-major is timed beside it;
+  * ``cp``: one rank's share of the 256K sequence split 8 ways (32,768 tokens,
+    H=64, d=128 bf16, the last rank): its prefill from a zero state
+    (la_prefill), the fold of the 8 gathered local states into its incoming
+    state (la_cp_fold) and the correction of its output (la_cp_correct).
 """
 from __future__ import annotations
 
@@ -230,6 +234,53 @@ def measure_decode_multi(dev, stream, reps):
             "four_single_steps_ms": round(ms_single, 4),
             "speedup_vs_single_steps": round(ms_single / ms, 3),
             "kernel": "decode_multi_kernel<bf16,128>"}
+
+
+def measure_cp(dev, stream, reps):
+    import torch
+    from long_context_layers_amd import binding, inputs
+    R = 8
+    B, H, d = PREFILL["B"], PREFILL["H"], PREFILL["d"]
+    L = PREFILL["N"] // R
+    with torch.cuda.stream(stream):
+        x = inputs.make_prefill(B, H, L, d, torch.bfloat16, seed=1008, init_state=False, device=dev)
+        g = torch.Generator(device=dev).manual_seed(1009)
+        loc = 0.1 * torch.randn((R, B, H, d, d), generator=g, device=dev)   # gathered local states
+        init = 0.1 * torch.randn((B, H, d, d), generator=g, device=dev)
+        st = torch.zeros((B, H, d, d), device=dev)
+        s_in = torch.empty((B, H, d, d), device=dev)
+        out = torch.empty_like(x.q)
+    stream.synchronize()
+
+    def local():
+        binding.prefill(x.q, x.k, x.v, x.slopes, st, out=out)
+
+    def fold():
+        binding.cp_fold(loc, [L] * R, R - 1, x.slopes, init, out=s_in)
+
+    def correct():
+        binding.cp_correct(x.q, x.slopes, s_in, out)
+
+    with torch.cuda.stream(stream):
+        ms_loc = time_launches(stream, local, reps)
+        ms_fold = time_launches(stream, fold, reps)
+        ms_corr = time_launches(stream, correct, reps)
+    state_bytes = B * H * d * d * 4
+    by_fold = (R - 1 + 2) * state_bytes                 # 7 local states + S_init read, S_in written
+    by_corr = B * H * L * d * 2 * 3 + state_bytes        # q, out read, out written; S_in read
+    del x, loc, init, st, s_in, out
+    gf, gc = by_fold / (ms_fold * 1e-3) / 1e9, by_corr / (ms_corr * 1e-3) / 1e9
+    return {"workload": f"rank {R - 1} of {R}: shard B{B} H{H} L{L} d{d} bf16 of the 256K "
+                        "sequence; the all-gather of the local states is not run (one GPU)",
+            "local_prefill_ms": round(ms_loc, 4),
+            "local_prefill_tflops": round(prefill_flops(B, H, L, d) / (ms_loc * 1e-3) / 1e12, 3),
+            "cp_fold": {"ms": round(ms_fold, 4), "gbs": round(gf, 1),
+                        "frac_of_hbm_peak": round(gf / HBM_PEAK_GBS, 4),
+                        "algorithmic_bytes": by_fold, "kernel": "cp_fold_kernel"},
+            "cp_correct": {"ms": round(ms_corr, 4), "gbs": round(gc, 1),
+                           "frac_of_hbm_peak": round(gc / HBM_PEAK_GBS, 4),
+                           "algorithmic_bytes": by_corr, "kernel": "cp_correct_kernel<128>"},
+            "overhead_vs_local_prefill": round((ms_fold + ms_corr) / ms_loc, 4)}
 
 
 def kernel_hash():
@@ -451,6 +502,9 @@ def main():
         torch.cuda.empty_cache()
         print("[bench] layer ops (QK norm + RoPE, grouped norm x gate)", file=sys.stderr, flush=True)
         res["layer_ops"] = measure_layer_ops(dev, stream, args.extra_reps, pre_ms)
+        torch.cuda.empty_cache()
+        print("[bench] sequence-sharded prefill steps", file=sys.stderr, flush=True)
+        res["cp"] = measure_cp(dev, stream, args.extra_reps)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(dict(q=p.q, k=p.k, v=p.v, slopes=p.slopes, N=N, d=d, H=H))

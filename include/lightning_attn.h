@@ -258,6 +258,49 @@ int la_group_norm_gate(const void *o, int64_t o_bstride, int64_t o_hstride, int6
                        int64_t group, float eps, void *y, int64_t B, int64_t N, int64_t H,
                        int64_t d, void *stream);
 
+/*
+ * Sequence-sharded (context-parallel) prefill: the two steps a rank adds after
+ * running la_prefill over its own shard of a long sequence from a zero state.
+ * Source: the report's §4.1.1 and Fig. 10 - every rank computes a local state
+ * and a local output, the [B,H,D,D] local states are all-gathered, each rank
+ * folds the states of the shards before it into its incoming state and
+ * corrects its local output with it.  The gather itself is the caller's (one
+ * all-gather of the local states); these calls do the arithmetic around it.
+ *
+ * la_cp_fold: the state entering shard `rank`.
+ *   local_states  [nshards,B,H,d,d] fp32, read only: shard j's state after its
+ *                 own tokens from a zero state (la_prefill's final state), in
+ *                 shard order; only the first `rank` are read (may be NULL
+ *                 for rank 0).
+ *   shard_lens    HOST pointer to nshards int64 token counts (>= 0; only the
+ *                 first `rank` are read; may be NULL for rank 0).
+ *   nshards       1..64 (more gives LA_ERR_UNSUPPORTED); rank in 0..nshards
+ *                 (nshards gives the state after the whole sequence).
+ *   state_init    [B,H,d,d] fp32, the state before the sequence, or NULL (zero).
+ *   state_in      [B,H,d,d] fp32, written:
+ *     S_in(0) = S_init,  S_in(j+1) = lambda^shard_lens[j] S_in(j) + local_states[j],
+ *   in that order, fp32.  state_in may be state_init itself (in place); it
+ *   must not overlap local_states or partly overlap state_init.
+ *
+ * la_cp_correct: a shard's output from its local output and incoming state.
+ *   q          [B,H,L,d] bf16, read only: the shard's queries.
+ *   state_in   [B,H,d,d] fp32 (la_cp_fold's result for this shard).
+ *   out        [B,H,L,d] bf16, IN/OUT: the local output (la_prefill from a zero
+ *              state) on entry; on exit out_a + lambda^(a+1) q_a . S_in for local
+ *              token a, with S_in rounded to bf16 for the product (as the
+ *              prefill's inter-block term uses it), fp32 accumulation, one bf16
+ *              rounding.  Must not overlap q or state_in.
+ *   L == 0 is a no-op; L > 2^31 - 256 gives LA_ERR_UNSUPPORTED.
+ * Together: shard r's corrected output and la_cp_fold(rank = nshards) equal one
+ * la_prefill over the whole sequence up to rounding.
+ */
+int la_cp_fold(const float *local_states, const int64_t *shard_lens, int64_t nshards,
+               int64_t rank, const float *slopes, const float *state_init, float *state_in,
+               int64_t B, int64_t H, int64_t d, void *stream);
+
+int la_cp_correct(const void *q, const float *slopes, const float *state_in, void *out,
+                  int64_t B, int64_t H, int64_t L, int64_t d, void *stream);
+
 /* Static, NUL-terminated description of a status code ("unknown status" for
  * values outside la_status).  Never NULL; the caller must not free it. */
 const char *la_status_string(int status);

@@ -39,6 +39,8 @@ SIGNATURES = {
                          _P, _P, _P, _I64, _I64, _I64, _I64, _P], _INT),
     "la_group_norm_gate": ([_P, _I64, _I64, _I64, _P, _I64, _P, _I64, ctypes.c_float, _P,
                             _I64, _I64, _I64, _I64, _P], _INT),
+    "la_cp_fold": ([_P, _P, _I64, _I64, _P, _P, _P, _I64, _I64, _I64, _P], _INT),
+    "la_cp_correct": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], _INT),
     "la_status_string": ([_INT], ctypes.c_char_p),
     "la_abi_version": ([], _INT),
 }
@@ -399,4 +401,65 @@ def group_norm_gate(o: torch.Tensor, gate: torch.Tensor, norm_weight: torch.Tens
                                     norm_weight.data_ptr(), d if group is None else group,
                                     float(eps), out.data_ptr(), B, N, H, d, _stream(dev))
     _check(rc, "la_group_norm_gate")
+    return out
+
+
+def cp_fold(local_states: torch.Tensor, shard_lens, rank: int, slopes: torch.Tensor,
+            state_init: Optional[torch.Tensor] = None,
+            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """State entering shard ``rank`` of a sequence-sharded prefill.
+
+    local_states: [R,B,H,d,d] fp32 (each shard's la_prefill final state from a
+    zero state, e.g. the result of an all-gather); shard_lens: R token counts
+    (host ints); rank in 0..R; state_init: [B,H,d,d] fp32 or None (zero).
+    Returns [B,H,d,d] fp32 (``out`` may be ``state_init`` itself).
+    """
+    if not isinstance(local_states, torch.Tensor) or local_states.dim() != 5:
+        raise ValueError("local_states must be a [R,B,H,d,d] tensor")
+    dev = local_states.device
+    if dev.type != "cuda":
+        raise ValueError("cp_fold runs on GPU tensors only (no CPU path)")
+    R, B, H, d, _ = local_states.shape
+    _need(local_states, "local_states", torch.float32, dev, (R, B, H, d, d))
+    lens = [int(x) for x in shard_lens]
+    if len(lens) != R:
+        raise ValueError("shard_lens must have one entry per shard")
+    _need(slopes, "slopes", torch.float32, dev, (H,))
+    if state_init is not None:
+        _need(state_init, "state_init", torch.float32, dev, (B, H, d, d))
+    if out is None:
+        out = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    else:
+        _need(out, "out", torch.float32, dev, (B, H, d, d))
+    arr = (ctypes.c_int64 * max(R, 1))(*lens)
+    with torch.cuda.device(dev):
+        rc = load_library().la_cp_fold(local_states.data_ptr(), ctypes.cast(arr, ctypes.c_void_p),
+                                       R, int(rank), slopes.data_ptr(),
+                                       None if state_init is None else state_init.data_ptr(),
+                                       out.data_ptr(), B, H, d, _stream(dev))
+    _check(rc, "la_cp_fold")
+    return out
+
+
+def cp_correct(q: torch.Tensor, slopes: torch.Tensor, state_in: torch.Tensor,
+               out: torch.Tensor) -> torch.Tensor:
+    """Correct a shard's local output in place: out_a += lambda^(a+1) q_a S_in.
+
+    q, out: [B,H,L,d] bf16 (out = la_prefill's output over the shard from a
+    zero state); state_in: [B,H,d,d] fp32 (``cp_fold`` for this shard).
+    """
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a [B,H,L,d] tensor")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("cp_correct runs on GPU tensors only (no CPU path)")
+    B, H, L, d = q.shape
+    _need(q, "q", torch.bfloat16, dev, (B, H, L, d))
+    _need(out, "out", torch.bfloat16, dev, (B, H, L, d))
+    _need(slopes, "slopes", torch.float32, dev, (H,))
+    _need(state_in, "state_in", torch.float32, dev, (B, H, d, d))
+    with torch.cuda.device(dev):
+        rc = load_library().la_cp_correct(q.data_ptr(), slopes.data_ptr(), state_in.data_ptr(),
+                                          out.data_ptr(), B, H, L, d, _stream(dev))
+    _check(rc, "la_cp_correct")
     return out

@@ -479,6 +479,60 @@ int la_group_norm_gate(const void *o, int64_t o_bstride, int64_t o_hstride, int6
         static_cast<hipStream_t>(stream)));
 }
 
+int la_cp_fold(const float *local_states, const int64_t *shard_lens, int64_t nshards,
+               int64_t rank, const float *slopes, const float *state_init, float *state_in,
+               int64_t B, int64_t H, int64_t d, void *stream)
+{
+    if (!slopes || !state_in) return LA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1) return LA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
+    if (nshards < 1 || rank < 0 || rank > nshards) return LA_ERR_INVALID_ARG;
+    if (nshards > la::MAX_CP_SHARDS) return LA_ERR_UNSUPPORTED;
+    if (rank > 0 && (!local_states || !shard_lens)) return LA_ERR_INVALID_ARG;
+    int lens[la::MAX_CP_SHARDS];
+    for (int64_t j = 0; j < rank; ++j) {
+        if (shard_lens[j] < 0) return LA_ERR_INVALID_ARG;
+        if (shard_lens[j] > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+        lens[j] = (int)shard_lens[j];
+    }
+    int64_t bh, st, st_bytes, loc_bytes;
+    if (!mul_ok(B, H, &bh) || !mul_ok(bh, d * d, &st) || !mul_ok(st, 4, &st_bytes) ||
+        !mul_ok(st_bytes, rank, &loc_bytes))
+        return LA_ERR_INVALID_ARG;
+    if (!aligned(state_in, 16) || !aligned(state_init, 16) || !aligned(local_states, 16) ||
+        !aligned(slopes, 4))
+        return LA_ERR_INVALID_ARG;
+    // state_in may be state_init itself (fold in place), but no other overlap
+    if (state_init != state_in && overlap(state_in, st_bytes, state_init, st_bytes))
+        return LA_ERR_INVALID_ARG;
+    if (rank > 0 && overlap(state_in, st_bytes, local_states, loc_bytes))
+        return LA_ERR_INVALID_ARG;
+    return hip_status(la::launch_cp_fold(local_states, lens, (int)rank, state_init, state_in,
+                                         slopes, B, H, (int)d, static_cast<hipStream_t>(stream)));
+}
+
+int la_cp_correct(const void *q, const float *slopes, const float *state_in, void *out,
+                  int64_t B, int64_t H, int64_t L, int64_t d, void *stream)
+{
+    if (!slopes || !state_in) return LA_ERR_INVALID_ARG;
+    if (B < 1 || H < 1 || L < 0) return LA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
+    if (L > 0 && (!q || !out)) return LA_ERR_INVALID_ARG;
+    int64_t bh, act, act_bytes, st, st_bytes;
+    if (!mul_ok(B, H, &bh) || !mul_ok(bh, L, &act) || !mul_ok(act, d * 2, &act_bytes) ||
+        !mul_ok(bh, d * d, &st) || !mul_ok(st, 4, &st_bytes))
+        return LA_ERR_INVALID_ARG;
+    if (!aligned(q, 16) || !aligned(out, 16) || !aligned(state_in, 16) || !aligned(slopes, 4))
+        return LA_ERR_INVALID_ARG;
+    if (overlap(out, act_bytes, q, act_bytes) || overlap(out, act_bytes, state_in, st_bytes))
+        return LA_ERR_INVALID_ARG;
+    if (L > 0x7fffff00 || la::cp_correct_grid(B, H, L) > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+    if (L == 0) return LA_OK;
+    return hip_status(la::launch_cp_correct(
+        static_cast<const uint16_t *>(q), slopes, state_in, static_cast<uint16_t *>(out), B, H,
+        L, (int)d, static_cast<hipStream_t>(stream)));
+}
+
 const char *la_status_string(int status)
 {
     switch (status) {
@@ -489,7 +543,8 @@ const char *la_status_string(int status)
         case LA_ERR_UNSUPPORTED:
             return "LA_ERR_UNSUPPORTED: head dimension not in {64, 128}, more tokens per "
                    "decode call than supported, a rotary dimension or norm group size the "
-                   "kernels do not take, or grid too large";
+                   "kernels do not take, a stride, shard count or length above the "
+                   "supported limit, or grid too large";
         case LA_ERR_HIP: return "LA_ERR_HIP: the kernel launch failed";
         default: return "unknown status";
     }

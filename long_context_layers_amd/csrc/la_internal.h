@@ -80,6 +80,18 @@ hipError_t launch_group_norm_gate(const uint16_t *o, const int64_t os[3], const 
                                   uint16_t *y, int64_t B, int64_t N, int64_t H, int d,
                                   hipStream_t stream);
 
+// sequence-sharded prefill: fold of the gathered local states (Horner order
+// over the first nfold shards, lens = their token counts) and correction of a
+// shard's local output with its incoming state
+constexpr int MAX_CP_SHARDS = 64;
+hipError_t launch_cp_fold(const float *loc, const int *lens, int nfold, const float *init,
+                          float *out, const float *slopes, int64_t B, int64_t H, int d,
+                          hipStream_t stream);
+hipError_t launch_cp_correct(const uint16_t *q, const float *slopes, const float *s_in,
+                             uint16_t *out, int64_t B, int64_t H, int64_t L, int d,
+                             hipStream_t stream);
+int64_t cp_correct_grid(int64_t B, int64_t H, int64_t L);
+
 // number of workgroups one prefill launch over `seqs` sequences uses
 int64_t prefill_bf16_grid(int64_t seqs, int64_t H, int d);
 int64_t prefill_f32_grid(int64_t seqs, int64_t H, int d);

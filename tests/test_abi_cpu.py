@@ -366,3 +366,71 @@ def test_strided_rejects_bad_arguments(lib, fn, bad, code):
 ])
 def test_strided_rejects_overlap_and_limits(lib, fn, bad, code):
     assert getattr(lib, fn)(*_strided_args(fn, N=3, **bad)) == code
+
+
+def _fold_args(lens=(3, 4, 5), **kw):
+    arr = (ctypes.c_int64 * len(lens))(*lens)
+    a = dict(loc=FAKE, lensp=ctypes.cast(arr, ctypes.c_void_p).value, nshards=len(lens), rank=2,
+             slopes=FAKE + 0x900000, init=FAKE + 0xa00000, out=FAKE + 0xb00000, B=1, H=2, d=64,
+             stream=None)
+    a.update(kw)
+    return arr, [a[n] for n in ("loc", "lensp", "nshards", "rank", "slopes", "init", "out", "B",
+                                "H", "d", "stream")]
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("bad,code", [
+    (dict(nshards=0, rank=0), LA_ERR_INVALID_ARG), (dict(rank=-1), LA_ERR_INVALID_ARG),
+    (dict(rank=4), LA_ERR_INVALID_ARG),                        # rank > nshards
+    (dict(nshards=65, rank=1), LA_ERR_UNSUPPORTED),
+    (dict(lensp=None), LA_ERR_INVALID_ARG), (dict(loc=None), LA_ERR_INVALID_ARG),
+    (dict(slopes=None), LA_ERR_INVALID_ARG), (dict(out=None), LA_ERR_INVALID_ARG),
+    (dict(d=96), LA_ERR_UNSUPPORTED), (dict(B=0), LA_ERR_INVALID_ARG),
+    (dict(out=FAKE + 0xb00008), LA_ERR_INVALID_ARG),           # misaligned
+    (dict(out=FAKE + 0x4000), LA_ERR_INVALID_ARG),             # inside the local states
+    (dict(out=FAKE + 0xa00010), LA_ERR_INVALID_ARG),           # partly over state_init
+])
+def test_cp_fold_rejects_bad_arguments(lib, bad, code):
+    arr, args = _fold_args(**bad)
+    assert lib.la_cp_fold(*args) == code
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("lens,code", [((3, -1, 5), LA_ERR_INVALID_ARG),
+                                       ((3, 2 ** 31, 5), LA_ERR_UNSUPPORTED)])
+def test_cp_fold_rejects_bad_lengths(lib, lens, code):
+    arr, args = _fold_args(lens=lens)
+    assert lib.la_cp_fold(*args) == code
+
+
+def _correct_args(**kw):
+    a = dict(q=FAKE, slopes=FAKE + 0x100000, state=FAKE + 0x200000, out=FAKE + 0x300000, B=1,
+             H=2, L=0, d=64, stream=None)
+    a.update(kw)
+    return [a[n] for n in ("q", "slopes", "state", "out", "B", "H", "L", "d", "stream")]
+
+
+def test_cp_correct_empty_shard_is_a_noop(lib):
+    assert lib.la_cp_correct(*_correct_args(L=0)) == LA_OK
+    assert lib.la_cp_correct(*_correct_args(L=0, q=None, out=None)) == LA_OK
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(slopes=None), LA_ERR_INVALID_ARG), (dict(state=None), LA_ERR_INVALID_ARG),
+    (dict(B=0), LA_ERR_INVALID_ARG), (dict(L=-1), LA_ERR_INVALID_ARG),
+    (dict(d=32), LA_ERR_UNSUPPORTED), (dict(q=FAKE + 8), LA_ERR_INVALID_ARG),
+    (dict(state=FAKE + 0x200004), LA_ERR_INVALID_ARG),
+])
+def test_cp_correct_rejects_bad_arguments(lib, bad, code):
+    assert lib.la_cp_correct(*_correct_args(**bad)) == code
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("bad,code", [
+    (dict(out=FAKE), LA_ERR_INVALID_ARG),                      # out aliases q
+    (dict(out=FAKE + 0x200000), LA_ERR_INVALID_ARG),           # out aliases the state
+    (dict(q=None), LA_ERR_INVALID_ARG), (dict(out=None), LA_ERR_INVALID_ARG),
+    (dict(L=2 ** 31 - 1, out=FAKE + 2 ** 45), LA_ERR_UNSUPPORTED),
+])
+def test_cp_correct_rejects_overlap_and_limits(lib, bad, code):
+    assert lib.la_cp_correct(*_correct_args(L=bad.pop("L", 5), **bad)) == code

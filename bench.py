@@ -14,7 +14,9 @@ whatever block length the kernel uses), from HIP events around each prefill
 launch on its stream.  The decode step is reported in GB/s of state traffic.
 ``roofline`` is the prefill kernel's HBM roofline (algorithmic bytes per
 launch / launch time against 8 TB/s); ``cpu_baseline`` times the fp64 CPU
-oracle on a bounded sample of the same workload.
+oracle on a bounded sample of the same workload; ``ceilings`` holds what the
+same GPU sustains in probe kernels (lib/liblapeak.so: an MFMA loop and read,
+write and copy streams) and the prefill and decode against them.
 
 Outside the timed step, two more launches are measured the same way (HIP
 events on the launch stream, mean over ``--extra-reps``):
@@ -236,6 +238,69 @@ def measure_decode_multi(dev, stream, reps):
             "kernel": "decode_multi_kernel<bf16,128>"}
 
 
+def measure_ceilings(dev, stream, pre_ms, pre_tflops, dec_gbs):
+    """Probe kernels on this GPU: bf16 MFMA loop, HBM read / write / copy /
+    in-place update streams; the prefill's time floor at the measured read and
+    write rates (its reads and writes taken one after the other, as the copy
+    stream shows they are), and decode against the in-place update stream."""
+    import ctypes
+    import torch
+    from long_context_layers_amd import build
+    lib = ctypes.CDLL(build.PEAK_LIB)
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    lib.la_peak_mfma_bf16.argtypes = [I64, I64, P, P]
+    lib.la_peak_read.argtypes = [P, I64, P, P]
+    lib.la_peak_write.argtypes = [P, I64, P]
+    lib.la_peak_copy.argtypes = [P, P, I64, P]
+    lib.la_peak_update.argtypes = [P, I64, P]
+    for f in (lib.la_peak_mfma_bf16, lib.la_peak_read, lib.la_peak_write, lib.la_peak_copy,
+              lib.la_peak_update):
+        f.restype = ctypes.c_int
+    h = stream.cuda_stream
+    nbytes = 4 << 30
+    with torch.cuda.stream(stream):
+        a = torch.zeros(nbytes // 4, dtype=torch.float32, device=dev)
+        b = torch.zeros(nbytes // 8, dtype=torch.float32, device=dev)
+        sink = torch.zeros(1 << 16, dtype=torch.float32, device=dev)
+    stream.synchronize()
+    blocks, iters = 256 * 4, 20000
+    chains = 4
+
+    def best(fn, n=3):
+        def call():
+            rc = fn()
+            if rc != 0:
+                raise RuntimeError(f"probe launch failed ({rc})")
+        return min(time_launches(stream, call, 1) for _ in range(n))
+
+    with torch.cuda.stream(stream):
+        ms_mfma = best(lambda: lib.la_peak_mfma_bf16(iters, blocks, sink.data_ptr(), h))
+        ms_read = best(lambda: lib.la_peak_read(a.data_ptr(), nbytes, sink.data_ptr(), h))
+        ms_write = best(lambda: lib.la_peak_write(a.data_ptr(), nbytes, h))
+        ms_copy = best(lambda: lib.la_peak_copy(a.data_ptr(), b.data_ptr(), nbytes // 2, h))
+        ms_upd = best(lambda: lib.la_peak_update(a.data_ptr(), nbytes // 2, h))
+    del a, b, sink
+    tf = blocks * 4 * iters * chains * 32768 / (ms_mfma * 1e-3) / 1e12
+    rd, wr, cp, up = (x / (ms * 1e-3) / 1e9 for x, ms in
+                      ((nbytes, ms_read), (nbytes, ms_write), (nbytes, ms_copy), (nbytes, ms_upd)))
+    B, H, N, d = PREFILL["B"], PREFILL["H"], PREFILL["N"], PREFILL["d"]
+    st = B * H * d * d * 4
+    rbytes, wbytes = B * H * N * d * 2 * 3 + st, B * H * N * d * 2 + st
+    floor_ms = (rbytes / (rd * 1e9) + wbytes / (wr * 1e9)) * 1e3
+    return {"mfma_bf16_tflops": round(tf, 1), "hbm_read_gbs": round(rd, 1),
+            "hbm_write_gbs": round(wr, 1), "hbm_copy_gbs": round(cp, 1),
+            "hbm_update_gbs": round(up, 1),
+            "probes": "lib/liblapeak.so: v_mfma_f32_32x32x16_bf16 chains on registers "
+                      f"({blocks} workgroups of 4 waves, {chains} chains each); streams over "
+                      "4 GiB in 64 KB chunks, one per workgroup, each chunk's 16-byte "
+                      "nontemporal accesses all in flight (copy and in-place update: 2 GiB "
+                      "read + 2 GiB written, counted as 4 GiB); best of 3",
+            "prefill_frac_of_mfma_loop": round(pre_tflops / tf, 4),
+            "prefill_floor_ms_at_stream_rates": round(floor_ms, 4),
+            "prefill_frac_of_stream_floor": round(floor_ms / pre_ms, 4),
+            "decode_frac_of_update_stream": round(dec_gbs / up, 4)}
+
+
 def measure_cp(dev, stream, reps):
     import torch
     from long_context_layers_amd import binding, inputs
@@ -370,6 +435,8 @@ def main():
                     help="skip the CPU oracle timing (for profiler runs)")
     ap.add_argument("--copy-only", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the probe kernels that measure this GPU's MFMA and HBM ceilings")
     ap.add_argument("--extra-reps", type=int, default=5,
                     help="launches timed for the packed-prefill and draft-verification lines "
                          "(0 skips them)")
@@ -493,6 +560,10 @@ def main():
             "kernel": "decode_kernel<bf16,128>",
         },
     }
+    if not args.no_ceilings:
+        print("[bench] ceilings (MFMA loop, HBM streams)", file=sys.stderr, flush=True)
+        res["ceilings"] = measure_ceilings(dev, stream, pre_ms, tflops, dgbs)
+        torch.cuda.empty_cache()
     if args.extra_reps > 0:
         print("[bench] packed variable-length prefill", file=sys.stderr, flush=True)
         res["varlen"] = measure_varlen(dev, stream, args.extra_reps, tflops)

@@ -3,7 +3,8 @@
     python -m long_context_layers_amd.build
 
 Each HIP source is compiled to an object (in parallel), then linked into
-``long_context_layers_amd/lib/liblightning_attn.so``.  Always recompiles.
+``long_context_layers_amd/lib/liblightning_attn.so``; the benchmark's
+ceiling probes go into ``lib/liblapeak.so``.  Always recompiles.
 """
 from __future__ import annotations
 
@@ -23,6 +24,8 @@ LIB = os.path.join(LIB_DIR, "liblightning_attn.so")
 
 SOURCES = ["la_api.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip", "layer_ops.hip",
            "cp.hip"]
+PEAK_SOURCES = ["peak_probe.hip"]
+PEAK_LIB = os.path.join(LIB_DIR, "liblapeak.so")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
@@ -49,19 +52,25 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    os.makedirs(LIB_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"[build] {LIB}")
+        print(f"[build] {lib}")
+
+
+def build(verbose: bool = True) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(LIB_DIR, exist_ok=True)
+    srcs = SOURCES + PEAK_SOURCES
+    with ThreadPoolExecutor(max_workers=min(len(srcs), os.cpu_count() or 4)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB, verbose)
+    _link(objs[len(SOURCES):], PEAK_LIB, verbose)
     return LIB
 
 

@@ -1,0 +1,173 @@
+// peak_probe.hip — measured ceilings of the GPU the kernels run on (a
+// separate library, liblapeak.so, used by the benchmark; not part of the
+// lightning_attn C ABI).  The published MI355X figures (8 TB/s HBM3E, 2.5
+// PFLOP/s dense bf16 MFMA) are what the roofline fractions are quoted
+// against; these probes measure what the same chip sustains:
+//
+//   la_peak_mfma_bf16   every wave runs independent chains of
+//                       v_mfma_f32_32x32x16_bf16 on register operands
+//                       (32,768 flop each), 8 waves per CU;
+//   la_peak_read        a buffer read in 64 KB chunks, one per workgroup, the
+//                       whole chunk in flight, folded into a value that is
+//                       written only if it takes one particular bit pattern;
+//   la_peak_write       the same chunks written;
+//   la_peak_copy        chunks read, then written to a second buffer;
+//   la_peak_update      chunks read, then written back in place (the access
+//                       pattern of a state updated where it lives).
+//
+// extern "C", plain pointers and sizes, enqueued on the caller's stream (no
+// synchronisation, no allocation).  Return: 0, or the hipError_t of the launch;
+// -1 for bad arguments (null pointers; stream sizes that are not a positive
+// multiple of 64 KB).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int PT = 256;            // threads per workgroup (4 waves)
+constexpr int NACC = 4;            // independent accumulator chains per wave
+
+__global__ __launch_bounds__(PT) void mfma_loop_kernel(int64_t iters, float *sink)
+{
+    const int lane = threadIdx.x % 64;
+    bf16x8 a, b;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        a[e] = (__bf16)(1.0f + 0.001f * (lane + e));
+        b[e] = (__bf16)(1.0f - 0.001f * (lane + e));
+    }
+    f32x16 acc[NACC];
+#pragma unroll
+    for (int c = 0; c < NACC; ++c) acc[c] = f32x16{};
+    for (int64_t i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int c = 0; c < NACC; ++c)
+            acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < NACC; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s += acc[c][r];
+    if (s == 12345.678f) sink[blockIdx.x] = s;   // keeps the chains live; never true in practice
+}
+
+// Streams: workgroup g owns the 64 KB chunk g; each thread issues all UNR of
+// its 16-byte accesses (elements t + 256 u of the chunk) before using any, so
+// a workgroup has the whole chunk in flight (every instruction covers 4 KB of
+// consecutive bytes).
+constexpr int UNR = 16;
+constexpr int64_t CHUNK16 = (int64_t)PT * UNR;      // 16-byte elements per chunk (64 KB)
+
+__global__ __launch_bounds__(PT) void read_kernel(const u32x4 *__restrict__ src,
+                                                  float *__restrict__ sink)
+{
+    const u32x4 *p = src + blockIdx.x * CHUNK16 + threadIdx.x;
+    u32x4 x[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) x[u] = __builtin_nontemporal_load(&p[u * PT]);
+    u32x4 acc = x[0];
+#pragma unroll
+    for (int u = 1; u < UNR; ++u) acc ^= x[u];
+    const unsigned v = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+    if (v == 0x9e3779b9u) sink[blockIdx.x % 4096] = (float)v;   // keeps the loads live
+}
+
+__global__ __launch_bounds__(PT) void write_kernel(u32x4 *__restrict__ dst)
+{
+    u32x4 *p = dst + blockIdx.x * CHUNK16 + threadIdx.x;
+    const u32x4 v = {1u, 2u, 3u, 4u};
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) __builtin_nontemporal_store(v, &p[u * PT]);
+}
+
+__global__ __launch_bounds__(PT) void copy_kernel(const u32x4 *__restrict__ src,
+                                                  u32x4 *__restrict__ dst)
+{
+    const u32x4 *p = src + blockIdx.x * CHUNK16 + threadIdx.x;
+    u32x4 *q = dst + blockIdx.x * CHUNK16 + threadIdx.x;
+    u32x4 x[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) x[u] = __builtin_nontemporal_load(&p[u * PT]);
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) __builtin_nontemporal_store(x[u], &q[u * PT]);
+}
+
+// in-place update: each element read, changed and written back where it lives
+// (the access pattern of a state updated in place)
+__global__ __launch_bounds__(PT) void update_kernel(u32x4 *__restrict__ buf)
+{
+    u32x4 *p = buf + blockIdx.x * CHUNK16 + threadIdx.x;
+    u32x4 x[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) x[u] = __builtin_nontemporal_load(&p[u * PT]);
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) __builtin_nontemporal_store(x[u] + 1u, &p[u * PT]);
+}
+
+// bytes must be a positive multiple of one chunk (64 KB), grid = chunks
+bool chunks_of(int64_t bytes, unsigned *grid) {
+    if (bytes <= 0 || bytes % (CHUNK16 * 16) != 0 || bytes / (CHUNK16 * 16) > 0x7fffffff)
+        return false;
+    *grid = (unsigned)(bytes / (CHUNK16 * 16));
+    return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+// flop = blocks * 4 waves * iters * NACC * 32768
+int la_peak_mfma_bf16(int64_t iters, int64_t blocks, float *sink, void *stream)
+{
+    if (iters < 1 || blocks < 1 || blocks > 0x7fffffff || !sink) return -1;
+    hipLaunchKernelGGL(mfma_loop_kernel, dim3((unsigned)blocks), dim3(PT), 0,
+                       static_cast<hipStream_t>(stream), iters, sink);
+    return (int)hipGetLastError();
+}
+
+int la_peak_mfma_chains(void) { return NACC; }
+
+// sink: at least 4096 floats
+int la_peak_read(const void *src, int64_t bytes, float *sink, void *stream)
+{
+    unsigned g;
+    if (!src || !sink || !chunks_of(bytes, &g)) return -1;
+    hipLaunchKernelGGL(read_kernel, dim3(g), dim3(PT), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const u32x4 *>(src), sink);
+    return (int)hipGetLastError();
+}
+
+int la_peak_write(void *dst, int64_t bytes, void *stream)
+{
+    unsigned g;
+    if (!dst || !chunks_of(bytes, &g)) return -1;
+    hipLaunchKernelGGL(write_kernel, dim3(g), dim3(PT), 0, static_cast<hipStream_t>(stream),
+                       static_cast<u32x4 *>(dst));
+    return (int)hipGetLastError();
+}
+
+// bytes read (and as many written)
+int la_peak_copy(const void *src, void *dst, int64_t bytes, void *stream)
+{
+    unsigned g;
+    if (!src || !dst || !chunks_of(bytes, &g)) return -1;
+    hipLaunchKernelGGL(copy_kernel, dim3(g), dim3(PT), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const u32x4 *>(src), static_cast<u32x4 *>(dst));
+    return (int)hipGetLastError();
+}
+
+int la_peak_update(void *buf, int64_t bytes, void *stream)
+{
+    unsigned g;
+    if (!buf || !chunks_of(bytes, &g)) return -1;
+    hipLaunchKernelGGL(update_kernel, dim3(g), dim3(PT), 0, static_cast<hipStream_t>(stream),
+                       static_cast<u32x4 *>(buf));
+    return (int)hipGetLastError();
+}
+
+}  // extern "C"

@@ -434,3 +434,28 @@ def test_cp_correct_rejects_bad_arguments(lib, bad, code):
 ])
 def test_cp_correct_rejects_overlap_and_limits(lib, bad, code):
     assert lib.la_cp_correct(*_correct_args(L=bad.pop("L", 5), **bad)) == code
+
+
+def test_peak_probe_library_loads_and_rejects_bad_arguments():
+    # the benchmark's ceiling probes (lib/liblapeak.so): every call checks its
+    # arguments on the host before any launch
+    from long_context_layers_amd import build
+    peak = ctypes.CDLL(build.PEAK_LIB)
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    for name in ("la_peak_mfma_bf16", "la_peak_read", "la_peak_write", "la_peak_copy",
+                 "la_peak_update", "la_peak_mfma_chains"):
+        assert hasattr(peak, name), name
+    peak.la_peak_mfma_bf16.argtypes = [I64, I64, P, P]
+    peak.la_peak_read.argtypes = [P, I64, P, P]
+    peak.la_peak_write.argtypes = [P, I64, P]
+    peak.la_peak_copy.argtypes = [P, P, I64, P]
+    assert peak.la_peak_mfma_chains() == 4
+    assert peak.la_peak_mfma_bf16(0, 1, FAKE, None) == -1
+    assert peak.la_peak_mfma_bf16(1, 0, FAKE, None) == -1
+    assert peak.la_peak_mfma_bf16(1, 1, None, None) == -1
+    assert peak.la_peak_read(FAKE, 24, FAKE, None) == -1          # not a multiple of 16
+    assert peak.la_peak_read(None, 32, FAKE, None) == -1
+    assert peak.la_peak_write(FAKE, 0, None) == -1
+    assert peak.la_peak_copy(FAKE, None, 32, None) == -1
+    peak.la_peak_update.argtypes = [P, I64, P]
+    assert peak.la_peak_update(FAKE, 8, None) == -1

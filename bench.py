@@ -34,6 +34,11 @@ events on the launch stream, mean over ``--extra-reps``):
     in the projection buffer, la_prefill_strided reading q, k, v from it and
     writing [B,H,N,d], la_group_norm_gate on that output); the strided
     prefill writing its output token-major is timed beside it;
+  * ``sizes``: the prefill at the other context lengths of the metric's range:
+    4K (B=1, H=64, d=128, zero state; a 512 MB buffer is read between
+    launches so the 256 MB MALL does not serve the ~200 MB of inputs - a read,
+    because a written buffer would leave its write-back to the timed launch) and
+    the 32K crossover continuing from a random fp32 state;
   * ``cp``: one rank's share of the 256K sequence split 8 ways (32,768 tokens,
     H=64, d=128 bf16, the last rank): its prefill from a zero state
     (la_prefill), the fold of the 8 gathered local states into its incoming
@@ -299,6 +304,43 @@ def measure_ceilings(dev, stream, pre_ms, pre_tflops, dec_gbs):
             "prefill_floor_ms_at_stream_rates": round(floor_ms, 4),
             "prefill_frac_of_stream_floor": round(floor_ms / pre_ms, 4),
             "decode_frac_of_update_stream": round(dec_gbs / up, 4)}
+
+
+def measure_sizes(dev, stream, reps):
+    import torch
+    from long_context_layers_amd import binding, inputs
+    res = {}
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)      # 512 MB
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    for name in ("prefill_4k", "prefill_32k_state"):
+        w = inputs.WORKLOADS[name]
+        with torch.cuda.stream(stream):
+            x = inputs.make_workload(name, device=dev)
+            st = x.state.clone()
+            out = torch.empty_like(x.q)
+        stream.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        with torch.cuda.stream(stream):
+            binding.prefill(x.q, x.k, x.v, x.slopes, st, out=out)      # warm-up
+            for a, b in evs:
+                torch.sum(flush, dim=0, out=sink)                       # evicts the MALL
+                st.copy_(x.state)
+                a.record(stream)
+                binding.prefill(x.q, x.k, x.v, x.slopes, st, out=out)
+                b.record(stream)
+        stream.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in evs) / reps
+        fl = prefill_flops(w.B, w.H, w.N, w.d)
+        by = prefill_bytes(w.B, w.H, w.N, w.d)
+        res[name] = {"config": f"B{w.B} H{w.H} N{w.N} d{w.d} bf16, "
+                               + ("random fp32 initial state" if w.init_state else "zero state"),
+                     "ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 3),
+                     "gbs": round(by / (ms * 1e-3) / 1e9, 1),
+                     "frac_of_hbm_peak": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del x, st, out
+    del flush, sink
+    return res
 
 
 def measure_cp(dev, stream, reps):
@@ -573,6 +615,9 @@ def main():
         torch.cuda.empty_cache()
         print("[bench] layer ops (QK norm + RoPE, grouped norm x gate)", file=sys.stderr, flush=True)
         res["layer_ops"] = measure_layer_ops(dev, stream, args.extra_reps, pre_ms)
+        torch.cuda.empty_cache()
+        print("[bench] prefill at 4K and 32K", file=sys.stderr, flush=True)
+        res["sizes"] = measure_sizes(dev, stream, args.extra_reps)
         torch.cuda.empty_cache()
         print("[bench] sequence-sharded prefill steps", file=sys.stderr, flush=True)
         res["cp"] = measure_cp(dev, stream, args.extra_reps)

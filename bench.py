@@ -593,6 +593,17 @@ def main():
             "algorithmic_bytes_per_launch": by,
             "kernel": "prefill_bf16_kernel<128>",
         },
+        "context": {
+            "pages_kernel_numbers": "none: the Ling and Ring 2.6 Technical Report gives no "
+                                    "kernel-level throughput for this path, so vs_baseline is null",
+            "attention_flop_share": "in the GQA predecessor attention takes more than 60% of "
+                                    "all FLOPs once contexts pass 32K tokens (report, §1 and "
+                                    "§2.1.3; hardware not stated)",
+            "context_parallel_speedup": "AllGather context parallelism with variable-length "
+                                        "fusion sped linear-attention training at 256K up by "
+                                        "about 68% end to end (report, §4.1.2; hardware not "
+                                        "stated); its on-GPU arithmetic is the cp line below",
+        },
         "decode": {
             "value": round(dgbs, 1),
             "unit": "GB/s",

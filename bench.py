@@ -126,7 +126,7 @@ def measure_varlen(dev, stream, reps, dense_tflops):
             "nseq": nseq, "ms": round(ms, 4), "tflops": round(tflops, 3),
             "gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
             "algorithmic_bytes_per_launch": by, "vs_dense_256k_tflops": round(tflops / dense_tflops, 4),
-            "kernel": "prefill_bf16_kernel<128> (packed sequence map)"}
+            "kernel": "prefill_bf16_kernel<128, false> (packed sequence map)"}
 
 
 def measure_layer_ops(dev, stream, reps, pre_ms):
@@ -591,7 +591,7 @@ def main():
             "frac": round(gbs / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(),
             "algorithmic_bytes_per_launch": by,
-            "kernel": "prefill_bf16_kernel<128>",
+            "kernel": "prefill_bf16_kernel<128, false>",
         },
         "context": {
             "pages_kernel_numbers": "none: the Ling and Ring 2.6 Technical Report gives no "

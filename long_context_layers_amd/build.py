@@ -4,7 +4,9 @@
 
 Each HIP source is compiled to an object (in parallel), then linked into
 ``long_context_layers_amd/lib/liblightning_attn.so``; the benchmark's
-ceiling probes go into ``lib/liblapeak.so``.  Always recompiles.
+ceiling probes go into ``lib/liblapeak.so``, and the plain-C test program
+``tests/c/la_c_program.c`` (gcc, C99, HIP runtime C API) into
+``tests/c/la_c_program``.  Always recompiles.
 """
 from __future__ import annotations
 
@@ -26,6 +28,9 @@ SOURCES = ["la_api.hip", "prefill_bf16.hip", "prefill_f32.hip", "decode.hip", "l
            "cp.hip"]
 PEAK_SOURCES = ["peak_probe.hip"]
 PEAK_LIB = os.path.join(LIB_DIR, "liblapeak.so")
+C_PROGRAM_SRC = os.path.join(ROOT, "tests", "c", "la_c_program.c")
+C_PROGRAM = os.path.join(ROOT, "tests", "c", "la_c_program")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
@@ -71,7 +76,27 @@ def build(verbose: bool = True) -> str:
         objs = list(ex.map(_compile, srcs))
     _link(objs[:len(SOURCES)], LIB, verbose)
     _link(objs[len(SOURCES):], PEAK_LIB, verbose)
+    _build_c_program(verbose)
     return LIB
+
+
+def _build_c_program(verbose: bool) -> None:
+    """The C ABI from a plain C99 program (gcc, HIP runtime C API)."""
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        raise RuntimeError("gcc not found: needed for tests/c/la_c_program")
+    tmp = C_PROGRAM + ".tmp%d" % os.getpid()
+    cmd = [gcc, "-std=c99", "-O2", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROCM, "include"), "-I", INCLUDE, C_PROGRAM_SRC, "-o", tmp,
+           "-L", LIB_DIR, "-llightning_attn", "-L", os.path.join(ROCM, "lib"), "-lamdhip64", "-lm",
+           "-Wl,-rpath,$ORIGIN/../../long_context_layers_amd/lib",
+           "-Wl,-rpath," + os.path.join(ROCM, "lib")]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"C program build failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, C_PROGRAM)
+    if verbose:
+        print(f"[build] {C_PROGRAM}")
 
 
 if __name__ == "__main__":

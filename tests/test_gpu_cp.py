@@ -3,7 +3,7 @@
 cp_fold / cp_correct on the same bytes, and end to end: every shard run by
 la_prefill from a zero state, folded and corrected, against the oracle's
 recurrence over the unsplit sequence.  Bars: fp32 fold 1e-5 (fp32 sums of at
-most a few dozen terms), bf16 outputs and states 2e-2 (as for the prefill)."""
+most 65 terms), bf16 outputs and states 2e-2 (as for the prefill)."""
 import numpy as np
 import pytest
 import torch
@@ -137,3 +137,20 @@ def test_cp_256k_in_8_shards_sampled_heads():
     es = rel_l2(final.index_select(1, idx), s_ref)
     log(f"  heads {heads}: out rel-L2 {eo:.3e}  final state rel-L2 {es:.3e}")
     assert eo <= BF16_TOL and es <= BF16_TOL
+
+
+@pytest.mark.parametrize("R", [1, 64])
+def test_cp_fold_shard_count_limits(R):
+    # one shard, and the most shards a call takes (64), with uneven lengths
+    B, H, d = 1, 2, 64
+    lens = [(7 * j) % 5 for j in range(R)]
+    log(f"cp_fold with {R} shards {lens[:8]}...")
+    g = torch.Generator(device=DEV).manual_seed(70 + R)
+    loc = 0.1 * torch.randn((R, B, H, d, d), generator=g, device=DEV)
+    init = 0.1 * torch.randn((B, H, d, d), generator=g, device=DEV)
+    s = slopes_of("slow", H)
+    for r in sorted({0, 1, R // 2, R}):
+        got = binding.cp_fold(loc, lens, r, s, init)
+        torch.cuda.synchronize()
+        ref = oracle.cp_fold(np64(loc), lens, np64(s), r, np64(init))
+        assert rel_l2(got, ref) <= FOLD_TOL, r

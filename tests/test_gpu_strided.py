@@ -168,6 +168,20 @@ def test_qk_norm_rope_in_place_bitwise(d, rot):
     assert torch.equal(vo, v_before.unflatten(-1, (H, d)).transpose(1, 2))
 
 
+def test_qk_norm_rope_in_place_with_v_copied_out():
+    # q, k normed and rotated in place while v is still moved to [B,H,N,d]
+    B, N, H, d = 1, 40, 4, 128
+    log(f"qk_norm_rope in place with v out B{B} N{N} H{H} d{d}")
+    buf, (q, k, v, _) = projection(B, N, H, d, 750)
+    w = torch.linspace(0.7, 1.3, d, device=DEV)
+    qo, ko, vo = binding.qk_norm_rope(q, k, v, w, w, H, rot_dim=64)
+    v_ref = v.clone()
+    qi, ki, vi = binding.qk_norm_rope(q, k, v, w, w, H, rot_dim=64, inplace=True)
+    torch.cuda.synchronize()
+    assert torch.equal(qi, qo) and torch.equal(ki, ko)
+    assert torch.equal(vi, vo) and torch.equal(v, v_ref)          # v copied out, not changed
+
+
 def test_group_norm_gate_token_major_o_bitwise():
     B, N, H, d = 2, 37, 4, 128
     log(f"group_norm_gate token-major o B{B} N{N} H{H} d{d}")

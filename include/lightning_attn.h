@@ -200,6 +200,29 @@ int la_decode_multi_f32(const float *q, const float *k, const float *v, const fl
                         int64_t B, int64_t H, int64_t T, int64_t d, void *stream);
 
 /*
+ * Strided decode (bf16): la_decode_step / la_decode_multi reading q, k, v
+ * through element strides, e.g. straight out of a token-major projection
+ * buffer of the new token(s), with no layout copy (the serving counterpart of
+ * la_prefill_strided).  Row (b, h) of q, k, v starts at element
+ * b*in_bstride + h*in_hstride (+ t*in_tstride for token t of la_decode_multi)
+ * from each base pointer and holds d contiguous bf16 channels; strides >= 0,
+ * inputs 2-byte aligned, their rows may overlap (they are only read).  out
+ * stays [B,H,d] / [B,H,T,d] contiguous, 2-byte aligned, and must not overlap
+ * the inputs' spans or the state.  Same arithmetic and results, bitwise, as
+ * the contiguous calls; every other rule as there.  Source: as la_decode_step
+ * and la_decode_multi (the report's §4.3 and Fig. 12 serve the layer of Fig. 2,
+ * whose projections are token-major).
+ */
+int la_decode_step_strided(const void *q, const void *k, const void *v, const float *slopes,
+                           float *state, void *out, int64_t B, int64_t H, int64_t d,
+                           int64_t in_bstride, int64_t in_hstride, void *stream);
+
+int la_decode_multi_strided(const void *q, const void *k, const void *v, const float *slopes,
+                            const int32_t *n_commit, float *state, void *out, int64_t B,
+                            int64_t H, int64_t T, int64_t d, int64_t in_bstride,
+                            int64_t in_hstride, int64_t in_tstride, void *stream);
+
+/*
  * The layer's neighbouring ops, each one fused kernel (bf16 activations, fp32
  * weights and arithmetic).  Source: the report's Fig. 2 (the linear-attention
  * layer: QKV projection -> QK Norm -> RoPE -> this library's kernel -> grouped

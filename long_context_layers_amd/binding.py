@@ -35,6 +35,9 @@ SIGNATURES = {
     "la_decode_multi": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], _INT),
     "la_decode_multi_f32": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], _INT),
     "la_decode_step_f32": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], _INT),
+    "la_decode_step_strided": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P], _INT),
+    "la_decode_multi_strided": ([_P, _P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64,
+                                 _I64, _P], _INT),
     "la_qk_norm_rope": ([_P, _P, _P, _I64, _P, _P, ctypes.c_double, _I64, _I64, ctypes.c_float,
                          _P, _P, _P, _I64, _I64, _I64, _I64, _P], _INT),
     "la_group_norm_gate": ([_P, _I64, _I64, _I64, _P, _I64, _P, _I64, ctypes.c_float, _P,
@@ -236,6 +239,9 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: torch
     """One recurrent step: state = lambda*state + k^T v (in place); returns q . state.
 
     q, k, v: [B,H,d] bf16 or fp32; slopes [H] fp32; state [B,H,d,d] fp32.
+    bf16 q, k, v may be strided views sharing one set of strides (unit
+    channel stride), e.g. head-split slices of a projection buffer
+    (``la_decode_step_strided``); out is [B,H,d] contiguous.
     """
     if not isinstance(q, torch.Tensor) or q.dim() != 3:
         raise ValueError("q must be a [B,H,d] tensor")
@@ -247,13 +253,20 @@ def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: torch
     if dt not in (torch.bfloat16, torch.float32):
         raise TypeError("q/k/v must be bfloat16 or float32")
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n, dt, dev, (B, H, d))
+        _view(t, n, dt, dev, (B, H, d))
     _need(slopes, "slopes", torch.float32, dev, (H,))
     _need(state, "state", torch.float32, dev, (B, H, d, d))
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty((B, H, d), dtype=dt, device=dev)
     else:
         _need(out, "out", dt, dev, (B, H, d))
+    if _strided(q, k, v, None, dt, dev, (B, H, d)):
+        with torch.cuda.device(dev):
+            rc = load_library().la_decode_step_strided(
+                q.data_ptr(), k.data_ptr(), v.data_ptr(), slopes.data_ptr(), state.data_ptr(),
+                out.data_ptr(), B, H, d, *q.stride()[:-1], _stream(dev))
+        _check(rc, "la_decode_step_strided")
+        return out
     lib = load_library()
     fn = lib.la_decode_step if dt == torch.bfloat16 else lib.la_decode_step_f32
     with torch.cuda.device(dev):
@@ -271,7 +284,9 @@ def decode_multi(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: torc
     q, k, v: [B,H,T,d] bf16 or fp32; slopes [H] fp32; state [B,H,d,d] fp32,
     updated in place to the state after n_commit[b] tokens (all T if n_commit
     is None); n_commit: [B] int32 on the same GPU.  Returns out [B,H,T,d] with
-    o_t = q_t S_t for every token.
+    o_t = q_t S_t for every token.  bf16 q, k, v may be strided views sharing
+    one set of strides, e.g. [B,T,H*d] projection slices viewed as [B,H,T,d]
+    (``la_decode_multi_strided``).
     """
     if not isinstance(q, torch.Tensor) or q.dim() != 4:
         raise ValueError("q must be a [B,H,T,d] tensor")
@@ -283,15 +298,23 @@ def decode_multi(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: torc
     if dt not in (torch.bfloat16, torch.float32):
         raise TypeError("q/k/v must be bfloat16 or float32")
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n, dt, dev, (B, H, T, d))
+        _view(t, n, dt, dev, (B, H, T, d))
     _need(slopes, "slopes", torch.float32, dev, (H,))
     _need(state, "state", torch.float32, dev, (B, H, d, d))
     if n_commit is not None:
         _need(n_commit, "n_commit", torch.int32, dev, (B,))
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty((B, H, T, d), dtype=dt, device=dev)
     else:
         _need(out, "out", dt, dev, (B, H, T, d))
+    if _strided(q, k, v, None, dt, dev, (B, H, T, d)):
+        with torch.cuda.device(dev):
+            rc = load_library().la_decode_multi_strided(
+                q.data_ptr(), k.data_ptr(), v.data_ptr(), slopes.data_ptr(),
+                None if n_commit is None else n_commit.data_ptr(), state.data_ptr(),
+                out.data_ptr(), B, H, T, d, *q.stride()[:-1], _stream(dev))
+        _check(rc, "la_decode_multi_strided")
+        return out
     lib = load_library()
     fn = lib.la_decode_multi if dt == torch.bfloat16 else lib.la_decode_multi_f32
     with torch.cuda.device(dev):

@@ -7,6 +7,9 @@
 //
 // The step is bound by HBM: every state is read once and written once
 // (2 x 64 KiB per (b, h) at d = 128) while the arithmetic is 4 d^2 flops.
+// q, k, v are read through element strides (row (b, h[, t]) at b*sb + h*sh
+// [+ t*st], channels contiguous), so they can come straight out of a
+// token-major projection buffer; out is [B,H,d] ([B,H,T,d]) contiguous.
 // One workgroup streams one (b, h) state: thread t owns the 4-column group
 // t % (D/4) on rows t / (D/4) + (256 / (D/4)) m.  All of a thread's rows are
 // loaded up front (dwordx4, non-temporal: a state is touched once per step),
@@ -34,7 +37,8 @@ template <> __device__ __forceinline__ void store_act<float>(float *p, float x) 
 template <typename T, int D>
 __global__ __launch_bounds__(DT) void decode_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
-    const float *__restrict__ slopes, float *__restrict__ state, T *__restrict__ out, int64_t H)
+    const float *__restrict__ slopes, float *__restrict__ state, T *__restrict__ out, int64_t H,
+    int64_t sb, int64_t sh)
 {
     constexpr int CG = D / 4;         // float4 column groups per row
     constexpr int RG = DT / CG;       // row groups
@@ -52,11 +56,12 @@ __global__ __launch_bounds__(DT) void decode_kernel(
 #pragma unroll
     for (int m = 0; m < RPT; ++m) s[m] = __builtin_nontemporal_load(&S[(rg + RG * m) * CG + cg]);
 
+    const int64_t in0 = (bh / H) * sb + (bh % H) * sh;
     if (tid < D) {
-        qk[0][tid] = load_act<T>(q + bh * D + tid);
-        qk[1][tid] = load_act<T>(k + bh * D + tid);
+        qk[0][tid] = load_act<T>(q + in0 + tid);
+        qk[1][tid] = load_act<T>(k + in0 + tid);
     }
-    const T *vb = v + bh * D + 4 * cg;
+    const T *vb = v + in0 + 4 * cg;
     const float v0 = load_act<T>(vb), v1 = load_act<T>(vb + 1), v2 = load_act<T>(vb + 2),
                 v3 = load_act<T>(vb + 3);
     __syncthreads();
@@ -103,7 +108,8 @@ template <typename T, int D>
 __global__ __launch_bounds__(DT) void decode_multi_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ slopes, const int32_t *__restrict__ n_commit,
-    float *__restrict__ state, T *__restrict__ out, int64_t H, int NT)
+    float *__restrict__ state, T *__restrict__ out, int64_t H, int NT,
+    int64_t sb, int64_t sh, int64_t st)
 {
     constexpr int CG = D / 4;         // float4 column groups per row
     constexpr int RG = DT / CG;       // row groups
@@ -122,10 +128,11 @@ __global__ __launch_bounds__(DT) void decode_multi_kernel(
 #pragma unroll
     for (int m = 0; m < RPT; ++m) s[m] = __builtin_nontemporal_load(&S[(rg + RG * m) * CG + cg]);
 
-    const int64_t a0 = bh * NT * D;   // first activation element of this (b, h)
+    const int64_t a0 = bh * NT * D;   // first output element of this (b, h)
+    const int64_t in0 = (bh / H) * sb + (bh % H) * sh;   // its first input row
     for (int e = tid; e < NT * D; e += DT) {
-        qk[e / D][0][e % D] = load_act<T>(q + a0 + e);
-        qk[e / D][1][e % D] = load_act<T>(k + a0 + e);
+        qk[e / D][0][e % D] = load_act<T>(q + in0 + (e / D) * st + e % D);
+        qk[e / D][1][e % D] = load_act<T>(k + in0 + (e / D) * st + e % D);
     }
     float vv[MAXT][4];
 #pragma unroll
@@ -134,7 +141,7 @@ __global__ __launch_bounds__(DT) void decode_multi_kernel(
         for (int j = 0; j < 4; ++j) vv[t][j] = 0.f;
         if (t < NT) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) vv[t][j] = load_act<T>(v + a0 + t * D + 4 * cg + j);
+            for (int j = 0; j < 4; ++j) vv[t][j] = load_act<T>(v + in0 + t * st + 4 * cg + j);
         }
     }
     __syncthreads();
@@ -179,11 +186,13 @@ __global__ __launch_bounds__(DT) void decode_multi_kernel(
 template <typename T>
 hipError_t launch_decode_multi(const T *q, const T *k, const T *v, const float *slopes,
                                const int32_t *n_commit, float *state, T *out, int64_t B,
-                               int64_t H, int nt, int d, hipStream_t stream)
+                               int64_t H, int nt, int d, const Strides &in, hipStream_t stream)
 {
     const dim3 grid((unsigned)(B * H)), block(DT);
+    int64_t sb = in.sb, sh = in.sh, st = in.st;
     void *args[] = {(void *)&q, (void *)&k, (void *)&v, (void *)&slopes, (void *)&n_commit,
-                    (void *)&state, (void *)&out, (void *)&H, (void *)&nt};
+                    (void *)&state, (void *)&out, (void *)&H, (void *)&nt, (void *)&sb,
+                    (void *)&sh, (void *)&st};
     const void *fn = d == 64 ? (const void *)decode_multi_kernel<T, 64>
                              : (const void *)decode_multi_kernel<T, 128>;
     return hipLaunchKernel(fn, grid, block, args, 0, stream);
@@ -191,11 +200,13 @@ hipError_t launch_decode_multi(const T *q, const T *k, const T *v, const float *
 
 template <typename T>
 hipError_t launch_decode(const T *q, const T *k, const T *v, const float *slopes, float *state,
-                         T *out, int64_t B, int64_t H, int d, hipStream_t stream)
+                         T *out, int64_t B, int64_t H, int d, const Strides &in,
+                         hipStream_t stream)
 {
     const dim3 grid((unsigned)(B * H)), block(DT);
+    int64_t sb = in.sb, sh = in.sh;
     void *args[] = {(void *)&q, (void *)&k, (void *)&v, (void *)&slopes,
-                    (void *)&state, (void *)&out, (void *)&H};
+                    (void *)&state, (void *)&out, (void *)&H, (void *)&sb, (void *)&sh};
     const void *fn = d == 64 ? (const void *)decode_kernel<T, 64>
                              : (const void *)decode_kernel<T, 128>;
     return hipLaunchKernel(fn, grid, block, args, 0, stream);
@@ -205,25 +216,26 @@ hipError_t launch_decode(const T *q, const T *k, const T *v, const float *slopes
 
 hipError_t launch_decode_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                               const float *slopes, float *state, uint16_t *out,
-                              int64_t B, int64_t H, int d, hipStream_t stream)
+                              int64_t B, int64_t H, int d, const Strides &in, hipStream_t stream)
 {
-    return launch_decode<uint16_t>(q, k, v, slopes, state, out, B, H, d, stream);
+    return launch_decode<uint16_t>(q, k, v, slopes, state, out, B, H, d, in, stream);
 }
 
 hipError_t launch_decode_f32(const float *q, const float *k, const float *v,
                              const float *slopes, float *state, float *out,
                              int64_t B, int64_t H, int d, hipStream_t stream)
 {
-    return launch_decode<float>(q, k, v, slopes, state, out, B, H, d, stream);
+    const Strides in = {H * d, d, d};
+    return launch_decode<float>(q, k, v, slopes, state, out, B, H, d, in, stream);
 }
 
 hipError_t launch_decode_multi_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                     const float *slopes, const int32_t *n_commit, float *state,
                                     uint16_t *out, int64_t B, int64_t H, int nt, int d,
-                                    hipStream_t stream)
+                                    const Strides &in, hipStream_t stream)
 {
     return launch_decode_multi<uint16_t>(q, k, v, slopes, n_commit, state, out, B, H, nt, d,
-                                         stream);
+                                         in, stream);
 }
 
 hipError_t launch_decode_multi_f32(const float *q, const float *k, const float *v,
@@ -231,7 +243,8 @@ hipError_t launch_decode_multi_f32(const float *q, const float *k, const float *
                                    float *out, int64_t B, int64_t H, int nt, int d,
                                    hipStream_t stream)
 {
-    return launch_decode_multi<float>(q, k, v, slopes, n_commit, state, out, B, H, nt, d,
+    const Strides in = {H * nt * d, nt * d, d};
+    return launch_decode_multi<float>(q, k, v, slopes, n_commit, state, out, B, H, nt, d, in,
                                       stream);
 }
 

@@ -208,6 +208,30 @@ int check_strided(const void *q, const void *k, const void *v, const float *slop
     return LA_OK;
 }
 
+// strided bf16 decode: q, k, v rows (b, h, t) at b*s[0] + h*s[1] + t*s[2]
+// (n = {B, H, T}), out [B,H,T,d] contiguous; inputs are read element by
+// element (2-byte aligned), out and the state as in the contiguous calls
+int check_decode_strided(const void *q, const void *k, const void *v, const float *slopes,
+                         const float *state, const void *out, const int64_t n[3],
+                         const int64_t si[3], int64_t d)
+{
+    if (!q || !k || !v || !slopes || !out || !state) return LA_ERR_INVALID_ARG;
+    if (n[0] < 1 || n[1] < 1) return LA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
+    int64_t bh, act, out_bytes, st, st_bytes, in_bytes;
+    if (!mul_ok(n[0], n[1], &bh) || !mul_ok(bh, n[2] * d, &act) || !mul_ok(act, 2, &out_bytes) ||
+        !mul_ok(bh, d * d, &st) || !mul_ok(st, 4, &st_bytes) || !view_span(n, si, d, 2, &in_bytes))
+        return LA_ERR_INVALID_ARG;
+    if (!aligned(q, 2) || !aligned(k, 2) || !aligned(v, 2) || !aligned(out, 2) ||
+        !aligned(state, 16) || !aligned(slopes, 4))
+        return LA_ERR_INVALID_ARG;
+    if (overlap(out, out_bytes, q, in_bytes) || overlap(out, out_bytes, k, in_bytes) ||
+        overlap(out, out_bytes, v, in_bytes) || overlap(out, out_bytes, state, st_bytes))
+        return LA_ERR_INVALID_ARG;
+    if (bh > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+    return LA_OK;
+}
+
 // dense [seqs, H, N, d] strides, and the packed [H, T, d] ones
 la::Strides dense_strides(int64_t H, int64_t N, int64_t d) { return {H * N * d, N * d, d}; }
 la::Strides packed_strides(int64_t T, int64_t d) { return {0, T * d, d}; }
@@ -355,10 +379,26 @@ int la_decode_step(const void *q, const void *k, const void *v, const float *slo
 {
     const int rc = check_decode(q, k, v, slopes, state, out, B, H, d, 2);
     if (rc != LA_OK) return rc;
+    const la::Strides in = {H * d, d, d};
     return hip_status(la::launch_decode_bf16(
         static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
         static_cast<const uint16_t *>(v), slopes, state, static_cast<uint16_t *>(out), B, H,
-        (int)d, static_cast<hipStream_t>(stream)));
+        (int)d, in, static_cast<hipStream_t>(stream)));
+}
+
+int la_decode_step_strided(const void *q, const void *k, const void *v, const float *slopes,
+                           float *state, void *out, int64_t B, int64_t H, int64_t d,
+                           int64_t in_bstride, int64_t in_hstride, void *stream)
+{
+    const int64_t n[3] = {B, H, 1};
+    const int64_t si[3] = {in_bstride, in_hstride, 0};
+    const int rc = check_decode_strided(q, k, v, slopes, state, out, n, si, d);
+    if (rc != LA_OK) return rc;
+    const la::Strides in = {in_bstride, in_hstride, 0};
+    return hip_status(la::launch_decode_bf16(
+        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+        static_cast<const uint16_t *>(v), slopes, state, static_cast<uint16_t *>(out), B, H,
+        (int)d, in, static_cast<hipStream_t>(stream)));
 }
 
 int la_decode_step_f32(const float *q, const float *k, const float *v, const float *slopes,
@@ -376,10 +416,30 @@ int la_decode_multi(const void *q, const void *k, const void *v, const float *sl
 {
     const int rc = check_decode_multi(q, k, v, slopes, n_commit, state, out, B, H, T, d, 2);
     if (rc != LA_OK) return rc;
+    const la::Strides in = {H * T * d, T * d, d};
     return hip_status(la::launch_decode_multi_bf16(
         static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
         static_cast<const uint16_t *>(v), slopes, n_commit, state, static_cast<uint16_t *>(out),
-        B, H, (int)T, (int)d, static_cast<hipStream_t>(stream)));
+        B, H, (int)T, (int)d, in, static_cast<hipStream_t>(stream)));
+}
+
+int la_decode_multi_strided(const void *q, const void *k, const void *v, const float *slopes,
+                            const int32_t *n_commit, float *state, void *out, int64_t B,
+                            int64_t H, int64_t T, int64_t d, int64_t in_bstride,
+                            int64_t in_hstride, int64_t in_tstride, void *stream)
+{
+    if (T < 1) return LA_ERR_INVALID_ARG;
+    if (T > la::decode_multi_max_tokens()) return LA_ERR_UNSUPPORTED;
+    if (n_commit && !aligned(n_commit, 4)) return LA_ERR_INVALID_ARG;
+    const int64_t n[3] = {B, H, T};
+    const int64_t si[3] = {in_bstride, in_hstride, in_tstride};
+    const int rc = check_decode_strided(q, k, v, slopes, state, out, n, si, d);
+    if (rc != LA_OK) return rc;
+    const la::Strides in = {in_bstride, in_hstride, in_tstride};
+    return hip_status(la::launch_decode_multi_bf16(
+        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+        static_cast<const uint16_t *>(v), slopes, n_commit, state, static_cast<uint16_t *>(out),
+        B, H, (int)T, (int)d, in, static_cast<hipStream_t>(stream)));
 }
 
 int la_decode_multi_f32(const float *q, const float *k, const float *v, const float *slopes,

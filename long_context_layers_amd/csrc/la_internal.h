@@ -51,9 +51,11 @@ hipError_t launch_prefill_bf16(const uint16_t *q, const uint16_t *k, const uint1
 hipError_t launch_prefill_f32(const float *q, const float *k, const float *v,
                               const float *slopes, float *out, float *state,
                               int64_t seqs, const SeqMap &map, int d, hipStream_t stream);
+// bf16 decode reads q, k, v through element strides (in.st unused by the
+// single-token step); out is contiguous
 hipError_t launch_decode_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                               const float *slopes, float *state, uint16_t *out,
-                              int64_t B, int64_t H, int d, hipStream_t stream);
+                              int64_t B, int64_t H, int d, const Strides &in, hipStream_t stream);
 hipError_t launch_decode_f32(const float *q, const float *k, const float *v,
                              const float *slopes, float *state, float *out,
                              int64_t B, int64_t H, int d, hipStream_t stream);
@@ -62,7 +64,7 @@ hipError_t launch_decode_f32(const float *q, const float *k, const float *v,
 hipError_t launch_decode_multi_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                     const float *slopes, const int32_t *n_commit, float *state,
                                     uint16_t *out, int64_t B, int64_t H, int T, int d,
-                                    hipStream_t stream);
+                                    const Strides &in, hipStream_t stream);
 hipError_t launch_decode_multi_f32(const float *q, const float *k, const float *v,
                                    const float *slopes, const int32_t *n_commit, float *state,
                                    float *out, int64_t B, int64_t H, int T, int d,

@@ -459,3 +459,41 @@ def test_peak_probe_library_loads_and_rejects_bad_arguments():
     assert peak.la_peak_copy(FAKE, None, 32, None) == -1
     peak.la_peak_update.argtypes = [P, I64, P]
     assert peak.la_peak_update(FAKE, 8, None) == -1
+
+
+def _dstr_args(**kw):
+    a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, slopes=FAKE + 0x300000, nc=None,
+             state=FAKE + 0x400000, out=FAKE + 0x900000, B=2, H=2, T=3, d=64, sb=3 * 2 * 64,
+             sh=64, st=6 * 64 * 3, stream=None)
+    a.update(kw)
+    return a
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("bad,code", [
+    (dict(q=None), LA_ERR_INVALID_ARG), (dict(state=None), LA_ERR_INVALID_ARG),
+    (dict(d=96), LA_ERR_UNSUPPORTED), (dict(B=0), LA_ERR_INVALID_ARG),
+    (dict(sb=-8), LA_ERR_INVALID_ARG),                          # negative stride
+    (dict(q=FAKE + 1), LA_ERR_INVALID_ARG),                     # not 2-byte aligned
+    (dict(state=FAKE + 0x400008), LA_ERR_INVALID_ARG),
+    (dict(out=FAKE + 64), LA_ERR_INVALID_ARG),                  # out inside q's span
+    (dict(out=FAKE + 0x400000), LA_ERR_INVALID_ARG),            # out over the state
+])
+def test_decode_step_strided_rejects_bad_arguments(lib, bad, code):
+    a = _dstr_args(**bad)
+    assert lib.la_decode_step_strided(a["q"], a["k"], a["v"], a["slopes"], a["state"], a["out"],
+                                      a["B"], a["H"], a["d"], a["sb"], a["sh"], a["stream"]) == code
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("bad,code", [
+    (dict(T=0), LA_ERR_INVALID_ARG), (dict(T=9), LA_ERR_UNSUPPORTED),
+    (dict(nc=FAKE + 0xa00002), LA_ERR_INVALID_ARG),             # misaligned n_commit
+    (dict(v=None), LA_ERR_INVALID_ARG), (dict(st=-64), LA_ERR_INVALID_ARG),
+    (dict(out=FAKE + 0x200010), LA_ERR_INVALID_ARG),            # out inside v's span
+])
+def test_decode_multi_strided_rejects_bad_arguments(lib, bad, code):
+    a = _dstr_args(**bad)
+    assert lib.la_decode_multi_strided(a["q"], a["k"], a["v"], a["slopes"], a["nc"], a["state"],
+                                       a["out"], a["B"], a["H"], a["T"], a["d"], a["sb"], a["sh"],
+                                       a["st"], a["stream"]) == code

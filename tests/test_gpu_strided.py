@@ -233,3 +233,43 @@ def test_layer_chain_without_layout_copies():
                      / np.linalg.norm(ry.reshape(-1, H * d), axis=1)))
     log(f"  y rel-L2 {e:.3e} (bar 2e-2)")
     assert e <= 2e-2
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_step_strided_bitwise(d):
+    # one new token per sequence, q | k | v of all heads in one row per sequence
+    B, H = 5, 4
+    log(f"strided decode step B{B} H{H} d{d}")
+    x = inputs.make_decode(B, H, d, 1, torch.bfloat16, seed=120 + d, device=DEV)
+    st_ref = x.state.clone()
+    o_ref = binding.decode_step(x.q[0], x.k[0], x.v[0], x.slopes, st_ref)
+    row = torch.full((B, 3 * H * d + 16), SENTINEL, dtype=torch.bfloat16, device=DEV)
+    qv, kv, vv = (row[:, i * H * d:(i + 1) * H * d].unflatten(-1, (H, d)) for i in range(3))
+    for dst, src in ((qv, x.q[0]), (kv, x.k[0]), (vv, x.v[0])):
+        dst.copy_(src)
+    st = x.state.clone()
+    o = binding.decode_step(qv, kv, vv, x.slopes, st)
+    torch.cuda.synchronize()
+    assert qv.stride() == (3 * H * d + 16, d, 1)
+    assert torch.equal(o, o_ref) and torch.equal(st, st_ref)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_multi_strided_bitwise(d):
+    # draft tokens straight from a [B, T, 4*H*d] projection buffer
+    B, H, T = 3, 4, 4
+    log(f"strided multi-token decode B{B} H{H} T{T} d{d}")
+    x = inputs.make_decode(B, H, d, T, torch.bfloat16, seed=130 + d, device=DEV)
+    q, k, v = (t.permute(1, 2, 0, 3).contiguous() for t in (x.q, x.k, x.v))   # [B,H,T,d]
+    ncommit = torch.tensor([1, 4, 0], dtype=torch.int32, device=DEV)
+    st_ref = x.state.clone()
+    o_ref = binding.decode_multi(q, k, v, x.slopes, st_ref, n_commit=ncommit)
+    buf = torch.full((B, T, 4 * H * d), SENTINEL, dtype=torch.bfloat16, device=DEV)
+    views = [heads_view(buf, i * H * d, H, d) for i in range(3)]
+    for dst, src in zip(views, (q, k, v)):
+        dst.copy_(src)
+    st = x.state.clone()
+    o = binding.decode_multi(*views, x.slopes, st, n_commit=ncommit)
+    torch.cuda.synchronize()
+    assert views[0].stride() == (T * 4 * H * d, d, 4 * H * d, 1)
+    assert torch.equal(o, o_ref) and torch.equal(st, st_ref)

@@ -42,6 +42,9 @@ events on the launch stream, mean over ``--extra-reps``):
     launches so the 256 MB MALL does not serve the ~200 MB of inputs - a read,
     because a written buffer would leave its write-back to the timed launch) and
     the 32K crossover continuing from a random fp32 state;
+  * ``decode_latency``: one sequence (B=1, H=64, d=128) decoded for 64
+    steps, launched one call at a time and replayed from one captured HIP
+    graph (torch.cuda.CUDAGraph): per-step latency of each;
   * ``cp``: one rank's share of the 256K sequence split 8 ways (32,768 tokens,
     H=64, d=128 bf16, the last rank): its prefill from a zero state
     (la_prefill), the fold of the 8 gathered local states into its incoming
@@ -346,6 +349,39 @@ def measure_sizes(dev, stream, reps):
     return res
 
 
+def measure_decode_latency(dev, stream, reps):
+    import torch
+    from long_context_layers_amd import binding, inputs
+    B, H, d, steps = 1, DECODE["H"], DECODE["d"], 64
+    x = inputs.make_decode(B, H, d, steps, torch.bfloat16, DECODE["seed"], dev)
+    st = x.state.clone()
+    out = torch.empty_like(x.q[0])
+
+    def run():
+        for t in range(steps):
+            binding.decode_step(x.q[t], x.k[t], x.v[t], x.slopes, st, out=out)
+
+    with torch.cuda.stream(stream):
+        ms_eager = min(time_launches(stream, run, 1) for _ in range(reps)) / steps
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        run()
+    with torch.cuda.stream(stream):
+        ms_graph = min(time_launches(stream, g.replay, 1) for _ in range(reps)) / steps
+    torch.cuda.synchronize()
+    by = decode_bytes(B, H, d)
+    del g, x, st, out
+    return {"workload": f"B{B} H{H} d{d} bf16, {steps} decode steps of one sequence",
+            "eager_us_per_step": round(ms_eager * 1e3, 2),
+            "graph_us_per_step": round(ms_graph * 1e3, 2),
+            "graph_speedup": round(ms_eager / ms_graph, 3),
+            "graph_gbs": round(by / (ms_graph * 1e-3) / 1e9, 1),
+            "algorithmic_bytes_per_step": by,
+            "kernel": "decode_kernel<bf16,128,4>: 4 column slices per head, 256 workgroups "
+                      "per step"}
+
+
 def measure_cp(dev, stream, reps):
     import torch
     from long_context_layers_amd import binding, inputs
@@ -646,6 +682,10 @@ def main():
         torch.cuda.empty_cache()
         print("[bench] prefill at 4K and 32K", file=sys.stderr, flush=True)
         res["sizes"] = measure_sizes(dev, stream, args.extra_reps)
+        torch.cuda.empty_cache()
+        print("[bench] single-sequence decode latency (eager, HIP graph)", file=sys.stderr,
+              flush=True)
+        res["decode_latency"] = measure_decode_latency(dev, stream, args.extra_reps)
         torch.cuda.empty_cache()
         print("[bench] sequence-sharded prefill steps", file=sys.stderr, flush=True)
         res["cp"] = measure_cp(dev, stream, args.extra_reps)

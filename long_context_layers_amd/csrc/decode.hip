@@ -10,11 +10,14 @@
 // q, k, v are read through element strides (row (b, h[, t]) at b*sb + h*sh
 // [+ t*st], channels contiguous), so they can come straight out of a
 // token-major projection buffer; out is [B,H,d] ([B,H,T,d]) contiguous.
-// One workgroup streams one (b, h) state: thread t owns the 4-column group
-// t % (D/4) on rows t / (D/4) + (256 / (D/4)) m.  All of a thread's rows are
-// loaded up front (dwordx4, non-temporal: a state is touched once per step),
-// updated in registers, written back, and the partial o = q S' sums over
-// rows are reduced across the row groups in LDS (fixed order, no atomics).
+// A workgroup streams the D/NS columns js*D/NS .. of one (b, h) state (NS = 1
+// for large batches; 2 or 4 when B*H workgroups would not fill the chip: an
+// output column only sums over rows, so the column slices are independent):
+// thread t owns the 4-column group t % CG of the slice on rows
+// t / CG + (256 / CG) m.  All of a thread's rows are loaded up front (dwordx4,
+// non-temporal: a state is touched once per step), updated in registers,
+// written back, and the partial o = q S' sums over rows are reduced across
+// the row groups in LDS (fixed order, no atomics).
 #include "la_internal.h"
 
 namespace la {
@@ -34,34 +37,36 @@ template <> __device__ __forceinline__ void store_act<uint16_t>(uint16_t *p, flo
 }
 template <> __device__ __forceinline__ void store_act<float>(float *p, float x) { *p = x; }
 
-template <typename T, int D>
+template <typename T, int D, int NS>
 __global__ __launch_bounds__(DT) void decode_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ slopes, float *__restrict__ state, T *__restrict__ out, int64_t H,
     int64_t sb, int64_t sh)
 {
-    constexpr int CG = D / 4;         // float4 column groups per row
+    constexpr int DC = D / NS;        // columns of this workgroup's slice
+    constexpr int CG = DC / 4;        // float4 column groups of the slice
     constexpr int RG = DT / CG;       // row groups
     constexpr int RPT = D / RG;       // rows per thread
-    __shared__ float red[RG][D];
+    __shared__ float red[RG][DC];
     __shared__ float qk[2][D];
 
     const int tid = threadIdx.x;
-    const int64_t bh = blockIdx.x;
+    const int64_t bh = blockIdx.x / NS;
+    const int j0 = (int)(blockIdx.x % NS) * DC;
     const float lam = decay_pow(slopes[bh % H], 1);
     const int cg = tid % CG, rg = tid / CG;
 
-    f32x4 *S = reinterpret_cast<f32x4 *>(state + bh * D * D);
+    f32x4 *S = reinterpret_cast<f32x4 *>(state + bh * D * D + j0);
     f32x4 s[RPT];
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) s[m] = __builtin_nontemporal_load(&S[(rg + RG * m) * CG + cg]);
+    for (int m = 0; m < RPT; ++m) s[m] = __builtin_nontemporal_load(&S[(rg + RG * m) * (D / 4) + cg]);
 
     const int64_t in0 = (bh / H) * sb + (bh % H) * sh;
     if (tid < D) {
         qk[0][tid] = load_act<T>(q + in0 + tid);
         qk[1][tid] = load_act<T>(k + in0 + tid);
     }
-    const T *vb = v + in0 + 4 * cg;
+    const T *vb = v + in0 + j0 + 4 * cg;
     const float v0 = load_act<T>(vb), v1 = load_act<T>(vb + 1), v2 = load_act<T>(vb + 2),
                 v3 = load_act<T>(vb + 3);
     __syncthreads();
@@ -76,7 +81,7 @@ __global__ __launch_bounds__(DT) void decode_kernel(
         x.y = fmaf(lam, x.y, ki * v1);
         x.z = fmaf(lam, x.z, ki * v2);
         x.w = fmaf(lam, x.w, ki * v3);
-        __builtin_nontemporal_store(x, &S[i * CG + cg]);
+        __builtin_nontemporal_store(x, &S[i * (D / 4) + cg]);
         o0 = fmaf(qi, x.x, o0);
         o1 = fmaf(qi, x.y, o1);
         o2 = fmaf(qi, x.z, o2);
@@ -87,11 +92,11 @@ __global__ __launch_bounds__(DT) void decode_kernel(
     red[rg][4 * cg + 2] = o2;
     red[rg][4 * cg + 3] = o3;
     __syncthreads();
-    if (tid < D) {
+    if (tid < DC) {
         float acc = 0.f;
 #pragma unroll
         for (int g = 0; g < RG; ++g) acc += red[g][tid];
-        store_act<T>(out + bh * D + tid, acc);
+        store_act<T>(out + bh * D + j0 + tid, acc);
     }
 }
 
@@ -104,29 +109,31 @@ __global__ __launch_bounds__(DT) void decode_kernel(
 // share one LDS pass.
 constexpr int MAXT = 8;   // tokens per sequence and call
 
-template <typename T, int D>
+template <typename T, int D, int NS>
 __global__ __launch_bounds__(DT) void decode_multi_kernel(
     const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
     const float *__restrict__ slopes, const int32_t *__restrict__ n_commit,
     float *__restrict__ state, T *__restrict__ out, int64_t H, int NT,
     int64_t sb, int64_t sh, int64_t st)
 {
-    constexpr int CG = D / 4;         // float4 column groups per row
+    constexpr int DC = D / NS;        // columns of this workgroup's slice
+    constexpr int CG = DC / 4;        // float4 column groups of the slice
     constexpr int RG = DT / CG;       // row groups
     constexpr int RPT = D / RG;       // rows per thread
-    __shared__ float red[RG][MAXT][D];
+    __shared__ float red[RG][MAXT][DC];
     __shared__ float qk[MAXT][2][D];
 
     const int tid = threadIdx.x;
-    const int64_t bh = blockIdx.x;
+    const int64_t bh = blockIdx.x / NS;
+    const int j0 = (int)(blockIdx.x % NS) * DC;
     const float lam = decay_pow(slopes[bh % H], 1);
     const int ncommit = n_commit ? min(max(n_commit[bh / H], 0), NT) : NT;
     const int cg = tid % CG, rg = tid / CG;
 
-    f32x4 *S = reinterpret_cast<f32x4 *>(state + bh * D * D);
+    f32x4 *S = reinterpret_cast<f32x4 *>(state + bh * D * D + j0);
     f32x4 s[RPT];
 #pragma unroll
-    for (int m = 0; m < RPT; ++m) s[m] = __builtin_nontemporal_load(&S[(rg + RG * m) * CG + cg]);
+    for (int m = 0; m < RPT; ++m) s[m] = __builtin_nontemporal_load(&S[(rg + RG * m) * (D / 4) + cg]);
 
     const int64_t a0 = bh * NT * D;   // first output element of this (b, h)
     const int64_t in0 = (bh / H) * sb + (bh % H) * sh;   // its first input row
@@ -141,7 +148,7 @@ __global__ __launch_bounds__(DT) void decode_multi_kernel(
         for (int j = 0; j < 4; ++j) vv[t][j] = 0.f;
         if (t < NT) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) vv[t][j] = load_act<T>(v + in0 + t * st + 4 * cg + j);
+            for (int j = 0; j < 4; ++j) vv[t][j] = load_act<T>(v + in0 + t * st + j0 + 4 * cg + j);
         }
     }
     __syncthreads();
@@ -167,7 +174,7 @@ __global__ __launch_bounds__(DT) void decode_multi_kernel(
         }
         if (t == ncommit - 1) {
 #pragma unroll
-            for (int m = 0; m < RPT; ++m) __builtin_nontemporal_store(s[m], &S[(rg + RG * m) * CG + cg]);
+            for (int m = 0; m < RPT; ++m) __builtin_nontemporal_store(s[m], &S[(rg + RG * m) * (D / 4) + cg]);
         }
         red[rg][t][4 * cg + 0] = o0;
         red[rg][t][4 * cg + 1] = o1;
@@ -175,12 +182,30 @@ __global__ __launch_bounds__(DT) void decode_multi_kernel(
         red[rg][t][4 * cg + 3] = o3;
     }
     __syncthreads();
-    for (int e = tid; e < NT * D; e += DT) {
+    for (int e = tid; e < NT * DC; e += DT) {
         float acc = 0.f;
 #pragma unroll
-        for (int g = 0; g < RG; ++g) acc += red[g][e / D][e % D];
-        store_act<T>(out + a0 + e, acc);
+        for (int g = 0; g < RG; ++g) acc += red[g][e / DC][e % DC];
+        store_act<T>(out + a0 + (e / DC) * D + j0 + e % DC, acc);
     }
+}
+
+// column slices per (b, h) state: enough workgroups to fill the chip (the
+// single and multi-token kernels use the same split, so their results agree
+// bitwise)
+int decode_slices(int64_t bh) { return bh <= 256 ? 4 : (bh <= 1024 ? 2 : 1); }
+
+template <typename T, int D>
+const void *decode_fn(int ns) {
+    return ns == 4 ? (const void *)decode_kernel<T, D, 4>
+         : ns == 2 ? (const void *)decode_kernel<T, D, 2> : (const void *)decode_kernel<T, D, 1>;
+}
+
+template <typename T, int D>
+const void *decode_multi_fn(int ns) {
+    return ns == 4 ? (const void *)decode_multi_kernel<T, D, 4>
+         : ns == 2 ? (const void *)decode_multi_kernel<T, D, 2>
+                   : (const void *)decode_multi_kernel<T, D, 1>;
 }
 
 template <typename T>
@@ -188,13 +213,13 @@ hipError_t launch_decode_multi(const T *q, const T *k, const T *v, const float *
                                const int32_t *n_commit, float *state, T *out, int64_t B,
                                int64_t H, int nt, int d, const Strides &in, hipStream_t stream)
 {
-    const dim3 grid((unsigned)(B * H)), block(DT);
+    const int ns = decode_slices(B * H);
+    const dim3 grid((unsigned)(B * H * ns)), block(DT);
     int64_t sb = in.sb, sh = in.sh, st = in.st;
     void *args[] = {(void *)&q, (void *)&k, (void *)&v, (void *)&slopes, (void *)&n_commit,
                     (void *)&state, (void *)&out, (void *)&H, (void *)&nt, (void *)&sb,
                     (void *)&sh, (void *)&st};
-    const void *fn = d == 64 ? (const void *)decode_multi_kernel<T, 64>
-                             : (const void *)decode_multi_kernel<T, 128>;
+    const void *fn = d == 64 ? decode_multi_fn<T, 64>(ns) : decode_multi_fn<T, 128>(ns);
     return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 
@@ -203,12 +228,12 @@ hipError_t launch_decode(const T *q, const T *k, const T *v, const float *slopes
                          T *out, int64_t B, int64_t H, int d, const Strides &in,
                          hipStream_t stream)
 {
-    const dim3 grid((unsigned)(B * H)), block(DT);
+    const int ns = decode_slices(B * H);
+    const dim3 grid((unsigned)(B * H * ns)), block(DT);
     int64_t sb = in.sb, sh = in.sh;
     void *args[] = {(void *)&q, (void *)&k, (void *)&v, (void *)&slopes,
                     (void *)&state, (void *)&out, (void *)&H, (void *)&sb, (void *)&sh};
-    const void *fn = d == 64 ? (const void *)decode_kernel<T, 64>
-                             : (const void *)decode_kernel<T, 128>;
+    const void *fn = d == 64 ? decode_fn<T, 64>(ns) : decode_fn<T, 128>(ns);
     return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 

@@ -1,0 +1,113 @@
+"""The library's calls captured in HIP graphs (torch.cuda.CUDAGraph): every
+launch goes to the caller's stream and nothing is allocated or cleared inside
+a call, so a captured decode step, multi-token decode or prefill chunk
+replays with whatever the static input buffers hold.  Each replay is checked
+bitwise against the same call run eagerly, with eager work and
+synchronisations between the replays."""
+import pytest
+import torch
+
+from long_context_layers_amd import binding, inputs
+from tests.gpu_util import log
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    binding.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def test_decode_steps_replayed_from_a_graph():
+    B, H, d, steps = 4, 8, 128, 6
+    log(f"graph: decode step B{B} H{H} d{d}, {steps} replays")
+    x = inputs.make_decode(B, H, d, steps, torch.bfloat16, seed=140, device=DEV)
+    q, k, v = (torch.empty_like(x.q[0]) for _ in range(3))        # static inputs
+    state = x.state.clone()
+    out = torch.empty_like(x.q[0])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                                      # warm-up outside the capture
+        binding.decode_step(q, k, v, x.slopes, state.clone(), out=torch.empty_like(out))
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        binding.decode_step(q, k, v, x.slopes, state, out=out)
+    state.copy_(x.state)                                            # capture ran nothing
+    ref_state = x.state.clone()
+    for t in range(steps):
+        q.copy_(x.q[t]); k.copy_(x.k[t]); v.copy_(x.v[t])
+        g.replay()
+        ref = binding.decode_step(x.q[t], x.k[t], x.v[t], x.slopes, ref_state)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), t
+        assert torch.equal(state, ref_state), t
+
+
+def test_multi_token_decode_replayed_from_a_graph():
+    B, H, T, d = 3, 4, 4, 64
+    log(f"graph: multi-token decode B{B} H{H} T{T} d{d}")
+    x = inputs.make_decode(B, H, d, 3 * T, torch.bfloat16, seed=141, device=DEV)
+    toks = [(t.permute(1, 2, 0, 3).contiguous()) for t in (x.q, x.k, x.v)]   # [B,H,3T,d]
+    q, k, v = (torch.empty((B, H, T, d), dtype=torch.bfloat16, device=DEV) for _ in range(3))
+    ncommit = torch.empty(B, dtype=torch.int32, device=DEV)
+    state = x.state.clone()
+    out = torch.empty_like(q)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        binding.decode_multi(q, k, v, x.slopes, state.clone(), n_commit=ncommit.zero_(),
+                             out=torch.empty_like(out))
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        binding.decode_multi(q, k, v, x.slopes, state, n_commit=ncommit, out=out)
+    state.copy_(x.state)
+    ref_state = x.state.clone()
+    for r, counts in enumerate(([4, 1, 2], [0, 3, 4], [2, 2, 1])):
+        for dst, src in zip((q, k, v), toks):
+            dst.copy_(src[:, :, r * T:(r + 1) * T])
+        ncommit.copy_(torch.tensor(counts, dtype=torch.int32))
+        g.replay()
+        ref = binding.decode_multi(q.clone(), k.clone(), v.clone(), x.slopes, ref_state,
+                                   n_commit=ncommit.clone())
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), r
+        assert torch.equal(state, ref_state), r
+
+
+def test_prefill_chunks_replayed_from_a_graph():
+    # chunked prefill: one captured 192-token chunk replayed over a longer
+    # sequence, the state carried from chunk to chunk inside the static buffer
+    B, H, C, d, nchunk = 1, 4, 192, 128, 4
+    log(f"graph: prefill chunks of {C} tokens B{B} H{H} d{d}, {nchunk} replays")
+    x = inputs.make_prefill(B, H, C * nchunk, d, torch.bfloat16, seed=142, init_state=True,
+                            device=DEV)
+    q, k, v = (torch.empty((B, H, C, d), dtype=torch.bfloat16, device=DEV) for _ in range(3))
+    state = x.state.clone()
+    out = torch.empty_like(q)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        binding.prefill(q, k, v, x.slopes, state.clone(), out=torch.empty_like(out))
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        binding.prefill(q, k, v, x.slopes, state, out=out)
+    state.copy_(x.state)
+    ref_state = x.state.clone()
+    for c in range(nchunk):
+        sl = slice(c * C, (c + 1) * C)
+        q.copy_(x.q[:, :, sl]); k.copy_(x.k[:, :, sl]); v.copy_(x.v[:, :, sl])
+        g.replay()
+        ref = binding.prefill(x.q[:, :, sl].contiguous(), x.k[:, :, sl].contiguous(),
+                              x.v[:, :, sl].contiguous(), x.slopes, ref_state)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), c
+        assert torch.equal(state, ref_state), c

@@ -65,13 +65,25 @@ def test_prefill_32k_with_initial_state():
     check_prefill(inp, BF16_TOL, what="prefill_32k_state")
 
 
-def test_prefill_256k_sampled_heads():
-    # the full 256K launch (all 64 heads, as timed by the benchmark); the
-    # oracle recomputes 4 heads, always including the fastest (h = 0) and the
-    # slowest (h = 63) decay
-    log("prefill_256k: B1 H64 N262144 d128 bf16, oracle on heads 0, 21, 42, 63")
+def test_prefill_256k_all_heads():
+    # the full 256K launch as timed by the benchmark, every one of the 64 heads
+    # against the oracle (16 heads at a time to bound host memory)
+    log("prefill_256k: B1 H64 N262144 d128 bf16, oracle on all 64 heads in groups of 16")
     inp = inputs.make_workload("prefill_256k", device=DEV)
-    check_prefill(inp, BF16_TOL, heads=[0, 21, 42, 63], what="prefill_256k")
+    st = inp.state.clone()
+    out = binding.prefill(inp.q, inp.k, inp.v, inp.slopes, st)
+    torch.cuda.synchronize()
+    worst_o = worst_s = 0.0
+    for h0 in range(0, 64, 16):
+        heads = list(range(h0, h0 + 16))
+        o_ref, s_ref = oracle_prefill(inp.q, inp.k, inp.v, inp.slopes, inp.state, heads=heads)
+        idx = torch.tensor(heads, device=DEV)
+        eo = rel_l2(out.index_select(1, idx), o_ref)
+        es = rel_l2(st.index_select(1, idx), s_ref)
+        log(f"  heads {h0}..{h0 + 15}: out rel-L2 {eo:.3e}  state rel-L2 {es:.3e}")
+        worst_o, worst_s = max(worst_o, eo), max(worst_s, es)
+        del o_ref, s_ref
+    assert worst_o <= BF16_TOL and worst_s <= BF16_TOL
 
 
 def test_decode_b256_64_steps():

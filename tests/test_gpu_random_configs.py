@@ -1,0 +1,124 @@
+"""Seeded random small configurations against the fp64 oracle (GPU): dense,
+packed and strided prefill, decode and multi-token decode, with random batch
+sizes, head counts, lengths (ragged, empty and one-token sequences included),
+head dimensions, initial states and decay ranges (the pages' slopes, slow
+decays near 1, a head with lambda = 0).  Bars as for the named workloads:
+2e-2 bf16, 1e-3 fp32 (max over slices of the relative L2 error)."""
+import random
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_layers_amd import binding, inputs
+from tests.gpu_util import BF16_TOL, F32_TOL, log, np64, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    binding.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def draw_slopes(rng, H):
+    kind = rng.choice(["pages", "slow", "mixed"])
+    if kind == "pages":
+        return inputs.slopes(H, DEV)
+    if kind == "slow":
+        return torch.tensor([rng.uniform(1e-4, 1e-2) for _ in range(H)], device=DEV)
+    s = [rng.uniform(1e-3, 2.0) for _ in range(H)]
+    s[rng.randrange(H)] = float("inf")                               # lambda = 0
+    return torch.tensor(s, dtype=torch.float32, device=DEV)
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_dense_and_strided_prefill(case):
+    rng = random.Random(1000 + case)
+    B, H = rng.randint(1, 3), rng.randint(1, 6)
+    N = rng.choice([1, 2, 31, 64, 65, 127, 200, rng.randint(1, 700)])
+    d = rng.choice([64, 128])
+    dtype = torch.bfloat16 if case % 4 else torch.float32
+    init = rng.random() < 0.6
+    log(f"case {case}: B{B} H{H} N{N} d{d} {dtype} init {init}")
+    x = inputs.make_prefill(B, H, N, d, dtype, seed=2000 + case, init_state=init, device=DEV)
+    x.slopes = draw_slopes(rng, H)
+    tol = BF16_TOL if dtype == torch.bfloat16 else F32_TOL
+    o_ref, s_ref = oracle.prefill(np64(x.q), np64(x.k), np64(x.v), np64(x.slopes), np64(x.state))
+    st = x.state.clone()
+    out = binding.prefill(x.q, x.k, x.v, x.slopes, st)
+    torch.cuda.synchronize()
+    assert rel_l2(out, o_ref) <= tol and rel_l2(st, s_ref) <= tol
+    if dtype == torch.bfloat16:
+        # the same values through a token-major buffer with a random row padding
+        pad = 8 * rng.randint(0, 4)
+        buf = torch.zeros((B, N, 3 * H * d + pad), dtype=dtype, device=DEV)
+        views = [buf[..., i * H * d:(i + 1) * H * d].unflatten(-1, (H, d)).transpose(1, 2)
+                 for i in range(3)]
+        for dst, src in zip(views, (x.q, x.k, x.v)):
+            dst.copy_(src)
+        st2 = x.state.clone()
+        out2 = binding.prefill(*views, x.slopes, st2)
+        torch.cuda.synchronize()
+        assert torch.equal(out2, out) and torch.equal(st2, st)
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_random_packed_prefill(case):
+    rng = random.Random(3000 + case)
+    H, d = rng.randint(1, 5), rng.choice([64, 128])
+    lens = [rng.choice([0, 1, rng.randint(1, 64), rng.randint(65, 400)])
+            for _ in range(rng.randint(1, 7))]
+    if sum(lens) == 0:
+        lens[0] = 5
+    log(f"packed case {case}: H{H} d{d} lens {lens}")
+    x = inputs.make_varlen(H, lens, d, torch.bfloat16, seed=4000 + case, init_state=True,
+                           device=DEV)
+    x.slopes = draw_slopes(rng, H)
+    st = x.states.clone()
+    out = binding.prefill_varlen(x.q, x.k, x.v, x.slopes, x.cu_seqlens, st)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.prefill_varlen(np64(x.q), np64(x.k), np64(x.v), np64(x.slopes),
+                                         x.cu_seqlens.cpu().numpy(), np64(x.states))
+    cu = x.cu_seqlens.cpu().numpy()
+    for i in range(len(lens)):
+        a, b = int(cu[i]), int(cu[i + 1])
+        if b > a:
+            assert oracle.rel_l2(np64(out)[:, a:b], o_ref[:, a:b]) <= BF16_TOL, i
+        assert oracle.rel_l2(np64(st)[i], s_ref[i]) <= BF16_TOL, i
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_random_decode_and_multi_token_decode(case):
+    rng = random.Random(5000 + case)
+    B, H, d = rng.randint(1, 40), rng.randint(1, 8), rng.choice([64, 128])
+    T = rng.randint(1, 8)
+    dtype = torch.bfloat16 if case % 3 else torch.float32
+    tol = BF16_TOL if dtype == torch.bfloat16 else F32_TOL
+    log(f"decode case {case}: B{B} H{H} d{d} T{T} {dtype}")
+    x = inputs.make_decode(B, H, d, T, dtype, seed=6000 + case, device=DEV)
+    x.slopes = draw_slopes(rng, H)
+    # one step
+    st = x.state.clone()
+    o = binding.decode_step(x.q[0], x.k[0], x.v[0], x.slopes, st)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.decode_step(np64(x.q[0]), np64(x.k[0]), np64(x.v[0]), np64(x.slopes),
+                                      np64(x.state))
+    assert rel_l2(o, o_ref) <= tol and rel_l2(st, s_ref) <= tol
+    # T tokens with random commit counts
+    q, k, v = (t.permute(1, 2, 0, 3).contiguous() for t in (x.q, x.k, x.v))
+    n = [rng.randint(0, T) for _ in range(B)]
+    st = x.state.clone()
+    om = binding.decode_multi(q, k, v, x.slopes, st,
+                              n_commit=torch.tensor(n, dtype=torch.int32, device=DEV))
+    torch.cuda.synchronize()
+    om_ref, sm_ref = oracle.decode_multi(np64(q), np64(k), np64(v), np64(x.slopes),
+                                         np64(x.state), n)
+    assert rel_l2(om, om_ref) <= tol and rel_l2(st, sm_ref) <= tol

@@ -106,33 +106,48 @@ def time_launches(stream, fn, reps):
 
 
 def measure_varlen(dev, stream, reps, dense_tflops):
+    """Packed prefill: the 256K packed workload (74 sequences, log-uniform
+    lengths) and, beside it, 512 sequences of 512 tokens (short prompts)."""
     import torch
     from long_context_layers_amd import binding, inputs
-    with torch.cuda.stream(stream):
-        inp = inputs.make_workload("varlen_256k", device=dev)
-        st = inp.states.clone()
-        out = torch.empty_like(inp.q)
-    stream.synchronize()
-    H, T, d = inp.q.shape
-    nseq = len(inp.lens)
 
-    def run():
-        binding.prefill_varlen(inp.q, inp.k, inp.v, inp.slopes, inp.cu_seqlens, st, out=out)
+    def one(make, what):
+        with torch.cuda.stream(stream):
+            inp = make()
+            st = inp.states.clone()
+            out = torch.empty_like(inp.q)
+        stream.synchronize()
+        H, T, d = inp.q.shape
+        nseq = len(inp.lens)
 
-    with torch.cuda.stream(stream):
-        ms = time_launches(stream, run, reps)
-    fl = H * T * (4 * d * d + 2 * (C_COUNT + 1) * d)
-    by = H * T * d * 2 * 4 + nseq * H * d * d * 4 * 2
-    tflops = fl / (ms * 1e-3) / 1e12
-    gbs = by / (ms * 1e-3) / 1e9
-    lo, hi = min(inp.lens), max(inp.lens)
-    del inp, st, out
-    return {"workload": f"packed prefill H{H} T{T} d{d} bf16: {nseq} sequences of "
-                        f"{lo}..{hi} tokens (seeded log-uniform), per-sequence fp32 states",
-            "nseq": nseq, "ms": round(ms, 4), "tflops": round(tflops, 3),
-            "gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
-            "algorithmic_bytes_per_launch": by, "vs_dense_256k_tflops": round(tflops / dense_tflops, 4),
-            "kernel": "prefill_bf16_kernel<128, false> (packed sequence map)"}
+        def run():
+            binding.prefill_varlen(inp.q, inp.k, inp.v, inp.slopes, inp.cu_seqlens, st, out=out)
+
+        with torch.cuda.stream(stream):
+            ms = time_launches(stream, run, reps)
+        fl = H * T * (4 * d * d + 2 * (C_COUNT + 1) * d)
+        by = H * T * d * 2 * 4 + nseq * H * d * d * 4 * 2
+        tflops = fl / (ms * 1e-3) / 1e12
+        gbs = by / (ms * 1e-3) / 1e9
+        lo, hi = min(inp.lens), max(inp.lens)
+        walks = binding.prefill_varlen_walks(nseq, H, T, d, dev)
+        del inp, st, out
+        return {"workload": f"packed prefill H{H} T{T} d{d} bf16: {nseq} sequences of "
+                            f"{lo}..{hi} tokens ({what}), per-sequence fp32 states",
+                "nseq": nseq, "ms": round(ms, 4), "tflops": round(tflops, 3),
+                "gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
+                "algorithmic_bytes_per_launch": by,
+                "vs_dense_256k_tflops": round(tflops / dense_tflops, 4),
+                "kernel": ("prefill_bf16_kernel<128, false, true>: one workgroup per head and "
+                           "32 columns walks every sequence" if walks else
+                           "prefill_bf16_kernel<128, false, false>: one workgroup per sequence, "
+                           "head and 32 columns")}
+
+    res = one(lambda: inputs.make_workload("varlen_256k", device=dev), "seeded log-uniform")
+    res["short_sequences"] = one(
+        lambda: inputs.make_varlen(64, [512] * 512, 128, torch.bfloat16, seed=1006,
+                                   init_state=True, device=dev), "short prompts")
+    return res
 
 
 def measure_layer_ops(dev, stream, reps, pre_ms):
@@ -202,7 +217,7 @@ def measure_layer_ops(dev, stream, reps, pre_ms):
                 "prefill_strided": {"ms": round(ms_attn, 4),
                                     "tflops": round(fl / (ms_attn * 1e-3) / 1e12, 3),
                                     "vs_contiguous": round(pre_ms / ms_attn, 4),
-                                    "kernel": "prefill_bf16_kernel<128, true> (token stride "
+                                    "kernel": "prefill_bf16_kernel<128, true, false> (token stride "
                                               "4*H*d in, [B,H,N,d] out)"},
                 "layer_ms": round(ms_pro_ip + ms_attn + ms_epi, 4),
                 "token_major_out": {
@@ -641,7 +656,7 @@ def main():
             "frac": round(gbs / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(),
             "algorithmic_bytes_per_launch": by,
-            "kernel": "prefill_bf16_kernel<128, false>",
+            "kernel": "prefill_bf16_kernel<128, false, false>",
         },
         "context": {
             "pages_kernel_numbers": "none: the Ling and Ring 2.6 Technical Report gives no "

@@ -117,6 +117,25 @@ int la_prefill_varlen_f32(const float *q, const float *k, const float *v, const 
                           int64_t H, int64_t T, int64_t d, void *stream);
 
 /*
+ * Work split of a packed bf16 prefill (la_prefill_varlen, la_prefill_varlen_strided)
+ * with these sizes on the calling thread's current device, written to *walks:
+ *   1  one workgroup per (head, 32 output columns) walks the sequences in
+ *      order (its pipeline runs across sequence boundaries, and every
+ *      workgroup does the same work: all tokens of its head); batches of more
+ *      than 1024 sequences are walked 1024 at a time, one kernel launch each;
+ *   0  one workgroup per (sequence, head, 32 output columns).
+ * The walk is used when nseq >= 2, T < 2^31, the sequences are short on
+ * average (T / nseq < 8192: longer ones gain more from the hardware balancing
+ * a grid of per-sequence workgroups over the compute units) and its H*d/32
+ * workgroups fill whole waves of the device's compute units.  Both give the
+ * same results, bitwise.  No GPU work is enqueued.  Returns LA_OK; LA_ERR_INVALID_ARG for a
+ * null walks, nseq or H below 1 or T below 0; LA_ERR_UNSUPPORTED for d other
+ * than 64 or 128.  Source: as la_prefill_varlen (many short sequences packed
+ * into one launch, §4.1.2).
+ */
+int la_prefill_varlen_plan(int64_t nseq, int64_t H, int64_t T, int64_t d, int *walks);
+
+/*
  * Strided prefill: la_prefill / la_prefill_varlen reading q, k, v and writing
  * out through element strides, so the kernel can read straight out of a packed
  * projection buffer ([B,N,(q|k|v|...)*H*d], token-major) and write its output
@@ -331,7 +350,7 @@ const char *la_status_string(int status);
 /* ABI version of this header (incremented on incompatible changes). */
 int la_abi_version(void);
 
-#define LA_ABI_VERSION 2
+#define LA_ABI_VERSION 3
 
 #ifdef __cplusplus
 }

@@ -45,9 +45,10 @@ SIGNATURES = {
     "la_cp_fold": ([_P, _P, _I64, _I64, _P, _P, _P, _I64, _I64, _I64, _P], _INT),
     "la_cp_correct": ([_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], _INT),
     "la_status_string": ([_INT], ctypes.c_char_p),
+    "la_prefill_varlen_plan": ([_I64, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_int)], _INT),
     "la_abi_version": ([], _INT),
 }
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 _lock = threading.Lock()
 _lib = None
@@ -232,6 +233,20 @@ def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: to
                 nseq, out.data_ptr(), states.data_ptr(), H, T, d, _stream(dev))
     _check(rc, "la_prefill_varlen" if dt == torch.bfloat16 else "la_prefill_varlen_f32")
     return out
+
+
+def prefill_varlen_walks(nseq: int, H: int, T: int, d: int, device=None) -> bool:
+    """Whether a packed bf16 prefill of nseq sequences, H heads and T tokens
+    walks the sequences in one workgroup per (head, 32 output columns) on
+    ``device`` (``la_prefill_varlen_plan``); otherwise each (sequence, head,
+    column slice) has a workgroup of its own.  Both give the same results,
+    bitwise."""
+    walks = ctypes.c_int(0)
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    with torch.cuda.device(dev):
+        _check(load_library().la_prefill_varlen_plan(nseq, H, T, d, ctypes.byref(walks)),
+               "la_prefill_varlen_plan")
+    return bool(walks.value)
 
 
 def decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: torch.Tensor,

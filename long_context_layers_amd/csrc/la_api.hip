@@ -297,6 +297,14 @@ int la_prefill_varlen(const void *q, const void *k, const void *v, const float *
         map, (int)d, static_cast<hipStream_t>(stream)));
 }
 
+int la_prefill_varlen_plan(int64_t nseq, int64_t H, int64_t T, int64_t d, int *walks)
+{
+    if (!walks || nseq < 1 || H < 1 || T < 0) return LA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
+    *walks = la::prefill_bf16_walks(nseq, H, T, (int)d, true) ? 1 : 0;
+    return LA_OK;
+}
+
 int la_prefill_f32(const float *q, const float *k, const float *v, const float *slopes,
                    float *out, float *state, int64_t B, int64_t H, int64_t N, int64_t d,
                    void *stream)

@@ -43,6 +43,14 @@ __device__ __forceinline__ void seq_slice(const SeqMap &m, int64_t seq, int64_t 
     *len = b - a;
 }
 
+// length of sequence seq (the same clamping as seq_slice)
+__device__ __forceinline__ int64_t seq_len(const SeqMap &m, int64_t seq)
+{
+    if (!m.cu) return m.N;
+    const int64_t a = min(max(m.cu[seq], (int64_t)0), m.T);
+    return min(max(m.cu[seq + 1], a), m.T) - a;
+}
+
 // ---- launchers (return the launch status; arguments already validated) ----
 // Prefill over `seqs` sequences (B for dense launches, nseq for packed ones).
 hipError_t launch_prefill_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
@@ -96,6 +104,9 @@ int64_t cp_correct_grid(int64_t B, int64_t H, int64_t L);
 
 // number of workgroups one prefill launch over `seqs` sequences uses
 int64_t prefill_bf16_grid(int64_t seqs, int64_t H, int d);
+// whether a packed launch over seqs sequences (T tokens) walks them in one
+// workgroup per (head, column slice) on the current device
+bool prefill_bf16_walks(int64_t seqs, int64_t H, int64_t T, int d, bool packed);
 int64_t prefill_f32_grid(int64_t seqs, int64_t H, int d);
 
 // ---- device helpers ----

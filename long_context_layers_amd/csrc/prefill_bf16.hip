@@ -20,7 +20,12 @@
 // over 4 workgroups of 32 columns (the columns of S evolve independently).
 // Each workgroup recomputes the block's scores (they need all of d); the
 // four workgroups of a head are placed on one XCD so Q and K come from HBM
-// once and from that XCD's L2 for the other three.
+// once and from that XCD's L2 for the other three.  A packed batch of short
+// sequences runs one workgroup per (head, column slice) that walks every
+// sequence in order (WALK): the pipeline then runs across sequence
+// boundaries, the scan hands each final state out and the next initial state
+// in (loaded a whole sequence ahead), instead of a workgroup per sequence
+// paying its own pipeline fill and drain.
 //
 // Roles inside a workgroup (8 waves).  Waves 4..7 are producers: they only
 // load Q, K and the workgroup's 64 x 32 slice of V with 16-byte buffer loads,
@@ -58,6 +63,7 @@
 // r0 .. r0 + 3: a k-contiguous MFMA operand for a contraction over rows.
 #include "la_internal.h"
 
+#include <atomic>
 #include <type_traits>
 
 namespace la {
@@ -119,12 +125,133 @@ struct alignas(16) Smem {
     float OP[2][64][20];             // W3 -> W2 partial outputs (one lane's 16 values)
 };
 
+
+// ---- the blocks a workgroup visits, in order --------------------------------
+
+// One block's place: its sequence, its first token within that sequence, the
+// sequence's length and the element offsets of the (sequence, head) slice in
+// the inputs and the output (j: the sequence's entry in a walk's table).  A
+// block never spans two sequences.  Blocks with no tokens (past the end of
+// the work) read zeros and their stores are dropped.
+struct Pos {
+    int64_t seq, t0, n, in0, out0;
+    int j;
+};
+
+// The non-empty sequences of a walking launch, in order, with their clamped
+// offsets (a walking launch has at most WALK_SEQS sequences and fewer than
+// 2^31 tokens).  Built once per workgroup, so advancing a position is a
+// broadcast LDS read instead of dependent loads of the offsets from memory.
+constexpr int WALK_SEQS = 1024;
+
+struct WalkTable {
+    int seq[WALK_SEQS], start[WALK_SEQS], len[WALK_SEQS];
+    int count;                  // entries
+    int nblk;                   // blocks with tokens
+};
+
+// one wave fills the table (a barrier must follow before anyone reads it)
+__device__ void build_table(WalkTable &tb, const SeqMap &m, int64_t nseq, int lane)
+{
+    int count = 0, nblk = 0;
+    for (int64_t base = 0; base < nseq; base += 64) {
+        const int64_t s = base + lane;
+        int a = 0, n = 0;
+        if (s < nseq) {
+            const int64_t a64 = min(max(m.cu[s], (int64_t)0), m.T);
+            a = (int)a64;
+            n = (int)(min(max(m.cu[s + 1], a64), m.T) - a64);
+        }
+        const uint64_t mask = __ballot(n > 0);
+        const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+        if (n > 0) {
+            tb.seq[count + before] = (int)s;
+            tb.start[count + before] = a;
+            tb.len[count + before] = n;
+        }
+        count += __popcll(mask);
+        int b = (n + PC - 1) / PC;
+        for (int off = 32; off > 0; off >>= 1) b += __shfl_xor(b, off);
+        nblk += b;
+    }
+    if (lane == 0) {
+        tb.count = count;
+        tb.nblk = nblk;
+    }
+}
+
+// WALK = false: the blocks of one (sequence, head) slice, then blocks past its
+// end.  WALK = true (a packed launch with one workgroup per head and column
+// slice): the blocks of every non-empty sequence, sequence after sequence, so
+// the pipeline below runs across sequence boundaries; then blocks with no
+// tokens.  Every value here is uniform across the workgroup.
+template <bool WALK>
+struct Walk {
+    SeqMap map;
+    int64_t nseq, h;
+    const WalkTable *tb;        // WALK: the table, in LDS
+
+    __device__ static int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+    // WALK: the first block of table entry j (no tokens past the table's end)
+    __device__ Pos entry(int j) const {
+        Pos p = {nseq, 0, 0, 0, 0, j};
+        if (j < uni(tb->count)) {
+            const int64_t a = uni(tb->start[j]);
+            p.seq = uni(tb->seq[j]);
+            p.n = uni(tb->len[j]);
+            p.in0 = h * map.in.sh + a * map.in.st;
+            p.out0 = h * map.out.sh + a * map.out.st;
+        }
+        return p;
+    }
+    __device__ Pos first(int64_t seq) const {
+        if constexpr (WALK) {
+            return entry(0);
+        } else {
+            Pos p = {seq, 0, 0, 0, 0, 0};
+            seq_slice(map, seq, h, &p.in0, &p.out0, &p.n);
+            return p;
+        }
+    }
+    __device__ void next(Pos &p) const {
+        p.t0 += PC;
+        if constexpr (WALK) {
+            if (p.t0 >= p.n) p = entry(p.j + 1);
+        }
+    }
+    // the block is the last of its sequence
+    __device__ static bool last(const Pos &p) { return p.t0 < p.n && p.t0 + PC >= p.n; }
+    // WALK: the sequence of table entry j, or -1 past the table's end
+    __device__ int64_t seq_at(int j) const { return j < uni(tb->count) ? uni(tb->seq[j]) : -1; }
+    // blocks with tokens
+    __device__ int64_t blocks(const Pos &p0) const {
+        if constexpr (WALK) return uni(tb->nblk);
+        else return (p0.n + PC - 1) / PC;
+    }
+};
+
+template <int D>
+struct Ctx {                          // per-thread constants of one workgroup
+    const uint16_t *q, *k, *v;        // the launch's inputs (slices at Pos::in0)
+    uint16_t *o;                      // its output (slices at Pos::out0)
+    float *state;                     // its states, [sequence][H][D][D]
+    int64_t H, h, nblk;               // nblk: blocks processed (a multiple of NSET)
+    int ts, ots;                      // token strides (elements) of q/k/v and of out (<= 2^24)
+    float s;
+    int j0;
+
+    // this workgroup's columns of the state of sequence seq: element (i, j) at i * D + j
+    __device__ float *state_of(int64_t seq) const { return state + (seq * H + h) * D * D + j0; }
+};
+
 // ---- producer waves: global -> registers -> LDS ----------------------------
 
 template <int D>
 struct Regs {                        // one block's share of a producer thread
     static constexpr int NQ = PC * D / 8 / PT;   // 16-byte chunks of Q (and of K)
     uint4 q[NQ], k[NQ], v;
+    int c;                           // tokens in the block
 };
 
 template <int D>
@@ -162,19 +289,19 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 }
 
 template <int D>
-__device__ __forceinline__ void load_block(Regs<D> &r, const uint16_t *qh, const uint16_t *kh,
-                                           const uint16_t *vh, int64_t t0, int64_t N,
-                                           int64_t ts, const Addr<D> &ad)
+__device__ __forceinline__ void load_block(Regs<D> &r, const Ctx<D> &cx, const Pos &p,
+                                           const Addr<D> &ad)
 {
-    const __amdgpu_buffer_rsrc_t rq = block_rsrc<D>(qh, t0, N, ts);
-    const __amdgpu_buffer_rsrc_t rk = block_rsrc<D>(kh, t0, N, ts);
-    const __amdgpu_buffer_rsrc_t rv = block_rsrc<D>(vh, t0, N, ts);
+    const __amdgpu_buffer_rsrc_t rq = block_rsrc<D>(cx.q + p.in0, p.t0, p.n, cx.ts);
+    const __amdgpu_buffer_rsrc_t rk = block_rsrc<D>(cx.k + p.in0, p.t0, p.n, cx.ts);
+    const __amdgpu_buffer_rsrc_t rv = block_rsrc<D>(cx.v + p.in0, p.t0, p.n, cx.ts);
 #pragma unroll
     for (int u = 0; u < Regs<D>::NQ; ++u) {
         r.q[u] = bload16(rq, ad.qk[u]);
         r.k[u] = bload16(rk, ad.qk[u]);
     }
     r.v = bload16(rv, ad.v);
+    r.c = block_len(p.t0, p.n);
 }
 
 __device__ __forceinline__ uint32_t scale_pair(uint32_t x, float w) {
@@ -202,42 +329,34 @@ __device__ __forceinline__ void store_block(const Regs<D> &r, Smem<D> &sm, int p
     *reinterpret_cast<uint4 *>(&sm.VW[BUF][vrow][vc]) = w;
 }
 
-template <int D>
-struct Ctx {                          // per-thread constants of one workgroup
-    const uint16_t *qh, *kh, *vh;     // this (b, h) slice
-    const uint16_t *oh;
-    int64_t N, nblk;                  // nblk: blocks processed (a multiple of NSET)
-    int ts, ots;                      // token strides (elements) of q/k/v and of out (<= 2^24)
-    float s;
-    int j0;
-};
-
 template <int D, int BUF>
 __device__ __forceinline__ void produce_store(const Ctx<D> &cx, Smem<D> &sm, const Regs<D> &r,
-                                              int64_t blk, int p, float wfull)
+                                              int p, float wfull)
 {
-    const int c = block_len(blk * PC, cx.N);
     const int b = p / 4;
-    const float wv = c == PC ? wfull : (b < c ? decay_pow(cx.s, c - 1 - b) : 0.0f);
+    const float wv = r.c == PC ? wfull : (b < r.c ? decay_pow(cx.s, r.c - 1 - b) : 0.0f);
     store_block<D, BUF>(r, sm, p, wv);
 }
 
 // One producer step per block blk: after the block's barrier, stage block
 // blk+1 (register set SET) into the other LDS buffer, then reload SET with
-// block blk+1+NSET.  Loads past the end return zeros without touching
-// memory, so nothing here is conditional (exact vmcnt waits).
-template <int D, int SET>
-__device__ __forceinline__ void produce_step(const Ctx<D> &cx, Smem<D> &sm, Regs<D> (&rs)[NSET],
-                                             const Addr<D> &ad, int64_t blk, int p, float wfull)
+// block blk+1+NSET (at ld, which then moves on).  Loads past the end return
+// zeros without touching memory, so nothing here is conditional (exact vmcnt
+// waits).
+template <int D, int SET, bool WALK>
+__device__ __forceinline__ void produce_step(const Ctx<D> &cx, const Walk<WALK> &wk, Smem<D> &sm,
+                                             Regs<D> (&rs)[NSET], const Addr<D> &ad, Pos &ld, int p,
+                                             float wfull)
 {
     __syncthreads();                                   // barrier of block blk
-    if (SET % 2 == 1) produce_store<D, 1>(cx, sm, rs[SET], blk + 1, p, wfull);
-    else              produce_store<D, 0>(cx, sm, rs[SET], blk + 1, p, wfull);
-    load_block<D>(rs[SET], cx.qh, cx.kh, cx.vh, (blk + 1 + NSET) * PC, cx.N, cx.ts, ad);
+    if (SET % 2 == 1) produce_store<D, 1>(cx, sm, rs[SET], p, wfull);
+    else              produce_store<D, 0>(cx, sm, rs[SET], p, wfull);
+    load_block<D>(rs[SET], cx, ld, ad);
+    wk.next(ld);
 }
 
-template <int D>
-__device__ void producer(const Ctx<D> &cx, Smem<D> &sm, int p)
+template <int D, bool WALK>
+__device__ void producer(const Ctx<D> &cx, const Walk<WALK> &wk, Pos ld, Smem<D> &sm, int p)
 {
     Addr<D> ad;
 #pragma unroll
@@ -250,16 +369,20 @@ __device__ void producer(const Ctx<D> &cx, Smem<D> &sm, int p)
 
     Regs<D> rs[NSET];                                           // set i holds block i (mod NSET)
 #pragma unroll
-    for (int i = 0; i < NSET; ++i) load_block<D>(rs[i], cx.qh, cx.kh, cx.vh, i * PC, cx.N, cx.ts, ad);
-    produce_store<D, 0>(cx, sm, rs[0], 0, p, wfull);
-    load_block<D>(rs[0], cx.qh, cx.kh, cx.vh, NSET * PC, cx.N, cx.ts, ad);
+    for (int i = 0; i < NSET; ++i) {
+        load_block<D>(rs[i], cx, ld, ad);
+        wk.next(ld);
+    }
+    produce_store<D, 0>(cx, sm, rs[0], p, wfull);
+    load_block<D>(rs[0], cx, ld, ad);
+    wk.next(ld);
 
     // block blk stages block blk+1 from set (blk+1) % NSET into buffer (blk+1) % 2
     for (int64_t blk = 0; blk < cx.nblk; blk += NSET) {
-        produce_step<D, 1>(cx, sm, rs, ad, blk + 0, p, wfull);
-        produce_step<D, 2>(cx, sm, rs, ad, blk + 1, p, wfull);
-        produce_step<D, 3>(cx, sm, rs, ad, blk + 2, p, wfull);
-        produce_step<D, 0>(cx, sm, rs, ad, blk + 3, p, wfull);
+        produce_step<D, 1>(cx, wk, sm, rs, ad, ld, p, wfull);
+        produce_step<D, 2>(cx, wk, sm, rs, ad, ld, p, wfull);
+        produce_step<D, 3>(cx, wk, sm, rs, ad, ld, p, wfull);
+        produce_step<D, 0>(cx, wk, sm, rs, ad, ld, p, wfull);
     }
     __syncthreads();                                   // final barrier (matches the consumers)
 }
@@ -269,6 +392,9 @@ __device__ void producer(const Ctx<D> &cx, Smem<D> &sm, int p)
 // Four consumer waves, one per SIMD (each shares its SIMD with one producer):
 //   W0  the state scan: S = lambda^c S + K^T (lambda^(c-1-b) V) on all D
 //       state rows, and the bf16 copy ST of the new state (double-buffered);
+//       at the last block of a sequence it stores the final state and, when
+//       sequences follow (WALK), takes up the next one's initial state, which
+//       it loaded into spare registers a whole sequence earlier;
 //   W1  tokens 0..31: inter term S^T Q^T + scores P^T(0,0) + V^T P^T, stored;
 //   W2  tokens 32..63: inter term + scores P^T(1,1) + their V^T P^T part;
 //   W3  tokens 32..63: scores P^T(0,1) + their V^T P^T part, handed to W2
@@ -284,6 +410,48 @@ struct Lane {                               // lane coordinates for 32x32 MFMAs
         : l32(lane % 32), h(lane / 32), l16(lane % 16), q2((lane / 16) % 2),
           trow((lane % 16) >> 2), tcol(4 * ((lane % 16) & 3)) {}
 };
+
+// A state slice in the scan's registers: tile it, register r of lane (l32, h)
+// holds row 32 it + 8 (r / 4) + 4 h + r % 4, column l32.  Buffer accesses: the
+// lane's part of the offset in one register, each register's part a constant
+// (used by the walk, whose scan also holds a second slice; a single-slice scan
+// keeps plain pointer accesses, which measured slightly faster there).
+template <int D>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t state_rsrc(const float *st) {
+    return __builtin_amdgcn_make_buffer_rsrc((void *)st, (short)0, ((D - 1) * D + PJ) * 4,
+                                             RSRC_WORD3);
+}
+
+template <int D>
+__device__ __forceinline__ int state_reg_offset(int it, int r) {   // bytes
+    return (32 * it + 8 * (r / 4) + r % 4) * D * 4;
+}
+
+template <int D>
+__device__ __forceinline__ void load_state(f32x16 (&x)[D / 32], const float *st, const Lane<D> &ln)
+{
+    const __amdgpu_buffer_rsrc_t rs = state_rsrc<D>(st);
+    const int lo = (4 * ln.h * D + ln.l32) * 4;
+#pragma unroll
+    for (int it = 0; it < D / 32; ++it)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            x[it][r] = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(rs, lo, state_reg_offset<D>(it, r), 0));
+}
+
+template <int D>
+__device__ __forceinline__ void store_state(float *st, const f32x16 (&x)[D / 32], const Lane<D> &ln)
+{
+    const __amdgpu_buffer_rsrc_t rs = state_rsrc<D>(st);
+    const int lo = (4 * ln.h * D + ln.l32) * 4;
+#pragma unroll
+    for (int it = 0; it < D / 32; ++it)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x[it][r]), rs, lo,
+                                                  state_reg_offset<D>(it, r), 0);
+}
 
 // decay of score accumulator register r for a tile whose a-half is ah and
 // b-half bh: lambda^(a-b), 0 above the diagonal
@@ -335,7 +503,7 @@ __device__ __forceinline__ void score_pv(const Smem<D> &sm, int buf, int bh,
     }
 }
 
-// store a 32x32 O^T tile (tokens 32ah.., columns j0..j0+31) of block t0.
+// store a 32x32 O^T tile (tokens 32ah.., columns j0..j0+31) of the block at p.
 // Accumulator register group q4 holds columns 8q4 + 4h + 0..3 of token a; a
 // lane-half swap (lanes l <-> l+32) of groups (0,1) and (2,3) gives lane h
 // columns 8h..8h+7 and 16+8h..16+8h+7, so each row is written as 32-byte runs
@@ -346,10 +514,10 @@ __device__ __forceinline__ int out_offset(const Ctx<D> &cx, int ah, const Lane<D
 }
 
 template <int D>
-__device__ __forceinline__ void store_out(const Ctx<D> &cx, int64_t t0, int ooff,
+__device__ __forceinline__ void store_out(const Ctx<D> &cx, const Pos &p, int ooff,
                                           const f32x16 &acc)
 {
-    const __amdgpu_buffer_rsrc_t ro = block_rsrc<D>(cx.oh, t0, cx.N, cx.ots);   // rows past N dropped
+    const __amdgpu_buffer_rsrc_t ro = block_rsrc<D>(cx.o + p.out0, p.t0, p.n, cx.ots);   // rows past the end dropped
 #pragma unroll
     for (int pr = 0; pr < 2; ++pr) {
         const int g0 = 2 * pr, g1 = 2 * pr + 1;
@@ -379,30 +547,42 @@ __device__ __forceinline__ void write_st(Smem<D> &sm, int buf, int it, const Lan
     }
 }
 
-// W0: the state scan
-template <int D>
-__device__ void scan_wave(const Ctx<D> &cx, Smem<D> &sm, float *St, int lane)
+// W0: the state scan (pos: block 0)
+template <int D, bool WALK>
+__device__ void scan_wave(const Ctx<D> &cx, const Walk<WALK> &wk, Pos pos, Smem<D> &sm, int lane)
 {
     constexpr int NT = D / 32;                  // 32-row state tiles
     const Lane<D> ln(lane);
     const float full_decay = decay_pow(cx.s, PC);
-    const int clast = (int)(cx.N - (cx.N - 1) / PC * PC);          // tokens of the last real block
-    const float last_decay = decay_pow(cx.s, clast);
 
-    f32x16 sacc[NT];
+    f32x16 sacc[NT], nxt[NT];                   // nxt (WALK): the next sequence's initial state
+    if (pos.n > 0) {
+        if constexpr (WALK) load_state<D>(sacc, cx.state_of(pos.seq), ln);
+        else {
+            const float *St = cx.state_of(pos.seq);
 #pragma unroll
-    for (int it = 0; it < NT; ++it) {
+            for (int it = 0; it < NT; ++it)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            sacc[it][r] = St[(32 * it + 8 * (r / 4) + 4 * ln.h + r % 4) * D + cx.j0 + ln.l32];
-        write_st<D>(sm, 1, it, ln, sacc[it]);   // read by block 0
+                for (int r = 0; r < 16; ++r)
+                    sacc[it][r] = St[(32 * it + 8 * (r / 4) + 4 * ln.h + r % 4) * D + ln.l32];
+        }
+    } else {
+#pragma unroll
+        for (int it = 0; it < NT; ++it) sacc[it] = f32x16{};
     }
+    if constexpr (WALK) {
+        const int64_t s1 = wk.seq_at(pos.j + 1);
+        if (s1 >= 0) load_state<D>(nxt, cx.state_of(s1), ln);
+    }
+#pragma unroll
+    for (int it = 0; it < NT; ++it) write_st<D>(sm, 1, it, ln, sacc[it]);   // read by block 0
 
-    auto step = [&](int64_t blk, auto BUFC) {
+    auto step = [&](auto BUFC) {
         constexpr int BUF = decltype(BUFC)::value;
-        const int c = block_len(blk * PC, cx.N);
+        const int c = block_len(pos.t0, pos.n);
+        const bool last = Walk<WALK>::last(pos);
         __syncthreads();
-        const float sdec = c == PC ? full_decay : (c == 0 ? 1.0f : last_decay);
+        const float sdec = c == PC ? full_decay : (c == 0 ? 1.0f : decay_pow(cx.s, c));
         bf16x8 vwf[PC / 16];
 #pragma unroll
         for (int ks = 0; ks < PC / 16; ++ks) {
@@ -423,47 +603,72 @@ __device__ void scan_wave(const Ctx<D> &cx, Smem<D> &sm, float *St, int lane)
             }
             write_st<D>(sm, BUF, it, ln, sacc[it]);
         }
+        if constexpr (WALK) {
+            if (last) {                         // the sequence's final state out
+                store_state<D>(cx.state_of(pos.seq), sacc, ln);
+                if (wk.seq_at(pos.j + 1) >= 0) {
+                    // the next sequence's initial state in (and its bf16 copy
+                    // over the one just written for the next block); then the
+                    // one after it starts loading
+#pragma unroll
+                    for (int it = 0; it < NT; ++it) {
+                        sacc[it] = nxt[it];
+                        write_st<D>(sm, BUF, it, ln, sacc[it]);
+                    }
+                    const int64_t s2 = wk.seq_at(pos.j + 2);
+                    if (s2 >= 0) load_state<D>(nxt, cx.state_of(s2), ln);
+                }
+            }
+        }
+        wk.next(pos);
     };
     for (int64_t blk = 0; blk < cx.nblk; blk += 2) {
-        step(blk, std::integral_constant<int, 0>());
-        step(blk + 1, std::integral_constant<int, 1>());
+        step(std::integral_constant<int, 0>());
+        step(std::integral_constant<int, 1>());
     }
     __syncthreads();                            // final barrier (W2's last store)
-
+    // one sequence: its final state, after the loop (a store inside the step
+    // measured slower: it sits on the scan's sequential path every block)
+    if constexpr (!WALK) {
+        if (cx.nblk > 0) {
+            float *St = cx.state_of(pos.seq);
 #pragma unroll
-    for (int it = 0; it < NT; ++it)
+            for (int it = 0; it < NT; ++it)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-            St[(32 * it + 8 * (r / 4) + 4 * ln.h + r % 4) * D + cx.j0 + ln.l32] = sacc[it][r];
+                for (int r = 0; r < 16; ++r)
+                    St[(32 * it + 8 * (r / 4) + 4 * ln.h + r % 4) * D + ln.l32] = sacc[it][r];
+        }
+    }
 }
 
 // W1: tokens 0..31, complete
-template <int D>
-__device__ void out0_wave(const Ctx<D> &cx, Smem<D> &sm, int lane)
+template <int D, bool WALK>
+__device__ void out0_wave(const Ctx<D> &cx, const Walk<WALK> &wk, Pos pos, Smem<D> &sm, int lane)
 {
     const Lane<D> ln(lane);
     float dec[16];
     score_decay(dec, cx.s, 0, 0, ln.l32, ln.h);
     const float scale = decay_pow(cx.s, ln.l32 + 1);               // lambda^(a+1)
     const int ooff = out_offset(cx, 0, ln);
-    auto step = [&](int64_t blk, auto BUFC) {
+    auto step = [&](auto BUFC) {
         constexpr int BUF = decltype(BUFC)::value;
         __syncthreads();
         bf16x8 qf[D / 16];
         f32x16 acc = inter_term<D>(sm, BUF, BUF ^ 1, 0, ln, scale, qf);
         score_pv<D>(sm, BUF, 0, qf, dec, ln, acc);
-        store_out<D>(cx, blk * PC, ooff, acc);
+        store_out<D>(cx, pos, ooff, acc);
+        wk.next(pos);
     };
     for (int64_t blk = 0; blk < cx.nblk; blk += 2) {
-        step(blk, std::integral_constant<int, 0>());
-        step(blk + 1, std::integral_constant<int, 1>());
+        step(std::integral_constant<int, 0>());
+        step(std::integral_constant<int, 1>());
     }
     __syncthreads();
 }
 
 // W2: tokens 32..63, inter term + diagonal scores; adds W3's part one block later
-template <int D>
-__device__ void out1_wave(const Ctx<D> &cx, Smem<D> &sm, int lane)
+template <int D, bool WALK>
+__device__ void out1_wave(const Ctx<D> &cx, const Walk<WALK> &wk, Pos pos, Smem<D> &sm, int lane)
 {
     const Lane<D> ln(lane);
     float dec[16];
@@ -471,7 +676,8 @@ __device__ void out1_wave(const Ctx<D> &cx, Smem<D> &sm, int lane)
     const float scale = decay_pow(cx.s, 32 + ln.l32 + 1);
     const int ooff = out_offset(cx, 1, ln);
     f32x16 prev = {};
-    auto finish_prev = [&](int64_t pblk, int pbuf) {               // block pblk's tokens 32..63
+    Pos ppos = pos;                                                // block of prev
+    auto finish_prev = [&](int pbuf) {                             // that block's tokens 32..63
         const float4 *op = reinterpret_cast<const float4 *>(&sm.OP[pbuf][lane][0]);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -479,7 +685,7 @@ __device__ void out1_wave(const Ctx<D> &cx, Smem<D> &sm, int lane)
             prev[4 * u + 0] += x.x; prev[4 * u + 1] += x.y;
             prev[4 * u + 2] += x.z; prev[4 * u + 3] += x.w;
         }
-        store_out<D>(cx, pblk * PC, ooff, prev);
+        store_out<D>(cx, ppos, ooff, prev);
     };
     auto step = [&](int64_t blk, auto BUFC) {
         constexpr int BUF = decltype(BUFC)::value;
@@ -487,15 +693,17 @@ __device__ void out1_wave(const Ctx<D> &cx, Smem<D> &sm, int lane)
         bf16x8 qf[D / 16];
         f32x16 acc = inter_term<D>(sm, BUF, BUF ^ 1, 1, ln, scale, qf);
         score_pv<D>(sm, BUF, 1, qf, dec, ln, acc);
-        if (blk > 0) finish_prev(blk - 1, BUF ^ 1);
+        if (blk > 0) finish_prev(BUF ^ 1);
         prev = acc;
+        ppos = pos;
+        wk.next(pos);
     };
     for (int64_t blk = 0; blk < cx.nblk; blk += 2) {
         step(blk, std::integral_constant<int, 0>());
         step(blk + 1, std::integral_constant<int, 1>());
     }
     __syncthreads();                            // W3's part of the last block is visible
-    if (cx.nblk > 0) finish_prev(cx.nblk - 1, (int)((cx.nblk - 1) & 1));   // (empty sequence: none)
+    if (cx.nblk > 0) finish_prev((int)((cx.nblk - 1) & 1));   // (no blocks: none)
 }
 
 // W3: tokens 32..63, off-diagonal scores P^T(0,1) and their V^T P^T part
@@ -505,7 +713,7 @@ __device__ void out1x_wave(const Ctx<D> &cx, Smem<D> &sm, int lane)
     const Lane<D> ln(lane);
     float dec[16];
     score_decay(dec, cx.s, 1, 0, ln.l32, ln.h);
-    auto step = [&](int64_t blk, auto BUFC) {
+    auto step = [&](auto BUFC) {
         constexpr int BUF = decltype(BUFC)::value;
         __syncthreads();
         bf16x8 qf[D / 16];
@@ -519,8 +727,8 @@ __device__ void out1x_wave(const Ctx<D> &cx, Smem<D> &sm, int lane)
             op[u] = make_float4(acc[4 * u + 0], acc[4 * u + 1], acc[4 * u + 2], acc[4 * u + 3]);
     };
     for (int64_t blk = 0; blk < cx.nblk; blk += 2) {
-        step(blk, std::integral_constant<int, 0>());
-        step(blk + 1, std::integral_constant<int, 1>());
+        step(std::integral_constant<int, 0>());
+        step(std::integral_constant<int, 1>());
     }
     __syncthreads();
 }
@@ -528,11 +736,13 @@ __device__ void out1x_wave(const Ctx<D> &cx, Smem<D> &sm, int lane)
 // STRIDED = false: rows of q, k, v and out are D elements apart (a
 // compile-time token stride; head and sequence offsets still come from the
 // map), so the contiguous layouts pay nothing for stride support.
-template <int D, bool STRIDED>
+// WALK = false: one workgroup per (sequence, head, column slice); WALK = true:
+// one per (head, column slice), walking all nseq sequences of a packed map.
+template <int D, bool STRIDED, bool WALK>
 __global__ __launch_bounds__(NTHREADS) void prefill_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const float *__restrict__ slopes,
-    uint16_t *__restrict__ out, float *__restrict__ state, SeqMap map)
+    uint16_t *__restrict__ out, float *__restrict__ state, SeqMap map, int64_t nseq)
 {
     constexpr int NJ = D / PJ;            // workgroups per head
     __shared__ Smem<D> sm;
@@ -542,10 +752,11 @@ __global__ __launch_bounds__(NTHREADS) void prefill_bf16_kernel(
 
     // XCD-aware placement: workgroup i runs on XCD i % 8 and workgroups start
     // in index order.  Workgroups 8q + x (x = 0..7) take slice q % NJ of
-    // (sequence, head) slot 8 (q / NJ) + x: the NJ slices of one head run on
-    // one XCD at the same time (Q and K come from HBM once, then from that
-    // XCD's L2), and consecutive heads of a sequence go to different XCDs, so
-    // every XCD gets an equal share of every sequence however long it is.
+    // (sequence, head) slot 8 (q / NJ) + x (WALK: of head 8 (q / NJ) + x): the
+    // NJ slices of one head run on one XCD at the same time (Q and K come from
+    // HBM once, then from that XCD's L2), and consecutive heads of a sequence
+    // go to different XCDs, so every XCD gets an equal share of every
+    // sequence however long it is.
     const int64_t nbh = gridDim.x / NJ;
     int64_t bh, slice;
     if (nbh % 8 == 0) {
@@ -556,51 +767,124 @@ __global__ __launch_bounds__(NTHREADS) void prefill_bf16_kernel(
         bh = blockIdx.x / NJ;
         slice = blockIdx.x % NJ;
     }
-    int64_t in0, out0, N;
-    seq_slice(map, bh / map.H, bh % map.H, &in0, &out0, &N);
+    Walk<WALK> wk;
+    wk.map = map;
+    wk.nseq = nseq;
+    wk.h = WALK ? bh : bh % map.H;
+    wk.tb = nullptr;
+    const int lane = tid % 64;
+    if constexpr (WALK) {
+        __shared__ WalkTable tb;
+        if (wave == 0) build_table(tb, map, nseq, lane);
+        __syncthreads();
+        wk.tb = &tb;
+    }
+    const Pos p0 = wk.first(WALK ? 0 : bh / map.H);
 
     Ctx<D> cx;
+    cx.q = q;
+    cx.k = k;
+    cx.v = v;
+    cx.o = out;
+    cx.state = state;
+    cx.H = map.H;
+    cx.h = wk.h;
     cx.j0 = (int)slice * PJ;
-    cx.s = slopes[bh % map.H];
-    cx.N = N;
+    cx.s = slopes[wk.h];
     // blocks processed: a multiple of NSET (trailing empty blocks are no-ops;
     // an empty sequence leaves its state unchanged)
-    cx.nblk = ((N + PC - 1) / PC + NSET - 1) / NSET * NSET;
-    cx.qh = q + in0;
-    cx.kh = k + in0;
-    cx.vh = v + in0;
-    cx.oh = out + out0;
+    cx.nblk = (wk.blocks(p0) + NSET - 1) / NSET * NSET;
     cx.ts = STRIDED ? (int)map.in.st : D;
     cx.ots = STRIDED ? (int)map.out.st : D;
 
-    const int lane = tid % 64;
     switch (wave) {
-        case 0: scan_wave<D>(cx, sm, state + bh * D * D, lane); break;
-        case 1: out0_wave<D>(cx, sm, lane); break;
-        case 2: out1_wave<D>(cx, sm, lane); break;
+        case 0: scan_wave<D>(cx, wk, p0, sm, lane); break;
+        case 1: out0_wave<D>(cx, wk, p0, sm, lane); break;
+        case 2: out1_wave<D>(cx, wk, p0, sm, lane); break;
         case 3: out1x_wave<D>(cx, sm, lane); break;
-        default: producer<D>(cx, sm, tid - 64 * NCONS); break;
+        default: producer<D>(cx, wk, p0, sm, tid - 64 * NCONS); break;
     }
+}
+
+// compute units of the current device (0 if unknown), looked up once per device
+int device_cus()
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+    if (dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
 }
 
 }  // namespace
 
 int64_t prefill_bf16_grid(int64_t seqs, int64_t H, int d) { return seqs * H * (d / PJ); }
 
+// A packed launch walks its sequences inside one workgroup per (head, column
+// slice) when the sequences are short on average (below WALK_MEAN_LEN tokens:
+// the walk saves each (sequence, head, slice) its own pipeline fill and drain,
+// while a grid of one workgroup per (sequence, head, slice) lets the hardware
+// balance long sequences over the compute units as workgroups finish), when
+// those workgroups fill whole waves of the device's compute units (every
+// workgroup then does the same work: all tokens of its head) and when the
+// offsets fit the walk's table (fewer than 2^31 tokens; batches of more than
+// WALK_SEQS sequences are walked WALK_SEQS at a time, one launch each).
+constexpr int64_t WALK_MEAN_LEN = 8192;
+
+bool prefill_bf16_walks(int64_t seqs, int64_t H, int64_t T, int d, bool packed)
+{
+    if (!packed || seqs < 2 || T > 0x7fffffff || T / seqs >= WALK_MEAN_LEN) return false;
+    const int cus = device_cus();
+    return cus > 0 && (H * (d / PJ)) % cus == 0;
+}
+
+template <bool WALK>
+const void *prefill_fn(int d, bool strided)
+{
+    if (d == 64)
+        return strided ? (const void *)prefill_bf16_kernel<64, true, WALK>
+                       : (const void *)prefill_bf16_kernel<64, false, WALK>;
+    return strided ? (const void *)prefill_bf16_kernel<128, true, WALK>
+                   : (const void *)prefill_bf16_kernel<128, false, WALK>;
+}
+
 hipError_t launch_prefill_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                const float *slopes, uint16_t *out, float *state,
                                int64_t seqs, const SeqMap &map, int d, hipStream_t stream)
 {
-    const dim3 grid((unsigned)prefill_bf16_grid(seqs, map.H, d)), block(NTHREADS);
-    SeqMap m = map;
-    void *args[] = {(void *)&q, (void *)&k, (void *)&v, (void *)&slopes,
-                    (void *)&out, (void *)&state, (void *)&m};
     const bool strided = map.in.st != d || map.out.st != d;
-    const void *fn = d == 64 ? (strided ? (const void *)prefill_bf16_kernel<64, true>
-                                        : (const void *)prefill_bf16_kernel<64, false>)
-                             : (strided ? (const void *)prefill_bf16_kernel<128, true>
-                                        : (const void *)prefill_bf16_kernel<128, false>);
-    return hipLaunchKernel(fn, grid, block, args, 0, stream);
+    const dim3 block(NTHREADS);
+    if (!prefill_bf16_walks(seqs, map.H, map.T, d, map.cu != nullptr)) {
+        SeqMap m = map;
+        int64_t nseq = seqs;
+        void *args[] = {(void *)&q, (void *)&k, (void *)&v, (void *)&slopes,
+                        (void *)&out, (void *)&state, (void *)&m, (void *)&nseq};
+        return hipLaunchKernel(prefill_fn<false>(d, strided),
+                               dim3((unsigned)prefill_bf16_grid(seqs, map.H, d)), block, args, 0,
+                               stream);
+    }
+    for (int64_t s0 = 0; s0 < seqs; s0 += WALK_SEQS) {
+        SeqMap m = map;
+        m.cu = map.cu + s0;
+        int64_t nseq = seqs - s0 < WALK_SEQS ? seqs - s0 : WALK_SEQS;
+        float *st = state + s0 * map.H * d * d;
+        void *args[] = {(void *)&q, (void *)&k, (void *)&v, (void *)&slopes,
+                        (void *)&out, (void *)&st, (void *)&m, (void *)&nseq};
+        const hipError_t e = hipLaunchKernel(prefill_fn<true>(d, strided),
+                                             dim3((unsigned)prefill_bf16_grid(1, map.H, d)), block,
+                                             args, 0, stream);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace la

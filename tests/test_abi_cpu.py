@@ -497,3 +497,18 @@ def test_decode_multi_strided_rejects_bad_arguments(lib, bad, code):
     assert lib.la_decode_multi_strided(a["q"], a["k"], a["v"], a["slopes"], a["nc"], a["state"],
                                        a["out"], a["B"], a["H"], a["T"], a["d"], a["sb"], a["sh"],
                                        a["st"], a["stream"]) == code
+
+
+@pytest.mark.parametrize("nseq,H,T,d,walks_null,code", [
+    (0, 64, 10, 128, False, LA_ERR_INVALID_ARG),
+    (2, 0, 10, 128, False, LA_ERR_INVALID_ARG),
+    (2, 64, -1, 128, False, LA_ERR_INVALID_ARG),
+    (2, 64, 10, 128, True, LA_ERR_INVALID_ARG),
+    (2, 64, 10, 96, False, LA_ERR_UNSUPPORTED),
+    (2, 64, 10, 32, False, LA_ERR_UNSUPPORTED),
+])
+def test_varlen_plan_rejects_bad_arguments(lib, nseq, H, T, d, walks_null, code):
+    walks = ctypes.c_int(7)
+    arg = None if walks_null else ctypes.byref(walks)
+    assert lib.la_prefill_varlen_plan(nseq, H, T, d, arg) == code
+    assert walks.value == 7            # untouched on error

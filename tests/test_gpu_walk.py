@@ -1,0 +1,143 @@
+"""GPU checks of the packed prefill's sequence walk: with H * d / 32
+workgroups filling whole waves of the compute units (H = 64 at d = 128,
+H = 128 at d = 64 on a 256-CU MI355X) one workgroup per (head, 32 output
+columns) runs every sequence of the batch in order, handing each sequence's
+final state out and the next one's initial state in at the boundaries.
+Checked against the fp64 packed oracle (bf16 bar 2e-2) and bitwise against
+launches over each sequence alone (which never walk), with empty, one-token,
+one-block and back-to-back one-block sequences, and through the strided call."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from long_context_layers_amd import binding, inputs
+from tests.gpu_util import BF16_TOL, log, np64
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+HEADS = {128: 64, 64: 128}          # heads that make the walk fill 256 compute units
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    binding.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def need_walk(nseq, H, T, d):
+    if not binding.prefill_varlen_walks(nseq, H, T, d):
+        pytest.skip(f"this device does not walk nseq={nseq} H={H} d={d} "
+                    f"({torch.cuda.get_device_properties(0).multi_processor_count} compute units)")
+
+
+def per_sequence(x, lens):
+    """each sequence by its own dense launch (one workgroup per head slice)"""
+    cu = x.cu_seqlens.cpu().tolist()
+    outs, sts = [], []
+    for i in range(len(lens)):
+        a, b = cu[i], cu[i + 1]
+        s1 = x.states[i:i + 1].clone()
+        if b > a:
+            q, k, v = (t[:, a:b].unsqueeze(0).contiguous() for t in (x.q, x.k, x.v))
+            outs.append(binding.prefill(q, k, v, x.slopes, s1)[0])
+        sts.append(s1[0])
+    torch.cuda.synchronize()
+    return torch.cat(outs, dim=1) if outs else None, torch.stack(sts)
+
+
+CASES = {
+    "mixed": [0, 1, 63, 64, 65, 130, 0, 1000, 7, 257],
+    "one_block_runs": [64, 1, 64, 2, 64, 64, 3, 64],          # a boundary at every block
+    "edges_empty": [0, 0, 100, 0, 0],
+    "two": [5, 700],
+}
+
+
+@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("case", sorted(CASES))
+def test_walk_matches_oracle_and_per_sequence_launches(case, d):
+    lens, H = CASES[case], HEADS[d]
+    need_walk(len(lens), H, sum(lens), d)
+    log(f"walk {case} {lens} H{H} d{d} bf16")
+    x = inputs.make_varlen(H, lens, d, torch.bfloat16, seed=600 + d + len(case), init_state=True,
+                           device=DEV)
+    st = x.states.clone()
+    out = binding.prefill_varlen(x.q, x.k, x.v, x.slopes, x.cu_seqlens, st)
+    torch.cuda.synchronize()
+    # bitwise: the walk computes every block exactly as a launch over its sequence alone
+    o1, s1 = per_sequence(x, lens)
+    if o1 is not None:
+        assert torch.equal(out, o1), "outputs differ from per-sequence launches"
+    assert torch.equal(st, s1), "states differ from per-sequence launches"
+    for i, n in enumerate(lens):
+        if n == 0:
+            assert torch.equal(st[i], x.states[i]), f"empty sequence {i} changed its state"
+    # and the oracle
+    o_ref, s_ref = oracle.prefill_varlen(np64(x.q), np64(x.k), np64(x.v), np64(x.slopes),
+                                         x.cu_seqlens.cpu().numpy(), np64(x.states))
+    cu = x.cu_seqlens.cpu().tolist()
+    eo = es = 0.0
+    o64, s64 = np64(out), np64(st)
+    for i in range(len(lens)):
+        a, b = cu[i], cu[i + 1]
+        if b > a:
+            eo = max(eo, oracle.rel_l2(o64[:, a:b], o_ref[:, a:b]))
+        es = max(es, oracle.rel_l2(s64[i], s_ref[i]))
+    log(f"  out rel-L2 {eo:.3e}  state rel-L2 {es:.3e}")
+    assert eo <= BF16_TOL and es <= BF16_TOL
+
+
+def test_walk_strided_bitwise_equals_contiguous():
+    lens, d = CASES["mixed"], 128
+    H = HEADS[d]
+    need_walk(len(lens), H, sum(lens), d)
+    log(f"walk through la_prefill_varlen_strided {lens} H{H} d{d}")
+    x = inputs.make_varlen(H, lens, d, torch.bfloat16, seed=661, init_state=True, device=DEV)
+    st_ref = x.states.clone()
+    out_ref = binding.prefill_varlen(x.q, x.k, x.v, x.slopes, x.cu_seqlens, st_ref)
+    T = x.q.shape[1]
+    # q, k, v as [H,T,d] views of one token-major [T, 3, H, d] buffer; out token-major
+    buf = torch.stack([t.transpose(0, 1) for t in (x.q, x.k, x.v)], dim=1).contiguous()
+    qv, kv, vv = (buf[:, j].transpose(0, 1) for j in range(3))
+    ob = torch.empty((T, H, d), dtype=torch.bfloat16, device=DEV)
+    st = x.states.clone()
+    binding.prefill_varlen(qv, kv, vv, x.slopes, x.cu_seqlens, st, out=ob.transpose(0, 1))
+    torch.cuda.synchronize()
+    assert torch.equal(ob.transpose(0, 1), out_ref) and torch.equal(st, st_ref)
+
+
+def test_walk_256k_workload_equals_per_sequence_launches():
+    # the packed 256K workload (74 sequences, 64 heads): every sequence's
+    # output and state bitwise against its own launch
+    x = inputs.make_workload("varlen_256k", device=DEV)
+    lens = x.lens
+    H, T, d = x.q.shape
+    need_walk(len(lens), H, sum(lens), d)
+    log(f"walk varlen_256k: H{H} T{T} d{d}, {len(lens)} sequences ({min(lens)}..{max(lens)})")
+    st = x.states.clone()
+    out = binding.prefill_varlen(x.q, x.k, x.v, x.slopes, x.cu_seqlens, st)
+    o1, s1 = per_sequence(x, lens)
+    bad = [i for i in range(len(lens)) if not torch.equal(st[i], s1[i])]
+    assert not bad, f"states differ for sequences {bad[:8]}"
+    assert torch.equal(out, o1), "outputs differ from per-sequence launches"
+
+
+def test_walk_more_sequences_than_one_table():
+    # 1100 short sequences (some empty): walked 1024 at a time, two launches
+    rng = np.random.default_rng(7)
+    lens = [int(x) for x in rng.integers(0, 40, size=1100)]
+    d, H = 128, HEADS[128]
+    need_walk(len(lens), H, sum(lens), d)
+    log(f"walk over {len(lens)} sequences of 0..39 tokens, H{H} d{d}")
+    x = inputs.make_varlen(H, lens, d, torch.bfloat16, seed=662, init_state=True, device=DEV)
+    st = x.states.clone()
+    out = binding.prefill_varlen(x.q, x.k, x.v, x.slopes, x.cu_seqlens, st)
+    o1, s1 = per_sequence(x, lens)
+    bad = [i for i in range(len(lens)) if not torch.equal(st[i], s1[i])]
+    assert not bad, f"states differ for sequences {bad[:8]}"
+    assert torch.equal(out, o1), "outputs differ from per-sequence launches"

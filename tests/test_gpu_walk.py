@@ -141,3 +141,43 @@ def test_walk_more_sequences_than_one_table():
     bad = [i for i in range(len(lens)) if not torch.equal(st[i], s1[i])]
     assert not bad, f"states differ for sequences {bad[:8]}"
     assert torch.equal(out, o1), "outputs differ from per-sequence launches"
+
+
+MALFORMED = {
+    # out of order, negative and past the end: sequence 2 clamps to rows 100..1099
+    "past_end": ([0, 300, 100, 1200, -5, 700, 1000], None),
+    # out of order and negative, nothing past row 999: rows 1000..1099 in no sequence
+    "short_tail": ([0, 300, 100, 900, -5, 700, 1000], 1000),
+}
+
+
+@pytest.mark.parametrize("case", sorted(MALFORMED))
+@pytest.mark.parametrize("H", [4, 64])
+def test_malformed_offsets_stay_inside_the_tensors(H, case):
+    # the results are unspecified, but every access stays inside q, k, v, out
+    # and the states (offsets are clamped into [0, T]), and rows outside every
+    # clamped sequence are not written.  H = 4: one workgroup per sequence;
+    # H = 64: the walk (on a 256-CU device).
+    offsets, free_from = MALFORMED[case]
+    d, T = 128, 1100
+    cu = torch.tensor(offsets, dtype=torch.int64, device=DEV)
+    nseq = cu.numel() - 1
+    log(f"malformed offsets {offsets} H{H} T{T} d{d}, walk={binding.prefill_varlen_walks(nseq, H, T, d)}")
+    g = torch.Generator(device=DEV).manual_seed(663)
+    q, k, v = ((torch.randn((H, T, d), generator=g, device=DEV) / d ** 0.5).to(torch.bfloat16)
+               for _ in range(3))
+    guard = 4096
+    canary = torch.tensor(-7.0, dtype=torch.bfloat16)
+    flat = torch.full((2 * guard + H * T * d,), float(canary), dtype=torch.bfloat16, device=DEV)
+    out = flat[guard:guard + H * T * d].view(H, T, d)
+    sflat = torch.full(((nseq + 2) * H * d * d,), 3.5, device=DEV)
+    states = sflat[H * d * d:(nseq + 1) * H * d * d].view(nseq, H, d, d)
+    states.normal_(generator=g).mul_(0.01)
+    binding.prefill_varlen(q, k, v, inputs.slopes(H, DEV), cu, states, out=out)
+    torch.cuda.synchronize()
+    assert bool((flat[:guard] == canary).all()) and bool((flat[-guard:] == canary).all())
+    assert bool((sflat[:H * d * d] == 3.5).all()) and bool((sflat[-H * d * d:] == 3.5).all())
+    end = T if free_from is None else free_from
+    assert bool(torch.isfinite(out[:, :end].float()).all()) and bool(torch.isfinite(states).all())
+    if free_from is not None:
+        assert bool((out[:, free_from:] == canary).all())

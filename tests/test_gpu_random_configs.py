@@ -1,5 +1,5 @@
 """Seeded random small configurations against the fp64 oracle (GPU): dense,
-packed and strided prefill, decode and multi-token decode, with random batch
+packed (both work splits) and strided prefill, decode and multi-token decode, with random batch
 sizes, head counts, lengths (ragged, empty and one-token sequences included),
 head dimensions, initial states and decay ranges (the pages' slopes, slow
 decays near 1, a head with lambda = 0).  Bars as for the named workloads:
@@ -80,6 +80,37 @@ def test_random_packed_prefill(case):
         lens[0] = 5
     log(f"packed case {case}: H{H} d{d} lens {lens}")
     x = inputs.make_varlen(H, lens, d, torch.bfloat16, seed=4000 + case, init_state=True,
+                           device=DEV)
+    x.slopes = draw_slopes(rng, H)
+    st = x.states.clone()
+    out = binding.prefill_varlen(x.q, x.k, x.v, x.slopes, x.cu_seqlens, st)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle.prefill_varlen(np64(x.q), np64(x.k), np64(x.v), np64(x.slopes),
+                                         x.cu_seqlens.cpu().numpy(), np64(x.states))
+    cu = x.cu_seqlens.cpu().numpy()
+    for i in range(len(lens)):
+        a, b = int(cu[i]), int(cu[i + 1])
+        if b > a:
+            assert oracle.rel_l2(np64(out)[:, a:b], o_ref[:, a:b]) <= BF16_TOL, i
+        assert oracle.rel_l2(np64(st)[i], s_ref[i]) <= BF16_TOL, i
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_random_packed_prefill_walk(case):
+    # head counts that make the packed launch walk its sequences (one
+    # workgroup per head and 32 columns on a 256-CU device); random lengths
+    # with empty, one-token and one-block sequences, random decays
+    rng = random.Random(7000 + case)
+    d = 128 if case % 2 == 0 else 64
+    H = 64 if d == 128 else 128
+    lens = [rng.choice([0, 1, 64, rng.randint(1, 63), rng.randint(65, 300)])
+            for _ in range(rng.randint(2, 9))]
+    if sum(lens) == 0:
+        lens[-1] = 7
+    if not binding.prefill_varlen_walks(len(lens), H, sum(lens), d):
+        pytest.skip("this device does not walk these launches")
+    log(f"walk case {case}: H{H} d{d} lens {lens}")
+    x = inputs.make_varlen(H, lens, d, torch.bfloat16, seed=8000 + case, init_state=True,
                            device=DEV)
     x.slopes = draw_slopes(rng, H)
     st = x.states.clone()

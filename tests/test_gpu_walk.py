@@ -92,12 +92,13 @@ def test_walk_matches_oracle_and_per_sequence_launches(case, d):
     assert eo <= BF16_TOL and es <= BF16_TOL
 
 
-def test_walk_strided_bitwise_equals_contiguous():
-    lens, d = CASES["mixed"], 128
+@pytest.mark.parametrize("d", [128, 64])
+def test_walk_strided_bitwise_equals_contiguous(d):
+    lens = CASES["mixed"]
     H = HEADS[d]
     need_walk(len(lens), H, sum(lens), d)
     log(f"walk through la_prefill_varlen_strided {lens} H{H} d{d}")
-    x = inputs.make_varlen(H, lens, d, torch.bfloat16, seed=661, init_state=True, device=DEV)
+    x = inputs.make_varlen(H, lens, d, torch.bfloat16, seed=661 + d, init_state=True, device=DEV)
     st_ref = x.states.clone()
     out_ref = binding.prefill_varlen(x.q, x.k, x.v, x.slopes, x.cu_seqlens, st_ref)
     T = x.q.shape[1]

@@ -648,6 +648,9 @@ def main():
         },
         "prefill_ms": round(pre_ms, 4),
         "prefill_tflops_frac_of_mfma_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        # the same launch at the pure recurrent count (4 d^2 per token-head: the inter
+        # term and the state update, no intra-block work)
+        "prefill_tflops_recurrent_count": round(B * H * N * 4 * d * d / (pre_ms * 1e-3) / 1e12, 3),
         "roofline": {
             "bound": "hbm",
             "achieved": round(gbs, 1),

@@ -22,7 +22,7 @@ same GPU sustains in probe kernels (lib/liblapeak.so: an MFMA loop and read,
 write and copy streams) and the prefill and decode against them.
 
 Outside the timed step, two more launches are measured the same way (HIP
-events on the launch stream, mean over ``--extra-reps``):
+events on the launch stream, median of ``--extra-reps`` after 3 warm-ups):
   * ``varlen``: packed prefill of 262,144 tokens split into 74 sub-sequences
     of 256..16,384 tokens (seeded log-uniform lengths), H=64, d=128 bf16, each
     sequence with its own fp32 state (la_prefill_varlen, one launch);
@@ -41,7 +41,8 @@ events on the launch stream, mean over ``--extra-reps``):
     4K (B=1, H=64, d=128, zero state; a 512 MB buffer is read between
     launches so the 256 MB MALL does not serve the ~200 MB of inputs - a read,
     because a written buffer would leave its write-back to the timed launch) and
-    the 32K crossover continuing from a random fp32 state;
+    the 32K crossover continuing from a random fp32 state (3 warm-ups, median
+    of 20 launches each);
   * ``decode_latency``: one sequence (B=1, H=64, d=128) decoded for 64
     steps, launched one call at a time and replayed from one captured HIP
     graph (torch.cuda.CUDAGraph): per-step latency of each;
@@ -90,10 +91,12 @@ def decode_bytes(B, H, d, T=1):
     return B * H * (2 * 4 * d * d + 4 * 2 * d * T)
 
 
-def time_launches(stream, fn, reps):
-    """mean ms of `reps` launches of fn() on `stream` (HIP events on that stream)."""
+def time_launches(stream, fn, reps, warmups=3):
+    """median ms of `reps` launches of fn() on `stream` (HIP events on that
+    stream), after `warmups` untimed launches."""
     import torch
-    fn()
+    for _ in range(warmups):
+        fn()
     stream.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(reps)]
@@ -102,7 +105,8 @@ def time_launches(stream, fn, reps):
         fn()
         b.record(stream)
     stream.synchronize()
-    return sum(a.elapsed_time(b) for a, b in evs) / reps
+    ts = sorted(a.elapsed_time(b) for a, b in evs)
+    return ts[len(ts) // 2] if len(ts) % 2 else 0.5 * (ts[len(ts) // 2 - 1] + ts[len(ts) // 2])
 
 
 def measure_varlen(dev, stream, reps, dense_tflops):
@@ -340,10 +344,12 @@ def measure_sizes(dev, stream, reps):
             st = x.state.clone()
             out = torch.empty_like(x.q)
         stream.synchronize()
+        n = max(reps, 20)                                               # short launches: 20 repetitions
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(reps)]
+               for _ in range(n)]
         with torch.cuda.stream(stream):
-            binding.prefill(x.q, x.k, x.v, x.slopes, st, out=out)      # warm-up
+            for _ in range(3):                                          # warm-ups
+                binding.prefill(x.q, x.k, x.v, x.slopes, st, out=out)
             for a, b in evs:
                 torch.sum(flush, dim=0, out=sink)                       # evicts the MALL
                 st.copy_(x.state)
@@ -351,7 +357,8 @@ def measure_sizes(dev, stream, reps):
                 binding.prefill(x.q, x.k, x.v, x.slopes, st, out=out)
                 b.record(stream)
         stream.synchronize()
-        ms = sum(a.elapsed_time(b) for a, b in evs) / reps
+        ts = sorted(a.elapsed_time(b) for a, b in evs)
+        ms = 0.5 * (ts[(n - 1) // 2] + ts[n // 2])                      # median
         fl = prefill_flops(w.B, w.H, w.N, w.d)
         by = prefill_bytes(w.B, w.H, w.N, w.d)
         res[name] = {"config": f"B{w.B} H{w.H} N{w.N} d{w.d} bf16, "

@@ -39,7 +39,7 @@ def draw_slopes(rng, H):
     return torch.tensor(s, dtype=torch.float32, device=DEV)
 
 
-@pytest.mark.parametrize("case", range(12))
+@pytest.mark.parametrize("case", range(40))
 def test_random_dense_and_strided_prefill(case):
     rng = random.Random(1000 + case)
     B, H = rng.randint(1, 3), rng.randint(1, 6)
@@ -70,7 +70,7 @@ def test_random_dense_and_strided_prefill(case):
         assert torch.equal(out2, out) and torch.equal(st2, st)
 
 
-@pytest.mark.parametrize("case", range(6))
+@pytest.mark.parametrize("case", range(20))
 def test_random_packed_prefill(case):
     rng = random.Random(3000 + case)
     H, d = rng.randint(1, 5), rng.choice([64, 128])
@@ -95,7 +95,7 @@ def test_random_packed_prefill(case):
         assert oracle.rel_l2(np64(st)[i], s_ref[i]) <= BF16_TOL, i
 
 
-@pytest.mark.parametrize("case", range(6))
+@pytest.mark.parametrize("case", range(16))
 def test_random_packed_prefill_walk(case):
     # head counts that make the packed launch walk its sequences (one
     # workgroup per head and 32 columns on a 256-CU device); random lengths
@@ -126,7 +126,7 @@ def test_random_packed_prefill_walk(case):
         assert oracle.rel_l2(np64(st)[i], s_ref[i]) <= BF16_TOL, i
 
 
-@pytest.mark.parametrize("case", range(6))
+@pytest.mark.parametrize("case", range(20))
 def test_random_decode_and_multi_token_decode(case):
     rng = random.Random(5000 + case)
     B, H, d = rng.randint(1, 40), rng.randint(1, 8), rng.choice([64, 128])

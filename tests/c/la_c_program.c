@@ -11,7 +11,9 @@
  *   2. la_prefill_varlen over two packed sequences equals two la_prefill
  *      calls, bitwise;
  *   3. argument errors: d = 96 -> LA_ERR_UNSUPPORTED, a null state ->
- *      LA_ERR_INVALID_ARG, la_status_string for every code.
+ *      LA_ERR_INVALID_ARG, la_status_string for every code;
+ *   4. la_prefill_varlen_plan answers 0 or 1 for a valid shape and rejects a
+ *      null result pointer.
  * Exit status 0 when every check holds; the first failure is printed.
  */
 #include <math.h>
@@ -238,6 +240,18 @@ int main(void)
     for (int c = 0; c <= 3; ++c)
         if (!la_status_string(c) || !la_status_string(c)[0]) return fail("la_status_string");
     if (la_abi_version() != LA_ABI_VERSION) return fail("ABI version");
+
+    /* 4. the packed prefill's work split for a shape (no GPU work) */
+    {
+        int walks = -1;
+        if (la_prefill_varlen_plan(74, 64, 262144, 128, &walks) != LA_OK || (walks != 0 && walks != 1))
+            return fail("la_prefill_varlen_plan");
+        if (la_prefill_varlen_plan(74, 64, 262144, 128, NULL) != LA_ERR_INVALID_ARG)
+            return fail("la_prefill_varlen_plan with a null result");
+        printf("packed prefill of 74 sequences x 64 heads: %s\n",
+               walks ? "one workgroup per head and 32 columns walks the sequences"
+                     : "one workgroup per sequence, head and 32 columns");
+    }
 
     HIP_OK(hipStreamDestroy(stream));
     printf("la_c_program: all checks passed\n");

@@ -39,13 +39,17 @@
 // What bounds it: every workgroup of a head pulls the full Q and K blocks
 // through its XCD's L2 (the four copies share one HBM read), and LDS carries
 // the producers' writes plus every MFMA operand.  Measured at 256K tokens, a
-// block takes about 2,000 cycles with LDS about 70% busy, set by the consumer
-// waves' reads and their dependent MFMA chains (the HBM stream alone would
-// take two thirds of that).  The layout therefore keeps each operand's LDS
-// reads few: 32x32x16 MFMAs (half the operand bytes per
-// flop of 16x16x32), scores kept in registers and fed straight into V^T P^T,
-// Q fragments shared by the score and inter-term products, and one barrier
-// per block (double-buffered tiles and state copy).
+// block takes about 2,075 cycles, of which about 1,690 are LDS traffic (some
+// 52 KB written, 96 KB read); the scan wave is the busiest (about 1,950
+// cycles, mostly waiting on its transposing reads), and giving any wave its
+// operands sooner only moves the queueing to the others (the HBM stream alone
+// would take about two thirds of the block).  The one barrier per block also
+// keeps the LDS shared fairly: without it, waves that finish early run ahead
+// and starve the busiest one.  The layout therefore keeps each operand's LDS
+// reads few: 32x32x16 MFMAs (half the operand bytes per flop of 16x16x32),
+// scores kept in registers and fed straight into V^T P^T, Q fragments shared
+// by the score and inter-term products, and double-buffered tiles and state
+// copy behind that single barrier.
 // Contractions over tokens (the state update K^T V and the intra output
 // V^T P^T) need the token index contiguous per lane; they read K and V from
 // their token-major LDS tiles with ds_read_b64_tr_b16 (gfx950 transposing LDS
@@ -124,7 +128,6 @@ struct alignas(16) Smem {
     uint16_t ST[2][PJ][D + QPAD];    // bf16 copies of the state slice, transposed
     float OP[2][64][20];             // W3 -> W2 partial outputs (one lane's 16 values)
 };
-
 
 // ---- the blocks a workgroup visits, in order --------------------------------
 

@@ -41,9 +41,10 @@
 // the producers' writes plus every MFMA operand.  Measured at 256K tokens, a
 // block takes about 2,075 cycles, of which about 1,690 are LDS traffic (some
 // 52 KB written, 96 KB read); the scan wave is the busiest (about 1,950
-// cycles, mostly waiting on its transposing reads), and giving any wave its
-// operands sooner only moves the queueing to the others (the HBM stream alone
-// would take about two thirds of the block).  The one barrier per block also
+// cycles, mostly waiting on its transposing reads), the busiest token wave and
+// the producers close behind, and relieving any one of them (giving the scan
+// its operands sooner, or even removing Q's LDS traffic) leaves the block time
+// unchanged (the HBM stream alone would take about two thirds of the block).  The one barrier per block also
 // keeps the LDS shared fairly: without it, waves that finish early run ahead
 // and starve the busiest one.  The layout therefore keeps each operand's LDS
 // reads few: 32x32x16 MFMAs (half the operand bytes per flop of 16x16x32),

@@ -125,6 +125,16 @@ def test_ragged_lengths_and_decay_extremes(dtype, tol, d, N):
     check_prefill(inp, tol, what=f"{dtype} d{d} N{N}")
 
 
+@pytest.mark.parametrize("dtype,tol,N", [(torch.float32, F32_TOL, 8192),
+                                         (torch.bfloat16, BF16_TOL, 32768)])
+def test_long_sequence_with_slow_decay(dtype, tol, N):
+    # decays close to 1 (lambda = 0.9999 .. 0.999) let the state accumulate over
+    # the whole sequence, so the inter term (the state's bf16 copy in the bf16
+    # kernel, fp32 FMAs in the fp32 one) dominates the outputs
+    inp = small_inputs(1, 2, N, 128, dtype, seed=N + 17, slopes=[1e-4, 1e-3])
+    check_prefill(inp, tol, what=f"{dtype} N{N} slow decay")
+
+
 @pytest.mark.parametrize("H", [1, 2, 5, 8])
 def test_head_counts_and_grid_mapping(H):
     # grids that are and are not multiples of the 8 XCDs

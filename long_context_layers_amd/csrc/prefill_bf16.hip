@@ -40,10 +40,10 @@
 // through its XCD's L2 (the four copies share one HBM read), and LDS carries
 // the producers' writes plus every MFMA operand.  Measured at 256K tokens, a
 // block takes about 2,075 cycles, of which about 1,690 are LDS traffic (some
-// 52 KB written, 96 KB read); the scan wave is the busiest (about 1,950
-// cycles, mostly waiting on its transposing reads), the busiest token wave and
-// the producers close behind, and relieving any one of them (giving the scan
-// its operands sooner, or even removing Q's LDS traffic) leaves the block time
+// 52 KB written, 96 KB read); the consumer waves are each busy 1,600 to 1,800
+// cycles of it, mostly waiting on LDS reads, the producers 1,300 to 1,650, and
+// relieving any one of them (giving the scan its operands sooner, moving work
+// between waves, or even removing Q's LDS traffic) leaves the block time
 // unchanged (the HBM stream alone would take about two thirds of the block).  The one barrier per block also
 // keeps the LDS shared fairly: without it, waves that finish early run ahead
 // and starve the busiest one.  The layout therefore keeps each operand's LDS
@@ -394,18 +394,22 @@ __device__ void producer(const Ctx<D> &cx, const Walk<WALK> &wk, Pos ld, Smem<D>
 // ---- consumer waves: scores, outputs, state scan ---------------------------
 //
 // Four consumer waves, one per SIMD (each shares its SIMD with one producer):
-//   W0  the state scan: S = lambda^c S + K^T (lambda^(c-1-b) V) on all D
-//       state rows, and the bf16 copy ST of the new state (double-buffered);
-//       at the last block of a sequence it stores the final state and, when
-//       sequences follow (WALK), takes up the next one's initial state, which
-//       it loaded into spare registers a whole sequence earlier;
+//   W0  the state scan: S = lambda^c S + K^T (lambda^(c-1-b) V) on the
+//       first D - 32 state rows, and the bf16 copy ST of those rows of the new
+//       state (double-buffered); at the last block of a sequence it stores
+//       their final state and, when sequences follow (WALK), takes up the next
+//       one's initial state, which it loaded into spare registers a whole
+//       sequence earlier;
 //   W1  tokens 0..31: inter term S^T Q^T + scores P^T(0,0) + V^T P^T, stored;
 //   W2  tokens 32..63: inter term + scores P^T(1,1) + their V^T P^T part;
 //   W3  tokens 32..63: scores P^T(0,1) + their V^T P^T part, handed to W2
 //       through LDS (fp32, double-buffered); W2 adds it one block later and
-//       stores that block's tokens 32..63 then.
-// The per-wave MFMA counts per block (d = 128) are 16 / 18 / 18 / 10, and the
-// sequential part of the method (the state scan) runs on its own wave.
+//       stores that block's tokens 32..63 then; and the scan of the last 32
+//       state rows, as W0 does for the others.
+// The per-wave MFMA counts per block (d = 128) are 12 / 18 / 18 / 14.  Giving
+// W3 a quarter of the scan (it was the least busy wave) leaves a dense launch's
+// time unchanged but halves the scan's work at every sequence boundary of a
+// walk (8% faster with 64-token sequences).
 
 template <int D>
 struct Lane {                               // lane coordinates for 32x32 MFMAs
@@ -431,30 +435,31 @@ __device__ __forceinline__ int state_reg_offset(int it, int r) {   // bytes
     return (32 * it + 8 * (r / 4) + r % 4) * D * 4;
 }
 
-template <int D>
-__device__ __forceinline__ void load_state(f32x16 (&x)[D / 32], const float *st, const Lane<D> &ln)
+// tiles T0 .. T0 + NTL - 1 of the slice at st (x[t] holds tile T0 + t)
+template <int D, int T0, int NTL>
+__device__ __forceinline__ void load_state(f32x16 (&x)[NTL], const float *st, const Lane<D> &ln)
 {
     const __amdgpu_buffer_rsrc_t rs = state_rsrc<D>(st);
     const int lo = (4 * ln.h * D + ln.l32) * 4;
 #pragma unroll
-    for (int it = 0; it < D / 32; ++it)
+    for (int t = 0; t < NTL; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-            x[it][r] = __builtin_bit_cast(
-                float, __builtin_amdgcn_raw_buffer_load_b32(rs, lo, state_reg_offset<D>(it, r), 0));
+            x[t][r] = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(rs, lo, state_reg_offset<D>(T0 + t, r), 0));
 }
 
-template <int D>
-__device__ __forceinline__ void store_state(float *st, const f32x16 (&x)[D / 32], const Lane<D> &ln)
+template <int D, int T0, int NTL>
+__device__ __forceinline__ void store_state(float *st, const f32x16 (&x)[NTL], const Lane<D> &ln)
 {
     const __amdgpu_buffer_rsrc_t rs = state_rsrc<D>(st);
     const int lo = (4 * ln.h * D + ln.l32) * 4;
 #pragma unroll
-    for (int it = 0; it < D / 32; ++it)
+    for (int t = 0; t < NTL; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x[it][r]), rs, lo,
-                                                  state_reg_offset<D>(it, r), 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x[t][r]), rs, lo,
+                                                  state_reg_offset<D>(T0 + t, r), 0);
 }
 
 // decay of score accumulator register r for a tile whose a-half is ah and
@@ -551,41 +556,49 @@ __device__ __forceinline__ void write_st(Smem<D> &sm, int buf, int it, const Lan
     }
 }
 
-// W0: the state scan (pos: block 0)
-template <int D, bool WALK>
-__device__ void scan_wave(const Ctx<D> &cx, const Walk<WALK> &wk, Pos pos, Smem<D> &sm, int lane)
-{
-    constexpr int NT = D / 32;                  // 32-row state tiles
-    const Lane<D> ln(lane);
-    const float full_decay = decay_pow(cx.s, PC);
+// The state scan over tiles T0 .. T0 + NTL - 1 (32 state rows each) of the
+// workgroup's column slice: S = lambda^c S + K^T (lambda^(c-1-b) V), fp32 in
+// registers for the whole walk, and each block's bf16 copy ST of those rows
+// (double-buffered).  At the last block of a sequence it stores the final
+// state of its rows and, when sequences follow (WALK), takes up the next one's
+// initial state, loaded into spare registers a whole sequence earlier.  The
+// tiles evolve independently, so they can be split over waves: the scan wave
+// runs all but the last, the off-diagonal score wave (the least busy) the last.
+template <int D, bool WALK, int T0, int NTL>
+struct Scan {
+    Lane<D> ln;
+    float full_decay;
+    f32x16 sacc[NTL], nxt[NTL];                 // nxt (WALK): the next sequence's initial state
 
-    f32x16 sacc[NT], nxt[NT];                   // nxt (WALK): the next sequence's initial state
-    if (pos.n > 0) {
-        if constexpr (WALK) load_state<D>(sacc, cx.state_of(pos.seq), ln);
-        else {
-            const float *St = cx.state_of(pos.seq);
+    __device__ Scan(const Ctx<D> &cx, int lane) : ln(lane), full_decay(decay_pow(cx.s, PC)) {}
+
+    __device__ void init(const Ctx<D> &cx, const Walk<WALK> &wk, const Pos &pos, Smem<D> &sm) {
+        if (pos.n > 0) {
+            if constexpr (WALK) load_state<D, T0, NTL>(sacc, cx.state_of(pos.seq), ln);
+            else {
+                const float *St = cx.state_of(pos.seq);
 #pragma unroll
-            for (int it = 0; it < NT; ++it)
+                for (int t = 0; t < NTL; ++t)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    sacc[it][r] = St[(32 * it + 8 * (r / 4) + 4 * ln.h + r % 4) * D + ln.l32];
+                    for (int r = 0; r < 16; ++r)
+                        sacc[t][r] = St[(32 * (T0 + t) + 8 * (r / 4) + 4 * ln.h + r % 4) * D + ln.l32];
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < NTL; ++t) sacc[t] = f32x16{};
         }
-    } else {
+        if constexpr (WALK) {
+            const int64_t s1 = wk.seq_at(pos.j + 1);
+            if (s1 >= 0) load_state<D, T0, NTL>(nxt, cx.state_of(s1), ln);
+        }
 #pragma unroll
-        for (int it = 0; it < NT; ++it) sacc[it] = f32x16{};
+        for (int t = 0; t < NTL; ++t) write_st<D>(sm, 1, T0 + t, ln, sacc[t]);   // read by block 0
     }
-    if constexpr (WALK) {
-        const int64_t s1 = wk.seq_at(pos.j + 1);
-        if (s1 >= 0) load_state<D>(nxt, cx.state_of(s1), ln);
-    }
-#pragma unroll
-    for (int it = 0; it < NT; ++it) write_st<D>(sm, 1, it, ln, sacc[it]);   // read by block 0
 
-    auto step = [&](auto BUFC) {
-        constexpr int BUF = decltype(BUFC)::value;
-        const int c = block_len(pos.t0, pos.n);
-        const bool last = Walk<WALK>::last(pos);
-        __syncthreads();
+    // block at pos (c tokens; last: it ends its sequence), LDS buffer BUF
+    template <int BUF>
+    __device__ void step(const Ctx<D> &cx, const Walk<WALK> &wk, const Pos &pos, Smem<D> &sm,
+                         int c, bool last) {
         const float sdec = c == PC ? full_decay : (c == 0 ? 1.0f : decay_pow(cx.s, c));
         bf16x8 vwf[PC / 16];
 #pragma unroll
@@ -594,36 +607,66 @@ __device__ void scan_wave(const Ctx<D> &cx, const Walk<WALK> &wk, Pos pos, Smem<
             vwf[ks] = ldtr8(&sm.VW[BUF][r0][16 * ln.q2 + ln.tcol], &sm.VW[BUF][r0 + 4][16 * ln.q2 + ln.tcol]);
         }
 #pragma unroll
-        for (int it = 0; it < NT; ++it) {
-            const int col = 32 * it + 16 * ln.q2 + ln.tcol;        // feature of this lane's chunk
+        for (int t = 0; t < NTL; ++t) {
+            const int col = 32 * (T0 + t) + 16 * ln.q2 + ln.tcol;   // feature of this lane's chunk
             const int ch = col >> 3, sub = col & 7;
-            sacc[it] *= sdec;
+            sacc[t] *= sdec;
 #pragma unroll
             for (int ks = 0; ks < PC / 16; ++ks) {
                 const int r0 = 16 * ks + 8 * ln.h + ln.trow;
                 const bf16x8 ka = ldtr8(&sm.K[BUF][r0][((ch ^ kswz(r0)) * 8) + sub],
                                         &sm.K[BUF][r0 + 4][((ch ^ kswz(r0 + 4)) * 8) + sub]);
-                sacc[it] = mfma(ka, vwf[ks], sacc[it]);
+                sacc[t] = mfma(ka, vwf[ks], sacc[t]);
             }
-            write_st<D>(sm, BUF, it, ln, sacc[it]);
+            write_st<D>(sm, BUF, T0 + t, ln, sacc[t]);
         }
         if constexpr (WALK) {
             if (last) {                         // the sequence's final state out
-                store_state<D>(cx.state_of(pos.seq), sacc, ln);
+                store_state<D, T0, NTL>(cx.state_of(pos.seq), sacc, ln);
                 if (wk.seq_at(pos.j + 1) >= 0) {
                     // the next sequence's initial state in (and its bf16 copy
                     // over the one just written for the next block); then the
                     // one after it starts loading
 #pragma unroll
-                    for (int it = 0; it < NT; ++it) {
-                        sacc[it] = nxt[it];
-                        write_st<D>(sm, BUF, it, ln, sacc[it]);
+                    for (int t = 0; t < NTL; ++t) {
+                        sacc[t] = nxt[t];
+                        write_st<D>(sm, BUF, T0 + t, ln, sacc[t]);
                     }
                     const int64_t s2 = wk.seq_at(pos.j + 2);
-                    if (s2 >= 0) load_state<D>(nxt, cx.state_of(s2), ln);
+                    if (s2 >= 0) load_state<D, T0, NTL>(nxt, cx.state_of(s2), ln);
                 }
             }
         }
+    }
+
+    // one sequence (no walk): its final state, after the loop (a store inside
+    // the step measured slower: it sits on the scan's sequential path)
+    __device__ void finish(const Ctx<D> &cx, const Pos &pos) {
+        if constexpr (!WALK) {
+            if (cx.nblk > 0) {
+                float *St = cx.state_of(pos.seq);
+#pragma unroll
+                for (int t = 0; t < NTL; ++t)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        St[(32 * (T0 + t) + 8 * (r / 4) + 4 * ln.h + r % 4) * D + ln.l32] = sacc[t][r];
+            }
+        }
+    }
+};
+
+// W0: the state scan on all tiles but the last (pos: block 0)
+template <int D, bool WALK>
+__device__ void scan_wave(const Ctx<D> &cx, const Walk<WALK> &wk, Pos pos, Smem<D> &sm, int lane)
+{
+    Scan<D, WALK, 0, D / 32 - 1> sc(cx, lane);
+    sc.init(cx, wk, pos, sm);
+    auto step = [&](auto BUFC) {
+        constexpr int BUF = decltype(BUFC)::value;
+        const int c = block_len(pos.t0, pos.n);
+        const bool last = Walk<WALK>::last(pos);
+        __syncthreads();
+        sc.template step<BUF>(cx, wk, pos, sm, c, last);
         wk.next(pos);
     };
     for (int64_t blk = 0; blk < cx.nblk; blk += 2) {
@@ -631,18 +674,7 @@ __device__ void scan_wave(const Ctx<D> &cx, const Walk<WALK> &wk, Pos pos, Smem<
         step(std::integral_constant<int, 1>());
     }
     __syncthreads();                            // final barrier (W2's last store)
-    // one sequence: its final state, after the loop (a store inside the step
-    // measured slower: it sits on the scan's sequential path every block)
-    if constexpr (!WALK) {
-        if (cx.nblk > 0) {
-            float *St = cx.state_of(pos.seq);
-#pragma unroll
-            for (int it = 0; it < NT; ++it)
-#pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    St[(32 * it + 8 * (r / 4) + 4 * ln.h + r % 4) * D + ln.l32] = sacc[it][r];
-        }
-    }
+    sc.finish(cx, pos);
 }
 
 // W1: tokens 0..31, complete
@@ -710,16 +742,22 @@ __device__ void out1_wave(const Ctx<D> &cx, const Walk<WALK> &wk, Pos pos, Smem<
     if (cx.nblk > 0) finish_prev((int)((cx.nblk - 1) & 1));   // (no blocks: none)
 }
 
-// W3: tokens 32..63, off-diagonal scores P^T(0,1) and their V^T P^T part
-template <int D>
-__device__ void out1x_wave(const Ctx<D> &cx, Smem<D> &sm, int lane)
+// W3: tokens 32..63, off-diagonal scores P^T(0,1) and their V^T P^T part,
+// and the state scan's last tile (pos: block 0)
+template <int D, bool WALK>
+__device__ void out1x_wave(const Ctx<D> &cx, const Walk<WALK> &wk, Pos pos, Smem<D> &sm, int lane)
 {
     const Lane<D> ln(lane);
     float dec[16];
     score_decay(dec, cx.s, 1, 0, ln.l32, ln.h);
+    Scan<D, WALK, D / 32 - 1, 1> sc(cx, lane);
+    sc.init(cx, wk, pos, sm);
     auto step = [&](auto BUFC) {
         constexpr int BUF = decltype(BUFC)::value;
+        const int c = block_len(pos.t0, pos.n);
+        const bool last = Walk<WALK>::last(pos);
         __syncthreads();
+        sc.template step<BUF>(cx, wk, pos, sm, c, last);
         bf16x8 qf[D / 16];
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) qf[ks] = ld8(&sm.Q[BUF][32 + ln.l32][16 * ks + 8 * ln.h]);
@@ -729,12 +767,14 @@ __device__ void out1x_wave(const Ctx<D> &cx, Smem<D> &sm, int lane)
 #pragma unroll
         for (int u = 0; u < 4; ++u)
             op[u] = make_float4(acc[4 * u + 0], acc[4 * u + 1], acc[4 * u + 2], acc[4 * u + 3]);
+        wk.next(pos);
     };
     for (int64_t blk = 0; blk < cx.nblk; blk += 2) {
         step(std::integral_constant<int, 0>());
         step(std::integral_constant<int, 1>());
     }
     __syncthreads();
+    sc.finish(cx, pos);
 }
 
 // STRIDED = false: rows of q, k, v and out are D elements apart (a
@@ -805,7 +845,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_bf16_kernel(
         case 0: scan_wave<D>(cx, wk, p0, sm, lane); break;
         case 1: out0_wave<D>(cx, wk, p0, sm, lane); break;
         case 2: out1_wave<D>(cx, wk, p0, sm, lane); break;
-        case 3: out1x_wave<D>(cx, sm, lane); break;
+        case 3: out1x_wave<D>(cx, wk, p0, sm, lane); break;
         default: producer<D>(cx, wk, p0, sm, tid - 64 * NCONS); break;
     }
 }

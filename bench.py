@@ -50,6 +50,11 @@ events on the launch stream, median of ``--extra-reps`` after 3 warm-ups):
     H=64, d=128 bf16, the last rank): its prefill from a zero state
     (la_prefill), the fold of the 8 gathered local states into its incoming
     state (la_cp_fold) and the correction of its output (la_cp_correct).
+With ``--power``, ``power`` holds the package power and graphics clock
+(`amd-smi metric -p -c`, run as a child process) sampled while the dense 256K
+prefill, the B=256 decode step, the MFMA loop probe and the HBM copy probe each
+run back to back for 8 s, with the package power limit (`rocm-smi
+--showmaxpower`) and the energy per launch.
 """
 from __future__ import annotations
 
@@ -107,6 +112,115 @@ def time_launches(stream, fn, reps, warmups=3):
     stream.synchronize()
     ts = sorted(a.elapsed_time(b) for a, b in evs)
     return ts[len(ts) // 2] if len(ts) % 2 else 0.5 * (ts[len(ts) // 2 - 1] + ts[len(ts) // 2])
+
+
+def smi_sample(args, timeout=30):
+    """stdout of one `amd-smi` / `rocm-smi` query, run as a child process (None if
+    the tool is missing or fails)."""
+    import shutil
+    import subprocess
+    exe = shutil.which(args[0]) or os.path.join("/opt/rocm/bin", args[0])
+    if not os.path.exists(exe):
+        return None
+    try:
+        r = subprocess.run([exe] + args[1:], capture_output=True, text=True, timeout=timeout)
+    except (OSError, subprocess.SubprocessError):
+        return None
+    return r.stdout if r.returncode == 0 else None
+
+
+def parse_power_clock(text):
+    """socket power (W) and the mean graphics clock over the XCDs (MHz) from
+    the text of `amd-smi metric -p -c`."""
+    if not text:
+        return None, None
+    m = re.search(r"SOCKET_POWER:\s*([0-9.]+)\s*W", text)
+    gfx = [float(x) for x in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*([0-9.]+)\s*MHz", text)]
+    return (float(m.group(1)) if m else None), (round(sum(gfx) / len(gfx)) if gfx else None)
+
+
+def measure_power(stream, workloads, seconds=8.0):
+    """Package power and graphics clock while each workload's launches run back
+    to back: `amd-smi metric -p -c` sampled twice from a child process, from
+    2.5 s into `seconds` of launches (the first seconds let the power controller
+    settle), with the launches timed by HIP events on `stream` meanwhile.
+    `workloads`: (name, launch function, launches per timed batch)."""
+    import threading
+    import torch
+    cap = None
+    t = smi_sample(["rocm-smi", "--showmaxpower"])
+    if t:
+        m = re.search(r"Max Graphics Package Power \(W\):\s*([0-9.]+)", t)
+        cap = float(m.group(1)) if m else None
+    stream.synchronize()
+    time.sleep(2.0)
+    idle_w, idle_mhz = parse_power_clock(smi_sample(["amd-smi", "metric", "-p", "-c"]))
+    res = {"tool": "amd-smi metric -p -c (socket power, graphics clock of each XCD), sampled "
+                   "twice while the launches run back to back",
+           "power_cap_w": cap, "idle_w": idle_w, "idle_gfx_mhz": idle_mhz}
+    for name, fn, per in workloads:
+        samples = []
+
+        def sampler():
+            for delay in (2.5, 1.5):
+                time.sleep(delay)
+                samples.append(parse_power_clock(smi_sample(["amd-smi", "metric", "-p", "-c"])))
+
+        th = threading.Thread(target=sampler)
+        ms = []
+        t_end = time.time() + seconds
+        th.start()
+        while time.time() < t_end:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(per):
+                fn()
+            b.record(stream)
+            stream.synchronize()
+            ms.append(a.elapsed_time(b) / per)
+        th.join()
+        watts = [w for w, _ in samples if w is not None]
+        mhz = [c for _, c in samples if c is not None]
+        ms_launch = sorted(ms)[len(ms) // 2]
+        w = sum(watts) / len(watts) if watts else None
+        res[name] = {"ms_per_launch": round(ms_launch, 4), "socket_w": watts, "gfx_mhz": mhz,
+                     "energy_j_per_launch": round(w * ms_launch * 1e-3, 3) if w else None}
+        print(f"[bench] power {name}: {ms_launch:.3f} ms per launch, {watts} W, {mhz} MHz",
+              file=sys.stderr, flush=True)
+    return res
+
+
+def measure_power_all(dev, stream, p, pstate, out, dcd, dstate, dout):
+    """measure_power over the dense 256K prefill, the B256 decode step and two
+    probe kernels (the bf16 MFMA loop and the HBM copy stream of lib/liblapeak.so)."""
+    import ctypes
+    import torch
+    from long_context_layers_amd import binding, build
+    lib = ctypes.CDLL(build.PEAK_LIB)
+    P, I64 = ctypes.c_void_p, ctypes.c_int64
+    lib.la_peak_mfma_bf16.argtypes = [I64, I64, P, P]
+    lib.la_peak_copy.argtypes = [P, P, I64, P]
+    lib.la_peak_mfma_bf16.restype = lib.la_peak_copy.restype = ctypes.c_int
+    h = stream.cuda_stream
+    with torch.cuda.stream(stream):
+        a = torch.zeros(1 << 29, dtype=torch.float32, device=dev)       # 2 GiB
+        b = torch.zeros(1 << 29, dtype=torch.float32, device=dev)
+        sink = torch.zeros(1 << 16, dtype=torch.float32, device=dev)
+
+    def check(rc):
+        if rc != 0:
+            raise RuntimeError(f"probe launch failed ({rc})")
+
+    work = [("prefill_256k", lambda: binding.prefill(p.q, p.k, p.v, p.slopes, pstate, out=out), 100),
+            ("decode_b256", lambda: binding.decode_step(dcd.q[0], dcd.k[0], dcd.v[0], dcd.slopes,
+                                                         dstate, out=dout), 1000),
+            ("mfma_probe", lambda: check(lib.la_peak_mfma_bf16(20000, 1024, sink.data_ptr(), h)), 100),
+            ("copy_probe_2gib", lambda: check(lib.la_peak_copy(a.data_ptr(), b.data_ptr(), 2 << 30, h)),
+             500)]
+    with torch.cuda.stream(stream):
+        res = measure_power(stream, work)
+    del a, b, sink
+    return res
 
 
 def measure_varlen(dev, stream, reps, dense_tflops):
@@ -540,6 +654,9 @@ def main():
                     help="only run a plain 1 GiB device copy (counter calibration)")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the probe kernels that measure this GPU's MFMA and HBM ceilings")
+    ap.add_argument("--power", action="store_true",
+                    help="also sample package power and graphics clock (amd-smi) while the "
+                         "prefill, the decode step and the probe kernels run back to back")
     ap.add_argument("--extra-reps", type=int, default=5,
                     help="launches timed for the packed-prefill and draft-verification lines "
                          "(0 skips them)")
@@ -691,6 +808,10 @@ def main():
             "kernel": "decode_kernel<bf16,128>",
         },
     }
+    if args.power:
+        print("[bench] package power and clock", file=sys.stderr, flush=True)
+        res["power"] = measure_power_all(dev, stream, p, pstate, out, dcd, dstate, dout)
+        torch.cuda.empty_cache()
     if not args.no_ceilings:
         print("[bench] ceilings (MFMA loop, HBM streams)", file=sys.stderr, flush=True)
         res["ceilings"] = measure_ceilings(dev, stream, pre_ms, tflops, dgbs)

@@ -565,7 +565,8 @@ __device__ __forceinline__ void write_st(Smem<D> &sm, int buf, int it, const Lan
 // state of its rows and, when sequences follow (WALK), takes up the next one's
 // initial state, loaded into spare registers a whole sequence earlier.  The
 // tiles evolve independently, so they can be split over waves: the scan wave
-// runs all but the last, the off-diagonal score wave (the least busy) the last.
+// runs all but the last, the off-diagonal score wave (which had the most
+// slack) the last.
 template <int D, bool WALK, int T0, int NTL>
 struct Scan {
     Lane<D> ln;

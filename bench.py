@@ -784,6 +784,9 @@ def main():
             "traffic": measured_traffic(),
             "algorithmic_bytes_per_launch": by,
             "kernel": "prefill_bf16_kernel<128, false, false>",
+            "binding_limit": "package power: the launch draws the 1400 W limit with the graphics "
+                             "clock lowered to about 2.05 GHz, measured with --power "
+                             "(profiles/prefill_bf16_256k_power.txt)",
         },
         "context": {
             "pages_kernel_numbers": "none: the Ling and Ring 2.6 Technical Report gives no "

@@ -52,9 +52,10 @@ events on the launch stream, median of ``--extra-reps`` after 3 warm-ups):
     state (la_cp_fold) and the correction of its output (la_cp_correct).
 With ``--power``, ``power`` holds the package power and graphics clock
 (`amd-smi metric -p -c`, run as a child process) sampled while the dense 256K
-prefill, the B=256 decode step, the MFMA loop probe and the HBM copy probe each
-run back to back for 8 s, with the package power limit (`rocm-smi
---showmaxpower`) and the energy per launch.
+prefill, the B=256 decode step and the probe kernels (MFMA loop, HBM copy, L2
+hits, LDS reads, light integer work) each run back to back for 8 s, with the
+package power limit (`rocm-smi --showmaxpower`), the energy per launch and the
+probes' energy per byte above the integer-work probe.
 """
 from __future__ import annotations
 
@@ -144,7 +145,8 @@ def measure_power(stream, workloads, seconds=8.0):
     to back: `amd-smi metric -p -c` sampled twice from a child process, from
     2.5 s into `seconds` of launches (the first seconds let the power controller
     settle), with the launches timed by HIP events on `stream` meanwhile.
-    `workloads`: (name, launch function, launches per timed batch)."""
+    `workloads`: (name, launch function, launches per timed batch, bytes moved
+    per launch or None, wave instructions of interest per launch or None)."""
     import threading
     import torch
     cap = None
@@ -156,9 +158,12 @@ def measure_power(stream, workloads, seconds=8.0):
     time.sleep(2.0)
     idle_w, idle_mhz = parse_power_clock(smi_sample(["amd-smi", "metric", "-p", "-c"]))
     res = {"tool": "amd-smi metric -p -c (socket power, graphics clock of each XCD), sampled "
-                   "twice while the launches run back to back",
+                   "twice while the launches run back to back; energies per byte and per "
+                   "instruction are taken above the idle sample (the GPU 2 s after the last "
+                   "work, clock as given); the probes' figures include their own few vector "
+                   "instructions per access",
            "power_cap_w": cap, "idle_w": idle_w, "idle_gfx_mhz": idle_mhz}
-    for name, fn, per in workloads:
+    for name, fn, per, nbytes, ninsts in workloads:
         samples = []
 
         def sampler():
@@ -185,6 +190,13 @@ def measure_power(stream, workloads, seconds=8.0):
         w = sum(watts) / len(watts) if watts else None
         res[name] = {"ms_per_launch": round(ms_launch, 4), "socket_w": watts, "gfx_mhz": mhz,
                      "energy_j_per_launch": round(w * ms_launch * 1e-3, 3) if w else None}
+        if nbytes:
+            res[name]["gbs"] = round(nbytes / (ms_launch * 1e-3) / 1e9, 1)
+        if w and idle_w and nbytes:
+            res[name]["pj_per_byte_above_idle"] = round((w - idle_w) / (nbytes / (ms_launch * 1e-3)) * 1e12, 2)
+        if w and idle_w and ninsts:
+            res[name]["nj_per_wave_instruction_above_idle"] = round(
+                (w - idle_w) / (ninsts / (ms_launch * 1e-3)) * 1e9, 3)
         print(f"[bench] power {name}: {ms_launch:.3f} ms per launch, {watts} W, {mhz} MHz",
               file=sys.stderr, flush=True)
     return res
@@ -200,7 +212,12 @@ def measure_power_all(dev, stream, p, pstate, out, dcd, dstate, dout):
     P, I64 = ctypes.c_void_p, ctypes.c_int64
     lib.la_peak_mfma_bf16.argtypes = [I64, I64, P, P]
     lib.la_peak_copy.argtypes = [P, P, I64, P]
-    lib.la_peak_mfma_bf16.restype = lib.la_peak_copy.restype = ctypes.c_int
+    lib.la_peak_l2_read.argtypes = [P, I64, I64, I64, P, P]
+    lib.la_peak_lds_read.argtypes = [I64, I64, P, P]
+    lib.la_peak_valu.argtypes = [I64, I64, P, P]
+    for f in (lib.la_peak_mfma_bf16, lib.la_peak_copy, lib.la_peak_l2_read, lib.la_peak_lds_read,
+              lib.la_peak_valu, lib.la_peak_lds_bytes_per_iter, lib.la_peak_mfma_chains):
+        f.restype = ctypes.c_int
     h = stream.cuda_stream
     with torch.cuda.stream(stream):
         a = torch.zeros(1 << 29, dtype=torch.float32, device=dev)       # 2 GiB
@@ -211,12 +228,25 @@ def measure_power_all(dev, stream, p, pstate, out, dcd, dstate, dout):
         if rc != 0:
             raise RuntimeError(f"probe launch failed ({rc})")
 
-    work = [("prefill_256k", lambda: binding.prefill(p.q, p.k, p.v, p.slopes, pstate, out=out), 100),
+    l2_region, l2_reps, lds_iters, blocks = 2 << 20, 40, 6000, 1024
+    lds_bytes = blocks * lib.la_peak_lds_bytes_per_iter() * lds_iters
+    mfma_iters, valu_iters = 20000, 500000
+    work = [("prefill_256k", lambda: binding.prefill(p.q, p.k, p.v, p.slopes, pstate, out=out), 100,
+             None, None),
             ("decode_b256", lambda: binding.decode_step(dcd.q[0], dcd.k[0], dcd.v[0], dcd.slopes,
-                                                         dstate, out=dout), 1000),
-            ("mfma_probe", lambda: check(lib.la_peak_mfma_bf16(20000, 1024, sink.data_ptr(), h)), 100),
+                                                         dstate, out=dout), 1000, None, None),
+            # wave instructions: MFMAs (4 waves x chains per iteration), integer adds (4 per iteration)
+            ("mfma_probe", lambda: check(lib.la_peak_mfma_bf16(mfma_iters, blocks, sink.data_ptr(), h)),
+             100, None, blocks * 4 * mfma_iters * lib.la_peak_mfma_chains()),
             ("copy_probe_2gib", lambda: check(lib.la_peak_copy(a.data_ptr(), b.data_ptr(), 2 << 30, h)),
-             500)]
+             500, 4 << 30, None),
+            ("l2_read_probe", lambda: check(lib.la_peak_l2_read(a.data_ptr(), l2_region, l2_reps, blocks,
+                                                                 sink.data_ptr(), h)), 100,
+             blocks * l2_region * l2_reps, None),
+            ("lds_read_probe", lambda: check(lib.la_peak_lds_read(lds_iters, blocks, sink.data_ptr(), h)),
+             100, lds_bytes, None),
+            ("valu_probe", lambda: check(lib.la_peak_valu(valu_iters, blocks, sink.data_ptr(), h)), 100,
+             None, blocks * 4 * valu_iters * 4)]
     with torch.cuda.stream(stream):
         res = measure_power(stream, work)
     del a, b, sink

@@ -13,7 +13,15 @@
 //   la_peak_write       the same chunks written;
 //   la_peak_copy        chunks read, then written to a second buffer;
 //   la_peak_update      chunks read, then written back in place (the access
-//                       pattern of a state updated where it lives).
+//                       pattern of a state updated where it lives);
+//   la_peak_l2_read     every workgroup sweeps one small region (a few MB,
+//                       held by each XCD's L2) again and again: L2 hits;
+//   la_peak_lds_read    every thread reads 16-byte LDS words in a loop, no
+//                       bank conflicts;
+//   la_peak_valu        four independent chains of integer adds per thread:
+//                       every CU busy at a light load (the power of active
+//                       CUs with little data movement, for the energy of the
+//                       others to be taken relative to).
 //
 // extern "C", plain pointers and sizes, enqueued on the caller's stream (no
 // synchronisation, no allocation).  Return: 0, or the hipError_t of the launch;
@@ -109,6 +117,59 @@ __global__ __launch_bounds__(PT) void update_kernel(u32x4 *__restrict__ buf)
     for (int u = 0; u < UNR; ++u) __builtin_nontemporal_store(x[u] + 1u, &p[u * PT]);
 }
 
+// L2 hits: each workgroup sweeps the region (region16 16-byte elements, a
+// multiple of a chunk) reps times, chunk by chunk, starting at a chunk of its
+// own so the workgroups spread over the L2 channels
+__global__ __launch_bounds__(PT) void l2_read_kernel(const u32x4 *__restrict__ src, int64_t region16,
+                                                     int64_t reps, float *__restrict__ sink)
+{
+    const int64_t nchunk = region16 / CHUNK16;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (int64_t r = 0; r < reps; ++r)
+        for (int64_t c = 0; c < nchunk; ++c) {
+            const u32x4 *p = src + ((c + blockIdx.x) % nchunk) * CHUNK16 + threadIdx.x;
+            u32x4 x[UNR];
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) x[u] = p[u * PT];
+#pragma unroll
+            for (int u = 0; u < UNR; ++u) acc ^= x[u];
+        }
+    const unsigned v = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+    if (v == 0x9e3779b9u) sink[blockIdx.x % 4096] = (float)v;   // keeps the loads live
+}
+
+// LDS reads: 64 KB per workgroup, each thread reading consecutive 16-byte
+// words (conflict-free) UNR at a time; the offset is hidden from the compiler
+// every iteration so the reads cannot be hoisted out of the loop
+constexpr int LDS16 = 4096;                          // 16-byte words (64 KB)
+__global__ __launch_bounds__(PT) void lds_read_kernel(int64_t iters, float *__restrict__ sink)
+{
+    __shared__ u32x4 buf[LDS16];
+    for (int i = threadIdx.x; i < LDS16; i += PT) buf[i] = u32x4{(unsigned)i, 1u, 2u, 3u};
+    __syncthreads();
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    int off = threadIdx.x;
+    for (int64_t i = 0; i < iters; ++i) {
+        asm volatile("" : "+v"(off));
+#pragma unroll
+        for (int u = 0; u < UNR; ++u) acc ^= buf[(off + u * PT) & (LDS16 - 1)];
+    }
+    const unsigned v = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+    if (v == 0x9e3779b9u) sink[blockIdx.x % 4096] = (float)v;
+}
+
+// active CUs at a light load: four dependent chains of integer adds per thread
+__global__ __launch_bounds__(PT) void valu_kernel(int64_t iters, float *__restrict__ sink)
+{
+    unsigned a = threadIdx.x, b = a ^ 1u, c = a ^ 2u, d = a ^ 3u;
+    for (int64_t i = 0; i < iters; ++i) {
+        asm volatile("" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+        a += 0x9e3779b9u; b += a; c += b; d += c;
+    }
+    const unsigned v = a ^ b ^ c ^ d;
+    if (v == 0x9e3779b9u) sink[blockIdx.x % 4096] = (float)v;
+}
+
 // bytes must be a positive multiple of one chunk (64 KB), grid = chunks
 bool chunks_of(int64_t bytes, unsigned *grid) {
     if (bytes <= 0 || bytes % (CHUNK16 * 16) != 0 || bytes / (CHUNK16 * 16) > 0x7fffffff)
@@ -167,6 +228,39 @@ int la_peak_update(void *buf, int64_t bytes, void *stream)
     if (!buf || !chunks_of(bytes, &g)) return -1;
     hipLaunchKernelGGL(update_kernel, dim3(g), dim3(PT), 0, static_cast<hipStream_t>(stream),
                        static_cast<u32x4 *>(buf));
+    return (int)hipGetLastError();
+}
+
+// region_bytes: a positive multiple of 64 KB; bytes read = blocks * region_bytes * reps
+int la_peak_l2_read(const void *src, int64_t region_bytes, int64_t reps, int64_t blocks, float *sink,
+                    void *stream)
+{
+    unsigned g;
+    if (!src || !sink || !chunks_of(region_bytes, &g) || reps < 1 || blocks < 1 ||
+        blocks > 0x7fffffff)
+        return -1;
+    hipLaunchKernelGGL(l2_read_kernel, dim3((unsigned)blocks), dim3(PT), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const u32x4 *>(src),
+                       region_bytes / 16, reps, sink);
+    return (int)hipGetLastError();
+}
+
+// bytes read = blocks * 256 threads * UNR * 16 B * iters
+int la_peak_lds_read(int64_t iters, int64_t blocks, float *sink, void *stream)
+{
+    if (iters < 1 || blocks < 1 || blocks > 0x7fffffff || !sink) return -1;
+    hipLaunchKernelGGL(lds_read_kernel, dim3((unsigned)blocks), dim3(PT), 0,
+                       static_cast<hipStream_t>(stream), iters, sink);
+    return (int)hipGetLastError();
+}
+
+int la_peak_lds_bytes_per_iter(void) { return PT * UNR * 16; }
+
+int la_peak_valu(int64_t iters, int64_t blocks, float *sink, void *stream)
+{
+    if (iters < 1 || blocks < 1 || blocks > 0x7fffffff || !sink) return -1;
+    hipLaunchKernelGGL(valu_kernel, dim3((unsigned)blocks), dim3(PT), 0,
+                       static_cast<hipStream_t>(stream), iters, sink);
     return (int)hipGetLastError();
 }
 

@@ -52,8 +52,9 @@ events on the launch stream, median of ``--extra-reps`` after 3 warm-ups):
     state (la_cp_fold) and the correction of its output (la_cp_correct).
 With ``--power``, ``power`` holds the package power and graphics clock
 (`amd-smi metric -p -c`, run as a child process) sampled while the dense 256K
-prefill, the B=256 decode step and the probe kernels (MFMA loop, HBM copy, L2
-hits, LDS reads, light integer work) each run back to back for 8 s, with the
+prefill, the B=256 decode step and the probe kernels (MFMA loops on constant
+and on changing random operands, HBM copy, L2 hits, LDS reads, integer adds)
+each run back to back for 8 s, with the
 package power limit (`rocm-smi --showmaxpower`), the energy per launch and the
 probes' energy per byte above the integer-work probe.
 """
@@ -215,8 +216,10 @@ def measure_power_all(dev, stream, p, pstate, out, dcd, dstate, dout):
     lib.la_peak_l2_read.argtypes = [P, I64, I64, I64, P, P]
     lib.la_peak_lds_read.argtypes = [I64, I64, P, P]
     lib.la_peak_valu.argtypes = [I64, I64, P, P]
+    lib.la_peak_mfma_bf16_data.argtypes = [I64, I64, P, P]
     for f in (lib.la_peak_mfma_bf16, lib.la_peak_copy, lib.la_peak_l2_read, lib.la_peak_lds_read,
-              lib.la_peak_valu, lib.la_peak_lds_bytes_per_iter, lib.la_peak_mfma_chains):
+              lib.la_peak_valu, lib.la_peak_lds_bytes_per_iter, lib.la_peak_mfma_chains,
+              lib.la_peak_mfma_bf16_data):
         f.restype = ctypes.c_int
     h = stream.cuda_stream
     with torch.cuda.stream(stream):
@@ -237,6 +240,9 @@ def measure_power_all(dev, stream, p, pstate, out, dcd, dstate, dout):
                                                          dstate, out=dout), 1000, None, None),
             # wave instructions: MFMAs (4 waves x chains per iteration), integer adds (4 per iteration)
             ("mfma_probe", lambda: check(lib.la_peak_mfma_bf16(mfma_iters, blocks, sink.data_ptr(), h)),
+             100, None, blocks * 4 * mfma_iters * lib.la_peak_mfma_chains()),
+            ("mfma_data_probe", lambda: check(lib.la_peak_mfma_bf16_data(mfma_iters, blocks,
+                                                                          sink.data_ptr(), h)),
              100, None, blocks * 4 * mfma_iters * lib.la_peak_mfma_chains()),
             ("copy_probe_2gib", lambda: check(lib.la_peak_copy(a.data_ptr(), b.data_ptr(), 2 << 30, h)),
              500, 4 << 30, None),

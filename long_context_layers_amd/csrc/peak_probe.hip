@@ -7,6 +7,9 @@
 //   la_peak_mfma_bf16   every wave runs independent chains of
 //                       v_mfma_f32_32x32x16_bf16 on register operands
 //                       (32,768 flop each), 8 waves per CU;
+//   la_peak_mfma_bf16_data  the same with operands of random bits that differ
+//                       from one MFMA to the next (the switching activity of
+//                       products on real data: the energy, not the rate);
 //   la_peak_read        a buffer read in 64 KB chunks, one per workgroup, the
 //                       whole chunk in flight, folded into a value that is
 //                       written only if it takes one particular bit pattern;
@@ -55,6 +58,37 @@ __global__ __launch_bounds__(PT) void mfma_loop_kernel(int64_t iters, float *sin
 #pragma unroll
         for (int c = 0; c < NACC; ++c)
             acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < NACC; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s += acc[c][r];
+    if (s == 12345.678f) sink[blockIdx.x] = s;   // keeps the chains live; never true in practice
+}
+
+// each chain has operands of its own, from a hash of (lane, chain, element):
+// normal-looking bf16 values in [-2, 2) with random low mantissa bits
+__global__ __launch_bounds__(PT) void mfma_data_kernel(int64_t iters, float *sink)
+{
+    const int lane = threadIdx.x % 64;
+    bf16x8 a[NACC], b[NACC];
+#pragma unroll
+    for (int c = 0; c < NACC; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            unsigned h = (unsigned)(lane * 131 + c * 17 + e) * 0x9e3779b9u;
+            h ^= h >> 15; h *= 0x85ebca6bu; h ^= h >> 13;
+            a[c][e] = (__bf16)((float)(h & 0xffffu) * (4.0f / 65536.0f) - 2.0f);
+            b[c][e] = (__bf16)((float)(h >> 16) * (4.0f / 65536.0f) - 2.0f);
+        }
+    f32x16 acc[NACC];
+#pragma unroll
+    for (int c = 0; c < NACC; ++c) acc[c] = f32x16{};
+    for (int64_t i = 0; i < iters; ++i) {
+#pragma unroll
+        for (int c = 0; c < NACC; ++c)
+            acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c], b[c], acc[c], 0, 0, 0);
     }
     float s = 0.f;
 #pragma unroll
@@ -192,6 +226,14 @@ int la_peak_mfma_bf16(int64_t iters, int64_t blocks, float *sink, void *stream)
 }
 
 int la_peak_mfma_chains(void) { return NACC; }
+
+int la_peak_mfma_bf16_data(int64_t iters, int64_t blocks, float *sink, void *stream)
+{
+    if (iters < 1 || blocks < 1 || blocks > 0x7fffffff || !sink) return -1;
+    hipLaunchKernelGGL(mfma_data_kernel, dim3((unsigned)blocks), dim3(PT), 0,
+                       static_cast<hipStream_t>(stream), iters, sink);
+    return (int)hipGetLastError();
+}
 
 // sink: at least 4096 floats
 int la_peak_read(const void *src, int64_t bytes, float *sink, void *stream)

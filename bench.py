@@ -52,7 +52,8 @@ events on the launch stream, median of ``--extra-reps`` after 3 warm-ups):
     state (la_cp_fold) and the correction of its output (la_cp_correct).
 With ``--power``, ``power`` holds the package power and graphics clock
 (`amd-smi metric -p -c`, run as a child process) sampled while the dense 256K
-prefill, the B=256 decode step and the probe kernels (MFMA loops on constant
+prefill (and its strided launch on a packed projection buffer), the B=256
+decode step and the probe kernels (MFMA loops on constant
 and on changing random operands, HBM copy, L2 hits, LDS reads, integer adds)
 each run back to back for 8 s, with the
 package power limit (`rocm-smi --showmaxpower`), the energy per launch and the
@@ -222,10 +223,17 @@ def measure_power_all(dev, stream, p, pstate, out, dcd, dstate, dout):
               lib.la_peak_mfma_bf16_data):
         f.restype = ctypes.c_int
     h = stream.cuda_stream
+    B, H, N, d = p.q.shape
     with torch.cuda.stream(stream):
         a = torch.zeros(1 << 29, dtype=torch.float32, device=dev)       # 2 GiB
         b = torch.zeros(1 << 29, dtype=torch.float32, device=dev)
         sink = torch.zeros(1 << 16, dtype=torch.float32, device=dev)
+        # the strided launch of the layer: q, k, v read from one packed
+        # [B,N,4*H*d] projection buffer (token stride 4*H*d)
+        proj = torch.empty((B, N, 4 * H * d), dtype=torch.bfloat16, device=dev)
+        proj.normal_(0.0, d ** -0.5, generator=torch.Generator(device=dev).manual_seed(11))
+        sq, sk, sv = (proj[..., i * H * d:(i + 1) * H * d].unflatten(-1, (H, d)).transpose(1, 2)
+                      for i in range(3))
 
     def check(rc):
         if rc != 0:
@@ -235,6 +243,8 @@ def measure_power_all(dev, stream, p, pstate, out, dcd, dstate, dout):
     lds_bytes = blocks * lib.la_peak_lds_bytes_per_iter() * lds_iters
     mfma_iters, valu_iters = 20000, 500000
     work = [("prefill_256k", lambda: binding.prefill(p.q, p.k, p.v, p.slopes, pstate, out=out), 100,
+             None, None),
+            ("prefill_256k_strided", lambda: binding.prefill(sq, sk, sv, p.slopes, pstate, out=out), 100,
              None, None),
             ("decode_b256", lambda: binding.decode_step(dcd.q[0], dcd.k[0], dcd.v[0], dcd.slopes,
                                                          dstate, out=dout), 1000, None, None),
@@ -255,7 +265,7 @@ def measure_power_all(dev, stream, p, pstate, out, dcd, dstate, dout):
              None, blocks * 4 * valu_iters * 4)]
     with torch.cuda.stream(stream):
         res = measure_power(stream, work)
-    del a, b, sink
+    del a, b, sink, proj, sq, sk, sv
     return res
 
 

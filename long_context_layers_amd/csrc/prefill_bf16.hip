@@ -24,7 +24,8 @@
 // sequences runs one workgroup per (head, column slice) that walks every
 // sequence in order (WALK): the pipeline then runs across sequence
 // boundaries, the scan hands each final state out and the next initial state
-// in (loaded a whole sequence ahead), instead of a workgroup per sequence
+// in (staged in LDS a whole sequence ahead, both moved 16 bytes per lane),
+// instead of a workgroup per sequence
 // paying its own pipeline fill and drain.
 //
 // Roles inside a workgroup (8 waves).  Waves 4..7 are producers: they only
@@ -197,6 +198,7 @@ struct Walk {
     SeqMap map;
     int64_t nseq, h;
     const WalkTable *tb;        // WALK: the table, in LDS
+    float *slot;                // WALK: the next sequence's initial state, staged in LDS
 
     __device__ static int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
     // WALK: the first block of table entry j (no tokens past the table's end)
@@ -400,8 +402,7 @@ __device__ void producer(const Ctx<D> &cx, const Walk<WALK> &wk, Pos ld, Smem<D>
 //       first D - 32 state rows, and the bf16 copy ST of those rows of the new
 //       state (double-buffered); at the last block of a sequence it stores
 //       their final state and, when sequences follow (WALK), takes up the next
-//       one's initial state, which it loaded into spare registers a whole
-//       sequence earlier;
+//       one's initial state, staged in an LDS slot a whole sequence earlier;
 //   W1  tokens 0..31: inter term S^T Q^T + scores P^T(0,0) + V^T P^T, stored;
 //   W2  tokens 32..63: inter term + scores P^T(1,1) + their V^T P^T part;
 //   W3  tokens 32..63: scores P^T(0,1) + their V^T P^T part, handed to W2
@@ -427,8 +428,9 @@ struct Lane {                               // lane coordinates for 32x32 MFMAs
 // (used by the walk, whose scan also holds a second slice; a single-slice scan
 // keeps plain pointer accesses, which measured slightly faster there).
 template <int D>
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t state_rsrc(const float *st) {
-    return __builtin_amdgcn_make_buffer_rsrc((void *)st, (short)0, ((D - 1) * D + PJ) * 4,
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t state_rsrc(const float *st, bool valid = true) {
+    // valid = false: a zero range, so loads return zeros and touch no memory
+    return __builtin_amdgcn_make_buffer_rsrc((void *)st, (short)0, valid ? ((D - 1) * D + PJ) * 4 : 0,
                                              RSRC_WORD3);
 }
 
@@ -462,6 +464,69 @@ __device__ __forceinline__ void store_state(float *st, const f32x16 (&x)[NTL], c
         for (int r = 0; r < 16; ++r)
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x[t][r]), rs, lo,
                                                   state_reg_offset<D>(T0 + t, r), 0);
+}
+
+// WALK: the slot holds state rows in LDS, row-major [D][32] fp32 (row = state
+// row, column = this workgroup's column), filled and drained 16 bytes per lane:
+// one instruction moves 8 rows (lane l: row 8 i + l / 8, columns 4 (l % 8) ..).
+
+// tiles T0 .. T0 + NTL - 1 of a sequence's initial state into the slot by
+// direct global -> LDS loads, so no registers wait for them; valid = false
+// stages zeros
+template <int D, int T0, int NTL>
+__device__ __forceinline__ void stage_state(float *slot, const float *st, int lane, bool valid)
+{
+    const __amdgpu_buffer_rsrc_t rs = state_rsrc<D>(st, valid);
+    const int lo = ((lane >> 3) * D + (lane & 7) * 4) * 4;
+#pragma unroll
+    for (int i = 0; i < 4 * NTL; ++i) {
+        const int row0 = 32 * T0 + 8 * i;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rs, (__attribute__((address_space(3))) void *)(slot + row0 * 32), 16, lo, row0 * D * 4, 0, 0);
+    }
+}
+
+// the staged rows into the scan's registers
+template <int D, int T0, int NTL>
+__device__ __forceinline__ void read_staged(f32x16 (&x)[NTL], const float *slot, const Lane<D> &ln)
+{
+#pragma unroll
+    for (int t = 0; t < NTL; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            x[t][r] = slot[(32 * (T0 + t) + 8 * (r / 4) + 4 * ln.h + r % 4) * 32 + ln.l32];
+}
+
+// the final state of these rows out through the slot (its staged contents
+// already read): registers -> slot -> 16-byte row pieces -> the state
+template <int D, int T0, int NTL>
+__device__ __forceinline__ void store_via_slot(float *slot, float *st, const f32x16 (&x)[NTL], const Lane<D> &ln,
+                                               int lane)
+{
+#pragma unroll
+    for (int t = 0; t < NTL; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            slot[(32 * (T0 + t) + 8 * (r / 4) + 4 * ln.h + r % 4) * 32 + ln.l32] = x[t][r];
+    const __amdgpu_buffer_rsrc_t rs = state_rsrc<D>(st);
+    const int lo = ((lane >> 3) * D + (lane & 7) * 4) * 4;
+#pragma unroll
+    for (int i = 0; i < 4 * NTL; ++i) {
+        const int row0 = 32 * T0 + 8 * i;
+        const float4 v = *reinterpret_cast<const float4 *>(&slot[(row0 + (lane >> 3)) * 32 + (lane & 7) * 4]);
+        const u32x4 w = {__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)};
+        __builtin_amdgcn_raw_buffer_store_b128(w, rs, lo, row0 * D * 4, 0);
+    }
+}
+
+// The block barrier of the waves that stage states (WALK): their own LDS
+// writes complete, then the barrier, with no wait for the direct loads still
+// in flight (a workgroup fence would wait for those too, their LDS writes
+// being counted with vector memory); the clobber keeps the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
 }
 
 // decay of score accumulator register r for a tile whose a-half is ah and
@@ -563,7 +628,7 @@ __device__ __forceinline__ void write_st(Smem<D> &sm, int buf, int it, const Lan
 // registers for the whole walk, and each block's bf16 copy ST of those rows
 // (double-buffered).  At the last block of a sequence it stores the final
 // state of its rows and, when sequences follow (WALK), takes up the next one's
-// initial state, loaded into spare registers a whole sequence earlier.  The
+// initial state, staged in LDS a whole sequence earlier.  The
 // tiles evolve independently, so they can be split over waves: the scan wave
 // runs all but the last, the off-diagonal score wave (which had the most
 // slack) the last.
@@ -571,7 +636,7 @@ template <int D, bool WALK, int T0, int NTL>
 struct Scan {
     Lane<D> ln;
     float full_decay;
-    f32x16 sacc[NTL], nxt[NTL];                 // nxt (WALK): the next sequence's initial state
+    f32x16 sacc[NTL];
 
     __device__ Scan(const Ctx<D> &cx, int lane) : ln(lane), full_decay(decay_pow(cx.s, PC)) {}
 
@@ -592,7 +657,7 @@ struct Scan {
         }
         if constexpr (WALK) {
             const int64_t s1 = wk.seq_at(pos.j + 1);
-            if (s1 >= 0) load_state<D, T0, NTL>(nxt, cx.state_of(s1), ln);
+            stage_state<D, T0, NTL>(wk.slot, cx.state_of(s1 >= 0 ? s1 : pos.seq), ln.l32 + 32 * ln.h, s1 >= 0);
         }
 #pragma unroll
         for (int t = 0; t < NTL; ++t) write_st<D>(sm, 1, T0 + t, ln, sacc[t]);   // read by block 0
@@ -624,19 +689,28 @@ struct Scan {
             write_st<D>(sm, BUF, T0 + t, ln, sacc[t]);
         }
         if constexpr (WALK) {
-            if (last) {                         // the sequence's final state out
-                store_state<D, T0, NTL>(cx.state_of(pos.seq), sacc, ln);
-                if (wk.seq_at(pos.j + 1) >= 0) {
-                    // the next sequence's initial state in (and its bf16 copy
-                    // over the one just written for the next block); then the
-                    // one after it starts loading
+            if (last) {
+                // the next sequence's initial state out of LDS first: the
+                // wait for its staging (issued a sequence ago) then covers no
+                // store of this block
+                const bool more = wk.seq_at(pos.j + 1) >= 0;
+                f32x16 nxt[NTL];
+                if (more) read_staged<D, T0, NTL>(nxt, wk.slot, ln);
+                store_via_slot<D, T0, NTL>(wk.slot, cx.state_of(pos.seq), sacc, ln,   // the final state out
+                                           ln.l32 + 32 * ln.h);
+                if (more) {
+                    // take up the next sequence (its bf16 copy over the one
+                    // just written for the next block), then stage the one
+                    // after it once the slot has been read
 #pragma unroll
                     for (int t = 0; t < NTL; ++t) {
                         sacc[t] = nxt[t];
                         write_st<D>(sm, BUF, T0 + t, ln, sacc[t]);
                     }
+                    __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0): the slot reads done
                     const int64_t s2 = wk.seq_at(pos.j + 2);
-                    if (s2 >= 0) load_state<D, T0, NTL>(nxt, cx.state_of(s2), ln);
+                    stage_state<D, T0, NTL>(wk.slot, cx.state_of(s2 >= 0 ? s2 : pos.seq), ln.l32 + 32 * ln.h,
+                                            s2 >= 0);
                 }
             }
         }
@@ -668,7 +742,8 @@ __device__ void scan_wave(const Ctx<D> &cx, const Walk<WALK> &wk, Pos pos, Smem<
         constexpr int BUF = decltype(BUFC)::value;
         const int c = block_len(pos.t0, pos.n);
         const bool last = Walk<WALK>::last(pos);
-        __syncthreads();
+        if constexpr (WALK) lds_barrier();
+        else __syncthreads();
         sc.template step<BUF>(cx, wk, pos, sm, c, last);
         wk.next(pos);
     };
@@ -759,7 +834,8 @@ __device__ void out1x_wave(const Ctx<D> &cx, const Walk<WALK> &wk, Pos pos, Smem
         constexpr int BUF = decltype(BUFC)::value;
         const int c = block_len(pos.t0, pos.n);
         const bool last = Walk<WALK>::last(pos);
-        __syncthreads();
+        if constexpr (WALK) lds_barrier();
+        else __syncthreads();
         sc.template step<BUF>(cx, wk, pos, sm, c, last);
         bf16x8 qf[D / 16];
 #pragma unroll
@@ -819,12 +895,15 @@ __global__ __launch_bounds__(NTHREADS) void prefill_bf16_kernel(
     wk.nseq = nseq;
     wk.h = WALK ? bh : bh % map.H;
     wk.tb = nullptr;
+    wk.slot = nullptr;
     const int lane = tid % 64;
     if constexpr (WALK) {
         __shared__ WalkTable tb;
+        __shared__ __attribute__((aligned(16))) float slot[D * 32];   // state rows [D][32], staged / drained
         if (wave == 0) build_table(tb, map, nseq, lane);
         __syncthreads();
         wk.tb = &tb;
+        wk.slot = slot;
     }
     const Pos p0 = wk.first(WALK ? 0 : bh / map.H);
 

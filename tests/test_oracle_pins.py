@@ -488,3 +488,113 @@ def test_cp_fold_rejects_bad_arguments():
         oracle.cp_fold(loc, CP_LENS[:-1], s, 1, S0)
     with pytest.raises(ValueError):
         oracle.cp_fold(loc, CP_LENS, s, len(CP_LENS) + 1, S0)
+
+
+# --- the parity checker itself: max over (b, h) slices of the relative L2
+# error, ||x - ref||_2 / ||ref||_2, absolute where ||ref||_2 = 0.  Every value
+# below is worked by hand; a checker that took one global ratio over all
+# slices, an absolute norm, a mean over slices, or the wrong axes gives a
+# different number.
+
+def _slice_3_4(scale=1.0):
+    """A [4, 5] slice with ||ref||_2 = 5 * scale: entries 3 and 4, rest 0."""
+    r = np.zeros((4, 5))
+    r[1, 2], r[3, 0] = 3.0, 4.0
+    return r * scale
+
+
+def test_rel_l2_is_the_worst_slice_not_a_global_ratio():
+    # [2, 3] slices of [4, 5]; every reference slice has norm 5.  Slice
+    # (1, 2) is off by (0, 0, ..., 2.5 at one entry): 2.5 / 5 = 0.5.  All
+    # other slices are exact.  A global ratio would give
+    # 2.5 / sqrt(6 * 25) = 0.2041, a mean over slices 0.5 / 6 = 0.0833.
+    ref = np.stack([np.stack([_slice_3_4() for _ in range(3)]) for _ in range(2)])
+    x = ref.copy()
+    x[1, 2, 0, 4] += 2.5
+    assert oracle.rel_l2(x, ref) == pytest.approx(0.5, abs=1e-15)
+    # one bad slice of 64 (the shape of a 64-head launch): still its own error
+    ref64 = np.ones((1, 64, 8, 16))                   # each slice norm sqrt(128)
+    x64 = ref64.copy()
+    x64[0, 37] *= 1.05                                # that slice: exactly 0.05
+    assert oracle.rel_l2(x64, ref64) == pytest.approx(0.05, rel=1e-12)
+
+
+@pytest.mark.parametrize("scale", [1e-150, 1e-3, 1.0, 1e3, 1e150])
+def test_rel_l2_is_relative_at_any_magnitude(scale):
+    # x = 7 ref: ||6 ref|| / ||ref|| = 6 whatever the magnitude
+    ref = np.stack([_slice_3_4(scale), 2.0 * _slice_3_4(scale)])[None]   # [1, 2, 4, 5]
+    assert oracle.rel_l2(7.0 * ref, ref) == pytest.approx(6.0, rel=1e-14)
+    # and a relative error of 1e-3 in every element stays 1e-3
+    assert oracle.rel_l2(ref * (1 + 1e-3), ref) == pytest.approx(1e-3, rel=1e-9)
+
+
+def test_rel_l2_zero_reference_slice_uses_the_absolute_norm():
+    ref = np.stack([np.zeros((4, 5)), _slice_3_4()])[None]      # [1, 2, 4, 5]
+    x = ref.copy()
+    x[0, 0, 2, 1], x[0, 0, 0, 3] = 3.0, 4.0     # ||x - 0|| = 5, absolute
+    assert oracle.rel_l2(x, ref) == pytest.approx(5.0, abs=1e-15)
+    x2 = ref.copy()
+    x2[0, 0, 0, 0] = 1e-4                       # small absolute error stays small
+    assert oracle.rel_l2(x2, ref) == pytest.approx(1e-4, rel=1e-12)
+    assert oracle.rel_l2(np.zeros((2, 3, 4)), np.zeros((2, 3, 4))) == 0.0
+
+
+def test_rel_l2_nan_or_inf_fails_any_tolerance():
+    ref = np.ones((1, 2, 4, 5))
+    for bad in (np.nan, np.inf, -np.inf):
+        x = ref.copy()
+        x[0, 1, 2, 3] = bad
+        r = oracle.rel_l2(x, ref)
+        assert not (r <= 1.0)          # a NaN or inf result never passes a bar
+
+
+def test_rel_l2_per_row_axes_for_decode_outputs():
+    # decode outputs [B, H, d] are compared per (b, h) row: axes=(-1,).
+    ref = np.zeros((2, 3, 5))
+    ref[..., 0], ref[..., 1] = 3.0, 4.0          # every row norm 5
+    x = ref.copy()
+    x[1, 0, 4] = 1.25                            # that row: 1.25 / 5 = 0.25
+    assert oracle.rel_l2(x, ref, axes=(-1,)) == pytest.approx(0.25, abs=1e-15)
+    # the same arrays sliced per b over (h, d) dilute it: 1.25 / sqrt(75)
+    assert oracle.rel_l2(x, ref, axes=(-2, -1)) == pytest.approx(1.25 / math.sqrt(75.0), rel=1e-14)
+
+
+def test_gpu_parity_helper_picks_the_slice_axes():
+    # tests/gpu_util.rel_l2 (what every GPU parity test calls) slices [B,H,N,d]
+    # and [B,H,d,d] tensors per (b, h) over the last two axes, [B,H,d] per row
+    gpu_util = pytest.importorskip("gpu_util")
+    ref4 = np.ones((1, 4, 6, 8))
+    x4 = ref4.copy()
+    x4[0, 2] *= 1.1                              # one head: 0.1
+    assert gpu_util.rel_l2(x4, ref4) == pytest.approx(0.1, rel=1e-12)
+    ref3 = np.ones((2, 4, 8))
+    x3 = ref3.copy()
+    x3[1, 3, :] *= 0.7                           # one row: 0.3
+    assert gpu_util.rel_l2(x3, ref3) == pytest.approx(0.3, rel=1e-12)
+    with pytest.raises(AssertionError):
+        gpu_util.rel_l2(np.ones((1, 2, 3, 4)), np.ones((1, 2, 4, 3)))
+
+
+def _mutant_rel_l2(x, ref, kind, axes=(-2, -1)):
+    """Plausible wrong checkers, each planted in a copy (CPU only)."""
+    x, ref = np.asarray(x, np.float64), np.asarray(ref, np.float64)
+    if kind == "global_ratio":
+        return float(np.linalg.norm(x - ref) / np.linalg.norm(ref))
+    num = np.sqrt(np.sum((x - ref) ** 2, axis=axes))
+    den = np.sqrt(np.sum(ref ** 2, axis=axes))
+    if kind == "absolute":
+        return float(np.max(num))
+    if kind == "mean_over_slices":
+        return float(np.mean(num / den))
+    if kind == "squared":
+        return float(np.max(num ** 2 / den ** 2))
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("kind", ["global_ratio", "absolute", "mean_over_slices", "squared"])
+def test_rel_l2_pins_detect_planted_checker_mistakes(kind):
+    ref = np.stack([np.stack([_slice_3_4() for _ in range(3)]) for _ in range(2)])
+    x = ref.copy()
+    x[1, 2, 0, 4] += 2.5
+    assert oracle.rel_l2(x, ref) == pytest.approx(0.5, abs=1e-15)
+    assert _mutant_rel_l2(x, ref, kind) != pytest.approx(0.5, rel=1e-3)

@@ -90,7 +90,8 @@ constexpr int PJ = 32;        // state / output columns per workgroup
 constexpr int NCONS = 4;      // consumer waves
 constexpr int PT = 256;       // producer threads (4 waves)
 constexpr int NTHREADS = 64 * NCONS + PT;
-constexpr int NSET = 4;       // producer register sets (blocks in flight)
+constexpr int NSET = 4;       // producer register sets (blocks in flight; even)
+static_assert(NSET % 2 == 0, "set i stages into LDS buffer i % 2");
 constexpr int QPAD = 8;       // bf16 padding of Q and state-copy rows
 constexpr int VP = 32;        // V row pitch (64 B, unpadded)
 
@@ -131,6 +132,7 @@ struct alignas(16) Smem {
     uint16_t VW[2][PC][VP];          // V slices times lambda^(c-1-b)
     uint16_t ST[2][PJ][D + QPAD];    // bf16 copies of the state slice, transposed
     float OP[2][64][20];             // W3 -> W2 partial outputs (one lane's 16 values)
+    uint16_t OT[2][32][PJ];          // W1 / W2 output tiles on their way to memory (swizzled)
 };
 
 // ---- the blocks a workgroup visits, in order --------------------------------
@@ -363,6 +365,17 @@ __device__ __forceinline__ void produce_step(const Ctx<D> &cx, const Walk<WALK> 
     wk.next(ld);
 }
 
+// the NSET producer steps of one round, sets 1 .. NSET-1, then 0
+template <int D, bool WALK, int I>
+struct ProduceRound {
+    __device__ static __forceinline__ void run(const Ctx<D> &cx, const Walk<WALK> &wk, Smem<D> &sm,
+                                               Regs<D> (&rs)[NSET], const Addr<D> &ad, Pos &ld, int p,
+                                               float wfull) {
+        produce_step<D, I % NSET>(cx, wk, sm, rs, ad, ld, p, wfull);
+        if constexpr (I < NSET) ProduceRound<D, WALK, I + 1>::run(cx, wk, sm, rs, ad, ld, p, wfull);
+    }
+};
+
 template <int D, bool WALK>
 __device__ void producer(const Ctx<D> &cx, const Walk<WALK> &wk, Pos ld, Smem<D> &sm, int p)
 {
@@ -386,12 +399,8 @@ __device__ void producer(const Ctx<D> &cx, const Walk<WALK> &wk, Pos ld, Smem<D>
     wk.next(ld);
 
     // block blk stages block blk+1 from set (blk+1) % NSET into buffer (blk+1) % 2
-    for (int64_t blk = 0; blk < cx.nblk; blk += NSET) {
-        produce_step<D, 1>(cx, wk, sm, rs, ad, ld, p, wfull);
-        produce_step<D, 2>(cx, wk, sm, rs, ad, ld, p, wfull);
-        produce_step<D, 3>(cx, wk, sm, rs, ad, ld, p, wfull);
-        produce_step<D, 0>(cx, wk, sm, rs, ad, ld, p, wfull);
-    }
+    for (int64_t blk = 0; blk < cx.nblk; blk += NSET)
+        ProduceRound<D, WALK, 1>::run(cx, wk, sm, rs, ad, ld, p, wfull);
     __syncthreads();                                   // final barrier (matches the consumers)
 }
 
@@ -582,18 +591,27 @@ __device__ __forceinline__ void score_pv(const Smem<D> &sm, int buf, int bh,
 // store a 32x32 O^T tile (tokens 32ah.., columns j0..j0+31) of the block at p.
 // Accumulator register group q4 holds columns 8q4 + 4h + 0..3 of token a; a
 // lane-half swap (lanes l <-> l+32) of groups (0,1) and (2,3) gives lane h
-// columns 8h..8h+7 and 16+8h..16+8h+7, so each row is written as 32-byte runs
-// by two 16-byte stores per lane.
+// columns 8h..8h+7 and 16+8h..16+8h+7 of token l32.  The tile goes through
+// the wave's own 2 KB of LDS so that each 16-byte store instruction covers 16
+// tokens with four lanes on each token's 64-byte slice, instead of 32 bytes of
+// each of 32 tokens: half as many, twice as large pieces of the 128-byte
+// lines that two workgroups share, which the memory system absorbs faster
+// (the launch is bound by its memory traffic).  Chunk c (8 columns) of tile
+// row r sits at chunk c ^ ((r >> 2) & 3): conflict-free for both the row-wise
+// writes and the 4-lanes-per-row reads.
+__device__ __forceinline__ int ot_chunk(int r, int c) { return c ^ ((r >> 2) & 3); }
+
 template <int D>
-__device__ __forceinline__ int out_offset(const Ctx<D> &cx, int ah, const Lane<D> &ln) {
-    return ((32 * ah + ln.l32) * cx.ots + cx.j0 + 8 * ln.h) * 2;   // bytes, row 32ah + l32
+__device__ __forceinline__ int out_offset(const Ctx<D> &cx, int ah, int pr, int lane) {
+    // bytes of this lane's 16-byte piece: token 32ah + 16pr + lane/4, chunk lane%4
+    return ((32 * ah + 16 * pr + lane / 4) * cx.ots + cx.j0 + 8 * (lane % 4)) * 2;
 }
 
 template <int D>
-__device__ __forceinline__ void store_out(const Ctx<D> &cx, const Pos &p, int ooff,
-                                          const f32x16 &acc)
+__device__ __forceinline__ void store_out(const Ctx<D> &cx, const Pos &p, const int (&ooff)[2],
+                                          const f32x16 &acc, uint16_t (*ot)[PJ], const Lane<D> &ln,
+                                          int lane)
 {
-    const __amdgpu_buffer_rsrc_t ro = block_rsrc<D>(cx.o + p.out0, p.t0, p.n, cx.ots);   // rows past the end dropped
 #pragma unroll
     for (int pr = 0; pr < 2; ++pr) {
         const int g0 = 2 * pr, g1 = 2 * pr + 1;
@@ -603,10 +621,20 @@ __device__ __forceinline__ void store_out(const Ctx<D> &cx, const Pos &p, int oo
         unsigned y1 = pack_bf16x2(acc[4 * g1 + 2], acc[4 * g1 + 3]);
         const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
         const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
-        u32x4 o;
-        o[0] = s0[0]; o[1] = s1[0]; o[2] = s0[1]; o[3] = s1[1];
-        __builtin_amdgcn_raw_buffer_store_b128(o, ro, ooff + 32 * pr, 0, 0);
+        uint4 o;
+        o.x = s0[0]; o.y = s1[0]; o.z = s0[1]; o.w = s1[1];
+        *reinterpret_cast<uint4 *>(&ot[ln.l32][8 * ot_chunk(ln.l32, ln.h + 2 * pr)]) = o;
     }
+    asm volatile("" : : : "memory");              // the reads below follow the writes
+    const __amdgpu_buffer_rsrc_t ro = block_rsrc<D>(cx.o + p.out0, p.t0, p.n, cx.ots);   // rows past the end dropped
+#pragma unroll
+    for (int pr = 0; pr < 2; ++pr) {
+        const int r = 16 * pr + lane / 4;
+        const uint4 x = *reinterpret_cast<const uint4 *>(&ot[r][8 * ot_chunk(r, lane % 4)]);
+        const u32x4 w = {x.x, x.y, x.z, x.w};
+        __builtin_amdgcn_raw_buffer_store_b128(w, ro, ooff[pr], 0, 0);
+    }
+    asm volatile("" : : : "memory");              // the next tile's writes follow these reads
 }
 
 // bf16 copy of state tile it (rows 32it..) into ST[buf][j][i]
@@ -763,14 +791,14 @@ __device__ void out0_wave(const Ctx<D> &cx, const Walk<WALK> &wk, Pos pos, Smem<
     float dec[16];
     score_decay(dec, cx.s, 0, 0, ln.l32, ln.h);
     const float scale = decay_pow(cx.s, ln.l32 + 1);               // lambda^(a+1)
-    const int ooff = out_offset(cx, 0, ln);
+    const int ooff[2] = {out_offset(cx, 0, 0, lane), out_offset(cx, 0, 1, lane)};
     auto step = [&](auto BUFC) {
         constexpr int BUF = decltype(BUFC)::value;
         __syncthreads();
         bf16x8 qf[D / 16];
         f32x16 acc = inter_term<D>(sm, BUF, BUF ^ 1, 0, ln, scale, qf);
         score_pv<D>(sm, BUF, 0, qf, dec, ln, acc);
-        store_out<D>(cx, pos, ooff, acc);
+        store_out<D>(cx, pos, ooff, acc, sm.OT[0], ln, lane);
         wk.next(pos);
     };
     for (int64_t blk = 0; blk < cx.nblk; blk += 2) {
@@ -788,7 +816,7 @@ __device__ void out1_wave(const Ctx<D> &cx, const Walk<WALK> &wk, Pos pos, Smem<
     float dec[16];
     score_decay(dec, cx.s, 1, 1, ln.l32, ln.h);
     const float scale = decay_pow(cx.s, 32 + ln.l32 + 1);
-    const int ooff = out_offset(cx, 1, ln);
+    const int ooff[2] = {out_offset(cx, 1, 0, lane), out_offset(cx, 1, 1, lane)};
     f32x16 prev = {};
     Pos ppos = pos;                                                // block of prev
     auto finish_prev = [&](int pbuf) {                             // that block's tokens 32..63
@@ -799,7 +827,7 @@ __device__ void out1_wave(const Ctx<D> &cx, const Walk<WALK> &wk, Pos pos, Smem<
             prev[4 * u + 0] += x.x; prev[4 * u + 1] += x.y;
             prev[4 * u + 2] += x.z; prev[4 * u + 3] += x.w;
         }
-        store_out<D>(cx, ppos, ooff, prev);
+        store_out<D>(cx, ppos, ooff, prev, sm.OT[1], ln, lane);
     };
     auto step = [&](int64_t blk, auto BUFC) {
         constexpr int BUF = decltype(BUFC)::value;

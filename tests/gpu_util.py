@@ -9,6 +9,15 @@ import oracle
 BF16_TOL = 2e-2      # max over (b, h) of relative L2 error, bf16 activations
 F32_TOL = 1e-3       # same, fp32 activations
 
+# Regression guards on the named bf16 workloads, below the pass bars: the
+# kernels measure 2.4e-3 .. 2.8e-3 (outputs: the bf16 scores, the bf16 copy of
+# the state and the bf16 output each round at ~2^-9 relative) and 1.7e-3 for
+# prefill states, 1.7e-6 for decode states (fp32, never rounded).  A change
+# that loses precision (an extra bf16 rounding, a state kept in bf16) moves
+# these well before it reaches the 2e-2 bar.
+BF16_GUARD = 4e-3     # outputs and prefill final states
+DECODE_STATE_GUARD = 1e-4
+
 
 def log(msg):
     print(msg, flush=True)

@@ -10,7 +10,8 @@ import torch
 
 import oracle
 from long_context_layers_amd import binding, inputs
-from tests.gpu_util import BF16_TOL, F32_TOL, log, np64, oracle_prefill, rel_l2
+from tests.gpu_util import (BF16_GUARD, BF16_TOL, DECODE_STATE_GUARD, F32_TOL, log, np64,
+                            oracle_prefill, rel_l2)
 
 pytestmark = pytest.mark.gpu
 
@@ -33,7 +34,7 @@ def gpu_prefill(inp, state=None):
     return out, st
 
 
-def check_prefill(inp, tol, heads=None, what=""):
+def check_prefill(inp, tol, heads=None, what="", guard=None):
     out, st = gpu_prefill(inp)
     o_ref, s_ref = oracle_prefill(inp.q, inp.k, inp.v, inp.slopes, inp.state, heads)
     if heads is not None:
@@ -42,6 +43,8 @@ def check_prefill(inp, tol, heads=None, what=""):
     eo, es = rel_l2(out, o_ref), rel_l2(st, s_ref)
     log(f"  {what}: out rel-L2 {eo:.3e}  state rel-L2 {es:.3e}  (tol {tol:g})")
     assert eo <= tol and es <= tol
+    if guard is not None:
+        assert eo <= guard and es <= guard, f"precision regression: {eo:.3e} / {es:.3e} > {guard:g}"
     return eo, es
 
 
@@ -56,13 +59,13 @@ def test_tiny_f32_workload():
 def test_prefill_4k_workload():
     log("prefill_4k: B1 H64 N4096 d128 bf16")
     inp = inputs.make_workload("prefill_4k", device=DEV)
-    check_prefill(inp, BF16_TOL, what="prefill_4k")
+    check_prefill(inp, BF16_TOL, what="prefill_4k", guard=BF16_GUARD)
 
 
 def test_prefill_32k_with_initial_state():
     log("prefill_32k_state: B1 H64 N32768 d128 bf16 + fp32 initial state")
     inp = inputs.make_workload("prefill_32k_state", device=DEV)
-    check_prefill(inp, BF16_TOL, what="prefill_32k_state")
+    check_prefill(inp, BF16_TOL, what="prefill_32k_state", guard=BF16_GUARD)
 
 
 def test_prefill_256k_all_heads():
@@ -84,6 +87,7 @@ def test_prefill_256k_all_heads():
         worst_o, worst_s = max(worst_o, eo), max(worst_s, es)
         del o_ref, s_ref
     assert worst_o <= BF16_TOL and worst_s <= BF16_TOL
+    assert worst_o <= BF16_GUARD and worst_s <= BF16_GUARD, "precision regression"
 
 
 def test_decode_b256_64_steps():
@@ -103,6 +107,7 @@ def test_decode_b256_64_steps():
     es = rel_l2(st, ref_st)
     log(f"  decode_b256: worst step out rel-L2 {worst:.3e}  final state {es:.3e}")
     assert es <= BF16_TOL
+    assert worst <= BF16_GUARD and es <= DECODE_STATE_GUARD, "precision regression"
 
 
 # ---- edge cases ------------------------------------------------------------

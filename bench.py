@@ -830,9 +830,12 @@ def main():
             "traffic": measured_traffic(),
             "algorithmic_bytes_per_launch": by,
             "kernel": "prefill_bf16_kernel<128, false, false>",
-            "binding_limit": "package power: the launch draws the 1400 W limit with the graphics "
-                             "clock lowered to about 2.05 GHz, measured with --power "
-                             "(profiles/prefill_bf16_256k_power.txt)",
+            "binding_limit": "memory traffic: a copy of the kernel with its compute removed "
+                             "(same loads and stores) takes as long; per compute unit, the full "
+                             "Q and K blocks every column slice reads through L2 and the output "
+                             "lines shared by two workgroups; not package power (with the "
+                             "redundant score tiles skipped the power drops below the limit and "
+                             "the clock rises 12% at the same time)",
         },
         "context": {
             "pages_kernel_numbers": "none: the Ling and Ring 2.6 Technical Report gives no "

@@ -37,24 +37,23 @@
 // on gfx9: one counter (vmcnt) tracks both, and a wave with both kinds in
 // flight must drain all of them before it can use any loaded register.
 //
-// What bounds it: every workgroup of a head pulls the full Q and K blocks
-// through its XCD's L2 (the four copies share one HBM read), and LDS carries
-// the producers' writes plus every MFMA operand.  Measured at 256K tokens, a
-// block takes about 2,075 cycles, of which about 1,690 are LDS traffic (some
-// 52 KB written, 96 KB read); the consumer waves are each busy 1,600 to 1,800
-// cycles of it, mostly waiting on LDS reads, the producers 1,300 to 1,650, and
-// relieving any one of them (giving the scan its operands sooner, moving work
-// between waves, or even removing Q's LDS traffic) leaves the time per launch
-// unchanged.  That time is set by the package power limit: the kernel draws
-// the whole 1400 W with the clock held near 2.05 GHz, while its loading half
-// and its compute half, each run alone, stay below the limit at 2.4 GHz.  A
-// block done in fewer cycles for the same energy only lowers the clock.  The one barrier per block also
-// keeps the LDS shared fairly: without it, waves that finish early run ahead
-// and starve the busiest one.  The layout therefore keeps each operand's LDS
-// reads few: 32x32x16 MFMAs (half the operand bytes per flop of 16x16x32),
-// scores kept in registers and fed straight into V^T P^T, Q fragments shared
-// by the score and inter-term products, and double-buffered tiles and state
-// copy behind that single barrier.
+// What bounds it: memory traffic, not arithmetic.  A copy of the kernel
+// with the consumers' LDS reads and MFMAs removed (the same loads and stores,
+// no compute) takes as long as the kernel itself, and one whose package power
+// falls below the limit (the redundant score tiles skipped) runs its clock
+// 12% higher in the same time.  Two parts of the traffic cost more than their
+// HBM bytes: each workgroup of a head pulls the full Q and K blocks through
+// its XCD's L2 (three of every four Q/K bytes a compute unit reads are L2
+// hits; reading only its own quarter, the same HBM bytes stream 1.4x faster),
+// and the output rows are shared between two workgroups per 128-byte line.
+// The layout therefore keeps the L2 sharing on one XCD (spreading a head's
+// slices over XCDs doubles the time), writes the output as 64-byte row slices
+// (below), and keeps each operand's LDS reads few: 32x32x16 MFMAs (half the
+// operand bytes per flop of 16x16x32), scores kept in registers and fed
+// straight into V^T P^T, Q fragments shared by the score and inter-term
+// products, and double-buffered tiles and state copy behind a single barrier
+// per block (without it, waves that finish early run ahead and starve the
+// busiest one).
 // Contractions over tokens (the state update K^T V and the intra output
 // V^T P^T) need the token index contiguous per lane; they read K and V from
 // their token-major LDS tiles with ds_read_b64_tr_b16 (gfx950 transposing LDS

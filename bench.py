@@ -311,6 +311,23 @@ def measure_varlen(dev, stream, reps, dense_tflops):
     res["short_sequences"] = one(
         lambda: inputs.make_varlen(64, [512] * 512, 128, torch.bfloat16, seed=1006,
                                    init_state=True, device=dev), "short prompts")
+    # the report's pain point (many short packed sub-sequences, §4.1.2)
+    res["many_short_sequences"] = one(
+        lambda: inputs.make_varlen(64, [64] * 4096, 128, torch.bfloat16, seed=1007,
+                                   init_state=True, device=dev), "one block each")
+    # the flash models' 32 heads (§2.1.1, Table 1): 128 column-slice workgroups
+    # fill half of the device, so only very short sequences walk
+    res["flash_heads"] = {
+        "many_short_sequences": one(
+            lambda: inputs.make_varlen(32, [64] * 4096, 128, torch.bfloat16, seed=1008,
+                                       init_state=True, device=dev), "one block each"),
+        "short_sequences": one(
+            lambda: inputs.make_varlen(32, [512] * 512, 128, torch.bfloat16, seed=1009,
+                                       init_state=True, device=dev), "short prompts"),
+        "mixed": one(
+            lambda: inputs.make_varlen(32, inputs.varlen_lengths(262144, 1005), 128,
+                                       torch.bfloat16, seed=1010, init_state=True, device=dev),
+            "seeded log-uniform")}
     return res
 
 
@@ -528,6 +545,21 @@ def measure_sizes(dev, stream, reps):
                      "frac_of_hbm_peak": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del x, st, out
     del flush, sink
+    # the flash models' head count (32 heads of 128, §2.1.1 and Table 1) at
+    # 256K tokens: 128 column-slice workgroups, half of the device
+    B, H, N, d = 1, 32, PREFILL["N"], 128
+    with torch.cuda.stream(stream):
+        x = inputs.make_prefill(B, H, N, d, torch.bfloat16, 1011, False, dev)
+        out = torch.empty_like(x.q)
+        ms = time_launches(stream, lambda: binding.prefill(x.q, x.k, x.v, x.slopes, x.state,
+                                                           out=out), max(reps, 5))
+    fl, by = prefill_flops(B, H, N, d), prefill_bytes(B, H, N, d)
+    res["prefill_256k_flash_heads"] = {
+        "config": f"B{B} H{H} N{N} d{d} bf16, zero state (128 workgroups)",
+        "ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 3),
+        "gbs": round(by / (ms * 1e-3) / 1e9, 1),
+        "frac_of_hbm_peak": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del x, out
     return res
 
 

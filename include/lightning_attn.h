@@ -126,9 +126,13 @@ int la_prefill_varlen_f32(const float *q, const float *k, const float *v, const 
  *   0  one workgroup per (sequence, head, 32 output columns).
  * The walk is used when nseq >= 2, T < 2^31, the sequences are short on
  * average (T / nseq < 8192: longer ones gain more from the hardware balancing
- * a grid of per-sequence workgroups over the compute units) and its H*d/32
- * workgroups fill whole waves of the device's compute units.  Both give the
- * same results, bitwise.  No GPU work is enqueued.  Returns LA_OK; LA_ERR_INVALID_ARG for a
+ * a grid of per-sequence workgroups over the compute units) and a cost
+ * estimate from the sizes and the device's compute-unit count favours it: a
+ * boundary costs the walk about 1.9 block steps and a per-sequence workgroup
+ * about 4.25, while the walk's H*d/32 workgroups may leave compute units idle
+ * (on a 256-unit MI355X: always at 64 heads and d = 128, at 32 heads only for
+ * sequences of about two blocks or less, never at 16).  Both give the same
+ * results, bitwise.  No GPU work is enqueued.  Returns LA_OK; LA_ERR_INVALID_ARG for a
  * null walks, nseq or H below 1 or T below 0; LA_ERR_UNSUPPORTED for d other
  * than 64 or 128.  Source: as la_prefill_varlen (many short sequences packed
  * into one launch, §4.1.2).

@@ -72,6 +72,7 @@
 #include "la_internal.h"
 
 #include <atomic>
+#include <cmath>
 #include <type_traits>
 
 namespace la {
@@ -983,21 +984,39 @@ int device_cus()
 int64_t prefill_bf16_grid(int64_t seqs, int64_t H, int d) { return seqs * H * (d / PJ); }
 
 // A packed launch walks its sequences inside one workgroup per (head, column
-// slice) when the sequences are short on average (below WALK_MEAN_LEN tokens:
-// the walk saves each (sequence, head, slice) its own pipeline fill and drain,
-// while a grid of one workgroup per (sequence, head, slice) lets the hardware
-// balance long sequences over the compute units as workgroups finish), when
-// those workgroups fill whole waves of the device's compute units (every
-// workgroup then does the same work: all tokens of its head) and when the
-// offsets fit the walk's table (fewer than 2^31 tokens; batches of more than
-// WALK_SEQS sequences are walked WALK_SEQS at a time, one launch each).
+// slice) when that is estimated to be faster than a grid of one workgroup per
+// (sequence, head, slice), and the sequences are short on average (below
+// WALK_MEAN_LEN tokens: longer ones gain from the hardware balancing the grid
+// over the compute units as workgroups finish) and the offsets fit the walk's
+// table (fewer than 2^31 tokens; batches of more than WALK_SEQS sequences are
+// walked WALK_SEQS at a time, one launch each).  The estimate, in units of
+// one 64-token block step of a full device, from measured launches (H = 16 ..
+// 64, 64 .. 512 tokens per sequence and mixed lengths at 256K tokens):
+//   walk: rounds * (T/64 + 1.9 nseq) * (0.6 + 0.4 occupancy), where rounds is
+//         the number of device-fills its H * d/32 workgroups take, occupancy
+//         the share of those rounds' compute units they use (a block step
+//         is that much shorter on a partly idle device), and 1.9 blocks per
+//         sequence the hand-over at a boundary plus the partial last block;
+//   grid: (H * d/32 / CUs) * (T/64 + 4.25 nseq), 4.25 blocks per sequence
+//         being each workgroup's pipeline fill and drain plus its block count
+//         rounded up to the producers' four-block unroll.
+// So at 64 heads (one full device) the walk wins for every short mean
+// length, at 32 heads only below about two blocks per sequence (the grid then
+// uses the whole device), and at 16 heads never.
 constexpr int64_t WALK_MEAN_LEN = 8192;
 
 bool prefill_bf16_walks(int64_t seqs, int64_t H, int64_t T, int d, bool packed)
 {
     if (!packed || seqs < 2 || T > 0x7fffffff || T / seqs >= WALK_MEAN_LEN) return false;
     const int cus = device_cus();
-    return cus > 0 && (H * (d / PJ)) % cus == 0;
+    if (cus <= 0) return false;
+    const double wg = (double)H * (d / PJ);
+    const double rounds = std::ceil(wg / cus);
+    const double occupancy = wg / (rounds * cus);
+    const double blocks = (double)T / PC, n = (double)seqs;
+    const double walk = rounds * (blocks + 1.9 * n) * (0.6 + 0.4 * occupancy);
+    const double grid = wg / cus * (blocks + 4.25 * n);
+    return walk < grid;
 }
 
 template <bool WALK>

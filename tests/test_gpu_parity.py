@@ -90,6 +90,14 @@ def test_prefill_256k_all_heads():
     assert worst_o <= BF16_GUARD and worst_s <= BF16_GUARD, "precision regression"
 
 
+def test_prefill_flash_heads_32k():
+    # the flash models' 32 heads of 128 (report §2.1.1, Table 1): 128 column-slice
+    # workgroups on a 256-CU device, a long sequence from a random initial state
+    log("prefill flash heads: B1 H32 N32768 d128 bf16 + fp32 initial state")
+    inp = inputs.make_prefill(1, 32, 32768, 128, torch.bfloat16, 1012, init_state=True, device=DEV)
+    check_prefill(inp, BF16_TOL, what="flash heads 32K", guard=BF16_GUARD)
+
+
 def test_decode_b256_64_steps():
     log("decode_b256: B256 H64 d128, 64 steps")
     inp = inputs.make_workload("decode_b256", device=DEV)

@@ -1,8 +1,10 @@
-"""GPU checks of the packed prefill's sequence walk: with H * d / 32
-workgroups filling whole waves of the compute units (H = 64 at d = 128,
-H = 128 at d = 64 on a 256-CU MI355X) one workgroup per (head, 32 output
-columns) runs every sequence of the batch in order, handing each sequence's
-final state out and the next one's initial state in at the boundaries.
+"""GPU checks of the packed prefill's sequence walk: one workgroup per (head,
+32 output columns) runs every sequence of the batch in order, handing each
+sequence's final state out and the next one's initial state in at the
+boundaries.  On a 256-CU MI355X it is taken for short sequences at H = 64
+(d = 128) and H = 128 (d = 64), whose workgroups fill the device, and at
+H = 32 (the flash models' head count, half the device) for sequences of
+about two blocks or less.
 Checked against the fp64 packed oracle (bf16 bar 2e-2) and bitwise against
 launches over each sequence alone (which never walk), with empty, one-token,
 one-block and back-to-back one-block sequences, and through the strided call."""
@@ -18,6 +20,7 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 HEADS = {128: 64, 64: 128}          # heads that make the walk fill 256 compute units
+SHAPES = [(128, 64), (128, 32), (64, 128)]   # (d, H); H = 32 walks short sequences only
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -55,15 +58,17 @@ CASES = {
     "one_block_runs": [64, 1, 64, 2, 64, 64, 3, 64],          # a boundary at every block
     "edges_empty": [0, 0, 100, 0, 0],
     "two": [5, 700],
+    # many short prompts (the report's §4.1.2 pain point), 0..120 tokens
+    "short_many": [int(n) for n in np.random.default_rng(664).integers(0, 121, size=300)],
 }
 
 
-@pytest.mark.parametrize("d", [128, 64])
+@pytest.mark.parametrize("d,H", SHAPES)
 @pytest.mark.parametrize("case", sorted(CASES))
-def test_walk_matches_oracle_and_per_sequence_launches(case, d):
-    lens, H = CASES[case], HEADS[d]
+def test_walk_matches_oracle_and_per_sequence_launches(case, d, H):
+    lens = CASES[case]
     need_walk(len(lens), H, sum(lens), d)
-    log(f"walk {case} {lens} H{H} d{d} bf16")
+    log(f"walk {case} {lens[:12]}{'...' if len(lens) > 12 else ''} ({len(lens)}) H{H} d{d} bf16")
     x = inputs.make_varlen(H, lens, d, torch.bfloat16, seed=600 + d + len(case), init_state=True,
                            device=DEV)
     st = x.states.clone()
@@ -92,10 +97,9 @@ def test_walk_matches_oracle_and_per_sequence_launches(case, d):
     assert eo <= BF16_TOL and es <= BF16_TOL
 
 
-@pytest.mark.parametrize("d", [128, 64])
-def test_walk_strided_bitwise_equals_contiguous(d):
-    lens = CASES["mixed"]
-    H = HEADS[d]
+@pytest.mark.parametrize("d,H", SHAPES)
+def test_walk_strided_bitwise_equals_contiguous(d, H):
+    lens = CASES["mixed"] if H * d // 32 >= 256 else CASES["one_block_runs"]
     need_walk(len(lens), H, sum(lens), d)
     log(f"walk through la_prefill_varlen_strided {lens} H{H} d{d}")
     x = inputs.make_varlen(H, lens, d, torch.bfloat16, seed=661 + d, init_state=True, device=DEV)

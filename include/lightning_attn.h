@@ -79,6 +79,39 @@ int la_prefill(const void *q, const void *k, const void *v, const float *slopes,
                void *out, float *state,
                int64_t B, int64_t H, int64_t N, int64_t d, void *stream);
 
+/*
+ * Dense bf16 prefill that may use the whole device when its grid would not:
+ * with B = 1 and H * d/32 column-slice workgroups filling at most half of the
+ * compute units, each head's sequence is cut into S = CUs / (H * d/32)
+ * segments (each at least 16384 tokens, at most 64 of them) that run in one
+ * launch, the first from the caller's state and the others from zero; the
+ * segments' states are then chained into the state at each boundary and the
+ * final state, and each later segment's outputs are corrected with the state
+ * at its start (o_a += lambda^(a+1) q_a S for its local token index a).  This
+ * is the report's context-parallel decomposition (§4.1.1, Fig. 10: local
+ * output and local state per piece, joined through the carried state) run on
+ * one device.  Same semantics and argument rules as la_prefill; results equal
+ * la_prefill's within rounding (the later segments' outputs are rounded to
+ * bf16 once more).  Tokens whose factor lambda^(a+1) is exactly 0 in fp32 get
+ * no correction work.
+ *   la_prefill_workspace_bytes: the workspace bytes la_prefill_ws needs for
+ *     these sizes on the calling thread's current device, written to *bytes;
+ *     0 means no split (la_prefill_ws then runs exactly as la_prefill and
+ *     ignores the workspace).  LA_ERR_INVALID_ARG for a null bytes, B or H
+ *     below 1 or N below 0; LA_ERR_UNSUPPORTED for d other than 64 or 128.
+ *     Enqueues nothing.
+ *   la_prefill_ws: workspace is device memory of at least that many bytes,
+ *     256-byte aligned, owned by the caller, not overlapping any argument; its
+ *     contents on entry do not matter and are unspecified afterwards.  Calls
+ *     that share a workspace must be ordered (one stream).  LA_ERR_INVALID_ARG
+ *     also for a workspace that is null, smaller than needed, misaligned or
+ *     overlapping, when a split is planned.
+ */
+int la_prefill_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t *bytes);
+int la_prefill_ws(const void *q, const void *k, const void *v, const float *slopes,
+                  void *out, float *state, int64_t B, int64_t H, int64_t N, int64_t d,
+                  void *workspace, int64_t workspace_bytes, void *stream);
+
 /* Prefill with fp32 activations: same semantics, q, k, v, out are float. */
 int la_prefill_f32(const float *q, const float *k, const float *v, const float *slopes,
                    float *out, float *state,
@@ -354,7 +387,7 @@ const char *la_status_string(int status);
 /* ABI version of this header (incremented on incompatible changes). */
 int la_abi_version(void);
 
-#define LA_ABI_VERSION 3
+#define LA_ABI_VERSION 4
 
 #ifdef __cplusplus
 }

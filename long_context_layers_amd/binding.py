@@ -25,6 +25,8 @@ _P, _I64, _INT = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
 SIGNATURES = {
     "la_prefill": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], _INT),
     "la_prefill_f32": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], _INT),
+    "la_prefill_workspace_bytes": ([_I64, _I64, _I64, _I64, ctypes.POINTER(_I64)], _INT),
+    "la_prefill_ws": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _I64, _P], _INT),
     "la_prefill_varlen": ([_P, _P, _P, _P, _P, _I64, _P, _P, _I64, _I64, _I64, _P], _INT),
     "la_prefill_varlen_f32": ([_P, _P, _P, _P, _P, _I64, _P, _P, _I64, _I64, _I64, _P], _INT),
     "la_prefill_strided": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64,
@@ -48,7 +50,7 @@ SIGNATURES = {
     "la_prefill_varlen_plan": ([_I64, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_int)], _INT),
     "la_abi_version": ([], _INT),
 }
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 _lock = threading.Lock()
 _lib = None
@@ -172,12 +174,34 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: torch.Ten
     else:
         _need(out, "out", dt, dev, (B, H, N, d))
     lib = load_library()
+    if dt == torch.bfloat16:
+        ws = prefill_workspace_bytes(B, H, N, d, dev)
+        if ws > 0:
+            # the sequence split over the whole device (la_prefill_ws); the
+            # workspace comes from torch's caching allocator
+            work = torch.empty(ws, dtype=torch.uint8, device=dev)
+            with torch.cuda.device(dev):
+                rc = lib.la_prefill_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), slopes.data_ptr(),
+                                       out.data_ptr(), state.data_ptr(), B, H, N, d,
+                                       work.data_ptr(), ws, _stream(dev))
+            _check(rc, "la_prefill_ws")
+            return out
     fn = lib.la_prefill if dt == torch.bfloat16 else lib.la_prefill_f32
     with torch.cuda.device(dev):
         rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), slopes.data_ptr(), out.data_ptr(),
                 state.data_ptr(), B, H, N, d, _stream(dev))
     _check(rc, "la_prefill" if dt == torch.bfloat16 else "la_prefill_f32")
     return out
+
+
+def prefill_workspace_bytes(B: int, H: int, N: int, d: int, device=None) -> int:
+    """Workspace bytes la_prefill_ws needs for a dense bf16 prefill of these
+    sizes on `device` (0: no sequence split, la_prefill is used)."""
+    n = ctypes.c_int64(0)
+    with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+        rc = load_library().la_prefill_workspace_bytes(B, H, N, d, ctypes.byref(n))
+    _check(rc, "la_prefill_workspace_bytes")
+    return int(n.value)
 
 
 def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: torch.Tensor,

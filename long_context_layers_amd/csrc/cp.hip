@@ -77,22 +77,29 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t *base
                                              (int)(c * D * 2), RSRC_W3);
 }
 
-// A workgroup corrects CTOK tokens of one (b, h) in 64-token tiles.  q and
-// out tiles move between HBM and LDS as whole rows (thread i takes 16-byte
-// chunks i, i + 256, ...: every load or store instruction covers 4 KB of
-// consecutive rows), the next tile's loads are issued before the current
-// tile's products, and the read-modify-write of out happens in LDS.
+// A workgroup corrects CTOK tokens of one (segment, b, h) in 64-token tiles.
+// q and out tiles move between HBM and LDS as whole rows (thread i takes
+// 16-byte chunks i, i + 256, ...: every load or store instruction covers 4 KB
+// of consecutive rows), the next tile's loads are issued before the current
+// tile's products, and the read-modify-write of out happens in LDS.  A tile
+// whose first token's factor lambda^(a+1) has underflowed to exactly 0 in
+// fp32 adds nothing, nor does any tile after it (the factor only falls), so
+// the workgroup stops there: with decays below 1 the correction is confined
+// to the first tokens of the segment, and nothing about the result changes.
 // Products: O^T = S^T Q^T with v_mfma_f32_32x32x16_bf16; wave w owns output
 // columns 32 (w % NCT) .. +31 for the token halves w / NCT, w / NCT + 4 / NCT,
 // ...; A = S^T (row j = lane % 32, k = 8 (lane / 32) + e of each 16-wide k
 // step, read once from the fp32 state, rounded to bf16, kept in registers),
 // B = Q^T (column = token lane % 32: 16 contiguous bytes of its q row), C
 // register r = column 8 (r / 4) + 4 (lane / 32) + r % 4 of token lane % 32.
+// Segments: segment g of a (b, h) row covers tokens t_off + g * seg .. (up to
+// the row's ntok tokens, hs elements between (b, h) rows) and takes the state
+// s_in + (g * BH + bh) * D * D.  A shard correction is one segment at t_off = 0.
 template <int D>
 __global__ __launch_bounds__(CT) void cp_correct_kernel(
     const uint16_t *__restrict__ q, const float *__restrict__ slopes,
-    const float *__restrict__ s_in, uint16_t *__restrict__ out, int64_t H, int64_t L,
-    int64_t chunks)
+    const float *__restrict__ s_in, uint16_t *__restrict__ out, int64_t H, int64_t BH,
+    int64_t hs, int64_t t_off, int64_t seg, int64_t ntok, int64_t chunks)
 {
     constexpr int NCT = D / 32;        // 32-column tiles
     constexpr int KS = D / 16;         // 16-wide k steps
@@ -102,10 +109,19 @@ __global__ __launch_bounds__(CT) void cp_correct_kernel(
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
     const int l32 = lane % 32, hf = lane / 32;
     const int ct = wave % NCT;
-    const int64_t bh = blockIdx.x / chunks, chunk = blockIdx.x % chunks;
+    const int64_t chunk = blockIdx.x % chunks, bh = (blockIdx.x / chunks) % BH;
+    const int64_t g = blockIdx.x / chunks / BH;
     const float s = slopes[bh % H];
 
-    const float *S = s_in + bh * D * D;
+    const int64_t a0 = t_off + g * seg;                       // the segment's first token
+    const int64_t L = max((int64_t)0, min(seg, ntok - a0));   // its tokens
+    const int64_t tbeg = chunk * CTOK;
+    int ntile = (int)((min(L, tbeg + CTOK) - tbeg + TT - 1) / TT);
+    for (int it = 0; it < ntile; ++it)                        // tiles before the underflow
+        if (decay_pow(s, (int)(tbeg + (int64_t)it * TT + 1)) == 0.0f) { ntile = it; break; }
+    if (ntile <= 0) return;
+
+    const float *S = s_in + (g * BH + bh) * D * D;
     bf16x8 a[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
@@ -113,10 +129,8 @@ __global__ __launch_bounds__(CT) void cp_correct_kernel(
         for (int e = 0; e < 8; ++e)
             a[ks][e] = (__bf16)S[(16 * ks + 8 * hf + e) * D + 32 * ct + l32];
 
-    const uint16_t *qb = q + bh * L * D;
-    uint16_t *ob = out + bh * L * D;
-    const int64_t tbeg = chunk * CTOK;
-    const int ntile = (int)((min(L, tbeg + CTOK) - tbeg + TT - 1) / TT);
+    const uint16_t *qb = q + bh * hs + a0 * D;
+    uint16_t *ob = out + bh * hs + a0 * D;
 
     uint4 rq[NCH], ro[NCH];
     auto fetch = [&](int64_t t0) {
@@ -152,13 +166,13 @@ __global__ __launch_bounds__(CT) void cp_correct_kernel(
                     0, 0, 0);
             const float sc = decay_pow(s, (int)(t0 + row + 1));
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                uint2 *p = reinterpret_cast<uint2 *>(&sm.O[row][32 * ct + 8 * g + 4 * hf]);
+            for (int gq = 0; gq < 4; ++gq) {
+                uint2 *p = reinterpret_cast<uint2 *>(&sm.O[row][32 * ct + 8 * gq + 4 * hf]);
                 uint2 w = *p;
-                const float o0 = fmaf(sc, acc[4 * g + 0], bf16_to_f32(w.x & 0xffffu));
-                const float o1 = fmaf(sc, acc[4 * g + 1], bf16_to_f32(w.x >> 16));
-                const float o2 = fmaf(sc, acc[4 * g + 2], bf16_to_f32(w.y & 0xffffu));
-                const float o3 = fmaf(sc, acc[4 * g + 3], bf16_to_f32(w.y >> 16));
+                const float o0 = fmaf(sc, acc[4 * gq + 0], bf16_to_f32(w.x & 0xffffu));
+                const float o1 = fmaf(sc, acc[4 * gq + 1], bf16_to_f32(w.x >> 16));
+                const float o2 = fmaf(sc, acc[4 * gq + 2], bf16_to_f32(w.y & 0xffffu));
+                const float o3 = fmaf(sc, acc[4 * gq + 3], bf16_to_f32(w.y >> 16));
                 w.x = pack_bf16x2(o0, o1);
                 w.y = pack_bf16x2(o2, o3);
                 *p = w;
@@ -172,6 +186,45 @@ __global__ __launch_bounds__(CT) void cp_correct_kernel(
             const uint4 x = *reinterpret_cast<const uint4 *>(&sm.O[row][col]);
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x), rst, c * 16, 0, 0);
         }
+    }
+}
+
+// ---- the sequence split of a prefill whose grid fills at most half the
+// device: S segments of each (b = 0, h) row run as one packed launch, the first
+// from the caller's state and the others from zero; then the states are
+// chained and the later segments' outputs corrected (the same fold and
+// correction as the sharded prefill, here on one device).
+
+// slot 0 <- the caller's state, slots 1.. <- 0, cu <- the segment offsets
+__global__ __launch_bounds__(FT) void split_prep_kernel(
+    const f32x4 *__restrict__ state, f32x4 *__restrict__ slots, int64_t *__restrict__ cu,
+    int64_t n4, int nseg, int64_t seg, int64_t ntok)
+{
+    const int64_t i0 = blockIdx.x * (int64_t)FT + threadIdx.x;
+    if (i0 <= nseg) cu[i0] = min(i0 * seg, ntok);
+    for (int64_t i = i0; i < n4 * nseg; i += (int64_t)gridDim.x * FT)
+        slots[i] = i < n4 ? state[i] : f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// slot g <- lambda^len(g) slot(g-1) + slot g for g = 1 .. nseg-1 (each slot
+// then holds the state at the end of its segment), and the caller's state <-
+// the last; one thread per 4 elements, a fixed order (deterministic)
+__global__ __launch_bounds__(FT) void split_fold_kernel(
+    f32x4 *__restrict__ slots, f32x4 *__restrict__ state, const float *__restrict__ slopes,
+    int64_t n4, int64_t slice4, int64_t H, int nseg, int64_t seg, int64_t ntok)
+{
+    for (int64_t i = blockIdx.x * (int64_t)FT + threadIdx.x; i < n4;
+         i += (int64_t)gridDim.x * FT) {
+        const float s = slopes[(i / slice4) % H];
+        f32x4 acc = slots[i];
+        for (int g = 1; g < nseg; ++g) {
+            const float lam = decay_pow(s, (int)min(seg, ntok - g * seg));
+            const f32x4 x = slots[g * n4 + i];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = fmaf(lam, acc[e], x[e]);
+            slots[g * n4 + i] = acc;
+        }
+        state[i] = acc;
     }
 }
 
@@ -200,17 +253,75 @@ hipError_t launch_cp_fold(const float *loc, const int *lens, int nfold, const fl
     return hipLaunchKernel((const void *)cp_fold_kernel, grid, block, args, 0, stream);
 }
 
+static hipError_t launch_correct(const uint16_t *q, const float *slopes, const float *s_in,
+                                 uint16_t *out, int64_t BH, int64_t H, int64_t hs, int64_t t_off,
+                                 int64_t seg, int64_t ntok, int64_t nseg, int d,
+                                 hipStream_t stream)
+{
+    int64_t chunks = (seg + CTOK - 1) / CTOK;
+    const dim3 grid((unsigned)(nseg * BH * chunks)), block(CT);
+    void *args[] = {(void *)&q, (void *)&slopes, (void *)&s_in, (void *)&out, (void *)&H,
+                    (void *)&BH, (void *)&hs, (void *)&t_off, (void *)&seg, (void *)&ntok,
+                    (void *)&chunks};
+    const void *fn = d == 64 ? (const void *)cp_correct_kernel<64>
+                             : (const void *)cp_correct_kernel<128>;
+    return hipLaunchKernel(fn, grid, block, args, 0, stream);
+}
+
 hipError_t launch_cp_correct(const uint16_t *q, const float *slopes, const float *s_in,
                              uint16_t *out, int64_t B, int64_t H, int64_t L, int d,
                              hipStream_t stream)
 {
-    int64_t chunks = (L + CTOK - 1) / CTOK;
-    const dim3 grid((unsigned)cp_correct_grid(B, H, L)), block(CT);
-    void *args[] = {(void *)&q, (void *)&slopes, (void *)&s_in, (void *)&out, (void *)&H,
-                    (void *)&L, (void *)&chunks};
-    const void *fn = d == 64 ? (const void *)cp_correct_kernel<64>
-                             : (const void *)cp_correct_kernel<128>;
-    return hipLaunchKernel(fn, grid, block, args, 0, stream);
+    return launch_correct(q, slopes, s_in, out, B * H, H, L * d, 0, L, L, 1, d, stream);
+}
+
+int64_t split_workspace_bytes(int64_t H, int nseg, int d)
+{
+    return nseg < 2 ? 0 : (int64_t)nseg * H * d * d * 4 + ((nseg + 1) * 8 + 255) / 256 * 256;
+}
+
+hipError_t launch_prefill_bf16_split(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                     const float *slopes, uint16_t *out, float *state,
+                                     int64_t H, int64_t N, int d, int nseg, void *workspace,
+                                     hipStream_t stream)
+{
+    // workspace: nseg state slots [nseg][H][d][d] fp32, then nseg + 1 offsets
+    float *slots = static_cast<float *>(workspace);
+    int64_t *cu = reinterpret_cast<int64_t *>(slots + (int64_t)nseg * H * d * d);
+    int64_t seg = (N + nseg - 1) / nseg;
+    seg = (seg + 63) / 64 * 64;                          // segments start on 64-token blocks
+    const int64_t slice4 = (int64_t)d * d / 4, n4 = H * slice4;
+    f32x4 *s4 = reinterpret_cast<f32x4 *>(slots);
+    f32x4 *st4 = reinterpret_cast<f32x4 *>(state);
+    const dim3 block(FT);
+    {
+        const int64_t blocks = (n4 * nseg + FT - 1) / FT;
+        const dim3 grid((unsigned)(blocks < FMAX_GRID ? blocks : FMAX_GRID));
+        const f32x4 *in4 = st4;
+        int64_t nn = n4, sg = seg, nt = N;
+        int ns = nseg;
+        void *args[] = {(void *)&in4, (void *)&s4, (void *)&cu, (void *)&nn, (void *)&ns,
+                        (void *)&sg, (void *)&nt};
+        const hipError_t e = hipLaunchKernel((const void *)split_prep_kernel, grid, block, args, 0,
+                                             stream);
+        if (e != hipSuccess) return e;
+    }
+    const Strides st = {0, N * d, d};
+    const SeqMap map = {cu, H, 0, N, st, st};
+    hipError_t e = launch_prefill_bf16_nowalk(q, k, v, slopes, out, slots, nseg, map, d, stream);
+    if (e != hipSuccess) return e;
+    {
+        const int64_t blocks = (n4 + FT - 1) / FT;
+        const dim3 grid((unsigned)(blocks < FMAX_GRID ? blocks : FMAX_GRID));
+        int64_t nn = n4, sl = slice4, hh = H, sg = seg, nt = N;
+        int ns = nseg;
+        void *args[] = {(void *)&s4, (void *)&st4, (void *)&slopes, (void *)&nn, (void *)&sl,
+                        (void *)&hh, (void *)&ns, (void *)&sg, (void *)&nt};
+        e = hipLaunchKernel((const void *)split_fold_kernel, grid, block, args, 0, stream);
+        if (e != hipSuccess) return e;
+    }
+    // segment g >= 1 is corrected with slot g - 1 (the state at its start)
+    return launch_correct(q, slopes, slots, out, H, H, N * d, seg, seg, N, nseg - 1, d, stream);
 }
 
 }  // namespace la

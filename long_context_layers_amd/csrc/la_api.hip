@@ -281,6 +281,38 @@ int la_prefill(const void *q, const void *k, const void *v, const float *slopes,
         (int)d, static_cast<hipStream_t>(stream)));
 }
 
+int la_prefill_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t *bytes)
+{
+    if (!bytes || B < 1 || H < 1 || N < 0) return LA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
+    const int nseg = la::prefill_split_segments(B, H, N, (int)d);
+    *bytes = la::split_workspace_bytes(H, nseg, (int)d);
+    return LA_OK;
+}
+
+int la_prefill_ws(const void *q, const void *k, const void *v, const float *slopes, void *out,
+                  float *state, int64_t B, int64_t H, int64_t N, int64_t d, void *workspace,
+                  int64_t workspace_bytes, void *stream)
+{
+    const int rc = check_prefill(q, k, v, slopes, out, state, B, H, N, d, 2);
+    if (rc != LA_OK) return rc;
+    const int nseg = la::prefill_split_segments(B, H, N, (int)d);
+    if (nseg < 2) return la_prefill(q, k, v, slopes, out, state, B, H, N, d, stream);
+    const int64_t need = la::split_workspace_bytes(H, nseg, (int)d);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return LA_ERR_INVALID_ARG;
+    const uint64_t act = (uint64_t)B * H * N * d * 2, st = (uint64_t)B * H * d * d * 4;
+    if (overlap(workspace, need, q, act) || overlap(workspace, need, k, act) ||
+        overlap(workspace, need, v, act) || overlap(workspace, need, out, act) ||
+        overlap(workspace, need, state, st) || overlap(workspace, need, slopes, H * 4))
+        return LA_ERR_INVALID_ARG;
+    if (la::prefill_bf16_grid(nseg, H, (int)d) > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+    return hip_status(la::launch_prefill_bf16_split(
+        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+        static_cast<const uint16_t *>(v), slopes, static_cast<uint16_t *>(out), state, H, N,
+        (int)d, nseg, workspace, static_cast<hipStream_t>(stream)));
+}
+
 int la_prefill_varlen(const void *q, const void *k, const void *v, const float *slopes,
                       const int64_t *cu_seqlens, int64_t nseq, void *out, float *states,
                       int64_t H, int64_t T, int64_t d, void *stream)

@@ -102,6 +102,20 @@ hipError_t launch_cp_correct(const uint16_t *q, const float *slopes, const float
                              hipStream_t stream);
 int64_t cp_correct_grid(int64_t B, int64_t H, int64_t L);
 
+// one workgroup per (sequence, head, column slice): never the packed walk
+hipError_t launch_prefill_bf16_nowalk(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                      const float *slopes, uint16_t *out, float *state,
+                                      int64_t seqs, const SeqMap &map, int d, hipStream_t stream);
+// the sequence split of a dense B = 1 prefill whose grid fills at most half
+// of the device: segments per row (1 = no split) on the current device, the
+// workspace it needs, and the launches (prep, packed prefill, fold, correct)
+int prefill_split_segments(int64_t B, int64_t H, int64_t N, int d);
+int64_t split_workspace_bytes(int64_t H, int nseg, int d);
+hipError_t launch_prefill_bf16_split(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                     const float *slopes, uint16_t *out, float *state,
+                                     int64_t H, int64_t N, int d, int nseg, void *workspace,
+                                     hipStream_t stream);
+
 // number of workgroups one prefill launch over `seqs` sequences uses
 int64_t prefill_bf16_grid(int64_t seqs, int64_t H, int d);
 // whether a packed launch over seqs sequences (T tokens) walks them in one

@@ -71,6 +71,7 @@
 // r0 .. r0 + 3: a k-contiguous MFMA operand for a contraction over rows.
 #include "la_internal.h"
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <type_traits>
@@ -1029,21 +1030,48 @@ const void *prefill_fn(int d, bool strided)
                    : (const void *)prefill_bf16_kernel<128, false, WALK>;
 }
 
+// A dense launch over B = 1 whose grid fills at most half of the device runs
+// as S >= 2 segments of the sequence at once (one packed launch, the later
+// segments from a zero state, then the fold of the states and the correction
+// of the later segments' outputs): S = CUs / (H * d/32) workgroup sets, each
+// segment at least SPLIT_MIN_LEN tokens, at most MAX_SPLIT segments.
+constexpr int64_t SPLIT_MIN_LEN = 16384;
+constexpr int MAX_SPLIT = 64;
+
+int prefill_split_segments(int64_t B, int64_t H, int64_t N, int d)
+{
+    if (B != 1 || H < 1 || N < 2 * SPLIT_MIN_LEN) return 1;
+    const int cus = device_cus();
+    const int64_t wg = H * (d / PJ);
+    int64_t S = cus > 0 ? cus / wg : 1;
+    S = std::min<int64_t>(S, N / SPLIT_MIN_LEN);
+    S = std::min<int64_t>(S, MAX_SPLIT);
+    return S >= 2 ? (int)S : 1;
+}
+
+// one workgroup per (sequence, head, column slice), never the walk
+hipError_t launch_prefill_bf16_nowalk(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                                      const float *slopes, uint16_t *out, float *state,
+                                      int64_t seqs, const SeqMap &map, int d, hipStream_t stream)
+{
+    const bool strided = map.in.st != d || map.out.st != d;
+    SeqMap m = map;
+    int64_t nseq = seqs;
+    void *args[] = {(void *)&q, (void *)&k, (void *)&v, (void *)&slopes,
+                    (void *)&out, (void *)&state, (void *)&m, (void *)&nseq};
+    return hipLaunchKernel(prefill_fn<false>(d, strided),
+                           dim3((unsigned)prefill_bf16_grid(seqs, map.H, d)), dim3(NTHREADS), args,
+                           0, stream);
+}
+
 hipError_t launch_prefill_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                const float *slopes, uint16_t *out, float *state,
                                int64_t seqs, const SeqMap &map, int d, hipStream_t stream)
 {
     const bool strided = map.in.st != d || map.out.st != d;
     const dim3 block(NTHREADS);
-    if (!prefill_bf16_walks(seqs, map.H, map.T, d, map.cu != nullptr)) {
-        SeqMap m = map;
-        int64_t nseq = seqs;
-        void *args[] = {(void *)&q, (void *)&k, (void *)&v, (void *)&slopes,
-                        (void *)&out, (void *)&state, (void *)&m, (void *)&nseq};
-        return hipLaunchKernel(prefill_fn<false>(d, strided),
-                               dim3((unsigned)prefill_bf16_grid(seqs, map.H, d)), block, args, 0,
-                               stream);
-    }
+    if (!prefill_bf16_walks(seqs, map.H, map.T, d, map.cu != nullptr))
+        return launch_prefill_bf16_nowalk(q, k, v, slopes, out, state, seqs, map, d, stream);
     for (int64_t s0 = 0; s0 < seqs; s0 += WALK_SEQS) {
         SeqMap m = map;
         m.cu = map.cu + s0;

@@ -512,3 +512,39 @@ def test_varlen_plan_rejects_bad_arguments(lib, nseq, H, T, d, walks_null, code)
     arg = None if walks_null else ctypes.byref(walks)
     assert lib.la_prefill_varlen_plan(nseq, H, T, d, arg) == code
     assert walks.value == 7            # untouched on error
+
+
+def _prefill_ws_args(workspace=None, ws_bytes=0, **kw):
+    a = _prefill_args(**kw)
+    return a[:-1] + [workspace, ws_bytes, a[-1]]
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(slopes=None), LA_ERR_INVALID_ARG), (dict(state=None), LA_ERR_INVALID_ARG),
+    (dict(B=0), LA_ERR_INVALID_ARG), (dict(H=0), LA_ERR_INVALID_ARG),
+    (dict(N=-5), LA_ERR_INVALID_ARG), (dict(d=96), LA_ERR_UNSUPPORTED),
+    (dict(q=FAKE + 2), LA_ERR_INVALID_ARG), (dict(out=FAKE + 8), LA_ERR_INVALID_ARG),
+])
+def test_prefill_ws_rejects_bad_arguments(lib, bad, code):
+    # the workspace prefill takes la_prefill's checks first (N = 0: no launch)
+    assert lib.la_prefill_ws(*_prefill_ws_args(**bad)) == code
+    assert lib.la_prefill_ws(*_prefill_ws_args(N=0)) == LA_OK
+
+
+@pytest.mark.parametrize("B,H,N,d,null,code", [
+    (1, 32, 262144, 128, True, LA_ERR_INVALID_ARG), (0, 32, 1024, 128, False, LA_ERR_INVALID_ARG),
+    (1, 0, 1024, 128, False, LA_ERR_INVALID_ARG), (1, 32, -1, 128, False, LA_ERR_INVALID_ARG),
+    (1, 32, 1024, 96, False, LA_ERR_UNSUPPORTED),
+])
+def test_prefill_workspace_bytes_rejects_bad_arguments(lib, B, H, N, d, null, code):
+    n = ctypes.c_int64(-1)
+    assert lib.la_prefill_workspace_bytes(B, H, N, d, None if null else ctypes.byref(n)) == code
+
+
+@needs_no_gpu
+def test_prefill_workspace_bytes_without_a_device_is_zero(lib):
+    # no device: no compute units to fill, so no split and no workspace
+    for B, H, N in ((1, 32, 262144), (1, 1, 1 << 20), (4, 64, 4096)):
+        n = ctypes.c_int64(-1)
+        assert lib.la_prefill_workspace_bytes(B, H, N, 128, ctypes.byref(n)) == LA_OK
+        assert n.value == 0

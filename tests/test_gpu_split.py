@@ -1,0 +1,120 @@
+"""GPU checks of the dense prefill's sequence split (la_prefill_ws): a B = 1
+launch whose column-slice workgroups fill at most half the device runs S
+segments of each head's sequence at once, chains their states and corrects
+the later segments (the report's §4.1.1 / Fig. 10 decomposition on one
+device).  Checked against the fp64 oracle (outputs and final states, bf16 bar
+2e-2 and the 4e-3 guard) with slow, unit and infinite-slope decays, ragged
+lengths and a random initial state; against the unsplit launch; and the
+workspace rules (too small, null, misaligned) are refused before any launch."""
+import ctypes
+import math
+
+import pytest
+import torch
+
+from long_context_layers_amd import binding, inputs
+from tests.gpu_util import BF16_GUARD, BF16_TOL, log, oracle_prefill, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    binding.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def need_split(B, H, N, d=128):
+    ws = binding.prefill_workspace_bytes(B, H, N, d, DEV)
+    if ws == 0:
+        pytest.skip(f"no split for B{B} H{H} N{N} on this device "
+                    f"({torch.cuda.get_device_properties(0).multi_processor_count} compute units)")
+    return ws
+
+
+def unsplit(inp, state):
+    out = torch.empty_like(inp.q)
+    B, H, N, d = inp.q.shape
+    rc = binding.load_library().la_prefill(inp.q.data_ptr(), inp.k.data_ptr(), inp.v.data_ptr(),
+                                           inp.slopes.data_ptr(), out.data_ptr(), state.data_ptr(),
+                                           B, H, N, d, torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    return out
+
+
+@pytest.mark.parametrize("H,N,slopes", [
+    (32, 40000, None),                                   # 2 segments, ragged, the model's decays
+    (8, 65536 + 77, [0.0, 1e-4, 1e-3, 0.01, 0.1, 1.0, 5.0, math.inf]),   # 4 segments; lambda = 1 .. 0
+    (1, 70000, [1e-4]),                                  # 4 segments, slow decay: full corrections
+])
+def test_split_matches_oracle(H, N, slopes):
+    ws = need_split(1, H, N)
+    inp = inputs.make_prefill(1, H, N, 128, torch.bfloat16, 700 + H, init_state=True, device=DEV)
+    if slopes is not None:
+        inp = inputs.PrefillInputs(inp.q, inp.k, inp.v,
+                                   torch.tensor(slopes, dtype=torch.float32, device=DEV), inp.state)
+    log(f"split prefill B1 H{H} N{N} d128 (workspace {ws} B), slopes {slopes or 'model'}")
+    st = inp.state.clone()
+    out = binding.prefill(inp.q, inp.k, inp.v, inp.slopes, st)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_prefill(inp.q, inp.k, inp.v, inp.slopes, inp.state)
+    eo, es = rel_l2(out, o_ref), rel_l2(st, s_ref)
+    # and the unsplit launch on the same inputs
+    st1 = inp.state.clone()
+    out1 = unsplit(inp, st1)
+    torch.cuda.synchronize()
+    eo1, es1 = rel_l2(out1, o_ref), rel_l2(st1, s_ref)
+    log(f"  split: out {eo:.3e} state {es:.3e}; unsplit: out {eo1:.3e} state {es1:.3e}")
+    assert eo <= BF16_TOL and es <= BF16_TOL
+    assert eo <= BF16_GUARD and es <= BF16_GUARD, "precision regression"
+
+
+def test_split_is_deterministic():
+    H, N = 32, 40000
+    need_split(1, H, N)
+    inp = inputs.make_prefill(1, H, N, 128, torch.bfloat16, 711, init_state=True, device=DEV)
+    st1, st2 = inp.state.clone(), inp.state.clone()
+    o1 = binding.prefill(inp.q, inp.k, inp.v, inp.slopes, st1)
+    o2 = binding.prefill(inp.q, inp.k, inp.v, inp.slopes, st2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(st1, st2)
+
+
+def test_workspace_rules_are_checked_before_any_launch():
+    H, N, d = 32, 40000, 128
+    ws = need_split(1, H, N)
+    inp = inputs.make_prefill(1, H, N, d, torch.bfloat16, 712, init_state=True, device=DEV)
+    out = torch.full_like(inp.q, 3.0)
+    st = inp.state.clone()
+    work = torch.empty(ws + 512, dtype=torch.uint8, device=DEV)
+    lib = binding.load_library()
+    s = torch.cuda.current_stream().cuda_stream
+
+    def call(wp, nb):
+        return lib.la_prefill_ws(inp.q.data_ptr(), inp.k.data_ptr(), inp.v.data_ptr(),
+                                 inp.slopes.data_ptr(), out.data_ptr(), st.data_ptr(), 1, H, N, d,
+                                 wp, nb, s)
+    assert call(None, ws) == 1                          # null workspace
+    assert call(work.data_ptr(), ws - 1) == 1           # too small
+    assert call(work.data_ptr() + 128, ws) == 1         # not 256-byte aligned
+    assert call(out.data_ptr(), ws) == 1                # overlaps out
+    torch.cuda.synchronize()
+    assert bool((out == 3.0).all()) and torch.equal(st, inp.state)   # nothing ran
+    assert call(work.data_ptr(), ws) == 0
+    torch.cuda.synchronize()
+    assert not bool((out == 3.0).all())
+
+
+def test_no_split_when_the_grid_fills_the_device():
+    # 64 heads of 128 fill 256 compute units: la_prefill_ws is la_prefill
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if cus > 256:
+        pytest.skip("a larger device may split 64 heads")
+    assert binding.prefill_workspace_bytes(1, 64, 262144, 128, DEV) == 0
+    assert binding.prefill_workspace_bytes(2, 32, 262144, 128, DEV) == 0
+    assert binding.prefill_workspace_bytes(1, 32, 16384, 128, DEV) == 0     # too short to split

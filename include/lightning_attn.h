@@ -112,6 +112,23 @@ int la_prefill_ws(const void *q, const void *k, const void *v, const float *slop
                   void *out, float *state, int64_t B, int64_t H, int64_t N, int64_t d,
                   void *workspace, int64_t workspace_bytes, void *stream);
 
+/*
+ * la_prefill_ws without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It allocates nothing: when a sequence
+ * split is planned it uses a scratch array of 8 MiB that the library holds on
+ * each device it runs on until the process ends (found on the first call on
+ * that device); a split needing more (only on devices with more than 512
+ * compute units) gives LA_ERR_UNSUPPORTED.  Every call on one device shares
+ * that array and sets up what it reads itself, so calls that overlap on one
+ * device (other streams, other threads) race; order them.  Same semantics,
+ * argument rules and results as la_prefill_ws; LA_ERR_HIP also if the
+ * scratch cannot be found.
+ */
+int la_prefill_noalloc(const void *q, const void *k, const void *v, const float *slopes,
+                       void *out, float *state, int64_t B, int64_t H, int64_t N, int64_t d,
+                       void *stream);
+
 /* Prefill with fp32 activations: same semantics, q, k, v, out are float. */
 int la_prefill_f32(const float *q, const float *k, const float *v, const float *slopes,
                    float *out, float *state,

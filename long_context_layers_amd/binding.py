@@ -27,6 +27,7 @@ SIGNATURES = {
     "la_prefill_f32": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], _INT),
     "la_prefill_workspace_bytes": ([_I64, _I64, _I64, _I64, ctypes.POINTER(_I64)], _INT),
     "la_prefill_ws": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _I64, _P], _INT),
+    "la_prefill_noalloc": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], _INT),
     "la_prefill_varlen": ([_P, _P, _P, _P, _P, _I64, _P, _P, _I64, _I64, _I64, _P], _INT),
     "la_prefill_varlen_f32": ([_P, _P, _P, _P, _P, _I64, _P, _P, _I64, _I64, _I64, _P], _INT),
     "la_prefill_strided": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64,

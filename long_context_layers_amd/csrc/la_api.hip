@@ -6,7 +6,46 @@
 
 #include <stdint.h>
 
+#include <atomic>
+#include <mutex>
+
+// Scratch of the allocation-free prefill (la_prefill_noalloc): one array per
+// device for the life of the process.  In host code `scratch` only stands in
+// for the symbol; the device address comes from hipGetSymbolAddress, looked
+// up once per device with that device current, and is what every launch gets.
+static constexpr int64_t NOALLOC_SCRATCH_BYTES = int64_t(8) << 20;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::atomic<void *> scratch_addr[NOALLOC_MAX_DEVICES];
+std::mutex scratch_mu;
+
+// this device's scratch address (LA_OK), or the failure of the lookup
+int current_device_scratch(void **ptr)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return LA_ERR_HIP;
+    }
+    if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return LA_ERR_UNSUPPORTED;
+    void *p = scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(scratch_mu);
+        p = scratch_addr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+                (void)hipGetLastError();
+                return LA_ERR_HIP;
+            }
+            scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    return LA_OK;
+}
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -311,6 +350,21 @@ int la_prefill_ws(const void *q, const void *k, const void *v, const float *slop
         static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
         static_cast<const uint16_t *>(v), slopes, static_cast<uint16_t *>(out), state, H, N,
         (int)d, nseg, workspace, static_cast<hipStream_t>(stream)));
+}
+
+int la_prefill_noalloc(const void *q, const void *k, const void *v, const float *slopes,
+                       void *out, float *state, int64_t B, int64_t H, int64_t N, int64_t d,
+                       void *stream)
+{
+    const int rc = check_prefill(q, k, v, slopes, out, state, B, H, N, d, 2);
+    if (rc != LA_OK) return rc;
+    const int nseg = la::prefill_split_segments(B, H, N, (int)d);
+    if (nseg < 2) return la_prefill(q, k, v, slopes, out, state, B, H, N, d, stream);
+    if (la::split_workspace_bytes(H, nseg, (int)d) > NOALLOC_SCRATCH_BYTES) return LA_ERR_UNSUPPORTED;
+    void *ws = nullptr;
+    const int rs = current_device_scratch(&ws);
+    if (rs != LA_OK) return rs;
+    return la_prefill_ws(q, k, v, slopes, out, state, B, H, N, d, ws, NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int la_prefill_varlen(const void *q, const void *k, const void *v, const float *slopes,
@@ -644,7 +698,8 @@ const char *la_status_string(int status)
             return "LA_ERR_UNSUPPORTED: head dimension not in {64, 128}, more tokens per "
                    "decode call than supported, a rotary dimension or norm group size the "
                    "kernels do not take, a stride, shard count or length above the "
-                   "supported limit, or grid too large";
+                   "supported limit, a sequence split needing more than the 8 MiB "
+                   "scratch of la_prefill_noalloc, or grid too large";
         case LA_ERR_HIP: return "LA_ERR_HIP: the kernel launch failed";
         default: return "unknown status";
     }

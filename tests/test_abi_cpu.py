@@ -548,3 +548,14 @@ def test_prefill_workspace_bytes_without_a_device_is_zero(lib):
         n = ctypes.c_int64(-1)
         assert lib.la_prefill_workspace_bytes(B, H, N, 128, ctypes.byref(n)) == LA_OK
         assert n.value == 0
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(slopes=None), LA_ERR_INVALID_ARG), (dict(state=None), LA_ERR_INVALID_ARG),
+    (dict(B=0), LA_ERR_INVALID_ARG), (dict(N=-5), LA_ERR_INVALID_ARG),
+    (dict(d=96), LA_ERR_UNSUPPORTED), (dict(q=FAKE + 2), LA_ERR_INVALID_ARG),
+])
+def test_prefill_noalloc_rejects_bad_arguments(lib, bad, code):
+    # the allocation-free prefill takes la_prefill's checks first (N = 0: no launch)
+    assert lib.la_prefill_noalloc(*_prefill_args(**bad)) == code
+    assert lib.la_prefill_noalloc(*_prefill_args(N=0)) == LA_OK

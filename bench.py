@@ -666,6 +666,73 @@ def measured_traffic():
     return float(m_bytes.group(1))
 
 
+def _counter_rows(path):
+    """(kernel name, grid size, value) per dispatch, in dispatch order, from a
+    rocprofv3 --pmc csv (one counter per run), or from every
+    *counter_collection.csv under a directory."""
+    import csv
+    import glob
+    files = [path] if os.path.isfile(path) else sorted(
+        glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True))
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                rows.append((int(r.get("Dispatch_Id") or 0), r["Kernel_Name"],
+                             int(float(r.get("Grid_Size") or 0)), float(r["Counter_Value"])))
+    rows.sort()
+    return [(k, g, v) for _, k, g, v in rows]
+
+
+def write_traffic_summary(fetch, write, copy_fetch, copy_write, commands, out=TRAFFIC_FILE):
+    """The HBM bytes per launch of the headline prefill kernel from FETCH_SIZE
+    and WRITE_SIZE (KiB per dispatch) of a restricted bench run, each scaled by
+    what the same counter reads for a plain device copy of known size; written
+    with the hash of the kernel source the counters belong to."""
+    B, H, N, d = PREFILL["B"], PREFILL["H"], PREFILL["N"], PREFILL["d"]
+    name = "prefill_bf16_kernel<128, false, false>"
+    copy_kib = (1 << 30) / 1024.0
+
+    def per(rows, pick):
+        return [v for k, g, v in rows if pick(k)]
+    is_pre = lambda k: "prefill_bf16_kernel<128, false, false>" in k
+    is_copy = lambda k: "copyBuffer" in k or "copy" in k.lower()
+    f_pre, w_pre = per(_counter_rows(fetch), is_pre), per(_counter_rows(write), is_pre)
+    f_cp, w_cp = per(_counter_rows(copy_fetch), is_copy), per(_counter_rows(copy_write), is_copy)
+    if not (f_pre and w_pre and f_cp and w_cp):
+        raise SystemExit("missing dispatches in the counter files")
+    kf, kw = copy_kib / min(f_cp), copy_kib / min(w_cp)      # KiB counted per KiB moved, inverted
+    steady = lambda xs: xs[len(xs) // 2:]                     # the first dispatches carry earlier dirt
+    fr = sum(steady(f_pre)) / len(steady(f_pre)) * kf * 1024
+    wr = sum(steady(w_pre)) / len(steady(w_pre)) * kw * 1024
+    algo = prefill_bytes(B, H, N, d)
+    lines = [
+        f"HBM traffic of {name} (the launch bench.py times) on the 256K prefill workload",
+        f"(B={B}, H={H}, N={N}, d={d}, bf16, zero initial state), MI355X, rocprofv3 PMC,",
+        "written by `python bench.py --traffic-summary` from the counter files (no value typed by hand).",
+        "",
+        f"kernel_source_sha256_16: {kernel_hash()}   (code with comments and blank space removed)",
+        "",
+        "Commands (one counter per run, from /tmp with TMPDIR=/tmp; the repository at $R):",
+        *["  " + c for c in commands],
+        "",
+        "Raw counters (KiB per dispatch, in dispatch order):",
+        f"  copy 1 GiB  FETCH_SIZE {', '.join('%.0f' % x for x in f_cp)} -> factor {kf:.4f}",
+        f"  copy 1 GiB  WRITE_SIZE {', '.join('%.0f' % x for x in w_cp)} -> factor {kw:.4f}",
+        f"  prefill     FETCH_SIZE {', '.join('%.0f' % x for x in f_pre)}",
+        f"  prefill     WRITE_SIZE {', '.join('%.0f' % x for x in w_pre)}",
+        "",
+        f"Per prefill launch (steady state: the last {len(steady(f_pre))} dispatches averaged, "
+        "calibrated; the counters need a few launches to settle after the inputs are written):",
+        f"  reads  {fr / 1e9:.3f} GB   writes {wr / 1e9:.3f} GB",
+        f"hbm_bytes_per_launch: {fr + wr:.0f}",
+        f"algorithmic_bytes_per_launch: {algo}   (ratio {(fr + wr) / algo:.4f})",
+        ""]
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def cpu_baseline(pre, target_s=12.0):
     """The fp64 oracle on a bounded sample of the prefill workload: groups of
     16 heads over all N tokens, group after group until about ``target_s``
@@ -735,10 +802,19 @@ def main():
     ap.add_argument("--power", action="store_true",
                     help="also sample package power and graphics clock (amd-smi) while the "
                          "prefill, the decode step and the probe kernels run back to back")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="write the prefill's HBM-traffic profile from four rocprofv3 --pmc "
+                         "outputs (files or directories: FETCH_SIZE and WRITE_SIZE of a "
+                         "--no-ceilings --extra-reps 0 run, then of a --copy-only run); no GPU")
+    ap.add_argument("--traffic-commands", nargs="*", default=[],
+                    help="the commands that made those outputs, recorded in the profile")
     ap.add_argument("--extra-reps", type=int, default=5,
                     help="launches timed for the packed-prefill and draft-verification lines "
                          "(0 skips them)")
     args = ap.parse_args()
+    if args.traffic_summary:
+        write_traffic_summary(*args.traffic_summary, commands=args.traffic_commands)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "

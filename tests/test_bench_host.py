@@ -53,3 +53,42 @@ def test_more_than_one_gpu_exits(n):
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def _pmc_csv(path, rows):
+    cols = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id",
+            "Grid_Size", "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size",
+            "Scratch_Size", "VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "Counter_Name",
+            "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    with open(path, "w") as f:
+        f.write(",".join(f'"{c}"' for c in cols) + "\n")
+        for i, (name, val) in enumerate(rows):
+            r = dict.fromkeys(cols, "0")
+            r.update(Dispatch_Id=str(i + 1), Kernel_Name=name, Grid_Size="131072",
+                     Counter_Name="X", Counter_Value=str(val))
+            f.write(",".join(f'"{r[c]}"' for c in cols) + "\n")
+
+
+def test_traffic_summary_is_calibrated_and_keyed_by_the_source(tmp_path, monkeypatch):
+    # made-up counters: the copy reads count twice (factor 1/2), writes once;
+    # the prefill's steady dispatches (3..) read 6,000,000 KiB and write 4,000,000
+    pre = "void la::(anonymous namespace)::prefill_bf16_kernel<128, false, false>(...)"
+    cp = "__amd_rocclr_copyBuffer"
+    gib = 1 << 20
+    _pmc_csv(tmp_path / "f.csv", [(pre, 7e6), (pre, 6.5e6), (pre, 6e6), (pre, 6e6)])
+    _pmc_csv(tmp_path / "w.csv", [(pre, 4.5e6), (pre, 4.1e6), (pre, 4e6), (pre, 4e6)])
+    _pmc_csv(tmp_path / "cf.csv", [(cp, 2 * gib), (cp, 2 * gib + 10)])
+    _pmc_csv(tmp_path / "cw.csv", [(cp, gib), (cp, gib)])
+    out = tmp_path / "traffic.txt"
+    bench.write_traffic_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"),
+                                str(tmp_path / "cf.csv"), str(tmp_path / "cw.csv"),
+                                ["rocprofv3 ..."], out=str(out))
+    text = out.read_text()
+    assert f"kernel_source_sha256_16: {bench.kernel_hash()}" in text
+    want = (6e6 / 2 + 4e6) * 1024
+    assert f"hbm_bytes_per_launch: {want:.0f}" in text
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
+    assert bench.measured_traffic() == pytest.approx(want)
+    # a profile keyed by another source is not used
+    out.write_text(text.replace(bench.kernel_hash(), "0" * 16))
+    assert bench.measured_traffic() is None

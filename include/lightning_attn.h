@@ -80,10 +80,11 @@ int la_prefill(const void *q, const void *k, const void *v, const float *slopes,
                int64_t B, int64_t H, int64_t N, int64_t d, void *stream);
 
 /*
- * Dense bf16 prefill that may use the whole device when its grid would not:
- * with B = 1 and H * d/32 column-slice workgroups filling at most half of the
- * compute units, each head's sequence is cut into S = CUs / (H * d/32)
- * segments (each at least 16384 tokens, at most 64 of them) that run in one
+ * Dense bf16 prefill that cuts each head's sequence into segments run at once
+ * when B = 1: with workgroups of 64 output columns (d = 128; 32 at d = 64),
+ * which read each head's Q and K through L2 half as often as la_prefill's
+ * and write whole 128-byte output lines, S = CUs / (H * d/64) segments (each
+ * at least 16384 tokens, at most 64 of them; none below 2) run in one
  * launch, the first from the caller's state and the others from zero; the
  * segments' states are then chained into the state at each boundary and the
  * final state, and each later segment's outputs are corrected with the state
@@ -116,10 +117,11 @@ int la_prefill_ws(const void *q, const void *k, const void *v, const float *slop
  * la_prefill_ws without a workspace argument, for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc.  It allocates nothing: when a sequence
- * split is planned it uses a scratch array of 8 MiB that the library holds on
- * each device it runs on until the process ends (found on the first call on
- * that device); a split needing more (only on devices with more than 512
- * compute units) gives LA_ERR_UNSUPPORTED.  Every call on one device shares
+ * split is planned it uses a scratch array of 8 MiB + 4 KiB that the library
+ * holds on each device it runs on until the process ends (found on the first
+ * call on that device; the split needs at most 32 KiB per compute unit plus
+ * a few hundred bytes); a split needing more (only on devices with more than
+ * 256 compute units) gives LA_ERR_UNSUPPORTED.  Every call on one device shares
  * that array and sets up what it reads itself, so calls that overlap on one
  * device (other streams, other threads) race; order them.  Same semantics,
  * argument rules and results as la_prefill_ws; LA_ERR_HIP also if the

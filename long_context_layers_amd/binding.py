@@ -136,7 +136,8 @@ def _strided(q, k, v, out, dt, dev, shape) -> bool:
 
 
 def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: torch.Tensor,
-            state: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+            state: torch.Tensor, out: Optional[torch.Tensor] = None,
+            split: bool = True) -> torch.Tensor:
     """Blockwise decayed causal linear attention over N tokens.
 
     q, k, v: [B,H,N,d] bf16 or fp32 on one GPU; slopes: [H] fp32;
@@ -144,7 +145,10 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: torch.Ten
     Returns out [B,H,N,d] (same dtype as q).  Enqueued on the current stream.
     bf16 q, k, v (sharing one set of strides) and out may be strided views
     with a unit channel stride, e.g. head-split slices of a token-major
-    projection buffer; such calls go to ``la_prefill_strided``.
+    projection buffer; such calls go to ``la_prefill_strided``.  Contiguous
+    bf16 calls go to ``la_prefill_ws`` (the sequence split, with a workspace
+    from torch's allocator) when it plans a split, unless ``split`` is False
+    (then ``la_prefill``, as the strided calls).
     """
     if not isinstance(q, torch.Tensor) or q.dim() != 4:
         raise ValueError("q must be a [B,H,N,d] tensor")
@@ -175,7 +179,7 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: torch.Ten
     else:
         _need(out, "out", dt, dev, (B, H, N, d))
     lib = load_library()
-    if dt == torch.bfloat16:
+    if dt == torch.bfloat16 and split:
         ws = prefill_workspace_bytes(B, H, N, d, dev)
         if ws > 0:
             # the sequence split over the whole device (la_prefill_ws); the

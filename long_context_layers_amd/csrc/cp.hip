@@ -282,8 +282,8 @@ int64_t split_workspace_bytes(int64_t H, int nseg, int d)
 
 hipError_t launch_prefill_bf16_split(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                      const float *slopes, uint16_t *out, float *state,
-                                     int64_t H, int64_t N, int d, int nseg, void *workspace,
-                                     hipStream_t stream)
+                                     int64_t H, int64_t N, int d, int nseg, int njt,
+                                     void *workspace, hipStream_t stream)
 {
     // workspace: nseg state slots [nseg][H][d][d] fp32, then nseg + 1 offsets
     float *slots = static_cast<float *>(workspace);
@@ -308,7 +308,7 @@ hipError_t launch_prefill_bf16_split(const uint16_t *q, const uint16_t *k, const
     }
     const Strides st = {0, N * d, d};
     const SeqMap map = {cu, H, 0, N, st, st};
-    hipError_t e = launch_prefill_bf16_nowalk(q, k, v, slopes, out, slots, nseg, map, d, stream);
+    hipError_t e = launch_prefill_bf16_nowalk(q, k, v, slopes, out, slots, nseg, map, d, stream, njt);
     if (e != hipSuccess) return e;
     {
         const int64_t blocks = (n4 + FT - 1) / FT;

@@ -13,7 +13,9 @@
 // device for the life of the process.  In host code `scratch` only stands in
 // for the symbol; the device address comes from hipGetSymbolAddress, looked
 // up once per device with that device current, and is what every launch gets.
-static constexpr int64_t NOALLOC_SCRATCH_BYTES = int64_t(8) << 20;
+// (the sequence split needs at most 32 KiB of state slots per compute unit
+// plus its segment offsets: 8 MiB + 520 bytes on a 256-CU MI355X)
+static constexpr int64_t NOALLOC_SCRATCH_BYTES = (int64_t(8) << 20) + 4096;
 static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
 
 namespace {
@@ -324,7 +326,8 @@ int la_prefill_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64
 {
     if (!bytes || B < 1 || H < 1 || N < 0) return LA_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
-    const int nseg = la::prefill_split_segments(B, H, N, (int)d);
+    int njt = 1;
+    const int nseg = la::prefill_split_plan(B, H, N, (int)d, &njt);
     *bytes = la::split_workspace_bytes(H, nseg, (int)d);
     return LA_OK;
 }
@@ -335,7 +338,8 @@ int la_prefill_ws(const void *q, const void *k, const void *v, const float *slop
 {
     const int rc = check_prefill(q, k, v, slopes, out, state, B, H, N, d, 2);
     if (rc != LA_OK) return rc;
-    const int nseg = la::prefill_split_segments(B, H, N, (int)d);
+    int njt = 1;
+    const int nseg = la::prefill_split_plan(B, H, N, (int)d, &njt);
     if (nseg < 2) return la_prefill(q, k, v, slopes, out, state, B, H, N, d, stream);
     const int64_t need = la::split_workspace_bytes(H, nseg, (int)d);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
@@ -345,11 +349,11 @@ int la_prefill_ws(const void *q, const void *k, const void *v, const float *slop
         overlap(workspace, need, v, act) || overlap(workspace, need, out, act) ||
         overlap(workspace, need, state, st) || overlap(workspace, need, slopes, H * 4))
         return LA_ERR_INVALID_ARG;
-    if (la::prefill_bf16_grid(nseg, H, (int)d) > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+    if (la::prefill_bf16_grid(nseg, H, (int)d, njt) > 0x7fffffff) return LA_ERR_UNSUPPORTED;
     return hip_status(la::launch_prefill_bf16_split(
         static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
         static_cast<const uint16_t *>(v), slopes, static_cast<uint16_t *>(out), state, H, N,
-        (int)d, nseg, workspace, static_cast<hipStream_t>(stream)));
+        (int)d, nseg, njt, workspace, static_cast<hipStream_t>(stream)));
 }
 
 int la_prefill_noalloc(const void *q, const void *k, const void *v, const float *slopes,
@@ -358,7 +362,8 @@ int la_prefill_noalloc(const void *q, const void *k, const void *v, const float 
 {
     const int rc = check_prefill(q, k, v, slopes, out, state, B, H, N, d, 2);
     if (rc != LA_OK) return rc;
-    const int nseg = la::prefill_split_segments(B, H, N, (int)d);
+    int njt = 1;
+    const int nseg = la::prefill_split_plan(B, H, N, (int)d, &njt);
     if (nseg < 2) return la_prefill(q, k, v, slopes, out, state, B, H, N, d, stream);
     if (la::split_workspace_bytes(H, nseg, (int)d) > NOALLOC_SCRATCH_BYTES) return LA_ERR_UNSUPPORTED;
     void *ws = nullptr;
@@ -698,8 +703,8 @@ const char *la_status_string(int status)
             return "LA_ERR_UNSUPPORTED: head dimension not in {64, 128}, more tokens per "
                    "decode call than supported, a rotary dimension or norm group size the "
                    "kernels do not take, a stride, shard count or length above the "
-                   "supported limit, a sequence split needing more than the 8 MiB "
-                   "scratch of la_prefill_noalloc, or grid too large";
+                   "supported limit, a sequence split needing more than the "
+                   "8 MiB + 4 KiB scratch of la_prefill_noalloc, or grid too large";
         case LA_ERR_HIP: return "LA_ERR_HIP: the kernel launch failed";
         default: return "unknown status";
     }

@@ -102,22 +102,26 @@ hipError_t launch_cp_correct(const uint16_t *q, const float *slopes, const float
                              hipStream_t stream);
 int64_t cp_correct_grid(int64_t B, int64_t H, int64_t L);
 
-// one workgroup per (sequence, head, column slice): never the packed walk
+// one workgroup per (sequence, head, njt 32-column tiles): never the packed
+// walk (njt = 2 only at d = 128 with contiguous rows)
 hipError_t launch_prefill_bf16_nowalk(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                       const float *slopes, uint16_t *out, float *state,
-                                      int64_t seqs, const SeqMap &map, int d, hipStream_t stream);
-// the sequence split of a dense B = 1 prefill whose grid fills at most half
-// of the device: segments per row (1 = no split) on the current device, the
+                                      int64_t seqs, const SeqMap &map, int d, hipStream_t stream,
+                                      int njt);
+
+// the sequence split of a dense B = 1 prefill: segments per row (1 = no
+// split) on the current device and the column tiles per workgroup (*njt), the
 // workspace it needs, and the launches (prep, packed prefill, fold, correct)
-int prefill_split_segments(int64_t B, int64_t H, int64_t N, int d);
+int prefill_split_plan(int64_t B, int64_t H, int64_t N, int d, int *njt);
 int64_t split_workspace_bytes(int64_t H, int nseg, int d);
 hipError_t launch_prefill_bf16_split(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                      const float *slopes, uint16_t *out, float *state,
-                                     int64_t H, int64_t N, int d, int nseg, void *workspace,
-                                     hipStream_t stream);
+                                     int64_t H, int64_t N, int d, int nseg, int njt,
+                                     void *workspace, hipStream_t stream);
 
-// number of workgroups one prefill launch over `seqs` sequences uses
-int64_t prefill_bf16_grid(int64_t seqs, int64_t H, int d);
+// number of workgroups one prefill launch over `seqs` sequences uses, with
+// njt 32-column tiles per workgroup
+int64_t prefill_bf16_grid(int64_t seqs, int64_t H, int d, int njt = 1);
 // whether a packed launch over seqs sequences (T tokens) walks them in one
 // workgroup per (head, column slice) on the current device
 bool prefill_bf16_walks(int64_t seqs, int64_t H, int64_t T, int d, bool packed);

@@ -87,14 +87,13 @@ typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int PC = 64;        // tokens per block
-constexpr int PJ = 32;        // state / output columns per workgroup
+constexpr int PJ = 32;        // state / output columns of one column tile
 constexpr int NCONS = 4;      // consumer waves
 constexpr int PT = 256;       // producer threads (4 waves)
 constexpr int NTHREADS = 64 * NCONS + PT;
 constexpr int NSET = 4;       // producer register sets (blocks in flight; even)
 static_assert(NSET % 2 == 0, "set i stages into LDS buffer i % 2");
 constexpr int QPAD = 8;       // bf16 padding of Q and state-copy rows
-constexpr int VP = 32;        // V row pitch (64 B, unpadded)
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -125,15 +124,17 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const f32x16 &x, int base) {
 // 16-byte-chunk swizzle of K rows (see the header comment)
 __device__ __forceinline__ int kswz(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
 
-template <int D>
+// NJT: 32-column tiles of the state and output per workgroup (1 or 2)
+template <int D, int NJT>
 struct alignas(16) Smem {
+    static constexpr int W = PJ * NJT;    // columns of the workgroup
     uint16_t Q[2][PC][D + QPAD];     // Q blocks, token-major
     uint16_t K[2][PC][D];            // K blocks, token-major, chunk-swizzled
-    uint16_t V[2][PC][VP];           // V slices, token-major
-    uint16_t VW[2][PC][VP];          // V slices times lambda^(c-1-b)
-    uint16_t ST[2][PJ][D + QPAD];    // bf16 copies of the state slice, transposed
-    float OP[2][64][20];             // W3 -> W2 partial outputs (one lane's 16 values)
-    uint16_t OT[2][32][PJ];          // W1 / W2 output tiles on their way to memory (swizzled)
+    uint16_t V[2][PC][W];            // V slices, token-major
+    uint16_t VW[2][PC][W];           // V slices times lambda^(c-1-b)
+    uint16_t ST[2][W][D + QPAD];     // bf16 copies of the state slice, transposed
+    float OP[2][64][16 * NJT + 4];   // W3 -> W2 partial outputs (one lane's 16 values per tile)
+    uint16_t OT[2][32][W];           // W1 / W2 output tiles on their way to memory (swizzled)
 };
 
 // ---- the blocks a workgroup visits, in order --------------------------------
@@ -258,17 +259,17 @@ struct Ctx {                          // per-thread constants of one workgroup
 
 // ---- producer waves: global -> registers -> LDS ----------------------------
 
-template <int D>
+template <int D, int NJT>
 struct Regs {                        // one block's share of a producer thread
     static constexpr int NQ = PC * D / 8 / PT;   // 16-byte chunks of Q (and of K)
-    uint4 q[NQ], k[NQ], v;
+    uint4 q[NQ], k[NQ], v[NJT];      // v[t]: column tile t of the V slice
     int c;                           // tokens in the block
 };
 
-template <int D>
+template <int D, int NJT>
 struct Addr {                        // per-thread byte offsets inside a block
-    uint32_t qk[Regs<D>::NQ];
-    uint32_t v;
+    uint32_t qk[Regs<D, NJT>::NQ];
+    uint32_t v[NJT];
 };
 
 // Buffer resource over rows [t0, t0 + 64) of a (b, h) slice: 16-byte loads
@@ -299,19 +300,20 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
     return make_uint4(x[0], x[1], x[2], x[3]);
 }
 
-template <int D>
-__device__ __forceinline__ void load_block(Regs<D> &r, const Ctx<D> &cx, const Pos &p,
-                                           const Addr<D> &ad)
+template <int D, int NJT>
+__device__ __forceinline__ void load_block(Regs<D, NJT> &r, const Ctx<D> &cx, const Pos &p,
+                                           const Addr<D, NJT> &ad)
 {
     const __amdgpu_buffer_rsrc_t rq = block_rsrc<D>(cx.q + p.in0, p.t0, p.n, cx.ts);
     const __amdgpu_buffer_rsrc_t rk = block_rsrc<D>(cx.k + p.in0, p.t0, p.n, cx.ts);
     const __amdgpu_buffer_rsrc_t rv = block_rsrc<D>(cx.v + p.in0, p.t0, p.n, cx.ts);
 #pragma unroll
-    for (int u = 0; u < Regs<D>::NQ; ++u) {
+    for (int u = 0; u < Regs<D, NJT>::NQ; ++u) {
         r.q[u] = bload16(rq, ad.qk[u]);
         r.k[u] = bload16(rk, ad.qk[u]);
     }
-    r.v = bload16(rv, ad.v);
+#pragma unroll
+    for (int t = 0; t < NJT; ++t) r.v[t] = bload16(rv, ad.v[t]);
     r.c = block_len(p.t0, p.n);
 }
 
@@ -320,33 +322,38 @@ __device__ __forceinline__ uint32_t scale_pair(uint32_t x, float w) {
 }
 
 // registers -> LDS buffer BUF; wv = lambda^(c-1-b) for this thread's token b
-template <int D, int BUF>
-__device__ __forceinline__ void store_block(const Regs<D> &r, Smem<D> &sm, int p, float wv)
+// (thread p holds 16 bytes of V row p / 4 in each column tile)
+template <int D, int NJT, int BUF>
+__device__ __forceinline__ void store_block(const Regs<D, NJT> &r, Smem<D, NJT> &sm, int p, float wv)
 {
 #pragma unroll
-    for (int u = 0; u < Regs<D>::NQ; ++u) {
+    for (int u = 0; u < Regs<D, NJT>::NQ; ++u) {
         const int ch = p + PT * u;
         const int row = ch / (D / 8), c8 = ch % (D / 8);
         *reinterpret_cast<uint4 *>(&sm.Q[BUF][row][c8 * 8]) = r.q[u];
         *reinterpret_cast<uint4 *>(&sm.K[BUF][row][(c8 ^ kswz(row)) * 8]) = r.k[u];
     }
-    const int vrow = p / 4, vc = (p % 4) * 8;
-    *reinterpret_cast<uint4 *>(&sm.V[BUF][vrow][vc]) = r.v;
-    uint4 w;
-    w.x = scale_pair(r.v.x, wv);
-    w.y = scale_pair(r.v.y, wv);
-    w.z = scale_pair(r.v.z, wv);
-    w.w = scale_pair(r.v.w, wv);
-    *reinterpret_cast<uint4 *>(&sm.VW[BUF][vrow][vc]) = w;
+    const int vrow = p / 4;
+#pragma unroll
+    for (int t = 0; t < NJT; ++t) {
+        const int vc = PJ * t + (p % 4) * 8;
+        *reinterpret_cast<uint4 *>(&sm.V[BUF][vrow][vc]) = r.v[t];
+        uint4 w;
+        w.x = scale_pair(r.v[t].x, wv);
+        w.y = scale_pair(r.v[t].y, wv);
+        w.z = scale_pair(r.v[t].z, wv);
+        w.w = scale_pair(r.v[t].w, wv);
+        *reinterpret_cast<uint4 *>(&sm.VW[BUF][vrow][vc]) = w;
+    }
 }
 
-template <int D, int BUF>
-__device__ __forceinline__ void produce_store(const Ctx<D> &cx, Smem<D> &sm, const Regs<D> &r,
+template <int D, int NJT, int BUF>
+__device__ __forceinline__ void produce_store(const Ctx<D> &cx, Smem<D, NJT> &sm, const Regs<D, NJT> &r,
                                               int p, float wfull)
 {
     const int b = p / 4;
     const float wv = r.c == PC ? wfull : (b < r.c ? decay_pow(cx.s, r.c - 1 - b) : 0.0f);
-    store_block<D, BUF>(r, sm, p, wv);
+    store_block<D, NJT, BUF>(r, sm, p, wv);
 }
 
 // One producer step per block blk: after the block's barrier, stage block
@@ -354,54 +361,56 @@ __device__ __forceinline__ void produce_store(const Ctx<D> &cx, Smem<D> &sm, con
 // block blk+1+NSET (at ld, which then moves on).  Loads past the end return
 // zeros without touching memory, so nothing here is conditional (exact vmcnt
 // waits).
-template <int D, int SET, bool WALK>
-__device__ __forceinline__ void produce_step(const Ctx<D> &cx, const Walk<WALK> &wk, Smem<D> &sm,
-                                             Regs<D> (&rs)[NSET], const Addr<D> &ad, Pos &ld, int p,
-                                             float wfull)
+template <int D, int NJT, int SET, bool WALK>
+__device__ __forceinline__ void produce_step(const Ctx<D> &cx, const Walk<WALK> &wk, Smem<D, NJT> &sm,
+                                             Regs<D, NJT> (&rs)[NSET], const Addr<D, NJT> &ad, Pos &ld,
+                                             int p, float wfull)
 {
     __syncthreads();                                   // barrier of block blk
-    if (SET % 2 == 1) produce_store<D, 1>(cx, sm, rs[SET], p, wfull);
-    else              produce_store<D, 0>(cx, sm, rs[SET], p, wfull);
-    load_block<D>(rs[SET], cx, ld, ad);
+    if (SET % 2 == 1) produce_store<D, NJT, 1>(cx, sm, rs[SET], p, wfull);
+    else              produce_store<D, NJT, 0>(cx, sm, rs[SET], p, wfull);
+    load_block<D, NJT>(rs[SET], cx, ld, ad);
     wk.next(ld);
 }
 
 // the NSET producer steps of one round, sets 1 .. NSET-1, then 0
-template <int D, bool WALK, int I>
+template <int D, int NJT, bool WALK, int I>
 struct ProduceRound {
-    __device__ static __forceinline__ void run(const Ctx<D> &cx, const Walk<WALK> &wk, Smem<D> &sm,
-                                               Regs<D> (&rs)[NSET], const Addr<D> &ad, Pos &ld, int p,
-                                               float wfull) {
-        produce_step<D, I % NSET>(cx, wk, sm, rs, ad, ld, p, wfull);
-        if constexpr (I < NSET) ProduceRound<D, WALK, I + 1>::run(cx, wk, sm, rs, ad, ld, p, wfull);
+    __device__ static __forceinline__ void run(const Ctx<D> &cx, const Walk<WALK> &wk, Smem<D, NJT> &sm,
+                                               Regs<D, NJT> (&rs)[NSET], const Addr<D, NJT> &ad, Pos &ld,
+                                               int p, float wfull) {
+        produce_step<D, NJT, I % NSET>(cx, wk, sm, rs, ad, ld, p, wfull);
+        if constexpr (I < NSET) ProduceRound<D, NJT, WALK, I + 1>::run(cx, wk, sm, rs, ad, ld, p, wfull);
     }
 };
 
-template <int D, bool WALK>
-__device__ void producer(const Ctx<D> &cx, const Walk<WALK> &wk, Pos ld, Smem<D> &sm, int p)
+template <int D, int NJT, bool WALK>
+__device__ void producer(const Ctx<D> &cx, const Walk<WALK> &wk, Pos ld, Smem<D, NJT> &sm, int p)
 {
-    Addr<D> ad;
+    Addr<D, NJT> ad;
 #pragma unroll
-    for (int u = 0; u < Regs<D>::NQ; ++u) {
+    for (int u = 0; u < Regs<D, NJT>::NQ; ++u) {
         const int ch = p + PT * u;
         ad.qk[u] = (uint32_t)(((ch / (D / 8)) * cx.ts + (ch % (D / 8)) * 8) * 2);
     }
-    ad.v = (uint32_t)(((p / 4) * cx.ts + cx.j0 + (p % 4) * 8) * 2);
+#pragma unroll
+    for (int t = 0; t < NJT; ++t)
+        ad.v[t] = (uint32_t)(((p / 4) * cx.ts + cx.j0 + PJ * t + (p % 4) * 8) * 2);
     const float wfull = decay_pow(cx.s, PC - 1 - p / 4);       // lambda^(C-1-b)
 
-    Regs<D> rs[NSET];                                           // set i holds block i (mod NSET)
+    Regs<D, NJT> rs[NSET];                                      // set i holds block i (mod NSET)
 #pragma unroll
     for (int i = 0; i < NSET; ++i) {
-        load_block<D>(rs[i], cx, ld, ad);
+        load_block<D, NJT>(rs[i], cx, ld, ad);
         wk.next(ld);
     }
-    produce_store<D, 0>(cx, sm, rs[0], p, wfull);
-    load_block<D>(rs[0], cx, ld, ad);
+    produce_store<D, NJT, 0>(cx, sm, rs[0], p, wfull);
+    load_block<D, NJT>(rs[0], cx, ld, ad);
     wk.next(ld);
 
     // block blk stages block blk+1 from set (blk+1) % NSET into buffer (blk+1) % 2
     for (int64_t blk = 0; blk < cx.nblk; blk += NSET)
-        ProduceRound<D, WALK, 1>::run(cx, wk, sm, rs, ad, ld, p, wfull);
+        ProduceRound<D, NJT, WALK, 1>::run(cx, wk, sm, rs, ad, ld, p, wfull);
     __syncthreads();                                   // final barrier (matches the consumers)
 }
 
@@ -550,27 +559,32 @@ __device__ __forceinline__ void score_decay(float (&dec)[16], float s, int ah, i
     }
 }
 
-// O^T(a-half ah) = scale * S^T Q^T from state copy SB and Q buffer QB
-template <int D>
-__device__ __forceinline__ f32x16 inter_term(const Smem<D> &sm, int qb, int sb, int ah,
-                                              const Lane<D> &ln, float scale, bf16x8 (&qf)[D / 16])
+// O^T(a-half ah) = scale * S^T Q^T from state copy SB and Q buffer QB, one
+// accumulator per column tile (the Q fragments serve every tile)
+template <int D, int NJT>
+__device__ __forceinline__ void inter_term(const Smem<D, NJT> &sm, int qb, int sb, int ah,
+                                           const Lane<D> &ln, float scale, bf16x8 (&qf)[D / 16],
+                                           f32x16 (&acc)[NJT])
 {
-    f32x16 acc = {};
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) qf[ks] = ld8(&sm.Q[qb][32 * ah + ln.l32][16 * ks + 8 * ln.h]);
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-        acc = mfma(ld8(&sm.ST[sb][ln.l32][16 * ks + 8 * ln.h]), qf[ks], acc);
-    return acc * scale;
+    for (int jt = 0; jt < NJT; ++jt) {
+        f32x16 a = {};
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks)
+            a = mfma(ld8(&sm.ST[sb][PJ * jt + ln.l32][16 * ks + 8 * ln.h]), qf[ks], a);
+        acc[jt] = a * scale;
+    }
 }
 
 // score tile P^T(bh, ah) (decayed) from Q fragments qf, then acc += V^T P^T
 // over the tile's 32 tokens; the accumulator registers of P^T are the B
 // operand directly (registers 8s..8s+7 hold tokens 32bh + 16s + 8e' + 4h + 0..3)
-template <int D>
-__device__ __forceinline__ void score_pv(const Smem<D> &sm, int buf, int bh,
+template <int D, int NJT>
+__device__ __forceinline__ void score_pv(const Smem<D, NJT> &sm, int buf, int bh,
                                          const bf16x8 (&qf)[D / 16], const float (&dec)[16],
-                                         const Lane<D> &ln, f32x16 &acc)
+                                         const Lane<D> &ln, f32x16 (&acc)[NJT])
 {
     f32x16 pacc = {};
     const int krow = 32 * bh + ln.l32;
@@ -583,9 +597,12 @@ __device__ __forceinline__ void score_pv(const Smem<D> &sm, int buf, int bh,
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
         const int r0 = 32 * bh + 16 * s2 + 4 * ln.h + ln.trow;
-        const bf16x8 va = ldtr8(&sm.V[buf][r0][16 * ln.q2 + ln.tcol],
-                                &sm.V[buf][r0 + 8][16 * ln.q2 + ln.tcol]);
-        acc = mfma(va, to_bf16x8(pacc, 8 * s2), acc);
+#pragma unroll
+        for (int jt = 0; jt < NJT; ++jt) {
+            const bf16x8 va = ldtr8(&sm.V[buf][r0][PJ * jt + 16 * ln.q2 + ln.tcol],
+                                    &sm.V[buf][r0 + 8][PJ * jt + 16 * ln.q2 + ln.tcol]);
+            acc[jt] = mfma(va, to_bf16x8(pacc, 8 * s2), acc[jt]);
+        }
     }
 }
 
@@ -600,55 +617,65 @@ __device__ __forceinline__ void score_pv(const Smem<D> &sm, int buf, int bh,
 // (the launch is bound by its memory traffic).  Chunk c (8 columns) of tile
 // row r sits at chunk c ^ ((r >> 2) & 3): conflict-free for both the row-wise
 // writes and the 4-lanes-per-row reads.
-__device__ __forceinline__ int ot_chunk(int r, int c) { return c ^ ((r >> 2) & 3); }
-
-template <int D>
-__device__ __forceinline__ int out_offset(const Ctx<D> &cx, int ah, int pr, int lane) {
-    // bytes of this lane's 16-byte piece: token 32ah + 16pr + lane/4, chunk lane%4
-    return ((32 * ah + 16 * pr + lane / 4) * cx.ots + cx.j0 + 8 * (lane % 4)) * 2;
+// (with two column tiles a row is 128 bytes, eight lanes a row: chunk c of row
+// r sits at c ^ (r & 7))
+template <int NJT>
+__device__ __forceinline__ int ot_chunk(int r, int c) {
+    return NJT == 1 ? c ^ ((r >> 2) & 3) : c ^ (r & 7);
 }
 
-template <int D>
-__device__ __forceinline__ void store_out(const Ctx<D> &cx, const Pos &p, const int (&ooff)[2],
-                                          const f32x16 &acc, uint16_t (*ot)[PJ], const Lane<D> &ln,
-                                          int lane)
+// per lane, the byte offsets of its 16-byte pieces: store i covers tokens
+// 32ah + i * 64/CPR .., CPR = 4 NJT lanes on each token's PJ * NJT columns
+template <int D, int NJT>
+__device__ __forceinline__ int out_offset(const Ctx<D> &cx, int ah, int i, int lane) {
+    constexpr int CPR = 4 * NJT;
+    return ((32 * ah + i * (64 / CPR) + lane / CPR) * cx.ots + cx.j0 + 8 * (lane % CPR)) * 2;
+}
+
+template <int D, int NJT>
+__device__ __forceinline__ void store_out(const Ctx<D> &cx, const Pos &p, const int (&ooff)[2 * NJT],
+                                          const f32x16 (&acc)[NJT], uint16_t (*ot)[PJ * NJT],
+                                          const Lane<D> &ln, int lane)
 {
+    constexpr int CPR = 4 * NJT;                  // 16-byte chunks per tile row
 #pragma unroll
-    for (int pr = 0; pr < 2; ++pr) {
-        const int g0 = 2 * pr, g1 = 2 * pr + 1;
-        unsigned x0 = pack_bf16x2(acc[4 * g0 + 0], acc[4 * g0 + 1]);
-        unsigned x1 = pack_bf16x2(acc[4 * g0 + 2], acc[4 * g0 + 3]);
-        unsigned y0 = pack_bf16x2(acc[4 * g1 + 0], acc[4 * g1 + 1]);
-        unsigned y1 = pack_bf16x2(acc[4 * g1 + 2], acc[4 * g1 + 3]);
-        const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
-        const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
-        uint4 o;
-        o.x = s0[0]; o.y = s1[0]; o.z = s0[1]; o.w = s1[1];
-        *reinterpret_cast<uint4 *>(&ot[ln.l32][8 * ot_chunk(ln.l32, ln.h + 2 * pr)]) = o;
-    }
+    for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+            const int g0 = 2 * pr, g1 = 2 * pr + 1;
+            unsigned x0 = pack_bf16x2(acc[jt][4 * g0 + 0], acc[jt][4 * g0 + 1]);
+            unsigned x1 = pack_bf16x2(acc[jt][4 * g0 + 2], acc[jt][4 * g0 + 3]);
+            unsigned y0 = pack_bf16x2(acc[jt][4 * g1 + 0], acc[jt][4 * g1 + 1]);
+            unsigned y1 = pack_bf16x2(acc[jt][4 * g1 + 2], acc[jt][4 * g1 + 3]);
+            const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+            uint4 o;
+            o.x = s0[0]; o.y = s1[0]; o.z = s0[1]; o.w = s1[1];
+            *reinterpret_cast<uint4 *>(&ot[ln.l32][8 * ot_chunk<NJT>(ln.l32, 4 * jt + ln.h + 2 * pr)]) = o;
+        }
     asm volatile("" : : : "memory");              // the reads below follow the writes
     const __amdgpu_buffer_rsrc_t ro = block_rsrc<D>(cx.o + p.out0, p.t0, p.n, cx.ots);   // rows past the end dropped
 #pragma unroll
-    for (int pr = 0; pr < 2; ++pr) {
-        const int r = 16 * pr + lane / 4;
-        const uint4 x = *reinterpret_cast<const uint4 *>(&ot[r][8 * ot_chunk(r, lane % 4)]);
+    for (int i = 0; i < CPR / 2; ++i) {
+        const int r = (64 / CPR) * i + lane / CPR;
+        const uint4 x = *reinterpret_cast<const uint4 *>(&ot[r][8 * ot_chunk<NJT>(r, lane % CPR)]);
         const u32x4 w = {x.x, x.y, x.z, x.w};
-        __builtin_amdgcn_raw_buffer_store_b128(w, ro, ooff[pr], 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(w, ro, ooff[i], 0, 0);
     }
     asm volatile("" : : : "memory");              // the next tile's writes follow these reads
 }
 
-// bf16 copy of state tile it (rows 32it..) into ST[buf][j][i]
-template <int D>
-__device__ __forceinline__ void write_st(Smem<D> &sm, int buf, int it, const Lane<D> &ln,
-                                         const f32x16 &s)
+// bf16 copy of state tile it (rows 32it..) of column tile jt into ST[buf][j][i]
+template <int D, int NJT>
+__device__ __forceinline__ void write_st(Smem<D, NJT> &sm, int buf, int it, int jt,
+                                         const Lane<D> &ln, const f32x16 &s)
 {
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
         uint2 p;
         p.x = pack_bf16x2(s[4 * q4 + 0], s[4 * q4 + 1]);
         p.y = pack_bf16x2(s[4 * q4 + 2], s[4 * q4 + 3]);
-        *reinterpret_cast<uint2 *>(&sm.ST[buf][ln.l32][32 * it + 8 * q4 + 4 * ln.h]) = p;
+        *reinterpret_cast<uint2 *>(&sm.ST[buf][PJ * jt + ln.l32][32 * it + 8 * q4 + 4 * ln.h]) = p;
     }
 }
 
@@ -660,62 +687,77 @@ __device__ __forceinline__ void write_st(Smem<D> &sm, int buf, int it, const Lan
 // initial state, staged in LDS a whole sequence earlier.  The
 // tiles evolve independently, so they can be split over waves: the scan wave
 // runs all but the last, the off-diagonal score wave (which had the most
-// slack) the last.
-template <int D, bool WALK, int T0, int NTL>
+// slack) the last.  With NJT column tiles each row tile has NJT accumulators
+// (sacc[jt][t]); the walk runs one column tile.
+template <int D, int NJT, bool WALK, int T0, int NTL>
 struct Scan {
+    static_assert(!WALK || NJT == 1, "the walk's state hand-over moves one column tile");
     Lane<D> ln;
     float full_decay;
-    f32x16 sacc[NTL];
+    f32x16 sacc[NJT][NTL];
 
     __device__ Scan(const Ctx<D> &cx, int lane) : ln(lane), full_decay(decay_pow(cx.s, PC)) {}
 
-    __device__ void init(const Ctx<D> &cx, const Walk<WALK> &wk, const Pos &pos, Smem<D> &sm) {
+    __device__ void init(const Ctx<D> &cx, const Walk<WALK> &wk, const Pos &pos, Smem<D, NJT> &sm) {
         if (pos.n > 0) {
-            if constexpr (WALK) load_state<D, T0, NTL>(sacc, cx.state_of(pos.seq), ln);
+            if constexpr (WALK) load_state<D, T0, NTL>(sacc[0], cx.state_of(pos.seq), ln);
             else {
                 const float *St = cx.state_of(pos.seq);
 #pragma unroll
-                for (int t = 0; t < NTL; ++t)
+                for (int jt = 0; jt < NJT; ++jt)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        sacc[t][r] = St[(32 * (T0 + t) + 8 * (r / 4) + 4 * ln.h + r % 4) * D + ln.l32];
+                    for (int t = 0; t < NTL; ++t)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            sacc[jt][t][r] = St[(32 * (T0 + t) + 8 * (r / 4) + 4 * ln.h + r % 4) * D +
+                                                PJ * jt + ln.l32];
             }
         } else {
 #pragma unroll
-            for (int t = 0; t < NTL; ++t) sacc[t] = f32x16{};
+            for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+                for (int t = 0; t < NTL; ++t) sacc[jt][t] = f32x16{};
         }
         if constexpr (WALK) {
             const int64_t s1 = wk.seq_at(pos.j + 1);
             stage_state<D, T0, NTL>(wk.slot, cx.state_of(s1 >= 0 ? s1 : pos.seq), ln.l32 + 32 * ln.h, s1 >= 0);
         }
 #pragma unroll
-        for (int t = 0; t < NTL; ++t) write_st<D>(sm, 1, T0 + t, ln, sacc[t]);   // read by block 0
+        for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+            for (int t = 0; t < NTL; ++t) write_st<D, NJT>(sm, 1, T0 + t, jt, ln, sacc[jt][t]);   // read by block 0
     }
 
     // block at pos (c tokens; last: it ends its sequence), LDS buffer BUF
     template <int BUF>
-    __device__ void step(const Ctx<D> &cx, const Walk<WALK> &wk, const Pos &pos, Smem<D> &sm,
+    __device__ void step(const Ctx<D> &cx, const Walk<WALK> &wk, const Pos &pos, Smem<D, NJT> &sm,
                          int c, bool last) {
         const float sdec = c == PC ? full_decay : (c == 0 ? 1.0f : decay_pow(cx.s, c));
-        bf16x8 vwf[PC / 16];
+        bf16x8 vwf[NJT][PC / 16];
 #pragma unroll
-        for (int ks = 0; ks < PC / 16; ++ks) {
-            const int r0 = 16 * ks + 8 * ln.h + ln.trow;
-            vwf[ks] = ldtr8(&sm.VW[BUF][r0][16 * ln.q2 + ln.tcol], &sm.VW[BUF][r0 + 4][16 * ln.q2 + ln.tcol]);
-        }
+        for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+            for (int ks = 0; ks < PC / 16; ++ks) {
+                const int r0 = 16 * ks + 8 * ln.h + ln.trow;
+                vwf[jt][ks] = ldtr8(&sm.VW[BUF][r0][PJ * jt + 16 * ln.q2 + ln.tcol],
+                                    &sm.VW[BUF][r0 + 4][PJ * jt + 16 * ln.q2 + ln.tcol]);
+            }
 #pragma unroll
         for (int t = 0; t < NTL; ++t) {
             const int col = 32 * (T0 + t) + 16 * ln.q2 + ln.tcol;   // feature of this lane's chunk
             const int ch = col >> 3, sub = col & 7;
-            sacc[t] *= sdec;
+#pragma unroll
+            for (int jt = 0; jt < NJT; ++jt) sacc[jt][t] *= sdec;
 #pragma unroll
             for (int ks = 0; ks < PC / 16; ++ks) {
                 const int r0 = 16 * ks + 8 * ln.h + ln.trow;
                 const bf16x8 ka = ldtr8(&sm.K[BUF][r0][((ch ^ kswz(r0)) * 8) + sub],
                                         &sm.K[BUF][r0 + 4][((ch ^ kswz(r0 + 4)) * 8) + sub]);
-                sacc[t] = mfma(ka, vwf[ks], sacc[t]);
+#pragma unroll
+                for (int jt = 0; jt < NJT; ++jt) sacc[jt][t] = mfma(ka, vwf[jt][ks], sacc[jt][t]);
             }
-            write_st<D>(sm, BUF, T0 + t, ln, sacc[t]);
+#pragma unroll
+            for (int jt = 0; jt < NJT; ++jt) write_st<D, NJT>(sm, BUF, T0 + t, jt, ln, sacc[jt][t]);
         }
         if constexpr (WALK) {
             if (last) {
@@ -725,7 +767,7 @@ struct Scan {
                 const bool more = wk.seq_at(pos.j + 1) >= 0;
                 f32x16 nxt[NTL];
                 if (more) read_staged<D, T0, NTL>(nxt, wk.slot, ln);
-                store_via_slot<D, T0, NTL>(wk.slot, cx.state_of(pos.seq), sacc, ln,   // the final state out
+                store_via_slot<D, T0, NTL>(wk.slot, cx.state_of(pos.seq), sacc[0], ln,   // the final state out
                                            ln.l32 + 32 * ln.h);
                 if (more) {
                     // take up the next sequence (its bf16 copy over the one
@@ -733,8 +775,8 @@ struct Scan {
                     // after it once the slot has been read
 #pragma unroll
                     for (int t = 0; t < NTL; ++t) {
-                        sacc[t] = nxt[t];
-                        write_st<D>(sm, BUF, T0 + t, ln, sacc[t]);
+                        sacc[0][t] = nxt[t];
+                        write_st<D, NJT>(sm, BUF, T0 + t, 0, ln, sacc[0][t]);
                     }
                     __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0): the slot reads done
                     const int64_t s2 = wk.seq_at(pos.j + 2);
@@ -752,20 +794,23 @@ struct Scan {
             if (cx.nblk > 0) {
                 float *St = cx.state_of(pos.seq);
 #pragma unroll
-                for (int t = 0; t < NTL; ++t)
+                for (int jt = 0; jt < NJT; ++jt)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        St[(32 * (T0 + t) + 8 * (r / 4) + 4 * ln.h + r % 4) * D + ln.l32] = sacc[t][r];
+                    for (int t = 0; t < NTL; ++t)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            St[(32 * (T0 + t) + 8 * (r / 4) + 4 * ln.h + r % 4) * D + PJ * jt + ln.l32] =
+                                sacc[jt][t][r];
             }
         }
     }
 };
 
 // W0: the state scan on all tiles but the last (pos: block 0)
-template <int D, bool WALK>
-__device__ void scan_wave(const Ctx<D> &cx, const Walk<WALK> &wk, Pos pos, Smem<D> &sm, int lane)
+template <int D, int NJT, bool WALK>
+__device__ void scan_wave(const Ctx<D> &cx, const Walk<WALK> &wk, Pos pos, Smem<D, NJT> &sm, int lane)
 {
-    Scan<D, WALK, 0, D / 32 - 1> sc(cx, lane);
+    Scan<D, NJT, WALK, 0, D / 32 - 1> sc(cx, lane);
     sc.init(cx, wk, pos, sm);
     auto step = [&](auto BUFC) {
         constexpr int BUF = decltype(BUFC)::value;
@@ -784,22 +829,31 @@ __device__ void scan_wave(const Ctx<D> &cx, const Walk<WALK> &wk, Pos pos, Smem<
     sc.finish(cx, pos);
 }
 
+// the per-lane store offsets of a token half ah
+template <int D, int NJT>
+__device__ __forceinline__ void out_offsets(int (&ooff)[2 * NJT], const Ctx<D> &cx, int ah, int lane) {
+#pragma unroll
+    for (int i = 0; i < 2 * NJT; ++i) ooff[i] = out_offset<D, NJT>(cx, ah, i, lane);
+}
+
 // W1: tokens 0..31, complete
-template <int D, bool WALK>
-__device__ void out0_wave(const Ctx<D> &cx, const Walk<WALK> &wk, Pos pos, Smem<D> &sm, int lane)
+template <int D, int NJT, bool WALK>
+__device__ void out0_wave(const Ctx<D> &cx, const Walk<WALK> &wk, Pos pos, Smem<D, NJT> &sm, int lane)
 {
     const Lane<D> ln(lane);
     float dec[16];
     score_decay(dec, cx.s, 0, 0, ln.l32, ln.h);
     const float scale = decay_pow(cx.s, ln.l32 + 1);               // lambda^(a+1)
-    const int ooff[2] = {out_offset(cx, 0, 0, lane), out_offset(cx, 0, 1, lane)};
+    int ooff[2 * NJT];
+    out_offsets<D, NJT>(ooff, cx, 0, lane);
     auto step = [&](auto BUFC) {
         constexpr int BUF = decltype(BUFC)::value;
         __syncthreads();
         bf16x8 qf[D / 16];
-        f32x16 acc = inter_term<D>(sm, BUF, BUF ^ 1, 0, ln, scale, qf);
-        score_pv<D>(sm, BUF, 0, qf, dec, ln, acc);
-        store_out<D>(cx, pos, ooff, acc, sm.OT[0], ln, lane);
+        f32x16 acc[NJT];
+        inter_term<D, NJT>(sm, BUF, BUF ^ 1, 0, ln, scale, qf, acc);
+        score_pv<D, NJT>(sm, BUF, 0, qf, dec, ln, acc);
+        store_out<D, NJT>(cx, pos, ooff, acc, sm.OT[0], ln, lane);
         wk.next(pos);
     };
     for (int64_t blk = 0; blk < cx.nblk; blk += 2) {
@@ -810,34 +864,40 @@ __device__ void out0_wave(const Ctx<D> &cx, const Walk<WALK> &wk, Pos pos, Smem<
 }
 
 // W2: tokens 32..63, inter term + diagonal scores; adds W3's part one block later
-template <int D, bool WALK>
-__device__ void out1_wave(const Ctx<D> &cx, const Walk<WALK> &wk, Pos pos, Smem<D> &sm, int lane)
+template <int D, int NJT, bool WALK>
+__device__ void out1_wave(const Ctx<D> &cx, const Walk<WALK> &wk, Pos pos, Smem<D, NJT> &sm, int lane)
 {
     const Lane<D> ln(lane);
     float dec[16];
     score_decay(dec, cx.s, 1, 1, ln.l32, ln.h);
     const float scale = decay_pow(cx.s, 32 + ln.l32 + 1);
-    const int ooff[2] = {out_offset(cx, 1, 0, lane), out_offset(cx, 1, 1, lane)};
-    f32x16 prev = {};
+    int ooff[2 * NJT];
+    out_offsets<D, NJT>(ooff, cx, 1, lane);
+    f32x16 prev[NJT] = {};
     Pos ppos = pos;                                                // block of prev
     auto finish_prev = [&](int pbuf) {                             // that block's tokens 32..63
-        const float4 *op = reinterpret_cast<const float4 *>(&sm.OP[pbuf][lane][0]);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const float4 x = op[u];
-            prev[4 * u + 0] += x.x; prev[4 * u + 1] += x.y;
-            prev[4 * u + 2] += x.z; prev[4 * u + 3] += x.w;
+        for (int jt = 0; jt < NJT; ++jt) {
+            const float4 *op = reinterpret_cast<const float4 *>(&sm.OP[pbuf][lane][16 * jt]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float4 x = op[u];
+                prev[jt][4 * u + 0] += x.x; prev[jt][4 * u + 1] += x.y;
+                prev[jt][4 * u + 2] += x.z; prev[jt][4 * u + 3] += x.w;
+            }
         }
-        store_out<D>(cx, ppos, ooff, prev, sm.OT[1], ln, lane);
+        store_out<D, NJT>(cx, ppos, ooff, prev, sm.OT[1], ln, lane);
     };
     auto step = [&](int64_t blk, auto BUFC) {
         constexpr int BUF = decltype(BUFC)::value;
         __syncthreads();
         bf16x8 qf[D / 16];
-        f32x16 acc = inter_term<D>(sm, BUF, BUF ^ 1, 1, ln, scale, qf);
-        score_pv<D>(sm, BUF, 1, qf, dec, ln, acc);
+        f32x16 acc[NJT];
+        inter_term<D, NJT>(sm, BUF, BUF ^ 1, 1, ln, scale, qf, acc);
+        score_pv<D, NJT>(sm, BUF, 1, qf, dec, ln, acc);
         if (blk > 0) finish_prev(BUF ^ 1);
-        prev = acc;
+#pragma unroll
+        for (int jt = 0; jt < NJT; ++jt) prev[jt] = acc[jt];
         ppos = pos;
         wk.next(pos);
     };
@@ -851,13 +911,13 @@ __device__ void out1_wave(const Ctx<D> &cx, const Walk<WALK> &wk, Pos pos, Smem<
 
 // W3: tokens 32..63, off-diagonal scores P^T(0,1) and their V^T P^T part,
 // and the state scan's last tile (pos: block 0)
-template <int D, bool WALK>
-__device__ void out1x_wave(const Ctx<D> &cx, const Walk<WALK> &wk, Pos pos, Smem<D> &sm, int lane)
+template <int D, int NJT, bool WALK>
+__device__ void out1x_wave(const Ctx<D> &cx, const Walk<WALK> &wk, Pos pos, Smem<D, NJT> &sm, int lane)
 {
     const Lane<D> ln(lane);
     float dec[16];
     score_decay(dec, cx.s, 1, 0, ln.l32, ln.h);
-    Scan<D, WALK, D / 32 - 1, 1> sc(cx, lane);
+    Scan<D, NJT, WALK, D / 32 - 1, 1> sc(cx, lane);
     sc.init(cx, wk, pos, sm);
     auto step = [&](auto BUFC) {
         constexpr int BUF = decltype(BUFC)::value;
@@ -869,12 +929,16 @@ __device__ void out1x_wave(const Ctx<D> &cx, const Walk<WALK> &wk, Pos pos, Smem
         bf16x8 qf[D / 16];
 #pragma unroll
         for (int ks = 0; ks < D / 16; ++ks) qf[ks] = ld8(&sm.Q[BUF][32 + ln.l32][16 * ks + 8 * ln.h]);
-        f32x16 acc = {};
-        score_pv<D>(sm, BUF, 0, qf, dec, ln, acc);
-        float4 *op = reinterpret_cast<float4 *>(&sm.OP[BUF][lane][0]);
+        f32x16 acc[NJT] = {};
+        score_pv<D, NJT>(sm, BUF, 0, qf, dec, ln, acc);
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-            op[u] = make_float4(acc[4 * u + 0], acc[4 * u + 1], acc[4 * u + 2], acc[4 * u + 3]);
+        for (int jt = 0; jt < NJT; ++jt) {
+            float4 *op = reinterpret_cast<float4 *>(&sm.OP[BUF][lane][16 * jt]);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                op[u] = make_float4(acc[jt][4 * u + 0], acc[jt][4 * u + 1], acc[jt][4 * u + 2],
+                                    acc[jt][4 * u + 3]);
+        }
         wk.next(pos);
     };
     for (int64_t blk = 0; blk < cx.nblk; blk += 2) {
@@ -890,14 +954,18 @@ __device__ void out1x_wave(const Ctx<D> &cx, const Walk<WALK> &wk, Pos pos, Smem
 // map), so the contiguous layouts pay nothing for stride support.
 // WALK = false: one workgroup per (sequence, head, column slice); WALK = true:
 // one per (head, column slice), walking all nseq sequences of a packed map.
-template <int D, bool STRIDED, bool WALK>
+// NJT: 32-column tiles per workgroup (2 halves how often each head's Q and K
+// are read through L2 and writes whole 128-byte output lines, for half as
+// many workgroups per head; the walk takes 1).
+template <int D, bool STRIDED, bool WALK, int NJT>
 __global__ __launch_bounds__(NTHREADS) void prefill_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const float *__restrict__ slopes,
     uint16_t *__restrict__ out, float *__restrict__ state, SeqMap map, int64_t nseq)
 {
-    constexpr int NJ = D / PJ;            // workgroups per head
-    __shared__ Smem<D> sm;
+    static_assert(!WALK || NJT == 1, "the walk runs one column tile per workgroup");
+    constexpr int NJ = D / (PJ * NJT);    // workgroups per head
+    __shared__ Smem<D, NJT> sm;
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -944,7 +1012,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_bf16_kernel(
     cx.state = state;
     cx.H = map.H;
     cx.h = wk.h;
-    cx.j0 = (int)slice * PJ;
+    cx.j0 = (int)slice * PJ * NJT;
     cx.s = slopes[wk.h];
     // blocks processed: a multiple of NSET (trailing empty blocks are no-ops;
     // an empty sequence leaves its state unchanged)
@@ -953,11 +1021,11 @@ __global__ __launch_bounds__(NTHREADS) void prefill_bf16_kernel(
     cx.ots = STRIDED ? (int)map.out.st : D;
 
     switch (wave) {
-        case 0: scan_wave<D>(cx, wk, p0, sm, lane); break;
-        case 1: out0_wave<D>(cx, wk, p0, sm, lane); break;
-        case 2: out1_wave<D>(cx, wk, p0, sm, lane); break;
-        case 3: out1x_wave<D>(cx, wk, p0, sm, lane); break;
-        default: producer<D>(cx, wk, p0, sm, tid - 64 * NCONS); break;
+        case 0: scan_wave<D, NJT>(cx, wk, p0, sm, lane); break;
+        case 1: out0_wave<D, NJT>(cx, wk, p0, sm, lane); break;
+        case 2: out1_wave<D, NJT>(cx, wk, p0, sm, lane); break;
+        case 3: out1x_wave<D, NJT>(cx, wk, p0, sm, lane); break;
+        default: producer<D, NJT>(cx, wk, p0, sm, tid - 64 * NCONS); break;
     }
 }
 
@@ -982,7 +1050,9 @@ int device_cus()
 
 }  // namespace
 
-int64_t prefill_bf16_grid(int64_t seqs, int64_t H, int d) { return seqs * H * (d / PJ); }
+int64_t prefill_bf16_grid(int64_t seqs, int64_t H, int d, int njt) {
+    return seqs * H * (d / (PJ * njt));
+}
 
 // A packed launch walks its sequences inside one workgroup per (head, column
 // slice) when that is estimated to be faster than a grid of one workgroup per
@@ -1024,44 +1094,62 @@ template <bool WALK>
 const void *prefill_fn(int d, bool strided)
 {
     if (d == 64)
-        return strided ? (const void *)prefill_bf16_kernel<64, true, WALK>
-                       : (const void *)prefill_bf16_kernel<64, false, WALK>;
-    return strided ? (const void *)prefill_bf16_kernel<128, true, WALK>
-                   : (const void *)prefill_bf16_kernel<128, false, WALK>;
+        return strided ? (const void *)prefill_bf16_kernel<64, true, WALK, 1>
+                       : (const void *)prefill_bf16_kernel<64, false, WALK, 1>;
+    return strided ? (const void *)prefill_bf16_kernel<128, true, WALK, 1>
+                   : (const void *)prefill_bf16_kernel<128, false, WALK, 1>;
 }
 
-// A dense launch over B = 1 whose grid fills at most half of the device runs
-// as S >= 2 segments of the sequence at once (one packed launch, the later
-// segments from a zero state, then the fold of the states and the correction
-// of the later segments' outputs): S = CUs / (H * d/32) workgroup sets, each
-// segment at least SPLIT_MIN_LEN tokens, at most MAX_SPLIT segments.
+// A dense launch over B = 1 can run as S >= 2 segments of the sequence at
+// once (one packed launch, the later segments from a zero state, then the
+// fold of the states and the correction of the later segments' outputs).
+// The segments take workgroups of njt 32-column tiles.  Two tiles (64
+// columns, d = 128) pass each head's Q and K through L2 twice instead of four
+// times and write every output row slice as one whole 128-byte line: a copy
+// of the kernel with the compute removed streams the 256K, 64-head workload
+// in 3.34 against 4.27 ms.  With njt tiles, S = CUs / (H * d/(32 njt)), each
+// segment at least SPLIT_MIN_LEN tokens and at most MAX_SPLIT segments; the
+// wide tiles are taken unless the narrow ones keep markedly more workgroups
+// busy (few heads on a short sequence: the segment length bounds S).
 constexpr int64_t SPLIT_MIN_LEN = 16384;
 constexpr int MAX_SPLIT = 64;
 
-int prefill_split_segments(int64_t B, int64_t H, int64_t N, int d)
+int prefill_split_plan(int64_t B, int64_t H, int64_t N, int d, int *njt)
 {
+    *njt = 1;
     if (B != 1 || H < 1 || N < 2 * SPLIT_MIN_LEN) return 1;
     const int cus = device_cus();
-    const int64_t wg = H * (d / PJ);
-    int64_t S = cus > 0 ? cus / wg : 1;
-    S = std::min<int64_t>(S, N / SPLIT_MIN_LEN);
-    S = std::min<int64_t>(S, MAX_SPLIT);
-    return S >= 2 ? (int)S : 1;
+    if (cus <= 0) return 1;
+    int best_s = 1;
+    double best = 0.0;
+    for (int t = (d == 128 ? 2 : 1); t >= 1; --t) {
+        const int64_t wg = H * (d / (PJ * t));
+        int64_t S = std::min<int64_t>(cus / wg, N / SPLIT_MIN_LEN);
+        S = std::min<int64_t>(S, MAX_SPLIT);
+        if (S < 2) continue;
+        const double busy = (double)std::min<int64_t>(S * wg, cus) * (t == 2 ? 1.2 : 1.0);
+        if (busy > best) { best = busy; best_s = (int)S; *njt = t; }
+    }
+    return best_s;
 }
 
-// one workgroup per (sequence, head, column slice), never the walk
+// one workgroup per (sequence, head, njt column tiles), never the walk
+// (njt = 2: d = 128, contiguous rows only)
 hipError_t launch_prefill_bf16_nowalk(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                       const float *slopes, uint16_t *out, float *state,
-                                      int64_t seqs, const SeqMap &map, int d, hipStream_t stream)
+                                      int64_t seqs, const SeqMap &map, int d, hipStream_t stream,
+                                      int njt)
 {
     const bool strided = map.in.st != d || map.out.st != d;
+    if (njt != 1 && (njt != 2 || d != 128 || strided)) return hipErrorInvalidValue;
     SeqMap m = map;
     int64_t nseq = seqs;
     void *args[] = {(void *)&q, (void *)&k, (void *)&v, (void *)&slopes,
                     (void *)&out, (void *)&state, (void *)&m, (void *)&nseq};
-    return hipLaunchKernel(prefill_fn<false>(d, strided),
-                           dim3((unsigned)prefill_bf16_grid(seqs, map.H, d)), dim3(NTHREADS), args,
-                           0, stream);
+    const void *fn = njt == 2 ? (const void *)prefill_bf16_kernel<128, false, false, 2>
+                              : prefill_fn<false>(d, strided);
+    return hipLaunchKernel(fn, dim3((unsigned)prefill_bf16_grid(seqs, map.H, d, njt)),
+                           dim3(NTHREADS), args, 0, stream);
 }
 
 hipError_t launch_prefill_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
@@ -1071,7 +1159,7 @@ hipError_t launch_prefill_bf16(const uint16_t *q, const uint16_t *k, const uint1
     const bool strided = map.in.st != d || map.out.st != d;
     const dim3 block(NTHREADS);
     if (!prefill_bf16_walks(seqs, map.H, map.T, d, map.cu != nullptr))
-        return launch_prefill_bf16_nowalk(q, k, v, slopes, out, state, seqs, map, d, stream);
+        return launch_prefill_bf16_nowalk(q, k, v, slopes, out, state, seqs, map, d, stream, 1);
     for (int64_t s0 = 0; s0 < seqs; s0 += WALK_SEQS) {
         SeqMap m = map;
         m.cu = map.cu + s0;
@@ -1080,7 +1168,7 @@ hipError_t launch_prefill_bf16(const uint16_t *q, const uint16_t *k, const uint1
         void *args[] = {(void *)&q, (void *)&k, (void *)&v, (void *)&slopes,
                         (void *)&out, (void *)&st, (void *)&m, (void *)&nseq};
         const hipError_t e = hipLaunchKernel(prefill_fn<true>(d, strided),
-                                             dim3((unsigned)prefill_bf16_grid(1, map.H, d)), block,
+                                             dim3((unsigned)prefill_bf16_grid(1, map.H, d, 1)), block,
                                              args, 0, stream);
         if (e != hipSuccess) return e;
     }

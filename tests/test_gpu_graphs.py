@@ -111,3 +111,40 @@ def test_prefill_chunks_replayed_from_a_graph():
         torch.cuda.synchronize()
         assert torch.equal(out, ref), c
         assert torch.equal(state, ref_state), c
+
+
+def test_split_prefill_noalloc_replayed_from_a_graph():
+    # the allocation-free split prefill (la_prefill_noalloc: its scratch is the
+    # library's own, no allocation under capture) captured once and replayed,
+    # each replay bitwise against the eager call on the same inputs
+    B, H, N, d = 1, 32, 40000, 128
+    if binding.prefill_workspace_bytes(B, H, N, d, DEV) == 0:
+        pytest.skip("no sequence split planned on this device")
+    log(f"graph: la_prefill_noalloc B{B} H{H} N{N} d{d}, 3 replays")
+    lib = binding.load_library()
+    x = inputs.make_prefill(B, H, N, d, torch.bfloat16, seed=143, init_state=True, device=DEV)
+    out = torch.empty_like(x.q)
+    state = x.state.clone()
+
+    def call(o, st):
+        rc = lib.la_prefill_noalloc(x.q.data_ptr(), x.k.data_ptr(), x.v.data_ptr(), x.slopes.data_ptr(),
+                                    o.data_ptr(), st.data_ptr(), B, H, N, d,
+                                    torch.cuda.current_stream().cuda_stream)
+        assert rc == 0
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call(torch.empty_like(out), state.clone())          # the first call finds the scratch
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(out, state)
+    for r in range(3):
+        state.copy_(x.state)
+        g.replay()
+        ref_state = x.state.clone()
+        ref = torch.empty_like(out)
+        call(ref, ref_state)                                 # eager, between the replays
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), r
+        assert torch.equal(state, ref_state), r

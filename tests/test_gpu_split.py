@@ -48,8 +48,10 @@ def unsplit(inp, state):
 
 
 @pytest.mark.parametrize("H,N,slopes", [
-    (32, 40000, None),                                   # 2 segments, ragged, the model's decays
+    (64, 40000, None),                                   # 2 segments, ragged, the model's decays
+    (32, 40000, None),                                   # 2 segments
     (8, 65536 + 77, [0.0, 1e-4, 1e-3, 0.01, 0.1, 1.0, 5.0, math.inf]),   # 4 segments; lambda = 1 .. 0
+    (64, 262144, None),                                  # the 256K workload's shape: 2 segments
     (1, 70000, [1e-4]),                                  # 4 segments, slow decay: full corrections
 ])
 def test_split_matches_oracle(H, N, slopes):
@@ -110,11 +112,16 @@ def test_workspace_rules_are_checked_before_any_launch():
     assert not bool((out == 3.0).all())
 
 
-def test_no_split_when_the_grid_fills_the_device():
-    # 64 heads of 128 fill 256 compute units: la_prefill_ws is la_prefill
+def test_split_plan():
+    # segments of 64-column workgroups (d = 128) or 32-column ones (d = 64):
+    # 64 heads of 128 split in two on 256 compute units, 128 heads of 64 fill
+    # the device unsplit, B > 1 and short sequences never split
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    if cus > 256:
-        pytest.skip("a larger device may split 64 heads")
-    assert binding.prefill_workspace_bytes(1, 64, 262144, 128, DEV) == 0
+    if cus != 256:
+        pytest.skip("the expected plans are those of a 256-CU device")
+    d128 = 64 * 128 * 128 * 4
+    assert binding.prefill_workspace_bytes(1, 64, 262144, 128, DEV) == 2 * d128 + 256
+    assert binding.prefill_workspace_bytes(1, 32, 262144, 128, DEV) == 4 * d128 // 2 + 256
+    assert binding.prefill_workspace_bytes(1, 128, 262144, 64, DEV) == 0
     assert binding.prefill_workspace_bytes(2, 32, 262144, 128, DEV) == 0
-    assert binding.prefill_workspace_bytes(1, 32, 16384, 128, DEV) == 0     # too short to split
+    assert binding.prefill_workspace_bytes(1, 64, 16384, 128, DEV) == 0     # too short to split

@@ -125,7 +125,7 @@ def test_strided_prefill_full_256k_bitwise():
     log(f"strided prefill 256K: B{w.B} H{w.H} N{w.N} d{w.d}")
     x = inputs.make_workload("prefill_256k", device=DEV)
     st_ref = x.state.clone()
-    out_ref = binding.prefill(x.q, x.k, x.v, x.slopes, st_ref)
+    out_ref = binding.prefill(x.q, x.k, x.v, x.slopes, st_ref, split=False)   # la_prefill
     _, (qv, kv, vv) = pack_token_major([x.q, x.k, x.v], pad=0)
     obuf = torch.empty((w.B, w.N, w.H * w.d), dtype=torch.bfloat16, device=DEV)
     st = torch.zeros_like(st_ref)

@@ -82,7 +82,9 @@ DECODE = dict(B=256, H=64, d=128, steps=64, seed=1004)
 MTP = dict(B=256, H=64, T=4, d=128, seed=1006)
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_256k_traffic.txt")
-KERNEL_SRC = os.path.join(ROOT, "long_context_layers_amd", "csrc", "prefill_bf16.hip")
+# the sources of the timed prefill call's kernels (the traffic profile is keyed by their hash)
+KERNEL_SRCS = [os.path.join(ROOT, "long_context_layers_amd", "csrc", f)
+               for f in ("prefill_bf16.hip", "cp.hip")]
 
 
 def prefill_flops(B, H, N, d):
@@ -644,9 +646,10 @@ def measure_cp(dev, stream, reps):
 
 
 def kernel_hash():
-    """sha256 (first 16 hex digits) of the prefill kernel's code with comments
-    and blank space removed, so comment edits keep the recorded counters."""
-    text = open(KERNEL_SRC).read()
+    """sha256 (first 16 hex digits) of the prefill call's kernel sources with
+    comments and blank space removed, so comment edits keep the recorded
+    counters."""
+    text = "\n".join(open(f).read() for f in KERNEL_SRCS)
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", " ", text)
     text = " ".join(text.split())
@@ -690,26 +693,38 @@ def write_traffic_summary(fetch, write, copy_fetch, copy_write, commands, out=TR
     what the same counter reads for a plain device copy of known size; written
     with the hash of the kernel source the counters belong to."""
     B, H, N, d = PREFILL["B"], PREFILL["H"], PREFILL["N"], PREFILL["d"]
-    name = "prefill_bf16_kernel<128, false, false>"
     copy_kib = (1 << 30) / 1024.0
+    # the kernels of one la_prefill_ws call on this workload, in launch order
+    parts = [("split_prep_kernel", "split_prep_kernel"),
+             ("prefill_bf16_kernel<128, false, false, 2>", "prefill_bf16_kernel<128, false, false, 2>"),
+             ("split_fold_kernel", "split_fold_kernel"),
+             ("cp_correct_kernel<128>", "cp_correct_kernel<128>")]
 
     def per(rows, pick):
         return [v for k, g, v in rows if pick(k)]
-    is_pre = lambda k: "prefill_bf16_kernel<128, false, false>" in k
     is_copy = lambda k: "copyBuffer" in k or "copy" in k.lower()
-    f_pre, w_pre = per(_counter_rows(fetch), is_pre), per(_counter_rows(write), is_pre)
+    fetch_rows, write_rows = _counter_rows(fetch), _counter_rows(write)
     f_cp, w_cp = per(_counter_rows(copy_fetch), is_copy), per(_counter_rows(copy_write), is_copy)
-    if not (f_pre and w_pre and f_cp and w_cp):
-        raise SystemExit("missing dispatches in the counter files")
+    if not (f_cp and w_cp):
+        raise SystemExit("missing copy dispatches in the counter files")
     kf, kw = copy_kib / min(f_cp), copy_kib / min(w_cp)      # KiB counted per KiB moved, inverted
     steady = lambda xs: xs[len(xs) // 2:]                     # the first dispatches carry earlier dirt
-    fr = sum(steady(f_pre)) / len(steady(f_pre)) * kf * 1024
-    wr = sum(steady(w_pre)) / len(steady(w_pre)) * kw * 1024
+    raw, fr, wr = [], 0.0, 0.0
+    for label, key in parts:
+        fv, wv = per(fetch_rows, lambda k: key in k), per(write_rows, lambda k: key in k)
+        if not (fv and wv):
+            raise SystemExit(f"missing dispatches of {label} in the counter files")
+        fr += sum(steady(fv)) / len(steady(fv)) * kf * 1024
+        wr += sum(steady(wv)) / len(steady(wv)) * kw * 1024
+        raw += [f"  {label}  FETCH_SIZE {', '.join('%.0f' % x for x in fv)}",
+                f"  {label}  WRITE_SIZE {', '.join('%.0f' % x for x in wv)}"]
     algo = prefill_bytes(B, H, N, d)
     lines = [
-        f"HBM traffic of {name} (the launch bench.py times) on the 256K prefill workload",
-        f"(B={B}, H={H}, N={N}, d={d}, bf16, zero initial state), MI355X, rocprofv3 PMC,",
-        "written by `python bench.py --traffic-summary` from the counter files (no value typed by hand).",
+        "HBM traffic of the prefill call bench.py times (la_prefill_ws: split_prep_kernel,",
+        "prefill_bf16_kernel<128, false, false, 2> over two segments per head, split_fold_kernel,",
+        f"cp_correct_kernel<128>) on the 256K prefill workload (B={B}, H={H}, N={N}, d={d}, bf16,",
+        "zero initial state), MI355X, rocprofv3 PMC, written by `python bench.py --traffic-summary`",
+        "from the counter files (no value typed by hand).",
         "",
         f"kernel_source_sha256_16: {kernel_hash()}   (code with comments and blank space removed)",
         "",
@@ -719,11 +734,11 @@ def write_traffic_summary(fetch, write, copy_fetch, copy_write, commands, out=TR
         "Raw counters (KiB per dispatch, in dispatch order):",
         f"  copy 1 GiB  FETCH_SIZE {', '.join('%.0f' % x for x in f_cp)} -> factor {kf:.4f}",
         f"  copy 1 GiB  WRITE_SIZE {', '.join('%.0f' % x for x in w_cp)} -> factor {kw:.4f}",
-        f"  prefill     FETCH_SIZE {', '.join('%.0f' % x for x in f_pre)}",
-        f"  prefill     WRITE_SIZE {', '.join('%.0f' % x for x in w_pre)}",
+        *raw,
         "",
-        f"Per prefill launch (steady state: the last {len(steady(f_pre))} dispatches averaged, "
-        "calibrated; the counters need a few launches to settle after the inputs are written):",
+        "Per prefill call (each kernel's steady state: the second half of its dispatches averaged,",
+        "calibrated, then summed over the call's kernels; the counters need a few launches to",
+        "settle after the inputs are written):",
         f"  reads  {fr / 1e9:.3f} GB   writes {wr / 1e9:.3f} GB",
         f"hbm_bytes_per_launch: {fr + wr:.0f}",
         f"algorithmic_bytes_per_launch: {algo}   (ratio {(fr + wr) / algo:.4f})",
@@ -919,8 +934,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": "prefill B1 H64 N262144 d128 bf16 from a zero state + one decode "
-                        "step B256 H64 d128 (fp32 states)",
+            "workload": "prefill B1 H64 N262144 d128 bf16 from a zero state (la_prefill_ws: "
+                        "two segments per head on 64-column workgroups, states folded, the "
+                        "second segment corrected) + one decode step B256 H64 d128 (fp32 states)",
             "prefill": {"B": B, "H": H, "N": N, "d": d, "flop_count_block": C_COUNT},
             "decode": {"B": DECODE["B"], "H": DECODE["H"], "d": DECODE["d"]},
         },
@@ -937,7 +953,9 @@ def main():
             "frac": round(gbs / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(),
             "algorithmic_bytes_per_launch": by,
-            "kernel": "prefill_bf16_kernel<128, false, false>",
+            "kernel": "prefill_bf16_kernel<128, false, false, 2> (64-column workgroups, the "
+                      "sequence in two segments per head), timed with the rest of its la_prefill_ws "
+                      "call: split_prep_kernel, split_fold_kernel, cp_correct_kernel<128>",
             "binding_limit": "memory traffic: a copy of the kernel with its compute removed "
                              "(same loads and stores) takes as long; per compute unit, the full "
                              "Q and K blocks every column slice reads through L2 and the output "

@@ -72,11 +72,16 @@ def _pmc_csv(path, rows):
 def test_traffic_summary_is_calibrated_and_keyed_by_the_source(tmp_path, monkeypatch):
     # made-up counters: the copy reads count twice (factor 1/2), writes once;
     # the prefill's steady dispatches (3..) read 6,000,000 KiB and write 4,000,000
-    pre = "void la::(anonymous namespace)::prefill_bf16_kernel<128, false, false>(...)"
+    pre = "void la::(anonymous namespace)::prefill_bf16_kernel<128, false, false, 2>(...)"
+    prep, fold = "la::split_prep_kernel(...)", "la::split_fold_kernel(...)"
+    corr = "void la::(anonymous namespace)::cp_correct_kernel<128>(...)"
     cp = "__amd_rocclr_copyBuffer"
     gib = 1 << 20
-    _pmc_csv(tmp_path / "f.csv", [(pre, 7e6), (pre, 6.5e6), (pre, 6e6), (pre, 6e6)])
-    _pmc_csv(tmp_path / "w.csv", [(pre, 4.5e6), (pre, 4.1e6), (pre, 4e6), (pre, 4e6)])
+    call = lambda a, b, c, e: [(prep, a), (pre, b), (fold, c), (corr, e)]
+    _pmc_csv(tmp_path / "f.csv", call(9, 7e6, 9, 90) + call(9, 6.5e6, 9, 90) +
+             call(1, 6e6, 2, 10) + call(1, 6e6, 2, 10))
+    _pmc_csv(tmp_path / "w.csv", call(9, 4.5e6, 9, 90) + call(9, 4.1e6, 9, 90) +
+             call(3, 4e6, 4, 5) + call(3, 4e6, 4, 5))
     _pmc_csv(tmp_path / "cf.csv", [(cp, 2 * gib), (cp, 2 * gib + 10)])
     _pmc_csv(tmp_path / "cw.csv", [(cp, gib), (cp, gib)])
     out = tmp_path / "traffic.txt"
@@ -85,7 +90,7 @@ def test_traffic_summary_is_calibrated_and_keyed_by_the_source(tmp_path, monkeyp
                                 ["rocprofv3 ..."], out=str(out))
     text = out.read_text()
     assert f"kernel_source_sha256_16: {bench.kernel_hash()}" in text
-    want = (6e6 / 2 + 4e6) * 1024
+    want = ((1 + 6e6 + 2 + 10) / 2 + (3 + 4e6 + 4 + 5)) * 1024
     assert f"hbm_bytes_per_launch: {want:.0f}" in text
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
     assert bench.measured_traffic() == pytest.approx(want)

@@ -720,7 +720,7 @@ struct Scan {
         }
         if constexpr (WALK) {
             const int64_t s1 = wk.seq_at(pos.j + 1);
-            stage_state<D, T0, NTL>(wk.slot, cx.state_of(s1 >= 0 ? s1 : pos.seq), ln.l32 + 32 * ln.h, s1 >= 0);
+            if (s1 >= 0) stage_state<D, T0, NTL>(wk.slot, cx.state_of(s1), ln.l32 + 32 * ln.h, true);
         }
 #pragma unroll
         for (int jt = 0; jt < NJT; ++jt)
@@ -765,6 +765,9 @@ struct Scan {
                 // wait for its staging (issued a sequence ago) then covers no
                 // store of this block
                 const bool more = wk.seq_at(pos.j + 1) >= 0;
+                // the slot's direct loads (a sequence ago) have landed before
+                // it is read or refilled: they count as vector memory
+                asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
                 f32x16 nxt[NTL];
                 if (more) read_staged<D, T0, NTL>(nxt, wk.slot, ln);
                 store_via_slot<D, T0, NTL>(wk.slot, cx.state_of(pos.seq), sacc[0], ln,   // the final state out
@@ -780,8 +783,7 @@ struct Scan {
                     }
                     __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0): the slot reads done
                     const int64_t s2 = wk.seq_at(pos.j + 2);
-                    stage_state<D, T0, NTL>(wk.slot, cx.state_of(s2 >= 0 ? s2 : pos.seq), ln.l32 + 32 * ln.h,
-                                            s2 >= 0);
+                    if (s2 >= 0) stage_state<D, T0, NTL>(wk.slot, cx.state_of(s2), ln.l32 + 32 * ln.h, true);
                 }
             }
         }

@@ -220,6 +220,19 @@ int la_prefill_strided(const void *q, const void *k, const void *v, const float 
                        int64_t out_bstride, int64_t out_hstride, int64_t out_tstride,
                        void *stream);
 
+/*
+ * la_prefill_strided with the sequence split of la_prefill_ws (same plan,
+ * same workspace rules and la_prefill_workspace_bytes; without a split it
+ * runs exactly as la_prefill_strided).  Same results as la_prefill_ws on
+ * contiguous copies of the same values, bitwise.  Source: as la_prefill_ws
+ * and la_prefill_strided.
+ */
+int la_prefill_strided_ws(const void *q, const void *k, const void *v, const float *slopes,
+                          void *out, float *state, int64_t B, int64_t H, int64_t N, int64_t d,
+                          int64_t in_bstride, int64_t in_hstride, int64_t in_tstride,
+                          int64_t out_bstride, int64_t out_hstride, int64_t out_tstride,
+                          void *workspace, int64_t workspace_bytes, void *stream);
+
 int la_prefill_varlen_strided(const void *q, const void *k, const void *v, const float *slopes,
                               const int64_t *cu_seqlens, int64_t nseq, void *out, float *states,
                               int64_t H, int64_t T, int64_t d, int64_t in_hstride,
@@ -406,7 +419,7 @@ const char *la_status_string(int status);
 /* ABI version of this header (incremented on incompatible changes). */
 int la_abi_version(void);
 
-#define LA_ABI_VERSION 4
+#define LA_ABI_VERSION 5
 
 #ifdef __cplusplus
 }

@@ -32,6 +32,8 @@ SIGNATURES = {
     "la_prefill_varlen_f32": ([_P, _P, _P, _P, _P, _I64, _P, _P, _I64, _I64, _I64, _P], _INT),
     "la_prefill_strided": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64,
                             _I64, _I64, _I64, _I64, _I64, _I64, _P], _INT),
+    "la_prefill_strided_ws": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64,
+                               _I64, _I64, _I64, _I64, _I64, _I64, _P, _I64, _P], _INT),
     "la_prefill_varlen_strided": ([_P, _P, _P, _P, _P, _I64, _P, _P, _I64, _I64, _I64,
                                    _I64, _I64, _I64, _I64, _P], _INT),
     "la_decode_step": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], _INT),
@@ -51,7 +53,7 @@ SIGNATURES = {
     "la_prefill_varlen_plan": ([_I64, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_int)], _INT),
     "la_abi_version": ([], _INT),
 }
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 _lock = threading.Lock()
 _lib = None
@@ -145,10 +147,10 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: torch.Ten
     Returns out [B,H,N,d] (same dtype as q).  Enqueued on the current stream.
     bf16 q, k, v (sharing one set of strides) and out may be strided views
     with a unit channel stride, e.g. head-split slices of a token-major
-    projection buffer; such calls go to ``la_prefill_strided``.  Contiguous
-    bf16 calls go to ``la_prefill_ws`` (the sequence split, with a workspace
-    from torch's allocator) when it plans a split, unless ``split`` is False
-    (then ``la_prefill``, as the strided calls).
+    projection buffer; such calls go to ``la_prefill_strided``.  bf16 calls
+    go to ``la_prefill_ws`` / ``la_prefill_strided_ws`` (the sequence split,
+    with a workspace from torch's allocator) when a split is planned, unless
+    ``split`` is False (then ``la_prefill`` / ``la_prefill_strided``).
     """
     if not isinstance(q, torch.Tensor) or q.dim() != 4:
         raise ValueError("q must be a [B,H,N,d] tensor")
@@ -168,7 +170,15 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: torch.Ten
             out = torch.empty((B, H, N, d), dtype=dt, device=dev)
         so = _view(out, "out", dt, dev, (B, H, N, d))
         si = q.stride()[:-1]
+        ws = prefill_workspace_bytes(B, H, N, d, dev) if split else 0
         with torch.cuda.device(dev):
+            if ws > 0:
+                work = torch.empty(ws, dtype=torch.uint8, device=dev)
+                rc = load_library().la_prefill_strided_ws(
+                    q.data_ptr(), k.data_ptr(), v.data_ptr(), slopes.data_ptr(), out.data_ptr(),
+                    state.data_ptr(), B, H, N, d, *si, *so, work.data_ptr(), ws, _stream(dev))
+                _check(rc, "la_prefill_strided_ws")
+                return out
             rc = load_library().la_prefill_strided(
                 q.data_ptr(), k.data_ptr(), v.data_ptr(), slopes.data_ptr(), out.data_ptr(),
                 state.data_ptr(), B, H, N, d, *si, *so, _stream(dev))

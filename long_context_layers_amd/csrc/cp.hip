@@ -66,15 +66,16 @@ struct CorrSmem {
     uint16_t O[TT][D + CPAD];
 };
 
-// rows t0 .. t0 + c - 1 of one (b, h) slice (c = 0 past the end): loads past
-// the range read zero, stores past it are dropped
+// rows t0 .. t0 + c - 1 of one (b, h) slice, ts elements apart (c = 0 past
+// the end): the range ends after the last real row, so loads past it read
+// zero and stores past it are dropped
 template <int D>
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t *base, int64_t t0,
-                                                             int64_t L)
+                                                             int64_t L, int64_t ts)
 {
     const int64_t c = max((int64_t)0, min((int64_t)TT, L - t0));
-    return __builtin_amdgcn_make_buffer_rsrc((void *)(base + t0 * D), (short)0,
-                                             (int)(c * D * 2), RSRC_W3);
+    return __builtin_amdgcn_make_buffer_rsrc((void *)(base + t0 * ts), (short)0,
+                                             c == 0 ? 0 : (int)(((c - 1) * ts + D) * 2), RSRC_W3);
 }
 
 // A workgroup corrects CTOK tokens of one (segment, b, h) in 64-token tiles.
@@ -93,13 +94,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t *base
 // B = Q^T (column = token lane % 32: 16 contiguous bytes of its q row), C
 // register r = column 8 (r / 4) + 4 (lane / 32) + r % 4 of token lane % 32.
 // Segments: segment g of a (b, h) row covers tokens t_off + g * seg .. (up to
-// the row's ntok tokens, hs elements between (b, h) rows) and takes the state
-// s_in + (g * BH + bh) * D * D.  A shard correction is one segment at t_off = 0.
+// the row's ntok tokens) and takes the state s_in + (g * BH + bh) * D * D.  A
+// shard correction is one segment at t_off = 0.  q and out rows: (b, h) rows
+// qhs / ohs elements apart, tokens qts / ots apart (>= D), channels contiguous.
 template <int D>
 __global__ __launch_bounds__(CT) void cp_correct_kernel(
     const uint16_t *__restrict__ q, const float *__restrict__ slopes,
     const float *__restrict__ s_in, uint16_t *__restrict__ out, int64_t H, int64_t BH,
-    int64_t hs, int64_t t_off, int64_t seg, int64_t ntok, int64_t chunks)
+    int64_t qhs, int64_t qts, int64_t ohs, int64_t ots, int64_t t_off, int64_t seg, int64_t ntok,
+    int64_t chunks)
 {
     constexpr int NCT = D / 32;        // 32-column tiles
     constexpr int KS = D / 16;         // 16-wide k steps
@@ -129,18 +132,25 @@ __global__ __launch_bounds__(CT) void cp_correct_kernel(
         for (int e = 0; e < 8; ++e)
             a[ks][e] = (__bf16)S[(16 * ks + 8 * hf + e) * D + 32 * ct + l32];
 
-    const uint16_t *qb = q + bh * hs + a0 * D;
-    uint16_t *ob = out + bh * hs + a0 * D;
+    const uint16_t *qb = q + bh * qhs + a0 * qts;
+    uint16_t *ob = out + bh * ohs + a0 * ots;
+    // thread chunk u: row (tid + CT u) / CPR, 16 bytes at column 8 ((tid + CT u) % CPR)
+    int qoff[NCH], ooff[NCH];
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+        const int c = tid + CT * u, row = c / CPR, col = (c % CPR) * 8;
+        qoff[u] = (int)((row * qts + col) * 2);
+        ooff[u] = (int)((row * ots + col) * 2);
+    }
 
     uint4 rq[NCH], ro[NCH];
     auto fetch = [&](int64_t t0) {
-        const __amdgpu_buffer_rsrc_t rsq = tile_rsrc<D>(qb, t0, L);
-        const __amdgpu_buffer_rsrc_t rso = tile_rsrc<D>(ob, t0, L);
+        const __amdgpu_buffer_rsrc_t rsq = tile_rsrc<D>(qb, t0, L, qts);
+        const __amdgpu_buffer_rsrc_t rso = tile_rsrc<D>(ob, t0, L, ots);
 #pragma unroll
         for (int u = 0; u < NCH; ++u) {
-            const int off = (tid + CT * u) * 16;
-            rq[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsq, off, 0, 0));
-            ro[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rso, off, 0, 0));
+            rq[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsq, qoff[u], 0, 0));
+            ro[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rso, ooff[u], 0, 0));
         }
     };
     fetch(tbeg);
@@ -179,12 +189,12 @@ __global__ __launch_bounds__(CT) void cp_correct_kernel(
             }
         }
         __syncthreads();
-        const __amdgpu_buffer_rsrc_t rst = tile_rsrc<D>(ob, t0, L);
+        const __amdgpu_buffer_rsrc_t rst = tile_rsrc<D>(ob, t0, L, ots);
 #pragma unroll
         for (int u = 0; u < NCH; ++u) {
             const int c = tid + CT * u, row = c / CPR, col = (c % CPR) * 8;
             const uint4 x = *reinterpret_cast<const uint4 *>(&sm.O[row][col]);
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x), rst, c * 16, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x), rst, ooff[u], 0, 0);
         }
     }
 }
@@ -254,15 +264,15 @@ hipError_t launch_cp_fold(const float *loc, const int *lens, int nfold, const fl
 }
 
 static hipError_t launch_correct(const uint16_t *q, const float *slopes, const float *s_in,
-                                 uint16_t *out, int64_t BH, int64_t H, int64_t hs, int64_t t_off,
-                                 int64_t seg, int64_t ntok, int64_t nseg, int d,
-                                 hipStream_t stream)
+                                 uint16_t *out, int64_t BH, int64_t H, int64_t qhs, int64_t qts,
+                                 int64_t ohs, int64_t ots, int64_t t_off, int64_t seg,
+                                 int64_t ntok, int64_t nseg, int d, hipStream_t stream)
 {
     int64_t chunks = (seg + CTOK - 1) / CTOK;
     const dim3 grid((unsigned)(nseg * BH * chunks)), block(CT);
     void *args[] = {(void *)&q, (void *)&slopes, (void *)&s_in, (void *)&out, (void *)&H,
-                    (void *)&BH, (void *)&hs, (void *)&t_off, (void *)&seg, (void *)&ntok,
-                    (void *)&chunks};
+                    (void *)&BH, (void *)&qhs, (void *)&qts, (void *)&ohs, (void *)&ots,
+                    (void *)&t_off, (void *)&seg, (void *)&ntok, (void *)&chunks};
     const void *fn = d == 64 ? (const void *)cp_correct_kernel<64>
                              : (const void *)cp_correct_kernel<128>;
     return hipLaunchKernel(fn, grid, block, args, 0, stream);
@@ -272,7 +282,7 @@ hipError_t launch_cp_correct(const uint16_t *q, const float *slopes, const float
                              uint16_t *out, int64_t B, int64_t H, int64_t L, int d,
                              hipStream_t stream)
 {
-    return launch_correct(q, slopes, s_in, out, B * H, H, L * d, 0, L, L, 1, d, stream);
+    return launch_correct(q, slopes, s_in, out, B * H, H, L * d, d, L * d, d, 0, L, L, 1, d, stream);
 }
 
 int64_t split_workspace_bytes(int64_t H, int nseg, int d)
@@ -283,7 +293,8 @@ int64_t split_workspace_bytes(int64_t H, int nseg, int d)
 hipError_t launch_prefill_bf16_split(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                      const float *slopes, uint16_t *out, float *state,
                                      int64_t H, int64_t N, int d, int nseg, int njt,
-                                     void *workspace, hipStream_t stream)
+                                     const Strides &in, const Strides &ost, void *workspace,
+                                     hipStream_t stream)
 {
     // workspace: nseg state slots [nseg][H][d][d] fp32, then nseg + 1 offsets
     float *slots = static_cast<float *>(workspace);
@@ -306,8 +317,7 @@ hipError_t launch_prefill_bf16_split(const uint16_t *q, const uint16_t *k, const
                                              stream);
         if (e != hipSuccess) return e;
     }
-    const Strides st = {0, N * d, d};
-    const SeqMap map = {cu, H, 0, N, st, st};
+    const SeqMap map = {cu, H, 0, N, {0, in.sh, in.st}, {0, ost.sh, ost.st}};
     hipError_t e = launch_prefill_bf16_nowalk(q, k, v, slopes, out, slots, nseg, map, d, stream, njt);
     if (e != hipSuccess) return e;
     {
@@ -321,7 +331,8 @@ hipError_t launch_prefill_bf16_split(const uint16_t *q, const uint16_t *k, const
         if (e != hipSuccess) return e;
     }
     // segment g >= 1 is corrected with slot g - 1 (the state at its start)
-    return launch_correct(q, slopes, slots, out, H, H, N * d, seg, seg, N, nseg - 1, d, stream);
+    return launch_correct(q, slopes, slots, out, H, H, in.sh, in.st, ost.sh, ost.st, seg, seg, N,
+                          nseg - 1, d, stream);
 }
 
 }  // namespace la

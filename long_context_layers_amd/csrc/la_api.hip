@@ -350,10 +350,11 @@ int la_prefill_ws(const void *q, const void *k, const void *v, const float *slop
         overlap(workspace, need, state, st) || overlap(workspace, need, slopes, H * 4))
         return LA_ERR_INVALID_ARG;
     if (la::prefill_bf16_grid(nseg, H, (int)d, njt) > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+    const la::Strides s = dense_strides(H, N, d);
     return hip_status(la::launch_prefill_bf16_split(
         static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
         static_cast<const uint16_t *>(v), slopes, static_cast<uint16_t *>(out), state, H, N,
-        (int)d, nseg, njt, workspace, static_cast<hipStream_t>(stream)));
+        (int)d, nseg, njt, s, s, workspace, static_cast<hipStream_t>(stream)));
 }
 
 int la_prefill_noalloc(const void *q, const void *k, const void *v, const float *slopes,
@@ -446,6 +447,44 @@ int la_prefill_strided(const void *q, const void *k, const void *v, const float 
         static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
         static_cast<const uint16_t *>(v), slopes, static_cast<uint16_t *>(out), state, B, map,
         (int)d, static_cast<hipStream_t>(stream)));
+}
+
+int la_prefill_strided_ws(const void *q, const void *k, const void *v, const float *slopes,
+                          void *out, float *state, int64_t B, int64_t H, int64_t N, int64_t d,
+                          int64_t in_bstride, int64_t in_hstride, int64_t in_tstride,
+                          int64_t out_bstride, int64_t out_hstride, int64_t out_tstride,
+                          void *workspace, int64_t workspace_bytes, void *stream)
+{
+    if (B < 1 || H < 1 || N < 0) return LA_ERR_INVALID_ARG;
+    int64_t bh;
+    if (!mul_ok(B, H, &bh)) return LA_ERR_INVALID_ARG;
+    const int64_t n[3] = {B, H, N};
+    const int64_t si[3] = {in_bstride, in_hstride, in_tstride};
+    const int64_t so[3] = {out_bstride, out_hstride, out_tstride};
+    const int rc = check_strided(q, k, v, slopes, out, state, n, si, so, bh, d);
+    if (rc != LA_OK) return rc;
+    int njt = 1;
+    const int nseg = la::prefill_split_plan(B, H, N, (int)d, &njt);
+    if (nseg < 2)
+        return la_prefill_strided(q, k, v, slopes, out, state, B, H, N, d, in_bstride, in_hstride,
+                                  in_tstride, out_bstride, out_hstride, out_tstride, stream);
+    const int64_t need = la::split_workspace_bytes(H, nseg, (int)d);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return LA_ERR_INVALID_ARG;
+    int64_t in_bytes = 0, out_bytes = 0;
+    (void)view_span(n, si, d, 2, &in_bytes);          // checked above
+    (void)view_span(n, so, d, 2, &out_bytes);
+    const uint64_t st = (uint64_t)bh * d * d * 4;
+    if (overlap(workspace, need, q, in_bytes) || overlap(workspace, need, k, in_bytes) ||
+        overlap(workspace, need, v, in_bytes) || overlap(workspace, need, out, out_bytes) ||
+        overlap(workspace, need, state, st) || overlap(workspace, need, slopes, H * 4))
+        return LA_ERR_INVALID_ARG;
+    if (la::prefill_bf16_grid(nseg, H, (int)d, njt) > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+    const la::Strides in = {0, in_hstride, in_tstride}, os = {0, out_hstride, out_tstride};
+    return hip_status(la::launch_prefill_bf16_split(
+        static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
+        static_cast<const uint16_t *>(v), slopes, static_cast<uint16_t *>(out), state, H, N,
+        (int)d, nseg, njt, in, os, workspace, static_cast<hipStream_t>(stream)));
 }
 
 int la_prefill_varlen_strided(const void *q, const void *k, const void *v, const float *slopes,

@@ -103,7 +103,7 @@ hipError_t launch_cp_correct(const uint16_t *q, const float *slopes, const float
 int64_t cp_correct_grid(int64_t B, int64_t H, int64_t L);
 
 // one workgroup per (sequence, head, njt 32-column tiles): never the packed
-// walk (njt = 2 only at d = 128 with contiguous rows)
+// walk (njt = 2 only at d = 128)
 hipError_t launch_prefill_bf16_nowalk(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                       const float *slopes, uint16_t *out, float *state,
                                       int64_t seqs, const SeqMap &map, int d, hipStream_t stream,
@@ -117,7 +117,8 @@ int64_t split_workspace_bytes(int64_t H, int nseg, int d);
 hipError_t launch_prefill_bf16_split(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                      const float *slopes, uint16_t *out, float *state,
                                      int64_t H, int64_t N, int d, int nseg, int njt,
-                                     void *workspace, hipStream_t stream);
+                                     const Strides &in, const Strides &out_strides, void *workspace,
+                                     hipStream_t stream);
 
 // number of workgroups one prefill launch over `seqs` sequences uses, with
 // njt 32-column tiles per workgroup

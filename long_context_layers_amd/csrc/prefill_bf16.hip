@@ -1136,20 +1136,21 @@ int prefill_split_plan(int64_t B, int64_t H, int64_t N, int d, int *njt)
 }
 
 // one workgroup per (sequence, head, njt column tiles), never the walk
-// (njt = 2: d = 128, contiguous rows only)
+// (njt = 2: d = 128 only)
 hipError_t launch_prefill_bf16_nowalk(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                       const float *slopes, uint16_t *out, float *state,
                                       int64_t seqs, const SeqMap &map, int d, hipStream_t stream,
                                       int njt)
 {
     const bool strided = map.in.st != d || map.out.st != d;
-    if (njt != 1 && (njt != 2 || d != 128 || strided)) return hipErrorInvalidValue;
+    if (njt != 1 && (njt != 2 || d != 128)) return hipErrorInvalidValue;
     SeqMap m = map;
     int64_t nseq = seqs;
     void *args[] = {(void *)&q, (void *)&k, (void *)&v, (void *)&slopes,
                     (void *)&out, (void *)&state, (void *)&m, (void *)&nseq};
-    const void *fn = njt == 2 ? (const void *)prefill_bf16_kernel<128, false, false, 2>
-                              : prefill_fn<false>(d, strided);
+    const void *fn = njt == 1 ? prefill_fn<false>(d, strided)
+                     : strided ? (const void *)prefill_bf16_kernel<128, true, false, 2>
+                               : (const void *)prefill_bf16_kernel<128, false, false, 2>;
     return hipLaunchKernel(fn, dim3((unsigned)prefill_bf16_grid(seqs, map.H, d, njt)),
                            dim3(NTHREADS), args, 0, stream);
 }

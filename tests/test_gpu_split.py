@@ -14,6 +14,7 @@ import torch
 
 from long_context_layers_amd import binding, inputs
 from tests.gpu_util import BF16_GUARD, BF16_TOL, log, oracle_prefill, rel_l2
+from tests.test_gpu_strided import heads_view, pack_token_major
 
 pytestmark = pytest.mark.gpu
 
@@ -125,3 +126,25 @@ def test_split_plan():
     assert binding.prefill_workspace_bytes(1, 128, 262144, 64, DEV) == 0
     assert binding.prefill_workspace_bytes(2, 32, 262144, 128, DEV) == 0
     assert binding.prefill_workspace_bytes(1, 64, 16384, 128, DEV) == 0     # too short to split
+
+
+@pytest.mark.parametrize("H,N,d", [(32, 40000, 128), (64, 65536 + 300, 64)])
+def test_strided_split_bitwise_equals_contiguous_split(H, N, d):
+    # q, k, v from one token-major projection buffer, out token-major
+    # (la_prefill_strided_ws), against la_prefill_ws on the same values, and
+    # the oracle
+    ws = need_split(1, H, N, d)
+    log(f"strided split prefill B1 H{H} N{N} d{d} (workspace {ws} B)")
+    x = inputs.make_prefill(1, H, N, d, torch.bfloat16, 730 + H, init_state=True, device=DEV)
+    st_ref = x.state.clone()
+    out_ref = binding.prefill(x.q, x.k, x.v, x.slopes, st_ref)
+    _, (qv, kv, vv) = pack_token_major([x.q, x.k, x.v], pad=8)
+    obuf = torch.empty((1, N, H * d), dtype=torch.bfloat16, device=DEV)
+    st = x.state.clone()
+    binding.prefill(qv, kv, vv, x.slopes, st, out=heads_view(obuf, 0, H, d))
+    torch.cuda.synchronize()
+    assert torch.equal(heads_view(obuf, 0, H, d), out_ref) and torch.equal(st, st_ref)
+    o_ref, s_ref = oracle_prefill(x.q, x.k, x.v, x.slopes, x.state)
+    eo, es = rel_l2(out_ref, o_ref), rel_l2(st_ref, s_ref)
+    log(f"  bitwise equal; oracle out {eo:.3e} state {es:.3e}")
+    assert eo <= BF16_GUARD and es <= BF16_GUARD

@@ -120,12 +120,13 @@ def test_strided_varlen_bitwise_equals_contiguous(d):
 def test_strided_prefill_full_256k_bitwise():
     # the 256K-token, 64-head, d = 128 workload in the launch the layer uses:
     # q, k, v read from one token-major projection buffer, out written
-    # token-major, against the contiguous launch on the same values
+    # token-major, against the contiguous launch on the same values (both
+    # with the sequence split: la_prefill_strided_ws against la_prefill_ws)
     w = inputs.WORKLOADS["prefill_256k"]
     log(f"strided prefill 256K: B{w.B} H{w.H} N{w.N} d{w.d}")
     x = inputs.make_workload("prefill_256k", device=DEV)
     st_ref = x.state.clone()
-    out_ref = binding.prefill(x.q, x.k, x.v, x.slopes, st_ref, split=False)   # la_prefill
+    out_ref = binding.prefill(x.q, x.k, x.v, x.slopes, st_ref)    # la_prefill_ws (the split)
     _, (qv, kv, vv) = pack_token_major([x.q, x.k, x.v], pad=0)
     obuf = torch.empty((w.B, w.N, w.H * w.d), dtype=torch.bfloat16, device=DEV)
     st = torch.zeros_like(st_ref)

@@ -373,6 +373,10 @@ def measure_layer_ops(dev, stream, reps, pre_ms):
     def epi_tm():
         binding.group_norm_gate(heads(o_tm), gate, wo, out=y)
 
+    def attn_fused():                                 # QK Norm + RoPE inside the prefill's loads
+        binding.prefill_qk_norm_rope(heads(q), heads(k), heads(v), slopes, st, wq, wq,
+                                     theta=6e6, rot_dim=64, out=outs[2])
+
     with torch.cuda.stream(stream):
         ms_pro = time_launches(stream, pro, reps)
         ms_epi = time_launches(stream, epi, reps)
@@ -380,6 +384,7 @@ def measure_layer_ops(dev, stream, reps, pre_ms):
         ms_attn = time_launches(stream, attn_strided, reps)
         ms_attn_tm = time_launches(stream, attn_strided_tm, reps)
         ms_epi_tm = time_launches(stream, epi_tm, reps)
+        ms_fused = time_launches(stream, attn_fused, reps)
     elems = B * N * H * d
     by_pro, by_epi, by_pro_ip = elems * 2 * 6, elems * 2 * 3, elems * 2 * 4
     del proj, q, k, v, gate, outs, y, o_tm, st
@@ -406,7 +411,14 @@ def measure_layer_ops(dev, stream, reps, pre_ms):
                 "token_major_out": {
                     "prefill_strided_ms": round(ms_attn_tm, 4),
                     "group_norm_gate": line(ms_epi_tm, by_epi, "group_norm_gate_kernel<128>"),
-                    "layer_ms": round(ms_pro_ip + ms_attn_tm + ms_epi_tm, 4)}}}
+                    "layer_ms": round(ms_pro_ip + ms_attn_tm + ms_epi_tm, 4)}},
+            "fused_prologue": {
+                "prefill_qk_norm_rope_ms": round(ms_fused, 4),
+                "tflops": round(fl / (ms_fused * 1e-3) / 1e12, 3),
+                "vs_prefill_alone": round(ms_attn / ms_fused, 4),
+                "kernel": "prefill_bf16_kernel<128, true, false, 2, true> (QK Norm + RoPE in the "
+                          "producers' loads) and cp_correct_kernel<128, true>",
+                "layer_ms": round(ms_fused + ms_epi, 4)}}
 
 
 def measure_decode_multi(dev, stream, reps):

@@ -233,6 +233,39 @@ int la_prefill_strided_ws(const void *q, const void *k, const void *v, const flo
                           int64_t out_bstride, int64_t out_hstride, int64_t out_tstride,
                           void *workspace, int64_t workspace_bytes, void *stream);
 
+/*
+ * la_prefill_qk_norm_rope_ws: the layer's attention step straight from the
+ * projection's raw q and k.  QK Norm and RoPE (exactly as la_qk_norm_rope
+ * defines them: RMSNorm over d with q_norm_weight / k_norm_weight, then
+ * rotate-half RoPE on the first rot_dim channels at position pos0 + t) are
+ * applied inside the attention kernels as each q and k block is loaded, and
+ * the decayed linear attention of la_prefill_strided_ws runs on the result;
+ * normalised q and k are never written to memory.  The same as
+ * la_qk_norm_rope (in place) followed by la_prefill_strided_ws, up to
+ * rounding (here each normalised value is rounded to bf16 once, inside the
+ * kernel, where the two-call path stores it as bf16).
+ * Source: Ling and Ring 2.6 Technical Report, Fig. 2 (QKV projection -> QK
+ * Norm -> RoPE -> linear attention) and §4.3 (QK Norm + RoPE fused into one
+ * kernel; here into the attention kernel itself), §2.1.1 (epsilon 1e-6, base
+ * 6e6, rotary dims 64 of 128).
+ *   q, k, v, slopes, out, state, the strides, workspace: as la_prefill_strided_ws
+ *                (the same split plan and la_prefill_workspace_bytes).
+ *   q_norm_weight, k_norm_weight  [d] fp32, 16-byte aligned.
+ *   theta, rot_dim, pos0: as la_qk_norm_rope; every batch row starts at pos0.
+ *   eps        a normal positive float (at least FLT_MIN; zero or subnormal
+ *              gives LA_ERR_INVALID_ARG): rows past the end of a block are
+ *              loaded as zeros and must normalise to zeros.
+ *   d          128 only (other head dims give LA_ERR_UNSUPPORTED);
+ *              rot_dim in {0, 16, 32, 64, 128}.
+ */
+int la_prefill_qk_norm_rope_ws(const void *q, const void *k, const void *v, const float *slopes,
+                               const float *q_norm_weight, const float *k_norm_weight,
+                               double theta, int64_t rot_dim, int64_t pos0, float eps, void *out,
+                               float *state, int64_t B, int64_t H, int64_t N, int64_t d,
+                               int64_t in_bstride, int64_t in_hstride, int64_t in_tstride,
+                               int64_t out_bstride, int64_t out_hstride, int64_t out_tstride,
+                               void *workspace, int64_t workspace_bytes, void *stream);
+
 int la_prefill_varlen_strided(const void *q, const void *k, const void *v, const float *slopes,
                               const int64_t *cu_seqlens, int64_t nseq, void *out, float *states,
                               int64_t H, int64_t T, int64_t d, int64_t in_hstride,
@@ -419,7 +452,7 @@ const char *la_status_string(int status);
 /* ABI version of this header (incremented on incompatible changes). */
 int la_abi_version(void);
 
-#define LA_ABI_VERSION 5
+#define LA_ABI_VERSION 6
 
 #ifdef __cplusplus
 }

@@ -34,6 +34,9 @@ SIGNATURES = {
                             _I64, _I64, _I64, _I64, _I64, _I64, _P], _INT),
     "la_prefill_strided_ws": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64,
                                _I64, _I64, _I64, _I64, _I64, _I64, _P, _I64, _P], _INT),
+    "la_prefill_qk_norm_rope_ws": ([_P, _P, _P, _P, _P, _P, ctypes.c_double, _I64, _I64,
+                                    ctypes.c_float, _P, _P, _I64, _I64, _I64, _I64,
+                                    _I64, _I64, _I64, _I64, _I64, _I64, _P, _I64, _P], _INT),
     "la_prefill_varlen_strided": ([_P, _P, _P, _P, _P, _I64, _P, _P, _I64, _I64, _I64,
                                    _I64, _I64, _I64, _I64, _P], _INT),
     "la_decode_step": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], _INT),
@@ -53,7 +56,7 @@ SIGNATURES = {
     "la_prefill_varlen_plan": ([_I64, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_int)], _INT),
     "la_abi_version": ([], _INT),
 }
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 _lock = threading.Lock()
 _lib = None
@@ -206,6 +209,52 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: torch.Ten
         rc = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), slopes.data_ptr(), out.data_ptr(),
                 state.data_ptr(), B, H, N, d, _stream(dev))
     _check(rc, "la_prefill" if dt == torch.bfloat16 else "la_prefill_f32")
+    return out
+
+
+def prefill_qk_norm_rope(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: torch.Tensor,
+                         state: torch.Tensor, q_norm_weight: torch.Tensor,
+                         k_norm_weight: torch.Tensor, theta: float = 6.0e6, rot_dim: int = 64,
+                         pos0: int = 0, eps: float = 1e-6,
+                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The prefill straight from the projection's raw q and k
+    (``la_prefill_qk_norm_rope_ws``): QK RMSNorm + RoPE (as ``qk_norm_rope``
+    defines them) applied inside the attention kernels, then the decayed
+    linear attention.
+
+    q, k, v: [B,H,N,128] bf16 views sharing one set of strides with a unit
+    channel stride (e.g. head-split slices of a packed [B,N,4*H*d]
+    projection output); weights [128] fp32; state [B,H,d,d] fp32 in/out.
+    Returns out [B,H,N,d] (or writes the given bf16 view).  The sequence
+    split's workspace, when planned, comes from torch's allocator.
+    """
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a [B,H,N,d] tensor")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("prefill_qk_norm_rope runs on GPU tensors only (no CPU path)")
+    B, H, N, d = q.shape
+    dt = torch.bfloat16
+    si = _view(q, "q", dt, dev, (B, H, N, d))
+    for t, n in ((k, "k"), (v, "v")):
+        if _view(t, n, dt, dev, (B, H, N, d)) != si:
+            raise ValueError("q, k and v must share one set of strides")
+    _need(slopes, "slopes", torch.float32, dev, (H,))
+    _need(state, "state", torch.float32, dev, (B, H, d, d))
+    _need(q_norm_weight, "q_norm_weight", torch.float32, dev, (d,))
+    _need(k_norm_weight, "k_norm_weight", torch.float32, dev, (d,))
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=dt, device=dev)
+    so = _view(out, "out", dt, dev, (B, H, N, d))
+    ws = prefill_workspace_bytes(B, H, N, d, dev)
+    with torch.cuda.device(dev):
+        work = torch.empty(ws, dtype=torch.uint8, device=dev) if ws else None
+        rc = load_library().la_prefill_qk_norm_rope_ws(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), slopes.data_ptr(), q_norm_weight.data_ptr(),
+            k_norm_weight.data_ptr(), float(theta), rot_dim, pos0, float(eps), out.data_ptr(),
+            state.data_ptr(), B, H, N, d, *si, *so, None if work is None else work.data_ptr(), ws,
+            _stream(dev))
+    _check(rc, "la_prefill_qk_norm_rope_ws")
     return out
 
 

@@ -16,6 +16,7 @@
 //   by HBM: q read, out read and written, 6d bytes per token-head; at
 //   d = 128 that is 42.7 flop per byte against a ridge near 315.
 #include "la_internal.h"
+#include "qk_prologue.h"
 
 namespace la {
 namespace {
@@ -97,13 +98,16 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t *base
 // the row's ntok tokens) and takes the state s_in + (g * BH + bh) * D * D.  A
 // shard correction is one segment at t_off = 0.  q and out rows: (b, h) rows
 // qhs / ohs elements apart, tokens qts / ots apart (>= D), channels contiguous.
-template <int D>
+// PRO: q is the projection's raw q, normalised and rotated (QK Norm + RoPE at
+// position pr.pos0 + token) as each tile arrives, as the prefill does.
+template <int D, bool PRO>
 __global__ __launch_bounds__(CT) void cp_correct_kernel(
     const uint16_t *__restrict__ q, const float *__restrict__ slopes,
     const float *__restrict__ s_in, uint16_t *__restrict__ out, int64_t H, int64_t BH,
     int64_t qhs, int64_t qts, int64_t ohs, int64_t ots, int64_t t_off, int64_t seg, int64_t ntok,
-    int64_t chunks)
+    int64_t chunks, QkPrologue pr)
 {
+    static_assert(!PRO || D == pro::PD, "the fused prologue handles 128-channel rows");
     constexpr int NCT = D / 32;        // 32-column tiles
     constexpr int KS = D / 16;         // 16-wide k steps
     constexpr int NCH = TT * D / 8 / CT;   // 16-byte chunks per thread per tile
@@ -134,12 +138,22 @@ __global__ __launch_bounds__(CT) void cp_correct_kernel(
 
     const uint16_t *qb = q + bh * qhs + a0 * qts;
     uint16_t *ob = out + bh * ohs + a0 * ots;
-    // thread chunk u: row (tid + CT u) / CPR, 16 bytes at column 8 ((tid + CT u) % CPR)
-    int qoff[NCH], ooff[NCH];
+    // thread chunk u: row (tid + CT u) / CPR, 16 bytes at column 8 ((tid + CT u) % CPR);
+    // with PRO q takes the prologue's layout instead: row tid / 4, chunks tid % 4 + 4u
+    pro::Lane pl;
+    if constexpr (PRO) {
+        static_assert(NCH == pro::NC, "the prologue's row layout");
+        QkPrologue qonly = pr;
+        qonly.kw = nullptr;
+        pl.init(qonly, tid % pro::LPR);
+    }
+    int qrow[NCH], qcol[NCH], qoff[NCH], ooff[NCH];
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
         const int c = tid + CT * u, row = c / CPR, col = (c % CPR) * 8;
-        qoff[u] = (int)((row * qts + col) * 2);
+        qrow[u] = PRO ? tid / pro::LPR : row;
+        qcol[u] = PRO ? (tid % pro::LPR + pro::LPR * u) * 8 : col;
+        qoff[u] = (int)((qrow[u] * qts + qcol[u]) * 2);
         ooff[u] = (int)((row * ots + col) * 2);
     }
 
@@ -156,10 +170,14 @@ __global__ __launch_bounds__(CT) void cp_correct_kernel(
     fetch(tbeg);
     for (int it = 0; it < ntile; ++it) {
         const int64_t t0 = tbeg + (int64_t)it * TT;
+        if constexpr (PRO) {                 // row tid/4 at position pos0 + a0 + t0 + tid/4
+            const pro::RowAngles a = pro::row_angles(pl, pr.pos0 + a0 + t0 + tid / pro::LPR);
+            pro::norm_rope(rq, pl.wq, pl, a, pr.eps);
+        }
 #pragma unroll
         for (int u = 0; u < NCH; ++u) {
             const int c = tid + CT * u, row = c / CPR, col = (c % CPR) * 8;
-            *reinterpret_cast<uint4 *>(&sm.Q[row][col]) = rq[u];
+            *reinterpret_cast<uint4 *>(&sm.Q[qrow[u]][qcol[u]]) = rq[u];
             *reinterpret_cast<uint4 *>(&sm.O[row][col]) = ro[u];
         }
         __syncthreads();
@@ -266,15 +284,19 @@ hipError_t launch_cp_fold(const float *loc, const int *lens, int nfold, const fl
 static hipError_t launch_correct(const uint16_t *q, const float *slopes, const float *s_in,
                                  uint16_t *out, int64_t BH, int64_t H, int64_t qhs, int64_t qts,
                                  int64_t ohs, int64_t ots, int64_t t_off, int64_t seg,
-                                 int64_t ntok, int64_t nseg, int d, hipStream_t stream)
+                                 int64_t ntok, int64_t nseg, int d, hipStream_t stream,
+                                 const QkPrologue *pro = nullptr)
 {
+    if (pro && d != 128) return hipErrorInvalidValue;
     int64_t chunks = (seg + CTOK - 1) / CTOK;
     const dim3 grid((unsigned)(nseg * BH * chunks)), block(CT);
+    QkPrologue pr = pro ? *pro : QkPrologue{nullptr, nullptr, 0.0, 0, 0.0f, 0};
     void *args[] = {(void *)&q, (void *)&slopes, (void *)&s_in, (void *)&out, (void *)&H,
                     (void *)&BH, (void *)&qhs, (void *)&qts, (void *)&ohs, (void *)&ots,
-                    (void *)&t_off, (void *)&seg, (void *)&ntok, (void *)&chunks};
-    const void *fn = d == 64 ? (const void *)cp_correct_kernel<64>
-                             : (const void *)cp_correct_kernel<128>;
+                    (void *)&t_off, (void *)&seg, (void *)&ntok, (void *)&chunks, (void *)&pr};
+    const void *fn = pro ? (const void *)cp_correct_kernel<128, true>
+                     : d == 64 ? (const void *)cp_correct_kernel<64, false>
+                               : (const void *)cp_correct_kernel<128, false>;
     return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 
@@ -294,7 +316,7 @@ hipError_t launch_prefill_bf16_split(const uint16_t *q, const uint16_t *k, const
                                      const float *slopes, uint16_t *out, float *state,
                                      int64_t H, int64_t N, int d, int nseg, int njt,
                                      const Strides &in, const Strides &ost, void *workspace,
-                                     hipStream_t stream)
+                                     hipStream_t stream, const QkPrologue *pro)
 {
     // workspace: nseg state slots [nseg][H][d][d] fp32, then nseg + 1 offsets
     float *slots = static_cast<float *>(workspace);
@@ -318,7 +340,8 @@ hipError_t launch_prefill_bf16_split(const uint16_t *q, const uint16_t *k, const
         if (e != hipSuccess) return e;
     }
     const SeqMap map = {cu, H, 0, N, {0, in.sh, in.st}, {0, ost.sh, ost.st}};
-    hipError_t e = launch_prefill_bf16_nowalk(q, k, v, slopes, out, slots, nseg, map, d, stream, njt);
+    hipError_t e = launch_prefill_bf16_nowalk(q, k, v, slopes, out, slots, nseg, map, d, stream, njt,
+                                              pro);
     if (e != hipSuccess) return e;
     {
         const int64_t blocks = (n4 + FT - 1) / FT;
@@ -332,7 +355,7 @@ hipError_t launch_prefill_bf16_split(const uint16_t *q, const uint16_t *k, const
     }
     // segment g >= 1 is corrected with slot g - 1 (the state at its start)
     return launch_correct(q, slopes, slots, out, H, H, in.sh, in.st, ost.sh, ost.st, seg, seg, N,
-                          nseg - 1, d, stream);
+                          nseg - 1, d, stream, pro);
 }
 
 }  // namespace la

@@ -6,6 +6,8 @@
 
 #include <stdint.h>
 
+#include <cfloat>
+
 #include <atomic>
 #include <mutex>
 
@@ -449,25 +451,35 @@ int la_prefill_strided(const void *q, const void *k, const void *v, const float 
         (int)d, static_cast<hipStream_t>(stream)));
 }
 
-int la_prefill_strided_ws(const void *q, const void *k, const void *v, const float *slopes,
-                          void *out, float *state, int64_t B, int64_t H, int64_t N, int64_t d,
-                          int64_t in_bstride, int64_t in_hstride, int64_t in_tstride,
-                          int64_t out_bstride, int64_t out_hstride, int64_t out_tstride,
-                          void *workspace, int64_t workspace_bytes, void *stream)
+namespace {
+
+// la_prefill_strided_ws, and with pro the same launches with the fused QK Norm + RoPE
+int prefill_strided_ws(const void *q, const void *k, const void *v, const float *slopes, void *out,
+                       float *state, int64_t B, int64_t H, int64_t N, int64_t d,
+                       const int64_t si[3], const int64_t so[3], void *workspace,
+                       int64_t workspace_bytes, void *stream, const la::QkPrologue *pro)
 {
     if (B < 1 || H < 1 || N < 0) return LA_ERR_INVALID_ARG;
     int64_t bh;
     if (!mul_ok(B, H, &bh)) return LA_ERR_INVALID_ARG;
     const int64_t n[3] = {B, H, N};
-    const int64_t si[3] = {in_bstride, in_hstride, in_tstride};
-    const int64_t so[3] = {out_bstride, out_hstride, out_tstride};
     const int rc = check_strided(q, k, v, slopes, out, state, n, si, so, bh, d);
     if (rc != LA_OK) return rc;
     int njt = 1;
     const int nseg = la::prefill_split_plan(B, H, N, (int)d, &njt);
-    if (nseg < 2)
-        return la_prefill_strided(q, k, v, slopes, out, state, B, H, N, d, in_bstride, in_hstride,
-                                  in_tstride, out_bstride, out_hstride, out_tstride, stream);
+    if (nseg < 2) {
+        if (la::prefill_bf16_grid(B, H, (int)d) > 0x7fffffff) return LA_ERR_UNSUPPORTED;
+        if (N == 0) return LA_OK;
+        const la::SeqMap map = {nullptr, H, N, 0, {si[0], si[1], si[2]}, {so[0], so[1], so[2]}};
+        const uint16_t *q16 = static_cast<const uint16_t *>(q), *k16 = static_cast<const uint16_t *>(k),
+                       *v16 = static_cast<const uint16_t *>(v);
+        uint16_t *o16 = static_cast<uint16_t *>(out);
+        const hipStream_t st = static_cast<hipStream_t>(stream);
+        return hip_status(pro ? la::launch_prefill_bf16_nowalk(q16, k16, v16, slopes, o16, state, B,
+                                                               map, (int)d, st, 1, pro)
+                              : la::launch_prefill_bf16(q16, k16, v16, slopes, o16, state, B, map,
+                                                        (int)d, st));
+    }
     const int64_t need = la::split_workspace_bytes(H, nseg, (int)d);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
         return LA_ERR_INVALID_ARG;
@@ -479,12 +491,52 @@ int la_prefill_strided_ws(const void *q, const void *k, const void *v, const flo
         overlap(workspace, need, v, in_bytes) || overlap(workspace, need, out, out_bytes) ||
         overlap(workspace, need, state, st) || overlap(workspace, need, slopes, H * 4))
         return LA_ERR_INVALID_ARG;
+    if (pro && (overlap(workspace, need, pro->qw, d * 4) || overlap(workspace, need, pro->kw, d * 4)))
+        return LA_ERR_INVALID_ARG;
     if (la::prefill_bf16_grid(nseg, H, (int)d, njt) > 0x7fffffff) return LA_ERR_UNSUPPORTED;
-    const la::Strides in = {0, in_hstride, in_tstride}, os = {0, out_hstride, out_tstride};
+    const la::Strides in = {0, si[1], si[2]}, os = {0, so[1], so[2]};
     return hip_status(la::launch_prefill_bf16_split(
         static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
         static_cast<const uint16_t *>(v), slopes, static_cast<uint16_t *>(out), state, H, N,
-        (int)d, nseg, njt, in, os, workspace, static_cast<hipStream_t>(stream)));
+        (int)d, nseg, njt, in, os, workspace, static_cast<hipStream_t>(stream), pro));
+}
+
+}  // namespace
+
+int la_prefill_strided_ws(const void *q, const void *k, const void *v, const float *slopes,
+                          void *out, float *state, int64_t B, int64_t H, int64_t N, int64_t d,
+                          int64_t in_bstride, int64_t in_hstride, int64_t in_tstride,
+                          int64_t out_bstride, int64_t out_hstride, int64_t out_tstride,
+                          void *workspace, int64_t workspace_bytes, void *stream)
+{
+    const int64_t si[3] = {in_bstride, in_hstride, in_tstride};
+    const int64_t so[3] = {out_bstride, out_hstride, out_tstride};
+    return prefill_strided_ws(q, k, v, slopes, out, state, B, H, N, d, si, so, workspace,
+                              workspace_bytes, stream, nullptr);
+}
+
+int la_prefill_qk_norm_rope_ws(const void *q, const void *k, const void *v, const float *slopes,
+                               const float *q_norm_weight, const float *k_norm_weight,
+                               double theta, int64_t rot_dim, int64_t pos0, float eps, void *out,
+                               float *state, int64_t B, int64_t H, int64_t N, int64_t d,
+                               int64_t in_bstride, int64_t in_hstride, int64_t in_tstride,
+                               int64_t out_bstride, int64_t out_hstride, int64_t out_tstride,
+                               void *workspace, int64_t workspace_bytes, void *stream)
+{
+    if (d != 128) return LA_ERR_UNSUPPORTED;
+    if (!q_norm_weight || !k_norm_weight || !aligned(q_norm_weight, 16) ||
+        !aligned(k_norm_weight, 16))
+        return LA_ERR_INVALID_ARG;
+    if (rot_dim != 0 && !pow2_in(rot_dim, 16, d)) return LA_ERR_UNSUPPORTED;
+    if (rot_dim != 0 && !(theta > 1.0)) return LA_ERR_INVALID_ARG;      // also rejects NaN
+    if (N < 0 || pos0 < 0 || pos0 > INT64_MAX - N) return LA_ERR_INVALID_ARG;
+    // rows past a block's end load as zeros and must normalise to zeros
+    if (!(eps >= FLT_MIN) || !(eps <= FLT_MAX)) return LA_ERR_INVALID_ARG;
+    const la::QkPrologue pro = {q_norm_weight, k_norm_weight, theta, (int)rot_dim, eps, pos0};
+    const int64_t si[3] = {in_bstride, in_hstride, in_tstride};
+    const int64_t so[3] = {out_bstride, out_hstride, out_tstride};
+    return prefill_strided_ws(q, k, v, slopes, out, state, B, H, N, d, si, so, workspace,
+                              workspace_bytes, stream, &pro);
 }
 
 int la_prefill_varlen_strided(const void *q, const void *k, const void *v, const float *slopes,

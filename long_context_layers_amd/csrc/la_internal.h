@@ -51,6 +51,16 @@ __device__ __forceinline__ int64_t seq_len(const SeqMap &m, int64_t seq)
     return min(max(m.cu[seq + 1], a), m.T) - a;
 }
 
+// QK Norm + RoPE fused into the prefill's loads of q and k (kernel argument;
+// the arithmetic is in qk_prologue.h)
+struct QkPrologue {
+    const float *qw, *kw;     // [128] fp32 RMSNorm weights of q and k
+    double theta;             // RoPE base (> 1 when rot > 0)
+    int rot;                  // rotary dims: 0, 16, 32, 64 or 128
+    float eps;                // RMSNorm epsilon (a normal positive float)
+    int64_t pos0;             // position of a sequence's first token
+};
+
 // ---- launchers (return the launch status; arguments already validated) ----
 // Prefill over `seqs` sequences (B for dense launches, nseq for packed ones).
 hipError_t launch_prefill_bf16(const uint16_t *q, const uint16_t *k, const uint16_t *v,
@@ -104,10 +114,13 @@ int64_t cp_correct_grid(int64_t B, int64_t H, int64_t L);
 
 // one workgroup per (sequence, head, njt 32-column tiles): never the packed
 // walk (njt = 2 only at d = 128)
+// (pro: QK Norm + RoPE on q and k as they are loaded, d = 128; positions
+// pro->pos0 + t, t counted from a dense sequence's start or, in a packed
+// launch, from the first packed token: the segments of one sequence)
 hipError_t launch_prefill_bf16_nowalk(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                       const float *slopes, uint16_t *out, float *state,
                                       int64_t seqs, const SeqMap &map, int d, hipStream_t stream,
-                                      int njt);
+                                      int njt, const QkPrologue *pro = nullptr);
 
 // the sequence split of a dense B = 1 prefill: segments per row (1 = no
 // split) on the current device and the column tiles per workgroup (*njt), the
@@ -118,7 +131,7 @@ hipError_t launch_prefill_bf16_split(const uint16_t *q, const uint16_t *k, const
                                      const float *slopes, uint16_t *out, float *state,
                                      int64_t H, int64_t N, int d, int nseg, int njt,
                                      const Strides &in, const Strides &out_strides, void *workspace,
-                                     hipStream_t stream);
+                                     hipStream_t stream, const QkPrologue *pro = nullptr);
 
 // number of workgroups one prefill launch over `seqs` sequences uses, with
 // njt 32-column tiles per workgroup

@@ -70,6 +70,7 @@
 // c0 + 4 (l16 % 4) of a row-major tile, it receives column c0 + l16 of rows
 // r0 .. r0 + 3: a k-contiguous MFMA operand for a contraction over rows.
 #include "la_internal.h"
+#include "qk_prologue.h"
 
 #include <algorithm>
 #include <atomic>
@@ -91,8 +92,11 @@ constexpr int PJ = 32;        // state / output columns of one column tile
 constexpr int NCONS = 4;      // consumer waves
 constexpr int PT = 256;       // producer threads (4 waves)
 constexpr int NTHREADS = 64 * NCONS + PT;
-constexpr int NSET = 4;       // producer register sets (blocks in flight; even)
-static_assert(NSET % 2 == 0, "set i stages into LDS buffer i % 2");
+// producer register sets (blocks in flight; even): 4, or 2 with the fused
+// QK prologue (PRO), whose per-lane constants and arithmetic need the registers
+template <bool PRO>
+constexpr int nset() { return PRO ? 2 : 4; }
+static_assert(nset<false>() % 2 == 0 && nset<true>() % 2 == 0, "set i stages into LDS buffer i % 2");
 constexpr int QPAD = 8;       // bf16 padding of Q and state-copy rows
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -147,6 +151,7 @@ struct alignas(16) Smem {
 struct Pos {
     int64_t seq, t0, n, in0, out0;
     int j;
+    int64_t tok0;               // the sequence's first token in a packed launch (0: dense)
 };
 
 // The non-empty sequences of a walking launch, in order, with their clamped
@@ -207,9 +212,10 @@ struct Walk {
     __device__ static int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
     // WALK: the first block of table entry j (no tokens past the table's end)
     __device__ Pos entry(int j) const {
-        Pos p = {nseq, 0, 0, 0, 0, j};
+        Pos p = {nseq, 0, 0, 0, 0, j, 0};
         if (j < uni(tb->count)) {
             const int64_t a = uni(tb->start[j]);
+            p.tok0 = a;
             p.seq = uni(tb->seq[j]);
             p.n = uni(tb->len[j]);
             p.in0 = h * map.in.sh + a * map.in.st;
@@ -221,8 +227,9 @@ struct Walk {
         if constexpr (WALK) {
             return entry(0);
         } else {
-            Pos p = {seq, 0, 0, 0, 0, 0};
+            Pos p = {seq, 0, 0, 0, 0, 0, 0};
             seq_slice(map, seq, h, &p.in0, &p.out0, &p.n);
+            if (map.cu) p.tok0 = min(max(map.cu[seq], (int64_t)0), map.T);
             return p;
         }
     }
@@ -248,7 +255,7 @@ struct Ctx {                          // per-thread constants of one workgroup
     const uint16_t *q, *k, *v;        // the launch's inputs (slices at Pos::in0)
     uint16_t *o;                      // its output (slices at Pos::out0)
     float *state;                     // its states, [sequence][H][D][D]
-    int64_t H, h, nblk;               // nblk: blocks processed (a multiple of NSET)
+    int64_t H, h, nblk;               // nblk: blocks processed (a multiple of the producer's sets)
     int ts, ots;                      // token strides (elements) of q/k/v and of out (<= 2^24)
     float s;
     int j0;
@@ -264,6 +271,7 @@ struct Regs {                        // one block's share of a producer thread
     static constexpr int NQ = PC * D / 8 / PT;   // 16-byte chunks of Q (and of K)
     uint4 q[NQ], k[NQ], v[NJT];      // v[t]: column tile t of the V slice
     int c;                           // tokens in the block
+    int64_t pos;                     // its first token's place in the packed token order
 };
 
 template <int D, int NJT>
@@ -300,39 +308,73 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
     return make_uint4(x[0], x[1], x[2], x[3]);
 }
 
-template <int D, int NJT>
+// The loads of one block into a register set: the parts PARTS of it (a mask
+// of PART_Q, PART_K, PART_V), and its tokens and position with PART_META.
+// (PRO: the quad layout's offsets are ad.qk[0] + 64 u, immediate offsets of
+// one register.)
+constexpr int PART_Q = 1, PART_K = 2, PART_V = 4, PART_META = 8, PART_ALL = 15;
+
+template <int D, int NJT, bool PRO, int PARTS = PART_ALL>
 __device__ __forceinline__ void load_block(Regs<D, NJT> &r, const Ctx<D> &cx, const Pos &p,
                                            const Addr<D, NJT> &ad)
 {
-    const __amdgpu_buffer_rsrc_t rq = block_rsrc<D>(cx.q + p.in0, p.t0, p.n, cx.ts);
-    const __amdgpu_buffer_rsrc_t rk = block_rsrc<D>(cx.k + p.in0, p.t0, p.n, cx.ts);
-    const __amdgpu_buffer_rsrc_t rv = block_rsrc<D>(cx.v + p.in0, p.t0, p.n, cx.ts);
+    if constexpr ((PARTS & (PART_Q | PART_K)) != 0) {
+        const __amdgpu_buffer_rsrc_t rq = block_rsrc<D>(cx.q + p.in0, p.t0, p.n, cx.ts);
+        const __amdgpu_buffer_rsrc_t rk = block_rsrc<D>(cx.k + p.in0, p.t0, p.n, cx.ts);
 #pragma unroll
-    for (int u = 0; u < Regs<D, NJT>::NQ; ++u) {
-        r.q[u] = bload16(rq, ad.qk[u]);
-        r.k[u] = bload16(rk, ad.qk[u]);
+        for (int u = 0; u < Regs<D, NJT>::NQ; ++u) {
+            const uint32_t off = PRO ? ad.qk[0] + 16 * pro::LPR * u : ad.qk[u];
+            if constexpr ((PARTS & PART_Q) != 0) r.q[u] = bload16(rq, off);
+            if constexpr ((PARTS & PART_K) != 0) r.k[u] = bload16(rk, off);
+        }
     }
+    if constexpr ((PARTS & PART_V) != 0) {
+        const __amdgpu_buffer_rsrc_t rv = block_rsrc<D>(cx.v + p.in0, p.t0, p.n, cx.ts);
 #pragma unroll
-    for (int t = 0; t < NJT; ++t) r.v[t] = bload16(rv, ad.v[t]);
-    r.c = block_len(p.t0, p.n);
+        for (int t = 0; t < NJT; ++t) r.v[t] = bload16(rv, ad.v[0] + 2 * PJ * t);
+    }
+    if constexpr ((PARTS & PART_META) != 0) {
+        r.c = block_len(p.t0, p.n);
+        r.pos = p.tok0 + p.t0;
+    }
 }
 
 __device__ __forceinline__ uint32_t scale_pair(uint32_t x, float w) {
     return pack_bf16x2(bf16_to_f32(x & 0xffffu) * w, bf16_to_f32(x >> 16) * w);
 }
 
-// registers -> LDS buffer BUF; wv = lambda^(c-1-b) for this thread's token b
-// (thread p holds 16 bytes of V row p / 4 in each column tile)
-template <int D, int NJT, int BUF>
+// Q/K chunk u of producer thread p: its row of the block and 16-byte chunk.
+// Without the prologue 16 lanes (D = 128) cover a row, chunk p % (D/8) of
+// rows p / (D/8) + u PT / (D/8); with it (PRO) a quad of lanes covers one
+// row p / 4, chunks p % 4 + 4u (the prologue's layout: one position per lane).
+template <int D, bool PRO>
+__device__ __forceinline__ void qk_slot(int p, int u, int &row, int &c8)
+{
+    if constexpr (PRO) {
+        row = p / pro::LPR;
+        c8 = p % pro::LPR + pro::LPR * u;
+    } else {
+        row = (p + PT * u) / (D / 8);
+        c8 = p % (D / 8);
+    }
+}
+
+// registers -> LDS buffer BUF: the parts PARTS of the set; wv = lambda^(c-1-b)
+// for this thread's token b (thread p holds 16 bytes of V row p / 4 in each
+// column tile)
+template <int D, int NJT, int BUF, bool PRO, int PARTS = PART_ALL>
 __device__ __forceinline__ void store_block(const Regs<D, NJT> &r, Smem<D, NJT> &sm, int p, float wv)
 {
 #pragma unroll
     for (int u = 0; u < Regs<D, NJT>::NQ; ++u) {
-        const int ch = p + PT * u;
-        const int row = ch / (D / 8), c8 = ch % (D / 8);
-        *reinterpret_cast<uint4 *>(&sm.Q[BUF][row][c8 * 8]) = r.q[u];
-        *reinterpret_cast<uint4 *>(&sm.K[BUF][row][(c8 ^ kswz(row)) * 8]) = r.k[u];
+        int row, c8;
+        qk_slot<D, PRO>(p, u, row, c8);
+        if constexpr ((PARTS & PART_Q) != 0)
+            *reinterpret_cast<uint4 *>(&sm.Q[BUF][row][c8 * 8]) = r.q[u];
+        if constexpr ((PARTS & PART_K) != 0)
+            *reinterpret_cast<uint4 *>(&sm.K[BUF][row][(c8 ^ kswz(row)) * 8]) = r.k[u];
     }
+    if constexpr ((PARTS & PART_V) == 0) return;
     const int vrow = p / 4;
 #pragma unroll
     for (int t = 0; t < NJT; ++t) {
@@ -347,70 +389,120 @@ __device__ __forceinline__ void store_block(const Regs<D, NJT> &r, Smem<D, NJT> 
     }
 }
 
-template <int D, int NJT, int BUF>
-__device__ __forceinline__ void produce_store(const Ctx<D> &cx, Smem<D, NJT> &sm, const Regs<D, NJT> &r,
-                                              int p, float wfull)
+// The fused prologue's per-thread state (PRO: QK Norm + RoPE on the Q and K
+// chunks before they go to LDS).
+template <bool PRO>
+struct ProState {
+};
+template <>
+struct ProState<true> {
+    pro::Lane ln;
+    int64_t pos;                     // position of the thread's row in a block at pos 0
+    float eps;
+};
+
+// lambda^(c-1-b) for this thread's token b of a block of c tokens
+template <int D>
+__device__ __forceinline__ float v_weight(const Ctx<D> &cx, int c, int p, float wfull)
 {
     const int b = p / 4;
-    const float wv = r.c == PC ? wfull : (b < r.c ? decay_pow(cx.s, r.c - 1 - b) : 0.0f);
-    store_block<D, NJT, BUF>(r, sm, p, wv);
+    return c == PC ? wfull : (b < c ? decay_pow(cx.s, c - 1 - b) : 0.0f);
+}
+
+template <int D, int NJT, int BUF, bool PRO>
+__device__ __forceinline__ void produce_store(const Ctx<D> &cx, Smem<D, NJT> &sm, Regs<D, NJT> &r,
+                                              int p, float wfull, ProState<PRO> &ps)
+{
+    if constexpr (PRO) {                 // row p/4 of the block, at position ps.pos + r.pos
+        const pro::RowAngles a = pro::row_angles(ps.ln, ps.pos + r.pos);
+        pro::norm_rope(r.q, ps.ln.wq, ps.ln, a, ps.eps);
+        pro::norm_rope(r.k, ps.ln.wk, ps.ln, a, ps.eps);
+    }
+    store_block<D, NJT, BUF, PRO>(r, sm, p, v_weight(cx, r.c, p, wfull));
 }
 
 // One producer step per block blk: after the block's barrier, stage block
 // blk+1 (register set SET) into the other LDS buffer, then reload SET with
-// block blk+1+NSET (at ld, which then moves on).  Loads past the end return
+// block blk+1+NSET (NSET = nset<PRO>(), at ld, which then moves on).  Loads past the end return
 // zeros without touching memory, so nothing here is conditional (exact vmcnt
-// waits).
-template <int D, int NJT, int SET, bool WALK>
+// waits).  With the prologue (PRO) the set is staged and reloaded a part at
+// a time, V, then Q, then K, so that the next loads start while the
+// prologue's arithmetic runs.
+template <int D, int NJT, int SET, bool WALK, bool PRO>
 __device__ __forceinline__ void produce_step(const Ctx<D> &cx, const Walk<WALK> &wk, Smem<D, NJT> &sm,
-                                             Regs<D, NJT> (&rs)[NSET], const Addr<D, NJT> &ad, Pos &ld,
-                                             int p, float wfull)
+                                             Regs<D, NJT> (&rs)[nset<PRO>()], const Addr<D, NJT> &ad, Pos &ld,
+                                             int p, float wfull, ProState<PRO> &ps)
 {
+    constexpr int BUF = SET % 2;
     __syncthreads();                                   // barrier of block blk
-    if (SET % 2 == 1) produce_store<D, NJT, 1>(cx, sm, rs[SET], p, wfull);
-    else              produce_store<D, NJT, 0>(cx, sm, rs[SET], p, wfull);
-    load_block<D, NJT>(rs[SET], cx, ld, ad);
+    Regs<D, NJT> &r = rs[SET];
+    if constexpr (PRO) {
+        store_block<D, NJT, BUF, PRO, PART_V>(r, sm, p, v_weight(cx, r.c, p, wfull));
+        load_block<D, NJT, PRO, PART_V>(r, cx, ld, ad);
+        const pro::RowAngles a = pro::row_angles(ps.ln, ps.pos + r.pos);
+        pro::norm_rope(r.q, ps.ln.wq, ps.ln, a, ps.eps);
+        store_block<D, NJT, BUF, PRO, PART_Q>(r, sm, p, 0.0f);
+        load_block<D, NJT, PRO, PART_Q>(r, cx, ld, ad);
+        pro::norm_rope(r.k, ps.ln.wk, ps.ln, a, ps.eps);
+        store_block<D, NJT, BUF, PRO, PART_K>(r, sm, p, 0.0f);
+        load_block<D, NJT, PRO, PART_K | PART_META>(r, cx, ld, ad);
+    } else {
+        produce_store<D, NJT, BUF>(cx, sm, r, p, wfull, ps);
+        load_block<D, NJT, PRO>(r, cx, ld, ad);
+    }
     wk.next(ld);
 }
 
 // the NSET producer steps of one round, sets 1 .. NSET-1, then 0
-template <int D, int NJT, bool WALK, int I>
+template <int D, int NJT, bool WALK, bool PRO, int I>
 struct ProduceRound {
     __device__ static __forceinline__ void run(const Ctx<D> &cx, const Walk<WALK> &wk, Smem<D, NJT> &sm,
-                                               Regs<D, NJT> (&rs)[NSET], const Addr<D, NJT> &ad, Pos &ld,
-                                               int p, float wfull) {
-        produce_step<D, NJT, I % NSET>(cx, wk, sm, rs, ad, ld, p, wfull);
-        if constexpr (I < NSET) ProduceRound<D, NJT, WALK, I + 1>::run(cx, wk, sm, rs, ad, ld, p, wfull);
+                                               Regs<D, NJT> (&rs)[nset<PRO>()], const Addr<D, NJT> &ad, Pos &ld,
+                                               int p, float wfull, ProState<PRO> &ps) {
+        constexpr int NSET = nset<PRO>();
+        produce_step<D, NJT, I % NSET>(cx, wk, sm, rs, ad, ld, p, wfull, ps);
+        if constexpr (I < NSET)
+            ProduceRound<D, NJT, WALK, PRO, I + 1>::run(cx, wk, sm, rs, ad, ld, p, wfull, ps);
     }
 };
 
-template <int D, int NJT, bool WALK>
-__device__ void producer(const Ctx<D> &cx, const Walk<WALK> &wk, Pos ld, Smem<D, NJT> &sm, int p)
+template <int D, int NJT, bool WALK, bool PRO>
+__device__ void producer(const Ctx<D> &cx, const Walk<WALK> &wk, Pos ld, Smem<D, NJT> &sm, int p,
+                         const QkPrologue &pr)
 {
+    ProState<PRO> ps;
+    if constexpr (PRO) {
+        static_assert(D == pro::PD && Regs<D, NJT>::NQ == pro::NC, "the prologue's row layout");
+        ps.ln.init(pr, p % pro::LPR);
+        ps.pos = pr.pos0 + p / pro::LPR;
+        ps.eps = pr.eps;
+    }
     Addr<D, NJT> ad;
 #pragma unroll
     for (int u = 0; u < Regs<D, NJT>::NQ; ++u) {
-        const int ch = p + PT * u;
-        ad.qk[u] = (uint32_t)(((ch / (D / 8)) * cx.ts + (ch % (D / 8)) * 8) * 2);
+        int row, c8;
+        qk_slot<D, PRO>(p, u, row, c8);
+        ad.qk[u] = (uint32_t)((row * cx.ts + c8 * 8) * 2);
     }
 #pragma unroll
     for (int t = 0; t < NJT; ++t)
         ad.v[t] = (uint32_t)(((p / 4) * cx.ts + cx.j0 + PJ * t + (p % 4) * 8) * 2);
     const float wfull = decay_pow(cx.s, PC - 1 - p / 4);       // lambda^(C-1-b)
 
+    constexpr int NSET = nset<PRO>();
     Regs<D, NJT> rs[NSET];                                      // set i holds block i (mod NSET)
 #pragma unroll
     for (int i = 0; i < NSET; ++i) {
-        load_block<D, NJT>(rs[i], cx, ld, ad);
+        load_block<D, NJT, PRO>(rs[i], cx, ld, ad);
         wk.next(ld);
     }
-    produce_store<D, NJT, 0>(cx, sm, rs[0], p, wfull);
-    load_block<D, NJT>(rs[0], cx, ld, ad);
+    produce_store<D, NJT, 0>(cx, sm, rs[0], p, wfull, ps);
+    load_block<D, NJT, PRO>(rs[0], cx, ld, ad);
     wk.next(ld);
 
     // block blk stages block blk+1 from set (blk+1) % NSET into buffer (blk+1) % 2
     for (int64_t blk = 0; blk < cx.nblk; blk += NSET)
-        ProduceRound<D, NJT, WALK, 1>::run(cx, wk, sm, rs, ad, ld, p, wfull);
+        ProduceRound<D, NJT, WALK, PRO, 1>::run(cx, wk, sm, rs, ad, ld, p, wfull, ps);
     __syncthreads();                                   // final barrier (matches the consumers)
 }
 
@@ -959,13 +1051,15 @@ __device__ void out1x_wave(const Ctx<D> &cx, const Walk<WALK> &wk, Pos pos, Smem
 // NJT: 32-column tiles per workgroup (2 halves how often each head's Q and K
 // are read through L2 and writes whole 128-byte output lines, for half as
 // many workgroups per head; the walk takes 1).
-template <int D, bool STRIDED, bool WALK, int NJT>
+template <int D, bool STRIDED, bool WALK, int NJT, bool PRO = false>
 __global__ __launch_bounds__(NTHREADS) void prefill_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const float *__restrict__ slopes,
-    uint16_t *__restrict__ out, float *__restrict__ state, SeqMap map, int64_t nseq)
+    uint16_t *__restrict__ out, float *__restrict__ state, SeqMap map, int64_t nseq,
+    QkPrologue pr)
 {
     static_assert(!WALK || NJT == 1, "the walk runs one column tile per workgroup");
+    static_assert(!WALK || !PRO, "the fused prologue runs on dense and split launches");
     constexpr int NJ = D / (PJ * NJT);    // workgroups per head
     __shared__ Smem<D, NJT> sm;
 
@@ -1016,8 +1110,9 @@ __global__ __launch_bounds__(NTHREADS) void prefill_bf16_kernel(
     cx.h = wk.h;
     cx.j0 = (int)slice * PJ * NJT;
     cx.s = slopes[wk.h];
-    // blocks processed: a multiple of NSET (trailing empty blocks are no-ops;
+    // blocks processed: a multiple of the producer's sets (trailing empty blocks are no-ops;
     // an empty sequence leaves its state unchanged)
+    constexpr int NSET = nset<PRO>();
     cx.nblk = (wk.blocks(p0) + NSET - 1) / NSET * NSET;
     cx.ts = STRIDED ? (int)map.in.st : D;
     cx.ots = STRIDED ? (int)map.out.st : D;
@@ -1027,7 +1122,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_bf16_kernel(
         case 1: out0_wave<D, NJT>(cx, wk, p0, sm, lane); break;
         case 2: out1_wave<D, NJT>(cx, wk, p0, sm, lane); break;
         case 3: out1x_wave<D, NJT>(cx, wk, p0, sm, lane); break;
-        default: producer<D, NJT>(cx, wk, p0, sm, tid - 64 * NCONS); break;
+        default: producer<D, NJT, WALK, PRO>(cx, wk, p0, sm, tid - 64 * NCONS, pr); break;
     }
 }
 
@@ -1136,21 +1231,30 @@ int prefill_split_plan(int64_t B, int64_t H, int64_t N, int d, int *njt)
 }
 
 // one workgroup per (sequence, head, njt column tiles), never the walk
-// (njt = 2: d = 128 only)
+// (njt = 2: d = 128 only; the fused prologue pro, if given: d = 128 only)
 hipError_t launch_prefill_bf16_nowalk(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                       const float *slopes, uint16_t *out, float *state,
                                       int64_t seqs, const SeqMap &map, int d, hipStream_t stream,
-                                      int njt)
+                                      int njt, const QkPrologue *pro)
 {
     const bool strided = map.in.st != d || map.out.st != d;
     if (njt != 1 && (njt != 2 || d != 128)) return hipErrorInvalidValue;
+    if (pro && d != 128) return hipErrorInvalidValue;
     SeqMap m = map;
     int64_t nseq = seqs;
+    QkPrologue pr = pro ? *pro : QkPrologue{nullptr, nullptr, 0.0, 0, 0.0f, 0};
     void *args[] = {(void *)&q, (void *)&k, (void *)&v, (void *)&slopes,
-                    (void *)&out, (void *)&state, (void *)&m, (void *)&nseq};
-    const void *fn = njt == 1 ? prefill_fn<false>(d, strided)
-                     : strided ? (const void *)prefill_bf16_kernel<128, true, false, 2>
-                               : (const void *)prefill_bf16_kernel<128, false, false, 2>;
+                    (void *)&out, (void *)&state, (void *)&m, (void *)&nseq, (void *)&pr};
+    const void *fn;
+    if (pro)
+        fn = njt == 1 ? (strided ? (const void *)prefill_bf16_kernel<128, true, false, 1, true>
+                                 : (const void *)prefill_bf16_kernel<128, false, false, 1, true>)
+                      : (strided ? (const void *)prefill_bf16_kernel<128, true, false, 2, true>
+                                 : (const void *)prefill_bf16_kernel<128, false, false, 2, true>);
+    else
+        fn = njt == 1 ? prefill_fn<false>(d, strided)
+             : strided ? (const void *)prefill_bf16_kernel<128, true, false, 2>
+                       : (const void *)prefill_bf16_kernel<128, false, false, 2>;
     return hipLaunchKernel(fn, dim3((unsigned)prefill_bf16_grid(seqs, map.H, d, njt)),
                            dim3(NTHREADS), args, 0, stream);
 }
@@ -1162,14 +1266,16 @@ hipError_t launch_prefill_bf16(const uint16_t *q, const uint16_t *k, const uint1
     const bool strided = map.in.st != d || map.out.st != d;
     const dim3 block(NTHREADS);
     if (!prefill_bf16_walks(seqs, map.H, map.T, d, map.cu != nullptr))
-        return launch_prefill_bf16_nowalk(q, k, v, slopes, out, state, seqs, map, d, stream, 1);
+        return launch_prefill_bf16_nowalk(q, k, v, slopes, out, state, seqs, map, d, stream, 1,
+                                          nullptr);
     for (int64_t s0 = 0; s0 < seqs; s0 += WALK_SEQS) {
         SeqMap m = map;
         m.cu = map.cu + s0;
         int64_t nseq = seqs - s0 < WALK_SEQS ? seqs - s0 : WALK_SEQS;
         float *st = state + s0 * map.H * d * d;
+        QkPrologue pr = {nullptr, nullptr, 0.0, 0, 0.0f, 0};
         void *args[] = {(void *)&q, (void *)&k, (void *)&v, (void *)&slopes,
-                        (void *)&out, (void *)&st, (void *)&m, (void *)&nseq};
+                        (void *)&out, (void *)&st, (void *)&m, (void *)&nseq, (void *)&pr};
         const hipError_t e = hipLaunchKernel(prefill_fn<true>(d, strided),
                                              dim3((unsigned)prefill_bf16_grid(1, map.H, d, 1)), block,
                                              args, 0, stream);

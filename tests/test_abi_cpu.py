@@ -559,3 +559,43 @@ def test_prefill_noalloc_rejects_bad_arguments(lib, bad, code):
     # the allocation-free prefill takes la_prefill's checks first (N = 0: no launch)
     assert lib.la_prefill_noalloc(*_prefill_args(**bad)) == code
     assert lib.la_prefill_noalloc(*_prefill_args(N=0)) == LA_OK
+
+
+def _fused_args(**kw):
+    # la_prefill_qk_norm_rope_ws; defaults: B=1, H=2, no tokens, d=128,
+    # token-major [B,N,3*H*d] projection rows, the layer's prologue constants
+    a = dict(q=FAKE, k=FAKE + 0x100000, v=FAKE + 0x200000, slopes=FAKE + 0x300000,
+             qw=FAKE + 0x340000, kw=FAKE + 0x360000, theta=6e6, rot=64, pos0=0, eps=1e-6,
+             out=FAKE + 0x400000, state=FAKE + 0x500000, B=1, H=2, N=0, d=128,
+             ib=0, ih=128, it=768, ob=0, oh=128, ot=256, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return [a[n] for n in ("q", "k", "v", "slopes", "qw", "kw", "theta", "rot", "pos0", "eps",
+                           "out", "state", "B", "H", "N", "d", "ib", "ih", "it", "ob", "oh", "ot",
+                           "ws", "wsb", "stream")]
+
+
+def test_fused_prologue_prefill_empty_is_a_noop(lib):
+    assert lib.la_prefill_qk_norm_rope_ws(*_fused_args()) == LA_OK
+    assert lib.la_prefill_qk_norm_rope_ws(*_fused_args(q=None, k=None, v=None, out=None)) == LA_OK
+    for rot in (0, 16, 32, 128):
+        assert lib.la_prefill_qk_norm_rope_ws(*_fused_args(rot=rot)) == LA_OK
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(d=64), LA_ERR_UNSUPPORTED), (dict(d=96), LA_ERR_UNSUPPORTED),
+    (dict(rot=48), LA_ERR_UNSUPPORTED), (dict(rot=256), LA_ERR_UNSUPPORTED),
+    (dict(rot=8), LA_ERR_UNSUPPORTED),
+    (dict(qw=None), LA_ERR_INVALID_ARG), (dict(kw=None), LA_ERR_INVALID_ARG),
+    (dict(kw=FAKE + 0x360004), LA_ERR_INVALID_ARG),             # weights not 16-byte aligned
+    (dict(theta=1.0), LA_ERR_INVALID_ARG), (dict(theta=float("nan")), LA_ERR_INVALID_ARG),
+    (dict(eps=0.0), LA_ERR_INVALID_ARG), (dict(eps=1e-40), LA_ERR_INVALID_ARG),   # subnormal
+    (dict(eps=float("inf")), LA_ERR_INVALID_ARG), (dict(eps=float("nan")), LA_ERR_INVALID_ARG),
+    (dict(eps=-1e-6), LA_ERR_INVALID_ARG),
+    (dict(pos0=-1), LA_ERR_INVALID_ARG), (dict(pos0=2 ** 63 - 1, N=1), LA_ERR_INVALID_ARG),
+    (dict(slopes=None), LA_ERR_INVALID_ARG), (dict(state=None), LA_ERR_INVALID_ARG),
+    (dict(ih=60), LA_ERR_INVALID_ARG), (dict(it=64), LA_ERR_INVALID_ARG),   # stride rules
+    (dict(B=0), LA_ERR_INVALID_ARG), (dict(N=-1), LA_ERR_INVALID_ARG),
+])
+def test_fused_prologue_prefill_rejects_bad_arguments(lib, bad, code):
+    # no tokens (or a rejected position range): no check can reach a launch
+    assert lib.la_prefill_qk_norm_rope_ws(*_fused_args(**bad)) == code

@@ -98,15 +98,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t *base
 // the row's ntok tokens) and takes the state s_in + (g * BH + bh) * D * D.  A
 // shard correction is one segment at t_off = 0.  q and out rows: (b, h) rows
 // qhs / ohs elements apart, tokens qts / ots apart (>= D), channels contiguous.
-// PRO: q is the projection's raw q, normalised and rotated (QK Norm + RoPE at
-// position pr.pos0 + token) as each tile arrives, as the prefill does.
-template <int D, bool PRO>
+// PROT >= 0: q is the projection's raw q, normalised and rotated (QK Norm +
+// RoPE with PROT rotary dims at position pr.pos0 + token) as each tile
+// arrives, as the prefill does.
+template <int D, int PROT>
 __global__ __launch_bounds__(CT) void cp_correct_kernel(
     const uint16_t *__restrict__ q, const float *__restrict__ slopes,
     const float *__restrict__ s_in, uint16_t *__restrict__ out, int64_t H, int64_t BH,
     int64_t qhs, int64_t qts, int64_t ohs, int64_t ots, int64_t t_off, int64_t seg, int64_t ntok,
     int64_t chunks, QkPrologue pr)
 {
+    constexpr bool PRO = PROT >= 0;
     static_assert(!PRO || D == pro::PD, "the fused prologue handles 128-channel rows");
     constexpr int NCT = D / 32;        // 32-column tiles
     constexpr int KS = D / 16;         // 16-wide k steps
@@ -140,7 +142,7 @@ __global__ __launch_bounds__(CT) void cp_correct_kernel(
     uint16_t *ob = out + bh * ohs + a0 * ots;
     // thread chunk u: row (tid + CT u) / CPR, 16 bytes at column 8 ((tid + CT u) % CPR);
     // with PRO q takes the prologue's layout instead: row tid / 4, chunks tid % 4 + 4u
-    pro::Lane pl;
+    pro::Lane<PRO ? PROT : 0> pl;
     if constexpr (PRO) {
         static_assert(NCH == pro::NC, "the prologue's row layout");
         QkPrologue qonly = pr;
@@ -172,7 +174,7 @@ __global__ __launch_bounds__(CT) void cp_correct_kernel(
         const int64_t t0 = tbeg + (int64_t)it * TT;
         if constexpr (PRO) {                 // row tid/4 at position pos0 + a0 + t0 + tid/4
             const pro::RowAngles a = pro::row_angles(pl, pr.pos0 + a0 + t0 + tid / pro::LPR);
-            pro::norm_rope(rq, pl.wq, pl, a, pr.eps);
+            pro::norm_rope<PROT>(rq, pl.wq, a, pr.eps);
         }
 #pragma unroll
         for (int u = 0; u < NCH; ++u) {
@@ -294,9 +296,18 @@ static hipError_t launch_correct(const uint16_t *q, const float *slopes, const f
     void *args[] = {(void *)&q, (void *)&slopes, (void *)&s_in, (void *)&out, (void *)&H,
                     (void *)&BH, (void *)&qhs, (void *)&qts, (void *)&ohs, (void *)&ots,
                     (void *)&t_off, (void *)&seg, (void *)&ntok, (void *)&chunks, (void *)&pr};
-    const void *fn = pro ? (const void *)cp_correct_kernel<128, true>
-                     : d == 64 ? (const void *)cp_correct_kernel<64, false>
-                               : (const void *)cp_correct_kernel<128, false>;
+    const void *fn = d == 64 ? (const void *)cp_correct_kernel<64, -1>
+                               : (const void *)cp_correct_kernel<128, -1>;
+    if (pro) {
+        switch (pro->rot) {
+            case 0: fn = (const void *)cp_correct_kernel<128, 0>; break;
+            case 16: fn = (const void *)cp_correct_kernel<128, 16>; break;
+            case 32: fn = (const void *)cp_correct_kernel<128, 32>; break;
+            case 64: fn = (const void *)cp_correct_kernel<128, 64>; break;
+            case 128: fn = (const void *)cp_correct_kernel<128, 128>; break;
+            default: return hipErrorInvalidValue;
+        }
+    }
     return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 

@@ -389,16 +389,17 @@ __device__ __forceinline__ void store_block(const Regs<D, NJT> &r, Smem<D, NJT> 
     }
 }
 
-// The fused prologue's per-thread state (PRO: QK Norm + RoPE on the Q and K
-// chunks before they go to LDS).
-template <bool PRO>
+// The fused prologue's per-thread state (PROT >= 0: QK Norm + RoPE with PROT
+// rotary dims on the Q and K chunks before they go to LDS; -1: none).
+template <int PROT>
 struct ProState {
-};
-template <>
-struct ProState<true> {
-    pro::Lane ln;
+    pro::Lane<PROT> ln;
+    pro::BlockAngles<PROT> an;       // the angles of the thread's row, block after block
     int64_t pos;                     // position of the thread's row in a block at pos 0
     float eps;
+};
+template <>
+struct ProState<-1> {
 };
 
 // lambda^(c-1-b) for this thread's token b of a block of c tokens
@@ -409,14 +410,15 @@ __device__ __forceinline__ float v_weight(const Ctx<D> &cx, int c, int p, float 
     return c == PC ? wfull : (b < c ? decay_pow(cx.s, c - 1 - b) : 0.0f);
 }
 
-template <int D, int NJT, int BUF, bool PRO>
+template <int D, int NJT, int BUF, int PROT>
 __device__ __forceinline__ void produce_store(const Ctx<D> &cx, Smem<D, NJT> &sm, Regs<D, NJT> &r,
-                                              int p, float wfull, ProState<PRO> &ps)
+                                              int p, float wfull, ProState<PROT> &ps)
 {
+    constexpr bool PRO = PROT >= 0;
     if constexpr (PRO) {                 // row p/4 of the block, at position ps.pos + r.pos
-        const pro::RowAngles a = pro::row_angles(ps.ln, ps.pos + r.pos);
-        pro::norm_rope(r.q, ps.ln.wq, ps.ln, a, ps.eps);
-        pro::norm_rope(r.k, ps.ln.wk, ps.ln, a, ps.eps);
+        const pro::RowAngles &a = ps.an.next(ps.ln, ps.pos + r.pos);
+        pro::norm_rope<PROT>(r.q, ps.ln.wq, a, ps.eps);
+        pro::norm_rope<PROT>(r.k, ps.ln.wk, a, ps.eps);
     }
     store_block<D, NJT, BUF, PRO>(r, sm, p, v_weight(cx, r.c, p, wfull));
 }
@@ -428,22 +430,23 @@ __device__ __forceinline__ void produce_store(const Ctx<D> &cx, Smem<D, NJT> &sm
 // waits).  With the prologue (PRO) the set is staged and reloaded a part at
 // a time, V, then Q, then K, so that the next loads start while the
 // prologue's arithmetic runs.
-template <int D, int NJT, int SET, bool WALK, bool PRO>
+template <int D, int NJT, int SET, bool WALK, int PROT>
 __device__ __forceinline__ void produce_step(const Ctx<D> &cx, const Walk<WALK> &wk, Smem<D, NJT> &sm,
-                                             Regs<D, NJT> (&rs)[nset<PRO>()], const Addr<D, NJT> &ad, Pos &ld,
-                                             int p, float wfull, ProState<PRO> &ps)
+                                             Regs<D, NJT> (&rs)[nset<(PROT >= 0)>()], const Addr<D, NJT> &ad,
+                                             Pos &ld, int p, float wfull, ProState<PROT> &ps)
 {
+    constexpr bool PRO = PROT >= 0;
     constexpr int BUF = SET % 2;
     __syncthreads();                                   // barrier of block blk
     Regs<D, NJT> &r = rs[SET];
     if constexpr (PRO) {
         store_block<D, NJT, BUF, PRO, PART_V>(r, sm, p, v_weight(cx, r.c, p, wfull));
         load_block<D, NJT, PRO, PART_V>(r, cx, ld, ad);
-        const pro::RowAngles a = pro::row_angles(ps.ln, ps.pos + r.pos);
-        pro::norm_rope(r.q, ps.ln.wq, ps.ln, a, ps.eps);
+        const pro::RowAngles &a = ps.an.next(ps.ln, ps.pos + r.pos);
+        pro::norm_rope<PROT>(r.q, ps.ln.wq, a, ps.eps);
         store_block<D, NJT, BUF, PRO, PART_Q>(r, sm, p, 0.0f);
         load_block<D, NJT, PRO, PART_Q>(r, cx, ld, ad);
-        pro::norm_rope(r.k, ps.ln.wk, ps.ln, a, ps.eps);
+        pro::norm_rope<PROT>(r.k, ps.ln.wk, a, ps.eps);
         store_block<D, NJT, BUF, PRO, PART_K>(r, sm, p, 0.0f);
         load_block<D, NJT, PRO, PART_K | PART_META>(r, cx, ld, ad);
     } else {
@@ -454,26 +457,29 @@ __device__ __forceinline__ void produce_step(const Ctx<D> &cx, const Walk<WALK> 
 }
 
 // the NSET producer steps of one round, sets 1 .. NSET-1, then 0
-template <int D, int NJT, bool WALK, bool PRO, int I>
+template <int D, int NJT, bool WALK, int PROT, int I>
 struct ProduceRound {
     __device__ static __forceinline__ void run(const Ctx<D> &cx, const Walk<WALK> &wk, Smem<D, NJT> &sm,
-                                               Regs<D, NJT> (&rs)[nset<PRO>()], const Addr<D, NJT> &ad, Pos &ld,
-                                               int p, float wfull, ProState<PRO> &ps) {
-        constexpr int NSET = nset<PRO>();
+                                               Regs<D, NJT> (&rs)[nset<(PROT >= 0)>()],
+                                               const Addr<D, NJT> &ad, Pos &ld, int p, float wfull,
+                                               ProState<PROT> &ps) {
+        constexpr int NSET = nset<(PROT >= 0)>();
         produce_step<D, NJT, I % NSET>(cx, wk, sm, rs, ad, ld, p, wfull, ps);
         if constexpr (I < NSET)
-            ProduceRound<D, NJT, WALK, PRO, I + 1>::run(cx, wk, sm, rs, ad, ld, p, wfull, ps);
+            ProduceRound<D, NJT, WALK, PROT, I + 1>::run(cx, wk, sm, rs, ad, ld, p, wfull, ps);
     }
 };
 
-template <int D, int NJT, bool WALK, bool PRO>
+template <int D, int NJT, bool WALK, int PROT>
 __device__ void producer(const Ctx<D> &cx, const Walk<WALK> &wk, Pos ld, Smem<D, NJT> &sm, int p,
                          const QkPrologue &pr)
 {
-    ProState<PRO> ps;
+    constexpr bool PRO = PROT >= 0;
+    ProState<PROT> ps;
     if constexpr (PRO) {
         static_assert(D == pro::PD && Regs<D, NJT>::NQ == pro::NC, "the prologue's row layout");
         ps.ln.init(pr, p % pro::LPR);
+        ps.an.init(ps.ln);
         ps.pos = pr.pos0 + p / pro::LPR;
         ps.eps = pr.eps;
     }
@@ -502,7 +508,7 @@ __device__ void producer(const Ctx<D> &cx, const Walk<WALK> &wk, Pos ld, Smem<D,
 
     // block blk stages block blk+1 from set (blk+1) % NSET into buffer (blk+1) % 2
     for (int64_t blk = 0; blk < cx.nblk; blk += NSET)
-        ProduceRound<D, NJT, WALK, PRO, 1>::run(cx, wk, sm, rs, ad, ld, p, wfull, ps);
+        ProduceRound<D, NJT, WALK, PROT, 1>::run(cx, wk, sm, rs, ad, ld, p, wfull, ps);
     __syncthreads();                                   // final barrier (matches the consumers)
 }
 
@@ -1051,7 +1057,7 @@ __device__ void out1x_wave(const Ctx<D> &cx, const Walk<WALK> &wk, Pos pos, Smem
 // NJT: 32-column tiles per workgroup (2 halves how often each head's Q and K
 // are read through L2 and writes whole 128-byte output lines, for half as
 // many workgroups per head; the walk takes 1).
-template <int D, bool STRIDED, bool WALK, int NJT, bool PRO = false>
+template <int D, bool STRIDED, bool WALK, int NJT, int PROT = -1>
 __global__ __launch_bounds__(NTHREADS) void prefill_bf16_kernel(
     const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
     const uint16_t *__restrict__ v, const float *__restrict__ slopes,
@@ -1059,6 +1065,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_bf16_kernel(
     QkPrologue pr)
 {
     static_assert(!WALK || NJT == 1, "the walk runs one column tile per workgroup");
+    constexpr bool PRO = PROT >= 0;
     static_assert(!WALK || !PRO, "the fused prologue runs on dense and split launches");
     constexpr int NJ = D / (PJ * NJT);    // workgroups per head
     __shared__ Smem<D, NJT> sm;
@@ -1122,7 +1129,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_bf16_kernel(
         case 1: out0_wave<D, NJT>(cx, wk, p0, sm, lane); break;
         case 2: out1_wave<D, NJT>(cx, wk, p0, sm, lane); break;
         case 3: out1x_wave<D, NJT>(cx, wk, p0, sm, lane); break;
-        default: producer<D, NJT, WALK, PRO>(cx, wk, p0, sm, tid - 64 * NCONS, pr); break;
+        default: producer<D, NJT, WALK, PROT>(cx, wk, p0, sm, tid - 64 * NCONS, pr); break;
     }
 }
 
@@ -1230,6 +1237,25 @@ int prefill_split_plan(int64_t B, int64_t H, int64_t N, int d, int *njt)
     return best_s;
 }
 
+// the fused-prologue kernels (d = 128, token strides at run time) by column
+// tiles and rotary dims (null if unsupported)
+template <int NJT>
+const void *prologue_fn_njt(int rot)
+{
+    switch (rot) {
+        case 0: return (const void *)prefill_bf16_kernel<128, true, false, NJT, 0>;
+        case 16: return (const void *)prefill_bf16_kernel<128, true, false, NJT, 16>;
+        case 32: return (const void *)prefill_bf16_kernel<128, true, false, NJT, 32>;
+        case 64: return (const void *)prefill_bf16_kernel<128, true, false, NJT, 64>;
+        case 128: return (const void *)prefill_bf16_kernel<128, true, false, NJT, 128>;
+        default: return nullptr;
+    }
+}
+const void *prologue_fn(int njt, int rot)
+{
+    return njt == 1 ? prologue_fn_njt<1>(rot) : prologue_fn_njt<2>(rot);
+}
+
 // one workgroup per (sequence, head, njt column tiles), never the walk
 // (njt = 2: d = 128 only; the fused prologue pro, if given: d = 128 only)
 hipError_t launch_prefill_bf16_nowalk(const uint16_t *q, const uint16_t *k, const uint16_t *v,
@@ -1245,12 +1271,10 @@ hipError_t launch_prefill_bf16_nowalk(const uint16_t *q, const uint16_t *k, cons
     QkPrologue pr = pro ? *pro : QkPrologue{nullptr, nullptr, 0.0, 0, 0.0f, 0};
     void *args[] = {(void *)&q, (void *)&k, (void *)&v, (void *)&slopes,
                     (void *)&out, (void *)&state, (void *)&m, (void *)&nseq, (void *)&pr};
+    if (pro && !prologue_fn(njt, pro->rot)) return hipErrorInvalidValue;
     const void *fn;
     if (pro)
-        fn = njt == 1 ? (strided ? (const void *)prefill_bf16_kernel<128, true, false, 1, true>
-                                 : (const void *)prefill_bf16_kernel<128, false, false, 1, true>)
-                      : (strided ? (const void *)prefill_bf16_kernel<128, true, false, 2, true>
-                                 : (const void *)prefill_bf16_kernel<128, false, false, 2, true>);
+        fn = prologue_fn(njt, pro->rot);
     else
         fn = njt == 1 ? prefill_fn<false>(d, strided)
              : strided ? (const void *)prefill_bf16_kernel<128, true, false, 2>

@@ -56,10 +56,12 @@ __device__ __forceinline__ double pair_rev(int i, int rot, double log2_theta)
     return exp2(-2.0 * i / rot * log2_theta) * 0.15915494309189535;
 }
 
-// Per-lane constants, computed once per kernel.
+// Per-lane constants, computed once per kernel (ROT: the rotary dims, a
+// compile-time constant of the kernel, equal to QkPrologue::rot).
+template <int ROT>
 struct Lane {
+    static_assert(ROT == 0 || ROT == 16 || ROT == 32 || ROT == 64 || ROT == 128, "rotary dims");
     int j;                    // quad index: chunks j + 4u
-    int rot;
     float wq[NC][8], wk[NC][8];   // norm weights of the lane's channels (wk: 0 if q only)
     double g[8];              // revolutions per position of the lane's pair indices:
                               //   rot 64: chunk j (and its partner j+4);  rot 128: j (with
@@ -69,8 +71,8 @@ struct Lane {
 
     __device__ void init(const QkPrologue &pr, int quad_lane)
     {
+        constexpr int rot = ROT;
         j = quad_lane;
-        rot = pr.rot;
         const double lt = rot > 0 ? log2(pr.theta) : 0.0;
         kb = rot == 128 ? exp2(-0.5 * lt) : 0.0;
 #pragma unroll
@@ -185,55 +187,93 @@ __device__ __forceinline__ void rotate_quad(uint4 &x, const float (&w)[8], const
     x = pack(y, inv);
 }
 
-// One row's chunks (this lane's four) normalised with their weights w and
-// rotated, in place; (ca, sa) are the angles of g, (cb, sb) those of g * kb.
-__device__ __forceinline__ void norm_rope_row(uint4 (&x)[NC], const float (&w)[NC][8], int rot,
-                                              const float (&ca)[8], const float (&sa)[8],
-                                              const float (&cb)[8], const float (&sb)[8], float eps)
-{
-    const float inv = inv_rms(x, eps);
-    if (rot == 64) {
-        rotate_pair(x[0], x[1], w[0], w[1], ca, sa, inv);
-        scale_only(x[2], w[2], inv);
-        scale_only(x[3], w[3], inv);
-    } else if (rot == 128) {
-        rotate_pair(x[0], x[2], w[0], w[2], ca, sa, inv);
-        rotate_pair(x[1], x[3], w[1], w[3], cb, sb, inv);
-    } else {
-        if (rot == 16) rotate_quad<0xB1>(x[0], w[0], ca, sa, inv);         // quad_perm [1,0,3,2]
-        else if (rot == 32) rotate_quad<0x4E>(x[0], w[0], ca, sa, inv);    // quad_perm [2,3,0,1]
-        else scale_only(x[0], w[0], inv);
-        scale_only(x[1], w[1], inv);
-        scale_only(x[2], w[2], inv);
-        scale_only(x[3], w[3], inv);
-    }
-}
-
-// QK Norm + RoPE of the lane's q or k row in place.  All four lanes of the
-// quad take part (DPP).
+// the angles of a lane's row: (ca, sa) of g, and at rot 128 (cb, sb) of g * kb
 struct RowAngles {
     float ca[8], sa[8], cb[8], sb[8];
 };
 
 // the angles of the lane's row at position pos
-__device__ __forceinline__ RowAngles row_angles(const Lane &L, int64_t pos)
+template <int ROT>
+__device__ __forceinline__ RowAngles row_angles(const Lane<ROT> &L, int64_t pos)
 {
     RowAngles a;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        a.ca[e] = a.cb[e] = 1.0f;
-        a.sa[e] = a.sb[e] = 0.0f;
-    }
-    if (L.rot > 0) angles(L.g, 1.0, pos, a.ca, a.sa);
-    if (L.rot == 128) angles(L.g, L.kb, pos, a.cb, a.sb);
+    if constexpr (ROT > 0) angles(L.g, 1.0, pos, a.ca, a.sa);
+    if constexpr (ROT == 128) angles(L.g, L.kb, pos, a.cb, a.sb);
     return a;
 }
 
-// one q or k row of the lane (weights w: L.wq or L.wk) with its angles a
-__device__ __forceinline__ void norm_rope(uint4 (&x)[NC], const float (&w)[NC][8], const Lane &L,
-                                          const RowAngles &a, float eps)
+// The angles of a lane's row block after block, for a kernel that visits
+// one row's blocks in order, 64 positions apart: exact on the first block and
+// on every RESYNC-th, in between the previous block's turned by the exact
+// angle of 64 positions (a complex multiplication: 4 fp32 operations per
+// pair instead of an fp64 reduction, a sine and a cosine), so the rounding
+// of the recurrence never exceeds about RESYNC fp32 roundings.  rot = 128
+// (two sets of pairs) takes exact angles on every block.
+constexpr int RESYNC = 16;
+
+template <int ROT>
+struct BlockAngles {
+    static constexpr bool TURN = ROT > 0 && ROT < 128;
+    RowAngles a;
+    float c64[8], s64[8];     // TURN: cos, sin of each pair's angle over 64 positions
+    int step;                 // blocks since the last exact angles
+
+    __device__ void init(const Lane<ROT> &L)
+    {
+        step = 0;
+        if constexpr (TURN) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                double r = 64.0 * L.g[e];
+                r -= rint(r);
+                sincospif(2.0f * (float)r, &s64[e], &c64[e]);
+            }
+        }
+    }
+    // the angles of the next block's row, at position pos
+    __device__ __forceinline__ const RowAngles &next(const Lane<ROT> &L, int64_t pos)
+    {
+        if constexpr (TURN) {
+            if (step == 0) {
+                a = row_angles(L, pos);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float c = a.ca[e], s = a.sa[e];
+                    a.ca[e] = fmaf(c, c64[e], -s * s64[e]);
+                    a.sa[e] = fmaf(s, c64[e], c * s64[e]);
+                }
+            }
+            step = step + 1 == RESYNC ? 0 : step + 1;
+        } else {
+            a = row_angles(L, pos);
+        }
+        return a;
+    }
+};
+
+// QK Norm + RoPE of one q or k row of the lane (weights w: L.wq or L.wk) in
+// place, with the row's angles a.  All four lanes of the quad take part (DPP).
+template <int ROT>
+__device__ __forceinline__ void norm_rope(uint4 (&x)[NC], const float (&w)[NC][8], const RowAngles &a,
+                                          float eps)
 {
-    norm_rope_row(x, w, L.rot, a.ca, a.sa, a.cb, a.sb, eps);
+    const float inv = inv_rms(x, eps);
+    if constexpr (ROT == 64) {
+        rotate_pair(x[0], x[1], w[0], w[1], a.ca, a.sa, inv);
+        scale_only(x[2], w[2], inv);
+        scale_only(x[3], w[3], inv);
+    } else if constexpr (ROT == 128) {
+        rotate_pair(x[0], x[2], w[0], w[2], a.ca, a.sa, inv);
+        rotate_pair(x[1], x[3], w[1], w[3], a.cb, a.sb, inv);
+    } else {
+        if constexpr (ROT == 16) rotate_quad<0xB1>(x[0], w[0], a.ca, a.sa, inv);      // quad_perm [1,0,3,2]
+        else if constexpr (ROT == 32) rotate_quad<0x4E>(x[0], w[0], a.ca, a.sa, inv); // quad_perm [2,3,0,1]
+        else scale_only(x[0], w[0], inv);
+        scale_only(x[1], w[1], inv);
+        scale_only(x[2], w[2], inv);
+        scale_only(x[3], w[3], inv);
+    }
 }
 
 }  // namespace pro

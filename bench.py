@@ -416,8 +416,8 @@ def measure_layer_ops(dev, stream, reps, pre_ms):
                 "prefill_qk_norm_rope_ms": round(ms_fused, 4),
                 "tflops": round(fl / (ms_fused * 1e-3) / 1e12, 3),
                 "vs_prefill_alone": round(ms_attn / ms_fused, 4),
-                "kernel": "prefill_bf16_kernel<128, true, false, 2, true> (QK Norm + RoPE in the "
-                          "producers' loads) and cp_correct_kernel<128, true>",
+                "kernel": "prefill_bf16_kernel<128, true, false, 2, 64> (QK Norm + RoPE with 64 rotary "
+                          "dims in the producers' loads) and cp_correct_kernel<128, 64>",
                 "layer_ms": round(ms_fused + ms_epi, 4)}}
 
 

@@ -82,6 +82,28 @@ DECODE = dict(B=256, H=64, d=128, steps=64, seed=1004)
 MTP = dict(B=256, H=64, T=4, d=128, seed=1006)
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_bf16_256k_traffic.txt")
+FUSED_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_qk_norm_rope_256k_traffic.txt")
+
+# the kernels of one timed call, in launch order: the headline la_prefill_ws
+# call, and the layer's la_prefill_qk_norm_rope_ws (64 rotary dims)
+TRAFFIC_CALLS = {
+    "split": dict(
+        kernels=["split_prep_kernel", "prefill_bf16_kernel<128, false, false, 2, -1>",
+                 "split_fold_kernel", "cp_correct_kernel<128, -1>"],
+        what=["HBM traffic of the prefill call bench.py times (la_prefill_ws: split_prep_kernel,",
+              "prefill_bf16_kernel<128, false, false, 2, -1> over two segments per head,",
+              "split_fold_kernel, cp_correct_kernel<128, -1>) on the 256K prefill workload",
+              "(B={B}, H={H}, N={N}, d={d}, bf16, zero initial state)"],
+        out=TRAFFIC_FILE),
+    "fused": dict(
+        kernels=["split_prep_kernel", "prefill_bf16_kernel<128, true, false, 2, 64>",
+                 "split_fold_kernel", "cp_correct_kernel<128, 64>"],
+        what=["HBM traffic of the layer's fused call bench.py times (la_prefill_qk_norm_rope_ws:",
+              "split_prep_kernel, prefill_bf16_kernel<128, true, false, 2, 64> over two segments",
+              "per head with QK Norm + RoPE in its loads, split_fold_kernel, cp_correct_kernel<128, 64>)",
+              "on the 256K layer workload (B={B}, H={H}, N={N}, d={d}, bf16; raw q, k, v in one",
+              "[B, N, 4*H*d] projection buffer, [B,H,N,d] output, zero initial state)"],
+        out=FUSED_TRAFFIC_FILE)}
 # the sources of the timed prefill call's kernels (the traffic profile is keyed by their hash)
 KERNEL_SRCS = [os.path.join(ROOT, "long_context_layers_amd", "csrc", f)
                for f in ("prefill_bf16.hip", "cp.hip")]
@@ -304,9 +326,9 @@ def measure_varlen(dev, stream, reps, dense_tflops):
                 "gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                 "algorithmic_bytes_per_launch": by,
                 "vs_dense_256k_tflops": round(tflops / dense_tflops, 4),
-                "kernel": ("prefill_bf16_kernel<128, false, true>: one workgroup per head and "
+                "kernel": ("prefill_bf16_kernel<128, false, true, 1, -1>: one workgroup per head and "
                            "32 columns walks every sequence" if walks else
-                           "prefill_bf16_kernel<128, false, false>: one workgroup per sequence, "
+                           "prefill_bf16_kernel<128, false, false, 1, -1>: one workgroup per sequence, "
                            "head and 32 columns")}
 
     res = one(lambda: inputs.make_workload("varlen_256k", device=dev), "seeded log-uniform")
@@ -405,7 +427,7 @@ def measure_layer_ops(dev, stream, reps, pre_ms):
                 "prefill_strided": {"ms": round(ms_attn, 4),
                                     "tflops": round(fl / (ms_attn * 1e-3) / 1e12, 3),
                                     "vs_contiguous": round(pre_ms / ms_attn, 4),
-                                    "kernel": "prefill_bf16_kernel<128, true, false> (token stride "
+                                    "kernel": "prefill_bf16_kernel<128, true, false, 2, -1> (token stride "
                                               "4*H*d in, [B,H,N,d] out)"},
                 "layer_ms": round(ms_pro_ip + ms_attn + ms_epi, 4),
                 "token_major_out": {
@@ -653,7 +675,7 @@ def measure_cp(dev, stream, reps):
                         "algorithmic_bytes": by_fold, "kernel": "cp_fold_kernel"},
             "cp_correct": {"ms": round(ms_corr, 4), "gbs": round(gc, 1),
                            "frac_of_hbm_peak": round(gc / HBM_PEAK_GBS, 4),
-                           "algorithmic_bytes": by_corr, "kernel": "cp_correct_kernel<128>"},
+                           "algorithmic_bytes": by_corr, "kernel": "cp_correct_kernel<128, -1>"},
             "overhead_vs_local_prefill": round((ms_fold + ms_corr) / ms_loc, 4)}
 
 
@@ -699,18 +721,16 @@ def _counter_rows(path):
     return [(k, g, v) for _, k, g, v in rows]
 
 
-def write_traffic_summary(fetch, write, copy_fetch, copy_write, commands, out=TRAFFIC_FILE):
-    """The HBM bytes per launch of the headline prefill kernel from FETCH_SIZE
+def write_traffic_summary(fetch, write, copy_fetch, copy_write, commands, out=None, call="split"):
+    """The HBM bytes per launch of a timed call (TRAFFIC_CALLS) from FETCH_SIZE
     and WRITE_SIZE (KiB per dispatch) of a restricted bench run, each scaled by
     what the same counter reads for a plain device copy of known size; written
     with the hash of the kernel source the counters belong to."""
     B, H, N, d = PREFILL["B"], PREFILL["H"], PREFILL["N"], PREFILL["d"]
+    spec = TRAFFIC_CALLS[call]
+    out = out or spec["out"]
     copy_kib = (1 << 30) / 1024.0
-    # the kernels of one la_prefill_ws call on this workload, in launch order
-    parts = [("split_prep_kernel", "split_prep_kernel"),
-             ("prefill_bf16_kernel<128, false, false, 2>", "prefill_bf16_kernel<128, false, false, 2>"),
-             ("split_fold_kernel", "split_fold_kernel"),
-             ("cp_correct_kernel<128>", "cp_correct_kernel<128>")]
+    parts = [(k, k) for k in spec["kernels"]]
 
     def per(rows, pick):
         return [v for k, g, v in rows if pick(k)]
@@ -732,10 +752,8 @@ def write_traffic_summary(fetch, write, copy_fetch, copy_write, commands, out=TR
                 f"  {label}  WRITE_SIZE {', '.join('%.0f' % x for x in wv)}"]
     algo = prefill_bytes(B, H, N, d)
     lines = [
-        "HBM traffic of the prefill call bench.py times (la_prefill_ws: split_prep_kernel,",
-        "prefill_bf16_kernel<128, false, false, 2> over two segments per head, split_fold_kernel,",
-        f"cp_correct_kernel<128>) on the 256K prefill workload (B={B}, H={H}, N={N}, d={d}, bf16,",
-        "zero initial state), MI355X, rocprofv3 PMC, written by `python bench.py --traffic-summary`",
+        *[w.format(B=B, H=H, N=N, d=d) for w in spec["what"]],
+        f"MI355X, rocprofv3 PMC, written by `python bench.py --traffic-summary --traffic-call {call}`",
         "from the counter files (no value typed by hand).",
         "",
         f"kernel_source_sha256_16: {kernel_hash()}   (code with comments and blank space removed)",
@@ -833,14 +851,21 @@ def main():
                     help="write the prefill's HBM-traffic profile from four rocprofv3 --pmc "
                          "outputs (files or directories: FETCH_SIZE and WRITE_SIZE of a "
                          "--no-ceilings --extra-reps 0 run, then of a --copy-only run); no GPU")
+    ap.add_argument("--traffic-call", choices=sorted(TRAFFIC_CALLS), default="split",
+                    help="which timed call the --traffic-summary counters cover: the headline "
+                         "la_prefill_ws (split) or the layer's la_prefill_qk_norm_rope_ws (fused)")
     ap.add_argument("--traffic-commands", nargs="*", default=[],
                     help="the commands that made those outputs, recorded in the profile")
+    ap.add_argument("--extras", default="",
+                    help="comma-separated subset of the extra measurements to run (varlen, "
+                         "decode_multi, layer_ops, sizes, decode_latency, cp; default all)")
     ap.add_argument("--extra-reps", type=int, default=5,
                     help="launches timed for the packed-prefill and draft-verification lines "
                          "(0 skips them)")
     args = ap.parse_args()
     if args.traffic_summary:
-        write_traffic_summary(*args.traffic_summary, commands=args.traffic_commands)
+        write_traffic_summary(*args.traffic_summary, commands=args.traffic_commands,
+                              call=args.traffic_call)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -965,9 +990,9 @@ def main():
             "frac": round(gbs / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(),
             "algorithmic_bytes_per_launch": by,
-            "kernel": "prefill_bf16_kernel<128, false, false, 2> (64-column workgroups, the "
+            "kernel": "prefill_bf16_kernel<128, false, false, 2, -1> (64-column workgroups, the "
                       "sequence in two segments per head), timed with the rest of its la_prefill_ws "
-                      "call: split_prep_kernel, split_fold_kernel, cp_correct_kernel<128>",
+                      "call: split_prep_kernel, split_fold_kernel, cp_correct_kernel<128, -1>",
             "binding_limit": "memory traffic: a copy of the kernel with its compute removed "
                              "(same loads and stores) takes as long; per compute unit, the full "
                              "Q and K blocks every column slice reads through L2 and the output "
@@ -1006,25 +1031,27 @@ def main():
         print("[bench] ceilings (MFMA loop, HBM streams)", file=sys.stderr, flush=True)
         res["ceilings"] = measure_ceilings(dev, stream, pre_ms, tflops, dgbs)
         torch.cuda.empty_cache()
+    extras = [
+        ("varlen", "packed variable-length prefill",
+         lambda: measure_varlen(dev, stream, args.extra_reps, tflops)),
+        ("decode_multi", "multi-token decode", lambda: measure_decode_multi(dev, stream, args.extra_reps)),
+        ("layer_ops", "layer ops (QK norm + RoPE, grouped norm x gate, the fused prologue)",
+         lambda: measure_layer_ops(dev, stream, args.extra_reps, pre_ms)),
+        ("sizes", "prefill at 4K and 32K", lambda: measure_sizes(dev, stream, args.extra_reps)),
+        ("decode_latency", "single-sequence decode latency (eager, HIP graph)",
+         lambda: measure_decode_latency(dev, stream, args.extra_reps)),
+        ("cp", "sequence-sharded prefill steps", lambda: measure_cp(dev, stream, args.extra_reps))]
+    wanted = set(args.extras.split(",")) if args.extras else {k for k, _, _ in extras}
+    unknown = wanted - {k for k, _, _ in extras}
+    if unknown:
+        raise SystemExit(f"unknown --extras {sorted(unknown)}")
     if args.extra_reps > 0:
-        print("[bench] packed variable-length prefill", file=sys.stderr, flush=True)
-        res["varlen"] = measure_varlen(dev, stream, args.extra_reps, tflops)
-        torch.cuda.empty_cache()
-        print("[bench] multi-token decode", file=sys.stderr, flush=True)
-        res["decode_multi"] = measure_decode_multi(dev, stream, args.extra_reps)
-        torch.cuda.empty_cache()
-        print("[bench] layer ops (QK norm + RoPE, grouped norm x gate)", file=sys.stderr, flush=True)
-        res["layer_ops"] = measure_layer_ops(dev, stream, args.extra_reps, pre_ms)
-        torch.cuda.empty_cache()
-        print("[bench] prefill at 4K and 32K", file=sys.stderr, flush=True)
-        res["sizes"] = measure_sizes(dev, stream, args.extra_reps)
-        torch.cuda.empty_cache()
-        print("[bench] single-sequence decode latency (eager, HIP graph)", file=sys.stderr,
-              flush=True)
-        res["decode_latency"] = measure_decode_latency(dev, stream, args.extra_reps)
-        torch.cuda.empty_cache()
-        print("[bench] sequence-sharded prefill steps", file=sys.stderr, flush=True)
-        res["cp"] = measure_cp(dev, stream, args.extra_reps)
+        for key, what, fn in extras:
+            if key not in wanted:
+                continue
+            print(f"[bench] {what}", file=sys.stderr, flush=True)
+            res[key] = fn()
+            torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(dict(q=p.q, k=p.k, v=p.v, slopes=p.slopes, N=N, d=d, H=H))

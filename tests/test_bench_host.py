@@ -72,9 +72,9 @@ def _pmc_csv(path, rows):
 def test_traffic_summary_is_calibrated_and_keyed_by_the_source(tmp_path, monkeypatch):
     # made-up counters: the copy reads count twice (factor 1/2), writes once;
     # the prefill's steady dispatches (3..) read 6,000,000 KiB and write 4,000,000
-    pre = "void la::(anonymous namespace)::prefill_bf16_kernel<128, false, false, 2>(...)"
+    pre = "void la::(anonymous namespace)::prefill_bf16_kernel<128, false, false, 2, -1>(...)"
     prep, fold = "la::split_prep_kernel(...)", "la::split_fold_kernel(...)"
-    corr = "void la::(anonymous namespace)::cp_correct_kernel<128>(...)"
+    corr = "void la::(anonymous namespace)::cp_correct_kernel<128, -1>(...)"
     cp = "__amd_rocclr_copyBuffer"
     gib = 1 << 20
     call = lambda a, b, c, e: [(prep, a), (pre, b), (fold, c), (corr, e)]
@@ -97,3 +97,30 @@ def test_traffic_summary_is_calibrated_and_keyed_by_the_source(tmp_path, monkeyp
     # a profile keyed by another source is not used
     out.write_text(text.replace(bench.kernel_hash(), "0" * 16))
     assert bench.measured_traffic() is None
+
+
+def test_traffic_summary_of_the_fused_call(tmp_path):
+    # the layer's fused call has its own kernels and its own profile file; the
+    # headline's counters do not satisfy it
+    pre = "void la::(anonymous namespace)::prefill_bf16_kernel<128, true, false, 2, 64>(...)"
+    corr = "void la::(anonymous namespace)::cp_correct_kernel<128, 64>(...)"
+    prep, fold = "la::split_prep_kernel(...)", "la::split_fold_kernel(...)"
+    cp = "__amd_rocclr_copyBuffer"
+    gib = 1 << 20
+    call = lambda b: [(prep, 2), (pre, b), (fold, 4), (corr, 8)]
+    _pmc_csv(tmp_path / "f.csv", call(7e6) + call(6e6) + call(6e6))
+    _pmc_csv(tmp_path / "w.csv", call(4e6) + call(4e6) + call(4e6))
+    _pmc_csv(tmp_path / "cf.csv", [(cp, 2 * gib)])
+    _pmc_csv(tmp_path / "cw.csv", [(cp, gib)])
+    out = tmp_path / "fused.txt"
+    bench.write_traffic_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"),
+                                str(tmp_path / "cf.csv"), str(tmp_path / "cw.csv"),
+                                ["rocprofv3 ..."], out=str(out), call="fused")
+    text = out.read_text()
+    assert "la_prefill_qk_norm_rope_ws" in text and "--traffic-call fused" in text
+    want = ((2 + 6e6 + 4 + 8) / 2 + (2 + 4e6 + 4 + 8)) * 1024
+    assert f"hbm_bytes_per_launch: {want:.0f}" in text
+    with pytest.raises(SystemExit):
+        bench.write_traffic_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"),
+                                    str(tmp_path / "cf.csv"), str(tmp_path / "cw.csv"),
+                                    [], out=str(tmp_path / "x.txt"), call="split")

@@ -18,6 +18,8 @@
 #include "la_internal.h"
 #include "qk_prologue.h"
 
+#include <algorithm>
+
 namespace la {
 namespace {
 
@@ -57,7 +59,8 @@ __global__ __launch_bounds__(FT) void cp_fold_kernel(
 
 constexpr int CT = 256;            // correct: threads per workgroup (4 waves)
 constexpr int TT = 64;             // correct: tokens per tile
-constexpr int CTOK = 512;          // correct: tokens per workgroup (8 tiles)
+constexpr int CTOK = 512;          // correct: tokens per chunk (8 tiles)
+constexpr int CWG = 32;            // correct: workgroups per (segment, b, h) at most
 constexpr int CPAD = 8;            // LDS row padding (bf16 elements)
 constexpr int RSRC_W3 = 0x00020000;   // buffer descriptor word 3 (raw 32-bit access)
 
@@ -79,14 +82,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t *base
                                              c == 0 ? 0 : (int)(((c - 1) * ts + D) * 2), RSRC_W3);
 }
 
-// A workgroup corrects CTOK tokens of one (segment, b, h) in 64-token tiles.
+// A workgroup corrects the CTOK-token chunks c, c + cstride, ... of one
+// (segment, b, h) in 64-token tiles (cstride = min(chunks, CWG) workgroups
+// per row: a launch is a few thousand workgroups, not one per chunk, and each
+// reads its state once).
 // q and out tiles move between HBM and LDS as whole rows (thread i takes
 // 16-byte chunks i, i + 256, ...: every load or store instruction covers 4 KB
 // of consecutive rows), the next tile's loads are issued before the current
 // tile's products, and the read-modify-write of out happens in LDS.  A tile
 // whose first token's factor lambda^(a+1) has underflowed to exactly 0 in
 // fp32 adds nothing, nor does any tile after it (the factor only falls), so
-// the workgroup stops there: with decays below 1 the correction is confined
+// the workgroup stops there (and at its later chunks, all past that point):
+// with decays below 1 the correction is confined
 // to the first tokens of the segment, and nothing about the result changes.
 // Products: O^T = S^T Q^T with v_mfma_f32_32x32x16_bf16; wave w owns output
 // columns 32 (w % NCT) .. +31 for the token halves w / NCT, w / NCT + 4 / NCT,
@@ -106,7 +113,7 @@ __global__ __launch_bounds__(CT) void cp_correct_kernel(
     const uint16_t *__restrict__ q, const float *__restrict__ slopes,
     const float *__restrict__ s_in, uint16_t *__restrict__ out, int64_t H, int64_t BH,
     int64_t qhs, int64_t qts, int64_t ohs, int64_t ots, int64_t t_off, int64_t seg, int64_t ntok,
-    int64_t chunks, QkPrologue pr)
+    int64_t chunks, int64_t cstride, QkPrologue pr)
 {
     constexpr bool PRO = PROT >= 0;
     static_assert(!PRO || D == pro::PD, "the fused prologue handles 128-channel rows");
@@ -118,17 +125,21 @@ __global__ __launch_bounds__(CT) void cp_correct_kernel(
     const int tid = threadIdx.x, wave = tid / 64, lane = tid % 64;
     const int l32 = lane % 32, hf = lane / 32;
     const int ct = wave % NCT;
-    const int64_t chunk = blockIdx.x % chunks, bh = (blockIdx.x / chunks) % BH;
-    const int64_t g = blockIdx.x / chunks / BH;
+    const int64_t c0 = blockIdx.x % cstride, bh = (blockIdx.x / cstride) % BH;
+    const int64_t g = blockIdx.x / cstride / BH;
     const float s = slopes[bh % H];
 
     const int64_t a0 = t_off + g * seg;                       // the segment's first token
     const int64_t L = max((int64_t)0, min(seg, ntok - a0));   // its tokens
-    const int64_t tbeg = chunk * CTOK;
-    int ntile = (int)((min(L, tbeg + CTOK) - tbeg + TT - 1) / TT);
-    for (int it = 0; it < ntile; ++it)                        // tiles before the underflow
-        if (decay_pow(s, (int)(tbeg + (int64_t)it * TT + 1)) == 0.0f) { ntile = it; break; }
-    if (ntile <= 0) return;
+    // tiles of chunk c before the underflow (0: none here or in any later chunk)
+    auto tiles = [&](int64_t c) {
+        const int64_t tbeg = c * CTOK;
+        int n = (int)max((int64_t)0, (min(L, tbeg + CTOK) - tbeg + TT - 1) / TT);
+        for (int it = 0; it < n; ++it)
+            if (decay_pow(s, (int)(tbeg + (int64_t)it * TT + 1)) == 0.0f) return it;
+        return n;
+    };
+    if (c0 >= chunks || tiles(c0) <= 0) return;
 
     const float *S = s_in + (g * BH + bh) * D * D;
     bf16x8 a[KS];
@@ -169,6 +180,10 @@ __global__ __launch_bounds__(CT) void cp_correct_kernel(
             ro[u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rso, ooff[u], 0, 0));
         }
     };
+    for (int64_t chunk = c0; chunk < chunks; chunk += cstride) {
+    const int64_t tbeg = chunk * CTOK;
+    const int ntile = tiles(chunk);
+    if (ntile <= 0) break;
     fetch(tbeg);
     for (int it = 0; it < ntile; ++it) {
         const int64_t t0 = tbeg + (int64_t)it * TT;
@@ -217,6 +232,7 @@ __global__ __launch_bounds__(CT) void cp_correct_kernel(
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, x), rst, ooff[u], 0, 0);
         }
     }
+    }
 }
 
 // ---- the sequence split of a prefill whose grid fills at most half the
@@ -261,7 +277,7 @@ __global__ __launch_bounds__(FT) void split_fold_kernel(
 }  // namespace
 
 int64_t cp_correct_grid(int64_t B, int64_t H, int64_t L) {
-    return B * H * ((L + CTOK - 1) / CTOK);
+    return B * H * std::min<int64_t>((L + CTOK - 1) / CTOK, CWG);
 }
 
 hipError_t launch_cp_fold(const float *loc, const int *lens, int nfold, const float *init,
@@ -291,11 +307,13 @@ static hipError_t launch_correct(const uint16_t *q, const float *slopes, const f
 {
     if (pro && d != 128) return hipErrorInvalidValue;
     int64_t chunks = (seg + CTOK - 1) / CTOK;
-    const dim3 grid((unsigned)(nseg * BH * chunks)), block(CT);
+    int64_t cstride = std::max<int64_t>(1, std::min<int64_t>(chunks, CWG));
+    const dim3 grid((unsigned)(nseg * BH * cstride)), block(CT);
     QkPrologue pr = pro ? *pro : QkPrologue{nullptr, nullptr, 0.0, 0, 0.0f, 0};
     void *args[] = {(void *)&q, (void *)&slopes, (void *)&s_in, (void *)&out, (void *)&H,
                     (void *)&BH, (void *)&qhs, (void *)&qts, (void *)&ohs, (void *)&ots,
-                    (void *)&t_off, (void *)&seg, (void *)&ntok, (void *)&chunks, (void *)&pr};
+                    (void *)&t_off, (void *)&seg, (void *)&ntok, (void *)&chunks, (void *)&cstride,
+                    (void *)&pr};
     const void *fn = d == 64 ? (const void *)cp_correct_kernel<64, -1>
                                : (const void *)cp_correct_kernel<128, -1>;
     if (pro) {

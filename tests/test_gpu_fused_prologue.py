@@ -183,3 +183,88 @@ def test_fused_prologue_deterministic():
         outs.append((binding.prefill_qk_norm_rope(q, k, v, slopes, st, wq, wk), st))
     torch.cuda.synchronize()
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_fused_prologue_batch_without_split_contiguous_inputs():
+    # B > 1 never splits: one workgroup per (b, head, 32 columns) through 129
+    # blocks; q, k, v contiguous [B,H,N,d] (token stride d) rather than views
+    B, H, N, rot, pos0 = 2, 4, 8192 + 33, 64, 17
+    log(f"fused prologue B{B} H{H} N{N} contiguous, no split")
+    _, (q, k, v) = projection(B, N, H, 950)
+    q, k, v = (t.contiguous() for t in (q, k, v))
+    assert binding.prefill_workspace_bytes(B, H, N, D, DEV) == 0
+    wq, wk = weights(951)
+    slopes = inputs.slopes(H, DEV)
+    st0 = inputs.make_prefill(B, H, 1, D, torch.bfloat16, 952, init_state=True, device=DEV).state
+    st = st0.clone()
+    out = binding.prefill_qk_norm_rope(q, k, v, slopes, st, wq, wk, THETA, rot, pos0, EPS)
+    torch.cuda.synchronize()
+    check(out, st, oracle_chain(q, k, v, wq, wk, slopes, st0, rot, pos0), "fused, B2 contiguous")
+
+
+def test_fused_prologue_positions_near_2_40():
+    # the exact fp64 reduction of the angles at positions about 10^12 (the
+    # fastest pair turns by about 10^12 rad) and the block-to-block turns from there
+    B, H, N, rot, pos0 = 1, 2, 2000, 64, (1 << 40) + 12345
+    log(f"fused prologue at positions {pos0}..")
+    _, (q, k, v) = projection(B, N, H, 960)
+    wq, wk = weights(961)
+    slopes = inputs.slopes(H, DEV)
+    st0 = torch.zeros((B, H, D, D), device=DEV)
+    st = st0.clone()
+    out = binding.prefill_qk_norm_rope(q, k, v, slopes, st, wq, wk, THETA, rot, pos0, EPS)
+    torch.cuda.synchronize()
+    check(out, st, oracle_chain(q, k, v, wq, wk, slopes, st0, rot, pos0), "fused, positions ~2^40")
+
+
+def test_fused_prologue_empty_sequence_is_a_noop():
+    B, H = 1, 2
+    _, (q, k, v) = projection(B, 1, H, 970)
+    q, k, v = (t[:, :, :0] for t in (q, k, v))
+    wq, wk = weights(971)
+    st = torch.randn((B, H, D, D), device=DEV)
+    ref = st.clone()
+    out = binding.prefill_qk_norm_rope(q, k, v, inputs.slopes(H, DEV), st, wq, wk)
+    torch.cuda.synchronize()
+    assert out.shape == (B, H, 0, D) and torch.equal(st, ref)
+
+
+def test_fused_prologue_replayed_from_a_graph():
+    # the call with a caller-held workspace captured once and replayed: each
+    # replay bitwise against the eager call on the same inputs
+    B, H, N = 1, 32, 40000
+    ws = binding.prefill_workspace_bytes(B, H, N, D, DEV)
+    log(f"graph: la_prefill_qk_norm_rope_ws B{B} H{H} N{N} (workspace {ws} B), 3 replays")
+    lib = binding.load_library()
+    buf, (q, k, v) = projection(B, N, H, 980)
+    wq, wk = weights(981)
+    slopes = inputs.slopes(H, DEV)
+    st0 = inputs.make_prefill(B, H, 1, D, torch.bfloat16, 982, init_state=True, device=DEV).state
+    work = torch.empty(max(ws, 1), dtype=torch.uint8, device=DEV)
+    out = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=DEV)
+    state = st0.clone()
+    si = q.stride()[:-1]
+
+    def call(o, stt):
+        rc = lib.la_prefill_qk_norm_rope_ws(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), slopes.data_ptr(), wq.data_ptr(), wk.data_ptr(),
+            THETA, 64, 0, EPS, o.data_ptr(), stt.data_ptr(), B, H, N, D, *si, *o.stride()[:-1],
+            work.data_ptr() if ws else None, ws, torch.cuda.current_stream().cuda_stream)
+        assert rc == 0
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call(torch.empty_like(out), st0.clone())
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(out, state)
+    for r in range(3):
+        state.copy_(st0)
+        g.replay()
+        ref_state = st0.clone()
+        ref = torch.empty_like(out)
+        call(ref, ref_state)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), r
+        assert torch.equal(state, ref_state), r

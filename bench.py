@@ -319,6 +319,10 @@ def measure_varlen(dev, stream, reps, dense_tflops):
         gbs = by / (ms * 1e-3) / 1e9
         lo, hi = min(inp.lens), max(inp.lens)
         walks = binding.prefill_varlen_walks(nseq, H, T, d, dev)
+        # the grid's column tiles per workgroup (as the library chooses them:
+        # 64 columns when those workgroups still fill the device)
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        njt = 2 if d == 128 and 2 * H * nseq >= cus else 1
         del inp, st, out
         return {"workload": f"packed prefill H{H} T{T} d{d} bf16: {nseq} sequences of "
                             f"{lo}..{hi} tokens ({what}), per-sequence fp32 states",
@@ -328,8 +332,8 @@ def measure_varlen(dev, stream, reps, dense_tflops):
                 "vs_dense_256k_tflops": round(tflops / dense_tflops, 4),
                 "kernel": ("prefill_bf16_kernel<128, false, true, 1, -1>: one workgroup per head and "
                            "32 columns walks every sequence" if walks else
-                           "prefill_bf16_kernel<128, false, false, 1, -1>: one workgroup per sequence, "
-                           "head and 32 columns")}
+                           f"prefill_bf16_kernel<128, false, false, {njt}, -1>: one workgroup per "
+                           f"sequence, head and {32 * njt} columns")}
 
     res = one(lambda: inputs.make_workload("varlen_256k", device=dev), "seeded log-uniform")
     res["short_sequences"] = one(

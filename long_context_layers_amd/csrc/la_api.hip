@@ -476,7 +476,8 @@ int prefill_strided_ws(const void *q, const void *k, const void *v, const float 
         uint16_t *o16 = static_cast<uint16_t *>(out);
         const hipStream_t st = static_cast<hipStream_t>(stream);
         return hip_status(pro ? la::launch_prefill_bf16_nowalk(q16, k16, v16, slopes, o16, state, B,
-                                                               map, (int)d, st, 1, pro)
+                                                               map, (int)d, st,
+                                                               la::prefill_bf16_grid_njt(B, H, (int)d), pro)
                               : la::launch_prefill_bf16(q16, k16, v16, slopes, o16, state, B, map,
                                                         (int)d, st));
     }

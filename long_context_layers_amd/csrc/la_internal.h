@@ -139,6 +139,9 @@ int64_t prefill_bf16_grid(int64_t seqs, int64_t H, int d, int njt = 1);
 // whether a packed launch over seqs sequences (T tokens) walks them in one
 // workgroup per (head, column slice) on the current device
 bool prefill_bf16_walks(int64_t seqs, int64_t H, int64_t T, int d, bool packed);
+// column tiles per workgroup of a grid launch (one workgroup per sequence,
+// head and slice) over seqs sequences on the current device
+int prefill_bf16_grid_njt(int64_t seqs, int64_t H, int d);
 int64_t prefill_f32_grid(int64_t seqs, int64_t H, int d);
 
 // ---- device helpers ----

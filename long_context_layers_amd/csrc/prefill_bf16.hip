@@ -1158,26 +1158,43 @@ int64_t prefill_bf16_grid(int64_t seqs, int64_t H, int d, int njt) {
     return seqs * H * (d / (PJ * njt));
 }
 
+// Column tiles per workgroup of a grid launch (one workgroup per sequence,
+// head and column slice): 64-column workgroups (two tiles, d = 128) whenever
+// they still fill the device — they read each head's Q and K through L2 half
+// as often and write whole 128-byte output lines, so a block step costs 1.6x
+// a 32-column one for twice the columns (measured: 16 sequences of 16K
+// tokens at 64 heads 4.25 -> 3.39 ms, 74 mixed ones 4.57 -> 3.58 ms).  The
+// dense B = 1 launch, where they would leave half the device idle, runs as
+// segments instead (la_prefill_ws).
+int prefill_bf16_grid_njt(int64_t seqs, int64_t H, int d)
+{
+    if (d != 128) return 1;
+    const int cus = device_cus();
+    return cus > 0 && 2 * H * seqs >= cus ? 2 : 1;
+}
+
 // A packed launch walks its sequences inside one workgroup per (head, column
-// slice) when that is estimated to be faster than a grid of one workgroup per
-// (sequence, head, slice), and the sequences are short on average (below
-// WALK_MEAN_LEN tokens: longer ones gain from the hardware balancing the grid
-// over the compute units as workgroups finish) and the offsets fit the walk's
-// table (fewer than 2^31 tokens; batches of more than WALK_SEQS sequences are
-// walked WALK_SEQS at a time, one launch each).  The estimate, in units of
-// one 64-token block step of a full device, from measured launches (H = 16 ..
-// 64, 64 .. 512 tokens per sequence and mixed lengths at 256K tokens):
-//   walk: rounds * (T/64 + 1.9 nseq) * (0.6 + 0.4 occupancy), where rounds is
-//         the number of device-fills its H * d/32 workgroups take, occupancy
-//         the share of those rounds' compute units they use (a block step
-//         is that much shorter on a partly idle device), and 1.9 blocks per
-//         sequence the hand-over at a boundary plus the partial last block;
-//   grid: (H * d/32 / CUs) * (T/64 + 4.25 nseq), 4.25 blocks per sequence
-//         being each workgroup's pipeline fill and drain plus its block count
-//         rounded up to the producers' four-block unroll.
-// So at 64 heads (one full device) the walk wins for every short mean
-// length, at 32 heads only below about two blocks per sequence (the grid then
-// uses the whole device), and at 16 heads never.
+// slice) when that is estimated to be faster than the grid launch above, and
+// the sequences are short on average (below WALK_MEAN_LEN tokens: longer ones
+// gain from the hardware balancing the grid over the compute units as
+// workgroups finish) and the offsets fit the walk's table (fewer than 2^31
+// tokens; batches of more than WALK_SEQS sequences are walked WALK_SEQS at a
+// time, one launch each).  The estimates, in microseconds, fitted to measured
+// launches (H = 32 and 64, 64 .. 16384 tokens per sequence and mixed lengths
+// at 256K tokens, d = 128):
+//   walk: rounds * (0.98 T/64 + 1.51 nseq) * (0.6 + 0.4 occupancy), where
+//         rounds is the number of device-fills its H * d/32 workgroups take,
+//         occupancy the share of those rounds' compute units they use (a
+//         block step is that much shorter on a partly idle device), and the
+//         per-sequence term the hand-over at a boundary plus the partial
+//         last block;
+//   grid, 64-column workgroups: 1.66 * (T/64 + 4 nseq) * 2H / CUs;
+//   grid, 32-column workgroups: 1.05 * (T/64 + 4.25 nseq) * (H * d/32) / CUs,
+//         the per-sequence terms being each workgroup's pipeline fill and
+//         drain plus its block count rounded up to the producers' four-block
+//         unroll.
+// So the walk wins for sequences of up to about 256 tokens at 64 heads and
+// about 64 at 32 heads; the wide grid for longer ones.
 constexpr int64_t WALK_MEAN_LEN = 8192;
 
 bool prefill_bf16_walks(int64_t seqs, int64_t H, int64_t T, int d, bool packed)
@@ -1189,8 +1206,10 @@ bool prefill_bf16_walks(int64_t seqs, int64_t H, int64_t T, int d, bool packed)
     const double rounds = std::ceil(wg / cus);
     const double occupancy = wg / (rounds * cus);
     const double blocks = (double)T / PC, n = (double)seqs;
-    const double walk = rounds * (blocks + 1.9 * n) * (0.6 + 0.4 * occupancy);
-    const double grid = wg / cus * (blocks + 4.25 * n);
+    const double walk = rounds * (0.98 * blocks + 1.51 * n) * (0.6 + 0.4 * occupancy);
+    const double grid = prefill_bf16_grid_njt(seqs, H, d) == 2
+                            ? 1.66 * (blocks + 4.0 * n) * 2.0 * H / cus
+                            : 1.05 * (blocks + 4.25 * n) * wg / cus;
     return walk < grid;
 }
 
@@ -1290,8 +1309,8 @@ hipError_t launch_prefill_bf16(const uint16_t *q, const uint16_t *k, const uint1
     const bool strided = map.in.st != d || map.out.st != d;
     const dim3 block(NTHREADS);
     if (!prefill_bf16_walks(seqs, map.H, map.T, d, map.cu != nullptr))
-        return launch_prefill_bf16_nowalk(q, k, v, slopes, out, state, seqs, map, d, stream, 1,
-                                          nullptr);
+        return launch_prefill_bf16_nowalk(q, k, v, slopes, out, state, seqs, map, d, stream,
+                                          prefill_bf16_grid_njt(seqs, map.H, d), nullptr);
     for (int64_t s0 = 0; s0 < seqs; s0 += WALK_SEQS) {
         SeqMap m = map;
         m.cu = map.cu + s0;

@@ -85,6 +85,7 @@ def check(out, st, ref, what, heads=None):
     (2, 2, 190, 128, 12345),     # every channel rotates
     (1, 2, 64, 64, 0),           # exactly one block
     (1, 2, 1, 64, 5),            # one token
+    (2, 64, 300, 64, 3),         # a batch at 64 heads: 64-column workgroups without the split
 ])
 def test_fused_prologue_matches_oracle(B, H, N, rot, pos0):
     log(f"fused prologue B{B} H{H} N{N} d{D} rot{rot} pos0 {pos0}")

@@ -145,3 +145,41 @@ def test_varlen_empty_sequences_write_nothing_outside(dtype):
     tol = BF16_TOL if dtype == torch.bfloat16 else F32_TOL
     eo, es = max_err(out, st, o_ref, s_ref, inp.cu_seqlens.cpu().numpy())
     assert eo <= tol and es <= tol
+
+
+def test_varlen_wide_grid_equals_dense_per_sequence_bitwise():
+    # 64 heads and a dozen sequences of a few thousand tokens: the packed launch
+    # takes the grid of 64-column workgroups, which must give exactly the bits
+    # of 32-column launches of each sequence alone (la_prefill, no split)
+    lens = [3000, 700, 2048, 1500, 999, 2500, 64, 1, 1800, 2222, 1234, 2900]
+    H = 64
+    if binding.prefill_varlen_walks(len(lens), H, sum(lens), 128):
+        pytest.skip("this device walks these sequences")
+    log(f"varlen (64-column grid) vs dense launches per sequence, H{H} d128, {len(lens)} sequences")
+    inp = inputs.make_varlen(H, lens, 128, torch.bfloat16, seed=84, init_state=True, device=DEV)
+    out, st = run_varlen(inp)
+    cu = inp.cu_seqlens.cpu().tolist()
+    for i in range(len(lens)):
+        a, b = cu[i], cu[i + 1]
+        q, k, v = (t[:, a:b].unsqueeze(0).contiguous() for t in (inp.q, inp.k, inp.v))
+        s1 = inp.states[i:i + 1].clone()
+        o1 = binding.prefill(q, k, v, inp.slopes, s1, split=False)
+        torch.cuda.synchronize()
+        assert torch.equal(o1[0], out[:, a:b]), f"sequence {i}: outputs differ"
+        assert torch.equal(s1[0], st[i]), f"sequence {i}: states differ"
+
+
+def test_dense_batch_wide_grid_equals_single_rows_bitwise():
+    # B = 4 at 64 heads runs on 64-column workgroups; each batch row alone
+    # (B = 1, no split) runs on 32-column ones: the same bits
+    B, H, N = 4, 64, 1000 + 37
+    log(f"dense B{B} H{H} N{N} (64-column grid) vs B=1 launches")
+    x = inputs.make_prefill(B, H, N, 128, torch.bfloat16, seed=85, init_state=True, device=DEV)
+    st = x.state.clone()
+    out = binding.prefill(x.q, x.k, x.v, x.slopes, st)
+    for b in range(B):
+        s1 = x.state[b:b + 1].clone()
+        o1 = binding.prefill(x.q[b:b + 1], x.k[b:b + 1], x.v[b:b + 1], x.slopes, s1, split=False)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, out[b:b + 1]), f"row {b}: outputs differ"
+        assert torch.equal(s1, st[b:b + 1]), f"row {b}: states differ"

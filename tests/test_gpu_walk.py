@@ -116,14 +116,16 @@ def test_walk_strided_bitwise_equals_contiguous(d, H):
     assert torch.equal(ob.transpose(0, 1), out_ref) and torch.equal(st, st_ref)
 
 
-def test_walk_256k_workload_equals_per_sequence_launches():
-    # the packed 256K workload (74 sequences, 64 heads): every sequence's
-    # output and state bitwise against its own launch
+def test_packed_256k_workload_equals_per_sequence_launches():
+    # the packed 256K workload (74 sequences, 64 heads), whichever work split
+    # the plan takes for it (the grid of 64-column workgroups on a 256-CU
+    # device): every sequence's output and state bitwise against its own launch
     x = inputs.make_workload("varlen_256k", device=DEV)
     lens = x.lens
     H, T, d = x.q.shape
-    need_walk(len(lens), H, sum(lens), d)
-    log(f"walk varlen_256k: H{H} T{T} d{d}, {len(lens)} sequences ({min(lens)}..{max(lens)})")
+    walks = binding.prefill_varlen_walks(len(lens), H, sum(lens), d)
+    log(f"packed varlen_256k: H{H} T{T} d{d}, {len(lens)} sequences ({min(lens)}..{max(lens)}), "
+        f"walk={walks}")
     st = x.states.clone()
     out = binding.prefill_varlen(x.q, x.k, x.v, x.slopes, x.cu_seqlens, st)
     o1, s1 = per_sequence(x, lens)

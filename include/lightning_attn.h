@@ -273,6 +273,26 @@ int la_prefill_varlen_strided(const void *q, const void *k, const void *v, const
                               void *stream);
 
 /*
+ * la_prefill_varlen_from_zero: la_prefill_varlen_strided for sequences that
+ * all start from a zero state (fresh requests), with the states an output
+ * only: states [nseq,H,d,d] fp32 is written (the final state of each
+ * sequence; zeros for an empty one) and never read, which saves a state read
+ * per sequence and head (at 64 tokens per sequence and d = 128 the states are
+ * half of the launch's bytes).  The same results as la_prefill_varlen_strided
+ * on zero-filled states, bitwise; T = 0 writes zero states.  Every other rule
+ * (strides, offsets, sizes, errors): as la_prefill_varlen_strided; the
+ * contiguous layout is the strides (T*d, d, T*d, d).  Source: as
+ * la_prefill_varlen (Ling and Ring 2.6 Technical Report, §4.1.2: packed
+ * variable-length sequences); a zero state is the recurrence's state before
+ * any token.
+ */
+int la_prefill_varlen_from_zero(const void *q, const void *k, const void *v, const float *slopes,
+                                const int64_t *cu_seqlens, int64_t nseq, void *out, float *states,
+                                int64_t H, int64_t T, int64_t d, int64_t in_hstride,
+                                int64_t in_tstride, int64_t out_hstride, int64_t out_tstride,
+                                void *stream);
+
+/*
  * One decode step for B*H sequences (one new token each).
  *   q, k, v     [B,H,d] bf16, read only.
  *   state       [B,H,d,d] fp32, updated in place: S' = lambda S + k^T v.
@@ -452,7 +472,7 @@ const char *la_status_string(int status);
 /* ABI version of this header (incremented on incompatible changes). */
 int la_abi_version(void);
 
-#define LA_ABI_VERSION 6
+#define LA_ABI_VERSION 7
 
 #ifdef __cplusplus
 }

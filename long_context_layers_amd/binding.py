@@ -37,6 +37,8 @@ SIGNATURES = {
     "la_prefill_qk_norm_rope_ws": ([_P, _P, _P, _P, _P, _P, ctypes.c_double, _I64, _I64,
                                     ctypes.c_float, _P, _P, _I64, _I64, _I64, _I64,
                                     _I64, _I64, _I64, _I64, _I64, _I64, _P, _I64, _P], _INT),
+    "la_prefill_varlen_from_zero": ([_P, _P, _P, _P, _P, _I64, _P, _P, _I64, _I64, _I64,
+                                     _I64, _I64, _I64, _I64, _P], _INT),
     "la_prefill_varlen_strided": ([_P, _P, _P, _P, _P, _I64, _P, _P, _I64, _I64, _I64,
                                    _I64, _I64, _I64, _I64, _P], _INT),
     "la_decode_step": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P], _INT),
@@ -56,7 +58,7 @@ SIGNATURES = {
     "la_prefill_varlen_plan": ([_I64, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_int)], _INT),
     "la_abi_version": ([], _INT),
 }
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 _lock = threading.Lock()
 _lib = None
@@ -270,7 +272,7 @@ def prefill_workspace_bytes(B: int, H: int, N: int, d: int, device=None) -> int:
 
 def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: torch.Tensor,
                    cu_seqlens: torch.Tensor, states: torch.Tensor,
-                   out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                   out: Optional[torch.Tensor] = None, from_zero: bool = False) -> torch.Tensor:
     """Packed variable-length prefill: independent sequences in one launch.
 
     q, k, v: [H,T,d] bf16 or fp32 (sequence i is rows cu_seqlens[i]:cu_seqlens[i+1]
@@ -279,7 +281,9 @@ def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: to
     OUT = final states (in place).  Returns out [H,T,d].  Enqueued on the current
     stream; the offsets are not read on the host.  bf16 q, k, v (sharing one
     set of strides) and out may be strided [H,T,d] views with a unit channel
-    stride (``la_prefill_varlen_strided``).
+    stride (``la_prefill_varlen_strided``).  from_zero (bf16): every sequence
+    starts from a zero state and ``states`` is only written, never read
+    (``la_prefill_varlen_from_zero``; empty sequences get zero states).
     """
     if not isinstance(q, torch.Tensor) or q.dim() != 3:
         raise ValueError("q must be a [H,T,d] tensor")
@@ -298,6 +302,20 @@ def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: to
     _need(cu_seqlens, "cu_seqlens", torch.int64, dev, (nseq + 1,))
     _need(slopes, "slopes", torch.float32, dev, (H,))
     _need(states, "states", torch.float32, dev, (nseq, H, d, d))
+    if from_zero:
+        if dt != torch.bfloat16:
+            raise ValueError("from_zero is taken for bfloat16 only")
+        if out is None:
+            out = torch.empty((H, T, d), dtype=dt, device=dev)
+        so = _view(out, "out", dt, dev, (H, T, d))
+        si = q.stride()[:-1]
+        with torch.cuda.device(dev):
+            rc = load_library().la_prefill_varlen_from_zero(
+                q.data_ptr(), k.data_ptr(), v.data_ptr(), slopes.data_ptr(),
+                cu_seqlens.data_ptr(), nseq, out.data_ptr(), states.data_ptr(), H, T, d,
+                *si, *so, _stream(dev))
+        _check(rc, "la_prefill_varlen_from_zero")
+        return out
     if _strided(q, k, v, out, dt, dev, (H, T, d)):
         if out is None:
             out = torch.empty((H, T, d), dtype=dt, device=dev)

@@ -540,11 +540,14 @@ int la_prefill_qk_norm_rope_ws(const void *q, const void *k, const void *v, cons
                               workspace_bytes, stream, &pro);
 }
 
-int la_prefill_varlen_strided(const void *q, const void *k, const void *v, const float *slopes,
-                              const int64_t *cu_seqlens, int64_t nseq, void *out, float *states,
-                              int64_t H, int64_t T, int64_t d, int64_t in_hstride,
-                              int64_t in_tstride, int64_t out_hstride, int64_t out_tstride,
-                              void *stream)
+namespace {
+
+// la_prefill_varlen_strided, and with zero_init the same launches from zero
+// states that are only written
+int prefill_varlen_strided(const void *q, const void *k, const void *v, const float *slopes,
+                           const int64_t *cu_seqlens, int64_t nseq, void *out, float *states,
+                           int64_t H, int64_t T, int64_t d, int64_t in_hstride, int64_t in_tstride,
+                           int64_t out_hstride, int64_t out_tstride, void *stream, int zero_init)
 {
     if (!cu_seqlens || !aligned(cu_seqlens, 8)) return LA_ERR_INVALID_ARG;
     if (nseq < 1 || H < 1 || T < 0) return LA_ERR_INVALID_ARG;
@@ -556,13 +559,35 @@ int la_prefill_varlen_strided(const void *q, const void *k, const void *v, const
     const int rc = check_strided(q, k, v, slopes, out, states, n, si, so, nstate, d);
     if (rc != LA_OK) return rc;
     if (la::prefill_bf16_grid(nseq, H, (int)d) > 0x7fffffff) return LA_ERR_UNSUPPORTED;
-    if (T == 0) return LA_OK;
-    const la::SeqMap map = {cu_seqlens, H, 0, T, {0, in_hstride, in_tstride},
-                            {0, out_hstride, out_tstride}};
+    if (T == 0 && !zero_init) return LA_OK;     // (from zero, the empty sequences' states are written)
+    la::SeqMap map = {cu_seqlens, H, 0, T, {0, in_hstride, in_tstride}, {0, out_hstride, out_tstride}};
+    map.zero_init = zero_init;
     return hip_status(la::launch_prefill_bf16(
         static_cast<const uint16_t *>(q), static_cast<const uint16_t *>(k),
         static_cast<const uint16_t *>(v), slopes, static_cast<uint16_t *>(out), states, nseq,
         map, (int)d, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+int la_prefill_varlen_strided(const void *q, const void *k, const void *v, const float *slopes,
+                              const int64_t *cu_seqlens, int64_t nseq, void *out, float *states,
+                              int64_t H, int64_t T, int64_t d, int64_t in_hstride,
+                              int64_t in_tstride, int64_t out_hstride, int64_t out_tstride,
+                              void *stream)
+{
+    return prefill_varlen_strided(q, k, v, slopes, cu_seqlens, nseq, out, states, H, T, d,
+                                  in_hstride, in_tstride, out_hstride, out_tstride, stream, 0);
+}
+
+int la_prefill_varlen_from_zero(const void *q, const void *k, const void *v, const float *slopes,
+                                const int64_t *cu_seqlens, int64_t nseq, void *out, float *states,
+                                int64_t H, int64_t T, int64_t d, int64_t in_hstride,
+                                int64_t in_tstride, int64_t out_hstride, int64_t out_tstride,
+                                void *stream)
+{
+    return prefill_varlen_strided(q, k, v, slopes, cu_seqlens, nseq, out, states, H, T, d,
+                                  in_hstride, in_tstride, out_hstride, out_tstride, stream, 1);
 }
 
 int la_decode_step(const void *q, const void *k, const void *v, const float *slopes,

@@ -24,6 +24,8 @@ struct SeqMap {
     const int64_t *cu;    // null: dense launch
     int64_t H, N, T;      // heads; dense sequence length; packed total length
     Strides in, out;
+    int zero_init;        // 1: every sequence starts from a zero state and the states
+                          // are only written (empty sequences: zeros), never read
 };
 
 // start offsets (elements) of slice (seq, h) in the inputs and the output, and its length

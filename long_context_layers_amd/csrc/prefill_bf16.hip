@@ -164,12 +164,14 @@ struct WalkTable {
     int seq[WALK_SEQS], start[WALK_SEQS], len[WALK_SEQS];
     int count;                  // entries
     int nblk;                   // blocks with tokens
+    int empty[WALK_SEQS];       // the empty sequences (their states are zeroed from a zero start)
+    int nempty;
 };
 
 // one wave fills the table (a barrier must follow before anyone reads it)
 __device__ void build_table(WalkTable &tb, const SeqMap &m, int64_t nseq, int lane)
 {
-    int count = 0, nblk = 0;
+    int count = 0, nblk = 0, nempty = 0;
     for (int64_t base = 0; base < nseq; base += 64) {
         const int64_t s = base + lane;
         int a = 0, n = 0;
@@ -187,6 +189,11 @@ __device__ void build_table(WalkTable &tb, const SeqMap &m, int64_t nseq, int la
             tb.len[count + before] = n;
         }
         count += __popcll(mask);
+        const uint64_t emask = __ballot(s < nseq && n == 0);
+        const int ebefore = __builtin_amdgcn_mbcnt_hi((uint32_t)(emask >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)emask, 0));
+        if (s < nseq && n == 0) tb.empty[nempty + ebefore] = (int)s;
+        nempty += __popcll(emask);
         int b = (n + PC - 1) / PC;
         for (int off = 32; off > 0; off >>= 1) b += __shfl_xor(b, off);
         nblk += b;
@@ -194,6 +201,7 @@ __device__ void build_table(WalkTable &tb, const SeqMap &m, int64_t nseq, int la
     if (lane == 0) {
         tb.count = count;
         tb.nblk = nblk;
+        tb.nempty = nempty;
     }
 }
 
@@ -259,6 +267,7 @@ struct Ctx {                          // per-thread constants of one workgroup
     int ts, ots;                      // token strides (elements) of q/k/v and of out (<= 2^24)
     float s;
     int j0;
+    bool zero_init;                   // states start at zero and are only written
 
     // this workgroup's columns of the state of sequence seq: element (i, j) at i * D + j
     __device__ float *state_of(int64_t seq) const { return state + (seq * H + h) * D * D + j0; }
@@ -797,7 +806,7 @@ struct Scan {
     __device__ Scan(const Ctx<D> &cx, int lane) : ln(lane), full_decay(decay_pow(cx.s, PC)) {}
 
     __device__ void init(const Ctx<D> &cx, const Walk<WALK> &wk, const Pos &pos, Smem<D, NJT> &sm) {
-        if (pos.n > 0) {
+        if (pos.n > 0 && !cx.zero_init) {
             if constexpr (WALK) load_state<D, T0, NTL>(sacc[0], cx.state_of(pos.seq), ln);
             else {
                 const float *St = cx.state_of(pos.seq);
@@ -818,7 +827,7 @@ struct Scan {
         }
         if constexpr (WALK) {
             const int64_t s1 = wk.seq_at(pos.j + 1);
-            if (s1 >= 0) stage_state<D, T0, NTL>(wk.slot, cx.state_of(s1), ln.l32 + 32 * ln.h, true);
+            if (s1 >= 0 && !cx.zero_init) stage_state<D, T0, NTL>(wk.slot, cx.state_of(s1), ln.l32 + 32 * ln.h, true);
         }
 #pragma unroll
         for (int jt = 0; jt < NJT; ++jt)
@@ -863,11 +872,18 @@ struct Scan {
                 // wait for its staging (issued a sequence ago) then covers no
                 // store of this block
                 const bool more = wk.seq_at(pos.j + 1) >= 0;
-                // the slot's direct loads (a sequence ago) have landed before
-                // it is read or refilled: they count as vector memory
-                asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
                 f32x16 nxt[NTL];
-                if (more) read_staged<D, T0, NTL>(nxt, wk.slot, ln);
+                if (cx.zero_init) {
+                    // from zero nothing is staged: no wait for the slot (which
+                    // would also wait for the previous final state's stores)
+#pragma unroll
+                    for (int t = 0; t < NTL; ++t) nxt[t] = f32x16{};
+                } else {
+                    // the slot's direct loads (a sequence ago) have landed before
+                    // it is read or refilled: they count as vector memory
+                    asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
+                    if (more) read_staged<D, T0, NTL>(nxt, wk.slot, ln);
+                }
                 store_via_slot<D, T0, NTL>(wk.slot, cx.state_of(pos.seq), sacc[0], ln,   // the final state out
                                            ln.l32 + 32 * ln.h);
                 if (more) {
@@ -879,9 +895,12 @@ struct Scan {
                         sacc[0][t] = nxt[t];
                         write_st<D, NJT>(sm, BUF, T0 + t, 0, ln, sacc[0][t]);
                     }
-                    __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0): the slot reads done
-                    const int64_t s2 = wk.seq_at(pos.j + 2);
-                    if (s2 >= 0) stage_state<D, T0, NTL>(wk.slot, cx.state_of(s2), ln.l32 + 32 * ln.h, true);
+                    if (!cx.zero_init) {
+                        __builtin_amdgcn_s_waitcnt(0xc07f);      // lgkmcnt(0): the slot reads done
+                        const int64_t s2 = wk.seq_at(pos.j + 2);
+                        if (s2 >= 0) stage_state<D, T0, NTL>(wk.slot, cx.state_of(s2), ln.l32 + 32 * ln.h,
+                                                             true);
+                    }
                 }
             }
         }
@@ -891,7 +910,7 @@ struct Scan {
     // the step measured slower: it sits on the scan's sequential path)
     __device__ void finish(const Ctx<D> &cx, const Pos &pos) {
         if constexpr (!WALK) {
-            if (cx.nblk > 0) {
+            if (cx.nblk > 0 || cx.zero_init) {      // (an empty sequence from zero: zeros)
                 float *St = cx.state_of(pos.seq);
 #pragma unroll
                 for (int jt = 0; jt < NJT; ++jt)
@@ -1104,6 +1123,16 @@ __global__ __launch_bounds__(NTHREADS) void prefill_bf16_kernel(
         __syncthreads();
         wk.tb = &tb;
         wk.slot = slot;
+        if (map.zero_init) {             // empty sequences from zero: this slice of their states is 0
+            const int64_t j0 = (int64_t)slice * PJ * NJT;
+            for (int e = 0; e < tb.nempty; ++e) {
+                float *st = state + ((int64_t)tb.empty[e] * map.H + wk.h) * D * D + j0;
+                for (int i = tid; i < D * PJ * NJT / 4; i += NTHREADS) {
+                    const int row = i / (PJ * NJT / 4), c4 = i % (PJ * NJT / 4);
+                    *reinterpret_cast<float4 *>(st + row * D + 4 * c4) = make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+            }
+        }
     }
     const Pos p0 = wk.first(WALK ? 0 : bh / map.H);
 
@@ -1117,6 +1146,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_bf16_kernel(
     cx.h = wk.h;
     cx.j0 = (int)slice * PJ * NJT;
     cx.s = slopes[wk.h];
+    cx.zero_init = map.zero_init != 0;
     // blocks processed: a multiple of the producer's sets (trailing empty blocks are no-ops;
     // an empty sequence leaves its state unchanged)
     constexpr int NSET = nset<PRO>();

@@ -315,6 +315,9 @@ def test_group_norm_gate_rejects_overlap_and_nulls(lib, bad):
 
 
 STRIDED = ["la_prefill_strided", "la_prefill_varlen_strided"]
+# the argument checks are shared by the zero-start packed call (which, unlike
+# the others, launches even with no tokens: it writes the empty sequences' states)
+STRIDED_CHECKS = STRIDED + ["la_prefill_varlen_from_zero"]
 
 
 def _strided_args(fn, **kw):
@@ -338,7 +341,7 @@ def test_strided_empty_is_a_noop(lib, fn):
     assert getattr(lib, fn)(*_strided_args(fn, N=0, q=None, k=None, v=None, out=None)) == LA_OK
 
 
-@pytest.mark.parametrize("fn", STRIDED)
+@pytest.mark.parametrize("fn", STRIDED_CHECKS)
 @pytest.mark.parametrize("bad,code", [
     (dict(ih=60), LA_ERR_INVALID_ARG), (dict(it=-128), LA_ERR_INVALID_ARG),   # not a multiple of 8 / < 0
     (dict(oh=4), LA_ERR_INVALID_ARG),
@@ -354,7 +357,7 @@ def test_strided_rejects_bad_arguments(lib, fn, bad, code):
 
 
 @needs_no_gpu
-@pytest.mark.parametrize("fn", STRIDED)
+@pytest.mark.parametrize("fn", STRIDED_CHECKS)
 @pytest.mark.parametrize("bad,code", [
     (dict(ot=64), LA_ERR_INVALID_ARG),              # output tokens overlap heads (ot < H*d)
     (dict(ot=0), LA_ERR_INVALID_ARG),               # every output token on one row
@@ -599,3 +602,13 @@ def test_fused_prologue_prefill_empty_is_a_noop(lib):
 def test_fused_prologue_prefill_rejects_bad_arguments(lib, bad, code):
     # no tokens (or a rejected position range): no check can reach a launch
     assert lib.la_prefill_qk_norm_rope_ws(*_fused_args(**bad)) == code
+
+
+@needs_no_gpu
+@pytest.mark.parametrize("bad,code", [
+    (dict(cu=None), LA_ERR_INVALID_ARG), (dict(cu=FAKE + 0x380004), LA_ERR_INVALID_ARG),
+    (dict(nseq=0), LA_ERR_INVALID_ARG), (dict(H=0), LA_ERR_INVALID_ARG),
+    (dict(N=-1), LA_ERR_INVALID_ARG), (dict(state=None), LA_ERR_INVALID_ARG),
+])
+def test_varlen_from_zero_rejects_bad_arguments(lib, bad, code):
+    assert lib.la_prefill_varlen_from_zero(*_strided_args("la_prefill_varlen_from_zero", **bad)) == code

@@ -183,3 +183,30 @@ def test_dense_batch_wide_grid_equals_single_rows_bitwise():
         torch.cuda.synchronize()
         assert torch.equal(o1, out[b:b + 1]), f"row {b}: outputs differ"
         assert torch.equal(s1, st[b:b + 1]), f"row {b}: states differ"
+
+
+@pytest.mark.parametrize("H,lens", [
+    (64, [0, 1, 63, 64, 65, 130, 0, 1000, 7, 257]),          # the walk at 64 heads
+    (64, [3000, 0, 700, 2048, 1500, 0, 999, 2500]),           # the 64-column grid
+    (3, [5, 0, 200, 1, 129]),                                  # the 32-column grid
+    (64, [int(n) for n in np.random.default_rng(9).integers(0, 40, size=1100)]),   # two walk launches
+    (8, [0, 0, 0]),                                            # no tokens at all
+])
+def test_varlen_from_zero_equals_zero_states_bitwise(H, lens):
+    # la_prefill_varlen_from_zero never reads the states (filled with NaN
+    # here) and gives exactly the results of zero-filled IN/OUT states; the
+    # empty sequences' states come out as zeros
+    walks = binding.prefill_varlen_walks(len(lens), H, max(1, sum(lens)), 128)
+    log(f"varlen from zero: H{H}, {len(lens)} sequences, T{sum(lens)}, walk={walks}")
+    inp = inputs.make_varlen(H, lens, 128, torch.bfloat16, seed=86, init_state=True, device=DEV)
+    zero = torch.zeros_like(inp.states)
+    ref_st = zero.clone()
+    ref = binding.prefill_varlen(inp.q, inp.k, inp.v, inp.slopes, inp.cu_seqlens, ref_st)
+    st = torch.full_like(inp.states, float("nan"))
+    out = binding.prefill_varlen(inp.q, inp.k, inp.v, inp.slopes, inp.cu_seqlens, st, from_zero=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref), "outputs differ from the zero-state run"
+    assert torch.equal(st, ref_st), "states differ from the zero-state run"
+    for i, n in enumerate(lens):
+        if n == 0:
+            assert torch.equal(st[i], zero[i]), f"empty sequence {i}: state not zeroed"

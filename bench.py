@@ -64,6 +64,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -507,8 +508,9 @@ def measure_ceilings(dev, stream, pre_ms, pre_tflops, dec_gbs):
     lib.la_peak_write.argtypes = [P, I64, P]
     lib.la_peak_copy.argtypes = [P, P, I64, P]
     lib.la_peak_update.argtypes = [P, I64, P]
+    lib.la_peak_mix3.argtypes = [P, P, P, P, I64, P]
     for f in (lib.la_peak_mfma_bf16, lib.la_peak_read, lib.la_peak_write, lib.la_peak_copy,
-              lib.la_peak_update):
+              lib.la_peak_update, lib.la_peak_mix3):
         f.restype = ctypes.c_int
     h = stream.cuda_stream
     nbytes = 4 << 30
@@ -533,25 +535,31 @@ def measure_ceilings(dev, stream, pre_ms, pre_tflops, dec_gbs):
         ms_write = best(lambda: lib.la_peak_write(a.data_ptr(), nbytes, h))
         ms_copy = best(lambda: lib.la_peak_copy(a.data_ptr(), b.data_ptr(), nbytes // 2, h))
         ms_upd = best(lambda: lib.la_peak_update(a.data_ptr(), nbytes // 2, h))
+        q4 = nbytes // 4                        # three quarters of a read, b's first half written
+        ms_mix = best(lambda: lib.la_peak_mix3(a.data_ptr(), a.data_ptr() + q4, a.data_ptr() + 2 * q4,
+                                               b.data_ptr(), q4, h))
     del a, b, sink
     tf = blocks * 4 * iters * chains * 32768 / (ms_mfma * 1e-3) / 1e12
-    rd, wr, cp, up = (x / (ms * 1e-3) / 1e9 for x, ms in
-                      ((nbytes, ms_read), (nbytes, ms_write), (nbytes, ms_copy), (nbytes, ms_upd)))
+    rd, wr, cp, up, mx = (x / (ms * 1e-3) / 1e9 for x, ms in
+                          ((nbytes, ms_read), (nbytes, ms_write), (nbytes, ms_copy), (nbytes, ms_upd),
+                           (nbytes, ms_mix)))
     B, H, N, d = PREFILL["B"], PREFILL["H"], PREFILL["N"], PREFILL["d"]
     st = B * H * d * d * 4
     rbytes, wbytes = B * H * N * d * 2 * 3 + st, B * H * N * d * 2 + st
     floor_ms = (rbytes / (rd * 1e9) + wbytes / (wr * 1e9)) * 1e3
     return {"mfma_bf16_tflops": round(tf, 1), "hbm_read_gbs": round(rd, 1),
             "hbm_write_gbs": round(wr, 1), "hbm_copy_gbs": round(cp, 1),
-            "hbm_update_gbs": round(up, 1),
+            "hbm_update_gbs": round(up, 1), "hbm_mix3_gbs": round(mx, 1),
             "probes": "lib/liblapeak.so: v_mfma_f32_32x32x16_bf16 chains on registers "
                       f"({blocks} workgroups of 4 waves, {chains} chains each); streams over "
                       "4 GiB in 64 KB chunks, one per workgroup, each chunk's 16-byte "
                       "nontemporal accesses all in flight (copy and in-place update: 2 GiB "
-                      "read + 2 GiB written, counted as 4 GiB); best of 3",
+                      "read + 2 GiB written, counted as 4 GiB; mix3: 3 GiB read + 1 GiB "
+                      "written, the prefill's 3:1 mix); best of 3",
             "prefill_frac_of_mfma_loop": round(pre_tflops / tf, 4),
             "prefill_floor_ms_at_stream_rates": round(floor_ms, 4),
             "prefill_frac_of_stream_floor": round(floor_ms / pre_ms, 4),
+            "prefill_frac_of_mix3_stream": round((rbytes + wbytes) / (pre_ms * 1e-3) / 1e9 / mx, 4),
             "decode_frac_of_update_stream": round(dec_gbs / up, 4)}
 
 
@@ -643,6 +651,14 @@ def measure_decode_latency(dev, stream, reps):
                       "per step"}
 
 
+def corrected_tokens(slopes, L):
+    """token-heads of an L-token shard whose correction factor
+    lambda^(a+1) = exp(-s (a+1)) is not 0 in fp32: below 2^-150 it rounds to
+    zero, so head s contributes the tokens with s (a+1) < 150 ln 2."""
+    lim = 150.0 * math.log(2.0)
+    return sum(min(L, max(0, math.ceil(lim / s) - 1)) if s > 0 else L for s in slopes)
+
+
 def measure_cp(dev, stream, reps):
     import torch
     from long_context_layers_amd import binding, inputs
@@ -674,7 +690,10 @@ def measure_cp(dev, stream, reps):
         ms_corr = time_launches(stream, correct, reps)
     state_bytes = B * H * d * d * 4
     by_fold = (R - 1 + 2) * state_bytes                 # 7 local states + S_init read, S_in written
-    by_corr = B * H * L * d * 2 * 3 + state_bytes        # q, out read, out written; S_in read
+    # q, out read, out written for the tokens whose factor lambda^(a+1) is not 0
+    # in fp32 (the others add exactly nothing and are skipped); S_in read
+    ntok = B * corrected_tokens(x.slopes.tolist(), L)
+    by_corr = ntok * d * 2 * 3 + state_bytes
     del x, loc, init, st, s_in, out
     gf, gc = by_fold / (ms_fold * 1e-3) / 1e9, by_corr / (ms_corr * 1e-3) / 1e9
     return {"workload": f"rank {R - 1} of {R}: shard B{B} H{H} L{L} d{d} bf16 of the 256K "
@@ -686,7 +705,8 @@ def measure_cp(dev, stream, reps):
                         "algorithmic_bytes": by_fold, "kernel": "cp_fold_kernel"},
             "cp_correct": {"ms": round(ms_corr, 4), "gbs": round(gc, 1),
                            "frac_of_hbm_peak": round(gc / HBM_PEAK_GBS, 4),
-                           "algorithmic_bytes": by_corr, "kernel": "cp_correct_kernel<128, -1>"},
+                           "algorithmic_bytes": by_corr, "corrected_token_heads": ntok,
+                           "kernel": "cp_correct_kernel<128, -1>"},
             "overhead_vs_local_prefill": round((ms_fold + ms_corr) / ms_loc, 4)}
 
 

@@ -59,8 +59,8 @@ __global__ __launch_bounds__(FT) void cp_fold_kernel(
 
 constexpr int CT = 256;            // correct: threads per workgroup (4 waves)
 constexpr int TT = 64;             // correct: tokens per tile
-constexpr int CTOK = 512;          // correct: tokens per chunk (8 tiles)
-constexpr int CWG = 32;            // correct: workgroups per (segment, b, h) at most
+constexpr int CTOK = 128;          // correct: tokens per chunk (2 tiles)
+constexpr int CWG = 128;           // correct: workgroups per (segment, b, h) at most
 constexpr int CPAD = 8;            // LDS row padding (bf16 elements)
 constexpr int RSRC_W3 = 0x00020000;   // buffer descriptor word 3 (raw 32-bit access)
 
@@ -84,8 +84,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t *base
 
 // A workgroup corrects the CTOK-token chunks c, c + cstride, ... of one
 // (segment, b, h) in 64-token tiles (cstride = min(chunks, CWG) workgroups
-// per row: a launch is a few thousand workgroups, not one per chunk, and each
-// reads its state once).
+// per row, each reading its state once: the corrected tokens of the slowest
+// heads spread over many workgroups, at most two tiles apiece in each of
+// their chunks; the workgroups of a row whose first tile has underflowed
+// return at once).
 // q and out tiles move between HBM and LDS as whole rows (thread i takes
 // 16-byte chunks i, i + 256, ...: every load or store instruction covers 4 KB
 // of consecutive rows), the next tile's loads are issued before the current

@@ -17,6 +17,9 @@
 //   la_peak_copy        chunks read, then written to a second buffer;
 //   la_peak_update      chunks read, then written back in place (the access
 //                       pattern of a state updated where it lives);
+//   la_peak_mix3        chunks of three buffers read and one written (three
+//                       bytes read for every byte written: the prefill's mix
+//                       of q, k, v in and out back);
 //   la_peak_l2_read     every workgroup sweeps one small region (a few MB,
 //                       held by each XCD's L2) again and again: L2 hits;
 //   la_peak_lds_read    every thread reads 16-byte LDS words in a loop, no
@@ -151,6 +154,21 @@ __global__ __launch_bounds__(PT) void update_kernel(u32x4 *__restrict__ buf)
     for (int u = 0; u < UNR; ++u) __builtin_nontemporal_store(x[u] + 1u, &p[u * PT]);
 }
 
+// three reads for every write: chunk g of a, b and c in, their xor out to
+// chunk g of d
+__global__ __launch_bounds__(PT) void mix3_kernel(const u32x4 *__restrict__ a, const u32x4 *__restrict__ b,
+                                                  const u32x4 *__restrict__ c, u32x4 *__restrict__ d)
+{
+    const int64_t o = blockIdx.x * CHUNK16 + threadIdx.x;
+    u32x4 x[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u)
+        x[u] = __builtin_nontemporal_load(&a[o + u * PT]) ^ __builtin_nontemporal_load(&b[o + u * PT]) ^
+               __builtin_nontemporal_load(&c[o + u * PT]);
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) __builtin_nontemporal_store(x[u], &d[o + u * PT]);
+}
+
 // L2 hits: each workgroup sweeps the region (region16 16-byte elements, a
 // multiple of a chunk) reps times, chunk by chunk, starting at a chunk of its
 // own so the workgroups spread over the L2 channels
@@ -270,6 +288,17 @@ int la_peak_update(void *buf, int64_t bytes, void *stream)
     if (!buf || !chunks_of(bytes, &g)) return -1;
     hipLaunchKernelGGL(update_kernel, dim3(g), dim3(PT), 0, static_cast<hipStream_t>(stream),
                        static_cast<u32x4 *>(buf));
+    return (int)hipGetLastError();
+}
+
+// bytes: the size of each of the four buffers (3 x bytes read, bytes written)
+int la_peak_mix3(const void *a, const void *b, const void *c, void *d, int64_t bytes, void *stream)
+{
+    unsigned g;
+    if (!a || !b || !c || !d || !chunks_of(bytes, &g)) return -1;
+    hipLaunchKernelGGL(mix3_kernel, dim3(g), dim3(PT), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const u32x4 *>(a), static_cast<const u32x4 *>(b),
+                       static_cast<const u32x4 *>(c), static_cast<u32x4 *>(d));
     return (int)hipGetLastError();
 }
 

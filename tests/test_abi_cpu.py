@@ -446,7 +446,7 @@ def test_peak_probe_library_loads_and_rejects_bad_arguments():
     peak = ctypes.CDLL(build.PEAK_LIB)
     P, I64 = ctypes.c_void_p, ctypes.c_int64
     for name in ("la_peak_mfma_bf16", "la_peak_read", "la_peak_write", "la_peak_copy",
-                 "la_peak_update", "la_peak_mfma_chains"):
+                 "la_peak_update", "la_peak_mix3", "la_peak_mfma_chains"):
         assert hasattr(peak, name), name
     peak.la_peak_mfma_bf16.argtypes = [I64, I64, P, P]
     peak.la_peak_read.argtypes = [P, I64, P, P]
@@ -462,6 +462,9 @@ def test_peak_probe_library_loads_and_rejects_bad_arguments():
     assert peak.la_peak_copy(FAKE, None, 32, None) == -1
     peak.la_peak_update.argtypes = [P, I64, P]
     assert peak.la_peak_update(FAKE, 8, None) == -1
+    peak.la_peak_mix3.argtypes = [P, P, P, P, I64, P]
+    assert peak.la_peak_mix3(FAKE, FAKE, FAKE, None, 65536, None) == -1
+    assert peak.la_peak_mix3(FAKE, FAKE, FAKE, FAKE, 65536 + 16, None) == -1    # not whole chunks
 
 
 def _dstr_args(**kw):

@@ -4,6 +4,7 @@ import os
 import subprocess
 import sys
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -124,3 +125,22 @@ def test_traffic_summary_of_the_fused_call(tmp_path):
         bench.write_traffic_summary(str(tmp_path / "f.csv"), str(tmp_path / "w.csv"),
                                     str(tmp_path / "cf.csv"), str(tmp_path / "cw.csv"),
                                     [], out=str(tmp_path / "x.txt"), call="split")
+
+
+@pytest.mark.parametrize("s", [1.0, 0.5, 2.0 ** -0.125, 2.0 ** -4, 2.0 ** -8, 1e-3])
+def test_corrected_tokens_counts_nonzero_fp32_factors(s):
+    # the tokens whose factor exp(-s (a+1)) survives in fp32, by brute force
+    # over every token of the shard (numpy's fp32 exp; at most one token of
+    # difference at the rounding threshold)
+    L = 40000
+    a = np.arange(L, dtype=np.float64)
+    f = np.exp(-(np.float32(s) * (a + 1).astype(np.float32)), dtype=np.float32)
+    brute = int(np.count_nonzero(f))
+    assert abs(bench.corrected_tokens([s], L) - brute) <= 1
+
+
+def test_corrected_tokens_special_cases():
+    assert bench.corrected_tokens([0.0], 77) == 77              # lambda = 1: every token
+    assert bench.corrected_tokens([1e-9], 100) == 100           # nothing underflows in a short shard
+    assert bench.corrected_tokens([200.0], 100) == 0            # lambda^1 is already 0
+    assert bench.corrected_tokens([1.0, 1.0], 10) == 20         # a sum over heads

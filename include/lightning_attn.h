@@ -84,8 +84,9 @@ int la_prefill(const void *q, const void *k, const void *v, const float *slopes,
  * when B = 1: with workgroups of 64 output columns (d = 128; 32 at d = 64),
  * which read each head's Q and K through L2 half as often as la_prefill's
  * and write whole 128-byte output lines, S = CUs / (H * d/64) segments (each
- * at least 16384 tokens, at most 64 of them; none below 2) run in one
- * launch, the first from the caller's state and the others from zero; the
+ * at least 4096 tokens when la_prefill's grid of H * d/32 workgroups leaves
+ * compute units idle, else at least 8192; at most 64 of them; none below 2)
+ * run in one launch, the first from the caller's state and the others from zero; the
  * segments' states are then chained into the state at each boundary and the
  * final state, and each later segment's outputs are corrected with the state
  * at its start (o_a += lambda^(a+1) q_a S for its local token index a).  This

@@ -1261,10 +1261,17 @@ const void *prefill_fn(int d, bool strided)
 // times and write every output row slice as one whole 128-byte line: a copy
 // of the kernel with the compute removed streams the 256K, 64-head workload
 // in 3.34 against 4.27 ms.  With njt tiles, S = CUs / (H * d/(32 njt)), each
-// segment at least SPLIT_MIN_LEN tokens and at most MAX_SPLIT segments; the
-// wide tiles are taken unless the narrow ones keep markedly more workgroups
-// busy (few heads on a short sequence: the segment length bounds S).
-constexpr int64_t SPLIT_MIN_LEN = 16384;
+// segment at least min_len tokens and at most MAX_SPLIT segments; the wide
+// tiles are taken unless the narrow ones keep markedly more workgroups busy
+// (few heads on a short sequence: the segment length bounds S).  The later
+// segments' correction re-reads q and out for up to ~26K tokens of the
+// slowest heads, so a split pays on short sequences only when the unsplit
+// grid leaves compute units idle (segments from SPLIT_MIN_LEN tokens: at 32
+// heads 8K tokens 115 -> 96 us, 16K 237 -> 164 us); when it fills the device
+// the gain is the wide tiles' alone and needs segments from SPLIT_MIN_LEN_FULL
+// (64 heads: 16K tokens 278 -> 261 us, but 8K 141 -> 148 us).
+constexpr int64_t SPLIT_MIN_LEN = 4096;
+constexpr int64_t SPLIT_MIN_LEN_FULL = 8192;
 constexpr int MAX_SPLIT = 64;
 
 int prefill_split_plan(int64_t B, int64_t H, int64_t N, int d, int *njt)
@@ -1273,11 +1280,12 @@ int prefill_split_plan(int64_t B, int64_t H, int64_t N, int d, int *njt)
     if (B != 1 || H < 1 || N < 2 * SPLIT_MIN_LEN) return 1;
     const int cus = device_cus();
     if (cus <= 0) return 1;
+    const int64_t min_len = H * (d / PJ) >= cus ? SPLIT_MIN_LEN_FULL : SPLIT_MIN_LEN;
     int best_s = 1;
     double best = 0.0;
     for (int t = (d == 128 ? 2 : 1); t >= 1; --t) {
         const int64_t wg = H * (d / (PJ * t));
-        int64_t S = std::min<int64_t>(cus / wg, N / SPLIT_MIN_LEN);
+        int64_t S = std::min<int64_t>(cus / wg, N / min_len);
         S = std::min<int64_t>(S, MAX_SPLIT);
         if (S < 2) continue;
         const double busy = (double)std::min<int64_t>(S * wg, cus) * (t == 2 ? 1.2 : 1.0);

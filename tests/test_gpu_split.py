@@ -50,10 +50,14 @@ def unsplit(inp, state):
 
 @pytest.mark.parametrize("H,N,slopes", [
     (64, 40000, None),                                   # 2 segments, ragged, the model's decays
-    (32, 40000, None),                                   # 2 segments
-    (8, 65536 + 77, [0.0, 1e-4, 1e-3, 0.01, 0.1, 1.0, 5.0, math.inf]),   # 4 segments; lambda = 1 .. 0
+    (32, 40000, None),                                   # 4 segments
+    (8, 65536 + 77, [0.0, 1e-4, 1e-3, 0.01, 0.1, 1.0, 5.0, math.inf]),   # 16 segments; lambda = 1 .. 0
     (64, 262144, None),                                  # the 256K workload's shape: 2 segments
-    (1, 70000, [1e-4]),                                  # 4 segments, slow decay: full corrections
+    (1, 70000, [1e-4]),                                  # 17 segments, slow decay: full corrections
+    (64, 16384 + 100, None),                             # 2 segments of ~8K (full device unsplit)
+    (32, 8192 + 5, None),                                # 2 segments of ~4K (half the device unsplit)
+    (8, 16384 + 33, [0.0, 1e-4, 1e-3, 0.01, 0.1, 1.0, 5.0, 2.0 ** -8]),   # 4 segments of ~4K
+    (1, 33000, [2.0 ** -8]),                             # 8 segments, the slowest model decay
 ])
 def test_split_matches_oracle(H, N, slopes):
     ws = need_split(1, H, N)
@@ -116,7 +120,9 @@ def test_workspace_rules_are_checked_before_any_launch():
 def test_split_plan():
     # segments of 64-column workgroups (d = 128) or 32-column ones (d = 64):
     # 64 heads of 128 split in two on 256 compute units, 128 heads of 64 fill
-    # the device unsplit, B > 1 and short sequences never split
+    # the device unsplit, B > 1 never splits; segments of at least 8192 tokens
+    # where la_prefill's grid fills the device, of at least 4096 where it
+    # leaves compute units idle
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     if cus != 256:
         pytest.skip("the expected plans are those of a 256-CU device")
@@ -125,7 +131,14 @@ def test_split_plan():
     assert binding.prefill_workspace_bytes(1, 32, 262144, 128, DEV) == 4 * d128 // 2 + 256
     assert binding.prefill_workspace_bytes(1, 128, 262144, 64, DEV) == 0
     assert binding.prefill_workspace_bytes(2, 32, 262144, 128, DEV) == 0
-    assert binding.prefill_workspace_bytes(1, 64, 16384, 128, DEV) == 0     # too short to split
+    assert binding.prefill_workspace_bytes(1, 64, 16384, 128, DEV) == 2 * d128 + 256
+    assert binding.prefill_workspace_bytes(1, 64, 16383, 128, DEV) == 0     # too short to split
+    assert binding.prefill_workspace_bytes(1, 64, 8192, 128, DEV) == 0
+    assert binding.prefill_workspace_bytes(1, 32, 8192, 128, DEV) == d128 + 256
+    assert binding.prefill_workspace_bytes(1, 32, 8191, 128, DEV) == 0
+    assert binding.prefill_workspace_bytes(1, 8, 16384, 128, DEV) == 4 * d128 // 8 + 256
+    # one head: 64 segments of 4096 (at most 64), 65 offsets in the tail
+    assert binding.prefill_workspace_bytes(1, 1, 262144, 128, DEV) == 64 * d128 // 64 + 768
 
 
 @pytest.mark.parametrize("H,N,d", [(32, 40000, 128), (64, 65536 + 300, 64)])

@@ -31,7 +31,7 @@ def _call(fn, inp, out, st, *extra):
 
 def test_noalloc_equals_the_workspace_call_twice_in_a_row():
     lib = binding.load_library()
-    shapes = [(32, 40000, 801), (16, 33000, 802)]          # second call smaller
+    shapes = [(32, 40000, 801), (16, 12000, 802)]          # second call smaller (8 and 2 MiB)
     planned = [binding.prefill_workspace_bytes(1, H, N, 128, DEV) for H, N, _ in shapes]
     if not all(planned):
         pytest.skip(f"no sequence split planned on this device ({planned})")

@@ -105,9 +105,10 @@ TRAFFIC_CALLS = {
               "on the 256K layer workload (B={B}, H={H}, N={N}, d={d}, bf16; raw q, k, v in one",
               "[B, N, 4*H*d] projection buffer, [B,H,N,d] output, zero initial state)"],
         out=FUSED_TRAFFIC_FILE)}
-# the sources of the timed prefill call's kernels (the traffic profile is keyed by their hash)
+# the sources of the timed prefill calls' kernels, the headers they include
+# among them (the traffic profiles are keyed by their hash)
 KERNEL_SRCS = [os.path.join(ROOT, "long_context_layers_amd", "csrc", f)
-               for f in ("prefill_bf16.hip", "cp.hip")]
+               for f in ("prefill_bf16.hip", "cp.hip", "la_internal.h", "qk_prologue.h")]
 
 
 def prefill_flops(B, H, N, d):

@@ -336,7 +336,8 @@ def measure_varlen(dev, stream, reps, dense_tflops):
                 "algorithmic_bytes_per_launch": by,
                 "vs_dense_256k_tflops": round(tflops / dense_tflops, 4),
                 "kernel": ("prefill_bf16_kernel<128, false, true, 1, -1>: one workgroup per head and "
-                           "32 columns walks every sequence" if walks else
+                           "32 columns walks every sequence of its group (groups of sequences walked side "
+                           "by side fill the device)" if walks else
                            f"prefill_bf16_kernel<128, false, false, {njt}, -1>: one workgroup per "
                            f"sequence, head and {32 * njt} columns")}
 

@@ -26,6 +26,8 @@ struct SeqMap {
     Strides in, out;
     int zero_init;        // 1: every sequence starts from a zero state and the states
                           // are only written (empty sequences: zeros), never read
+    int walk_groups;      // a walking launch: groups of its sequences walked side by side
+                          // (0 or 1: one group)
 };
 
 // start offsets (elements) of slice (seq, h) in the inputs and the output, and its length

@@ -168,18 +168,38 @@ struct WalkTable {
     int nempty;
 };
 
-// one wave fills the table (a barrier must follow before anyone reads it)
-__device__ void build_table(WalkTable &tb, const SeqMap &m, int64_t nseq, int lane)
+// The sequences of a walking launch can be walked as `groups` groups side by
+// side (more workgroups when one per head and column slice would leave compute
+// units idle): a sequence belongs to the group its clamped start offset falls
+// in when the launch's token range is cut into `groups` equal parts, so the
+// groups carry about equal numbers of tokens, and every sequence, however
+// malformed its offsets, belongs to exactly one group.
+__device__ __forceinline__ int walk_group(int64_t start, int64_t first, int64_t span, int groups)
 {
+    if (groups <= 1 || span <= 0) return 0;
+    const int64_t g = max(start - first, (int64_t)0) * groups / span;
+    return (int)min(g, (int64_t)groups - 1);
+}
+
+// one wave fills the table with the sequences of group `group` (a barrier must
+// follow before anyone reads it)
+__device__ void build_table(WalkTable &tb, const SeqMap &m, int64_t nseq, int lane, int group)
+{
+    const int groups = m.walk_groups;
+    const int64_t first = min(max(m.cu[0], (int64_t)0), m.T);
+    const int64_t span = min(max(m.cu[nseq], (int64_t)0), m.T) - first;
     int count = 0, nblk = 0, nempty = 0;
     for (int64_t base = 0; base < nseq; base += 64) {
         const int64_t s = base + lane;
         int a = 0, n = 0;
+        bool mine = false;
         if (s < nseq) {
             const int64_t a64 = min(max(m.cu[s], (int64_t)0), m.T);
             a = (int)a64;
             n = (int)(min(max(m.cu[s + 1], a64), m.T) - a64);
+            mine = walk_group(a64, first, span, groups) == group;
         }
+        if (!mine) n = 0;
         const uint64_t mask = __ballot(n > 0);
         const int before = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
@@ -189,10 +209,11 @@ __device__ void build_table(WalkTable &tb, const SeqMap &m, int64_t nseq, int la
             tb.len[count + before] = n;
         }
         count += __popcll(mask);
-        const uint64_t emask = __ballot(s < nseq && n == 0);
+        const bool empty = mine && n == 0;
+        const uint64_t emask = __ballot(empty);
         const int ebefore = __builtin_amdgcn_mbcnt_hi((uint32_t)(emask >> 32),
                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)emask, 0));
-        if (s < nseq && n == 0) tb.empty[nempty + ebefore] = (int)s;
+        if (empty) tb.empty[nempty + ebefore] = (int)s;
         nempty += __popcll(emask);
         int b = (n + PC - 1) / PC;
         for (int off = 32; off > 0; off >>= 1) b += __shfl_xor(b, off);
@@ -1094,7 +1115,8 @@ __global__ __launch_bounds__(NTHREADS) void prefill_bf16_kernel(
 
     // XCD-aware placement: workgroup i runs on XCD i % 8 and workgroups start
     // in index order.  Workgroups 8q + x (x = 0..7) take slice q % NJ of
-    // (sequence, head) slot 8 (q / NJ) + x (WALK: of head 8 (q / NJ) + x): the
+    // (sequence, head) slot 8 (q / NJ) + x (WALK: of (group, head) slot
+    // 8 (q / NJ) + x, the head being the slot modulo H): the
     // NJ slices of one head run on one XCD at the same time (Q and K come from
     // HBM once, then from that XCD's L2), and consecutive heads of a sequence
     // go to different XCDs, so every XCD gets an equal share of every
@@ -1112,14 +1134,14 @@ __global__ __launch_bounds__(NTHREADS) void prefill_bf16_kernel(
     Walk<WALK> wk;
     wk.map = map;
     wk.nseq = nseq;
-    wk.h = WALK ? bh : bh % map.H;
+    wk.h = bh % map.H;                   // (WALK: head slot bh = group * H + head)
     wk.tb = nullptr;
     wk.slot = nullptr;
     const int lane = tid % 64;
     if constexpr (WALK) {
         __shared__ WalkTable tb;
         __shared__ __attribute__((aligned(16))) float slot[D * 32];   // state rows [D][32], staged / drained
-        if (wave == 0) build_table(tb, map, nseq, lane);
+        if (wave == 0) build_table(tb, map, nseq, lane, (int)(bh / map.H));
         __syncthreads();
         wk.tb = &tb;
         wk.slot = slot;
@@ -1212,33 +1234,46 @@ int prefill_bf16_grid_njt(int64_t seqs, int64_t H, int d)
 // time, one launch each).  The estimates, in microseconds, fitted to measured
 // launches (H = 32 and 64, 64 .. 16384 tokens per sequence and mixed lengths
 // at 256K tokens, d = 128):
-//   walk: rounds * (0.98 T/64 + 1.51 nseq) * (0.6 + 0.4 occupancy), where
-//         rounds is the number of device-fills its H * d/32 workgroups take,
-//         occupancy the share of those rounds' compute units they use (a
-//         block step is that much shorter on a partly idle device), and the
-//         per-sequence term the hand-over at a boundary plus the partial
-//         last block;
-//   grid, 64-column workgroups: 1.66 * (T/64 + 4 nseq) * 2H / CUs;
+//   walk: rounds * (0.98 T/64 + 1.51 nseq) / G * (0.6 + 0.4 occupancy), where
+//         G is the number of sequence groups walked side by side (as many as
+//         fill the device with H * d/32 workgroups each, at most one per
+//         sequence), rounds the number of device-fills the G * H * d/32
+//         workgroups take, occupancy the share of those rounds' compute units
+//         they use (a block step is that much shorter on a partly idle
+//         device), and the per-sequence term the hand-over at a boundary plus
+//         the partial last block;
+//   grid, 64-column workgroups: 1.57 * (T/64 + 3.2 nseq) * 2H / CUs;
 //   grid, 32-column workgroups: 1.05 * (T/64 + 4.25 nseq) * (H * d/32) / CUs,
 //         the per-sequence terms being each workgroup's pipeline fill and
 //         drain plus its block count rounded up to the producers' four-block
 //         unroll.
-// So the walk wins for sequences of up to about 256 tokens at 64 heads and
-// about 64 at 32 heads; the wide grid for longer ones.
+// So the walk wins for sequences of up to about 256 tokens at 8 to 64 heads
+// (measured at 256K tokens, walk / 64-column grid, ms: 64 heads 1024 x 256
+// 5.63 / 5.85, 512 x 512 4.76 / 4.50; 32 heads 2.81 / 2.94 and 2.49 / 2.29;
+// 8 heads 0.69 / 0.74 and 0.60 / 0.59), the wide grid for longer ones.
 constexpr int64_t WALK_MEAN_LEN = 8192;
+
+int prefill_bf16_walk_groups(int64_t nseq, int64_t H, int d)
+{
+    const int cus = device_cus();
+    const int64_t wg = H * (d / PJ);
+    if (cus <= 0 || wg >= cus) return 1;
+    return (int)std::max<int64_t>(1, std::min<int64_t>(cus / wg, nseq));
+}
 
 bool prefill_bf16_walks(int64_t seqs, int64_t H, int64_t T, int d, bool packed)
 {
     if (!packed || seqs < 2 || T > 0x7fffffff || T / seqs >= WALK_MEAN_LEN) return false;
     const int cus = device_cus();
     if (cus <= 0) return false;
-    const double wg = (double)H * (d / PJ);
+    const double groups = prefill_bf16_walk_groups(std::min<int64_t>(seqs, WALK_SEQS), H, d);
+    const double wg = (double)H * (d / PJ) * groups;
     const double rounds = std::ceil(wg / cus);
     const double occupancy = wg / (rounds * cus);
     const double blocks = (double)T / PC, n = (double)seqs;
-    const double walk = rounds * (0.98 * blocks + 1.51 * n) * (0.6 + 0.4 * occupancy);
+    const double walk = rounds * (0.98 * blocks + 1.51 * n) / groups * (0.6 + 0.4 * occupancy);
     const double grid = prefill_bf16_grid_njt(seqs, H, d) == 2
-                            ? 1.66 * (blocks + 4.0 * n) * 2.0 * H / cus
+                            ? 1.57 * (blocks + 3.2 * n) * 2.0 * H / cus
                             : 1.05 * (blocks + 4.25 * n) * wg / cus;
     return walk < grid;
 }
@@ -1353,13 +1388,14 @@ hipError_t launch_prefill_bf16(const uint16_t *q, const uint16_t *k, const uint1
         SeqMap m = map;
         m.cu = map.cu + s0;
         int64_t nseq = seqs - s0 < WALK_SEQS ? seqs - s0 : WALK_SEQS;
+        m.walk_groups = prefill_bf16_walk_groups(nseq, map.H, d);
         float *st = state + s0 * map.H * d * d;
         QkPrologue pr = {nullptr, nullptr, 0.0, 0, 0.0f, 0};
         void *args[] = {(void *)&q, (void *)&k, (void *)&v, (void *)&slopes,
                         (void *)&out, (void *)&st, (void *)&m, (void *)&nseq, (void *)&pr};
         const hipError_t e = hipLaunchKernel(prefill_fn<true>(d, strided),
-                                             dim3((unsigned)prefill_bf16_grid(1, map.H, d, 1)), block,
-                                             args, 0, stream);
+                                             dim3((unsigned)prefill_bf16_grid(m.walk_groups, map.H, d, 1)),
+                                             block, args, 0, stream);
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -191,6 +191,8 @@ def test_dense_batch_wide_grid_equals_single_rows_bitwise():
     (3, [5, 0, 200, 1, 129]),                                  # the 32-column grid
     (64, [int(n) for n in np.random.default_rng(9).integers(0, 40, size=1100)]),   # two walk launches
     (8, [0, 0, 0]),                                            # no tokens at all
+    (32, [int(n) for n in np.random.default_rng(10).integers(0, 121, size=300)]),   # walk groups
+    (8, [0, 0, 5, 0, 300, 0, 1]),                              # groups with only empty sequences
 ])
 def test_varlen_from_zero_equals_zero_states_bitwise(H, lens):
     # la_prefill_varlen_from_zero never reads the states (filled with NaN

@@ -20,7 +20,9 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 HEADS = {128: 64, 64: 128}          # heads that make the walk fill 256 compute units
-SHAPES = [(128, 64), (128, 32), (64, 128)]   # (d, H); H = 32 walks short sequences only
+# (d, H); fewer heads than fill the device walk their sequences as groups side
+# by side (32 heads: 2 groups, 16: 4, 8: 8 on 256 compute units)
+SHAPES = [(128, 64), (128, 32), (64, 128), (128, 16), (128, 8)]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -60,6 +62,9 @@ CASES = {
     "two": [5, 700],
     # many short prompts (the report's §4.1.2 pain point), 0..120 tokens
     "short_many": [int(n) for n in np.random.default_rng(664).integers(0, 121, size=300)],
+    # one long sequence among many short ones: the groups of a walk split the
+    # tokens, not the sequences, evenly (the long one fills a group alone)
+    "skewed": [3000, 1, 0, 2] + [int(n) for n in np.random.default_rng(665).integers(0, 41, size=150)],
 }
 
 
@@ -134,11 +139,13 @@ def test_packed_256k_workload_equals_per_sequence_launches():
     assert torch.equal(out, o1), "outputs differ from per-sequence launches"
 
 
-def test_walk_more_sequences_than_one_table():
+@pytest.mark.parametrize("H", [64, 32])
+def test_walk_more_sequences_than_one_table(H):
     # 1100 short sequences (some empty): walked 1024 at a time, two launches
+    # (at 32 heads each in two groups)
     rng = np.random.default_rng(7)
     lens = [int(x) for x in rng.integers(0, 40, size=1100)]
-    d, H = 128, HEADS[128]
+    d = 128
     need_walk(len(lens), H, sum(lens), d)
     log(f"walk over {len(lens)} sequences of 0..39 tokens, H{H} d{d}")
     x = inputs.make_varlen(H, lens, d, torch.bfloat16, seed=662, init_state=True, device=DEV)
@@ -159,12 +166,12 @@ MALFORMED = {
 
 
 @pytest.mark.parametrize("case", sorted(MALFORMED))
-@pytest.mark.parametrize("H", [4, 64])
+@pytest.mark.parametrize("H", [4, 16, 64])
 def test_malformed_offsets_stay_inside_the_tensors(H, case):
     # the results are unspecified, but every access stays inside q, k, v, out
     # and the states (offsets are clamped into [0, T]), and rows outside every
     # clamped sequence are not written.  H = 4: one workgroup per sequence;
-    # H = 64: the walk (on a 256-CU device).
+    # H = 16: the walk in groups; H = 64: the walk (on a 256-CU device).
     offsets, free_from = MALFORMED[case]
     d, T = 128, 1100
     cu = torch.tensor(offsets, dtype=torch.int64, device=DEV)

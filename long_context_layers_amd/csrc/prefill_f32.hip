@@ -1,9 +1,10 @@
 // prefill_f32.hip — blockwise decayed linear attention with fp32 activations.
 //
-// The same block decomposition as the bf16 MFMA kernel, evaluated with fp32
-// vector FMAs (the fp32 path keeps full fp32 operands; rounding them to bf16
-// for the matrix cores would cost more accuracy than fp32 callers expect).
-// For one (b, h) and the block of c tokens starting at t0 (local a, b < c):
+// The block decomposition of the bf16 kernel with every product on the fp32
+// matrix cores (v_mfma_f32_32x32x2_f32: fp32 operands, fp32 accumulation; the
+// fp32 path keeps full fp32 operands, rounding them to bf16 would cost more
+// accuracy than fp32 callers expect).  For one (b, h) and the block of c
+// tokens starting at t0 (local a, b < c):
 //   P[a][b] = lambda^(a-b) (q_a . k_b)              for b <= a, else 0
 //   O[a]    = sum_b P[a][b] v_b + lambda^(a+1) q_a S
 //   S       = lambda^c S + sum_b lambda^(c-1-b) k_b^T v_b
@@ -12,93 +13,206 @@
 // 2.6 Technical Report, §4.1.1 and Fig. 10), applied block after block.
 //
 // One workgroup per (sequence, head, 32-column slice of v/S/O) of a dense or
-// packed launch; the slice's state stays in LDS for the whole sequence.  Not a throughput kernel: the fp32 path
-// serves small fp32 problems and correctness checks.
+// packed launch, one wave per 32-row tile of the state (D/32 waves), blocks of
+// 32 tokens.  Wave t keeps state rows 32t..32t+31 of the slice in registers
+// (accumulator layout: lane (column j, half h), register r holds row
+// 8 (r/4) + 4h + r%4 of the tile) and per block computes, for its 32
+// features, the partial scores S^T = K_t Q_t^T and the partial inter term
+// S_t^T Q_t^T (both with Q_t^T as the B operand: the state registers are the
+// A operand as they stand), then its state tile's update K_t^T (lambda-
+// weighted V).  The partial scores of the D/32 waves are summed through LDS,
+// masked and decayed; each wave multiplies V^T by its share of the token rows
+// of P^T into its partial output, and the partial outputs are summed through
+// LDS and stored, 128 bytes per token row.  The next block's q, k and v are
+// loaded into registers while a block is computed; LDS tiles and partials are
+// double-buffered, two barriers per block.
 #include "la_internal.h"
 
 namespace la {
 namespace {
 
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
 constexpr int FC = 32;      // tokens per block
 constexpr int FJ = 32;      // state / output columns per workgroup
-constexpr int FT = 256;     // threads per workgroup
+constexpr int RP = 4;       // row padding of the LDS tiles (floats)
 
 template <int D>
-__global__ __launch_bounds__(FT) void prefill_f32_kernel(
+struct F32Smem {
+    float Q[2][FC][D + RP];
+    float K[2][FC][D + RP];
+    float V[2][FC][FJ + RP];
+    float P[2][D / 32][FC][FC + RP];     // partial scores of each feature tile, [b][a]
+    float O[2][D / 32][FJ][FC + RP];     // partial outputs of each wave, [j][a]
+    float pw[FC + 1];                    // lambda^n, n = 0..FC
+};
+
+// contraction index of MFMA step m for lane half h (and the accumulator row of
+// register m): 8 (m/4) + 4h + m%4 covers 0..31 once over m = 0..15, h = 0, 1
+__device__ __forceinline__ int kk(int m, int h) { return 8 * (m >> 2) + 4 * h + (m & 3); }
+
+__device__ __forceinline__ f32x16 mfma(float a, float b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * (D / 32)) void prefill_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ slopes, float *__restrict__ out, float *__restrict__ state,
     SeqMap map)
 {
-    constexpr int NJ = D / FJ;
-    __shared__ float Qs[FC][D + 1];
-    __shared__ float Ks[FC][D + 1];
-    __shared__ float Vs[FC][FJ];
-    __shared__ float Ps[FC][FC + 1];
-    __shared__ float Ss[D][FJ];
-    __shared__ float pw[FC + 1];          // lambda^n, n = 0..FC
+    constexpr int NT = D / 32;                  // feature tiles = waves
+    constexpr int NTH = 64 * NT;                // threads
+    constexpr int NJ = D / FJ;                  // workgroups per head
+    constexpr int NQ = FC * D / 4 / NTH;        // float4 of a q (k) block per thread
+    constexpr int NV = FC * FJ / 4 / NTH;       // float4 of a v block slice per thread
+    constexpr int BQ = FC / NT;                 // token rows of P^T (and output tokens) per wave
+    __shared__ F32Smem<D> sm;
 
     const int tid = threadIdx.x;
-    const int64_t bh = blockIdx.x / NJ;          // sequence * H + head
-    const int j0 = (blockIdx.x % NJ) * FJ;
-    const float s = slopes[bh % map.H];
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int lane = tid % 64, l32 = lane % 32, h = lane / 32;
+
+    // XCD-aware placement as in the bf16 kernel: the NJ slices of one
+    // (sequence, head) run on one XCD at once (q and k from HBM once, then
+    // from that XCD's L2), consecutive heads on different XCDs
+    const int64_t nbh = gridDim.x / NJ;
+    int64_t bh, slice;
+    if (nbh % 8 == 0) {
+        const int64_t q8 = blockIdx.x / 8;
+        bh = (q8 / NJ) * 8 + blockIdx.x % 8;
+        slice = q8 % NJ;
+    } else {
+        bh = blockIdx.x / NJ;
+        slice = blockIdx.x % NJ;
+    }
+    const int j0 = (int)slice * FJ;
+    const int64_t hd = bh % map.H;
+    const float s = slopes[hd];
     int64_t in0, out0, N;
-    seq_slice(map, bh / map.H, bh % map.H, &in0, &out0, &N);
+    seq_slice(map, bh / map.H, hd, &in0, &out0, &N);
     const int64_t ts = map.in.st, ots = map.out.st;   // token strides (elements)
-    if (tid <= FC) pw[tid] = decay_pow(s, tid);
-
-    float *St = state + bh * D * D;
-    for (int e = tid; e < D * FJ; e += FT) Ss[e / FJ][e % FJ] = St[(e / FJ) * D + j0 + e % FJ];
-
     const float *qb = q + in0, *kb = k + in0, *vb = v + in0;
     float *ob = out + out0;
+    if (tid <= FC) sm.pw[tid] = decay_pow(s, tid);
 
-    for (int64_t t0 = 0; t0 < N; t0 += FC) {
+    float *St = state + bh * D * D;
+    f32x16 S;                                   // state rows 32 wave + kk(r, h), column j0 + l32
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S[r] = St[(32 * wave + kk(r, h)) * D + j0 + l32];
+
+    float4 pq[NQ], pk[NQ], pv[NV];
+    auto load = [&](int64_t t0, int c) {        // rows c.. of the block read as zeros
+#pragma unroll
+        for (int u = 0; u < NQ; ++u) {
+            const int e = tid + NTH * u, row = e / (D / 4), c4 = e % (D / 4);
+            pq[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            pk[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (row < c) {
+                pq[u] = *reinterpret_cast<const float4 *>(qb + (t0 + row) * ts + 4 * c4);
+                pk[u] = *reinterpret_cast<const float4 *>(kb + (t0 + row) * ts + 4 * c4);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int e = tid + NTH * u, row = e / (FJ / 4), c4 = e % (FJ / 4);
+            pv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (row < c) pv[u] = *reinterpret_cast<const float4 *>(vb + (t0 + row) * ts + j0 + 4 * c4);
+        }
+    };
+    auto stage = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < NQ; ++u) {
+            const int e = tid + NTH * u, row = e / (D / 4), c4 = e % (D / 4);
+            *reinterpret_cast<float4 *>(&sm.Q[buf][row][4 * c4]) = pq[u];
+            *reinterpret_cast<float4 *>(&sm.K[buf][row][4 * c4]) = pk[u];
+        }
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int e = tid + NTH * u, row = e / (FJ / 4), c4 = e % (FJ / 4);
+            *reinterpret_cast<float4 *>(&sm.V[buf][row][4 * c4]) = pv[u];
+        }
+    };
+
+    const int64_t nblk = (N + FC - 1) / FC;
+    if (nblk > 0) {
+        load(0, (int)min((int64_t)FC, N));
+        stage(0);
+    }
+    __syncthreads();                            // block 0 and the powers visible
+    for (int64_t n = 0; n < nblk; ++n) {
+        const int buf = (int)(n & 1);
+        const int64_t t0 = n * FC;
         const int c = (int)min((int64_t)FC, N - t0);
-        __syncthreads();   // previous block's readers are done; pw / Ss visible
-        for (int e = tid; e < FC * D; e += FT) {
-            const int a = e / D, f = e % D;
-            const bool ok = a < c;
-            Qs[a][f] = ok ? qb[(t0 + a) * ts + f] : 0.0f;
-            Ks[a][f] = ok ? kb[(t0 + a) * ts + f] : 0.0f;
+        const bool more = n + 1 < nblk;
+        if (more) load(t0 + FC, (int)min((int64_t)FC, N - t0 - FC));
+
+        // partial scores S^T[b][a] and inter term over features 32 wave .. +31:
+        // A = K[b][k] (lane b) and S^T[j][k] (the state registers), B = Q^T[k][a] (lane a)
+        float qa[16], ka[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float4 x = *reinterpret_cast<const float4 *>(&sm.Q[buf][l32][32 * wave + 8 * g + 4 * h]);
+            const float4 y = *reinterpret_cast<const float4 *>(&sm.K[buf][l32][32 * wave + 8 * g + 4 * h]);
+            qa[4 * g] = x.x; qa[4 * g + 1] = x.y; qa[4 * g + 2] = x.z; qa[4 * g + 3] = x.w;
+            ka[4 * g] = y.x; ka[4 * g + 1] = y.y; ka[4 * g + 2] = y.z; ka[4 * g + 3] = y.w;
         }
-        for (int e = tid; e < FC * FJ; e += FT) {
-            const int a = e / FJ, j = e % FJ;
-            Vs[a][j] = a < c ? vb[(t0 + a) * ts + j0 + j] : 0.0f;
+        f32x16 sc = {}, oc = {};
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            sc = mfma(ka[m], qa[m], sc);
+            oc = mfma(S[m], qa[m], oc);
         }
-        __syncthreads();
-        // decayed causal scores of the block
-        for (int e = tid; e < FC * FC; e += FT) {
-            const int a = e / FC, b = e % FC;
-            float acc = 0.0f;
-            if (b <= a) {
-                for (int f = 0; f < D; ++f) acc = fmaf(Qs[a][f], Ks[b][f], acc);
-                acc *= pw[a - b];
+        oc *= sm.pw[l32 + 1];                   // lambda^(a+1) for token a = l32
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sm.P[buf][wave][kk(r, h)][l32] = sc[r];
+
+        // the state tile: S = lambda^c S + K_t^T (lambda^(c-1-b) V), A = K^T[i][b], B = VW[b][j]
+        S *= sm.pw[c];
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            const int b = kk(m, h);
+            const float kt = sm.K[buf][b][32 * wave + l32];
+            const float vw = sm.V[buf][b][l32] * sm.pw[max(c - 1 - b, 0)];   // (rows b >= c are 0)
+            S = mfma(kt, vw, S);
+        }
+
+        if (more) stage(buf ^ 1);
+        __syncthreads();                        // partial scores visible
+
+        // this wave's token rows b of P^T (summed, masked, decayed) times V^T:
+        // A = V^T[j][b] (lane j), B = P^T[b][a] (lane a)
+#pragma unroll
+        for (int m = 0; m < BQ / 2; ++m) {
+            const int b = BQ * wave + (BQ / 2) * h + m;
+            float p = 0.0f;
+#pragma unroll
+            for (int t = 0; t < NT; ++t) p += sm.P[buf][t][b][l32];
+            p = b <= l32 ? p * sm.pw[l32 - b] : 0.0f;
+            oc = mfma(sm.V[buf][b][l32], p, oc);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sm.O[buf][wave][kk(r, h)][l32] = oc[r];
+        __syncthreads();                        // partial outputs visible
+
+        // the outputs of this wave's tokens: 8 lanes per token row, 16 bytes each
+#pragma unroll
+        for (int pass = 0; pass < BQ / 8; ++pass) {
+            const int a = BQ * wave + 8 * pass + lane / 8, j = 4 * (lane % 8);
+            float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                o.x += sm.O[buf][t][j][a];
+                o.y += sm.O[buf][t][j + 1][a];
+                o.z += sm.O[buf][t][j + 2][a];
+                o.w += sm.O[buf][t][j + 3][a];
             }
-            Ps[a][b] = acc;
-        }
-        __syncthreads();
-        // outputs: intra-block scores times V, plus the carried state's term
-        for (int e = tid; e < FC * FJ; e += FT) {
-            const int a = e / FJ, j = e % FJ;
-            if (a < c) {
-                float inter = 0.0f, intra = 0.0f;
-                for (int i = 0; i < D; ++i) inter = fmaf(Qs[a][i], Ss[i][j], inter);
-                for (int b = 0; b <= a; ++b) intra = fmaf(Ps[a][b], Vs[b][j], intra);
-                ob[(t0 + a) * ots + j0 + j] = fmaf(pw[a + 1], inter, intra);
-            }
-        }
-        __syncthreads();
-        // decayed state scan: S = lambda^c S + sum_b lambda^(c-1-b) k_b^T v_b
-        const float dc = pw[c];
-        for (int e = tid; e < D * FJ; e += FT) {
-            const int i = e / FJ, j = e % FJ;
-            float acc = 0.0f;
-            for (int b = 0; b < c; ++b) acc = fmaf(pw[c - 1 - b] * Ks[b][i], Vs[b][j], acc);
-            Ss[i][j] = fmaf(dc, Ss[i][j], acc);
+            if (a < c) *reinterpret_cast<float4 *>(ob + (t0 + a) * ots + j0 + j) = o;
         }
     }
-    __syncthreads();
-    for (int e = tid; e < D * FJ; e += FT) St[(e / FJ) * D + j0 + e % FJ] = Ss[e / FJ][e % FJ];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) St[(32 * wave + kk(r, h)) * D + j0 + l32] = S[r];
 }
 
 }  // namespace
@@ -109,7 +223,7 @@ hipError_t launch_prefill_f32(const float *q, const float *k, const float *v,
                               const float *slopes, float *out, float *state,
                               int64_t seqs, const SeqMap &map, int d, hipStream_t stream)
 {
-    const dim3 grid((unsigned)prefill_f32_grid(seqs, map.H, d)), block(FT);
+    const dim3 grid((unsigned)prefill_f32_grid(seqs, map.H, d)), block(64 * (d / 32));
     SeqMap m = map;
     void *args[] = {(void *)&q, (void *)&k, (void *)&v, (void *)&slopes,
                     (void *)&out, (void *)&state, (void *)&m};

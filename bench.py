@@ -76,6 +76,7 @@ sys.path.insert(0, ROOT)
 METRIC = "Lightning-attn prefill TFLOP/s (H=64,d=128,N=32K-256K); decode state GB/s"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+FP32_MFMA_PEAK_TFLOPS = 157.3    # MI355X dense fp32 MFMA
 C_COUNT = 64                     # block length the flop count is fixed at
 
 PREFILL = dict(B=1, H=64, N=262144, d=128, seed=1003)
@@ -617,6 +618,24 @@ def measure_sizes(dev, stream, reps):
         "gbs": round(by / (ms * 1e-3) / 1e9, 1),
         "frac_of_hbm_peak": round(by / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     del x, out
+    # the fp32 path (fp32 q, k, v, out and state; fp32 matrix cores) at the 32K
+    # continuation shape: bound by the fp32 MFMA rate, not by memory
+    B, H, N, d = 1, 64, 32768, 128
+    with torch.cuda.stream(stream):
+        x = inputs.make_prefill(B, H, N, d, torch.float32, 1012, True, dev)
+        st = x.state.clone()
+        out = torch.empty_like(x.q)
+        ms = time_launches(stream, lambda: binding.prefill(x.q, x.k, x.v, x.slopes, st, out=out),
+                           max(reps, 5))
+    fl = prefill_flops(B, H, N, d)
+    by = B * H * N * d * 4 * 4 + 2 * B * H * d * d * 4
+    res["prefill_32k_fp32"] = {
+        "config": f"B{B} H{H} N{N} d{d} fp32, random fp32 initial state",
+        "kernel": "prefill_f32_kernel<128> (v_mfma_f32_32x32x2_f32)",
+        "ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 3),
+        "frac_of_fp32_mfma_peak": round(fl / (ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
+        "gbs": round(by / (ms * 1e-3) / 1e9, 1)}
+    del x, st, out
     return res
 
 

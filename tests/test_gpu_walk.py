@@ -2,9 +2,9 @@
 32 output columns) runs every sequence of the batch in order, handing each
 sequence's final state out and the next one's initial state in at the
 boundaries.  On a 256-CU MI355X it is taken for short sequences at H = 64
-(d = 128) and H = 128 (d = 64), whose workgroups fill the device, and at
-H = 32 (the flash models' head count, half the device) for sequences of
-about two blocks or less.
+(d = 128) and H = 128 (d = 64), whose workgroups fill the device; with fewer
+heads the sequences are cut into groups (by tokens) walked side by side so
+that the workgroups still fill it (32 heads: 2 groups, 16: 4, 8: 8, 3: 21).
 Checked against the fp64 packed oracle (bf16 bar 2e-2) and bitwise against
 launches over each sequence alone (which never walk), with empty, one-token,
 one-block and back-to-back one-block sequences, and through the strided call."""
@@ -119,6 +119,30 @@ def test_walk_strided_bitwise_equals_contiguous(d, H):
     binding.prefill_varlen(qv, kv, vv, x.slopes, x.cu_seqlens, st, out=ob.transpose(0, 1))
     torch.cuda.synchronize()
     assert torch.equal(ob.transpose(0, 1), out_ref) and torch.equal(st, st_ref)
+
+
+@pytest.mark.parametrize("H,d", [(3, 128), (5, 64), (12, 128), (24, 128), (48, 64)])
+def test_walk_groups_at_odd_head_counts(H, d):
+    # group counts 21, 25, 5, 2, 2 on 256 compute units; head slots that are
+    # not a multiple of 8 take the plain workgroup placement
+    rng = np.random.default_rng(666 + H)
+    lens = [int(n) for n in rng.integers(0, 150, size=90)] + [700, 0, 3]
+    need_walk(len(lens), H, sum(lens), d)
+    log(f"walk groups: H{H} d{d}, {len(lens)} sequences of 0..700 tokens")
+    x = inputs.make_varlen(H, lens, d, torch.bfloat16, seed=667 + H, init_state=True, device=DEV)
+    st = x.states.clone()
+    out = binding.prefill_varlen(x.q, x.k, x.v, x.slopes, x.cu_seqlens, st)
+    torch.cuda.synchronize()
+    o1, s1 = per_sequence(x, lens)
+    bad = [i for i in range(len(lens)) if not torch.equal(st[i], s1[i])]
+    assert not bad, f"states differ for sequences {bad[:8]}"
+    assert torch.equal(out, o1), "outputs differ from per-sequence launches"
+    o_ref, s_ref = oracle.prefill_varlen(np64(x.q), np64(x.k), np64(x.v), np64(x.slopes),
+                                         x.cu_seqlens.cpu().numpy(), np64(x.states))
+    eo = oracle.rel_l2(np64(out), o_ref)
+    es = max(oracle.rel_l2(np64(st)[i], s_ref[i]) for i in range(len(lens)))
+    log(f"  out rel-L2 {eo:.3e}  state rel-L2 {es:.3e}")
+    assert eo <= BF16_TOL and es <= BF16_TOL
 
 
 def test_packed_256k_workload_equals_per_sequence_launches():

@@ -162,8 +162,13 @@ __global__ __launch_bounds__(64 * (D / 32)) void prefill_f32_kernel(
         const int buf = (int)(n & 1);
         const int64_t t0 = n * FC;
         const int c = (int)min((int64_t)FC, N - t0);
-        const bool more = n + 1 < nblk;
-        if (more) load(t0 + FC, (int)min((int64_t)FC, N - t0 - FC));
+        // the next block into registers (after the last block: no rows, no
+        // accesses).  Unconditional, as is the staging below: with both under
+        // a condition the compiler takes the loads as possibly still in flight
+        // at the top of the next block and waits there, and since loads and
+        // stores share one counter that wait also took the previous block's
+        // output stores (3.36 -> 3.06 ms at 64 heads, 32K tokens)
+        load(t0 + FC, (int)min((int64_t)FC, N - t0 - FC));
 
         // partial scores S^T[b][a] and inter term over features 32 wave .. +31:
         // A = K[b][k] (lane b) and S^T[j][k] (the state registers), B = Q^T[k][a] (lane a)
@@ -184,17 +189,23 @@ __global__ __launch_bounds__(64 * (D / 32)) void prefill_f32_kernel(
         oc *= lam_a1;                           // lambda^(a+1) for token a = l32
 #pragma unroll
         for (int r = 0; r < 16; ++r) sm.P[wave][kk(r, h)][l32] = sc[r];
-        const bool full = c == FC;
-        S *= full ? lam_c : sm.pw[c];
+        if (c == FC) {
+            S *= lam_c;
 #pragma unroll
-        for (int m = 0; m < 16; ++m) {
-            const int b = kk(m, h);
-            const float kt = sm.K[buf][b][32 * wave + l32];
-            const float w = full ? vws[m] : sm.pw[max(c - 1 - b, 0)];    // (rows b >= c are 0)
-            S = mfma(kt, sm.V[buf][b][l32] * w, S);
+            for (int m = 0; m < 16; ++m) {
+                const int b = kk(m, h);
+                S = mfma(sm.K[buf][b][32 * wave + l32], sm.V[buf][b][l32] * vws[m], S);
+            }
+        } else {                                // the last, partial block (rows b >= c are 0)
+            S *= sm.pw[c];
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                const int b = kk(m, h);
+                S = mfma(sm.K[buf][b][32 * wave + l32], sm.V[buf][b][l32] * sm.pw[max(c - 1 - b, 0)], S);
+            }
         }
 
-        if (more) stage(buf ^ 1);
+        stage(buf ^ 1);                         // (after the last block: unused zeros)
         __syncthreads();                        // partial scores visible
 
         // this wave's token rows b of P^T (summed, masked, decayed) times V^T:

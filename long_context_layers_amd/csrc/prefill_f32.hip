@@ -189,20 +189,23 @@ __global__ __launch_bounds__(64 * (D / 32)) void prefill_f32_kernel(
         oc *= lam_a1;                           // lambda^(a+1) for token a = l32
 #pragma unroll
         for (int r = 0; r < 16; ++r) sm.P[wave][kk(r, h)][l32] = sc[r];
+        // (all operands read before the chain: its 16 MFMAs depend on each
+        // other, so a read per step would put the LDS latency between them)
+        float kt[16], vw[16];
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+            const int b = kk(m, h);
+            kt[m] = sm.K[buf][b][32 * wave + l32];
+            vw[m] = sm.V[buf][b][l32];
+        }
         if (c == FC) {
             S *= lam_c;
 #pragma unroll
-            for (int m = 0; m < 16; ++m) {
-                const int b = kk(m, h);
-                S = mfma(sm.K[buf][b][32 * wave + l32], sm.V[buf][b][l32] * vws[m], S);
-            }
+            for (int m = 0; m < 16; ++m) S = mfma(kt[m], vw[m] * vws[m], S);
         } else {                                // the last, partial block (rows b >= c are 0)
             S *= sm.pw[c];
 #pragma unroll
-            for (int m = 0; m < 16; ++m) {
-                const int b = kk(m, h);
-                S = mfma(sm.K[buf][b][32 * wave + l32], sm.V[buf][b][l32] * sm.pw[max(c - 1 - b, 0)], S);
-            }
+            for (int m = 0; m < 16; ++m) S = mfma(kt[m], vw[m] * sm.pw[max(c - 1 - kk(m, h), 0)], S);
         }
 
         stage(buf ^ 1);                         // (after the last block: unused zeros)

@@ -143,9 +143,26 @@ def test_ragged_lengths_and_decay_extremes(dtype, tol, d, N):
 def test_long_sequence_with_slow_decay(dtype, tol, N):
     # decays close to 1 (lambda = 0.9999 .. 0.999) let the state accumulate over
     # the whole sequence, so the inter term (the state's bf16 copy in the bf16
-    # kernel, fp32 FMAs in the fp32 one) dominates the outputs
+    # kernel, the fp32 state registers on the fp32 matrix cores in the fp32
+    # one) dominates the outputs
     inp = small_inputs(1, 2, N, 128, dtype, seed=N + 17, slopes=[1e-4, 1e-3])
     check_prefill(inp, tol, what=f"{dtype} N{N} slow decay")
+
+
+def test_fp32_at_the_benchmarked_shape():
+    # the fp32 path at the shape its benchmark line times (64 heads, 32K tokens
+    # and a ragged tail, 128 channels, a random fp32 initial state): all 256
+    # workgroups, every head against the oracle at the fp32 bar
+    x = inputs.make_prefill(1, 64, 32768 + 21, 128, torch.float32, seed=1012, init_state=True,
+                            device=DEV)
+    log("fp32 prefill B1 H64 N32789 d128, random initial state")
+    st = x.state.clone()
+    out = binding.prefill(x.q, x.k, x.v, x.slopes, st)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_prefill(x.q, x.k, x.v, x.slopes, x.state)
+    eo, es = rel_l2(out, o_ref), rel_l2(st, s_ref)
+    log(f"  out rel-L2 {eo:.3e}  state rel-L2 {es:.3e}")
+    assert eo <= F32_TOL and es <= F32_TOL
 
 
 @pytest.mark.parametrize("H", [1, 2, 5, 8])

@@ -25,10 +25,12 @@
 // of P^T into its partial output, and the partial outputs are summed through
 // LDS (token-major, 16-byte accesses) and stored, 128 bytes per token row.
 // The next block's q, k and v are loaded into registers while a block is
-// computed; the q, k, v tiles are double-buffered, the partials single (each
-// is read between the barriers that follow its writes and written again only
-// after every reader has passed the next block's first barrier); the decay
-// factors of a full block are kept in registers.  (Two waves per state tile,
+// computed; v is double-buffered, q and k single (read only before a block's
+// first barrier, the next block's are staged right after it), the partials
+// single too (each is read between the barriers that follow its writes and
+// written again only after every reader has passed the next block's first
+// barrier); the decay factors of a full block are kept in registers.  (Two
+// waves per state tile,
 // one for the scores and one for the state, measured slower at 64 heads:
 // 3.96 against 3.36 ms at 32K tokens.)
 #include "la_internal.h"
@@ -44,8 +46,8 @@ constexpr int RP = 4;       // row padding of the LDS tiles (floats)
 
 template <int D>
 struct alignas(16) F32Smem {
-    float Q[2][FC][D + RP];
-    float K[2][FC][D + RP];
+    float Q[FC][D + RP];                 // (single: read only before a block's first barrier)
+    float K[FC][D + RP];
     float V[2][FC][FJ + RP];
     float P[D / 32][FC][FC + RP];        // partial scores of each feature tile, [b][a]
     float O[D / 32][FC][FJ + RP];        // partial outputs of each wave, [a][j]
@@ -61,8 +63,11 @@ __device__ __forceinline__ f32x16 mfma(float a, float b, f32x16 c)
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+// (d = 128: registers for two workgroups per CU, which the 80 KB of LDS allow:
+// on grids of more than one workgroup per CU, 2.95 -> 2.25 ms for 2 x 16K
+// tokens at 64 heads)
 template <int D>
-__global__ __launch_bounds__(64 * (D / 32)) void prefill_f32_kernel(
+__global__ __launch_bounds__(64 * (D / 32), D == 128 ? 2 : 1) void prefill_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ k, const float *__restrict__ v,
     const float *__restrict__ slopes, float *__restrict__ out, float *__restrict__ state,
     SeqMap map)
@@ -126,13 +131,15 @@ __global__ __launch_bounds__(64 * (D / 32)) void prefill_f32_kernel(
             if (row < c) pv[u] = *reinterpret_cast<const float4 *>(vb + (t0 + row) * ts + j0 + 4 * c4);
         }
     };
-    auto stage = [&](int buf) {
+    auto stage_qk = [&]() {
 #pragma unroll
         for (int u = 0; u < NQ; ++u) {
             const int e = tid + NTH * u, row = e / (D / 4), c4 = e % (D / 4);
-            *reinterpret_cast<float4 *>(&sm.Q[buf][row][4 * c4]) = pq[u];
-            *reinterpret_cast<float4 *>(&sm.K[buf][row][4 * c4]) = pk[u];
+            *reinterpret_cast<float4 *>(&sm.Q[row][4 * c4]) = pq[u];
+            *reinterpret_cast<float4 *>(&sm.K[row][4 * c4]) = pk[u];
         }
+    };
+    auto stage_v = [&](int buf) {
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
             const int e = tid + NTH * u, row = e / (FJ / 4), c4 = e % (FJ / 4);
@@ -143,7 +150,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void prefill_f32_kernel(
     const int64_t nblk = (N + FC - 1) / FC;
     if (nblk > 0) {
         load(0, (int)min((int64_t)FC, N));
-        stage(0);
+        stage_qk();
+        stage_v(0);
     }
     __syncthreads();                            // block 0 and the powers visible
     // per-lane decay factors of a full block: lambda^(a+1) of token a = l32, the
@@ -175,8 +183,8 @@ __global__ __launch_bounds__(64 * (D / 32)) void prefill_f32_kernel(
         float qa[16], ka[16];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const float4 x = *reinterpret_cast<const float4 *>(&sm.Q[buf][l32][32 * wave + 8 * g + 4 * h]);
-            const float4 y = *reinterpret_cast<const float4 *>(&sm.K[buf][l32][32 * wave + 8 * g + 4 * h]);
+            const float4 x = *reinterpret_cast<const float4 *>(&sm.Q[l32][32 * wave + 8 * g + 4 * h]);
+            const float4 y = *reinterpret_cast<const float4 *>(&sm.K[l32][32 * wave + 8 * g + 4 * h]);
             qa[4 * g] = x.x; qa[4 * g + 1] = x.y; qa[4 * g + 2] = x.z; qa[4 * g + 3] = x.w;
             ka[4 * g] = y.x; ka[4 * g + 1] = y.y; ka[4 * g + 2] = y.z; ka[4 * g + 3] = y.w;
         }
@@ -195,7 +203,7 @@ __global__ __launch_bounds__(64 * (D / 32)) void prefill_f32_kernel(
 #pragma unroll
         for (int m = 0; m < 16; ++m) {
             const int b = kk(m, h);
-            kt[m] = sm.K[buf][b][32 * wave + l32];
+            kt[m] = sm.K[b][32 * wave + l32];
             vw[m] = sm.V[buf][b][l32];
         }
         if (c == FC) {
@@ -208,8 +216,9 @@ __global__ __launch_bounds__(64 * (D / 32)) void prefill_f32_kernel(
             for (int m = 0; m < 16; ++m) S = mfma(kt[m], vw[m] * sm.pw[max(c - 1 - kk(m, h), 0)], S);
         }
 
-        stage(buf ^ 1);                         // (after the last block: unused zeros)
-        __syncthreads();                        // partial scores visible
+        stage_v(buf ^ 1);                       // (after the last block: unused zeros)
+        __syncthreads();                        // partial scores visible; q, k of this block read
+        stage_qk();                             // the next block's q, k (visible after the next barrier)
 
         // this wave's token rows b of P^T (summed, masked, decayed) times V^T:
         // A = V^T[j][b] (lane j), B = P^T[b][a] (lane a)

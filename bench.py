@@ -627,14 +627,19 @@ def measure_sizes(dev, stream, reps):
         out = torch.empty_like(x.q)
         ms = time_launches(stream, lambda: binding.prefill(x.q, x.k, x.v, x.slopes, st, out=out),
                            max(reps, 5))
+        ms1 = time_launches(stream, lambda: binding.prefill(x.q, x.k, x.v, x.slopes, st, out=out,
+                                                            split=False), max(reps, 5))
+        nseg = binding.prefill_f32_workspace_bytes(B, H, N, d, dev) // (H * d * d * 4)
     fl = prefill_flops(B, H, N, d)
     by = B * H * N * d * 4 * 4 + 2 * B * H * d * d * 4
     res["prefill_32k_fp32"] = {
         "config": f"B{B} H{H} N{N} d{d} fp32, random fp32 initial state",
-        "kernel": "prefill_f32_kernel<128> (v_mfma_f32_32x32x2_f32)",
+        "kernel": "prefill_f32_kernel<128> (v_mfma_f32_32x32x2_f32)"
+                  + (f", {nseg} segments per head (la_prefill_f32_ws)" if nseg > 1 else ""),
         "ms": round(ms, 4), "tflops": round(fl / (ms * 1e-3) / 1e12, 3),
         "frac_of_fp32_mfma_peak": round(fl / (ms * 1e-3) / 1e12 / FP32_MFMA_PEAK_TFLOPS, 4),
-        "gbs": round(by / (ms * 1e-3) / 1e9, 1)}
+        "gbs": round(by / (ms * 1e-3) / 1e9, 1),
+        "unsplit_ms": round(ms1, 4)}
     del x, st, out
     return res
 

@@ -138,6 +138,35 @@ int la_prefill_f32(const float *q, const float *k, const float *v, const float *
                    int64_t B, int64_t H, int64_t N, int64_t d, void *stream);
 
 /*
+ * la_prefill_f32 with a caller's workspace: when B = 1 and the call's grid
+ * (H * d/32 workgroups) would not fill the device twice over, each head's
+ * sequence runs as S segments at once (each at least 8192 tokens, at most 64;
+ * none below 2), the first from the caller's state and the others from zero,
+ * then the segments' states are chained and each later segment's outputs are
+ * corrected with the state at its start (o_a += lambda^(a+1) q_a S for its
+ * local token index a, fp32 throughout) - the decomposition of la_prefill_ws
+ * (the report's §4.1.1 and Fig. 10, local output and local state per piece
+ * joined through the carried state) for fp32 q, k, v, out.  Same semantics and
+ * argument rules as la_prefill_f32; results equal la_prefill_f32's within fp32
+ * rounding.  Tokens whose factor lambda^(a+1) is exactly 0 in fp32 get no
+ * correction work.
+ *   la_prefill_f32_workspace_bytes: the workspace bytes la_prefill_f32_ws
+ *     needs for these sizes on the calling thread's current device, written
+ *     to *bytes; 0 means no split (la_prefill_f32_ws then runs exactly as
+ *     la_prefill_f32 and ignores the workspace).  LA_ERR_INVALID_ARG for a
+ *     null bytes, B or H below 1 or N below 0; LA_ERR_UNSUPPORTED for d other
+ *     than 64 or 128.  Enqueues nothing.
+ *   la_prefill_f32_ws: workspace rules as la_prefill_ws (device memory of at
+ *     least that many bytes, 256-byte aligned, owned by the caller, not
+ *     overlapping any argument, contents unspecified on entry and exit; calls
+ *     sharing a workspace ordered on one stream).
+ */
+int la_prefill_f32_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t *bytes);
+int la_prefill_f32_ws(const float *q, const float *k, const float *v, const float *slopes,
+                      float *out, float *state, int64_t B, int64_t H, int64_t N, int64_t d,
+                      void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
  * Packed variable-length prefill: nseq independent sequences of different
  * lengths in one launch, each with its own state (the state is reset between
  * sequences, unlike a dense run over the concatenated tokens).
@@ -473,7 +502,7 @@ const char *la_status_string(int status);
 /* ABI version of this header (incremented on incompatible changes). */
 int la_abi_version(void);
 
-#define LA_ABI_VERSION 7
+#define LA_ABI_VERSION 8
 
 #ifdef __cplusplus
 }

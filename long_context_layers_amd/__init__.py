@@ -7,8 +7,9 @@ The layer's kernels live in the HIP library ``lib/liblightning_attn.so``
 """
 from .binding import (prefill, prefill_varlen, prefill_varlen_walks, decode_step, decode_multi,  # noqa: F401
                       qk_norm_rope, prefill_qk_norm_rope, group_norm_gate, cp_fold, cp_correct,
-                      prefill_workspace_bytes, load_library, status_string, LightningAttnError)
+                      prefill_workspace_bytes, prefill_f32_workspace_bytes, load_library, status_string,
+                      LightningAttnError)
 
 __all__ = ["prefill", "prefill_varlen", "prefill_varlen_walks", "decode_step", "decode_multi", "qk_norm_rope",
-           "prefill_qk_norm_rope", "group_norm_gate", "cp_fold", "cp_correct", "prefill_workspace_bytes",
+           "prefill_qk_norm_rope", "group_norm_gate", "cp_fold", "cp_correct", "prefill_workspace_bytes", "prefill_f32_workspace_bytes",
            "load_library", "status_string", "LightningAttnError"]

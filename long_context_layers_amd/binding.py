@@ -27,6 +27,8 @@ SIGNATURES = {
     "la_prefill_f32": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], _INT),
     "la_prefill_workspace_bytes": ([_I64, _I64, _I64, _I64, ctypes.POINTER(_I64)], _INT),
     "la_prefill_ws": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _I64, _P], _INT),
+    "la_prefill_f32_workspace_bytes": ([_I64, _I64, _I64, _I64, ctypes.POINTER(_I64)], _INT),
+    "la_prefill_f32_ws": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P, _I64, _P], _INT),
     "la_prefill_noalloc": ([_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _P], _INT),
     "la_prefill_varlen": ([_P, _P, _P, _P, _P, _I64, _P, _P, _I64, _I64, _I64, _P], _INT),
     "la_prefill_varlen_f32": ([_P, _P, _P, _P, _P, _I64, _P, _P, _I64, _I64, _I64, _P], _INT),
@@ -58,7 +60,7 @@ SIGNATURES = {
     "la_prefill_varlen_plan": ([_I64, _I64, _I64, _I64, ctypes.POINTER(ctypes.c_int)], _INT),
     "la_abi_version": ([], _INT),
 }
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 _lock = threading.Lock()
 _lib = None
@@ -154,8 +156,9 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: torch.Ten
     with a unit channel stride, e.g. head-split slices of a token-major
     projection buffer; such calls go to ``la_prefill_strided``.  bf16 calls
     go to ``la_prefill_ws`` / ``la_prefill_strided_ws`` (the sequence split,
-    with a workspace from torch's allocator) when a split is planned, unless
-    ``split`` is False (then ``la_prefill`` / ``la_prefill_strided``).
+    with a workspace from torch's allocator) when a split is planned, fp32
+    calls to ``la_prefill_f32_ws``, unless ``split`` is False (then
+    ``la_prefill`` / ``la_prefill_strided`` / ``la_prefill_f32``).
     """
     if not isinstance(q, torch.Tensor) or q.dim() != 4:
         raise ValueError("q must be a [B,H,N,d] tensor")
@@ -205,6 +208,16 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: torch.Ten
                                        out.data_ptr(), state.data_ptr(), B, H, N, d,
                                        work.data_ptr(), ws, _stream(dev))
             _check(rc, "la_prefill_ws")
+            return out
+    if dt == torch.float32 and split:
+        ws = prefill_f32_workspace_bytes(B, H, N, d, dev)
+        if ws > 0:
+            work = torch.empty(ws, dtype=torch.uint8, device=dev)
+            with torch.cuda.device(dev):
+                rc = lib.la_prefill_f32_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), slopes.data_ptr(),
+                                           out.data_ptr(), state.data_ptr(), B, H, N, d,
+                                           work.data_ptr(), ws, _stream(dev))
+            _check(rc, "la_prefill_f32_ws")
             return out
     fn = lib.la_prefill if dt == torch.bfloat16 else lib.la_prefill_f32
     with torch.cuda.device(dev):
@@ -267,6 +280,16 @@ def prefill_workspace_bytes(B: int, H: int, N: int, d: int, device=None) -> int:
     with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
         rc = load_library().la_prefill_workspace_bytes(B, H, N, d, ctypes.byref(n))
     _check(rc, "la_prefill_workspace_bytes")
+    return int(n.value)
+
+
+def prefill_f32_workspace_bytes(B: int, H: int, N: int, d: int, device=None) -> int:
+    """Workspace bytes la_prefill_f32_ws needs for a dense fp32 prefill of
+    these sizes on `device` (0: no sequence split, la_prefill_f32 is used)."""
+    n = ctypes.c_int64(0)
+    with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+        rc = load_library().la_prefill_f32_workspace_bytes(B, H, N, d, ctypes.byref(n))
+    _check(rc, "la_prefill_f32_workspace_bytes")
     return int(n.value)
 
 

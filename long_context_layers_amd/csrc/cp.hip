@@ -343,50 +343,208 @@ int64_t split_workspace_bytes(int64_t H, int nseg, int d)
     return nseg < 2 ? 0 : (int64_t)nseg * H * d * d * 4 + ((nseg + 1) * 8 + 255) / 256 * 256;
 }
 
+// the segment length of a split into nseg (segments start on 64-token blocks)
+static int64_t split_segment(int64_t N, int nseg)
+{
+    const int64_t seg = (N + nseg - 1) / nseg;
+    return (seg + 63) / 64 * 64;
+}
+
+// workspace: nseg state slots [nseg][H][d][d] fp32, then nseg + 1 offsets;
+// slot 0 <- the caller's state, the others <- 0, the offsets <- the segments
+static hipError_t launch_split_prep(const float *state, float *slots, int64_t **cu, int64_t H,
+                                    int d, int nseg, int64_t seg, int64_t N, hipStream_t stream)
+{
+    *cu = reinterpret_cast<int64_t *>(slots + (int64_t)nseg * H * d * d);
+    const int64_t n4 = H * ((int64_t)d * d / 4);
+    const int64_t blocks = (n4 * nseg + FT - 1) / FT;
+    const dim3 grid((unsigned)(blocks < FMAX_GRID ? blocks : FMAX_GRID)), block(FT);
+    const f32x4 *in4 = reinterpret_cast<const f32x4 *>(state);
+    f32x4 *s4 = reinterpret_cast<f32x4 *>(slots);
+    int64_t *c = *cu;
+    int64_t nn = n4, sg = seg, nt = N;
+    int ns = nseg;
+    void *args[] = {(void *)&in4, (void *)&s4, (void *)&c, (void *)&nn, (void *)&ns,
+                    (void *)&sg, (void *)&nt};
+    return hipLaunchKernel((const void *)split_prep_kernel, grid, block, args, 0, stream);
+}
+
+// the slots chained into the state at each segment's end, the last into the caller's state
+static hipError_t launch_split_fold(float *slots, float *state, const float *slopes, int64_t H,
+                                    int d, int nseg, int64_t seg, int64_t N, hipStream_t stream)
+{
+    const int64_t slice4 = (int64_t)d * d / 4, n4 = H * slice4;
+    const int64_t blocks = (n4 + FT - 1) / FT;
+    const dim3 grid((unsigned)(blocks < FMAX_GRID ? blocks : FMAX_GRID)), block(FT);
+    f32x4 *s4 = reinterpret_cast<f32x4 *>(slots);
+    f32x4 *st4 = reinterpret_cast<f32x4 *>(state);
+    int64_t nn = n4, sl = slice4, hh = H, sg = seg, nt = N;
+    int ns = nseg;
+    void *args[] = {(void *)&s4, (void *)&st4, (void *)&slopes, (void *)&nn, (void *)&sl,
+                    (void *)&hh, (void *)&ns, (void *)&sg, (void *)&nt};
+    return hipLaunchKernel((const void *)split_fold_kernel, grid, block, args, 0, stream);
+}
+
 hipError_t launch_prefill_bf16_split(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                      const float *slopes, uint16_t *out, float *state,
                                      int64_t H, int64_t N, int d, int nseg, int njt,
                                      const Strides &in, const Strides &ost, void *workspace,
                                      hipStream_t stream, const QkPrologue *pro)
 {
-    // workspace: nseg state slots [nseg][H][d][d] fp32, then nseg + 1 offsets
     float *slots = static_cast<float *>(workspace);
-    int64_t *cu = reinterpret_cast<int64_t *>(slots + (int64_t)nseg * H * d * d);
-    int64_t seg = (N + nseg - 1) / nseg;
-    seg = (seg + 63) / 64 * 64;                          // segments start on 64-token blocks
-    const int64_t slice4 = (int64_t)d * d / 4, n4 = H * slice4;
-    f32x4 *s4 = reinterpret_cast<f32x4 *>(slots);
-    f32x4 *st4 = reinterpret_cast<f32x4 *>(state);
-    const dim3 block(FT);
-    {
-        const int64_t blocks = (n4 * nseg + FT - 1) / FT;
-        const dim3 grid((unsigned)(blocks < FMAX_GRID ? blocks : FMAX_GRID));
-        const f32x4 *in4 = st4;
-        int64_t nn = n4, sg = seg, nt = N;
-        int ns = nseg;
-        void *args[] = {(void *)&in4, (void *)&s4, (void *)&cu, (void *)&nn, (void *)&ns,
-                        (void *)&sg, (void *)&nt};
-        const hipError_t e = hipLaunchKernel((const void *)split_prep_kernel, grid, block, args, 0,
-                                             stream);
-        if (e != hipSuccess) return e;
-    }
-    const SeqMap map = {cu, H, 0, N, {0, in.sh, in.st}, {0, ost.sh, ost.st}};
-    hipError_t e = launch_prefill_bf16_nowalk(q, k, v, slopes, out, slots, nseg, map, d, stream, njt,
-                                              pro);
+    const int64_t seg = split_segment(N, nseg);
+    int64_t *cu = nullptr;
+    hipError_t e = launch_split_prep(state, slots, &cu, H, d, nseg, seg, N, stream);
     if (e != hipSuccess) return e;
-    {
-        const int64_t blocks = (n4 + FT - 1) / FT;
-        const dim3 grid((unsigned)(blocks < FMAX_GRID ? blocks : FMAX_GRID));
-        int64_t nn = n4, sl = slice4, hh = H, sg = seg, nt = N;
-        int ns = nseg;
-        void *args[] = {(void *)&s4, (void *)&st4, (void *)&slopes, (void *)&nn, (void *)&sl,
-                        (void *)&hh, (void *)&ns, (void *)&sg, (void *)&nt};
-        e = hipLaunchKernel((const void *)split_fold_kernel, grid, block, args, 0, stream);
-        if (e != hipSuccess) return e;
-    }
+    const SeqMap map = {cu, H, 0, N, {0, in.sh, in.st}, {0, ost.sh, ost.st}};
+    e = launch_prefill_bf16_nowalk(q, k, v, slopes, out, slots, nseg, map, d, stream, njt, pro);
+    if (e != hipSuccess) return e;
+    e = launch_split_fold(slots, state, slopes, H, d, nseg, seg, N, stream);
+    if (e != hipSuccess) return e;
     // segment g >= 1 is corrected with slot g - 1 (the state at its start)
     return launch_correct(q, slopes, slots, out, H, H, in.sh, in.st, ost.sh, ost.st, seg, seg, N,
                           nseg - 1, d, stream, pro);
+}
+
+// ---- the same split for fp32 q, k, v, out (B = 1, dense [1,H,N,d]): the
+// segments on the fp32 prefill kernel, the fold as above, and the correction
+// in fp32 on the fp32 matrix cores.
+
+namespace {
+
+constexpr int FCT = 32;            // fp32 correction: tokens per tile
+constexpr int FCTOK = 128;         // fp32 correction: tokens per chunk (4 tiles)
+constexpr int FCWG = 128;          // fp32 correction: workgroups per (segment, head, slice) at most
+
+template <int D>
+struct alignas(16) CorrF32Smem {
+    float Q[FCT][D + 4];
+    float O[D / 32][FCT][32 + 4];  // partial outputs per wave, [a][j]
+};
+
+__device__ __forceinline__ int kk32(int m, int h) { return 8 * (m >> 2) + 4 * h + (m & 3); }
+
+// out_a += lambda^(a+1) q_a S for token a of a later segment (S its starting
+// state), fp32 operands and accumulation (v_mfma_f32_32x32x2_f32): one
+// workgroup per (segment, head, 32 output columns, chunk walker), one wave per
+// 32-row tile t of S, holding S[32t.., j] in the accumulator layout (lane =
+// column j, register r = row 8 (r/4) + 4h + r%4), which is the A operand of
+// S_t^T Q_t^T as it stands; the D/32 partial outputs are summed through LDS and
+// added to out.  The walker takes the FCTOK-token chunks c, c + cstride, ...
+// and stops at the first 32-token tile whose first factor lambda^(a+1) is 0 in
+// fp32 (the factor only falls, so nothing after it changes).
+template <int D>
+__global__ __launch_bounds__(64 * (D / 32)) void cp_correct_f32_kernel(
+    const float *__restrict__ q, const float *__restrict__ slopes, const float *__restrict__ s_in,
+    float *__restrict__ out, int64_t H, int64_t hs, int64_t ts, int64_t t_off, int64_t seg,
+    int64_t ntok, int64_t chunks, int64_t cstride)
+{
+    constexpr int NT = D / 32, NTH = 64 * NT, NJ = D / 32;
+    constexpr int NQ = FCT * D / 4 / NTH;         // float4 of a q tile per thread
+    __shared__ CorrF32Smem<D> sm;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int lane = tid % 64, l32 = lane % 32, h = lane / 32;
+    const int64_t c0 = blockIdx.x % cstride, rest = blockIdx.x / cstride;
+    const int j0 = (int)(rest % NJ) * 32;
+    const int64_t hd = (rest / NJ) % H, g = rest / NJ / H;
+    const float s = slopes[hd];
+    const int64_t a0 = t_off + g * seg;                       // the segment's first token
+    const int64_t L = max((int64_t)0, min(seg, ntok - a0));   // its tokens
+    auto tiles = [&](int64_t c) {                             // tiles of chunk c before the underflow
+        const int64_t tbeg = c * FCTOK;
+        const int n = (int)max((int64_t)0, (min(L, tbeg + FCTOK) - tbeg + FCT - 1) / FCT);
+        for (int it = 0; it < n; ++it)
+            if (decay_pow(s, (int)(tbeg + (int64_t)it * FCT + 1)) == 0.0f) return it;
+        return n;
+    };
+    if (c0 >= chunks || tiles(c0) <= 0) return;
+
+    const float *S = s_in + (g * H + hd) * D * D;
+    f32x16 sa;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sa[r] = S[(32 * wave + kk32(r, h)) * D + j0 + l32];
+    const float *qb = q + hd * hs + a0 * ts;
+    float *ob = out + hd * hs + a0 * ts;
+    for (int64_t chunk = c0; chunk < chunks; chunk += cstride) {
+        const int ntile = tiles(chunk);
+        if (ntile <= 0) break;
+        for (int it = 0; it < ntile; ++it) {
+            const int64_t t0 = chunk * FCTOK + (int64_t)it * FCT;
+            const int c = (int)min((int64_t)FCT, L - t0);
+#pragma unroll
+            for (int u = 0; u < NQ; ++u) {
+                const int e = tid + NTH * u, row = e / (D / 4), c4 = e % (D / 4);
+                float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (row < c) x = *reinterpret_cast<const float4 *>(qb + (t0 + row) * ts + 4 * c4);
+                *reinterpret_cast<float4 *>(&sm.Q[row][4 * c4]) = x;
+            }
+            __syncthreads();                    // the q tile staged
+            float qa[16];
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                const float4 x = *reinterpret_cast<const float4 *>(&sm.Q[l32][32 * wave + 8 * gq + 4 * h]);
+                qa[4 * gq] = x.x; qa[4 * gq + 1] = x.y; qa[4 * gq + 2] = x.z; qa[4 * gq + 3] = x.w;
+            }
+            f32x16 acc = {};
+#pragma unroll
+            for (int m = 0; m < 16; ++m) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(sa[m], qa[m], acc, 0, 0, 0);
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq)      // acc: column j = kk32(r, h) of token a = l32
+                *reinterpret_cast<float4 *>(&sm.O[wave][l32][8 * gq + 4 * h]) =
+                    make_float4(acc[4 * gq], acc[4 * gq + 1], acc[4 * gq + 2], acc[4 * gq + 3]);
+            __syncthreads();                    // the partial outputs visible; the q tile read
+#pragma unroll
+            for (int pass = 0; pass < FCT / (NTH / 8); ++pass) {
+                const int a = pass * (NTH / 8) + tid / 8, j = 4 * (tid % 8);
+                if (a < c) {
+                    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) {
+                        const float4 x = *reinterpret_cast<const float4 *>(&sm.O[t][a][j]);
+                        o.x += x.x; o.y += x.y; o.z += x.z; o.w += x.w;
+                    }
+                    const float f = decay_pow(s, (int)(t0 + a + 1));
+                    float4 *po = reinterpret_cast<float4 *>(ob + (t0 + a) * ts + j0 + j);
+                    float4 y = *po;
+                    y.x = fmaf(f, o.x, y.x); y.y = fmaf(f, o.y, y.y);
+                    y.z = fmaf(f, o.z, y.z); y.w = fmaf(f, o.w, y.w);
+                    *po = y;
+                }
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_f32_split(const float *q, const float *k, const float *v,
+                                    const float *slopes, float *out, float *state, int64_t H,
+                                    int64_t N, int d, int nseg, void *workspace,
+                                    hipStream_t stream)
+{
+    float *slots = static_cast<float *>(workspace);
+    const int64_t seg = split_segment(N, nseg);
+    int64_t *cu = nullptr;
+    hipError_t e = launch_split_prep(state, slots, &cu, H, d, nseg, seg, N, stream);
+    if (e != hipSuccess) return e;
+    const Strides st = {0, N * d, d};
+    const SeqMap map = {cu, H, 0, N, st, st};
+    e = launch_prefill_f32(q, k, v, slopes, out, slots, nseg, map, d, stream);
+    if (e != hipSuccess) return e;
+    e = launch_split_fold(slots, state, slopes, H, d, nseg, seg, N, stream);
+    if (e != hipSuccess) return e;
+    // segment g >= 1 is corrected with slot g - 1 (the state at its start)
+    const int64_t chunks = (seg + FCTOK - 1) / FCTOK;
+    const int64_t cstride = std::max<int64_t>(1, std::min<int64_t>(chunks, FCWG));
+    const dim3 grid((unsigned)((nseg - 1) * H * (d / 32) * cstride)), block(64 * (d / 32));
+    int64_t hh = H, hs = N * d, ts = d, toff = seg, sg = seg, nt = N, ch = chunks, cs = cstride;
+    void *args[] = {(void *)&q, (void *)&slopes, (void *)&slots, (void *)&out, (void *)&hh,
+                    (void *)&hs, (void *)&ts, (void *)&toff, (void *)&sg, (void *)&nt,
+                    (void *)&ch, (void *)&cs};
+    const void *fn = d == 64 ? (const void *)cp_correct_f32_kernel<64>
+                             : (const void *)cp_correct_f32_kernel<128>;
+    return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 
 }  // namespace la

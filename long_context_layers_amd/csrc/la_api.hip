@@ -413,6 +413,39 @@ int la_prefill_f32(const float *q, const float *k, const float *v, const float *
                                              static_cast<hipStream_t>(stream)));
 }
 
+int la_prefill_f32_workspace_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int64_t *bytes)
+{
+    if (!bytes || B < 1 || H < 1 || N < 0) return LA_ERR_INVALID_ARG;
+    if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
+    *bytes = la::split_workspace_bytes(H, la::prefill_f32_split_plan(B, H, N, (int)d), (int)d);
+    return LA_OK;
+}
+
+int la_prefill_f32_ws(const float *q, const float *k, const float *v, const float *slopes,
+                      float *out, float *state, int64_t B, int64_t H, int64_t N, int64_t d,
+                      void *workspace, int64_t workspace_bytes, void *stream)
+{
+    const int rc = check_prefill(q, k, v, slopes, out, state, B, H, N, d, 4);
+    if (rc != LA_OK) return rc;
+    const int nseg = la::prefill_f32_split_plan(B, H, N, (int)d);
+    if (nseg < 2) return la_prefill_f32(q, k, v, slopes, out, state, B, H, N, d, stream);
+    const int64_t need = la::split_workspace_bytes(H, nseg, (int)d);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return LA_ERR_INVALID_ARG;
+    const uint64_t act = (uint64_t)B * H * N * d * 4, st = (uint64_t)B * H * d * d * 4;
+    if (overlap(workspace, need, q, act) || overlap(workspace, need, k, act) ||
+        overlap(workspace, need, v, act) || overlap(workspace, need, out, act) ||
+        overlap(workspace, need, state, st) || overlap(workspace, need, slopes, H * 4))
+        return LA_ERR_INVALID_ARG;
+    // the segments' grid, and the correction's (at most 128 workgroups per later
+    // segment, head and 32 columns)
+    if (la::prefill_f32_grid(nseg, H, (int)d) > 0x7fffffff ||
+        (int64_t)(nseg - 1) * H * (d / 32) * 128 > 0x7fffffff)
+        return LA_ERR_UNSUPPORTED;
+    return hip_status(la::launch_prefill_f32_split(q, k, v, slopes, out, state, H, N, (int)d, nseg,
+                                                   workspace, static_cast<hipStream_t>(stream)));
+}
+
 int la_prefill_varlen_f32(const float *q, const float *k, const float *v, const float *slopes,
                           const int64_t *cu_seqlens, int64_t nseq, float *out, float *states,
                           int64_t H, int64_t T, int64_t d, void *stream)

@@ -147,6 +147,16 @@ bool prefill_bf16_walks(int64_t seqs, int64_t H, int64_t T, int d, bool packed);
 // head and slice) over seqs sequences on the current device
 int prefill_bf16_grid_njt(int64_t seqs, int64_t H, int d);
 int64_t prefill_f32_grid(int64_t seqs, int64_t H, int d);
+// compute units of the current device (0 if unknown)
+int device_cus();
+// segments of a dense fp32 prefill (B = 1) run at once (1: no split)
+int prefill_f32_split_plan(int64_t B, int64_t H, int64_t N, int d);
+// the fp32 split over nseg >= 2 segments of a dense [1,H,N,d] prefill;
+// workspace as for the bf16 split (split_workspace_bytes)
+hipError_t launch_prefill_f32_split(const float *q, const float *k, const float *v,
+                                    const float *slopes, float *out, float *state, int64_t H,
+                                    int64_t N, int d, int nseg, void *workspace,
+                                    hipStream_t stream);
 
 // ---- device helpers ----
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {

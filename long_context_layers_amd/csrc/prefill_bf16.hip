@@ -1185,6 +1185,9 @@ __global__ __launch_bounds__(NTHREADS) void prefill_bf16_kernel(
     }
 }
 
+
+}  // namespace
+
 // compute units of the current device (0 if unknown), looked up once per device
 int device_cus()
 {
@@ -1203,8 +1206,6 @@ int device_cus()
     if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
     return n;
 }
-
-}  // namespace
 
 int64_t prefill_bf16_grid(int64_t seqs, int64_t H, int d, int njt) {
     return seqs * H * (d / (PJ * njt));

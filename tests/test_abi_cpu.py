@@ -558,6 +558,37 @@ def test_prefill_workspace_bytes_without_a_device_is_zero(lib):
 
 @pytest.mark.parametrize("bad,code", [
     (dict(slopes=None), LA_ERR_INVALID_ARG), (dict(state=None), LA_ERR_INVALID_ARG),
+    (dict(B=0), LA_ERR_INVALID_ARG), (dict(H=0), LA_ERR_INVALID_ARG),
+    (dict(N=-5), LA_ERR_INVALID_ARG), (dict(d=96), LA_ERR_UNSUPPORTED),
+    (dict(q=FAKE + 8), LA_ERR_INVALID_ARG), (dict(out=FAKE + 8), LA_ERR_INVALID_ARG),
+])
+def test_prefill_f32_ws_rejects_bad_arguments(lib, bad, code):
+    # the fp32 workspace prefill takes la_prefill_f32's checks first (16-byte
+    # aligned fp32 tensors; N = 0: no launch)
+    assert lib.la_prefill_f32_ws(*_prefill_ws_args(**bad)) == code
+    assert lib.la_prefill_f32_ws(*_prefill_ws_args(N=0)) == LA_OK
+
+
+@pytest.mark.parametrize("B,H,N,d,null,code", [
+    (1, 64, 32768, 128, True, LA_ERR_INVALID_ARG), (0, 32, 1024, 128, False, LA_ERR_INVALID_ARG),
+    (1, 0, 1024, 128, False, LA_ERR_INVALID_ARG), (1, 32, -1, 128, False, LA_ERR_INVALID_ARG),
+    (1, 32, 1024, 96, False, LA_ERR_UNSUPPORTED),
+])
+def test_prefill_f32_workspace_bytes_rejects_bad_arguments(lib, B, H, N, d, null, code):
+    n = ctypes.c_int64(-1)
+    assert lib.la_prefill_f32_workspace_bytes(B, H, N, d, None if null else ctypes.byref(n)) == code
+
+
+@needs_no_gpu
+def test_prefill_f32_workspace_bytes_without_a_device_is_zero(lib):
+    for B, H, N in ((1, 64, 32768), (1, 1, 1 << 20), (4, 64, 4096)):
+        n = ctypes.c_int64(-1)
+        assert lib.la_prefill_f32_workspace_bytes(B, H, N, 128, ctypes.byref(n)) == LA_OK
+        assert n.value == 0
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(slopes=None), LA_ERR_INVALID_ARG), (dict(state=None), LA_ERR_INVALID_ARG),
     (dict(B=0), LA_ERR_INVALID_ARG), (dict(N=-5), LA_ERR_INVALID_ARG),
     (dict(d=96), LA_ERR_UNSUPPORTED), (dict(q=FAKE + 2), LA_ERR_INVALID_ARG),
 ])

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 from long_context_layers_amd import binding, inputs
-from tests.gpu_util import BF16_GUARD, BF16_TOL, log, oracle_prefill, rel_l2
+from tests.gpu_util import BF16_GUARD, BF16_TOL, F32_TOL, log, oracle_prefill, rel_l2
 from tests.test_gpu_strided import heads_view, pack_token_major
 
 pytestmark = pytest.mark.gpu
@@ -161,3 +161,97 @@ def test_strided_split_bitwise_equals_contiguous_split(H, N, d):
     eo, es = rel_l2(out_ref, o_ref), rel_l2(st_ref, s_ref)
     log(f"  bitwise equal; oracle out {eo:.3e} state {es:.3e}")
     assert eo <= BF16_GUARD and es <= BF16_GUARD
+
+
+# ---- the fp32 split (la_prefill_f32_ws): the fp32 kernel's segments, the same
+# fold, an fp32 correction ----
+
+def need_f32_split(H, N, d=128):
+    ws = binding.prefill_f32_workspace_bytes(1, H, N, d, DEV)
+    if ws == 0:
+        pytest.skip(f"no fp32 split for B1 H{H} N{N} d{d} on this device")
+    return ws
+
+
+@pytest.mark.parametrize("H,N,d,slopes", [
+    (64, 32768 + 21, 128, None),                         # the fp32 benchmark's shape: 2 segments
+    (32, 32768 + 300, 128, None),                        # 4 segments
+    (8, 65536 + 77, 128, [0.0, 1e-4, 1e-3, 0.01, 0.1, 1.0, 5.0, math.inf]),   # 8; lambda = 1 .. 0
+    (1, 40000, 128, [1e-4]),                             # 4 segments, slow decay: full corrections
+    (1, 70000, 128, [2.0 ** -8]),                        # 8 segments, the slowest model decay
+    (64, 65536 + 5, 64, None),                           # d = 64: 4 segments
+])
+def test_f32_split_matches_oracle(H, N, d, slopes):
+    ws = need_f32_split(H, N, d)
+    inp = inputs.make_prefill(1, H, N, d, torch.float32, 740 + H, init_state=True, device=DEV)
+    if slopes is not None:
+        inp = inputs.PrefillInputs(inp.q, inp.k, inp.v,
+                                   torch.tensor(slopes, dtype=torch.float32, device=DEV), inp.state)
+    log(f"fp32 split prefill B1 H{H} N{N} d{d} (workspace {ws} B), slopes {slopes or 'model'}")
+    st = inp.state.clone()
+    out = binding.prefill(inp.q, inp.k, inp.v, inp.slopes, st)
+    st1 = inp.state.clone()
+    out1 = binding.prefill(inp.q, inp.k, inp.v, inp.slopes, st1, split=False)
+    torch.cuda.synchronize()
+    o_ref, s_ref = oracle_prefill(inp.q, inp.k, inp.v, inp.slopes, inp.state)
+    eo, es = rel_l2(out, o_ref), rel_l2(st, s_ref)
+    eo1, es1 = rel_l2(out1, o_ref), rel_l2(st1, s_ref)
+    log(f"  split: out {eo:.3e} state {es:.3e}; unsplit: out {eo1:.3e} state {es1:.3e}")
+    assert eo <= F32_TOL and es <= F32_TOL
+    assert eo1 <= F32_TOL and es1 <= F32_TOL
+    # fp32 throughout: both sit near single-precision rounding
+    assert max(eo, es, eo1, es1) <= 1e-5, "precision regression"
+
+
+def test_f32_split_is_deterministic():
+    H, N = 32, 40000
+    need_f32_split(H, N)
+    inp = inputs.make_prefill(1, H, N, 128, torch.float32, 751, init_state=True, device=DEV)
+    st1, st2 = inp.state.clone(), inp.state.clone()
+    o1 = binding.prefill(inp.q, inp.k, inp.v, inp.slopes, st1)
+    o2 = binding.prefill(inp.q, inp.k, inp.v, inp.slopes, st2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(st1, st2)
+
+
+def test_f32_workspace_rules_are_checked_before_any_launch():
+    H, N, d = 64, 32768, 128
+    ws = need_f32_split(H, N, d)
+    inp = inputs.make_prefill(1, H, N, d, torch.float32, 752, init_state=True, device=DEV)
+    out = torch.full_like(inp.q, 3.0)
+    st = inp.state.clone()
+    work = torch.empty(ws + 512, dtype=torch.uint8, device=DEV)
+    lib = binding.load_library()
+    s = torch.cuda.current_stream().cuda_stream
+
+    def call(wp, nb):
+        return lib.la_prefill_f32_ws(inp.q.data_ptr(), inp.k.data_ptr(), inp.v.data_ptr(),
+                                     inp.slopes.data_ptr(), out.data_ptr(), st.data_ptr(), 1, H, N,
+                                     d, wp, nb, s)
+    assert call(None, ws) == 1                          # null workspace
+    assert call(work.data_ptr(), ws - 1) == 1           # too small
+    assert call(work.data_ptr() + 128, ws) == 1         # not 256-byte aligned
+    assert call(out.data_ptr(), ws) == 1                # overlaps out
+    assert call(st.data_ptr(), ws) == 1                 # overlaps the state
+    torch.cuda.synchronize()
+    assert bool((out == 3.0).all()) and torch.equal(st, inp.state)   # nothing ran
+    assert call(work.data_ptr(), ws) == 0
+    torch.cuda.synchronize()
+    assert not bool((out == 3.0).all())
+
+
+def test_f32_split_plan():
+    # fp32 workgroups of 32 columns, two per compute unit: a B = 1 launch splits
+    # into S = min(2 x CUs / workgroups, N / 8192, 64) segments when S >= 2
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if cus != 256:
+        pytest.skip("the expected plans are those of a 256-CU device")
+    slot = lambda H, d: H * d * d * 4
+    assert binding.prefill_f32_workspace_bytes(1, 64, 32768, 128, DEV) == 2 * slot(64, 128) + 256
+    assert binding.prefill_f32_workspace_bytes(1, 64, 16384, 128, DEV) == 2 * slot(64, 128) + 256
+    assert binding.prefill_f32_workspace_bytes(1, 64, 16383, 128, DEV) == 0
+    assert binding.prefill_f32_workspace_bytes(1, 32, 32768, 128, DEV) == 4 * slot(32, 128) + 256
+    assert binding.prefill_f32_workspace_bytes(1, 128, 65536, 128, DEV) == 0   # fills the device
+    assert binding.prefill_f32_workspace_bytes(2, 64, 65536, 128, DEV) == 0
+    assert binding.prefill_f32_workspace_bytes(1, 64, 65536, 64, DEV) == 4 * slot(64, 64) + 256
+    assert binding.prefill_f32_workspace_bytes(1, 1, 1 << 20, 128, DEV) == 64 * slot(1, 128) + 768

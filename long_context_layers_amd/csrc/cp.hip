@@ -413,105 +413,86 @@ hipError_t launch_prefill_bf16_split(const uint16_t *q, const uint16_t *k, const
 namespace {
 
 constexpr int FCT = 32;            // fp32 correction: tokens per tile
-constexpr int FCTOK = 128;         // fp32 correction: tokens per chunk (4 tiles)
-constexpr int FCWG = 128;          // fp32 correction: workgroups per (segment, head, slice) at most
-
-template <int D>
-struct alignas(16) CorrF32Smem {
-    float Q[FCT][D + 4];
-    float O[D / 32][FCT][32 + 4];  // partial outputs per wave, [a][j]
-};
+constexpr int FCW = 64;            // fp32 correction: walkers per (segment, head), at most
 
 __device__ __forceinline__ int kk32(int m, int h) { return 8 * (m >> 2) + 4 * h + (m & 3); }
 
 // out_a += lambda^(a+1) q_a S for token a of a later segment (S its starting
 // state), fp32 operands and accumulation (v_mfma_f32_32x32x2_f32): one
-// workgroup per (segment, head, 32 output columns, chunk walker), one wave per
-// 32-row tile t of S, holding S[32t.., j] in the accumulator layout (lane =
-// column j, register r = row 8 (r/4) + 4h + r%4), which is the A operand of
-// S_t^T Q_t^T as it stands; the D/32 partial outputs are summed through LDS and
-// added to out.  The walker takes the FCTOK-token chunks c, c + cstride, ...
-// and stops at the first 32-token tile whose first factor lambda^(a+1) is 0 in
-// fp32 (the factor only falls, so nothing after it changes).
+// workgroup per (segment, head, walker), wave w owning output columns
+// 32w .. 32w + 31 and holding those columns of S for all D rows as B operands
+// (lane = column j, k = lane / 32, row 32t + 8 (m/4) + 4k + m%4 of step (t, m)).
+// A 32-token tile is (Q S)[a][j] = sum over the D rows in D/2 MFMAs, the A
+// operand Q[a = lane % 32][row] read straight from memory (the waves of a
+// workgroup read the same rows, the caches serve the repeats); the result
+// (lane = column, register r = token row 8 (r/4) + 4 (lane/32) + r%4) is added
+// to out with 128-byte row accesses.  No LDS, no barriers.  A head's tiles are
+// those before the first whose first factor lambda^(32 i + 1) is 0 in fp32
+// (found by bisection: the factor only falls; nothing after it changes), cut
+// into W contiguous runs, one per walker.
 template <int D>
 __global__ __launch_bounds__(64 * (D / 32)) void cp_correct_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ slopes, const float *__restrict__ s_in,
     float *__restrict__ out, int64_t H, int64_t hs, int64_t ts, int64_t t_off, int64_t seg,
-    int64_t ntok, int64_t chunks, int64_t cstride)
+    int64_t ntok, int64_t W)
 {
-    constexpr int NT = D / 32, NTH = 64 * NT, NJ = D / 32;
-    constexpr int NQ = FCT * D / 4 / NTH;         // float4 of a q tile per thread
-    __shared__ CorrF32Smem<D> sm;
+    constexpr int NT = D / 32;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
     const int lane = tid % 64, l32 = lane % 32, h = lane / 32;
-    const int64_t c0 = blockIdx.x % cstride, rest = blockIdx.x / cstride;
-    const int j0 = (int)(rest % NJ) * 32;
-    const int64_t hd = (rest / NJ) % H, g = rest / NJ / H;
+    const int64_t walker = blockIdx.x % W, rest = blockIdx.x / W;
+    const int64_t hd = rest % H, g = rest / H;
     const float s = slopes[hd];
     const int64_t a0 = t_off + g * seg;                       // the segment's first token
     const int64_t L = max((int64_t)0, min(seg, ntok - a0));   // its tokens
-    auto tiles = [&](int64_t c) {                             // tiles of chunk c before the underflow
-        const int64_t tbeg = c * FCTOK;
-        const int n = (int)max((int64_t)0, (min(L, tbeg + FCTOK) - tbeg + FCT - 1) / FCT);
-        for (int it = 0; it < n; ++it)
-            if (decay_pow(s, (int)(tbeg + (int64_t)it * FCT + 1)) == 0.0f) return it;
-        return n;
-    };
-    if (c0 >= chunks || tiles(c0) <= 0) return;
+    int64_t lo = 0, hi = (L + FCT - 1) / FCT;                 // first tile with a zero factor
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) / 2;
+        if (decay_pow(s, (int)(mid * FCT + 1)) == 0.0f) hi = mid; else lo = mid + 1;
+    }
+    const int64_t per = (lo + W - 1) / W;
+    const int64_t i0 = walker * per, i1 = min(lo, i0 + per);
+    if (i0 >= i1) return;
 
-    const float *S = s_in + (g * H + hd) * D * D;
-    f32x16 sa;
+    const float *S = s_in + (g * H + hd) * D * D + 32 * wave + l32;
+    float sb[NT][16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sa[r] = S[(32 * wave + kk32(r, h)) * D + j0 + l32];
-    const float *qb = q + hd * hs + a0 * ts;
-    float *ob = out + hd * hs + a0 * ts;
-    for (int64_t chunk = c0; chunk < chunks; chunk += cstride) {
-        const int ntile = tiles(chunk);
-        if (ntile <= 0) break;
-        for (int it = 0; it < ntile; ++it) {
-            const int64_t t0 = chunk * FCTOK + (int64_t)it * FCT;
-            const int c = (int)min((int64_t)FCT, L - t0);
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int u = 0; u < NQ; ++u) {
-                const int e = tid + NTH * u, row = e / (D / 4), c4 = e % (D / 4);
-                float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (row < c) x = *reinterpret_cast<const float4 *>(qb + (t0 + row) * ts + 4 * c4);
-                *reinterpret_cast<float4 *>(&sm.Q[row][4 * c4]) = x;
-            }
-            __syncthreads();                    // the q tile staged
-            float qa[16];
+        for (int m = 0; m < 16; ++m) sb[t][m] = S[(32 * t + kk32(m, h)) * D];
+    const float *qb = q + hd * hs + a0 * ts + 4 * h;
+    float *ob = out + hd * hs + a0 * ts + 32 * wave + l32;
+    for (int64_t i = i0; i < i1; ++i) {
+        const int64_t t0 = i * FCT;
+        const int c = (int)min((int64_t)FCT, L - t0);
+        float4 qa[NT][4];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
-                const float4 x = *reinterpret_cast<const float4 *>(&sm.Q[l32][32 * wave + 8 * gq + 4 * h]);
-                qa[4 * gq] = x.x; qa[4 * gq + 1] = x.y; qa[4 * gq + 2] = x.z; qa[4 * gq + 3] = x.w;
+                qa[t][gq] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (l32 < c)
+                    qa[t][gq] = *reinterpret_cast<const float4 *>(qb + (t0 + l32) * ts + 32 * t + 8 * gq);
             }
-            f32x16 acc = {};
+        float y[16];
 #pragma unroll
-            for (int m = 0; m < 16; ++m) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(sa[m], qa[m], acc, 0, 0, 0);
+        for (int r = 0; r < 16; ++r) {
+            y[r] = 0.f;
+            if (kk32(r, h) < c) y[r] = ob[(t0 + kk32(r, h)) * ts];
+        }
+        f32x16 acc = {};
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq)      // acc: column j = kk32(r, h) of token a = l32
-                *reinterpret_cast<float4 *>(&sm.O[wave][l32][8 * gq + 4 * h]) =
-                    make_float4(acc[4 * gq], acc[4 * gq + 1], acc[4 * gq + 2], acc[4 * gq + 3]);
-            __syncthreads();                    // the partial outputs visible; the q tile read
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int pass = 0; pass < FCT / (NTH / 8); ++pass) {
-                const int a = pass * (NTH / 8) + tid / 8, j = 4 * (tid % 8);
-                if (a < c) {
-                    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-                    for (int t = 0; t < NT; ++t) {
-                        const float4 x = *reinterpret_cast<const float4 *>(&sm.O[t][a][j]);
-                        o.x += x.x; o.y += x.y; o.z += x.z; o.w += x.w;
-                    }
-                    const float f = decay_pow(s, (int)(t0 + a + 1));
-                    float4 *po = reinterpret_cast<float4 *>(ob + (t0 + a) * ts + j0 + j);
-                    float4 y = *po;
-                    y.x = fmaf(f, o.x, y.x); y.y = fmaf(f, o.y, y.y);
-                    y.z = fmaf(f, o.z, y.z); y.w = fmaf(f, o.w, y.w);
-                    *po = y;
-                }
+            for (int m = 0; m < 16; ++m) {
+                const float4 x = qa[t][m >> 2];
+                const float av = (m & 3) == 0 ? x.x : (m & 3) == 1 ? x.y : (m & 3) == 2 ? x.z : x.w;
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, sb[t][m], acc, 0, 0, 0);
             }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int a = kk32(r, h);
+            if (a < c) ob[(t0 + a) * ts] = fmaf(decay_pow(s, (int)(t0 + a + 1)), acc[r], y[r]);
         }
     }
 }
@@ -534,14 +515,14 @@ hipError_t launch_prefill_f32_split(const float *q, const float *k, const float 
     if (e != hipSuccess) return e;
     e = launch_split_fold(slots, state, slopes, H, d, nseg, seg, N, stream);
     if (e != hipSuccess) return e;
-    // segment g >= 1 is corrected with slot g - 1 (the state at its start)
-    const int64_t chunks = (seg + FCTOK - 1) / FCTOK;
-    const int64_t cstride = std::max<int64_t>(1, std::min<int64_t>(chunks, FCWG));
-    const dim3 grid((unsigned)((nseg - 1) * H * (d / 32) * cstride)), block(64 * (d / 32));
-    int64_t hh = H, hs = N * d, ts = d, toff = seg, sg = seg, nt = N, ch = chunks, cs = cstride;
+    // segment g >= 1 is corrected with slot g - 1 (the state at its start), by
+    // about 4096 workgroups in all, at most FCW per segment and head
+    const int64_t W = std::max<int64_t>(1, std::min<int64_t>(FCW, 4096 / ((nseg - 1) * H)));
+    const dim3 grid((unsigned)((nseg - 1) * H * W)), block(64 * (d / 32));
+    int64_t hh = H, hs = N * d, ts = d, toff = seg, sg = seg, nt = N, w = W;
     void *args[] = {(void *)&q, (void *)&slopes, (void *)&slots, (void *)&out, (void *)&hh,
                     (void *)&hs, (void *)&ts, (void *)&toff, (void *)&sg, (void *)&nt,
-                    (void *)&ch, (void *)&cs};
+                    (void *)&w};
     const void *fn = d == 64 ? (const void *)cp_correct_f32_kernel<64>
                              : (const void *)cp_correct_f32_kernel<128>;
     return hipLaunchKernel(fn, grid, block, args, 0, stream);

@@ -437,10 +437,10 @@ int la_prefill_f32_ws(const float *q, const float *k, const float *v, const floa
         overlap(workspace, need, v, act) || overlap(workspace, need, out, act) ||
         overlap(workspace, need, state, st) || overlap(workspace, need, slopes, H * 4))
         return LA_ERR_INVALID_ARG;
-    // the segments' grid, and the correction's (at most 128 workgroups per later
-    // segment, head and 32 columns)
+    // the segments' grid, and the correction's (at most 64 workgroups per later
+    // segment and head)
     if (la::prefill_f32_grid(nseg, H, (int)d) > 0x7fffffff ||
-        (int64_t)(nseg - 1) * H * (d / 32) * 128 > 0x7fffffff)
+        (int64_t)(nseg - 1) * H * 64 > 0x7fffffff)
         return LA_ERR_UNSUPPORTED;
     return hip_status(la::launch_prefill_f32_split(q, k, v, slopes, out, state, H, N, (int)d, nseg,
                                                    workspace, static_cast<hipStream_t>(stream)));

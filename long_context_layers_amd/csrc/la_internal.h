@@ -131,6 +131,15 @@ hipError_t launch_prefill_bf16_nowalk(const uint16_t *q, const uint16_t *k, cons
 // workspace it needs, and the launches (prep, packed prefill, fold, correct)
 int prefill_split_plan(int64_t B, int64_t H, int64_t N, int d, int *njt);
 int64_t split_workspace_bytes(int64_t H, int nseg, int d);
+// the split's segment length (a multiple of 64), its prep (slot 0 <- the
+// caller's state, the others <- 0, *cu <- the segments' offsets after the
+// slots) and its fold (each slot <- the state at its segment's end, the last
+// into the caller's state)
+int64_t split_segment(int64_t N, int nseg);
+hipError_t launch_split_prep(const float *state, float *slots, int64_t **cu, int64_t H, int d,
+                             int nseg, int64_t seg, int64_t N, hipStream_t stream);
+hipError_t launch_split_fold(float *slots, float *state, const float *slopes, int64_t H, int d,
+                             int nseg, int64_t seg, int64_t N, hipStream_t stream);
 hipError_t launch_prefill_bf16_split(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                                      const float *slopes, uint16_t *out, float *state,
                                      int64_t H, int64_t N, int d, int nseg, int njt,

@@ -292,4 +292,124 @@ hipError_t launch_prefill_f32(const float *q, const float *k, const float *v,
     return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 
+// ---- the sequence split for fp32 q, k, v, out (B = 1, dense [1,H,N,d]): the
+// segments on the kernel above, the bf16 split's prep and fold (cp.hip), and
+// the correction in fp32 on the fp32 matrix cores.
+
+namespace {
+
+constexpr int FCT = 32;            // fp32 correction: tokens per tile
+constexpr int FCW = 64;            // fp32 correction: walkers per (segment, head), at most
+
+// out_a += lambda^(a+1) q_a S for token a of a later segment (S its starting
+// state), fp32 operands and accumulation (v_mfma_f32_32x32x2_f32): one
+// workgroup per (segment, head, walker), wave w owning output columns
+// 32w .. 32w + 31 and holding those columns of S for all D rows as B operands
+// (lane = column j, k = lane / 32, row 32t + 8 (m/4) + 4k + m%4 of step (t, m)).
+// A 32-token tile is (Q S)[a][j] = sum over the D rows in D/2 MFMAs, the A
+// operand Q[a = lane % 32][row] read straight from memory (the waves of a
+// workgroup read the same rows, the caches serve the repeats); the result
+// (lane = column, register r = token row 8 (r/4) + 4 (lane/32) + r%4) is added
+// to out with 128-byte row accesses.  No LDS, no barriers.  A head's tiles are
+// those before the first whose first factor lambda^(32 i + 1) is 0 in fp32
+// (found by bisection: the factor only falls; nothing after it changes), cut
+// into W contiguous runs, one per walker.
+template <int D>
+__global__ __launch_bounds__(64 * (D / 32)) void cp_correct_f32_kernel(
+    const float *__restrict__ q, const float *__restrict__ slopes, const float *__restrict__ s_in,
+    float *__restrict__ out, int64_t H, int64_t hs, int64_t ts, int64_t t_off, int64_t seg,
+    int64_t ntok, int64_t W)
+{
+    constexpr int NT = D / 32;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int lane = tid % 64, l32 = lane % 32, h = lane / 32;
+    const int64_t walker = blockIdx.x % W, rest = blockIdx.x / W;
+    const int64_t hd = rest % H, g = rest / H;
+    const float s = slopes[hd];
+    const int64_t a0 = t_off + g * seg;                       // the segment's first token
+    const int64_t L = max((int64_t)0, min(seg, ntok - a0));   // its tokens
+    int64_t lo = 0, hi = (L + FCT - 1) / FCT;                 // first tile with a zero factor
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) / 2;
+        if (decay_pow(s, (int)(mid * FCT + 1)) == 0.0f) hi = mid; else lo = mid + 1;
+    }
+    const int64_t per = (lo + W - 1) / W;
+    const int64_t i0 = walker * per, i1 = min(lo, i0 + per);
+    if (i0 >= i1) return;
+
+    const float *S = s_in + (g * H + hd) * D * D + 32 * wave + l32;
+    float sb[NT][16];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int m = 0; m < 16; ++m) sb[t][m] = S[(32 * t + kk(m, h)) * D];
+    const float *qb = q + hd * hs + a0 * ts + 4 * h;
+    float *ob = out + hd * hs + a0 * ts + 32 * wave + l32;
+    for (int64_t i = i0; i < i1; ++i) {
+        const int64_t t0 = i * FCT;
+        const int c = (int)min((int64_t)FCT, L - t0);
+        float4 qa[NT][4];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                qa[t][gq] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (l32 < c)
+                    qa[t][gq] = *reinterpret_cast<const float4 *>(qb + (t0 + l32) * ts + 32 * t + 8 * gq);
+            }
+        float y[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            y[r] = 0.f;
+            if (kk(r, h) < c) y[r] = ob[(t0 + kk(r, h)) * ts];
+        }
+        f32x16 acc = {};
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+                const float4 x = qa[t][m >> 2];
+                const float av = (m & 3) == 0 ? x.x : (m & 3) == 1 ? x.y : (m & 3) == 2 ? x.z : x.w;
+                acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, sb[t][m], acc, 0, 0, 0);
+            }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int a = kk(r, h);
+            if (a < c) ob[(t0 + a) * ts] = fmaf(decay_pow(s, (int)(t0 + a + 1)), acc[r], y[r]);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_f32_split(const float *q, const float *k, const float *v,
+                                    const float *slopes, float *out, float *state, int64_t H,
+                                    int64_t N, int d, int nseg, void *workspace,
+                                    hipStream_t stream)
+{
+    float *slots = static_cast<float *>(workspace);
+    const int64_t seg = split_segment(N, nseg);
+    int64_t *cu = nullptr;
+    hipError_t e = launch_split_prep(state, slots, &cu, H, d, nseg, seg, N, stream);
+    if (e != hipSuccess) return e;
+    const Strides st = {0, N * d, d};
+    const SeqMap map = {cu, H, 0, N, st, st};
+    e = launch_prefill_f32(q, k, v, slopes, out, slots, nseg, map, d, stream);
+    if (e != hipSuccess) return e;
+    e = launch_split_fold(slots, state, slopes, H, d, nseg, seg, N, stream);
+    if (e != hipSuccess) return e;
+    // segment g >= 1 is corrected with slot g - 1 (the state at its start), by
+    // about 4096 workgroups in all, at most FCW per segment and head
+    const int64_t W = std::max<int64_t>(1, std::min<int64_t>(FCW, 4096 / ((nseg - 1) * H)));
+    const dim3 grid((unsigned)((nseg - 1) * H * W)), block(64 * (d / 32));
+    int64_t hh = H, hs = N * d, ts = d, toff = seg, sg = seg, nt = N, w = W;
+    void *args[] = {(void *)&q, (void *)&slopes, (void *)&slots, (void *)&out, (void *)&hh,
+                    (void *)&hs, (void *)&ts, (void *)&toff, (void *)&sg, (void *)&nt,
+                    (void *)&w};
+    const void *fn = d == 64 ? (const void *)cp_correct_f32_kernel<64>
+                             : (const void *)cp_correct_f32_kernel<128>;
+    return hipLaunchKernel(fn, grid, block, args, 0, stream);
+}
+
 }  // namespace la

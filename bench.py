@@ -302,7 +302,7 @@ def measure_varlen(dev, stream, reps, dense_tflops):
     import torch
     from long_context_layers_amd import binding, inputs
 
-    def one(make, what, from_zero=False):
+    def one(make, what, from_zero=False, states_out=True):
         with torch.cuda.stream(stream):
             inp = make()
             st = inp.states.clone()
@@ -312,14 +312,14 @@ def measure_varlen(dev, stream, reps, dense_tflops):
         nseq = len(inp.lens)
 
         def run():
-            binding.prefill_varlen(inp.q, inp.k, inp.v, inp.slopes, inp.cu_seqlens, st, out=out,
-                                   from_zero=from_zero)
+            binding.prefill_varlen(inp.q, inp.k, inp.v, inp.slopes, inp.cu_seqlens,
+                                   st if states_out else None, out=out, from_zero=from_zero)
 
         with torch.cuda.stream(stream):
             ms = time_launches(stream, run, reps)
         fl = H * T * (4 * d * d + 2 * (C_COUNT + 1) * d)
         # q, k, v, out, and the states written (and read unless from zero)
-        by = H * T * d * 2 * 4 + nseq * H * d * d * 4 * (1 if from_zero else 2)
+        by = H * T * d * 2 * 4 + (nseq * H * d * d * 4 * (1 if from_zero else 2) if states_out else 0)
         tflops = fl / (ms * 1e-3) / 1e12
         gbs = by / (ms * 1e-3) / 1e9
         lo, hi = min(inp.lens), max(inp.lens)
@@ -330,8 +330,11 @@ def measure_varlen(dev, stream, reps, dense_tflops):
         njt = 2 if d == 128 and 2 * H * nseq >= cus else 1
         del inp, st, out
         return {"workload": f"packed prefill H{H} T{T} d{d} bf16: {nseq} sequences of "
-                            f"{lo}..{hi} tokens ({what}), per-sequence fp32 states"
-                            + (" written from zero (la_prefill_varlen_from_zero)" if from_zero else ""),
+                            f"{lo}..{hi} tokens ({what}), "
+                            + ("per-sequence fp32 states" if states_out else "outputs only")
+                            + (" written from zero (la_prefill_varlen_from_zero)" if from_zero and states_out
+                               else " from zero (la_prefill_varlen_from_zero, null states)" if from_zero
+                               else ""),
                 "nseq": nseq, "ms": round(ms, 4), "tflops": round(tflops, 3),
                 "gbs": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
                 "algorithmic_bytes_per_launch": by,
@@ -354,6 +357,12 @@ def measure_varlen(dev, stream, reps, dense_tflops):
     res["many_short_sequences_from_zero"] = one(
         lambda: inputs.make_varlen(64, [64] * 4096, 128, torch.bfloat16, seed=1007,
                                    init_state=False, device=dev), "one block each", from_zero=True)
+    # and with no states at all: a forward pass whose final states are not
+    # needed (training or scoring over packed sequences)
+    res["many_short_sequences_outputs_only"] = one(
+        lambda: inputs.make_varlen(64, [64] * 4096, 128, torch.bfloat16, seed=1007,
+                                   init_state=False, device=dev), "one block each", from_zero=True,
+        states_out=False)
     # the flash models' 32 heads (§2.1.1, Table 1): 128 column-slice workgroups
     # fill half of the device, so only very short sequences walk
     res["flash_heads"] = {

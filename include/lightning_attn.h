@@ -309,7 +309,10 @@ int la_prefill_varlen_strided(const void *q, const void *k, const void *v, const
  * sequence; zeros for an empty one) and never read, which saves a state read
  * per sequence and head (at 64 tokens per sequence and d = 128 the states are
  * half of the launch's bytes).  The same results as la_prefill_varlen_strided
- * on zero-filled states, bitwise; T = 0 writes zero states.  Every other rule
+ * on zero-filled states, bitwise; T = 0 writes zero states.  states may be
+ * NULL: no state is written (outputs only, for a forward pass whose final
+ * states are not needed, such as a training or scoring pass over packed
+ * sequences); the outputs are the same, bitwise.  Every other rule
  * (strides, offsets, sizes, errors): as la_prefill_varlen_strided; the
  * contiguous layout is the strides (T*d, d, T*d, d).  Source: as
  * la_prefill_varlen (Ling and Ring 2.6 Technical Report, §4.1.2: packed

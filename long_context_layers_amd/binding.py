@@ -294,7 +294,7 @@ def prefill_f32_workspace_bytes(B: int, H: int, N: int, d: int, device=None) -> 
 
 
 def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: torch.Tensor,
-                   cu_seqlens: torch.Tensor, states: torch.Tensor,
+                   cu_seqlens: torch.Tensor, states: Optional[torch.Tensor],
                    out: Optional[torch.Tensor] = None, from_zero: bool = False) -> torch.Tensor:
     """Packed variable-length prefill: independent sequences in one launch.
 
@@ -306,7 +306,8 @@ def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: to
     set of strides) and out may be strided [H,T,d] views with a unit channel
     stride (``la_prefill_varlen_strided``).  from_zero (bf16): every sequence
     starts from a zero state and ``states`` is only written, never read
-    (``la_prefill_varlen_from_zero``; empty sequences get zero states).
+    (``la_prefill_varlen_from_zero``; empty sequences get zero states);
+    ``states=None`` with from_zero: outputs only, no state is written.
     """
     if not isinstance(q, torch.Tensor) or q.dim() != 3:
         raise ValueError("q must be a [H,T,d] tensor")
@@ -324,7 +325,8 @@ def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: to
     nseq = cu_seqlens.numel() - 1
     _need(cu_seqlens, "cu_seqlens", torch.int64, dev, (nseq + 1,))
     _need(slopes, "slopes", torch.float32, dev, (H,))
-    _need(states, "states", torch.float32, dev, (nseq, H, d, d))
+    if states is not None or not from_zero:
+        _need(states, "states", torch.float32, dev, (nseq, H, d, d))
     if from_zero:
         if dt != torch.bfloat16:
             raise ValueError("from_zero is taken for bfloat16 only")
@@ -335,8 +337,8 @@ def prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, slopes: to
         with torch.cuda.device(dev):
             rc = load_library().la_prefill_varlen_from_zero(
                 q.data_ptr(), k.data_ptr(), v.data_ptr(), slopes.data_ptr(),
-                cu_seqlens.data_ptr(), nseq, out.data_ptr(), states.data_ptr(), H, T, d,
-                *si, *so, _stream(dev))
+                cu_seqlens.data_ptr(), nseq, out.data_ptr(),
+                None if states is None else states.data_ptr(), H, T, d, *si, *so, _stream(dev))
         _check(rc, "la_prefill_varlen_from_zero")
         return out
     if _strided(q, k, v, out, dt, dev, (H, T, d)):

@@ -225,12 +225,12 @@ bool strides_ok(const int64_t s[3]) {
 // strided bf16 prefill: q, k, v share the view (n, si), out has (n, so)
 int check_strided(const void *q, const void *k, const void *v, const float *slopes,
                   const void *out, const float *state, const int64_t n[3], const int64_t si[3],
-                  const int64_t so[3], int64_t nstate, int64_t d)
+                  const int64_t so[3], int64_t nstate, int64_t d, bool state_optional = false)
 {
     int64_t rows;
     if (!mul_ok(n[0], n[1], &rows) || !mul_ok(rows, n[2], &rows)) return LA_ERR_INVALID_ARG;
     if (rows > 0 && (!q || !k || !v || !out)) return LA_ERR_INVALID_ARG;
-    if (!slopes || !state) return LA_ERR_INVALID_ARG;
+    if (!slopes || (!state && !state_optional)) return LA_ERR_INVALID_ARG;
     if (d != 64 && d != 128) return LA_ERR_UNSUPPORTED;
     if (!strides_ok(si) || !strides_ok(so)) return LA_ERR_INVALID_ARG;
     // token rows of one slice never overlap: the kernel's buffer ranges end at
@@ -246,7 +246,7 @@ int check_strided(const void *q, const void *k, const void *v, const float *slop
         !aligned(state, 16) || !aligned(slopes, 4))
         return LA_ERR_INVALID_ARG;
     if (overlap(out, out_bytes, q, in_bytes) || overlap(out, out_bytes, k, in_bytes) ||
-        overlap(out, out_bytes, v, in_bytes) || overlap(out, out_bytes, state, st_bytes))
+        overlap(out, out_bytes, v, in_bytes) || (state && overlap(out, out_bytes, state, st_bytes)))
         return LA_ERR_INVALID_ARG;
     return LA_OK;
 }
@@ -589,10 +589,11 @@ int prefill_varlen_strided(const void *q, const void *k, const void *v, const fl
     const int64_t n[3] = {1, H, T};
     const int64_t si[3] = {0, in_hstride, in_tstride};
     const int64_t so[3] = {0, out_hstride, out_tstride};
-    const int rc = check_strided(q, k, v, slopes, out, states, n, si, so, nstate, d);
+    // from zero the states are an output only, and may be null (nothing written)
+    const int rc = check_strided(q, k, v, slopes, out, states, n, si, so, nstate, d, zero_init != 0);
     if (rc != LA_OK) return rc;
     if (la::prefill_bf16_grid(nseq, H, (int)d) > 0x7fffffff) return LA_ERR_UNSUPPORTED;
-    if (T == 0 && !zero_init) return LA_OK;     // (from zero, the empty sequences' states are written)
+    if (T == 0 && (!zero_init || !states)) return LA_OK;   // (from zero, empty sequences' states are written)
     la::SeqMap map = {cu_seqlens, H, 0, T, {0, in_hstride, in_tstride}, {0, out_hstride, out_tstride}};
     map.zero_init = zero_init;
     return hip_status(la::launch_prefill_bf16(

@@ -25,7 +25,8 @@ struct SeqMap {
     int64_t H, N, T;      // heads; dense sequence length; packed total length
     Strides in, out;
     int zero_init;        // 1: every sequence starts from a zero state and the states
-                          // are only written (empty sequences: zeros), never read
+                          // are only written (empty sequences: zeros), never read;
+                          // with a null state pointer nothing is written
     int walk_groups;      // a walking launch: groups of its sequences walked side by side
                           // (0 or 1: one group)
 };

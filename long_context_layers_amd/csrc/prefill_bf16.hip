@@ -289,6 +289,7 @@ struct Ctx {                          // per-thread constants of one workgroup
     float s;
     int j0;
     bool zero_init;                   // states start at zero and are only written
+    bool state_out;                   // final states written (false: from zero, outputs only)
 
     // this workgroup's columns of the state of sequence seq: element (i, j) at i * D + j
     __device__ float *state_of(int64_t seq) const { return state + (seq * H + h) * D * D + j0; }
@@ -905,8 +906,9 @@ struct Scan {
                     asm volatile("s_waitcnt vmcnt(0)" : : : "memory");
                     if (more) read_staged<D, T0, NTL>(nxt, wk.slot, ln);
                 }
-                store_via_slot<D, T0, NTL>(wk.slot, cx.state_of(pos.seq), sacc[0], ln,   // the final state out
-                                           ln.l32 + 32 * ln.h);
+                if (cx.state_out)
+                    store_via_slot<D, T0, NTL>(wk.slot, cx.state_of(pos.seq), sacc[0], ln,   // the final state out
+                                               ln.l32 + 32 * ln.h);
                 if (more) {
                     // take up the next sequence (its bf16 copy over the one
                     // just written for the next block), then stage the one
@@ -931,7 +933,7 @@ struct Scan {
     // the step measured slower: it sits on the scan's sequential path)
     __device__ void finish(const Ctx<D> &cx, const Pos &pos) {
         if constexpr (!WALK) {
-            if (cx.nblk > 0 || cx.zero_init) {      // (an empty sequence from zero: zeros)
+            if (cx.state_out && (cx.nblk > 0 || cx.zero_init)) {   // (an empty sequence from zero: zeros)
                 float *St = cx.state_of(pos.seq);
 #pragma unroll
                 for (int jt = 0; jt < NJT; ++jt)
@@ -1145,7 +1147,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_bf16_kernel(
         __syncthreads();
         wk.tb = &tb;
         wk.slot = slot;
-        if (map.zero_init) {             // empty sequences from zero: this slice of their states is 0
+        if (map.zero_init && state) {    // empty sequences from zero: this slice of their states is 0
             const int64_t j0 = (int64_t)slice * PJ * NJT;
             for (int e = 0; e < tb.nempty; ++e) {
                 float *st = state + ((int64_t)tb.empty[e] * map.H + wk.h) * D * D + j0;
@@ -1169,6 +1171,7 @@ __global__ __launch_bounds__(NTHREADS) void prefill_bf16_kernel(
     cx.j0 = (int)slice * PJ * NJT;
     cx.s = slopes[wk.h];
     cx.zero_init = map.zero_init != 0;
+    cx.state_out = state != nullptr;
     // blocks processed: a multiple of the producer's sets (trailing empty blocks are no-ops;
     // an empty sequence leaves its state unchanged)
     constexpr int NSET = nset<PRO>();
@@ -1390,7 +1393,7 @@ hipError_t launch_prefill_bf16(const uint16_t *q, const uint16_t *k, const uint1
         m.cu = map.cu + s0;
         int64_t nseq = seqs - s0 < WALK_SEQS ? seqs - s0 : WALK_SEQS;
         m.walk_groups = prefill_bf16_walk_groups(nseq, map.H, d);
-        float *st = state + s0 * map.H * d * d;
+        float *st = state ? state + s0 * map.H * d * d : nullptr;
         QkPrologue pr = {nullptr, nullptr, 0.0, 0, 0.0f, 0};
         void *args[] = {(void *)&q, (void *)&k, (void *)&v, (void *)&slopes,
                         (void *)&out, (void *)&st, (void *)&m, (void *)&nseq, (void *)&pr};

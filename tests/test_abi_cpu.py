@@ -353,6 +353,8 @@ def test_strided_empty_is_a_noop(lib, fn):
 ])
 def test_strided_rejects_bad_arguments(lib, fn, bad, code):
     # no tokens: even a missing check could not reach a launch
+    if fn == "la_prefill_varlen_from_zero" and bad == dict(state=None):
+        code = LA_OK          # from zero the states may be null: outputs only
     assert getattr(lib, fn)(*_strided_args(fn, N=0, **bad)) == code
 
 
@@ -642,7 +644,16 @@ def test_fused_prologue_prefill_rejects_bad_arguments(lib, bad, code):
 @pytest.mark.parametrize("bad,code", [
     (dict(cu=None), LA_ERR_INVALID_ARG), (dict(cu=FAKE + 0x380004), LA_ERR_INVALID_ARG),
     (dict(nseq=0), LA_ERR_INVALID_ARG), (dict(H=0), LA_ERR_INVALID_ARG),
-    (dict(N=-1), LA_ERR_INVALID_ARG), (dict(state=None), LA_ERR_INVALID_ARG),
+    (dict(N=-1), LA_ERR_INVALID_ARG), (dict(state=None, N=-1), LA_ERR_INVALID_ARG),
+    (dict(state=None, slopes=None), LA_ERR_INVALID_ARG), (dict(state=None, d=32), LA_ERR_UNSUPPORTED),
 ])
 def test_varlen_from_zero_rejects_bad_arguments(lib, bad, code):
     assert lib.la_prefill_varlen_from_zero(*_strided_args("la_prefill_varlen_from_zero", **bad)) == code
+
+
+@needs_no_gpu
+def test_varlen_from_zero_without_states_and_tokens_is_a_noop(lib):
+    # null states: outputs only; with no tokens there is nothing to write (the
+    # same call with states writes the empty sequences' zero states)
+    assert lib.la_prefill_varlen_from_zero(*_strided_args("la_prefill_varlen_from_zero", N=0,
+                                                          state=None)) == LA_OK

@@ -212,3 +212,12 @@ def test_varlen_from_zero_equals_zero_states_bitwise(H, lens):
     for i, n in enumerate(lens):
         if n == 0:
             assert torch.equal(st[i], zero[i]), f"empty sequence {i}: state not zeroed"
+    # no states at all (outputs only): the same outputs, and nothing else written
+    # (a guard buffer right after out stays as it was)
+    buf = torch.full((inp.q.numel() + 4096,), 7.0, dtype=torch.bfloat16, device=DEV)
+    out2 = buf[:inp.q.numel()].view(inp.q.shape)
+    binding.prefill_varlen(inp.q, inp.k, inp.v, inp.slopes, inp.cu_seqlens, None, out=out2,
+                           from_zero=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out2, ref), "outputs without states differ"
+    assert bool((buf[inp.q.numel():] == 7.0).all())

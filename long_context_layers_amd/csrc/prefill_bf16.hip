@@ -270,6 +270,10 @@ struct Walk {
     }
     // the block is the last of its sequence
     __device__ static bool last(const Pos &p) { return p.t0 < p.n && p.t0 + PC >= p.n; }
+    // WALK: the block starts a sequence that starts from a zero state (its
+    // inter term is 0: nothing is carried in)
+    template <class C>
+    __device__ static bool fresh(const C &cx, const Pos &p) { return WALK && cx.zero_init && p.t0 == 0; }
     // WALK: the sequence of table entry j, or -1 past the table's end
     __device__ int64_t seq_at(int j) const { return j < uni(tb->count) ? uni(tb->seq[j]) : -1; }
     // blocks with tokens
@@ -693,10 +697,15 @@ __device__ __forceinline__ void score_decay(float (&dec)[16], float s, int ah, i
 template <int D, int NJT>
 __device__ __forceinline__ void inter_term(const Smem<D, NJT> &sm, int qb, int sb, int ah,
                                            const Lane<D> &ln, float scale, bf16x8 (&qf)[D / 16],
-                                           f32x16 (&acc)[NJT])
+                                           f32x16 (&acc)[NJT], bool zero_state = false)
 {
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) qf[ks] = ld8(&sm.Q[qb][32 * ah + ln.l32][16 * ks + 8 * ln.h]);
+    if (zero_state) {                 // (what the products give on a zero state: +0)
+#pragma unroll
+        for (int jt = 0; jt < NJT; ++jt) acc[jt] = f32x16{};
+        return;
+    }
 #pragma unroll
     for (int jt = 0; jt < NJT; ++jt) {
         f32x16 a = {};
@@ -861,6 +870,19 @@ struct Scan {
     template <int BUF>
     __device__ void step(const Ctx<D> &cx, const Walk<WALK> &wk, const Pos &pos, Smem<D, NJT> &sm,
                          int c, bool last) {
+        // WALK, no state written and the sequence ends here: its state after
+        // this block is never used (the next sequence starts from zero and
+        // its copy for the next block is written below)
+        if (!(WALK && last && !cx.state_out)) update<BUF>(cx, sm, c);
+        if constexpr (WALK) {
+            if (last) hand_over<BUF>(cx, wk, pos, sm);
+        }
+    }
+
+    // the block's decayed update of this wave's state tiles, and their bf16
+    // copy for the next block's inter term
+    template <int BUF>
+    __device__ void update(const Ctx<D> &cx, Smem<D, NJT> &sm, int c) {
         const float sdec = c == PC ? full_decay : (c == 0 ? 1.0f : decay_pow(cx.s, c));
         bf16x8 vwf[NJT][PC / 16];
 #pragma unroll
@@ -888,8 +910,13 @@ struct Scan {
 #pragma unroll
             for (int jt = 0; jt < NJT; ++jt) write_st<D, NJT>(sm, BUF, T0 + t, jt, ln, sacc[jt][t]);
         }
+    }
+
+    // WALK: at the end of a sequence, its final state out and the next one's in
+    template <int BUF>
+    __device__ void hand_over(const Ctx<D> &cx, const Walk<WALK> &wk, const Pos &pos, Smem<D, NJT> &sm) {
         if constexpr (WALK) {
-            if (last) {
+            {
                 // the next sequence's initial state out of LDS first: the
                 // wait for its staging (issued a sequence ago) then covers no
                 // store of this block
@@ -993,7 +1020,7 @@ __device__ void out0_wave(const Ctx<D> &cx, const Walk<WALK> &wk, Pos pos, Smem<
         __syncthreads();
         bf16x8 qf[D / 16];
         f32x16 acc[NJT];
-        inter_term<D, NJT>(sm, BUF, BUF ^ 1, 0, ln, scale, qf, acc);
+        inter_term<D, NJT>(sm, BUF, BUF ^ 1, 0, ln, scale, qf, acc, Walk<WALK>::fresh(cx, pos));
         score_pv<D, NJT>(sm, BUF, 0, qf, dec, ln, acc);
         store_out<D, NJT>(cx, pos, ooff, acc, sm.OT[0], ln, lane);
         wk.next(pos);
@@ -1035,7 +1062,7 @@ __device__ void out1_wave(const Ctx<D> &cx, const Walk<WALK> &wk, Pos pos, Smem<
         __syncthreads();
         bf16x8 qf[D / 16];
         f32x16 acc[NJT];
-        inter_term<D, NJT>(sm, BUF, BUF ^ 1, 1, ln, scale, qf, acc);
+        inter_term<D, NJT>(sm, BUF, BUF ^ 1, 1, ln, scale, qf, acc, Walk<WALK>::fresh(cx, pos));
         score_pv<D, NJT>(sm, BUF, 1, qf, dec, ln, acc);
         if (blk > 0) finish_prev(BUF ^ 1);
 #pragma unroll

@@ -148,3 +148,71 @@ def test_split_prefill_noalloc_replayed_from_a_graph():
         torch.cuda.synchronize()
         assert torch.equal(out, ref), r
         assert torch.equal(state, ref_state), r
+
+
+def test_fp32_split_prefill_replayed_from_a_graph():
+    # la_prefill_f32_ws (prep, the fp32 segments, fold, fp32 correction) with a
+    # workspace allocated before the capture
+    B, H, N, d = 1, 16, 20000, 128
+    ws = binding.prefill_f32_workspace_bytes(B, H, N, d, DEV)
+    if ws == 0:
+        pytest.skip("no fp32 sequence split planned on this device")
+    log(f"graph: la_prefill_f32_ws B{B} H{H} N{N} d{d} (workspace {ws} B), 3 replays")
+    lib = binding.load_library()
+    x = inputs.make_prefill(B, H, N, d, torch.float32, seed=144, init_state=True, device=DEV)
+    work = torch.empty(ws, dtype=torch.uint8, device=DEV)
+    out = torch.empty_like(x.q)
+    state = x.state.clone()
+
+    def call(o, st):
+        rc = lib.la_prefill_f32_ws(x.q.data_ptr(), x.k.data_ptr(), x.v.data_ptr(), x.slopes.data_ptr(),
+                                   o.data_ptr(), st.data_ptr(), B, H, N, d, work.data_ptr(), ws,
+                                   torch.cuda.current_stream().cuda_stream)
+        assert rc == 0
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call(torch.empty_like(out), state.clone())
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(out, state)
+    for r in range(3):
+        state.copy_(x.state)
+        g.replay()
+        torch.cuda.synchronize()
+        got, got_state = out.clone(), state.clone()
+        ref_state = x.state.clone()
+        ref = torch.empty_like(out)
+        call(ref, ref_state)                                 # eager, between the replays
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), r
+        assert torch.equal(got_state, ref_state), r
+
+
+def test_outputs_only_packed_prefill_replayed_from_a_graph():
+    # la_prefill_varlen_from_zero with null states: only the kernel, no state
+    H, lens = 64, [64] * 300 + [1, 0, 200]
+    log(f"graph: la_prefill_varlen_from_zero H{H}, {len(lens)} sequences, null states, 3 replays")
+    x = inputs.make_varlen(H, lens, 128, torch.bfloat16, seed=145, init_state=False, device=DEV)
+    out = torch.empty_like(x.q)
+
+    def call(o):
+        binding.prefill_varlen(x.q, x.k, x.v, x.slopes, x.cu_seqlens, None, out=o, from_zero=True)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call(torch.empty_like(out))
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(out)
+    for r in range(3):
+        out.fill_(7.0)
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        ref = torch.empty_like(out)
+        call(ref)
+        torch.cuda.synchronize()
+        assert torch.equal(got, ref), r

@@ -13,7 +13,12 @@
  *   3. argument errors: d = 96 -> LA_ERR_UNSUPPORTED, a null state ->
  *      LA_ERR_INVALID_ARG, la_status_string for every code;
  *   4. la_prefill_varlen_plan answers 0 or 1 for a valid shape and rejects a
- *      null result pointer.
+ *      null result pointer;
+ *   5. la_prefill_ws (the sequence split through a caller's workspace, sized
+ *      by la_prefill_workspace_bytes) against la_prefill on a long sequence,
+ *      within the bf16 bar, outputs and final state;
+ *   6. la_prefill_varlen_from_zero with null states (outputs only) against
+ *      la_prefill_varlen on zero states, bitwise.
  * Exit status 0 when every check holds; the first failure is printed.
  */
 #include <math.h>
@@ -251,6 +256,85 @@ int main(void)
         printf("packed prefill of 74 sequences x 64 heads: %s\n",
                walks ? "one workgroup per head and 32 columns walks the sequences"
                      : "one workgroup per sequence, head and 32 columns");
+    }
+
+    /* 5. the sequence split through a caller's workspace: one long sequence */
+    {
+        const int64_t NL = 20000;
+        const size_t la = (size_t)H * NL * D;
+        uint16_t *lq = malloc(la * 2), *lk = malloc(la * 2), *lv = malloc(la * 2);
+        for (size_t i = 0; i < la; ++i) {
+            lq[i] = to_bf16(urand() * 0.125f);
+            lk[i] = to_bf16(urand() * 0.125f);
+            lv[i] = to_bf16(urand());
+        }
+        void *xq, *xk, *xv, *xo, *xo2, *work = NULL;
+        float *xs, *xs2;
+        HIP_OK(hipMalloc(&xq, la * 2));
+        HIP_OK(hipMalloc(&xk, la * 2));
+        HIP_OK(hipMalloc(&xv, la * 2));
+        HIP_OK(hipMalloc(&xo, la * 2));
+        HIP_OK(hipMalloc(&xo2, la * 2));
+        HIP_OK(hipMalloc((void **)&xs, (size_t)H * D * D * 4));
+        HIP_OK(hipMalloc((void **)&xs2, (size_t)H * D * D * 4));
+        HIP_OK(hipMemcpy(xq, lq, la * 2, hipMemcpyHostToDevice));
+        HIP_OK(hipMemcpy(xk, lk, la * 2, hipMemcpyHostToDevice));
+        HIP_OK(hipMemcpy(xv, lv, la * 2, hipMemcpyHostToDevice));
+        HIP_OK(hipMemcpy(xs, hs, (size_t)H * D * D * 4, hipMemcpyHostToDevice));
+        HIP_OK(hipMemcpy(xs2, hs, (size_t)H * D * D * 4, hipMemcpyHostToDevice));
+        int64_t wsb = -1;
+        if (la_prefill_workspace_bytes(1, H, NL, D, &wsb) != LA_OK || wsb < 0)
+            return fail("la_prefill_workspace_bytes");
+        if (wsb > 0) HIP_OK(hipMalloc(&work, (size_t)wsb));     /* hipMalloc: 256-byte aligned */
+        if (la_prefill_ws(xq, xk, xv, dslopes, xo, xs, 1, H, NL, D, work, wsb, stream) != LA_OK)
+            return fail("la_prefill_ws");
+        if (la_prefill(xq, xk, xv, dslopes, xo2, xs2, 1, H, NL, D, stream) != LA_OK)
+            return fail("la_prefill over the long sequence");
+        HIP_OK(hipStreamSynchronize(stream));
+        uint16_t *ho = malloc(la * 2), *ho2 = malloc(la * 2);
+        float *fo = malloc(la * 4), *fo2 = malloc(la * 4), *hs1 = malloc((size_t)H * D * D * 4),
+              *hs2 = malloc((size_t)H * D * D * 4);
+        HIP_OK(hipMemcpy(ho, xo, la * 2, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(ho2, xo2, la * 2, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(hs1, xs, (size_t)H * D * D * 4, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(hs2, xs2, (size_t)H * D * D * 4, hipMemcpyDeviceToHost));
+        for (size_t i = 0; i < la; ++i) {
+            fo[i] = from_bf16(ho[i]);
+            fo2[i] = from_bf16(ho2[i]);
+        }
+        const double e5o = max_rel_l2(fo, fo2, H, (int)(NL * D)), e5s = max_rel_l2(hs1, hs2, H, D * D);
+        printf("la_prefill_ws (%lld workspace bytes) vs la_prefill over %lld tokens: out %.3e, state %.3e\n",
+               (long long)wsb, (long long)NL, e5o, e5s);
+        if (!(e5o <= 2e-2) || !(e5s <= 2e-2)) return fail("la_prefill_ws differs from la_prefill");
+        if (work) HIP_OK(hipFree(work));
+        HIP_OK(hipFree(xq)); HIP_OK(hipFree(xk)); HIP_OK(hipFree(xv)); HIP_OK(hipFree(xo));
+        HIP_OK(hipFree(xo2)); HIP_OK(hipFree(xs)); HIP_OK(hipFree(xs2));
+        free(lq); free(lk); free(lv); free(ho); free(ho2); free(fo); free(fo2); free(hs1); free(hs2);
+    }
+
+    /* 6. fresh sequences, outputs only: null states against zero states */
+    {
+        const int64_t cu_h[4] = {0, 70, 71, T};
+        int64_t *cu;
+        float *zst;
+        HIP_OK(hipMalloc((void **)&cu, 4 * 8));
+        HIP_OK(hipMemcpy(cu, cu_h, 4 * 8, hipMemcpyHostToDevice));
+        HIP_OK(hipMalloc((void **)&zst, 3 * st * 4));
+        HIP_OK(hipMemset(zst, 0, 3 * st * 4));
+        if (la_prefill_varlen(q, k, v, dslopes, cu, 3, out, zst, H, T, D, stream) != LA_OK)
+            return fail("la_prefill_varlen on zero states");
+        if (la_prefill_varlen_from_zero(q, k, v, dslopes, cu, 3, out2, NULL, H, T, D,
+                                        (int64_t)T * D, D, (int64_t)T * D, D, stream) != LA_OK)
+            return fail("la_prefill_varlen_from_zero with null states");
+        HIP_OK(hipStreamSynchronize(stream));
+        uint16_t *o1 = malloc(act * 2), *o2h = malloc(act * 2);
+        HIP_OK(hipMemcpy(o1, out, act * 2, hipMemcpyDeviceToHost));
+        HIP_OK(hipMemcpy(o2h, out2, act * 2, hipMemcpyDeviceToHost));
+        if (memcmp(o1, o2h, act * 2) != 0) return fail("outputs-only packed prefill differs");
+        printf("packed prefill from zero, null states == zero states (bitwise)\n");
+        free(o1); free(o2h);
+        HIP_OK(hipFree(cu));
+        HIP_OK(hipFree(zst));
     }
 
     HIP_OK(hipStreamDestroy(stream));

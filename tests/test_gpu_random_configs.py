@@ -1,5 +1,5 @@
 """Seeded random small configurations against the fp64 oracle (GPU): dense,
-packed (both work splits) and strided prefill, decode and multi-token decode, with random batch
+packed (both work splits; also from zero, with and without states out) and strided prefill, decode and multi-token decode, with random batch
 sizes, head counts, lengths (ragged, empty and one-token sequences included),
 head dimensions, initial states and decay ranges (the pages' slopes, slow
 decays near 1, a head with lambda = 0).  Bars as for the named workloads:
@@ -118,6 +118,42 @@ def test_random_packed_prefill_walk(case):
     torch.cuda.synchronize()
     o_ref, s_ref = oracle.prefill_varlen(np64(x.q), np64(x.k), np64(x.v), np64(x.slopes),
                                          x.cu_seqlens.cpu().numpy(), np64(x.states))
+    cu = x.cu_seqlens.cpu().numpy()
+    for i in range(len(lens)):
+        a, b = int(cu[i]), int(cu[i + 1])
+        if b > a:
+            assert oracle.rel_l2(np64(out)[:, a:b], o_ref[:, a:b]) <= BF16_TOL, i
+        assert oracle.rel_l2(np64(st)[i], s_ref[i]) <= BF16_TOL, i
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_random_packed_prefill_from_zero(case):
+    # fresh sequences (la_prefill_varlen_from_zero): the final states written
+    # against the oracle from zero states, and with null states (outputs
+    # only) the same outputs, bitwise; walking and grid launches alternate
+    rng = random.Random(9000 + case)
+    if case % 3 == 0:
+        H, d = 64, 128
+    elif case % 3 == 1:
+        H, d = 128, 64
+    else:
+        H, d = rng.randint(1, 5), rng.choice([64, 128])
+    lens = [rng.choice([0, 1, 64, rng.randint(1, 63), rng.randint(65, 300)])
+            for _ in range(rng.randint(1, 12))]
+    if sum(lens) == 0:
+        lens[0] = 9
+    walks = binding.prefill_varlen_walks(len(lens), H, sum(lens), d)
+    log(f"from-zero case {case}: H{H} d{d} lens {lens} walk={walks}")
+    x = inputs.make_varlen(H, lens, d, torch.bfloat16, seed=9500 + case, init_state=False,
+                           device=DEV)
+    x.slopes = draw_slopes(rng, H)
+    st = torch.full_like(x.states, float("nan"))
+    out = binding.prefill_varlen(x.q, x.k, x.v, x.slopes, x.cu_seqlens, st, from_zero=True)
+    out2 = binding.prefill_varlen(x.q, x.k, x.v, x.slopes, x.cu_seqlens, None, from_zero=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2), "outputs-only call differs"
+    o_ref, s_ref = oracle.prefill_varlen(np64(x.q), np64(x.k), np64(x.v), np64(x.slopes),
+                                         x.cu_seqlens.cpu().numpy(), np.zeros_like(np64(x.states)))
     cu = x.cu_seqlens.cpu().numpy()
     for i in range(len(lens)):
         a, b = int(cu[i]), int(cu[i + 1])

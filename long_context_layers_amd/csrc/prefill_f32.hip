@@ -313,12 +313,16 @@ constexpr int FCW = 64;            // fp32 correction: walkers per (segment, hea
 // to out with 128-byte row accesses.  No LDS, no barriers.  A head's tiles are
 // those before the first whose first factor lambda^(32 i + 1) is 0 in fp32
 // (found by bisection: the factor only falls; nothing after it changes), cut
-// into W contiguous runs, one per walker.
+// into W contiguous runs, one per walker.  The split's layout is dense, token
+// rows D floats apart, so a tile's addresses share one base; each 32-row
+// slice t of the q operands is loaded right before its 16 products (the
+// scheduling barrier keeps the compiler from hoisting all D/2 values' loads),
+// which leaves registers for three waves per SIMD.
 template <int D>
 __global__ __launch_bounds__(64 * (D / 32)) void cp_correct_f32_kernel(
     const float *__restrict__ q, const float *__restrict__ slopes, const float *__restrict__ s_in,
-    float *__restrict__ out, int64_t H, int64_t hs, int64_t ts, int64_t t_off, int64_t seg,
-    int64_t ntok, int64_t W)
+    float *__restrict__ out, int64_t H, int64_t hs, int64_t t_off, int64_t seg, int64_t ntok,
+    int64_t W)
 {
     constexpr int NT = D / 32;
     const int tid = threadIdx.x;
@@ -344,39 +348,39 @@ __global__ __launch_bounds__(64 * (D / 32)) void cp_correct_f32_kernel(
     for (int t = 0; t < NT; ++t)
 #pragma unroll
         for (int m = 0; m < 16; ++m) sb[t][m] = S[(32 * t + kk(m, h)) * D];
-    const float *qb = q + hd * hs + a0 * ts + 4 * h;
-    float *ob = out + hd * hs + a0 * ts + 32 * wave + l32;
+    const float *qb = q + hd * hs + a0 * D + 4 * h;
+    float *ob = out + hd * hs + a0 * D + 32 * wave + l32;
     for (int64_t i = i0; i < i1; ++i) {
         const int64_t t0 = i * FCT;
         const int c = (int)min((int64_t)FCT, L - t0);
-        float4 qa[NT][4];
-#pragma unroll
-        for (int t = 0; t < NT; ++t)
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                qa[t][gq] = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (l32 < c)
-                    qa[t][gq] = *reinterpret_cast<const float4 *>(qb + (t0 + l32) * ts + 32 * t + 8 * gq);
-            }
         float y[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             y[r] = 0.f;
-            if (kk(r, h) < c) y[r] = ob[(t0 + kk(r, h)) * ts];
+            if (kk(r, h) < c) y[r] = ob[(t0 + kk(r, h)) * D];
         }
         f32x16 acc = {};
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
+        for (int t = 0; t < NT; ++t) {
+            float4 qa[4];
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                qa[gq] = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (l32 < c)
+                    qa[gq] = *reinterpret_cast<const float4 *>(qb + (t0 + l32) * D + 32 * t + 8 * gq);
+            }
 #pragma unroll
             for (int m = 0; m < 16; ++m) {
-                const float4 x = qa[t][m >> 2];
+                const float4 x = qa[m >> 2];
                 const float av = (m & 3) == 0 ? x.x : (m & 3) == 1 ? x.y : (m & 3) == 2 ? x.z : x.w;
                 acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, sb[t][m], acc, 0, 0, 0);
             }
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int a = kk(r, h);
-            if (a < c) ob[(t0 + a) * ts] = fmaf(decay_pow(s, (int)(t0 + a + 1)), acc[r], y[r]);
+            if (a < c) ob[(t0 + a) * D] = fmaf(decay_pow(s, (int)(t0 + a + 1)), acc[r], y[r]);
         }
     }
 }
@@ -403,10 +407,9 @@ hipError_t launch_prefill_f32_split(const float *q, const float *k, const float 
     // about 4096 workgroups in all, at most FCW per segment and head
     const int64_t W = std::max<int64_t>(1, std::min<int64_t>(FCW, 4096 / ((nseg - 1) * H)));
     const dim3 grid((unsigned)((nseg - 1) * H * W)), block(64 * (d / 32));
-    int64_t hh = H, hs = N * d, ts = d, toff = seg, sg = seg, nt = N, w = W;
+    int64_t hh = H, hs = N * d, toff = seg, sg = seg, nt = N, w = W;
     void *args[] = {(void *)&q, (void *)&slopes, (void *)&slots, (void *)&out, (void *)&hh,
-                    (void *)&hs, (void *)&ts, (void *)&toff, (void *)&sg, (void *)&nt,
-                    (void *)&w};
+                    (void *)&hs, (void *)&toff, (void *)&sg, (void *)&nt, (void *)&w};
     const void *fn = d == 64 ? (const void *)cp_correct_f32_kernel<64>
                              : (const void *)cp_correct_f32_kernel<128>;
     return hipLaunchKernel(fn, grid, block, args, 0, stream);

@@ -521,8 +521,9 @@ def measure_ceilings(dev, stream, pre_ms, pre_tflops, dec_gbs):
     lib.la_peak_copy.argtypes = [P, P, I64, P]
     lib.la_peak_update.argtypes = [P, I64, P]
     lib.la_peak_mix3.argtypes = [P, P, P, P, I64, P]
+    lib.la_peak_stream_persistent.argtypes = [ctypes.c_int, P, P, P, P, I64, I64, P, P]
     for f in (lib.la_peak_mfma_bf16, lib.la_peak_read, lib.la_peak_write, lib.la_peak_copy,
-              lib.la_peak_update, lib.la_peak_mix3):
+              lib.la_peak_update, lib.la_peak_mix3, lib.la_peak_stream_persistent):
         f.restype = ctypes.c_int
     h = stream.cuda_stream
     nbytes = 4 << 30
@@ -550,11 +551,25 @@ def measure_ceilings(dev, stream, pre_ms, pre_tflops, dec_gbs):
         q4 = nbytes // 4                        # three quarters of a read, b's first half written
         ms_mix = best(lambda: lib.la_peak_mix3(a.data_ptr(), a.data_ptr() + q4, a.data_ptr() + 2 * q4,
                                                b.data_ptr(), q4, h))
+        # the persistent forms (a fixed grid, each workgroup streaming its own region)
+        pers = {}
+        for nb in (1024, 2048):
+            pers[("read", nb)] = best(lambda: lib.la_peak_stream_persistent(
+                0, a.data_ptr(), None, None, None, nbytes, nb, sink.data_ptr(), h))
+            pers[("write", nb)] = best(lambda: lib.la_peak_stream_persistent(
+                1, None, None, None, a.data_ptr(), nbytes, nb, None, h))
+            pers[("mix3", nb)] = best(lambda: lib.la_peak_stream_persistent(
+                2, a.data_ptr(), a.data_ptr() + q4, a.data_ptr() + 2 * q4, b.data_ptr(), q4, nb, None, h))
     del a, b, sink
+    p_rd = max(nbytes / (ms * 1e-3) / 1e9 for (k, _), ms in pers.items() if k == "read")
+    p_wr = max(nbytes / (ms * 1e-3) / 1e9 for (k, _), ms in pers.items() if k == "write")
+    p_mx = max(nbytes / (ms * 1e-3) / 1e9 for (k, _), ms in pers.items() if k == "mix3")
     tf = blocks * 4 * iters * chains * 32768 / (ms_mfma * 1e-3) / 1e12
     rd, wr, cp, up, mx = (x / (ms * 1e-3) / 1e9 for x, ms in
                           ((nbytes, ms_read), (nbytes, ms_write), (nbytes, ms_copy), (nbytes, ms_upd),
                            (nbytes, ms_mix)))
+    chunk_rates = {"read": round(rd, 1), "write": round(wr, 1), "mix3": round(mx, 1)}
+    rd, wr, mx = max(rd, p_rd), max(wr, p_wr), max(mx, p_mx)
     B, H, N, d = PREFILL["B"], PREFILL["H"], PREFILL["N"], PREFILL["d"]
     st = B * H * d * d * 4
     rbytes, wbytes = B * H * N * d * 2 * 3 + st, B * H * N * d * 2 + st
@@ -567,7 +582,12 @@ def measure_ceilings(dev, stream, pre_ms, pre_tflops, dec_gbs):
                       "4 GiB in 64 KB chunks, one per workgroup, each chunk's 16-byte "
                       "nontemporal accesses all in flight (copy and in-place update: 2 GiB "
                       "read + 2 GiB written, counted as 4 GiB; mix3: 3 GiB read + 1 GiB "
-                      "written, the prefill's 3:1 mix); best of 3",
+                      "written, the prefill's 3:1 mix); read, write and mix3 also from 1024 "
+                      "and 2048 persistent workgroups each streaming its own region in 128 KB "
+                      "bursts, the better form reported; best of 3",
+            "chunked_form_gbs": chunk_rates,
+            "persistent_form_gbs": {"read": round(p_rd, 1), "write": round(p_wr, 1),
+                                    "mix3": round(p_mx, 1)},
             "prefill_frac_of_mfma_loop": round(pre_tflops / tf, 4),
             "prefill_floor_ms_at_stream_rates": round(floor_ms, 4),
             "prefill_frac_of_stream_floor": round(floor_ms / pre_ms, 4),

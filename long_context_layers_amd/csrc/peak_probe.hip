@@ -20,6 +20,10 @@
 //   la_peak_mix3        chunks of three buffers read and one written (three
 //                       bytes read for every byte written: the prefill's mix
 //                       of q, k, v in and out back);
+//   la_peak_stream_persistent  read, write or the 3:1 mix again, from a
+//                       fixed grid of workgroups each streaming its own
+//                       contiguous region in 128 KB bursts (higher mixed
+//                       rates than one chunk per workgroup on this chip);
 //   la_peak_l2_read     every workgroup sweeps one small region (a few MB,
 //                       held by each XCD's L2) again and again: L2 hits;
 //   la_peak_lds_read    every thread reads 16-byte LDS words in a loop, no
@@ -169,6 +173,44 @@ __global__ __launch_bounds__(PT) void mix3_kernel(const u32x4 *__restrict__ a, c
     for (int u = 0; u < UNR; ++u) __builtin_nontemporal_store(x[u], &d[o + u * PT]);
 }
 
+// Persistent streams: `blocks` workgroups, workgroup g owning the g-th
+// contiguous 1/blocks of every buffer and streaming it in bursts of BURST
+// 16-byte accesses per thread (128 KB of each buffer per burst): the burst's
+// reads of all NR input buffers are issued before any of its writes, so a
+// workgroup keeps many reads in flight and writes in runs of 128 KB.  On this
+// chip this form sustains a higher mixed read/write rate than one 64 KB chunk
+// per workgroup (the form above), so both are measured and the better taken.
+constexpr int BURST = 32;
+constexpr int64_t BURST16 = (int64_t)PT * BURST;      // 16-byte elements per burst (128 KB)
+
+template <int NR, bool WR>
+__global__ __launch_bounds__(PT) void stream_kernel(const u32x4 *__restrict__ a, const u32x4 *__restrict__ b,
+                                                    const u32x4 *__restrict__ c, u32x4 *__restrict__ d,
+                                                    int64_t region16, float *__restrict__ sink)
+{
+    const int64_t base = blockIdx.x * region16 + threadIdx.x;
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (int64_t o = base; o < base + region16 - threadIdx.x; o += BURST16) {
+        u32x4 x[BURST];
+#pragma unroll
+        for (int u = 0; u < BURST; ++u) {
+            x[u] = u32x4{(unsigned)u, 1u, 2u, 3u};
+            if (NR > 0) x[u] = __builtin_nontemporal_load(&a[o + u * PT]);
+            if (NR > 1) x[u] ^= __builtin_nontemporal_load(&b[o + u * PT]);
+            if (NR > 2) x[u] ^= __builtin_nontemporal_load(&c[o + u * PT]);
+        }
+        if (WR) {
+#pragma unroll
+            for (int u = 0; u < BURST; ++u) __builtin_nontemporal_store(x[u], &d[o + u * PT]);
+        } else {
+#pragma unroll
+            for (int u = 0; u < BURST; ++u) acc ^= x[u];
+        }
+    }
+    const unsigned v = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
+    if (!WR && v == 0x9e3779b9u) sink[blockIdx.x % 4096] = (float)v;   // keeps the loads live
+}
+
 // L2 hits: each workgroup sweeps the region (region16 16-byte elements, a
 // multiple of a chunk) reps times, chunk by chunk, starting at a chunk of its
 // own so the workgroups spread over the L2 channels
@@ -299,6 +341,39 @@ int la_peak_mix3(const void *a, const void *b, const void *c, void *d, int64_t b
     hipLaunchKernelGGL(mix3_kernel, dim3(g), dim3(PT), 0, static_cast<hipStream_t>(stream),
                        static_cast<const u32x4 *>(a), static_cast<const u32x4 *>(b),
                        static_cast<const u32x4 *>(c), static_cast<u32x4 *>(d));
+    return (int)hipGetLastError();
+}
+
+// Persistent forms: `blocks` workgroups (1..65536), bytes a positive multiple
+// of blocks * 128 KB.  kind 0: read `a` (sink: at least 4096 floats);
+// kind 1: write `d`; kind 2: read a, b, c and write their xor to d (the 3:1
+// mix, each buffer `bytes` long).
+int la_peak_stream_persistent(int kind, const void *a, const void *b, const void *c, void *d,
+                              int64_t bytes, int64_t blocks, float *sink, void *stream)
+{
+    if (blocks < 1 || blocks > 65536 || bytes <= 0 || bytes % (blocks * BURST16 * 16) != 0) return -1;
+    const int64_t region16 = bytes / 16 / blocks;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const u32x4 *pa = static_cast<const u32x4 *>(a), *pb = static_cast<const u32x4 *>(b),
+                *pc = static_cast<const u32x4 *>(c);
+    u32x4 *pd = static_cast<u32x4 *>(d);
+    const dim3 g((unsigned)blocks), t(PT);
+    switch (kind) {
+    case 0:
+        if (!a || !sink) return -1;
+        hipLaunchKernelGGL((stream_kernel<1, false>), g, t, 0, s, pa, pa, pa, pd, region16, sink);
+        break;
+    case 1:
+        if (!d) return -1;
+        hipLaunchKernelGGL((stream_kernel<0, true>), g, t, 0, s, pa, pa, pa, pd, region16, sink);
+        break;
+    case 2:
+        if (!a || !b || !c || !d) return -1;
+        hipLaunchKernelGGL((stream_kernel<3, true>), g, t, 0, s, pa, pb, pc, pd, region16, sink);
+        break;
+    default:
+        return -1;
+    }
     return (int)hipGetLastError();
 }
 

@@ -448,7 +448,8 @@ def test_peak_probe_library_loads_and_rejects_bad_arguments():
     peak = ctypes.CDLL(build.PEAK_LIB)
     P, I64 = ctypes.c_void_p, ctypes.c_int64
     for name in ("la_peak_mfma_bf16", "la_peak_read", "la_peak_write", "la_peak_copy",
-                 "la_peak_update", "la_peak_mix3", "la_peak_mfma_chains"):
+                 "la_peak_update", "la_peak_mix3", "la_peak_mfma_chains",
+                 "la_peak_stream_persistent"):
         assert hasattr(peak, name), name
     peak.la_peak_mfma_bf16.argtypes = [I64, I64, P, P]
     peak.la_peak_read.argtypes = [P, I64, P, P]
@@ -467,6 +468,16 @@ def test_peak_probe_library_loads_and_rejects_bad_arguments():
     peak.la_peak_mix3.argtypes = [P, P, P, P, I64, P]
     assert peak.la_peak_mix3(FAKE, FAKE, FAKE, None, 65536, None) == -1
     assert peak.la_peak_mix3(FAKE, FAKE, FAKE, FAKE, 65536 + 16, None) == -1    # not whole chunks
+    f = peak.la_peak_stream_persistent
+    f.argtypes = [ctypes.c_int, P, P, P, P, I64, I64, P, P]
+    burst = 256 * 32 * 16                                   # 128 KB per workgroup burst
+    assert f(0, FAKE, None, None, None, 4 * burst, 4, None, None) == -1        # read needs a sink
+    assert f(1, None, None, None, None, 4 * burst, 4, None, None) == -1        # write needs d
+    assert f(2, FAKE, FAKE, None, FAKE, 4 * burst, 4, None, None) == -1        # mix3 needs a, b, c, d
+    assert f(2, FAKE, FAKE, FAKE, FAKE, 4 * burst + 16, 4, None, None) == -1   # not whole bursts
+    assert f(2, FAKE, FAKE, FAKE, FAKE, 4 * burst, 0, None, None) == -1        # no workgroups
+    assert f(2, FAKE, FAKE, FAKE, FAKE, 4 * burst, 65537, None, None) == -1    # too many
+    assert f(3, FAKE, FAKE, FAKE, FAKE, 4 * burst, 4, FAKE, None) == -1        # unknown kind
 
 
 def _dstr_args(**kw):

@@ -1080,11 +1080,13 @@ def main():
                       "sequence in two segments per head), timed with the rest of its la_prefill_ws "
                       "call: split_prep_kernel, split_fold_kernel, cp_correct_kernel<128, -1>",
             "binding_limit": "memory traffic: a copy of the kernel with its compute removed "
-                             "(same loads and stores) takes as long; per compute unit, the full "
-                             "Q and K blocks every column slice reads through L2 and the output "
-                             "lines shared by two workgroups; not package power (with the "
-                             "redundant score tiles skipped the power drops below the limit and "
-                             "the clock rises 12% at the same time)",
+                             "(same loads and stores) takes as long; against the 3:1 read/write "
+                             "stream this chip sustains (ceilings.hbm_mix3_gbs) the gap is the "
+                             "second pass of each head's Q and K rows through L2 by its other "
+                             "column workgroup (a memory-only probe of that pattern: 3.7 against "
+                             "5.5 TB/s with each workgroup reading only its own bytes); not "
+                             "package power (with the redundant score tiles skipped the power "
+                             "drops below the limit and the clock rises 12% at the same time)",
         },
         "context": {
             "pages_kernel_numbers": "none: the Ling and Ring 2.6 Technical Report gives no "

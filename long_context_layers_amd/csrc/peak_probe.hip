@@ -24,6 +24,9 @@
 //                       fixed grid of workgroups each streaming its own
 //                       contiguous region in 128 KB bursts (higher mixed
 //                       rates than one chunk per workgroup on this chip);
+//   la_peak_pair_pattern  the prefill's memory pattern without arithmetic:
+//                       a pair of workgroups per head slot, each reading the
+//                       full q and k rows (shared) or only its half of them;
 //   la_peak_l2_read     every workgroup sweeps one small region (a few MB,
 //                       held by each XCD's L2) again and again: L2 hits;
 //   la_peak_lds_read    every thread reads 16-byte LDS words in a loop, no
@@ -211,6 +214,48 @@ __global__ __launch_bounds__(PT) void stream_kernel(const u32x4 *__restrict__ a,
     if (!WR && v == 0x9e3779b9u) sink[blockIdx.x % 4096] = (float)v;   // keeps the loads live
 }
 
+// The prefill's memory pattern without its arithmetic: `heads` head slots of
+// T tokens x 256-byte rows in four buffers q, k, v (read) and o (written);
+// workgroups w and w + 8 (one XCD) share a slot (slot (w / 16) 8 + w % 8,
+// half (w / 8) % 2), and walk its 64-token blocks in order.  SHARED: each
+// reads the full q and k rows of a block (the partner's copy an L2 hit, as
+// the prefill's two column workgroups of a head do) and its half of the v
+// rows, and writes its half of the o rows; !SHARED: each reads and writes
+// only its half of every row (the same HBM bytes, nothing read twice).
+template <bool SHARED>
+__global__ __launch_bounds__(PT) void pair_pattern_kernel(const u32x4 *__restrict__ q, const u32x4 *__restrict__ k,
+                                                          const u32x4 *__restrict__ v, u32x4 *__restrict__ o,
+                                                          int64_t T)
+{
+    constexpr int ROW16 = 16;                          // 16-byte chunks per row
+    const int w = blockIdx.x;
+    const int64_t slot = (w / 16) * 8 + w % 8;
+    const int half = (w / 8) % 2, t = threadIdx.x;
+    for (int64_t b0 = 0; b0 < T; b0 += 64) {
+        const int64_t blk = (slot * T + b0) * ROW16;      // first chunk of the block
+        u32x4 x = {0u, 0u, 0u, 0u};
+        if (SHARED) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)                  // 1024 chunks of q and of k
+                x ^= __builtin_nontemporal_load(&q[blk + u * PT + t]) ^
+                     __builtin_nontemporal_load(&k[blk + u * PT + t]);
+        }
+        u32x4 y[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {                    // this half of the 64 rows: 512 chunks
+            const int c = u * PT + t;
+            const int64_t e = blk + (c / 8) * ROW16 + half * 8 + c % 8;
+            if (!SHARED) x ^= __builtin_nontemporal_load(&q[e]) ^ __builtin_nontemporal_load(&k[e]);
+            y[u] = x ^ __builtin_nontemporal_load(&v[e]);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int c = u * PT + t;
+            __builtin_nontemporal_store(y[u], &o[blk + (c / 8) * ROW16 + half * 8 + c % 8]);
+        }
+    }
+}
+
 // L2 hits: each workgroup sweeps the region (region16 16-byte elements, a
 // multiple of a chunk) reps times, chunk by chunk, starting at a chunk of its
 // own so the workgroups spread over the L2 channels
@@ -374,6 +419,23 @@ int la_peak_stream_persistent(int kind, const void *a, const void *b, const void
     default:
         return -1;
     }
+    return (int)hipGetLastError();
+}
+
+// heads: a positive multiple of 8 (2 * heads workgroups); T: tokens per head,
+// a positive multiple of 64; each buffer heads * T * 256 bytes
+int la_peak_pair_pattern(int shared, const void *q, const void *k, const void *v, void *o,
+                         int64_t heads, int64_t T, void *stream)
+{
+    if (!q || !k || !v || !o || heads < 8 || heads % 8 != 0 || heads > (1 << 20) || T < 64 || T % 64 != 0)
+        return -1;
+    const dim3 g((unsigned)(2 * heads)), t(PT);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const u32x4 *pq = static_cast<const u32x4 *>(q), *pk = static_cast<const u32x4 *>(k),
+                *pv = static_cast<const u32x4 *>(v);
+    u32x4 *po = static_cast<u32x4 *>(o);
+    if (shared) hipLaunchKernelGGL(pair_pattern_kernel<true>, g, t, 0, s, pq, pk, pv, po, T);
+    else hipLaunchKernelGGL(pair_pattern_kernel<false>, g, t, 0, s, pq, pk, pv, po, T);
     return (int)hipGetLastError();
 }
 

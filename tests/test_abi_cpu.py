@@ -449,7 +449,7 @@ def test_peak_probe_library_loads_and_rejects_bad_arguments():
     P, I64 = ctypes.c_void_p, ctypes.c_int64
     for name in ("la_peak_mfma_bf16", "la_peak_read", "la_peak_write", "la_peak_copy",
                  "la_peak_update", "la_peak_mix3", "la_peak_mfma_chains",
-                 "la_peak_stream_persistent"):
+                 "la_peak_stream_persistent", "la_peak_pair_pattern"):
         assert hasattr(peak, name), name
     peak.la_peak_mfma_bf16.argtypes = [I64, I64, P, P]
     peak.la_peak_read.argtypes = [P, I64, P, P]
@@ -478,6 +478,12 @@ def test_peak_probe_library_loads_and_rejects_bad_arguments():
     assert f(2, FAKE, FAKE, FAKE, FAKE, 4 * burst, 0, None, None) == -1        # no workgroups
     assert f(2, FAKE, FAKE, FAKE, FAKE, 4 * burst, 65537, None, None) == -1    # too many
     assert f(3, FAKE, FAKE, FAKE, FAKE, 4 * burst, 4, FAKE, None) == -1        # unknown kind
+    pp = peak.la_peak_pair_pattern
+    pp.argtypes = [ctypes.c_int, P, P, P, P, I64, I64, P]
+    assert pp(1, FAKE, FAKE, FAKE, None, 8, 64, None) == -1      # null output
+    assert pp(1, FAKE, FAKE, FAKE, FAKE, 12, 64, None) == -1     # slots not a multiple of 8
+    assert pp(0, FAKE, FAKE, FAKE, FAKE, 8, 100, None) == -1     # tokens not whole blocks
+    assert pp(0, FAKE, FAKE, FAKE, FAKE, 0, 64, None) == -1      # no slots
 
 
 def _dstr_args(**kw):

@@ -522,7 +522,7 @@ def measure_ceilings(dev, stream, pre_ms, pre_tflops, dec_gbs):
     lib.la_peak_update.argtypes = [P, I64, P]
     lib.la_peak_mix3.argtypes = [P, P, P, P, I64, P]
     lib.la_peak_stream_persistent.argtypes = [ctypes.c_int, P, P, P, P, I64, I64, P, P]
-    lib.la_peak_pair_pattern.argtypes = [ctypes.c_int, P, P, P, P, I64, I64, P]
+    lib.la_peak_pair_pattern.argtypes = [ctypes.c_int, ctypes.c_int, P, P, P, P, I64, I64, P]
     for f in (lib.la_peak_mfma_bf16, lib.la_peak_read, lib.la_peak_write, lib.la_peak_copy,
               lib.la_peak_update, lib.la_peak_mix3, lib.la_peak_stream_persistent,
               lib.la_peak_pair_pattern):
@@ -564,9 +564,9 @@ def measure_ceilings(dev, stream, pre_ms, pre_tflops, dec_gbs):
                 2, a.data_ptr(), a.data_ptr() + q4, a.data_ptr() + 2 * q4, b.data_ptr(), q4, nb, None, h))
         # the prefill's pattern without arithmetic: 128 head slots of 32K tokens x 256 B
         # rows (1 GiB per buffer), q and k rows read by both workgroups of a slot or halved
-        pat = {sh: best(lambda: lib.la_peak_pair_pattern(
-            sh, a.data_ptr(), a.data_ptr() + q4, a.data_ptr() + 2 * q4, b.data_ptr(),
-            128, q4 // (128 * 256), h)) for sh in (1, 0)}
+        pat = {(mode, nf): best(lambda: lib.la_peak_pair_pattern(
+            mode, nf, a.data_ptr(), a.data_ptr() + q4, a.data_ptr() + 2 * q4, b.data_ptr(),
+            128, q4 // (128 * 256), h)) for mode in (0, 1, 2) for nf in (1, 4)}
     del a, b, sink
     p_rd = max(nbytes / (ms * 1e-3) / 1e9 for (k, _), ms in pers.items() if k == "read")
     p_wr = max(nbytes / (ms * 1e-3) / 1e9 for (k, _), ms in pers.items() if k == "write")
@@ -596,15 +596,17 @@ def measure_ceilings(dev, stream, pre_ms, pre_tflops, dec_gbs):
             "persistent_form_gbs": {"read": round(p_rd, 1), "write": round(p_wr, 1),
                                     "mix3": round(p_mx, 1)},
             "prefill_pattern_gbs": {
-                "shared_qk_rows": round(nbytes / (pat[1] * 1e-3) / 1e9, 1),
-                "own_half_rows": round(nbytes / (pat[0] * 1e-3) / 1e9, 1),
+                f"{name}_{nf}_in_flight": round(nbytes / (pat[(mode, nf)] * 1e-3) / 1e9, 1)
+                for mode, name in ((0, "column_split"), (1, "own_half_rows"), (2, "own_whole_rows"))
+                for nf in (1, 4)} | {
                 "probe": "la_peak_pair_pattern: 128 head slots x 32K tokens x 256-byte rows in "
                          "q, k, v (read) and o (written), a workgroup pair per slot on one XCD "
-                         "walking 64-token blocks; shared_qk_rows: each reads the full q and k "
-                         "rows (the partner's copy an L2 hit, as the prefill's two column "
-                         "workgroups of a head) and its half of v and o; own_half_rows: each "
-                         "moves only its half of every row (the same HBM bytes); GB/s of HBM "
-                         "bytes"},
+                         "walking 64-token blocks, 1 or 4 blocks loaded before their outputs are "
+                         "written; column_split: each reads the full q and k rows (the partner's "
+                         "copy an L2 hit, as the prefill's two column workgroups of a head) and "
+                         "its half of every v and o row; own_half_rows: each moves only its half "
+                         "of every row (the same HBM bytes); own_whole_rows: each moves the whole "
+                         "rows of its own tokens (a full-width split); GB/s of HBM bytes"},
             "prefill_frac_of_mfma_loop": round(pre_tflops / tf, 4),
             "prefill_floor_ms_at_stream_rates": round(floor_ms, 4),
             "prefill_frac_of_stream_floor": round(floor_ms / pre_ms, 4),

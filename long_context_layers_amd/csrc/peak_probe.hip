@@ -26,7 +26,8 @@
 //                       rates than one chunk per workgroup on this chip);
 //   la_peak_pair_pattern  the prefill's memory pattern without arithmetic:
 //                       a pair of workgroups per head slot, each reading the
-//                       full q and k rows (shared) or only its half of them;
+//                       full q and k rows (the column split), only its half
+//                       of every row, or the whole rows of its own tokens;
 //   la_peak_l2_read     every workgroup sweeps one small region (a few MB,
 //                       held by each XCD's L2) again and again: L2 hits;
 //   la_peak_lds_read    every thread reads 16-byte LDS words in a loop, no
@@ -217,12 +218,14 @@ __global__ __launch_bounds__(PT) void stream_kernel(const u32x4 *__restrict__ a,
 // The prefill's memory pattern without its arithmetic: `heads` head slots of
 // T tokens x 256-byte rows in four buffers q, k, v (read) and o (written);
 // workgroups w and w + 8 (one XCD) share a slot (slot (w / 16) 8 + w % 8,
-// half (w / 8) % 2), and walk its 64-token blocks in order.  SHARED: each
-// reads the full q and k rows of a block (the partner's copy an L2 hit, as
-// the prefill's two column workgroups of a head do) and its half of the v
-// rows, and writes its half of the o rows; !SHARED: each reads and writes
-// only its half of every row (the same HBM bytes, nothing read twice).
-template <bool SHARED>
+// half (w / 8) % 2) and walk its 64-token blocks in order, R blocks loaded
+// before their outputs are written.  MODE 0 (the column split): each reads
+// the full q and k rows of a block (the partner's copy an L2 hit) and its
+// half of every v row, and writes its half of every o row; MODE 1: each
+// moves only its half of every row (the same HBM bytes, nothing read twice);
+// MODE 2 (a full-width split): each moves the whole rows of its own 32 tokens
+// of the block.
+template <int MODE, int R>
 __global__ __launch_bounds__(PT) void pair_pattern_kernel(const u32x4 *__restrict__ q, const u32x4 *__restrict__ k,
                                                           const u32x4 *__restrict__ v, u32x4 *__restrict__ o,
                                                           int64_t T)
@@ -231,28 +234,35 @@ __global__ __launch_bounds__(PT) void pair_pattern_kernel(const u32x4 *__restric
     const int w = blockIdx.x;
     const int64_t slot = (w / 16) * 8 + w % 8;
     const int half = (w / 8) % 2, t = threadIdx.x;
-    for (int64_t b0 = 0; b0 < T; b0 += 64) {
-        const int64_t blk = (slot * T + b0) * ROW16;      // first chunk of the block
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (SHARED) {
+    // chunk u (0, 1) of this thread within a block: half rows, or whole rows of its tokens
+    auto mine = [&](int u) -> int64_t {
+        const int c = u * PT + t;
+        return MODE == 2 ? half * 32 * ROW16 + c : (c / 8) * ROW16 + half * 8 + c % 8;
+    };
+    for (int64_t b0 = 0; b0 < T; b0 += 64 * R) {
+        u32x4 y[R][2];
 #pragma unroll
-            for (int u = 0; u < 4; ++u)                  // 1024 chunks of q and of k
-                x ^= __builtin_nontemporal_load(&q[blk + u * PT + t]) ^
-                     __builtin_nontemporal_load(&k[blk + u * PT + t]);
-        }
-        u32x4 y[2];
+        for (int r = 0; r < R; ++r) {
+            const int64_t blk = (slot * T + b0 + 64 * r) * ROW16;    // first chunk of the block
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (MODE == 0) {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {                    // this half of the 64 rows: 512 chunks
-            const int c = u * PT + t;
-            const int64_t e = blk + (c / 8) * ROW16 + half * 8 + c % 8;
-            if (!SHARED) x ^= __builtin_nontemporal_load(&q[e]) ^ __builtin_nontemporal_load(&k[e]);
-            y[u] = x ^ __builtin_nontemporal_load(&v[e]);
+                for (int u = 0; u < 4; ++u)              // 1024 chunks of q and of k
+                    x ^= __builtin_nontemporal_load(&q[blk + u * PT + t]) ^
+                         __builtin_nontemporal_load(&k[blk + u * PT + t]);
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {                // 512 chunks of this workgroup's part
+                const int64_t e = blk + mine(u);
+                if (MODE != 0) x ^= __builtin_nontemporal_load(&q[e]) ^ __builtin_nontemporal_load(&k[e]);
+                y[r][u] = x ^ __builtin_nontemporal_load(&v[e]);
+            }
         }
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int c = u * PT + t;
-            __builtin_nontemporal_store(y[u], &o[blk + (c / 8) * ROW16 + half * 8 + c % 8]);
-        }
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                __builtin_nontemporal_store(y[r][u], &o[(slot * T + b0 + 64 * r) * ROW16 + mine(u)]);
     }
 }
 
@@ -422,20 +432,29 @@ int la_peak_stream_persistent(int kind, const void *a, const void *b, const void
     return (int)hipGetLastError();
 }
 
-// heads: a positive multiple of 8 (2 * heads workgroups); T: tokens per head,
-// a positive multiple of 64; each buffer heads * T * 256 bytes
-int la_peak_pair_pattern(int shared, const void *q, const void *k, const void *v, void *o,
+// mode 0, 1 or 2 (above); inflight 1 or 4 blocks; heads: a positive multiple
+// of 8 (2 * heads workgroups); T: tokens per head, a positive multiple of
+// 64 * inflight; each buffer heads * T * 256 bytes
+int la_peak_pair_pattern(int mode, int inflight, const void *q, const void *k, const void *v, void *o,
                          int64_t heads, int64_t T, void *stream)
 {
-    if (!q || !k || !v || !o || heads < 8 || heads % 8 != 0 || heads > (1 << 20) || T < 64 || T % 64 != 0)
+    if (!q || !k || !v || !o || mode < 0 || mode > 2 || (inflight != 1 && inflight != 4) ||
+        heads < 8 || heads % 8 != 0 || heads > (1 << 20) || T < 64 * inflight || T % (64 * inflight) != 0)
         return -1;
     const dim3 g((unsigned)(2 * heads)), t(PT);
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const u32x4 *pq = static_cast<const u32x4 *>(q), *pk = static_cast<const u32x4 *>(k),
                 *pv = static_cast<const u32x4 *>(v);
     u32x4 *po = static_cast<u32x4 *>(o);
-    if (shared) hipLaunchKernelGGL(pair_pattern_kernel<true>, g, t, 0, s, pq, pk, pv, po, T);
-    else hipLaunchKernelGGL(pair_pattern_kernel<false>, g, t, 0, s, pq, pk, pv, po, T);
+    const int sel = 3 * (inflight == 4) + mode;
+    switch (sel) {
+    case 0: hipLaunchKernelGGL((pair_pattern_kernel<0, 1>), g, t, 0, s, pq, pk, pv, po, T); break;
+    case 1: hipLaunchKernelGGL((pair_pattern_kernel<1, 1>), g, t, 0, s, pq, pk, pv, po, T); break;
+    case 2: hipLaunchKernelGGL((pair_pattern_kernel<2, 1>), g, t, 0, s, pq, pk, pv, po, T); break;
+    case 3: hipLaunchKernelGGL((pair_pattern_kernel<0, 4>), g, t, 0, s, pq, pk, pv, po, T); break;
+    case 4: hipLaunchKernelGGL((pair_pattern_kernel<1, 4>), g, t, 0, s, pq, pk, pv, po, T); break;
+    default: hipLaunchKernelGGL((pair_pattern_kernel<2, 4>), g, t, 0, s, pq, pk, pv, po, T); break;
+    }
     return (int)hipGetLastError();
 }
 

@@ -479,11 +479,14 @@ def test_peak_probe_library_loads_and_rejects_bad_arguments():
     assert f(2, FAKE, FAKE, FAKE, FAKE, 4 * burst, 65537, None, None) == -1    # too many
     assert f(3, FAKE, FAKE, FAKE, FAKE, 4 * burst, 4, FAKE, None) == -1        # unknown kind
     pp = peak.la_peak_pair_pattern
-    pp.argtypes = [ctypes.c_int, P, P, P, P, I64, I64, P]
-    assert pp(1, FAKE, FAKE, FAKE, None, 8, 64, None) == -1      # null output
-    assert pp(1, FAKE, FAKE, FAKE, FAKE, 12, 64, None) == -1     # slots not a multiple of 8
-    assert pp(0, FAKE, FAKE, FAKE, FAKE, 8, 100, None) == -1     # tokens not whole blocks
-    assert pp(0, FAKE, FAKE, FAKE, FAKE, 0, 64, None) == -1      # no slots
+    pp.argtypes = [ctypes.c_int, ctypes.c_int, P, P, P, P, I64, I64, P]
+    assert pp(0, 1, FAKE, FAKE, FAKE, None, 8, 64, None) == -1      # null output
+    assert pp(0, 1, FAKE, FAKE, FAKE, FAKE, 12, 64, None) == -1     # slots not a multiple of 8
+    assert pp(1, 1, FAKE, FAKE, FAKE, FAKE, 8, 100, None) == -1     # tokens not whole blocks
+    assert pp(1, 4, FAKE, FAKE, FAKE, FAKE, 8, 128, None) == -1     # not whole groups of 4 blocks
+    assert pp(2, 1, FAKE, FAKE, FAKE, FAKE, 0, 64, None) == -1      # no slots
+    assert pp(3, 1, FAKE, FAKE, FAKE, FAKE, 8, 64, None) == -1      # unknown mode
+    assert pp(0, 2, FAKE, FAKE, FAKE, FAKE, 8, 256, None) == -1     # 1 or 4 blocks in flight
 
 
 def _dstr_args(**kw):

@@ -90,6 +90,36 @@ def test_prefill_256k_all_heads():
     assert worst_o <= BF16_GUARD and worst_s <= BF16_GUARD, "precision regression"
 
 
+def test_prefill_beyond_4gib_per_tensor():
+    # maximum size: two 256K sequences (8 GiB per tensor, 2^32 elements), so
+    # the second sequence's slices lie past 4 GiB from each tensor's base.
+    # That sequence alone, launched from a view at its own base (offsets
+    # below 4 GiB, no split), must give the same bits; heads 0 and 63 of it
+    # against the oracle, from a random initial state.
+    B, H, N, d = 2, 64, 262144, 128
+    log(f"prefill B{B} H{H} N{N} d{d} bf16 (8 GiB per tensor) + fp32 initial state")
+    inp = inputs.make_prefill(B, H, N, d, torch.bfloat16, 1013, init_state=True, device=DEV)
+    st = inp.state.clone()
+    out = binding.prefill(inp.q, inp.k, inp.v, inp.slopes, st)
+    torch.cuda.synchronize()
+    st1 = inp.state[1:2].clone()
+    out1 = binding.prefill(inp.q[1:2], inp.k[1:2], inp.v[1:2], inp.slopes, st1, split=False)
+    torch.cuda.synchronize()
+    assert torch.equal(out[1:2], out1), "second sequence: outputs differ from its own launch"
+    assert torch.equal(st[1:2], st1), "second sequence: final states differ from its own launch"
+    del out1, st1
+    heads = [0, 63]
+    idx = torch.tensor(heads, device=DEV)
+    o_ref, s_ref = oracle_prefill(inp.q[1:2], inp.k[1:2], inp.v[1:2], inp.slopes, inp.state[1:2],
+                                  heads=heads)
+    eo = rel_l2(out[1:2].index_select(1, idx), o_ref)
+    es = rel_l2(st[1:2].index_select(1, idx), s_ref)
+    log(f"  bitwise equal to its own launch; heads 0, 63 of the second sequence: "
+        f"out rel-L2 {eo:.3e}  state rel-L2 {es:.3e}")
+    assert eo <= BF16_TOL and es <= BF16_TOL
+    assert eo <= BF16_GUARD and es <= BF16_GUARD, "precision regression"
+
+
 def test_prefill_flash_heads_32k():
     # the flash models' 32 heads of 128 (report §2.1.1, Table 1): 128 column-slice
     # workgroups on a 256-CU device, a long sequence from a random initial state

@@ -148,6 +148,31 @@ def test_decode_b256_64_steps():
     assert worst <= BF16_GUARD and es <= DECODE_STATE_GUARD, "precision regression"
 
 
+def test_decode_states_beyond_4gib():
+    # maximum size: 1100 sequences of 64 heads hold 4.3 GiB of fp32 states, so
+    # the last 76 sequences' states lie past 4 GiB; two steps, the last 8
+    # sequences (every head) against the oracle, and the first sequence too
+    B, H, d = 1100, 64, 128
+    log(f"decode B{B} H{H} d{d} bf16 (4.3 GiB of states), 2 steps")
+    dec = inputs.make_decode(B, H, d, 2, torch.bfloat16, seed=1014, device=DEV)
+    st = dec.state.clone()
+    rows = list(range(B - 8, B)) + [0]
+    idx = torch.tensor(rows, device=DEV)
+    ref = np64(dec.state.index_select(0, idx))
+    s64 = np64(dec.slopes)
+    for t in range(2):
+        o = binding.decode_step(dec.q[t], dec.k[t], dec.v[t], dec.slopes, st)
+        o_ref, ref = oracle.decode_step(np64(dec.q[t].index_select(0, idx)),
+                                        np64(dec.k[t].index_select(0, idx)),
+                                        np64(dec.v[t].index_select(0, idx)), s64, ref)
+        e = rel_l2(o.index_select(0, idx), o_ref)
+        log(f"  step {t}: out rel-L2 {e:.3e} (sequences {B - 8}..{B - 1} and 0)")
+        assert e <= BF16_TOL and e <= BF16_GUARD, (t, e)
+    es = rel_l2(st.index_select(0, idx), ref)
+    log(f"  final states rel-L2 {es:.3e}")
+    assert es <= DECODE_STATE_GUARD
+
+
 # ---- edge cases ------------------------------------------------------------
 
 EDGE_SLOPES = [0.0, 0.5, 30.0]       # lambda = 1, 0.61, ~1e-13

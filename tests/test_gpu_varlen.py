@@ -9,7 +9,7 @@ import torch
 
 import oracle
 from long_context_layers_amd import binding, inputs
-from tests.gpu_util import BF16_TOL, F32_TOL, log, np64
+from tests.gpu_util import BF16_GUARD, BF16_TOL, F32_TOL, log, np64, oracle_prefill, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -42,6 +42,35 @@ def max_err(out, st, o_ref, s_ref, cu, seqs=None):
             eo = max(eo, oracle.rel_l2(out[:, a:b], o_ref[:, a:b]))
         es = max(es, oracle.rel_l2(st[i], s_ref[i]))
     return eo, es
+
+
+def test_varlen_beyond_4gib_per_tensor():
+    # maximum size: 524,288 packed tokens at 64 heads (8 GiB per tensor), so the
+    # later heads' rows of both sequences lie past 4 GiB; the second sequence
+    # packed alone (offsets below 4 GiB) must give the same bits, and heads 0
+    # and 63 of it match the oracle from their random initial states
+    H, d, lens = 64, 128, [200000, 324288]
+    log(f"varlen H{H} d{d} lens {lens} (8 GiB per tensor)")
+    inp = inputs.make_varlen(H, lens, d, torch.bfloat16, seed=1015, init_state=True, device=DEV)
+    out, st = run_varlen(inp)
+    a, b = lens[0], sum(lens)
+    one = inputs.VarlenInputs(inp.q[:, a:b].contiguous(), inp.k[:, a:b].contiguous(),
+                              inp.v[:, a:b].contiguous(),
+                              torch.tensor([0, b - a], dtype=torch.int64, device=DEV),
+                              inp.slopes, inp.states[1:2].clone(), lens[1:])
+    out1, st1 = run_varlen(one)
+    assert torch.equal(out[:, a:b], out1), "second sequence: outputs differ from its own launch"
+    assert torch.equal(st[1:2], st1), "second sequence: final state differs from its own launch"
+    del out1, st1, one
+    heads = [0, 63]
+    idx = torch.tensor(heads, device=DEV)
+    o_ref, s_ref = oracle_prefill(inp.q[:, a:b].unsqueeze(0), inp.k[:, a:b].unsqueeze(0),
+                                  inp.v[:, a:b].unsqueeze(0), inp.slopes, inp.states[1:2], heads=heads)
+    eo = rel_l2(out[:, a:b].unsqueeze(0).index_select(1, idx), o_ref)
+    es = rel_l2(st[1:2].index_select(1, idx), s_ref)
+    log(f"  bitwise equal to its own launch; heads 0, 63: out rel-L2 {eo:.3e}  state rel-L2 {es:.3e}")
+    assert eo <= BF16_TOL and es <= BF16_TOL
+    assert eo <= BF16_GUARD and es <= BF16_GUARD, "precision regression"
 
 
 MIXED = [0, 1, 63, 64, 65, 130, 0, 1000, 7, 257]

@@ -148,6 +148,23 @@ def test_decode_b256_64_steps():
     assert worst <= BF16_GUARD and es <= DECODE_STATE_GUARD, "precision regression"
 
 
+def test_prefill_f32_beyond_4gib_per_tensor():
+    # fp32 activations at the 256K shape: 8 GiB per tensor, the later heads'
+    # rows past 4 GiB (the split call: two segments, fold, fp32 correction);
+    # heads 0 and 63 against the oracle from a random initial state
+    B, H, N, d = 1, 64, 262144, 128
+    log(f"prefill fp32 B{B} H{H} N{N} d{d} (8 GiB per tensor) + fp32 initial state")
+    inp = inputs.make_prefill(B, H, N, d, torch.float32, 1016, init_state=True, device=DEV)
+    out, st = gpu_prefill(inp)
+    heads = [0, 63]
+    idx = torch.tensor(heads, device=DEV)
+    o_ref, s_ref = oracle_prefill(inp.q, inp.k, inp.v, inp.slopes, inp.state, heads=heads)
+    eo = rel_l2(out.index_select(1, idx), o_ref)
+    es = rel_l2(st.index_select(1, idx), s_ref)
+    log(f"  heads 0, 63: out rel-L2 {eo:.3e}  state rel-L2 {es:.3e}")
+    assert eo <= F32_TOL and es <= F32_TOL
+
+
 def test_decode_states_beyond_4gib():
     # maximum size: 1100 sequences of 64 heads hold 4.3 GiB of fp32 states, so
     # the last 76 sequences' states lie past 4 GiB; two steps, the last 8

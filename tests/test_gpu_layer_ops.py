@@ -93,6 +93,32 @@ def test_group_norm_gate_matches_oracle(d, group):
     assert e <= TOL
 
 
+def test_layer_ops_at_256k_sampled_tokens():
+    # the bench's shape (B1 N262144 H64 d128, a 16 GiB projection buffer):
+    # both kernels over every token, checked against the oracle on the first,
+    # middle and last 64 tokens (every head; rotary positions up to 2^18)
+    B, N, H, d = 1, 262144, 64, 128
+    log(f"layer ops at B{B} N{N} H{H} d{d}, sampled tokens against the oracle")
+    _, (q, k, v, gate) = packed_projection(B, N, H, d, 700)
+    g = torch.Generator(device=DEV).manual_seed(701)
+    wq = (1 + 0.1 * torch.randn(d, generator=g, device=DEV)).float()
+    wk = (1 + 0.1 * torch.randn(d, generator=g, device=DEV)).float()
+    w = (1 + 0.1 * torch.randn(H * d, generator=g, device=DEV)).float()
+    qo, ko, vo = binding.qk_norm_rope(q, k, v, wq, wk, H, theta=6e6, rot_dim=64, pos0=0)
+    y = binding.group_norm_gate(qo, gate, w, group=d)
+    torch.cuda.synchronize()
+    for t0 in (0, N // 2 - 32, N - 64):
+        t1 = t0 + 64
+        r = lo.qk_norm_rope(*(np64(x[:, t0:t1]).reshape(B, t1 - t0, H, d) for x in (q, k, v)),
+                            np64(wq), np64(wk), 6e6, 64, t0, 1e-6)
+        eq, ek = rows_err(np64(qo[:, :, t0:t1]), r[0]), rows_err(np64(ko[:, :, t0:t1]), r[1])
+        assert torch.equal(vo[:, :, t0:t1], v[:, t0:t1].reshape(B, t1 - t0, H, d).permute(0, 2, 1, 3))
+        ref = lo.group_norm_gate(np64(qo[:, :, t0:t1]), np64(gate[:, t0:t1]), np64(w), d, 1e-6)
+        ey = rows_err(np64(y[:, t0:t1]), ref)
+        log(f"  tokens {t0}..{t1 - 1}: q {eq:.3e}  k {ek:.3e}  y {ey:.3e}")
+        assert eq <= TOL and ek <= TOL and ey <= TOL
+
+
 def test_layer_chain_matches_oracle():
     # projection outputs -> QK norm + RoPE -> prefill -> grouped norm x gate,
     # every stage on the GPU, against the same chain in fp64 (bar 2e-2: the
